@@ -69,9 +69,9 @@ def _bind(lib):
     lib.orc_silu_mul.restype = None
     lib.orc_silu_mul.argtypes = [_P, _I, _I, _P]
     lib.orc_combine.restype = None
-    lib.orc_combine.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P]
+    lib.orc_combine.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P, _P]
     lib.orc_fused_moe.restype = _I
-    lib.orc_fused_moe.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I]
+    lib.orc_fused_moe.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I]
     return lib
 
 
@@ -177,19 +177,23 @@ class Oracle:
         self.lib.orc_silu_mul(_ptr(gu), rows, two_i // 2, _ptr(h))
         return h
 
-    def combine(self, y, tw, topk_ids, E: int):
-        """y float64 [T*k,H] (binary32 values), tw float32 [T,k], ids int32 [T,k] -> bf16 bits [T,H]."""
+    def combine(self, y, tw, topk_ids, E: int, with_acc: bool = False):
+        """y float64 [T*k,H] (binary32 values), tw float32 [T,k], ids int32 [T,k] -> bf16 bits [T,H]
+        (and, with ``with_acc``, the binary32 accumulators before rounding as float64 [T,H])."""
         y = _c(y, np.float64)
         tw = _c(tw, np.float32)
         ids = _c(topk_ids, np.int32)
         T, k = ids.shape
         H = y.shape[1]
         out = np.empty((T, H), np.uint16)
-        self.lib.orc_combine(_ptr(y), _ptr(tw), _ptr(ids), T, k, E, H, _ptr(out))
-        return out
+        acc = np.empty((T, H), np.float64)
+        self.lib.orc_combine(_ptr(y), _ptr(tw), _ptr(ids), T, k, E, H, _ptr(out), _ptr(acc))
+        return (out, acc) if with_acc else out
 
     def fused_moe(self, x, topk_ids, tw, c13, s13, c2, s2, nthreads: int | None = None):
-        """Fused expert MLP; returns (out bf16 bits [T,H], h bf16 bits [R,I], y float64 [R,H])."""
+        """Fused expert MLP; returns (out bf16 bits [T,H], h bf16 bits [R,I], y float64 [R,H]).
+
+        ``self.last_out_acc`` then holds the combine's binary32 accumulators before rounding [T,H]."""
         x = _c(x, np.uint16)
         ids = _c(topk_ids, np.int32)
         tw = _c(tw, np.float32)
@@ -201,12 +205,14 @@ class Oracle:
         assert c2.shape == (E, H, I) and x.shape == (T, H)
         R = T * k
         out = np.empty((T, H), np.uint16)
+        out_acc = np.empty((T, H), np.float64)
         h = np.zeros((R, I), np.uint16)
         y = np.zeros((R, H), np.float64)
         rc = self.lib.orc_fused_moe(_ptr(x), _ptr(ids), _ptr(tw), T, k, E, H, I, _ptr(c13), _ptr(s13),
-                                    _ptr(c2), _ptr(s2), _ptr(out), _ptr(h), _ptr(y),
+                                    _ptr(c2), _ptr(s2), _ptr(out), _ptr(out_acc), _ptr(h), _ptr(y),
                                     nthreads or default_threads())
         assert rc == 0
+        self.last_out_acc = out_acc
         return out, h, y
 
 

@@ -261,7 +261,7 @@ void orc_silu_mul(const double* gu, int rows, int I, uint16_t* h) {
 /* ------------------------------------------------------------------ */
 
 void orc_combine(const double* y, const float* tw, const int32_t* topk_ids, int T, int k, int E, int H,
-                 uint16_t* out) {
+                 uint16_t* out, double* out_acc) {
     for (int t = 0; t < T; ++t)
         for (int n = 0; n < H; ++n) {
             float acc = 0.0f;
@@ -271,6 +271,7 @@ void orc_combine(const double* y, const float* tw, const int32_t* topk_ids, int 
                 acc = acc + tw[(size_t)t * k + j] * (float)y[((size_t)t * k + j) * H + n];
             }
             out[(size_t)t * H + n] = orc_bf16_rne(acc);
+            if (out_acc) out_acc[(size_t)t * H + n] = (double)acc;  /* the value before rounding */
         }
 }
 
@@ -278,7 +279,8 @@ void orc_combine(const double* y, const float* tw, const int32_t* topk_ids, int 
 /* Fused expert MLP: gate_up (binary32 accumulators, unrounded) ->       */
 /* h = bf16(silu(g) * u) -> down (binary32, unrounded) -> combine.      */
 /* w13: codes [E, 2I, H], scales [E, 2I, H/32]; w2: [E, H, I], [E,H,I/32]. */
-/* Optional outputs: h_out [R, I] bf16, y_out [R, H] (binary64 holder).  */
+/* Optional outputs: out_acc [T, H] (combine accumulators before rounding), */
+/* h_out [R, I] bf16, y_out [R, H] (binary64 holders of binary32 values).   */
 /* ------------------------------------------------------------------ */
 
 typedef struct {
@@ -323,7 +325,7 @@ static void* moe_worker(void* p) {
 int orc_fused_moe(const uint16_t* x, const int32_t* topk_ids, const float* tw, int T, int k,
                   int E, int H, int I,
                   const uint8_t* c13, const uint16_t* s13, const uint8_t* c2, const uint16_t* s2,
-                  uint16_t* out, uint16_t* h_out, double* y_out, int nthreads) {
+                  uint16_t* out, double* out_acc, uint16_t* h_out, double* y_out, int nthreads) {
     size_t R = (size_t)T * k;
     double* gu = (double*)malloc(sizeof(double) * (R ? R : 1) * 2 * (size_t)I);
     uint16_t* h = h_out ? h_out : (uint16_t*)malloc(sizeof(uint16_t) * (R ? R : 1) * (size_t)I);
@@ -337,7 +339,7 @@ int orc_fused_moe(const uint16_t* x, const int32_t* topk_ids, const float* tw, i
     }
     run_threads(moe_worker, jobs, sizeof(moe_job), nthreads);
     free(jobs);
-    orc_combine(y, tw, topk_ids, T, k, E, H, out);
+    orc_combine(y, tw, topk_ids, T, k, E, H, out, out_acc);
     free(gu);
     if (!h_out) free(h);
     if (!y_out) free(y);

@@ -372,7 +372,8 @@ def pin_combine(o):
     y[5] = [9.0, 9.0, 9.0, 9.0]
     tw = np.array([[0.25, 0.75], [2.0, 3.0], [1.0, 1.0]], np.float32)
     ids = np.array([[0, 1], [2, -1], [E, -3]], np.int32)
-    out = o.combine(y, tw, ids, E)
+    out, acc = o.combine(y, tw, ids, E, with_acc=True)
+    assert np.array_equal(acc[0], [6.25, 6.5, 6.75, 7.0]) and np.array_equal(acc[2], [0.0] * 4), acc
     assert np.array_equal(_bits_f32(out[0]), np.float32([6.25, 6.5, 6.75, 7.0])), out[0]
     assert np.array_equal(_bits_f32(out[1]), np.float32([10.0, -10.0, 1.0, 2.0])), out[1]
     assert np.all(out[2] == 0), "token without local routes must be zero"
@@ -402,8 +403,10 @@ def pin_fused_composition(o):
     assert np.array_equal(h[valid], h_ref[valid]), "h"
     y_ref, _ = o.grouped_gemm(h_ref, 1, c2, s2, ids, nthreads=2)
     assert np.array_equal(y[valid], y_ref[valid]), "y"
-    out_ref = o.combine(np.nan_to_num(y_ref, nan=0.0), tw, ids, E)
+    out_ref, acc_ref = o.combine(np.nan_to_num(y_ref, nan=0.0), tw, ids, E, with_acc=True)
     assert np.array_equal(out, out_ref), "combine"
+    assert np.array_equal(o.last_out_acc, acc_ref), "combine accumulators"
+    assert np.array_equal(_bf16_of(acc_ref.astype(np.float32)).reshape(out.shape), out), "acc rounds to out"
     assert np.all(out[4] == 0), "token without local routes"
     # gate rows come first: swapping the gate and up halves of w13 changes h
     c13s = np.concatenate([c13[:, I:], c13[:, :I]], axis=1)
