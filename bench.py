@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A16 MoE hot path on one MI355X.
+
+One step = one fused expert-MLP call on synthetic inputs already resident in
+HBM: routing preparation, gate_up grouped GEMM, SiLU*mul, down grouped GEMM
+and the weighted top-k combine.  The default workload is the
+Qwen3-30B-A3B-shaped layer (128 experts, top-8, hidden 2048, intermediate
+768) at 64 tokens, a decode batch with 4 routed rows per expert.
+
+Every step reads a different copy of the packed weights from a rotation pool
+of at least 1 GiB, larger than the 256 MiB Infinity Cache plus the L2s, so the
+weights come from HBM as they would in serving.
+
+Prints one JSON line: the metric (effective weight GB/s of the step, i.e.
+packed weight bytes of the experts that received a route divided by the step
+time), the roofline of the dominant kernel (the gate_up GEMM, timed with HIP
+events around its launch inside every timed step), and the CPU oracle timed
+on the host on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "us/call + effective weight GB/s (% HBM peak), W4A16 MoE grouped GEMM"
+HBM_PEAK_GBS = 8000.0
+ROTATION_BYTES = 1 << 30
+
+
+def workload_spec(name: str) -> dict:
+    """Shapes and routing of a named workload."""
+    import synth
+
+    def qwen3(T):
+        return dict(E=128, k=8, H=2048, I=768, T=T, cfg=2, routes=lambda: synth.qwen3_routes(T),
+                    desc="Qwen3-30B-A3B-shaped MoE layer: 128 experts, top-8 uniform, hidden 2048, "
+                         "intermediate 768, %d tokens" % T)
+
+    def kimi(T):
+        return dict(E=48, k=8, H=7168, I=2048, T=T, cfg=3, routes=lambda: synth.kimi_decode_routes(T),
+                    desc="Kimi-K2-shaped one-GPU expert share: 48 local of 384 experts, top-8 uniform "
+                         "(about 1/8 of routes local), hidden 7168, intermediate 2048, %d tokens" % T)
+
+    table = {}
+    for T in (1, 8, 64, 512):
+        table["qwen3-moe-t%d" % T] = qwen3(T)
+    for T in (1, 2, 4, 8, 16, 32, 64, 128, 256):
+        table["kimi-moe-t%d" % T] = kimi(T)
+    if name not in table:
+        raise SystemExit("unknown workload %s; choose from %s" % (name, ", ".join(sorted(table))))
+    spec = table[name]
+    spec["name"] = name
+    return spec
+
+
+def packed_weight_bytes(N: int, K: int) -> int:
+    # 16-row x 256-k superblocks of 2304 bytes: 4.5 bits per weight when N % 16 == 0 and K % 256 == 0
+    return ((N + 15) // 16) * ((K + 255) // 256) * 2304
+
+
+def make_inputs(spec):
+    import synth
+
+    E, k, H, I, T = spec["E"], spec["k"], spec["H"], spec["I"], spec["T"]
+    rng = synth.rng_for(spec["cfg"], 7)
+    x = synth.activations(rng, T, H)
+    c13, s13 = synth.expert_weights(spec["cfg"], E, 2 * I, H, salt=1)
+    c2, s2 = synth.expert_weights(spec["cfg"], E, H, I, salt=2)
+    ids = spec["routes"]()
+    tw = rng.uniform(0.1, 1.0, (T, k)).astype(np.float32)
+    tw /= tw.sum(axis=1, keepdims=True)
+    return x, ids, tw, c13, s13, c2, s2
+
+
+def cpu_baseline(spec, inputs, weight_bytes_step, budget_s=10.0):
+    """The oracle (test infrastructure, never the product) timed on the host's cores on this workload."""
+    import oracle
+
+    x, ids, tw, c13, s13, c2, s2 = inputs
+    o = oracle.Oracle(oracle.build())
+    threads = min(16, os.cpu_count() or 1)
+    T = spec["T"]
+    # whole steps when one fits the budget, else the first Ts tokens, extrapolated linearly in tokens
+    t0 = time.perf_counter()
+    o.fused_moe(x[:1], ids[:1], tw[:1], c13, s13, c2, s2, nthreads=threads)
+    one_tok = max(time.perf_counter() - t0, 1e-3)
+    Ts = T if one_tok * T <= 3 * budget_s else max(1, int(budget_s / one_tok))
+    times = []
+    start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        o.fused_moe(x[:Ts], ids[:Ts], tw[:Ts], c13, s13, c2, s2, nthreads=threads)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - start >= budget_s or len(times) >= 5:
+            break
+    med = statistics.median(times)
+    step_s = med * T / Ts
+    sample = ("oracle fused expert MLP (gate_up, SiLU*mul, down, combine; binary32 loops) on %s, "
+              "median of %d runs of %.2f s" % ("the full step of %d tokens" % T if Ts == T else
+                                                 "the first %d of %d tokens, scaled to the step" % (Ts, T),
+                                                 len(times), med))
+    return {"value": weight_bytes_step / step_s / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "us_per_step": step_s * 1e6}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="qwen3-moe-t64")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (no collectives); "
+              "run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import weight_only_int4_amd as w4
+    from weight_only_int4_amd import lib as L
+
+    assert torch.cuda.is_available(), "bench.py needs an MI355X"
+    dev = torch.device("cuda:0")
+    spec = workload_spec(args.workload)
+    E, k, H, I, T = spec["E"], spec["k"], spec["H"], spec["I"], spec["T"]
+    print("[bench] %s" % spec["desc"], file=sys.stderr, flush=True)
+    inputs = make_inputs(spec)
+    x, ids, tw, c13, s13, c2, s2 = inputs
+    flat = ids.reshape(-1)
+    valid = (flat >= 0) & (flat < E)
+    active = np.unique(flat[valid])
+    Rv = int(valid.sum())
+    wb13, wb2 = packed_weight_bytes(2 * I, H), packed_weight_bytes(H, I)
+    weight_bytes_step = len(active) * (wb13 + wb2)
+
+    def u16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    w13 = w4.pack_weights(torch.from_numpy(c13).to(dev), u16(s13))
+    w2 = w4.pack_weights(torch.from_numpy(c2).to(dev), u16(s2))
+    per_copy = w13.packed.numel() + w2.packed.numel()
+    ncopies = max(2, math.ceil(ROTATION_BYTES / per_copy) + 1)
+    copies = [(w13, w2)]
+    for _ in range(ncopies - 1):
+        copies.append((w13.rebind(w13.packed.clone()), w2.rebind(w2.packed.clone())))
+    xd = u16(x).view(torch.bfloat16)
+    idsd = torch.from_numpy(ids).to(dev)
+    twd = torch.from_numpy(tw).to(dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(w4.fused_moe_workspace_bytes(T, k, w13, w2), dtype=torch.uint8, device=dev)
+    p13, p2 = w4.fused_moe_plans(T, k, w13, w2)
+    print("[bench] plans: gate_up %r, down %r; %d active experts, %d local routes; weight pool %d copies x %.1f MB"
+          % (p13, p2, len(active), Rv, ncopies, per_copy / 1e6), file=sys.stderr, flush=True)
+
+    lib = L.load()
+
+    def fused_args(c, stream):
+        a, b = copies[c]
+        return (L._ptr(xd), L._ptr(idsd), L._ptr(twd), T, k, a.handle, b.handle, L._ptr(out), L._ptr(ws),
+                ws.numel(), L._stream(stream))
+
+    def check(rc):
+        if rc:
+            raise L.W4A16Error(rc, lib.w4a16_last_error().decode())
+
+    # ---- timed steps: HIP-graph replays of the fused call, one graph per weight copy
+    stream = torch.cuda.current_stream()
+    for c in range(ncopies):  # eager warm-up of every copy (also initialises the library's launch state)
+        check(lib.w4a16_fused_moe(*fused_args(c, stream)))
+    torch.cuda.synchronize()
+    graphs = []
+    for c in range(ncopies):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            check(lib.w4a16_fused_moe(*fused_args(c, torch.cuda.current_stream())))
+        graphs.append(g)
+    for i in range(args.warmup):
+        graphs[i % ncopies].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % ncopies].replay()
+    t_enqueue = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t0
+    ms_per_step = t_total * 1e3 / args.steps
+    if t_enqueue > 0.9 * t_total:
+        print("[bench] warning: host enqueue (%.1f us/step) is close to the step time" % (t_enqueue * 1e6 / args.steps),
+              file=sys.stderr)
+
+    # ---- per-stage GPU time: the same fused call with HIP events between its stages, on the same stream,
+    # enqueued behind a GPU-side sleep so that every event pair brackets only GPU work
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)  # create the underlying HIP event now
+        return e
+
+    events = [[ev() for _ in range(6)] for _ in range(args.steps)]
+    arrays = [ctypes_array(e) for e in events]  # (pointer, keep-alive array)
+    for c in range(ncopies):
+        check(lib.w4a16_fused_moe_profiled(*fused_args(c, stream), arrays[0][0]))
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2.4e9 * max(0.02, 400e-6 * args.steps)))  # ~clock rate x seconds of host enqueue
+    for i in range(args.steps):
+        check(lib.w4a16_fused_moe_profiled(*fused_args(i % ncopies, stream), arrays[i][0]))
+    torch.cuda.synchronize()
+    stage = np.array([[events[i][s].elapsed_time(events[i][s + 1]) * 1e3 for s in range(5)] for i in range(args.steps)])
+    gpu_step_us = float(np.mean([events[i][0].elapsed_time(events[i][5]) * 1e3 for i in range(args.steps)]))
+    gate_up_us = float(stage[:, 1].mean())
+    value = weight_bytes_step / (ms_per_step * 1e-3) / 1e9
+
+    # dominant kernel: gate_up grouped GEMM (decode or prefill kernel by plan)
+    maxP, maxB = L.route_bounds(T, k, E, p13.block_m)
+    alg_bytes = len(active) * wb13 + T * H * 2 + Rv * 2 * I * 4 + (maxP + maxB) * 4
+    achieved = alg_bytes / (gate_up_us * 1e-6) / 1e9
+    kname = "gemm_%s_kernel<MT=%d,NBW=%d,f32 out> (gate_up, %d waves)" % (
+        "decode" if p13.kernel == L.KERNEL_DECODE else "prefill", p13.block_m // 16, p13.n_blocks, p13.waves)
+
+    stages = ["route_prep", "gate_up", "silu_mul", "down", "combine"]
+    print("[bench] step %.1f us wall (graph replay), %.1f us GPU events; per stage (us): %s" % (
+        ms_per_step * 1e3, gpu_step_us, ", ".join("%s %.1f" % (n, v) for n, v in zip(stages, stage.mean(0)))),
+        file=sys.stderr, flush=True)
+
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s",
+        "us_per_call": round(ms_per_step * 1e3, 2), "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": spec["name"], "description": spec["desc"], "experts": E, "top_k": k,
+                   "tokens": T, "hidden": H, "intermediate": I, "active_experts": int(len(active)),
+                   "local_routes": Rv, "weight_bytes_per_step": int(weight_bytes_step),
+                   "weight_rotation_copies": ncopies, "parallelism": "none (one GPU)"},
+        "stages_us": {n: round(float(v), 2) for n, v in zip(stages, stage.mean(0))},
+        "gpu_us_per_step_events": round(gpu_step_us, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": kname,
+                     "bytes_per_launch": int(alg_bytes), "avg_launch_us": round(gate_up_us, 2)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(spec, inputs, weight_bytes_step, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+def ctypes_array(evs):
+    import ctypes
+
+    arr = (ctypes.c_void_p * len(evs))(*[ctypes.c_void_p(e.cuda_event) for e in evs])
+    return ctypes.cast(arr, ctypes.c_void_p), arr
+
+
+if __name__ == "__main__":
+    main()

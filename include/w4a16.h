@@ -1,0 +1,256 @@
+/*
+ * w4a16.h -- C ABI of libw4a16, a W4A16 mixture-of-experts grouped GEMM for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (sources are the pages this library was designed from):
+ *  - Expert weights are unsigned 4-bit codes q with one BF16 scale per 32
+ *    consecutive k of an (expert, output row); the weight is w = (q - 8) * s,
+ *    dequantised inside the kernels ("vLLM x Novita AI: Chord, Faster INT4 MoE
+ *    for Kimi K2.x", sections "Grouped SM90 kernels" and "H200 and Blackwell
+ *    indexed decode").
+ *  - Each routed activation row is multiplied by its expert's weight matrix
+ *    transposed: out[rows of e] = A[rows of e] @ W[e]^T
+ *    ("LegumMagister/nf4-grouped-gemm", section "Usage").
+ *  - Routing uses the indexed tensors sorted_ids / expert_ids /
+ *    num_tokens_padded, where activations stay unpadded and padding lives in
+ *    the indices as sentinels (Chord page, "Two kernel families" and
+ *    Figure 3), plus per-expert offsets (nf4 page, "Usage").
+ *  - The fused expert MLP chains gate_up, SiLU*mul, down and the weighted
+ *    top-k merge (humans& page, "Dedicated warps keep the pipeline busy").
+ *
+ * Conventions for every call:
+ *  - Returns W4A16_OK (0) or a negative status; the message of the last
+ *    failure on the calling thread is w4a16_last_error().
+ *  - Device buffers are allocated and owned by the caller and passed as raw
+ *    device pointers; the library never allocates device memory, never
+ *    synchronises and never reads device memory from the host.  Work is
+ *    enqueued on the given HIP stream (NULL = the null stream) and may be
+ *    captured into a HIP graph.
+ *  - All checks happen on the host before any launch; a failed check
+ *    launches nothing and leaves every output untouched.
+ *  - BF16 values are passed as uint16_t bit patterns, ids as int32_t,
+ *    router weights as float.  Arrays are row-major and contiguous.
+ *  - Routes are numbered i = t * k + j for token t and slot j.  A route is
+ *    valid (local) when 0 <= topk_ids[i] < E; other ids are skipped: no output
+ *    row is written for them and they contribute nothing to a combine.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    W4A16_OK = 0,
+    W4A16_INVALID_ARG = -1,          /* null pointer, negative size, bad enum */
+    W4A16_UNSUPPORTED_SHAPE = -2,    /* e.g. K not a multiple of 32, too many experts */
+    W4A16_LAYOUT_MISMATCH = -3,      /* weight handle does not match the call */
+    W4A16_WORKSPACE_TOO_SMALL = -4,  /* a caller buffer is smaller than required */
+    W4A16_HIP_ERROR = -5             /* a kernel launch failed */
+};
+
+enum { W4A16_KERNEL_DECODE = 1, W4A16_KERNEL_PREFILL = 2 };
+
+/* Largest expert count the routing kernel accepts. */
+#define W4A16_MAX_EXPERTS 1024
+
+/* Launch plan for one grouped GEMM, chosen by w4a16_plan_select (or filled
+ * by the caller).  block_m must equal the block_m used by w4a16_route_prep
+ * for the routing tensors passed with it. */
+typedef struct w4a16_plan {
+    int32_t kernel;        /* W4A16_KERNEL_DECODE or W4A16_KERNEL_PREFILL */
+    int32_t block_m;       /* rows per route block: 16, 32 or 64 (decode); 64 or 128 (prefill) */
+    int32_t n_blocks;      /* 16-column blocks per wavefront: 1, 2 or 4 */
+    int32_t waves;         /* wavefronts per workgroup: decode splits K across them, prefill splits N */
+    int32_t reserved[4];   /* must be zero */
+} w4a16_plan;
+
+/* Host handle describing one packed weight set (E experts of N x K). */
+typedef struct w4a16_weights w4a16_weights;
+
+/* Message of the last failure on this thread ("" if none). */
+const char* w4a16_last_error(void);
+
+/* Library version string, including the packed-layout version. */
+const char* w4a16_version(void);
+
+/* ---------------------------------------------------------------- weights
+ * Offline re-layout (Chord page, "Grouped SM90 kernels": codes [G,N,K] and
+ * scales [G,N,K/32] are repacked once, before the forward path sees them).
+ */
+
+/* Bytes of the packed buffer for E experts of N x K.  K % 32 == 0 required. */
+int w4a16_packed_bytes(int E, int N, int K, size_t* bytes);
+
+/* Pack one weight set.
+ *   codes   device, uint8 [E,N,K]; the low nibble of each byte is the code q
+ *           (the upper nibble is ignored).
+ *   scales  device, BF16 bits [E,N,K/32]; scales[e,n,g] applies to
+ *           k in [32g, 32g+32).
+ *   packed  device, packed_bytes >= w4a16_packed_bytes(E,N,K); written on
+ *           stream s.  The caller keeps it alive while the handle is used.
+ *   out     receives a host handle (free with w4a16_weights_destroy).
+ * Errors: INVALID_ARG (null pointers, E/N < 1), UNSUPPORTED_SHAPE (K < 32 or
+ * K % 32 != 0), WORKSPACE_TOO_SMALL (packed_bytes), HIP_ERROR. */
+int w4a16_pack_weights(const uint8_t* codes, const uint16_t* scales, int E, int N, int K,
+                       void* packed, size_t packed_bytes, hipStream_t s, w4a16_weights** out);
+
+/* A second handle for another device buffer that holds a byte-identical copy
+ * of w's packed image (for example a copy made with hipMemcpy).  Nothing is
+ * launched. */
+int w4a16_weights_rebind(const w4a16_weights* w, void* packed, w4a16_weights** out);
+
+/* Shape and packed buffer of a handle (any output pointer may be NULL). */
+int w4a16_weights_info(const w4a16_weights* w, int* E, int* N, int* K, void** packed, size_t* bytes);
+
+void w4a16_weights_destroy(w4a16_weights* w);
+
+/* Dequantise one expert from the packed buffer (verification path).
+ *   out_f32  device float [N,K] or NULL: (q - 8) * s, exact in binary32.
+ *   out_bf16 device BF16 bits [N,K] or NULL: that value rounded to nearest
+ *            even, the operand the tensor-core path multiplies.
+ * Errors: INVALID_ARG (expert out of range, both outputs NULL), HIP_ERROR. */
+int w4a16_dequant(const w4a16_weights* w, int expert, float* out_f32, uint16_t* out_bf16, hipStream_t s);
+
+/* ---------------------------------------------------------------- routing
+ * Indexed routing (Chord page, "Two kernel families", Figure 3, and "vLLM
+ * integration": over-allocated buffers consumed without reading the routed
+ * count back to the host).
+ */
+
+/* Capacity of the routing tensors for T tokens, top-k, E experts and block
+ * size block_m: max_padded = ceil((R + min(E,R)*(block_m-1)) / block_m) *
+ * block_m with R = T*k, and max_blocks = max_padded / block_m. */
+int w4a16_route_bounds(int T, int k, int E, int block_m, int* max_padded, int* max_blocks);
+
+/* Stable counting sort of the valid routes by expert (one launch).
+ *   topk_ids          device int32 [T,k]
+ *   sorted_ids        device int32 [max_padded]: expert 0's routes in
+ *                     ascending i, padded with the sentinel R = T*k to a
+ *                     multiple of block_m, then expert 1's, ...; every slot
+ *                     past num_tokens_padded also holds R.
+ *   expert_ids        device int32 [max_blocks]: owner of each block_m
+ *                     block, -1 past num_tokens_padded.  Experts with no
+ *                     routes own no block.
+ *   num_tokens_padded device int32 [1]
+ *   expert_offsets    device int32 [E+1]: exclusive prefix of counts
+ *   counts            device int32 [E]: valid routes per expert
+ * Errors: INVALID_ARG, UNSUPPORTED_SHAPE (E > W4A16_MAX_EXPERTS, block_m not
+ * a positive multiple of 16), HIP_ERROR.  T == 0 is valid. */
+int w4a16_route_prep(const int32_t* topk_ids, int T, int k, int E, int block_m, int32_t* sorted_ids,
+                     int32_t* expert_ids, int32_t* num_tokens_padded, int32_t* expert_offsets,
+                     int32_t* counts, hipStream_t s);
+
+/* ---------------------------------------------------------------- planning */
+
+/* Choose a plan from the routed rows per expert, not the token count (Chord
+ * page, "TL;DR" and "Indexed kernels").  expected_rows_per_expert <= 0 means
+ * T*k/E.  Host only and memoised; environment overrides W4A16_FORCE_KERNEL
+ * (decode|prefill), W4A16_BLOCK_M, W4A16_N_BLOCKS and W4A16_WAVES are read
+ * once and are part of the memo key. */
+int w4a16_plan_select(int T, int k, int E, int N, int K, float expected_rows_per_expert, w4a16_plan* out);
+
+/* ---------------------------------------------------------------- GEMM */
+
+/* Indexed grouped GEMM:
+ *   for every slot p < num_tokens_padded of a block b with expert_ids[b] =
+ *   e >= 0 and sorted_ids[p] = i < R:
+ *     out[i, n] = bf16( sum_k A[i / a_row_div, k] * w[e, n, k] ),  n < N
+ * accumulated in binary32 and rounded to nearest even.
+ *   A          device BF16 bits [*, K] (x [T,K] with a_row_div = k, or
+ *              h [R,K] with a_row_div = 1)
+ *   routing    as produced by w4a16_route_prep with p->block_m for R routes
+ *              and the handle's E experts
+ *   out        device BF16 bits [R, N]; rows of invalid routes untouched
+ *   ws         workspace of w4a16_gemm_workspace_bytes (may be NULL if 0)
+ * Errors: INVALID_ARG, LAYOUT_MISMATCH (bad handle), UNSUPPORTED_SHAPE (plan
+ * values outside the supported set), WORKSPACE_TOO_SMALL, HIP_ERROR. */
+int w4a16_gemm_workspace_bytes(const w4a16_plan* p, int R, int N, size_t* bytes);
+
+int w4a16_grouped_gemm(const uint16_t* A, int a_row_div, const w4a16_weights* w, const int32_t* sorted_ids,
+                       const int32_t* expert_ids, const int32_t* num_tokens_padded, int R,
+                       const w4a16_plan* p, uint16_t* out, void* ws, size_t ws_bytes, hipStream_t s);
+
+/* Same as w4a16_grouped_gemm, but out is device float [R, N] holding the
+ * binary32 accumulators unrounded (for a consumer that keeps full precision,
+ * such as the down projection feeding the weighted combine). */
+int w4a16_grouped_gemm_f32(const uint16_t* A, int a_row_div, const w4a16_weights* w, const int32_t* sorted_ids,
+                           const int32_t* expert_ids, const int32_t* num_tokens_padded, int R,
+                           const w4a16_plan* p, float* out, void* ws, size_t ws_bytes, hipStream_t s);
+
+/* Offsets-form grouped GEMM (nf4 page, "Usage": x sorted by expert, offsets =
+ * cumulative rows per expert): rows [expert_offsets[e], expert_offsets[e+1])
+ * of A_sorted belong to expert e, and
+ *   out[r, n] = bf16( sum_k A_sorted[r, k] * w[e(r), n, k] ),  r < expert_offsets[E].
+ *   expert_offsets  device int32 [E+1], non-decreasing, expert_offsets[E] <= rows_max
+ *   rows_max        host bound on expert_offsets[E] (sizes the launch)
+ *   ws              >= w4a16_offsets_workspace_bytes(rows_max, E, p)
+ * Rows r >= expert_offsets[E] of out are untouched. */
+int w4a16_offsets_workspace_bytes(int rows_max, int E, const w4a16_plan* p, size_t* bytes);
+
+int w4a16_grouped_gemm_offsets(const uint16_t* A_sorted, const int32_t* expert_offsets, int rows_max,
+                               const w4a16_weights* w, const w4a16_plan* p, uint16_t* out, void* ws,
+                               size_t ws_bytes, hipStream_t s);
+
+/* ---------------------------------------------------------------- expert MLP */
+
+/* h[r, c] = bf16( silu(gu[r, c]) * gu[r, I + c] ), silu(g) = g / (1 + exp(-g)),
+ * for r < rows, c < I.  gu device BF16 bits [rows, 2I] (gate columns first),
+ * h device BF16 bits [rows, I]. */
+int w4a16_silu_mul(const uint16_t* gu, int rows, int I, uint16_t* h, hipStream_t s);
+
+/* As w4a16_silu_mul with binary32 gate/up values: gu device float [rows, 2I]. */
+int w4a16_silu_mul_f32(const float* gu, int rows, int I, uint16_t* h, hipStream_t s);
+
+/* out[t, n] = bf16( sum over valid j ascending of topk_w[t,j] * y[t*k+j, n] ),
+ * binary32 accumulation; tokens without a valid route get zeros.
+ * y device float [T*k, H]; topk_w device float [T,k]; topk_ids device int32
+ * [T,k]; out device BF16 bits [T,H] (every row written). */
+int w4a16_moe_combine(const float* y, const float* topk_w, const int32_t* topk_ids, int T, int k, int E,
+                      int H, uint16_t* out, hipStream_t s);
+
+/* Fused expert MLP: route_prep -> gate_up GEMM -> SiLU*mul -> down GEMM ->
+ * weighted top-k combine.  It is exactly the sequence w4a16_route_prep,
+ * w4a16_grouped_gemm_f32 (gate_up, a_row_div = k), w4a16_silu_mul_f32,
+ * w4a16_grouped_gemm_f32 (down, a_row_div = 1), w4a16_moe_combine, with the
+ * plans of w4a16_fused_moe_plans and the buffers carved from ws.
+ *   x       device BF16 bits [T,H]
+ *   w13     handle of [E, 2I, H] weights, gate rows first then up rows
+ *   w2      handle of [E, H, I] weights
+ *   out     device BF16 bits [T,H]; every row written (zero rows for
+ *           tokens without a valid route)
+ *   ws      >= w4a16_fused_moe_workspace_bytes(T, k, w13, w2)
+ * Errors: INVALID_ARG, LAYOUT_MISMATCH (w13 not [E,2I,H] with w2 [E,H,I]),
+ * WORKSPACE_TOO_SMALL, HIP_ERROR. */
+int w4a16_fused_moe_workspace_bytes(int T, int k, const w4a16_weights* w13, const w4a16_weights* w2,
+                                    size_t* bytes);
+
+/* The two plans w4a16_fused_moe uses (they share block_m, hence one set of
+ * routing tensors). */
+int w4a16_fused_moe_plans(int T, int k, const w4a16_weights* w13, const w4a16_weights* w2, w4a16_plan* gate_up,
+                          w4a16_plan* down);
+
+int w4a16_fused_moe(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, int T, int k,
+                    const w4a16_weights* w13, const w4a16_weights* w2, uint16_t* out, void* ws,
+                    size_t ws_bytes, hipStream_t s);
+
+/* w4a16_fused_moe that also records caller-created events on the stream
+ * between its stages: stage_events[0] before routing, [1] before gate_up,
+ * [2] before the activation, [3] before down, [4] before the combine and [5]
+ * after it (NULL = no events, identical to w4a16_fused_moe).  For per-stage
+ * timing of eager calls; nothing else differs. */
+int w4a16_fused_moe_profiled(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, int T, int k,
+                             const w4a16_weights* w13, const w4a16_weights* w2, uint16_t* out, void* ws,
+                             size_t ws_bytes, hipStream_t s, hipEvent_t* stage_events);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

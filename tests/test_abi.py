@@ -1,0 +1,131 @@
+"""The C-ABI library loads and exports every entry point its header declares; host-side checks
+reject bad arguments before anything is launched (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a16_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from weight_only_int4_amd import build, lib as L
+
+    if not os.path.exists(L.LIB_PATH):
+        build.build()
+    return L.load()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("w4a16_pack_weights", "w4a16_route_prep", "w4a16_grouped_gemm", "w4a16_fused_moe",
+                     "w4a16_grouped_gemm_offsets", "w4a16_dequant", "w4a16_plan_select"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from weight_only_int4_amd import lib as L
+
+    for name in declared_functions():
+        assert hasattr(lib, name), "libw4a16.so does not export " + name
+        assert name in L._SIGS, "binding has no signature for " + name
+
+
+def test_packed_bytes(lib):
+    from weight_only_int4_amd import lib as L
+
+    # one superblock = 16 rows x 256 k = 2048 code bytes + 256 scale bytes
+    assert L.packed_bytes(1, 16, 256) == 2304
+    assert L.packed_bytes(8, 512, 256) == 8 * 32 * 2304
+    # ragged shapes pad to whole superblocks
+    assert L.packed_bytes(2, 17, 288) == 2 * 2 * 2 * 2304
+    # 4.5 bits per weight at the Kimi-K2 gate_up shape
+    assert L.packed_bytes(1, 4096, 7168) == 4096 * 7168 * 9 // 16
+
+
+def test_shape_errors(lib):
+    from weight_only_int4_amd import lib as L
+
+    with pytest.raises(L.W4A16Error) as ei:
+        L.packed_bytes(1, 16, 100)
+    assert ei.value.code == -2 and "multiple of 32" in str(ei.value)
+    with pytest.raises(L.W4A16Error) as ei:
+        L.packed_bytes(0, 16, 64)
+    assert ei.value.code == -1
+    sz = ctypes.c_size_t(0)
+    h = ctypes.c_void_p()
+    # pack into a too-small buffer fails before any launch (fake, never dereferenced device pointers)
+    rc = lib.w4a16_pack_weights(ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), 1, 16, 256, ctypes.c_void_p(0x3000),
+                                100, None, ctypes.byref(h))
+    assert rc == -4 and b"needs 2304" in lib.w4a16_last_error()
+    rc = lib.w4a16_pack_weights(None, ctypes.c_void_p(0x2000), 1, 16, 256, ctypes.c_void_p(0x3000), 4096, None,
+                                ctypes.byref(h))
+    assert rc == -1
+    del sz
+
+
+def test_route_bounds(lib):
+    from weight_only_int4_amd import lib as L
+
+    # R = 32 routes, 8 experts, block 16: 32 + 8*15 = 152 -> 160 slots, 10 blocks
+    assert L.route_bounds(16, 2, 8, 16) == (160, 10)
+    assert L.route_bounds(0, 8, 128, 16) == (0, 0)
+    # DeepSeek-V3-like prefill: 4096 tokens x 8, 256 experts, block 128
+    assert L.route_bounds(4096, 8, 256, 128) == (65280, 510)
+    with pytest.raises(L.W4A16Error):
+        L.route_bounds(4, 2, 8, 24)
+
+
+def test_route_bounds_match_oracle(lib, orc):
+    from weight_only_int4_amd import lib as L
+
+    for T, k, E, BM in [(1, 8, 48, 16), (64, 8, 128, 32), (8192, 8, 48, 128), (3, 3, 5, 64)]:
+        assert L.route_bounds(T, k, E, BM) == orc.route_bounds(T, k, E, BM)
+
+
+def test_plan_selector_keys_on_rows_per_expert(lib):
+    from weight_only_int4_amd import lib as L
+
+    # Qwen3-like decode: 64 tokens x 8 / 128 experts = 4 rows per expert
+    p = L.plan_select(64, 8, 128, 1536, 2048)
+    assert p.kernel == L.KERNEL_DECODE and p.block_m == 16
+    # same token count, far fewer experts: 64 x 8 / 4 = 128 rows per expert -> prefill
+    p = L.plan_select(64, 8, 4, 1536, 2048)
+    assert p.kernel == L.KERNEL_PREFILL and p.block_m == 128
+    # an explicit expectation overrides T*k/E
+    p = L.plan_select(64, 8, 128, 1536, 2048, expected_rows_per_expert=30.0)
+    assert p.kernel == L.KERNEL_DECODE and p.block_m == 48
+    # memoised: same answer twice
+    a = L.plan_select(256, 8, 48, 4096, 7168)
+    b = L.plan_select(256, 8, 48, 4096, 7168)
+    assert (a.kernel, a.block_m, a.n_blocks, a.waves) == (b.kernel, b.block_m, b.n_blocks, b.waves)
+
+
+def test_plan_validation(lib):
+    from weight_only_int4_amd import lib as L
+
+    sz = ctypes.c_size_t(0)
+    bad = L.make_plan("decode", 24, 4, 4)
+    assert lib.w4a16_gemm_workspace_bytes(ctypes.byref(bad), 32, 512, ctypes.byref(sz)) == -2
+    bad = L.make_plan("prefill", 96, 4, 4)
+    assert lib.w4a16_gemm_workspace_bytes(ctypes.byref(bad), 32, 512, ctypes.byref(sz)) == -2
+    good = L.make_plan("decode", 16, 4, 4)
+    assert lib.w4a16_gemm_workspace_bytes(ctypes.byref(good), 32, 512, ctypes.byref(sz)) == 0
+
+
+def test_bad_handle_is_rejected(lib):
+    # a host buffer that is not a handle: rejected on the host, nothing launched
+    junk = (ctypes.c_uint32 * 16)()
+    f = ctypes.c_void_p(0x1000)
+    rc = lib.w4a16_dequant(ctypes.cast(junk, ctypes.c_void_p), 0, f, None, None)
+    assert rc == -3 and b"not a w4a16 weight handle" in lib.w4a16_last_error()
+    assert lib.w4a16_dequant(None, 0, f, None, None) == -1

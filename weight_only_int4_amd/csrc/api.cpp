@@ -1,0 +1,553 @@
+// C ABI of libw4a16: argument checks, weight handles, the schedule selector
+// and the orchestration of the fused expert MLP.  No device memory is
+// allocated or read here; every device operation is a launch on the caller's
+// stream.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <map>
+#include <mutex>
+#include <new>
+#include <string>
+#include <tuple>
+
+#include "w4a16_internal.h"
+
+using namespace w4a16;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return W4A16_OK;
+}
+
+int check_launch(hipError_t err, const char* what) {
+    if (err != hipSuccess) return fail(W4A16_HIP_ERROR, "%s: launch failed: %s", what, hipGetErrorString(err));
+    return ok();
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int check_handle(const w4a16_weights* w, const char* what) {
+    if (!w) return fail(W4A16_INVALID_ARG, "%s: weight handle is NULL", what);
+    if (w->magic != kHandleMagic) return fail(W4A16_LAYOUT_MISMATCH, "%s: not a w4a16 weight handle", what);
+    if (w->layout_version != (uint32_t)kLayoutVersion)
+        return fail(W4A16_LAYOUT_MISMATCH, "%s: packed layout version %u, library expects %d", what,
+                    w->layout_version, kLayoutVersion);
+    return W4A16_OK;
+}
+
+void route_bounds(long T, long k, long E, long BM, int* maxP, int* maxB) {
+    const long R = T * k;
+    const long act = R < E ? R : E;
+    const long raw = R + act * (BM - 1);
+    const long blocks = (raw + BM - 1) / BM;
+    *maxP = (int)(blocks * BM);
+    *maxB = (int)blocks;
+}
+
+// ----------------------------------------------------------------- planner
+
+int env_int(const char* name, int dflt) {
+    const char* v = getenv(name);
+    if (!v || !*v) return dflt;
+    return atoi(v);
+}
+
+struct Overrides {
+    int force_kernel = 0;  // 0 auto, else W4A16_KERNEL_*
+    int block_m = 0, n_blocks = 0, waves = 0;
+};
+
+const Overrides& overrides() {
+    static Overrides o = [] {
+        Overrides r;
+        const char* fk = getenv("W4A16_FORCE_KERNEL");
+        if (fk && !strcmp(fk, "decode")) r.force_kernel = W4A16_KERNEL_DECODE;
+        if (fk && !strcmp(fk, "prefill")) r.force_kernel = W4A16_KERNEL_PREFILL;
+        r.block_m = env_int("W4A16_BLOCK_M", 0);
+        r.n_blocks = env_int("W4A16_N_BLOCKS", 0);
+        r.waves = env_int("W4A16_WAVES", 0);
+        return r;
+    }();
+    return o;
+}
+
+// Decode wins while the per-group scale FMAs (4 per output per group) cost
+// less than a full dequantisation of every weight, i.e. below about 60 rows
+// per expert; above that the prefill kernel amortises dequantisation over a
+// tall M tile.
+constexpr float kDecodeMaxRows = 48.0f;
+
+w4a16_plan select_plan(int T, int k, int E, int N, int K, float rows) {
+    const Overrides& ov = overrides();
+    w4a16_plan p;
+    memset(&p, 0, sizeof(p));
+    const int NB = (N + 15) / 16;
+    const int KB = (K + SB_K - 1) / SB_K;
+    int kernel = rows <= kDecodeMaxRows ? W4A16_KERNEL_DECODE : W4A16_KERNEL_PREFILL;
+    if (ov.force_kernel) kernel = ov.force_kernel;
+    p.kernel = kernel;
+    if (kernel == W4A16_KERNEL_DECODE) {
+        // cover ~1.3x the expected rows in one block so a slightly heavy expert
+        // does not spill into a second pass over all of K (Chord page, "Grouped
+        // SM90 kernels", masked decode sizing)
+        int bm = (int)ceilf(1.3f * rows / 16.0f) * 16;
+        p.block_m = bm < 16 ? 16 : (bm > 64 ? 64 : bm);
+        p.n_blocks = NB >= 64 ? 4 : (NB >= 8 ? 2 : 1);
+        p.waves = KB >= 4 ? 4 : (KB >= 2 ? 2 : 1);
+        // the cross-wavefront reduction buffer must fit in 64 KiB of LDS
+        while (p.waves > 1 && sizeof(float) * (size_t)p.waves * p.block_m * (p.n_blocks * 16 + 1) > 65536) --p.waves;
+    } else {
+        p.block_m = rows >= 96.0f ? 128 : 64;
+        p.n_blocks = 4;
+        p.waves = 4;
+    }
+    if (ov.block_m) p.block_m = ov.block_m;
+    if (ov.n_blocks) p.n_blocks = ov.n_blocks;
+    if (ov.waves) p.waves = ov.waves;
+    (void)T; (void)k; (void)E;
+    return p;
+}
+
+int validate_plan(const w4a16_plan* p, const char* what) {
+    if (!p) return fail(W4A16_INVALID_ARG, "%s: plan is NULL", what);
+    for (int i = 0; i < 4; ++i)
+        if (p->reserved[i]) return fail(W4A16_INVALID_ARG, "%s: plan.reserved must be zero", what);
+    if (p->kernel == W4A16_KERNEL_DECODE) {
+        if (p->block_m % 16 || p->block_m < 16 || p->block_m > 64)
+            return fail(W4A16_UNSUPPORTED_SHAPE, "%s: decode block_m %d not in {16,32,48,64}", what, p->block_m);
+        if (p->n_blocks != 1 && p->n_blocks != 2 && p->n_blocks != 4)
+            return fail(W4A16_UNSUPPORTED_SHAPE, "%s: decode n_blocks %d not in {1,2,4}", what, p->n_blocks);
+        if (p->waves < 1 || p->waves > 4)
+            return fail(W4A16_UNSUPPORTED_SHAPE, "%s: decode waves %d not in 1..4", what, p->waves);
+        const size_t lds = sizeof(float) * (size_t)p->waves * p->block_m * (p->n_blocks * 16 + 1);
+        if (lds > 65536)
+            return fail(W4A16_UNSUPPORTED_SHAPE, "%s: decode plan needs %zu bytes of LDS (max 65536)", what, lds);
+    } else if (p->kernel == W4A16_KERNEL_PREFILL) {
+        if (p->block_m != 64 && p->block_m != 128)
+            return fail(W4A16_UNSUPPORTED_SHAPE, "%s: prefill block_m %d not in {64,128}", what, p->block_m);
+        if (p->n_blocks != 2 && p->n_blocks != 4)
+            return fail(W4A16_UNSUPPORTED_SHAPE, "%s: prefill n_blocks %d not in {2,4}", what, p->n_blocks);
+        if (p->waves < 1 || p->waves > 4)
+            return fail(W4A16_UNSUPPORTED_SHAPE, "%s: prefill waves %d not in 1..4", what, p->waves);
+    } else {
+        return fail(W4A16_INVALID_ARG, "%s: unknown kernel %d", what, p->kernel);
+    }
+    return W4A16_OK;
+}
+
+hipError_t run_gemm(const GemmArgs& a, const w4a16_plan& p, hipStream_t s) {
+    return p.kernel == W4A16_KERNEL_DECODE ? launch_gemm_decode(a, p, s) : launch_gemm_prefill(a, p, s);
+}
+
+// Workspace carve-up of the fused expert MLP.
+struct FusedLayout {
+    int maxP, maxB;
+    size_t off_sorted, off_eids, off_ntp, off_offsets, off_counts, off_gu, off_h, off_y, total;
+};
+
+FusedLayout fused_layout(int T, int k, int E, int H, int I, int BM) {
+    FusedLayout f;
+    route_bounds(T, k, E, BM, &f.maxP, &f.maxB);
+    const size_t R = (size_t)T * k;
+    size_t o = 0;
+    f.off_sorted = o; o = align_up(o + sizeof(int32_t) * (size_t)f.maxP, 256);
+    f.off_eids = o;   o = align_up(o + sizeof(int32_t) * (size_t)f.maxB, 256);
+    f.off_ntp = o;    o = align_up(o + sizeof(int32_t), 256);
+    f.off_offsets = o; o = align_up(o + sizeof(int32_t) * (size_t)(E + 1), 256);
+    f.off_counts = o; o = align_up(o + sizeof(int32_t) * (size_t)E, 256);
+    f.off_gu = o;     o = align_up(o + sizeof(float) * R * 2 * I, 256);
+    f.off_h = o;      o = align_up(o + sizeof(uint16_t) * R * I, 256);
+    f.off_y = o;      o = align_up(o + sizeof(float) * R * H, 256);
+    f.total = o;
+    return f;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* w4a16_last_error(void) { return g_last_error.c_str(); }
+
+const char* w4a16_version(void) { return "libw4a16 0.1 (packed layout 1, gfx950)"; }
+
+int w4a16_packed_bytes(int E, int N, int K, size_t* bytes) {
+    if (!bytes) return fail(W4A16_INVALID_ARG, "w4a16_packed_bytes: bytes is NULL");
+    if (E < 1 || N < 1) return fail(W4A16_INVALID_ARG, "w4a16_packed_bytes: E=%d N=%d must be >= 1", E, N);
+    if (K < 32 || K % 32) return fail(W4A16_UNSUPPORTED_SHAPE, "w4a16_packed_bytes: K=%d must be a positive multiple of 32", K);
+    *bytes = packed_bytes(make_shape(E, N, K));
+    return ok();
+}
+
+int w4a16_pack_weights(const uint8_t* codes, const uint16_t* scales, int E, int N, int K, void* packed,
+                       size_t packed_bytes_avail, hipStream_t s, w4a16_weights** out) {
+    const char* what = "w4a16_pack_weights";
+    if (!codes || !scales || !packed || !out) return fail(W4A16_INVALID_ARG, "%s: NULL pointer argument", what);
+    size_t need = 0;
+    int rc = w4a16_packed_bytes(E, N, K, &need);
+    if (rc) return rc;
+    if (packed_bytes_avail < need)
+        return fail(W4A16_WORKSPACE_TOO_SMALL, "%s: packed buffer has %zu bytes, needs %zu", what, packed_bytes_avail, need);
+    if (!aligned16(packed)) return fail(W4A16_INVALID_ARG, "%s: packed buffer must be 16-byte aligned", what);
+    if (((uintptr_t)codes & 7u) != 0) return fail(W4A16_INVALID_ARG, "%s: codes must be 8-byte aligned", what);
+    w4a16_weights* w = new (std::nothrow) w4a16_weights;
+    if (!w) return fail(W4A16_INVALID_ARG, "%s: out of host memory", what);
+    w->magic = kHandleMagic;
+    w->layout_version = kLayoutVersion;
+    w->shape = make_shape(E, N, K);
+    w->packed = packed;
+    w->bytes = need;
+    rc = check_launch(launch_pack(codes, scales, w->shape, packed, s), what);
+    if (rc) {
+        delete w;
+        return rc;
+    }
+    *out = w;
+    return ok();
+}
+
+int w4a16_weights_rebind(const w4a16_weights* w, void* packed, w4a16_weights** out) {
+    int rc = check_handle(w, "w4a16_weights_rebind");
+    if (rc) return rc;
+    if (!packed || !out) return fail(W4A16_INVALID_ARG, "w4a16_weights_rebind: NULL pointer argument");
+    if (!aligned16(packed)) return fail(W4A16_INVALID_ARG, "w4a16_weights_rebind: packed buffer must be 16-byte aligned");
+    w4a16_weights* n = new (std::nothrow) w4a16_weights(*w);
+    if (!n) return fail(W4A16_INVALID_ARG, "w4a16_weights_rebind: out of host memory");
+    n->packed = packed;
+    *out = n;
+    return ok();
+}
+
+int w4a16_weights_info(const w4a16_weights* w, int* E, int* N, int* K, void** packed, size_t* bytes) {
+    int rc = check_handle(w, "w4a16_weights_info");
+    if (rc) return rc;
+    if (E) *E = w->shape.E;
+    if (N) *N = w->shape.N;
+    if (K) *K = w->shape.K;
+    if (packed) *packed = w->packed;
+    if (bytes) *bytes = w->bytes;
+    return ok();
+}
+
+void w4a16_weights_destroy(w4a16_weights* w) {
+    if (w && w->magic == kHandleMagic) {
+        w->magic = 0;
+        delete w;
+    }
+}
+
+int w4a16_dequant(const w4a16_weights* w, int expert, float* out_f32, uint16_t* out_bf16, hipStream_t s) {
+    const char* what = "w4a16_dequant";
+    int rc = check_handle(w, what);
+    if (rc) return rc;
+    if (expert < 0 || expert >= w->shape.E)
+        return fail(W4A16_INVALID_ARG, "%s: expert %d outside [0,%d)", what, expert, w->shape.E);
+    if (!out_f32 && !out_bf16) return fail(W4A16_INVALID_ARG, "%s: both outputs are NULL", what);
+    return check_launch(launch_dequant(w->packed, w->shape, expert, out_f32, out_bf16, s), what);
+}
+
+int w4a16_route_bounds(int T, int k, int E, int block_m, int* max_padded, int* max_blocks) {
+    if (!max_padded || !max_blocks) return fail(W4A16_INVALID_ARG, "w4a16_route_bounds: NULL output");
+    if (T < 0 || k < 1 || E < 1) return fail(W4A16_INVALID_ARG, "w4a16_route_bounds: T=%d k=%d E=%d", T, k, E);
+    if (block_m < 16 || block_m % 16)
+        return fail(W4A16_UNSUPPORTED_SHAPE, "w4a16_route_bounds: block_m %d must be a positive multiple of 16", block_m);
+    if ((long)T * k > (1L << 30)) return fail(W4A16_UNSUPPORTED_SHAPE, "w4a16_route_bounds: T*k too large");
+    route_bounds(T, k, E, block_m, max_padded, max_blocks);
+    return ok();
+}
+
+int w4a16_route_prep(const int32_t* topk_ids, int T, int k, int E, int block_m, int32_t* sorted_ids,
+                     int32_t* expert_ids, int32_t* num_tokens_padded, int32_t* expert_offsets, int32_t* counts,
+                     hipStream_t s) {
+    const char* what = "w4a16_route_prep";
+    int maxP, maxB;
+    int rc = w4a16_route_bounds(T, k, E, block_m, &maxP, &maxB);
+    if (rc) return rc;
+    if (E > W4A16_MAX_EXPERTS) return fail(W4A16_UNSUPPORTED_SHAPE, "%s: E=%d exceeds %d", what, E, W4A16_MAX_EXPERTS);
+    if ((T > 0 && !topk_ids) || (maxP > 0 && !sorted_ids) || (maxB > 0 && !expert_ids) || !num_tokens_padded ||
+        !expert_offsets || !counts)
+        return fail(W4A16_INVALID_ARG, "%s: NULL pointer argument", what);
+    return check_launch(launch_route_prep(topk_ids, T * k, E, block_m, maxP, maxB, sorted_ids, expert_ids,
+                                          num_tokens_padded, expert_offsets, counts, s),
+                        what);
+}
+
+int w4a16_plan_select(int T, int k, int E, int N, int K, float expected_rows_per_expert, w4a16_plan* out) {
+    if (!out) return fail(W4A16_INVALID_ARG, "w4a16_plan_select: out is NULL");
+    if (T < 0 || k < 1 || E < 1 || N < 1 || K < 32 || K % 32)
+        return fail(W4A16_INVALID_ARG, "w4a16_plan_select: bad shape T=%d k=%d E=%d N=%d K=%d", T, k, E, N, K);
+    const float rows = expected_rows_per_expert > 0 ? expected_rows_per_expert : (float)T * k / (float)E;
+    typedef std::tuple<int, int, int, int, int, float> Key;
+    static std::mutex mu;
+    static std::map<Key, w4a16_plan> memo;
+    const Key key(T, k, E, N, K, rows);
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        auto it = memo.find(key);
+        if (it != memo.end()) {
+            *out = it->second;
+            return ok();
+        }
+    }
+    w4a16_plan p = select_plan(T, k, E, N, K, rows);
+    int rc = validate_plan(&p, "w4a16_plan_select (after environment overrides)");
+    if (rc) return rc;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        if (memo.size() > 4096) memo.clear();
+        memo[key] = p;
+    }
+    *out = p;
+    return ok();
+}
+
+int w4a16_gemm_workspace_bytes(const w4a16_plan* p, int R, int N, size_t* bytes) {
+    int rc = validate_plan(p, "w4a16_gemm_workspace_bytes");
+    if (rc) return rc;
+    if (!bytes) return fail(W4A16_INVALID_ARG, "w4a16_gemm_workspace_bytes: bytes is NULL");
+    (void)R; (void)N;
+    *bytes = 0;
+    return ok();
+}
+
+static int grouped_gemm_impl(const char* what, const uint16_t* A, int a_row_div, const w4a16_weights* w,
+                             const int32_t* sorted_ids, const int32_t* expert_ids, int R, const w4a16_plan* p,
+                             void* out, int out_f32, hipStream_t s) {
+    int rc = check_handle(w, what);
+    if (rc) return rc;
+    rc = validate_plan(p, what);
+    if (rc) return rc;
+    if (R < 0 || a_row_div < 1) return fail(W4A16_INVALID_ARG, "%s: R=%d a_row_div=%d", what, R, a_row_div);
+    if (R == 0) return ok();
+    if (R % a_row_div) return fail(W4A16_INVALID_ARG, "%s: R=%d not a multiple of a_row_div=%d", what, R, a_row_div);
+    if (!A || !sorted_ids || !expert_ids || !out) return fail(W4A16_INVALID_ARG, "%s: NULL pointer argument", what);
+    if (!aligned16(A)) return fail(W4A16_INVALID_ARG, "%s: A must be 16-byte aligned", what);
+    int maxP, maxB;
+    route_bounds(R / a_row_div, a_row_div, w->shape.E, p->block_m, &maxP, &maxB);
+    GemmArgs a{A, a_row_div, w->packed, w->shape, sorted_ids, expert_ids, R, maxB, out, out_f32};
+    return check_launch(run_gemm(a, *p, s), what);
+}
+
+int w4a16_grouped_gemm(const uint16_t* A, int a_row_div, const w4a16_weights* w, const int32_t* sorted_ids,
+                       const int32_t* expert_ids, const int32_t* num_tokens_padded, int R, const w4a16_plan* p,
+                       uint16_t* out, void* ws, size_t ws_bytes, hipStream_t s) {
+    (void)ws; (void)ws_bytes; (void)num_tokens_padded;
+    return grouped_gemm_impl("w4a16_grouped_gemm", A, a_row_div, w, sorted_ids, expert_ids, R, p, out, 0, s);
+}
+
+int w4a16_grouped_gemm_f32(const uint16_t* A, int a_row_div, const w4a16_weights* w, const int32_t* sorted_ids,
+                           const int32_t* expert_ids, const int32_t* num_tokens_padded, int R, const w4a16_plan* p,
+                           float* out, void* ws, size_t ws_bytes, hipStream_t s) {
+    (void)ws; (void)ws_bytes; (void)num_tokens_padded;
+    return grouped_gemm_impl("w4a16_grouped_gemm_f32", A, a_row_div, w, sorted_ids, expert_ids, R, p, out, 1, s);
+}
+
+int w4a16_offsets_workspace_bytes(int rows_max, int E, const w4a16_plan* p, size_t* bytes) {
+    int rc = validate_plan(p, "w4a16_offsets_workspace_bytes");
+    if (rc) return rc;
+    if (!bytes || rows_max < 0 || E < 1) return fail(W4A16_INVALID_ARG, "w4a16_offsets_workspace_bytes: bad argument");
+    int maxP, maxB;
+    route_bounds(rows_max, 1, E, p->block_m, &maxP, &maxB);
+    *bytes = align_up(sizeof(int32_t) * (size_t)maxP, 256) + align_up(sizeof(int32_t) * (size_t)maxB, 256);
+    return ok();
+}
+
+int w4a16_grouped_gemm_offsets(const uint16_t* A_sorted, const int32_t* expert_offsets, int rows_max,
+                               const w4a16_weights* w, const w4a16_plan* p, uint16_t* out, void* ws,
+                               size_t ws_bytes, hipStream_t s) {
+    const char* what = "w4a16_grouped_gemm_offsets";
+    int rc = check_handle(w, what);
+    if (rc) return rc;
+    rc = validate_plan(p, what);
+    if (rc) return rc;
+    if (rows_max < 0) return fail(W4A16_INVALID_ARG, "%s: rows_max=%d", what, rows_max);
+    if (w->shape.E > W4A16_MAX_EXPERTS) return fail(W4A16_UNSUPPORTED_SHAPE, "%s: too many experts", what);
+    if (rows_max == 0) return ok();
+    size_t need = 0;
+    w4a16_offsets_workspace_bytes(rows_max, w->shape.E, p, &need);
+    if (!ws || ws_bytes < need)
+        return fail(W4A16_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, needs %zu", what, ws_bytes, need);
+    if (!A_sorted || !expert_offsets || !out) return fail(W4A16_INVALID_ARG, "%s: NULL pointer argument", what);
+    if (!aligned16(A_sorted)) return fail(W4A16_INVALID_ARG, "%s: A_sorted must be 16-byte aligned", what);
+    int maxP, maxB;
+    route_bounds(rows_max, 1, w->shape.E, p->block_m, &maxP, &maxB);
+    int32_t* sorted_ids = static_cast<int32_t*>(ws);
+    int32_t* expert_ids = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + align_up(sizeof(int32_t) * (size_t)maxP, 256));
+    rc = check_launch(launch_offsets_to_route(expert_offsets, w->shape.E, rows_max, p->block_m, maxP, maxB, sorted_ids,
+                                              expert_ids, s),
+                      what);
+    if (rc) return rc;
+    GemmArgs a{A_sorted, 1, w->packed, w->shape, sorted_ids, expert_ids, rows_max, maxB, out, 0};
+    return check_launch(run_gemm(a, *p, s), what);
+}
+
+int w4a16_silu_mul(const uint16_t* gu, int rows, int I, uint16_t* h, hipStream_t s) {
+    if (rows < 0 || I < 2 || I % 2) return fail(W4A16_INVALID_ARG, "w4a16_silu_mul: rows=%d I=%d (I must be even)", rows, I);
+    if (rows == 0) return ok();
+    if (!gu || !h) return fail(W4A16_INVALID_ARG, "w4a16_silu_mul: NULL pointer argument");
+    if (((uintptr_t)gu & 3u) || ((uintptr_t)h & 3u)) return fail(W4A16_INVALID_ARG, "w4a16_silu_mul: buffers must be 4-byte aligned");
+    return check_launch(launch_silu_mul(gu, rows, I, h, s), "w4a16_silu_mul");
+}
+
+int w4a16_silu_mul_f32(const float* gu, int rows, int I, uint16_t* h, hipStream_t s) {
+    if (rows < 0 || I < 2 || I % 2) return fail(W4A16_INVALID_ARG, "w4a16_silu_mul_f32: rows=%d I=%d (I must be even)", rows, I);
+    if (rows == 0) return ok();
+    if (!gu || !h) return fail(W4A16_INVALID_ARG, "w4a16_silu_mul_f32: NULL pointer argument");
+    if (((uintptr_t)gu & 7u) || ((uintptr_t)h & 3u)) return fail(W4A16_INVALID_ARG, "w4a16_silu_mul_f32: misaligned buffer");
+    return check_launch(launch_silu_mul_f32(gu, rows, I, h, s), "w4a16_silu_mul_f32");
+}
+
+int w4a16_moe_combine(const float* y, const float* topk_w, const int32_t* topk_ids, int T, int k, int E, int H,
+                      uint16_t* out, hipStream_t s) {
+    if (T < 0 || k < 1 || E < 1 || H < 2 || H % 2)
+        return fail(W4A16_INVALID_ARG, "w4a16_moe_combine: T=%d k=%d E=%d H=%d (H must be even)", T, k, E, H);
+    if (T == 0) return ok();
+    if (!y || !topk_w || !topk_ids || !out) return fail(W4A16_INVALID_ARG, "w4a16_moe_combine: NULL pointer argument");
+    if (((uintptr_t)y & 7u) || ((uintptr_t)out & 3u)) return fail(W4A16_INVALID_ARG, "w4a16_moe_combine: misaligned buffer");
+    return check_launch(launch_combine(y, topk_w, topk_ids, T, k, E, H, out, s), "w4a16_moe_combine");
+}
+
+int w4a16_fused_moe_workspace_bytes(int T, int k, const w4a16_weights* w13, const w4a16_weights* w2, size_t* bytes) {
+    const char* what = "w4a16_fused_moe_workspace_bytes";
+    int rc = check_handle(w13, what);
+    if (rc) return rc;
+    rc = check_handle(w2, what);
+    if (rc) return rc;
+    if (!bytes || T < 0 || k < 1) return fail(W4A16_INVALID_ARG, "%s: bad argument", what);
+    const int E = w13->shape.E, H = w13->shape.K, I = w2->shape.K;
+    // the route block is the same for both projections; size for every block the planner may choose
+    static const int kBlocks[] = {16, 32, 48, 64, 128};
+    size_t need = 0;
+    for (int bm : kBlocks) {
+        const size_t t = fused_layout(T, k, E, H, I, bm).total;
+        if (t > need) need = t;
+    }
+    *bytes = need;
+    return ok();
+}
+
+int w4a16_fused_moe_plans(int T, int k, const w4a16_weights* w13, const w4a16_weights* w2, w4a16_plan* gate_up,
+                          w4a16_plan* down) {
+    const char* what = "w4a16_fused_moe_plans";
+    int rc = check_handle(w13, what);
+    if (rc) return rc;
+    rc = check_handle(w2, what);
+    if (rc) return rc;
+    if (!gate_up || !down || k < 1 || T < 0) return fail(W4A16_INVALID_ARG, "%s: bad argument", what);
+    const int E = w13->shape.E, H = w13->shape.K, I = w2->shape.K;
+    w4a16_plan p13, p2;
+    rc = w4a16_plan_select(T, k, E, 2 * I, H, 0.f, &p13);
+    if (rc) return rc;
+    rc = w4a16_plan_select(T, k, E, H, I, 0.f, &p2);
+    if (rc) return rc;
+    p2.block_m = p13.block_m;  // both projections share one set of routing tensors
+    p2.kernel = p13.kernel;
+    if (p2.kernel == W4A16_KERNEL_PREFILL) {
+        if (p2.n_blocks != 2 && p2.n_blocks != 4) p2.n_blocks = 4;
+    } else {
+        while (p2.waves > 1 && sizeof(float) * (size_t)p2.waves * p2.block_m * (p2.n_blocks * 16 + 1) > 65536) --p2.waves;
+    }
+    rc = validate_plan(&p2, what);
+    if (rc) return rc;
+    *gate_up = p13;
+    *down = p2;
+    return ok();
+}
+
+int w4a16_fused_moe(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, int T, int k,
+                    const w4a16_weights* w13, const w4a16_weights* w2, uint16_t* out, void* ws, size_t ws_bytes,
+                    hipStream_t s) {
+    return w4a16_fused_moe_profiled(x, topk_ids, topk_w, T, k, w13, w2, out, ws, ws_bytes, s, nullptr);
+}
+
+int w4a16_fused_moe_profiled(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, int T, int k,
+                             const w4a16_weights* w13, const w4a16_weights* w2, uint16_t* out, void* ws,
+                             size_t ws_bytes, hipStream_t s, hipEvent_t* ev) {
+    const char* what = "w4a16_fused_moe";
+    int rc = check_handle(w13, what);
+    if (rc) return rc;
+    rc = check_handle(w2, what);
+    if (rc) return rc;
+    if (T < 0 || k < 1) return fail(W4A16_INVALID_ARG, "%s: T=%d k=%d", what, T, k);
+    const int E = w13->shape.E, H = w13->shape.K, I = w2->shape.K;
+    if (w2->shape.E != E || w13->shape.N != 2 * I || w2->shape.N != H)
+        return fail(W4A16_LAYOUT_MISMATCH, "%s: w13 is [%d,%d,%d] and w2 is [%d,%d,%d]; need [E,2I,H] and [E,H,I]", what,
+                    w13->shape.E, w13->shape.N, w13->shape.K, w2->shape.E, w2->shape.N, w2->shape.K);
+    if (E > W4A16_MAX_EXPERTS) return fail(W4A16_UNSUPPORTED_SHAPE, "%s: E=%d exceeds %d", what, E, W4A16_MAX_EXPERTS);
+    if (T == 0) return ok();
+    if (!x || !topk_ids || !topk_w || !out) return fail(W4A16_INVALID_ARG, "%s: NULL pointer argument", what);
+    if (!aligned16(x) || ((uintptr_t)out & 3u)) return fail(W4A16_INVALID_ARG, "%s: x must be 16-byte aligned", what);
+    size_t need = 0;
+    rc = w4a16_fused_moe_workspace_bytes(T, k, w13, w2, &need);
+    if (rc) return rc;
+    if (!ws || ws_bytes < need) return fail(W4A16_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, needs %zu", what, ws_bytes, need);
+    if (!aligned16(ws)) return fail(W4A16_INVALID_ARG, "%s: workspace must be 16-byte aligned", what);
+
+    w4a16_plan p13, p2;
+    rc = w4a16_fused_moe_plans(T, k, w13, w2, &p13, &p2);
+    if (rc) return rc;
+
+    const FusedLayout f = fused_layout(T, k, E, H, I, p13.block_m);
+    char* base = static_cast<char*>(ws);
+    int32_t* sorted_ids = reinterpret_cast<int32_t*>(base + f.off_sorted);
+    int32_t* expert_ids = reinterpret_cast<int32_t*>(base + f.off_eids);
+    int32_t* ntp = reinterpret_cast<int32_t*>(base + f.off_ntp);
+    int32_t* offsets = reinterpret_cast<int32_t*>(base + f.off_offsets);
+    int32_t* counts = reinterpret_cast<int32_t*>(base + f.off_counts);
+    float* gu = reinterpret_cast<float*>(base + f.off_gu);
+    uint16_t* h = reinterpret_cast<uint16_t*>(base + f.off_h);
+    float* y = reinterpret_cast<float*>(base + f.off_y);
+    const int R = T * k;
+
+#define W4A16_STAGE(i)                                                                     \
+    do {                                                                                   \
+        if (ev) {                                                                          \
+            hipError_t e_ = hipEventRecord(ev[i], s);                                      \
+            if (e_ != hipSuccess)                                                          \
+                return fail(W4A16_HIP_ERROR, "%s: event record failed: %s", what, hipGetErrorString(e_)); \
+        }                                                                                  \
+    } while (0)
+    W4A16_STAGE(0);
+    rc = check_launch(launch_route_prep(topk_ids, R, E, p13.block_m, f.maxP, f.maxB, sorted_ids, expert_ids, ntp, offsets,
+                                        counts, s),
+                      "w4a16_fused_moe (route_prep)");
+    if (rc) return rc;
+    W4A16_STAGE(1);
+    GemmArgs g13{x, k, w13->packed, w13->shape, sorted_ids, expert_ids, R, f.maxB, gu, 1};
+    rc = check_launch(run_gemm(g13, p13, s), "w4a16_fused_moe (gate_up)");
+    if (rc) return rc;
+    W4A16_STAGE(2);
+    rc = check_launch(launch_silu_mul_f32(gu, R, I, h, s), "w4a16_fused_moe (silu_mul)");
+    if (rc) return rc;
+    W4A16_STAGE(3);
+    GemmArgs g2{h, 1, w2->packed, w2->shape, sorted_ids, expert_ids, R, f.maxB, y, 1};
+    rc = check_launch(run_gemm(g2, p2, s), "w4a16_fused_moe (down)");
+    if (rc) return rc;
+    W4A16_STAGE(4);
+    rc = check_launch(launch_combine(y, topk_w, topk_ids, T, k, E, H, out, s), "w4a16_fused_moe (combine)");
+    if (rc) return rc;
+    W4A16_STAGE(5);
+#undef W4A16_STAGE
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,79 @@
+// Register-level helpers shared by the decode and prefill GEMM kernels.
+//
+// Both kernels use v_mfma_f32_16x16x32_bf16 with the activation rows as the
+// A operand (16 rows x 32 k) and the weights as the B operand (32 k x 16
+// output columns).  Lane L holds A row L%16 and B column L%16, each with the
+// eight k of slot L/16; the 16x16 fp32 result lands as rows 4*(L/16)+r,
+// r = 0..3, of column L%16.  Which eight k a slot holds only has to agree
+// between A and B, and the packed layout fixes it as k = 8*slot + u.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Eight codes of one packed word as BF16 values 128 + q (exact).  Code u = 2p
+// sits in bits [4p, 4p+4) and u = 2p+1 in [16+4p, 20+4p), so one shift, mask
+// and OR with the BF16 pattern of 128 (0x4300) builds two operands.
+__device__ __forceinline__ bf16x8 biased_codes(uint32_t w) {
+    u32x4 v;
+    v.x = (w & 0x000F000Fu) | 0x43004300u;
+    v.y = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
+    v.z = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
+    v.w = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// B operand with every element equal to -136 (BF16 0xC308): multiplying the
+// activation fragment by it gives -136 * (sum of the 32 activations of the
+// group) in every column, the correction that turns sum x*(128+q) into
+// sum x*(q-8).
+__device__ __forceinline__ bf16x8 minus136() {
+    u32x4 v = {0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// BF16 scale of group g (0..7) from the 16-byte scale row of a superblock.
+__device__ __forceinline__ float group_scale(u32x4 sc, int g) {
+    const uint32_t word = sc[g >> 1];
+    return __uint_as_float((g & 1) ? (word & 0xFFFF0000u) : (word << 16));
+}
+
+// Eight fully dequantised weights bf16((q - 8) * s) of one packed word.
+// (q - 8) * s is formed exactly by one fused multiply-add, q * s + (-8 s)
+// (the product needs at most 12 significant bits), then rounded once to BF16
+// with round-to-nearest-even.
+__device__ __forceinline__ bf16x8 dequant8(uint32_t w, float s, float neg8s) {
+    const uint32_t lo = w & 0x0F0F0F0Fu;         // codes 0, 4, 1, 5 in bytes 0..3
+    const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // codes 2, 6, 3, 7 in bytes 0..3
+    const float q0 = (float)(lo & 0xFFu), q4 = (float)((lo >> 8) & 0xFFu);
+    const float q1 = (float)((lo >> 16) & 0xFFu), q5 = (float)(lo >> 24);
+    const float q2 = (float)(hi & 0xFFu), q6 = (float)((hi >> 8) & 0xFFu);
+    const float q3 = (float)((hi >> 16) & 0xFFu), q7 = (float)(hi >> 24);
+    bf16x8 r;
+    r[0] = (__bf16)__builtin_fmaf(q0, s, neg8s);
+    r[1] = (__bf16)__builtin_fmaf(q1, s, neg8s);
+    r[2] = (__bf16)__builtin_fmaf(q2, s, neg8s);
+    r[3] = (__bf16)__builtin_fmaf(q3, s, neg8s);
+    r[4] = (__bf16)__builtin_fmaf(q4, s, neg8s);
+    r[5] = (__bf16)__builtin_fmaf(q5, s, neg8s);
+    r[6] = (__bf16)__builtin_fmaf(q6, s, neg8s);
+    r[7] = (__bf16)__builtin_fmaf(q7, s, neg8s);
+    return r;
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    __bf16 b = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, b);
+}
+
+}  // namespace w4a16

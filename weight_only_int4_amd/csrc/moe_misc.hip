@@ -1,0 +1,90 @@
+// Activation and weighted top-k combine of the expert MLP (humans& page,
+// "Dedicated warps keep the pipeline busy": FC1, FC2 and the top-K merge).
+#include "frag.h"
+#include "w4a16_internal.h"
+
+namespace w4a16 {
+namespace {
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// h[r,c] = bf16(silu(g) * u) with g = gu[r,c], u = gu[r,I+c]; two columns per thread.
+__global__ __launch_bounds__(256) void silu_mul_kernel(const uint16_t* __restrict__ gu, int rows, int I,
+                                                       uint16_t* __restrict__ h) {
+    const int pairs = I >> 1;
+    const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (long)rows * pairs) return;
+    const int r = (int)(idx / pairs), c = 2 * (int)(idx % pairs);
+    const uint32_t g2 = *reinterpret_cast<const uint32_t*>(gu + (size_t)r * 2 * I + c);
+    const uint32_t u2 = *reinterpret_cast<const uint32_t*>(gu + (size_t)r * 2 * I + I + c);
+    const float g0 = bf16_to_f32(g2 & 0xFFFFu), g1 = bf16_to_f32(g2 >> 16);
+    const float u0 = bf16_to_f32(u2 & 0xFFFFu), u1 = bf16_to_f32(u2 >> 16);
+    const float h0 = g0 / (1.0f + expf(-g0)) * u0;
+    const float h1 = g1 / (1.0f + expf(-g1)) * u1;
+    const uint32_t packed = (uint32_t)f32_to_bf16_bits(h0) | ((uint32_t)f32_to_bf16_bits(h1) << 16);
+    *reinterpret_cast<uint32_t*>(h + (size_t)r * I + c) = packed;
+}
+
+// Same activation from binary32 gate/up values (the fused MLP keeps the gate_up
+// accumulators unrounded): h[r,c] = bf16(silu(gu[r,c]) * gu[r,I+c]).
+__global__ __launch_bounds__(256) void silu_mul_f32_kernel(const float* __restrict__ gu, int rows, int I,
+                                                           uint16_t* __restrict__ h) {
+    const int pairs = I >> 1;
+    const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (long)rows * pairs) return;
+    const int r = (int)(idx / pairs), c = 2 * (int)(idx % pairs);
+    const float2 g = *reinterpret_cast<const float2*>(gu + (size_t)r * 2 * I + c);
+    const float2 u = *reinterpret_cast<const float2*>(gu + (size_t)r * 2 * I + I + c);
+    const float h0 = g.x / (1.0f + expf(-g.x)) * u.x;
+    const float h1 = g.y / (1.0f + expf(-g.y)) * u.y;
+    const uint32_t packed = (uint32_t)f32_to_bf16_bits(h0) | ((uint32_t)f32_to_bf16_bits(h1) << 16);
+    *reinterpret_cast<uint32_t*>(h + (size_t)r * I + c) = packed;
+}
+
+// out[t,n] = bf16(sum_{valid j ascending} tw[t,j] * y[t*k+j, n]); two columns per thread.
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const float* __restrict__ tw,
+                                                      const int32_t* __restrict__ ids, int T, int k, int E, int H,
+                                                      uint16_t* __restrict__ out) {
+    const int pairs = H >> 1;
+    const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (long)T * pairs) return;
+    const int t = (int)(idx / pairs), n = 2 * (int)(idx % pairs);
+    float a0 = 0.f, a1 = 0.f;
+    for (int jj = 0; jj < k; ++jj) {
+        const int e = ids[(size_t)t * k + jj];
+        if (e < 0 || e >= E) continue;
+        const float wt = tw[(size_t)t * k + jj];
+        const float2 v = *reinterpret_cast<const float2*>(y + ((size_t)t * k + jj) * H + n);
+        a0 = a0 + wt * v.x;
+        a1 = a1 + wt * v.y;
+    }
+    const uint32_t packed = (uint32_t)f32_to_bf16_bits(a0) | ((uint32_t)f32_to_bf16_bits(a1) << 16);
+    *reinterpret_cast<uint32_t*>(out + (size_t)t * H + n) = packed;
+}
+
+}  // namespace
+
+hipError_t launch_silu_mul(const uint16_t* gu, int rows, int I, uint16_t* h, hipStream_t s) {
+    const long work = (long)rows * (I / 2);
+    if (work == 0) return hipSuccess;
+    hipLaunchKernelGGL(silu_mul_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, gu, rows, I, h);
+    return hipGetLastError();
+}
+
+hipError_t launch_silu_mul_f32(const float* gu, int rows, int I, uint16_t* h, hipStream_t s) {
+    const long work = (long)rows * (I / 2);
+    if (work == 0) return hipSuccess;
+    hipLaunchKernelGGL(silu_mul_f32_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, gu, rows, I, h);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const float* y, const float* tw, const int32_t* ids, int T, int k, int E, int H,
+                          uint16_t* out, hipStream_t s) {
+    const long work = (long)T * (H / 2);
+    if (work == 0) return hipSuccess;
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, y, tw, ids, T, k, E, H,
+                       out);
+    return hipGetLastError();
+}
+
+}  // namespace w4a16

@@ -1,0 +1,214 @@
+// Routing preparation: stable counting sort of valid routes by expert.
+//
+// Produces the indexed routing tensors (Chord page, "Two kernel families" and
+// Figure 3: activations stay unpadded, padding lives in the index tensors as
+// sentinels) and per-expert offsets (nf4 page, "Usage").  Everything runs in
+// one workgroup with no host readback, so the routed count never leaves the
+// device (Chord page, "vLLM integration").
+//
+// Order inside an expert is ascending route index: each chunk of 1024 routes
+// is ranked by (earlier chunks) + (earlier wavefronts of this chunk) + (lower
+// lanes of this wavefront with the same expert).  The last term comes from a
+// lane-match mask built from one ballot per bit of the expert id.
+#include "w4a16_internal.h"
+
+namespace w4a16 {
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Exclusive scan of one int per thread across the workgroup; returns the
+// thread's exclusive prefix and writes the total to *total (all threads).
+__device__ int block_exclusive_scan(int v, int* wave_tot, int* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) wave_tot[wave] = incl;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int w = 0; w < kWaves; ++w) {
+            const int t = wave_tot[w];
+            wave_tot[w] = run;
+            run += t;
+        }
+        wave_tot[kWaves] = run;
+    }
+    __syncthreads();
+    const int excl = wave_tot[wave] + incl - v;
+    *total = wave_tot[kWaves];
+    __syncthreads();
+    return excl;
+}
+
+// Shared memory layout (ints): cnt[E] | pad_off[E+1] | base[E] | wave_cnt[kWaves][E] | wave_tot[kWaves+1]
+__global__ __launch_bounds__(kThreads) void route_prep_kernel(const int32_t* __restrict__ ids, int R, int E, int BM,
+                                                              int max_padded, int max_blocks,
+                                                              int32_t* __restrict__ sorted_ids,
+                                                              int32_t* __restrict__ expert_ids,
+                                                              int32_t* __restrict__ ntp_out,
+                                                              int32_t* __restrict__ offsets_out,
+                                                              int32_t* __restrict__ counts_out) {
+    extern __shared__ int smem[];
+    int* cnt = smem;
+    int* pad_off = cnt + E;
+    int* base = pad_off + E + 1;
+    int* wave_cnt = base + E;
+    int* wave_tot = wave_cnt + kWaves * E;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    for (int e = tid; e < E; e += kThreads) cnt[e] = 0;
+    for (int x = tid; x < kWaves * E; x += kThreads) wave_cnt[x] = 0;
+    __syncthreads();
+    for (int i = tid; i < R; i += kThreads) {
+        const int e = ids[i];
+        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+
+    // scans of counts (unpadded offsets) and padded sizes, E <= kThreads
+    const int c = tid < E ? cnt[tid] : 0;
+    const int padded = tid < E ? ceil_div(c, BM) * BM : 0;
+    int tot_c, tot_p;
+    const int off_c = block_exclusive_scan(c, wave_tot, &tot_c);
+    const int off_p = block_exclusive_scan(padded, wave_tot, &tot_p);
+    if (tid < E) {
+        counts_out[tid] = c;
+        offsets_out[tid] = off_c;
+        pad_off[tid] = off_p;
+        base[tid] = off_p;
+    }
+    if (tid == 0) {
+        offsets_out[E] = tot_c;
+        pad_off[E] = tot_p;
+        *ntp_out = tot_p;
+    }
+    __syncthreads();
+
+    // every slot starts as the sentinel; the scatter below overwrites valid ones
+    for (int p = tid; p < max_padded; p += kThreads) sorted_ids[p] = R;
+    for (int b = tid; b < max_blocks; b += kThreads) {
+        const int p = b * BM;
+        int owner = -1;
+        if (p < tot_p) {
+            int lo = 0, hi = E - 1;  // last e with pad_off[e] <= p
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (pad_off[mid] <= p) lo = mid; else hi = mid - 1;
+            }
+            owner = lo;
+        }
+        expert_ids[b] = owner;
+    }
+    int nbits = 1;
+    while ((1 << nbits) < E) ++nbits;
+    __syncthreads();  // sentinel stores complete before any scatter store
+
+    for (int chunk = 0; chunk < R; chunk += kThreads) {
+        const int i = chunk + tid;
+        const int e = i < R ? ids[i] : -1;
+        const bool valid = e >= 0 && e < E;
+        uint64_t match = __ballot(valid);
+        for (int bit = 0; bit < nbits; ++bit) {
+            const uint64_t ones = __ballot(valid && ((e >> bit) & 1));
+            match &= ((e >> bit) & 1) ? ones : ~ones;
+        }
+        const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        const int rank_w = __popcll(match & lower);
+        const bool leader = valid && rank_w == 0;
+        if (leader) wave_cnt[wave * E + e] = __popcll(match);
+        __syncthreads();
+        if (valid) {
+            int prior = base[e];
+            for (int w = 0; w < wave; ++w) prior += wave_cnt[w * E + e];
+            sorted_ids[prior + rank_w] = i;
+        }
+        __syncthreads();
+        if (leader) {
+            atomicAdd(&base[e], wave_cnt[wave * E + e]);
+            wave_cnt[wave * E + e] = 0;
+        }
+        __syncthreads();
+    }
+}
+
+// Offsets form -> indexed form: rows [off[e], off[e+1]) of expert e become
+// slots of e's padded segment; the sentinel is rows_max.
+__global__ __launch_bounds__(kThreads) void offsets_to_route_kernel(const int32_t* __restrict__ off, int E,
+                                                                    int rows_max, int BM, int max_padded,
+                                                                    int max_blocks, int32_t* __restrict__ sorted_ids,
+                                                                    int32_t* __restrict__ expert_ids) {
+    extern __shared__ int smem[];
+    int* pad_off = smem;            // E+1
+    int* wave_tot = pad_off + E + 1;  // kWaves+1
+    const int tid = threadIdx.x;
+    int c = 0;
+    if (tid < E) {
+        c = off[tid + 1] - off[tid];
+        if (c < 0) c = 0;
+    }
+    const int padded = ceil_div(c, BM) * BM;
+    int tot_p;
+    const int off_p = block_exclusive_scan(padded, wave_tot, &tot_p);
+    if (tid < E) pad_off[tid] = off_p;
+    if (tid == 0) pad_off[E] = tot_p;
+    __syncthreads();
+    for (int p = tid; p < max_padded; p += kThreads) {
+        int v = rows_max;
+        if (p < tot_p) {
+            int lo = 0, hi = E - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (pad_off[mid] <= p) lo = mid; else hi = mid - 1;
+            }
+            const int r = p - pad_off[lo];
+            const int row = off[lo] + r;
+            if (r < off[lo + 1] - off[lo] && row >= 0 && row < rows_max) v = row;
+        }
+        sorted_ids[p] = v;
+    }
+    for (int b = tid; b < max_blocks; b += kThreads) {
+        const int p = b * BM;
+        int owner = -1;
+        if (p < tot_p) {
+            int lo = 0, hi = E - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (pad_off[mid] <= p) lo = mid; else hi = mid - 1;
+            }
+            owner = lo;
+        }
+        expert_ids[b] = owner;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_route_prep(const int32_t* topk_ids, int R, int E, int block_m, int max_padded, int max_blocks,
+                             int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntp, int32_t* offsets,
+                             int32_t* counts, hipStream_t s) {
+    const size_t shmem = sizeof(int) * ((size_t)E + (E + 1) + E + (size_t)kWaves * E + (kWaves + 1));
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(route_prep_kernel),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (shmem > 65536 && attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(route_prep_kernel, dim3(1), dim3(kThreads), shmem, s, topk_ids, R, E, block_m, max_padded,
+                       max_blocks, sorted_ids, expert_ids, ntp, offsets, counts);
+    return hipGetLastError();
+}
+
+hipError_t launch_offsets_to_route(const int32_t* offsets, int E, int rows_max, int block_m, int max_padded,
+                                   int max_blocks, int32_t* sorted_ids, int32_t* expert_ids, hipStream_t s) {
+    const size_t shmem = sizeof(int) * ((size_t)E + 1 + kWaves + 1);
+    hipLaunchKernelGGL(offsets_to_route_kernel, dim3(1), dim3(kThreads), shmem, s, offsets, E, rows_max, block_m,
+                       max_padded, max_blocks, sorted_ids, expert_ids);
+    return hipGetLastError();
+}
+
+}  // namespace w4a16

@@ -1,0 +1,110 @@
+// Internal declarations of libw4a16 (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/w4a16.h"
+
+namespace w4a16 {
+
+// ---------------------------------------------------------------------------
+// Packed weight layout (version 1).
+//
+// The packed image of one weight set is a sequence of "superblocks", each
+// covering 16 output rows (an n-block) and 256 consecutive k (8 scale groups)
+// of one expert, stored at
+//     ((e * NB + nb) * KB + kb) * SB_BYTES
+// with NB = ceil(N/16) and KB = ceil(K/256).  One superblock is 2304 bytes:
+//
+//   bytes [0, 2048): codes, two halves h = 0, 1 of 1024 bytes.  In half h,
+//     the 16 bytes at (c*16 + j)*16 hold four 32-bit words d = 0..3 for
+//     output row n = 16*nb + j and scale group g = 4*h + d; word d carries
+//     the eight codes of k = 256*kb + 32*g + 8*c + u, u = 0..7, code u = 2p
+//     in bits [4p, 4p+4) and code u = 2p+1 in bits [16+4p, 20+4p).
+//   bytes [2048, 2304): scales, 16 bytes per row j: BF16 scale of groups
+//     g = 0..7 of row 16*nb + j.
+//
+// Rows n >= N carry code 8 and scale 0 (weight 0); groups past K carry code 8
+// and scale 0 and are never read by the GEMM kernels.
+//
+// Why this order: one wavefront of 64 lanes loading 16 contiguous bytes per
+// lane reads exactly one half (1024 bytes, fully coalesced), and lane
+// L = c*16 + j then holds, for each of four groups, the eight codes that the
+// 16x16x32 BF16 MFMA expects in its B operand for column j and k-slot c.  The
+// scales of a row ride in the same superblock, so the whole weight stream is
+// a single sequential read per (expert, n-block).  Decode and prefill kernels
+// read the same image.
+// ---------------------------------------------------------------------------
+constexpr int kLayoutVersion = 1;
+constexpr int NB_ROWS = 16;     // output rows per n-block
+constexpr int SB_K = 256;       // k per superblock
+constexpr int SB_GROUPS = 8;    // scale groups per superblock
+constexpr int SB_CODE_BYTES = 2048;
+constexpr int SB_SCALE_BYTES = 256;
+constexpr int SB_BYTES = SB_CODE_BYTES + SB_SCALE_BYTES;
+constexpr uint32_t kHandleMagic = 0x34413136u;  // "41A6"
+
+struct Shape {
+    int E, N, K;
+    int NB, KB, G;  // n-blocks, superblocks along K, scale groups (K/32)
+};
+
+inline Shape make_shape(int E, int N, int K) {
+    Shape s;
+    s.E = E; s.N = N; s.K = K;
+    s.NB = (N + NB_ROWS - 1) / NB_ROWS;
+    s.KB = (K + SB_K - 1) / SB_K;
+    s.G = K / 32;
+    return s;
+}
+
+inline size_t packed_bytes(const Shape& s) {
+    return (size_t)s.E * s.NB * s.KB * SB_BYTES;
+}
+
+}  // namespace w4a16
+
+// Host handle (opaque to callers).
+struct w4a16_weights {
+    uint32_t magic;
+    uint32_t layout_version;
+    w4a16::Shape shape;
+    void* packed;
+    size_t bytes;
+};
+
+namespace w4a16 {
+
+// Launchers (return hipError_t of the launch).
+hipError_t launch_pack(const uint8_t* codes, const uint16_t* scales, const Shape& sh, void* packed, hipStream_t s);
+hipError_t launch_dequant(const void* packed, const Shape& sh, int expert, float* out_f32, uint16_t* out_bf16,
+                          hipStream_t s);
+hipError_t launch_route_prep(const int32_t* topk_ids, int R, int E, int block_m, int max_padded, int max_blocks,
+                             int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntp, int32_t* offsets,
+                             int32_t* counts, hipStream_t s);
+hipError_t launch_offsets_to_route(const int32_t* offsets, int E, int rows_max, int block_m, int max_padded,
+                                   int max_blocks, int32_t* sorted_ids, int32_t* expert_ids, hipStream_t s);
+
+struct GemmArgs {
+    const uint16_t* A;
+    int a_row_div;
+    const void* packed;
+    Shape sh;
+    const int32_t* sorted_ids;
+    const int32_t* expert_ids;
+    int R;             // sentinel value / number of routes
+    int max_blocks;    // route blocks (grid.x)
+    void* out;         // BF16 bits [R,N] or float [R,N]
+    int out_f32;
+};
+
+hipError_t launch_gemm_decode(const GemmArgs& a, const w4a16_plan& p, hipStream_t s);
+hipError_t launch_gemm_prefill(const GemmArgs& a, const w4a16_plan& p, hipStream_t s);
+hipError_t launch_silu_mul(const uint16_t* gu, int rows, int I, uint16_t* h, hipStream_t s);
+hipError_t launch_silu_mul_f32(const float* gu, int rows, int I, uint16_t* h, hipStream_t s);
+hipError_t launch_combine(const float* y, const float* tw, const int32_t* ids, int T, int k, int E, int H,
+                          uint16_t* out, hipStream_t s);
+
+}  // namespace w4a16

@@ -1,0 +1,308 @@
+"""Thin Python binding of libw4a16 (ctypes).
+
+Argument marshalling only: every computation runs in the library's HIP
+kernels.  Tensors are torch tensors on the GPU; their device pointers and the
+current HIP stream are handed to the C ABI declared in ``include/w4a16.h``.
+There is no fallback: if the library is missing or a call fails, an exception
+is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw4a16.so")
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SZ = ctypes.c_size_t
+
+KERNEL_DECODE = 1
+KERNEL_PREFILL = 2
+
+
+class W4A16Error(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__("w4a16 error %d: %s" % (code, message))
+        self.code = code
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("block_m", ctypes.c_int32), ("n_blocks", ctypes.c_int32),
+                ("waves", ctypes.c_int32), ("reserved", ctypes.c_int32 * 4)]
+
+    def __repr__(self):
+        kind = {KERNEL_DECODE: "decode", KERNEL_PREFILL: "prefill"}.get(self.kernel, str(self.kernel))
+        return "Plan(%s, block_m=%d, n_blocks=%d, waves=%d)" % (kind, self.block_m, self.n_blocks, self.waves)
+
+
+# name -> (restype, argtypes)
+_SIGS = {
+    "w4a16_last_error": (ctypes.c_char_p, []),
+    "w4a16_version": (ctypes.c_char_p, []),
+    "w4a16_packed_bytes": (_I, [_I, _I, _I, ctypes.POINTER(_SZ)]),
+    "w4a16_pack_weights": (_I, [_P, _P, _I, _I, _I, _P, _SZ, _P, ctypes.POINTER(_P)]),
+    "w4a16_weights_rebind": (_I, [_P, _P, ctypes.POINTER(_P)]),
+    "w4a16_weights_info": (_I, [_P, ctypes.POINTER(_I), ctypes.POINTER(_I), ctypes.POINTER(_I),
+                                ctypes.POINTER(_P), ctypes.POINTER(_SZ)]),
+    "w4a16_weights_destroy": (None, [_P]),
+    "w4a16_dequant": (_I, [_P, _I, _P, _P, _P]),
+    "w4a16_route_bounds": (_I, [_I, _I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
+    "w4a16_route_prep": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
+    "w4a16_plan_select": (_I, [_I, _I, _I, _I, _I, ctypes.c_float, ctypes.POINTER(Plan)]),
+    "w4a16_gemm_workspace_bytes": (_I, [ctypes.POINTER(Plan), _I, _I, ctypes.POINTER(_SZ)]),
+    "w4a16_grouped_gemm": (_I, [_P, _I, _P, _P, _P, _P, _I, ctypes.POINTER(Plan), _P, _P, _SZ, _P]),
+    "w4a16_grouped_gemm_f32": (_I, [_P, _I, _P, _P, _P, _P, _I, ctypes.POINTER(Plan), _P, _P, _SZ, _P]),
+    "w4a16_silu_mul_f32": (_I, [_P, _I, _I, _P, _P]),
+    "w4a16_fused_moe_plans": (_I, [_I, _I, _P, _P, ctypes.POINTER(Plan), ctypes.POINTER(Plan)]),
+    "w4a16_offsets_workspace_bytes": (_I, [_I, _I, ctypes.POINTER(Plan), ctypes.POINTER(_SZ)]),
+    "w4a16_grouped_gemm_offsets": (_I, [_P, _P, _I, _P, ctypes.POINTER(Plan), _P, _P, _SZ, _P]),
+    "w4a16_silu_mul": (_I, [_P, _I, _I, _P, _P]),
+    "w4a16_moe_combine": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P]),
+    "w4a16_fused_moe_workspace_bytes": (_I, [_I, _I, _P, _P, ctypes.POINTER(_SZ)]),
+    "w4a16_fused_moe": (_I, [_P, _P, _P, _I, _I, _P, _P, _P, _P, _SZ, _P]),
+    "w4a16_fused_moe_profiled": (_I, [_P, _P, _P, _I, _I, _P, _P, _P, _P, _SZ, _P, _P]),
+}
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libw4a16.so (built in-tree by ``weight_only_int4_amd.build``); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise ImportError("libw4a16.so is not built (%s); run weight_only_int4_amd.build.build()" % path)
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise W4A16Error(rc, load().w4a16_last_error().decode())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def version() -> str:
+    return load().w4a16_version().decode()
+
+
+def symbol_names():
+    return list(_SIGS)
+
+
+# ---------------------------------------------------------------- weights
+
+def packed_bytes(E: int, N: int, K: int) -> int:
+    out = _SZ(0)
+    _check(load().w4a16_packed_bytes(E, N, K, ctypes.byref(out)))
+    return out.value
+
+
+class Weights:
+    """A packed weight set: device buffer plus the library's host handle."""
+
+    def __init__(self, handle: int, packed: torch.Tensor, E: int, N: int, K: int):
+        self.handle = ctypes.c_void_p(handle)
+        self.packed = packed
+        self.E, self.N, self.K = E, N, K
+
+    def rebind(self, packed: torch.Tensor) -> "Weights":
+        """Handle for another buffer holding a byte-identical copy of this packed image."""
+        h = ctypes.c_void_p()
+        _check(load().w4a16_weights_rebind(self.handle, _ptr(packed), ctypes.byref(h)))
+        return Weights(h.value, packed, self.E, self.N, self.K)
+
+    def info(self):
+        E, N, K = _I(), _I(), _I()
+        p, b = _P(), _SZ()
+        _check(load().w4a16_weights_info(self.handle, ctypes.byref(E), ctypes.byref(N), ctypes.byref(K),
+                                         ctypes.byref(p), ctypes.byref(b)))
+        return E.value, N.value, K.value, p.value, b.value
+
+    def __del__(self):
+        if _lib is not None and self.handle:
+            _lib.w4a16_weights_destroy(self.handle)
+            self.handle = None
+
+
+def pack_weights(codes: torch.Tensor, scales: torch.Tensor, packed: torch.Tensor | None = None,
+                 stream=None) -> Weights:
+    """codes uint8 [E,N,K] (low nibble), scales bf16 [E,N,K/32] -> Weights (packed on the GPU)."""
+    E, N, K = codes.shape
+    nbytes = packed_bytes(E, N, K)
+    if packed is None:
+        packed = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
+    h = ctypes.c_void_p()
+    _check(load().w4a16_pack_weights(_ptr(codes), _ptr(scales), E, N, K, _ptr(packed), packed.numel(),
+                                     _stream(stream), ctypes.byref(h)))
+    return Weights(h.value, packed, E, N, K)
+
+
+def dequant(w: Weights, expert: int, want_f32: bool = True, want_bf16: bool = True, stream=None):
+    dev = w.packed.device
+    f = torch.empty((w.N, w.K), dtype=torch.float32, device=dev) if want_f32 else None
+    b = torch.empty((w.N, w.K), dtype=torch.bfloat16, device=dev) if want_bf16 else None
+    _check(load().w4a16_dequant(w.handle, expert, _ptr(f), _ptr(b), _stream(stream)))
+    return f, b
+
+
+# ---------------------------------------------------------------- routing
+
+def route_bounds(T: int, k: int, E: int, block_m: int):
+    mp, mb = _I(), _I()
+    _check(load().w4a16_route_bounds(T, k, E, block_m, ctypes.byref(mp), ctypes.byref(mb)))
+    return mp.value, mb.value
+
+
+def route_prep(topk_ids: torch.Tensor, E: int, block_m: int, stream=None) -> dict:
+    """topk_ids int32 [T,k] on the GPU -> routing tensors (all on the GPU)."""
+    T, k = topk_ids.shape
+    maxP, maxB = route_bounds(T, k, E, block_m)
+    dev = topk_ids.device
+    out = dict(sorted_ids=torch.empty(max(maxP, 1), dtype=torch.int32, device=dev)[:maxP],
+               expert_ids=torch.empty(max(maxB, 1), dtype=torch.int32, device=dev)[:maxB],
+               num_tokens_padded=torch.empty(1, dtype=torch.int32, device=dev),
+               expert_offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+               counts=torch.empty(E, dtype=torch.int32, device=dev), block_m=block_m, R=T * k, E=E)
+    route_prep_into(topk_ids, E, block_m, out, stream)
+    return out
+
+
+def route_prep_into(topk_ids: torch.Tensor, E: int, block_m: int, out: dict, stream=None):
+    T, k = topk_ids.shape
+    L = load()
+    _check(L.w4a16_route_prep(_ptr(topk_ids) if T else None, T, k, E, block_m,
+                              ctypes.c_void_p(out["sorted_ids"].data_ptr()),
+                              ctypes.c_void_p(out["expert_ids"].data_ptr()), _ptr(out["num_tokens_padded"]),
+                              _ptr(out["expert_offsets"]), _ptr(out["counts"]), _stream(stream)))
+
+
+# ---------------------------------------------------------------- planning and GEMM
+
+def plan_select(T: int, k: int, E: int, N: int, K: int, expected_rows_per_expert: float = 0.0) -> Plan:
+    p = Plan()
+    _check(load().w4a16_plan_select(T, k, E, N, K, float(expected_rows_per_expert), ctypes.byref(p)))
+    return p
+
+
+def make_plan(kernel: str, block_m: int, n_blocks: int, waves: int) -> Plan:
+    p = Plan()
+    p.kernel = KERNEL_DECODE if kernel == "decode" else KERNEL_PREFILL
+    p.block_m, p.n_blocks, p.waves = block_m, n_blocks, waves
+    return p
+
+
+def grouped_gemm(A: torch.Tensor, a_row_div: int, w: Weights, route: dict, plan: Plan,
+                 out: torch.Tensor | None = None, out_f32: bool = False, stream=None) -> torch.Tensor:
+    """Indexed grouped GEMM; ``route`` from route_prep with plan.block_m.  Returns out [R, N], BF16 (or the
+    unrounded binary32 accumulators with ``out_f32``)."""
+    R = route["R"]
+    if route["block_m"] != plan.block_m:
+        raise ValueError("routing was prepared with block_m=%d but the plan uses %d" % (route["block_m"], plan.block_m))
+    if route["E"] != w.E:
+        raise ValueError("routing was prepared for %d experts but the weights hold %d" % (route["E"], w.E))
+    if out is None:
+        out = torch.empty((R, w.N), dtype=torch.float32 if out_f32 else torch.bfloat16, device=A.device)
+    fn = load().w4a16_grouped_gemm_f32 if out.dtype == torch.float32 else load().w4a16_grouped_gemm
+    _check(fn(_ptr(A), a_row_div, w.handle, ctypes.c_void_p(route["sorted_ids"].data_ptr()),
+              ctypes.c_void_p(route["expert_ids"].data_ptr()), _ptr(route["num_tokens_padded"]), R,
+              ctypes.byref(plan), _ptr(out), None, 0, _stream(stream)))
+    return out
+
+
+def offsets_workspace_bytes(rows_max: int, E: int, plan: Plan) -> int:
+    out = _SZ(0)
+    _check(load().w4a16_offsets_workspace_bytes(rows_max, E, ctypes.byref(plan), ctypes.byref(out)))
+    return out.value
+
+
+def grouped_gemm_offsets(A_sorted: torch.Tensor, expert_offsets: torch.Tensor, w: Weights, plan: Plan,
+                         out: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None):
+    rows_max = A_sorted.shape[0]
+    if out is None:
+        out = torch.empty((rows_max, w.N), dtype=torch.bfloat16, device=A_sorted.device)
+    need = offsets_workspace_bytes(rows_max, w.E, plan)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=A_sorted.device)
+    _check(load().w4a16_grouped_gemm_offsets(_ptr(A_sorted), _ptr(expert_offsets), rows_max, w.handle,
+                                             ctypes.byref(plan), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+# ---------------------------------------------------------------- expert MLP
+
+def silu_mul(gu: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """h = bf16(silu(gate) * up) from gu [rows, 2I] (BF16 or float32, gate columns first)."""
+    rows, two_i = gu.shape
+    I = two_i // 2
+    if out is None:
+        out = torch.empty((rows, I), dtype=torch.bfloat16, device=gu.device)
+    fn = load().w4a16_silu_mul_f32 if gu.dtype == torch.float32 else load().w4a16_silu_mul
+    _check(fn(_ptr(gu), rows, I, _ptr(out), _stream(stream)))
+    return out
+
+
+def moe_combine(y: torch.Tensor, topk_w: torch.Tensor, topk_ids: torch.Tensor, E: int,
+                out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    T, k = topk_ids.shape
+    H = y.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    _check(load().w4a16_moe_combine(_ptr(y), _ptr(topk_w), _ptr(topk_ids), T, k, E, H, _ptr(out), _stream(stream)))
+    return out
+
+
+def fused_moe_plans(T: int, k: int, w13: Weights, w2: Weights):
+    p13, p2 = Plan(), Plan()
+    _check(load().w4a16_fused_moe_plans(T, k, w13.handle, w2.handle, ctypes.byref(p13), ctypes.byref(p2)))
+    return p13, p2
+
+
+def fused_moe_workspace_bytes(T: int, k: int, w13: Weights, w2: Weights) -> int:
+    out = _SZ(0)
+    _check(load().w4a16_fused_moe_workspace_bytes(T, k, w13.handle, w2.handle, ctypes.byref(out)))
+    return out.value
+
+
+def fused_moe(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, w13: Weights, w2: Weights,
+              out: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None,
+              stage_events=None) -> torch.Tensor:
+    """Fused expert MLP.  ``stage_events``: 6 recorded-once torch.cuda.Event objects (timing) or None."""
+    T, k = topk_ids.shape
+    if out is None:
+        out = torch.empty((T, w2.N), dtype=torch.bfloat16, device=x.device)
+    if ws is None:
+        ws = torch.empty(max(fused_moe_workspace_bytes(T, k, w13, w2), 16), dtype=torch.uint8, device=x.device)
+    args = (_ptr(x) if T else None, _ptr(topk_ids) if T else None, _ptr(topk_w) if T else None, T, k, w13.handle,
+            w2.handle, _ptr(out) if T else None, _ptr(ws), ws.numel(), _stream(stream))
+    if stage_events is None:
+        _check(load().w4a16_fused_moe(*args))
+    else:
+        if len(stage_events) != 6:
+            raise ValueError("stage_events needs 6 events")
+        arr = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(e.cuda_event) for e in stage_events])
+        _check(load().w4a16_fused_moe_profiled(*args, ctypes.cast(arr, ctypes.c_void_p)))
+    return out
