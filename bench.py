@@ -161,7 +161,7 @@ def main():
     idsd = torch.from_numpy(ids).to(dev)
     twd = torch.from_numpy(tw).to(dev)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(w4.fused_moe_workspace_bytes(T, k, w13, w2), dtype=torch.uint8, device=dev)
+    ws = w4.zeroed_workspace(w4.fused_moe_workspace_bytes(T, k, w13, w2), dev)
     p13, p2 = w4.fused_moe_plans(T, k, w13, w2)
     print("[bench] plans: gate_up %r, down %r; %d active experts, %d local routes; weight pool %d copies x %.1f MB"
           % (p13, p2, len(active), Rv, ncopies, per_copy / 1e6), file=sys.stderr, flush=True)

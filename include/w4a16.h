@@ -65,10 +65,11 @@ enum { W4A16_KERNEL_DECODE = 1, W4A16_KERNEL_PREFILL = 2 };
  * for the routing tensors passed with it. */
 typedef struct w4a16_plan {
     int32_t kernel;        /* W4A16_KERNEL_DECODE or W4A16_KERNEL_PREFILL */
-    int32_t block_m;       /* rows per route block: 16, 32 or 64 (decode); 64 or 128 (prefill) */
+    int32_t block_m;       /* rows per route block: 16, 32, 48 or 64 (decode); 64 or 128 (prefill) */
     int32_t n_blocks;      /* 16-column blocks per wavefront: 1, 2 or 4 */
-    int32_t waves;         /* wavefronts per workgroup: decode splits K across them, prefill splits N */
-    int32_t reserved[4];   /* must be zero */
+    int32_t waves;         /* wavefronts per workgroup, each owning its own columns: 4 (decode), 1..4 (prefill) */
+    int32_t k_split;       /* decode: workgroups sharing one output tile along K (1..64); prefill: 1 */
+    int32_t reserved[3];   /* must be zero */
 } w4a16_plan;
 
 /* Host handle describing one packed weight set (E experts of N x K). */
@@ -168,10 +169,14 @@ int w4a16_plan_select(int T, int k, int E, int N, int K, float expected_rows_per
  *   routing    as produced by w4a16_route_prep with p->block_m for R routes
  *              and the handle's E experts
  *   out        device BF16 bits [R, N]; rows of invalid routes untouched
- *   ws         workspace of w4a16_gemm_workspace_bytes (may be NULL if 0)
+ *   ws         workspace of w4a16_gemm_workspace_bytes (may be NULL if 0).  A
+ *              plan with k_split > 1 keeps per-tile arrival counters in it:
+ *              the workspace must be zero-filled once before its first use,
+ *              and every call leaves the counters at zero again.  Calls that
+ *              share a workspace must not run concurrently.
  * Errors: INVALID_ARG, LAYOUT_MISMATCH (bad handle), UNSUPPORTED_SHAPE (plan
  * values outside the supported set), WORKSPACE_TOO_SMALL, HIP_ERROR. */
-int w4a16_gemm_workspace_bytes(const w4a16_plan* p, int R, int N, size_t* bytes);
+int w4a16_gemm_workspace_bytes(const w4a16_plan* p, int R, int E, int N, size_t* bytes);
 
 int w4a16_grouped_gemm(const uint16_t* A, int a_row_div, const w4a16_weights* w, const int32_t* sorted_ids,
                        const int32_t* expert_ids, const int32_t* num_tokens_padded, int R,
@@ -190,9 +195,10 @@ int w4a16_grouped_gemm_f32(const uint16_t* A, int a_row_div, const w4a16_weights
  *   out[r, n] = bf16( sum_k A_sorted[r, k] * w[e(r), n, k] ),  r < expert_offsets[E].
  *   expert_offsets  device int32 [E+1], non-decreasing, expert_offsets[E] <= rows_max
  *   rows_max        host bound on expert_offsets[E] (sizes the launch)
- *   ws              >= w4a16_offsets_workspace_bytes(rows_max, E, p)
+ *   ws              >= w4a16_offsets_workspace_bytes(rows_max, w, p), zero-filled
+ *                   once before its first use when p->k_split > 1
  * Rows r >= expert_offsets[E] of out are untouched. */
-int w4a16_offsets_workspace_bytes(int rows_max, int E, const w4a16_plan* p, size_t* bytes);
+int w4a16_offsets_workspace_bytes(int rows_max, const w4a16_weights* w, const w4a16_plan* p, size_t* bytes);
 
 int w4a16_grouped_gemm_offsets(const uint16_t* A_sorted, const int32_t* expert_offsets, int rows_max,
                                const w4a16_weights* w, const w4a16_plan* p, uint16_t* out, void* ws,
@@ -225,7 +231,9 @@ int w4a16_moe_combine(const float* y, const float* topk_w, const int32_t* topk_i
  *   w2      handle of [E, H, I] weights
  *   out     device BF16 bits [T,H]; every row written (zero rows for
  *           tokens without a valid route)
- *   ws      >= w4a16_fused_moe_workspace_bytes(T, k, w13, w2)
+ *   ws      >= w4a16_fused_moe_workspace_bytes(T, k, w13, w2), zero-filled
+ *           once before its first use (split-K counters; each call leaves
+ *           them at zero); calls sharing a workspace must not overlap.
  * Errors: INVALID_ARG, LAYOUT_MISMATCH (w13 not [E,2I,H] with w2 [E,H,I]),
  * WORKSPACE_TOO_SMALL, HIP_ERROR. */
 int w4a16_fused_moe_workspace_bytes(int T, int k, const w4a16_weights* w13, const w4a16_weights* w2,

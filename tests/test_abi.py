@@ -104,6 +104,9 @@ def test_plan_selector_keys_on_rows_per_expert(lib):
     # an explicit expectation overrides T*k/E
     p = L.plan_select(64, 8, 128, 1536, 2048, expected_rows_per_expert=30.0)
     assert p.kernel == L.KERNEL_DECODE and p.block_m == 48
+    # one token on a Kimi-K2-like expert share: few workgroups, so K is split across workgroups
+    p = L.plan_select(1, 8, 48, 4096, 7168, expected_rows_per_expert=1.0 / 48)
+    assert p.kernel == L.KERNEL_DECODE and p.k_split > 1
     # memoised: same answer twice
     a = L.plan_select(256, 8, 48, 4096, 7168)
     b = L.plan_select(256, 8, 48, 4096, 7168)
@@ -115,11 +118,18 @@ def test_plan_validation(lib):
 
     sz = ctypes.c_size_t(0)
     bad = L.make_plan("decode", 24, 4, 4)
-    assert lib.w4a16_gemm_workspace_bytes(ctypes.byref(bad), 32, 512, ctypes.byref(sz)) == -2
+    assert lib.w4a16_gemm_workspace_bytes(ctypes.byref(bad), 32, 8, 512, ctypes.byref(sz)) == -2
     bad = L.make_plan("prefill", 96, 4, 4)
-    assert lib.w4a16_gemm_workspace_bytes(ctypes.byref(bad), 32, 512, ctypes.byref(sz)) == -2
+    assert lib.w4a16_gemm_workspace_bytes(ctypes.byref(bad), 32, 8, 512, ctypes.byref(sz)) == -2
+    bad = L.make_plan("prefill", 64, 4, 4, k_split=2)
+    assert lib.w4a16_gemm_workspace_bytes(ctypes.byref(bad), 32, 8, 512, ctypes.byref(sz)) == -2
     good = L.make_plan("decode", 16, 4, 4)
-    assert lib.w4a16_gemm_workspace_bytes(ctypes.byref(good), 32, 512, ctypes.byref(sz)) == 0
+    assert lib.w4a16_gemm_workspace_bytes(ctypes.byref(good), 32, 8, 512, ctypes.byref(sz)) == 0
+    assert sz.value == 0
+    # split K: counters (one per route block and column tile) then fp32 partial tiles
+    split = L.make_plan("decode", 16, 4, 4, k_split=4)
+    # 10 route blocks x 2 column tiles of 256: 20 counters (one 256-byte line), 10*2*4 partial tiles of 16x256
+    assert L.gemm_workspace_bytes(split, 32, 8, 512) == 256 + 10 * 2 * 4 * 16 * 256 * 4
 
 
 def test_bad_handle_is_rejected(lib):

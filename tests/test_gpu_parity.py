@@ -105,9 +105,11 @@ def test_route_prep_bit_exact(orc, name, gen, E, BM):
 
 # ------------------------------------------------------------------ GEMM, tiny config, both kernels
 
-DECODE_PLANS = [("decode", bm, nbw, wv) for bm in (16, 32, 48, 64) for nbw in (1, 2, 4) for wv in (1, 4)
-                if 4 * wv * bm * (nbw * 16 + 1) <= 65536]  # the host rejects larger reduction buffers
-PREFILL_PLANS = [("prefill", bm, nbw, wv) for bm in (64, 128) for nbw in (2, 4) for wv in (1, 2, 4)]
+DECODE_PLANS = ([("decode", bm, nbw, 4, 1) for bm in (16, 32, 48, 64) for nbw in (1, 2, 4)]
+                + [("decode", 16, 4, 4, 2), ("decode", 32, 2, 4, 2), ("decode", 64, 1, 4, 2),
+                   ("decode", 16, 1, 4, 3)])  # 3 slices of a 2-stage K: one slice is empty
+PREFILL_PLANS = [("prefill", bm, nbw, wv, 1) for bm in (64, 128) for nbw in (2, 4) for wv in (1, 2, 4)]
+PLAN_ID = lambda p: "%s-bm%d-nb%d-w%d-ks%d" % p  # noqa: E731
 
 
 def _run_gemm(case, plan, a_row_div=None):
@@ -119,7 +121,7 @@ def _run_gemm(case, plan, a_row_div=None):
     return bits(out)
 
 
-@pytest.mark.parametrize("plan_args", DECODE_PLANS + PREFILL_PLANS, ids=lambda p: "%s-bm%d-nb%d-w%d" % p)
+@pytest.mark.parametrize("plan_args", DECODE_PLANS + PREFILL_PLANS, ids=PLAN_ID)
 def test_gemm_tiny_all_plans(orc, plan_args):
     _say("gemm tiny %s" % (plan_args,))
     case = synth.tiny_case()
@@ -130,8 +132,9 @@ def test_gemm_tiny_all_plans(orc, plan_args):
     _say("  worst ratio %.2e" % worst)
 
 
-@pytest.mark.parametrize("plan_args", [("decode", 16, 4, 4), ("decode", 64, 2, 2), ("prefill", 64, 4, 4),
-                                       ("prefill", 128, 2, 4)], ids=lambda p: "%s-bm%d-nb%d-w%d" % p)
+@pytest.mark.parametrize("plan_args", [("decode", 16, 4, 4, 1), ("decode", 64, 2, 4, 1), ("decode", 16, 4, 4, 3),
+                                       ("decode", 32, 2, 4, 7), ("prefill", 64, 4, 4, 1), ("prefill", 128, 2, 4, 1)],
+                         ids=PLAN_ID)
 @pytest.mark.parametrize("shape", [(24, 6, 2, 40, 512), (9, 4, 3, 64, 96), (70, 3, 2, 16, 2048),
                                    (5, 10, 8, 4096, 7168)], ids=lambda s: "T%d-E%d-k%d-N%d-K%d" % s)
 def test_gemm_integer_exact(orc, plan_args, shape):
@@ -180,9 +183,9 @@ def _edge_case(kind):
 EDGE = ["E1", "one hot expert", "empty and single", "ragged N and K", "tile edges", "non-local ids"]
 
 
-@pytest.mark.parametrize("plan_args", [("decode", 16, 1, 1), ("decode", 32, 4, 4), ("decode", 64, 2, 4),
-                                       ("prefill", 64, 2, 1), ("prefill", 128, 4, 4)],
-                         ids=lambda p: "%s-bm%d-nb%d-w%d" % p)
+@pytest.mark.parametrize("plan_args", [("decode", 16, 1, 4, 1), ("decode", 32, 4, 4, 1), ("decode", 64, 2, 4, 1),
+                                       ("decode", 16, 2, 4, 2), ("prefill", 64, 2, 1, 1), ("prefill", 128, 4, 4, 1)],
+                         ids=PLAN_ID)
 @pytest.mark.parametrize("kind", EDGE)
 def test_gemm_edge_cases(orc, kind, plan_args):
     _say("gemm edge %s %s" % (kind, plan_args))
@@ -197,7 +200,7 @@ def test_gemm_edge_cases(orc, kind, plan_args):
 def test_gemm_zero_tokens():
     case = synth.tiny_case()
     w = _pack(case.codes, case.scales)
-    plan = w4.make_plan("decode", 16, 4, 4)
+    plan = w4.make_plan("decode", 16, 4, 4, 1)
     route = w4.route_prep(i32(np.zeros((0, 2), np.int32)), case.E, 16)
     out = poison_bf16(1, case.N)
     w4.grouped_gemm(u16(case.A), 2, w, route, plan, out=out[:0])
@@ -208,7 +211,7 @@ def test_gemm_zero_tokens():
 
 def test_gemm_is_deterministic_and_permutation_equivariant(orc):
     case = synth.tiny_case()
-    for plan_args in (("decode", 16, 4, 4), ("prefill", 64, 4, 4)):
+    for plan_args in (("decode", 16, 4, 4, 1), ("decode", 16, 2, 4, 2), ("prefill", 64, 4, 4, 1)):
         plan = w4.make_plan(*plan_args)
         a = _run_gemm(case, plan)
         b = _run_gemm(case, plan)
@@ -224,7 +227,8 @@ def test_gemm_is_deterministic_and_permutation_equivariant(orc):
 
 # ------------------------------------------------------------------ offsets form
 
-@pytest.mark.parametrize("plan_args", [("decode", 16, 4, 4), ("prefill", 64, 4, 4)], ids=lambda p: p[0])
+@pytest.mark.parametrize("plan_args", [("decode", 16, 4, 4, 1), ("decode", 16, 2, 4, 2), ("prefill", 64, 4, 4, 1)],
+                         ids=PLAN_ID)
 def test_gemm_offsets_form(orc, plan_args):
     rng = np.random.default_rng(99)
     E, N, K = 6, 96, 256
@@ -336,3 +340,39 @@ def check_gemm_f32(got, ref, flat, E, label, tol=5e-3):
         den = np.abs(ref[rows]).max()
         ratio = np.abs(got[rows] - ref[rows]).max() / den
         assert ratio <= tol, "%s expert %d ratio %.3g" % (label, e, ratio)
+
+
+def test_fused_moe_graph_replays(orc):
+    """The fused call captured in a HIP graph: every replay (with eager work and synchronisations in between)
+    must equal the eager result bit for bit, including plans that split K (their counters reset each call)."""
+    rng = np.random.default_rng(77)
+    T, E, k, H, I = 2, 48, 8, 512, 256               # few routes: the planner splits K
+    x = synth.activations(rng, T, H)
+    c13, s13 = synth.codes(rng, E, 2 * I, H), synth.scales(rng, E, 2 * I, H)
+    c2, s2 = synth.codes(rng, E, H, I), synth.scales(rng, E, H, I)
+    ids = synth.uniform_topk(rng, T, E, k)
+    tw = rng.uniform(0.1, 1.0, (T, k)).astype(np.float32)
+    w13, w2 = _pack(c13, s13), _pack(c2, s2)
+    p13, p2 = w4.fused_moe_plans(T, k, w13, w2)
+    _say("graph replay plans %r %r" % (p13, p2))
+    xd, idsd, twd = u16(x), i32(ids), f32(tw)
+    ws = w4.zeroed_workspace(w4.fused_moe_workspace_bytes(T, k, w13, w2), xd.device)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    w4.fused_moe(xd, idsd, twd, w13, w2, out=out, ws=ws)
+    eager = bits(out)
+    orc.fused_moe(x, ids, tw, c13, s13, c2, s2)
+    ref = orc.last_out_acc
+    for t in range(T):
+        assert np.abs(orc_bf16_to_f64(eager[t]) - ref[t]).max() <= FUSED_TOL * np.abs(ref[t]).max()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        w4.fused_moe(xd, idsd, twd, w13, w2, out=out, ws=ws)
+    for rep in range(4):
+        out.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out), eager), "replay %d differs from the eager call" % rep
+        w4.fused_moe(xd, idsd, twd, w13, w2, out=out, ws=ws)  # eager work between replays
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out), eager)

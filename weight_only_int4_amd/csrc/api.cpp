@@ -74,7 +74,7 @@ int env_int(const char* name, int dflt) {
 
 struct Overrides {
     int force_kernel = 0;  // 0 auto, else W4A16_KERNEL_*
-    int block_m = 0, n_blocks = 0, waves = 0;
+    int block_m = 0, n_blocks = 0, waves = 0, k_split = 0;
 };
 
 const Overrides& overrides() {
@@ -86,6 +86,7 @@ const Overrides& overrides() {
         r.block_m = env_int("W4A16_BLOCK_M", 0);
         r.n_blocks = env_int("W4A16_N_BLOCKS", 0);
         r.waves = env_int("W4A16_WAVES", 0);
+        r.k_split = env_int("W4A16_K_SPLIT", 0);
         return r;
     }();
     return o;
@@ -102,20 +103,28 @@ w4a16_plan select_plan(int T, int k, int E, int N, int K, float rows) {
     w4a16_plan p;
     memset(&p, 0, sizeof(p));
     const int NB = (N + 15) / 16;
-    const int KB = (K + SB_K - 1) / SB_K;
+    const int nst = (K / 32 + 3) / 4;  // 128-k stages
     int kernel = rows <= kDecodeMaxRows ? W4A16_KERNEL_DECODE : W4A16_KERNEL_PREFILL;
     if (ov.force_kernel) kernel = ov.force_kernel;
     p.kernel = kernel;
+    p.k_split = 1;
     if (kernel == W4A16_KERNEL_DECODE) {
         // cover ~1.3x the expected rows in one block so a slightly heavy expert
         // does not spill into a second pass over all of K (Chord page, "Grouped
         // SM90 kernels", masked decode sizing)
         int bm = (int)ceilf(1.3f * rows / 16.0f) * 16;
         p.block_m = bm < 16 ? 16 : (bm > 64 ? 64 : bm);
-        p.n_blocks = NB >= 64 ? 4 : (NB >= 8 ? 2 : 1);
-        p.waves = KB >= 4 ? 4 : (KB >= 2 ? 2 : 1);
-        // the cross-wavefront reduction buffer must fit in 64 KiB of LDS
-        while (p.waves > 1 && sizeof(float) * (size_t)p.waves * p.block_m * (p.n_blocks * 16 + 1) > 65536) --p.waves;
+        p.n_blocks = NB >= 16 ? 4 : (NB >= 8 ? 2 : 1);
+        p.waves = 4;
+        // expected route blocks: experts that receive at least one row (Poisson estimate)
+        const double active = (double)E * (1.0 - exp(-(double)rows));
+        const double blocks = active * ceil((double)rows / p.block_m > 1.0 ? (double)rows / p.block_m : 1.0);
+        const int n_tiles = (NB + p.n_blocks * p.waves - 1) / (p.n_blocks * p.waves);
+        const double waves_total = blocks * n_tiles * p.waves;
+        // fill the machine with at least ~8 wavefronts per CU; keep >= 2 stages per split
+        int ks = (int)ceil(2048.0 / (waves_total > 1.0 ? waves_total : 1.0));
+        const int max_ks = nst / 2 > 1 ? nst / 2 : 1;
+        p.k_split = ks < 1 ? 1 : (ks > max_ks ? max_ks : (ks > 16 ? 16 : ks));
     } else {
         p.block_m = rows >= 96.0f ? 128 : 64;
         p.n_blocks = 4;
@@ -124,35 +133,55 @@ w4a16_plan select_plan(int T, int k, int E, int N, int K, float rows) {
     if (ov.block_m) p.block_m = ov.block_m;
     if (ov.n_blocks) p.n_blocks = ov.n_blocks;
     if (ov.waves) p.waves = ov.waves;
-    (void)T; (void)k; (void)E;
+    if (ov.k_split && p.kernel == W4A16_KERNEL_DECODE) p.k_split = ov.k_split;
+    (void)T; (void)k;
     return p;
 }
 
 int validate_plan(const w4a16_plan* p, const char* what) {
     if (!p) return fail(W4A16_INVALID_ARG, "%s: plan is NULL", what);
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 3; ++i)
         if (p->reserved[i]) return fail(W4A16_INVALID_ARG, "%s: plan.reserved must be zero", what);
+    if (p->waves < 1 || p->waves > 4) return fail(W4A16_UNSUPPORTED_SHAPE, "%s: waves %d not in 1..4", what, p->waves);
     if (p->kernel == W4A16_KERNEL_DECODE) {
         if (p->block_m % 16 || p->block_m < 16 || p->block_m > 64)
             return fail(W4A16_UNSUPPORTED_SHAPE, "%s: decode block_m %d not in {16,32,48,64}", what, p->block_m);
         if (p->n_blocks != 1 && p->n_blocks != 2 && p->n_blocks != 4)
             return fail(W4A16_UNSUPPORTED_SHAPE, "%s: decode n_blocks %d not in {1,2,4}", what, p->n_blocks);
-        if (p->waves < 1 || p->waves > 4)
-            return fail(W4A16_UNSUPPORTED_SHAPE, "%s: decode waves %d not in 1..4", what, p->waves);
-        const size_t lds = sizeof(float) * (size_t)p->waves * p->block_m * (p->n_blocks * 16 + 1);
-        if (lds > 65536)
-            return fail(W4A16_UNSUPPORTED_SHAPE, "%s: decode plan needs %zu bytes of LDS (max 65536)", what, lds);
+        if (p->k_split < 1 || p->k_split > 64)
+            return fail(W4A16_UNSUPPORTED_SHAPE, "%s: decode k_split %d not in 1..64", what, p->k_split);
+        if (p->waves != 4) return fail(W4A16_UNSUPPORTED_SHAPE, "%s: decode waves must be 4", what);
     } else if (p->kernel == W4A16_KERNEL_PREFILL) {
         if (p->block_m != 64 && p->block_m != 128)
             return fail(W4A16_UNSUPPORTED_SHAPE, "%s: prefill block_m %d not in {64,128}", what, p->block_m);
         if (p->n_blocks != 2 && p->n_blocks != 4)
             return fail(W4A16_UNSUPPORTED_SHAPE, "%s: prefill n_blocks %d not in {2,4}", what, p->n_blocks);
-        if (p->waves < 1 || p->waves > 4)
-            return fail(W4A16_UNSUPPORTED_SHAPE, "%s: prefill waves %d not in 1..4", what, p->waves);
+        if (p->k_split != 1) return fail(W4A16_UNSUPPORTED_SHAPE, "%s: prefill k_split must be 1", what);
     } else {
         return fail(W4A16_INVALID_ARG, "%s: unknown kernel %d", what, p->kernel);
     }
     return W4A16_OK;
+}
+
+// Split-K workspace of one GEMM: arrival counters first (so that GEMMs sharing a
+// workspace find them at the same place, all zero), then the partial tiles.
+struct GemmWs {
+    size_t counter_bytes, partial_bytes, total;
+};
+
+GemmWs gemm_ws(const Shape& sh, const w4a16_plan& p, int max_blocks) {
+    GemmWs g;
+    g.counter_bytes = align_up(sizeof(unsigned) * decode_counters(sh, p, max_blocks), 256);
+    g.partial_bytes = align_up(sizeof(float) * decode_partial_floats(sh, p, max_blocks), 256);
+    g.total = g.counter_bytes + g.partial_bytes;
+    return g;
+}
+
+// counters at ws, partials at ws + partial_offset
+void bind_ws(GemmArgs& a, const GemmWs& g, void* ws, size_t partial_offset) {
+    if (g.total == 0) return;
+    a.counters = static_cast<unsigned*>(ws);
+    a.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + partial_offset);
 }
 
 hipError_t run_gemm(const GemmArgs& a, const w4a16_plan& p, hipStream_t s) {
@@ -162,14 +191,16 @@ hipError_t run_gemm(const GemmArgs& a, const w4a16_plan& p, hipStream_t s) {
 // Workspace carve-up of the fused expert MLP.
 struct FusedLayout {
     int maxP, maxB;
-    size_t off_sorted, off_eids, off_ntp, off_offsets, off_counts, off_gu, off_h, off_y, total;
+    size_t off_sorted, off_eids, off_ntp, off_offsets, off_counts, off_gu, off_h, off_y, off_split, total;
 };
 
-FusedLayout fused_layout(int T, int k, int E, int H, int I, int BM) {
+// The split-K area goes first so its counters sit at a fixed place regardless of the route block.
+FusedLayout fused_layout(int T, int k, int E, int H, int I, int BM, size_t split_bytes) {
     FusedLayout f;
     route_bounds(T, k, E, BM, &f.maxP, &f.maxB);
     const size_t R = (size_t)T * k;
     size_t o = 0;
+    f.off_split = o;  o = align_up(o + split_bytes, 256);
     f.off_sorted = o; o = align_up(o + sizeof(int32_t) * (size_t)f.maxP, 256);
     f.off_eids = o;   o = align_up(o + sizeof(int32_t) * (size_t)f.maxB, 256);
     f.off_ntp = o;    o = align_up(o + sizeof(int32_t), 256);
@@ -320,18 +351,19 @@ int w4a16_plan_select(int T, int k, int E, int N, int K, float expected_rows_per
     return ok();
 }
 
-int w4a16_gemm_workspace_bytes(const w4a16_plan* p, int R, int N, size_t* bytes) {
+int w4a16_gemm_workspace_bytes(const w4a16_plan* p, int R, int E, int N, size_t* bytes) {
     int rc = validate_plan(p, "w4a16_gemm_workspace_bytes");
     if (rc) return rc;
-    if (!bytes) return fail(W4A16_INVALID_ARG, "w4a16_gemm_workspace_bytes: bytes is NULL");
-    (void)R; (void)N;
-    *bytes = 0;
+    if (!bytes || R < 0 || E < 1 || N < 1) return fail(W4A16_INVALID_ARG, "w4a16_gemm_workspace_bytes: bad argument");
+    int maxP, maxB;
+    route_bounds(R, 1, E, p->block_m, &maxP, &maxB);
+    *bytes = gemm_ws(make_shape(E, N, 32), *p, maxB).total;
     return ok();
 }
 
 static int grouped_gemm_impl(const char* what, const uint16_t* A, int a_row_div, const w4a16_weights* w,
                              const int32_t* sorted_ids, const int32_t* expert_ids, int R, const w4a16_plan* p,
-                             void* out, int out_f32, hipStream_t s) {
+                             void* out, int out_f32, void* ws, size_t ws_bytes, hipStream_t s) {
     int rc = check_handle(w, what);
     if (rc) return rc;
     rc = validate_plan(p, what);
@@ -343,31 +375,52 @@ static int grouped_gemm_impl(const char* what, const uint16_t* A, int a_row_div,
     if (!aligned16(A)) return fail(W4A16_INVALID_ARG, "%s: A must be 16-byte aligned", what);
     int maxP, maxB;
     route_bounds(R / a_row_div, a_row_div, w->shape.E, p->block_m, &maxP, &maxB);
+    const GemmWs g = gemm_ws(w->shape, *p, maxB);
+    if (g.total && (!ws || ws_bytes < g.total))
+        return fail(W4A16_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, needs %zu", what, ws_bytes, g.total);
+    if (g.total && !aligned16(ws)) return fail(W4A16_INVALID_ARG, "%s: workspace must be 16-byte aligned", what);
     GemmArgs a{A, a_row_div, w->packed, w->shape, sorted_ids, expert_ids, R, maxB, out, out_f32};
+    bind_ws(a, g, ws, g.counter_bytes);
     return check_launch(run_gemm(a, *p, s), what);
 }
 
 int w4a16_grouped_gemm(const uint16_t* A, int a_row_div, const w4a16_weights* w, const int32_t* sorted_ids,
                        const int32_t* expert_ids, const int32_t* num_tokens_padded, int R, const w4a16_plan* p,
                        uint16_t* out, void* ws, size_t ws_bytes, hipStream_t s) {
-    (void)ws; (void)ws_bytes; (void)num_tokens_padded;
-    return grouped_gemm_impl("w4a16_grouped_gemm", A, a_row_div, w, sorted_ids, expert_ids, R, p, out, 0, s);
+    (void)num_tokens_padded;
+    return grouped_gemm_impl("w4a16_grouped_gemm", A, a_row_div, w, sorted_ids, expert_ids, R, p, out, 0, ws, ws_bytes,
+                             s);
 }
 
 int w4a16_grouped_gemm_f32(const uint16_t* A, int a_row_div, const w4a16_weights* w, const int32_t* sorted_ids,
                            const int32_t* expert_ids, const int32_t* num_tokens_padded, int R, const w4a16_plan* p,
                            float* out, void* ws, size_t ws_bytes, hipStream_t s) {
-    (void)ws; (void)ws_bytes; (void)num_tokens_padded;
-    return grouped_gemm_impl("w4a16_grouped_gemm_f32", A, a_row_div, w, sorted_ids, expert_ids, R, p, out, 1, s);
+    (void)num_tokens_padded;
+    return grouped_gemm_impl("w4a16_grouped_gemm_f32", A, a_row_div, w, sorted_ids, expert_ids, R, p, out, 1, ws,
+                             ws_bytes, s);
 }
 
-int w4a16_offsets_workspace_bytes(int rows_max, int E, const w4a16_plan* p, size_t* bytes) {
-    int rc = validate_plan(p, "w4a16_offsets_workspace_bytes");
+// Offsets-form workspace: [split-K area][sorted_ids][expert_ids].
+static size_t offsets_layout(int rows_max, const w4a16_weights* w, const w4a16_plan* p, size_t* off_sorted,
+                             size_t* off_eids, int* maxP, int* maxB, GemmWs* g) {
+    route_bounds(rows_max, 1, w->shape.E, p->block_m, maxP, maxB);
+    *g = gemm_ws(w->shape, *p, *maxB);
+    *off_sorted = g->total;
+    *off_eids = *off_sorted + align_up(sizeof(int32_t) * (size_t)*maxP, 256);
+    return *off_eids + align_up(sizeof(int32_t) * (size_t)*maxB, 256);
+}
+
+int w4a16_offsets_workspace_bytes(int rows_max, const w4a16_weights* w, const w4a16_plan* p, size_t* bytes) {
+    const char* what = "w4a16_offsets_workspace_bytes";
+    int rc = check_handle(w, what);
     if (rc) return rc;
-    if (!bytes || rows_max < 0 || E < 1) return fail(W4A16_INVALID_ARG, "w4a16_offsets_workspace_bytes: bad argument");
+    rc = validate_plan(p, what);
+    if (rc) return rc;
+    if (!bytes || rows_max < 0) return fail(W4A16_INVALID_ARG, "%s: bad argument", what);
+    size_t a, b;
     int maxP, maxB;
-    route_bounds(rows_max, 1, E, p->block_m, &maxP, &maxB);
-    *bytes = align_up(sizeof(int32_t) * (size_t)maxP, 256) + align_up(sizeof(int32_t) * (size_t)maxB, 256);
+    GemmWs g;
+    *bytes = offsets_layout(rows_max, w, p, &a, &b, &maxP, &maxB, &g);
     return ok();
 }
 
@@ -382,21 +435,23 @@ int w4a16_grouped_gemm_offsets(const uint16_t* A_sorted, const int32_t* expert_o
     if (rows_max < 0) return fail(W4A16_INVALID_ARG, "%s: rows_max=%d", what, rows_max);
     if (w->shape.E > W4A16_MAX_EXPERTS) return fail(W4A16_UNSUPPORTED_SHAPE, "%s: too many experts", what);
     if (rows_max == 0) return ok();
-    size_t need = 0;
-    w4a16_offsets_workspace_bytes(rows_max, w->shape.E, p, &need);
+    size_t off_sorted, off_eids;
+    int maxP, maxB;
+    GemmWs g;
+    const size_t need = offsets_layout(rows_max, w, p, &off_sorted, &off_eids, &maxP, &maxB, &g);
     if (!ws || ws_bytes < need)
         return fail(W4A16_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, needs %zu", what, ws_bytes, need);
+    if (!aligned16(ws)) return fail(W4A16_INVALID_ARG, "%s: workspace must be 16-byte aligned", what);
     if (!A_sorted || !expert_offsets || !out) return fail(W4A16_INVALID_ARG, "%s: NULL pointer argument", what);
     if (!aligned16(A_sorted)) return fail(W4A16_INVALID_ARG, "%s: A_sorted must be 16-byte aligned", what);
-    int maxP, maxB;
-    route_bounds(rows_max, 1, w->shape.E, p->block_m, &maxP, &maxB);
-    int32_t* sorted_ids = static_cast<int32_t*>(ws);
-    int32_t* expert_ids = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + align_up(sizeof(int32_t) * (size_t)maxP, 256));
+    int32_t* sorted_ids = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + off_sorted);
+    int32_t* expert_ids = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + off_eids);
     rc = check_launch(launch_offsets_to_route(expert_offsets, w->shape.E, rows_max, p->block_m, maxP, maxB, sorted_ids,
                                               expert_ids, s),
                       what);
     if (rc) return rc;
     GemmArgs a{A_sorted, 1, w->packed, w->shape, sorted_ids, expert_ids, rows_max, maxB, out, 0};
+    bind_ws(a, g, ws, g.counter_bytes);
     return check_launch(run_gemm(a, *p, s), what);
 }
 
@@ -426,22 +481,27 @@ int w4a16_moe_combine(const float* y, const float* topk_w, const int32_t* topk_i
     return check_launch(launch_combine(y, topk_w, topk_ids, T, k, E, H, out, s), "w4a16_moe_combine");
 }
 
+// Fused workspace: split-K area shared by both GEMMs (counters at the start, sized for the larger of the two),
+// then routing tensors and intermediates.
+static FusedLayout fused_full_layout(int T, int k, const w4a16_weights* w13, const w4a16_weights* w2,
+                                     const w4a16_plan& p13, const w4a16_plan& p2, size_t* counter_bytes) {
+    const int E = w13->shape.E, H = w13->shape.K, I = w2->shape.K;
+    int maxP, maxB;
+    route_bounds(T, k, E, p13.block_m, &maxP, &maxB);
+    const GemmWs a = gemm_ws(w13->shape, p13, maxB), b = gemm_ws(w2->shape, p2, maxB);
+    *counter_bytes = a.counter_bytes > b.counter_bytes ? a.counter_bytes : b.counter_bytes;
+    const size_t partial_bytes = a.partial_bytes > b.partial_bytes ? a.partial_bytes : b.partial_bytes;
+    return fused_layout(T, k, E, H, I, p13.block_m, *counter_bytes + partial_bytes);
+}
+
 int w4a16_fused_moe_workspace_bytes(int T, int k, const w4a16_weights* w13, const w4a16_weights* w2, size_t* bytes) {
     const char* what = "w4a16_fused_moe_workspace_bytes";
-    int rc = check_handle(w13, what);
+    if (!bytes) return fail(W4A16_INVALID_ARG, "%s: bytes is NULL", what);
+    w4a16_plan p13, p2;
+    int rc = w4a16_fused_moe_plans(T, k, w13, w2, &p13, &p2);
     if (rc) return rc;
-    rc = check_handle(w2, what);
-    if (rc) return rc;
-    if (!bytes || T < 0 || k < 1) return fail(W4A16_INVALID_ARG, "%s: bad argument", what);
-    const int E = w13->shape.E, H = w13->shape.K, I = w2->shape.K;
-    // the route block is the same for both projections; size for every block the planner may choose
-    static const int kBlocks[] = {16, 32, 48, 64, 128};
-    size_t need = 0;
-    for (int bm : kBlocks) {
-        const size_t t = fused_layout(T, k, E, H, I, bm).total;
-        if (t > need) need = t;
-    }
-    *bytes = need;
+    size_t cb;
+    *bytes = fused_full_layout(T, k, w13, w2, p13, p2, &cb).total;
     return ok();
 }
 
@@ -463,8 +523,9 @@ int w4a16_fused_moe_plans(int T, int k, const w4a16_weights* w13, const w4a16_we
     p2.kernel = p13.kernel;
     if (p2.kernel == W4A16_KERNEL_PREFILL) {
         if (p2.n_blocks != 2 && p2.n_blocks != 4) p2.n_blocks = 4;
-    } else {
-        while (p2.waves > 1 && sizeof(float) * (size_t)p2.waves * p2.block_m * (p2.n_blocks * 16 + 1) > 65536) --p2.waves;
+        p2.k_split = 1;
+    } else if (p2.k_split < 1) {
+        p2.k_split = 1;
     }
     rc = validate_plan(&p2, what);
     if (rc) return rc;
@@ -506,7 +567,8 @@ int w4a16_fused_moe_profiled(const uint16_t* x, const int32_t* topk_ids, const f
     rc = w4a16_fused_moe_plans(T, k, w13, w2, &p13, &p2);
     if (rc) return rc;
 
-    const FusedLayout f = fused_layout(T, k, E, H, I, p13.block_m);
+    size_t counter_bytes;
+    const FusedLayout f = fused_full_layout(T, k, w13, w2, p13, p2, &counter_bytes);
     char* base = static_cast<char*>(ws);
     int32_t* sorted_ids = reinterpret_cast<int32_t*>(base + f.off_sorted);
     int32_t* expert_ids = reinterpret_cast<int32_t*>(base + f.off_eids);
@@ -533,6 +595,7 @@ int w4a16_fused_moe_profiled(const uint16_t* x, const int32_t* topk_ids, const f
     if (rc) return rc;
     W4A16_STAGE(1);
     GemmArgs g13{x, k, w13->packed, w13->shape, sorted_ids, expert_ids, R, f.maxB, gu, 1};
+    bind_ws(g13, gemm_ws(w13->shape, p13, f.maxB), base + f.off_split, counter_bytes);
     rc = check_launch(run_gemm(g13, p13, s), "w4a16_fused_moe (gate_up)");
     if (rc) return rc;
     W4A16_STAGE(2);
@@ -540,6 +603,7 @@ int w4a16_fused_moe_profiled(const uint16_t* x, const int32_t* topk_ids, const f
     if (rc) return rc;
     W4A16_STAGE(3);
     GemmArgs g2{h, 1, w2->packed, w2->shape, sorted_ids, expert_ids, R, f.maxB, y, 1};
+    bind_ws(g2, gemm_ws(w2->shape, p2, f.maxB), base + f.off_split, counter_bytes);
     rc = check_launch(run_gemm(g2, p2, s), "w4a16_fused_moe (down)");
     if (rc) return rc;
     W4A16_STAGE(4);

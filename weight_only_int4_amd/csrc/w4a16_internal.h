@@ -98,7 +98,13 @@ struct GemmArgs {
     int max_blocks;    // route blocks (grid.x)
     void* out;         // BF16 bits [R,N] or float [R,N]
     int out_f32;
+    float* partials = nullptr;     // split-K partial tiles (decode, k_split > 1)
+    unsigned* counters = nullptr;  // split-K arrival counters, zero between calls
 };
+
+int decode_n_tiles(const Shape& sh, const w4a16_plan& p);
+size_t decode_partial_floats(const Shape& sh, const w4a16_plan& p, int max_blocks);
+size_t decode_counters(const Shape& sh, const w4a16_plan& p, int max_blocks);
 
 hipError_t launch_gemm_decode(const GemmArgs& a, const w4a16_plan& p, hipStream_t s);
 hipError_t launch_gemm_prefill(const GemmArgs& a, const w4a16_plan& p, hipStream_t s);

@@ -32,11 +32,12 @@ class W4A16Error(RuntimeError):
 
 class Plan(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("block_m", ctypes.c_int32), ("n_blocks", ctypes.c_int32),
-                ("waves", ctypes.c_int32), ("reserved", ctypes.c_int32 * 4)]
+                ("waves", ctypes.c_int32), ("k_split", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
 
     def __repr__(self):
         kind = {KERNEL_DECODE: "decode", KERNEL_PREFILL: "prefill"}.get(self.kernel, str(self.kernel))
-        return "Plan(%s, block_m=%d, n_blocks=%d, waves=%d)" % (kind, self.block_m, self.n_blocks, self.waves)
+        return "Plan(%s, block_m=%d, n_blocks=%d, waves=%d, k_split=%d)" % (kind, self.block_m, self.n_blocks,
+                                                                          self.waves, self.k_split)
 
 
 # name -> (restype, argtypes)
@@ -53,12 +54,12 @@ _SIGS = {
     "w4a16_route_bounds": (_I, [_I, _I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
     "w4a16_route_prep": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     "w4a16_plan_select": (_I, [_I, _I, _I, _I, _I, ctypes.c_float, ctypes.POINTER(Plan)]),
-    "w4a16_gemm_workspace_bytes": (_I, [ctypes.POINTER(Plan), _I, _I, ctypes.POINTER(_SZ)]),
+    "w4a16_gemm_workspace_bytes": (_I, [ctypes.POINTER(Plan), _I, _I, _I, ctypes.POINTER(_SZ)]),
     "w4a16_grouped_gemm": (_I, [_P, _I, _P, _P, _P, _P, _I, ctypes.POINTER(Plan), _P, _P, _SZ, _P]),
     "w4a16_grouped_gemm_f32": (_I, [_P, _I, _P, _P, _P, _P, _I, ctypes.POINTER(Plan), _P, _P, _SZ, _P]),
     "w4a16_silu_mul_f32": (_I, [_P, _I, _I, _P, _P]),
     "w4a16_fused_moe_plans": (_I, [_I, _I, _P, _P, ctypes.POINTER(Plan), ctypes.POINTER(Plan)]),
-    "w4a16_offsets_workspace_bytes": (_I, [_I, _I, ctypes.POINTER(Plan), ctypes.POINTER(_SZ)]),
+    "w4a16_offsets_workspace_bytes": (_I, [_I, _P, ctypes.POINTER(Plan), ctypes.POINTER(_SZ)]),
     "w4a16_grouped_gemm_offsets": (_I, [_P, _P, _I, _P, ctypes.POINTER(Plan), _P, _P, _SZ, _P]),
     "w4a16_silu_mul": (_I, [_P, _I, _I, _P, _P]),
     "w4a16_moe_combine": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P]),
@@ -208,15 +209,27 @@ def plan_select(T: int, k: int, E: int, N: int, K: int, expected_rows_per_expert
     return p
 
 
-def make_plan(kernel: str, block_m: int, n_blocks: int, waves: int) -> Plan:
+def make_plan(kernel: str, block_m: int, n_blocks: int, waves: int, k_split: int = 1) -> Plan:
     p = Plan()
     p.kernel = KERNEL_DECODE if kernel == "decode" else KERNEL_PREFILL
-    p.block_m, p.n_blocks, p.waves = block_m, n_blocks, waves
+    p.block_m, p.n_blocks, p.waves, p.k_split = block_m, n_blocks, waves, k_split
     return p
 
 
+def gemm_workspace_bytes(plan: Plan, R: int, E: int, N: int) -> int:
+    out = _SZ(0)
+    _check(load().w4a16_gemm_workspace_bytes(ctypes.byref(plan), R, E, N, ctypes.byref(out)))
+    return out.value
+
+
+def zeroed_workspace(nbytes: int, device) -> torch.Tensor:
+    """A workspace as the library requires it: zero-filled before its first use."""
+    return torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
 def grouped_gemm(A: torch.Tensor, a_row_div: int, w: Weights, route: dict, plan: Plan,
-                 out: torch.Tensor | None = None, out_f32: bool = False, stream=None) -> torch.Tensor:
+                 out: torch.Tensor | None = None, out_f32: bool = False, ws: torch.Tensor | None = None,
+                 stream=None) -> torch.Tensor:
     """Indexed grouped GEMM; ``route`` from route_prep with plan.block_m.  Returns out [R, N], BF16 (or the
     unrounded binary32 accumulators with ``out_f32``)."""
     R = route["R"]
@@ -226,16 +239,18 @@ def grouped_gemm(A: torch.Tensor, a_row_div: int, w: Weights, route: dict, plan:
         raise ValueError("routing was prepared for %d experts but the weights hold %d" % (route["E"], w.E))
     if out is None:
         out = torch.empty((R, w.N), dtype=torch.float32 if out_f32 else torch.bfloat16, device=A.device)
+    if ws is None:
+        ws = zeroed_workspace(gemm_workspace_bytes(plan, R, w.E, w.N), A.device)
     fn = load().w4a16_grouped_gemm_f32 if out.dtype == torch.float32 else load().w4a16_grouped_gemm
     _check(fn(_ptr(A), a_row_div, w.handle, ctypes.c_void_p(route["sorted_ids"].data_ptr()),
               ctypes.c_void_p(route["expert_ids"].data_ptr()), _ptr(route["num_tokens_padded"]), R,
-              ctypes.byref(plan), _ptr(out), None, 0, _stream(stream)))
+              ctypes.byref(plan), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
     return out
 
 
-def offsets_workspace_bytes(rows_max: int, E: int, plan: Plan) -> int:
+def offsets_workspace_bytes(rows_max: int, w: Weights, plan: Plan) -> int:
     out = _SZ(0)
-    _check(load().w4a16_offsets_workspace_bytes(rows_max, E, ctypes.byref(plan), ctypes.byref(out)))
+    _check(load().w4a16_offsets_workspace_bytes(rows_max, w.handle, ctypes.byref(plan), ctypes.byref(out)))
     return out.value
 
 
@@ -244,9 +259,8 @@ def grouped_gemm_offsets(A_sorted: torch.Tensor, expert_offsets: torch.Tensor, w
     rows_max = A_sorted.shape[0]
     if out is None:
         out = torch.empty((rows_max, w.N), dtype=torch.bfloat16, device=A_sorted.device)
-    need = offsets_workspace_bytes(rows_max, w.E, plan)
     if ws is None:
-        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=A_sorted.device)
+        ws = zeroed_workspace(offsets_workspace_bytes(rows_max, w, plan), A_sorted.device)
     _check(load().w4a16_grouped_gemm_offsets(_ptr(A_sorted), _ptr(expert_offsets), rows_max, w.handle,
                                              ctypes.byref(plan), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
     return out
@@ -295,7 +309,7 @@ def fused_moe(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, w13
     if out is None:
         out = torch.empty((T, w2.N), dtype=torch.bfloat16, device=x.device)
     if ws is None:
-        ws = torch.empty(max(fused_moe_workspace_bytes(T, k, w13, w2), 16), dtype=torch.uint8, device=x.device)
+        ws = zeroed_workspace(fused_moe_workspace_bytes(T, k, w13, w2), x.device)
     args = (_ptr(x) if T else None, _ptr(topk_ids) if T else None, _ptr(topk_w) if T else None, T, k, w13.handle,
             w2.handle, _ptr(out) if T else None, _ptr(ws), ws.numel(), _stream(stream))
     if stage_events is None:
