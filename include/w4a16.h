@@ -67,7 +67,7 @@ typedef struct w4a16_plan {
     int32_t kernel;        /* W4A16_KERNEL_DECODE or W4A16_KERNEL_PREFILL */
     int32_t block_m;       /* rows per route block: 16, 32, 48 or 64 (decode); 64 or 128 (prefill) */
     int32_t n_blocks;      /* 16-column blocks per wavefront: 1, 2 or 4 */
-    int32_t waves;         /* wavefronts per workgroup, each owning its own columns: 4 (decode), 1..4 (prefill) */
+    int32_t waves;         /* wavefronts per workgroup, each owning its own columns: 4 */
     int32_t k_split;       /* decode: workgroups sharing one output tile along K (1..64); prefill: 1 */
     int32_t reserved[3];   /* must be zero */
 } w4a16_plan;

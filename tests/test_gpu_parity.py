@@ -108,7 +108,7 @@ def test_route_prep_bit_exact(orc, name, gen, E, BM):
 DECODE_PLANS = ([("decode", bm, nbw, 4, 1) for bm in (16, 32, 48, 64) for nbw in (1, 2, 4)]
                 + [("decode", 16, 4, 4, 2), ("decode", 32, 2, 4, 2), ("decode", 64, 1, 4, 2),
                    ("decode", 16, 1, 4, 3)])  # 3 slices of a 2-stage K: one slice is empty
-PREFILL_PLANS = [("prefill", bm, nbw, wv, 1) for bm in (64, 128) for nbw in (2, 4) for wv in (1, 2, 4)]
+PREFILL_PLANS = [("prefill", bm, nbw, 4, 1) for bm in (64, 128) for nbw in (2, 4)]
 PLAN_ID = lambda p: "%s-bm%d-nb%d-w%d-ks%d" % p  # noqa: E731
 
 
@@ -184,7 +184,7 @@ EDGE = ["E1", "one hot expert", "empty and single", "ragged N and K", "tile edge
 
 
 @pytest.mark.parametrize("plan_args", [("decode", 16, 1, 4, 1), ("decode", 32, 4, 4, 1), ("decode", 64, 2, 4, 1),
-                                       ("decode", 16, 2, 4, 2), ("prefill", 64, 2, 1, 1), ("prefill", 128, 4, 4, 1)],
+                                       ("decode", 16, 2, 4, 2), ("prefill", 64, 2, 4, 1), ("prefill", 128, 4, 4, 1)],
                          ids=PLAN_ID)
 @pytest.mark.parametrize("kind", EDGE)
 def test_gemm_edge_cases(orc, kind, plan_args):

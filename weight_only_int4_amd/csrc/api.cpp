@@ -142,7 +142,6 @@ int validate_plan(const w4a16_plan* p, const char* what) {
     if (!p) return fail(W4A16_INVALID_ARG, "%s: plan is NULL", what);
     for (int i = 0; i < 3; ++i)
         if (p->reserved[i]) return fail(W4A16_INVALID_ARG, "%s: plan.reserved must be zero", what);
-    if (p->waves < 1 || p->waves > 4) return fail(W4A16_UNSUPPORTED_SHAPE, "%s: waves %d not in 1..4", what, p->waves);
     if (p->kernel == W4A16_KERNEL_DECODE) {
         if (p->block_m % 16 || p->block_m < 16 || p->block_m > 64)
             return fail(W4A16_UNSUPPORTED_SHAPE, "%s: decode block_m %d not in {16,32,48,64}", what, p->block_m);
@@ -157,6 +156,7 @@ int validate_plan(const w4a16_plan* p, const char* what) {
         if (p->n_blocks != 2 && p->n_blocks != 4)
             return fail(W4A16_UNSUPPORTED_SHAPE, "%s: prefill n_blocks %d not in {2,4}", what, p->n_blocks);
         if (p->k_split != 1) return fail(W4A16_UNSUPPORTED_SHAPE, "%s: prefill k_split must be 1", what);
+        if (p->waves != 4) return fail(W4A16_UNSUPPORTED_SHAPE, "%s: prefill waves must be 4", what);
     } else {
         return fail(W4A16_INVALID_ARG, "%s: unknown kernel %d", what, p->kernel);
     }

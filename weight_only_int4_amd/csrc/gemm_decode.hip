@@ -4,15 +4,19 @@
 // of Chord's decode profile, "H200 and Blackwell indexed decode", and the
 // split-K program per (expert, N tile, K slice) of the nf4 page, "How it
 // works"):
-//  * One workgroup per (route block of BM rows, 16*NBW*WN output columns,
-//    K slice).  Its WN wavefronts own disjoint columns and walk the same K
-//    range in stages of 128 k, so the BM activation rows of a stage are
-//    gathered once into LDS (double-buffered, one barrier per stage) and read
-//    by every wavefront.
-//  * Each wavefront streams its packed superblocks with 16-byte loads (one
-//    fully coalesced 1 KiB read per half superblock per n-block) and keeps the
-//    next stage's weights in flight in registers while it computes the
-//    current one; weights never go through LDS.
+//  * One workgroup per (route block of BM rows, 64*NBW output columns, K
+//    slice); its four wavefronts own disjoint columns and walk the same K range
+//    in stages of 128 k.
+//  * Both operands stream HBM -> LDS with direct global-to-LDS loads
+//    (global_load_lds_dwordx4) into a ring of D stage slots, so D-1 stages are
+//    in flight per wavefront without holding a single register.  Each lane
+//    reads back exactly the 16 bytes it loaded (weights: the B fragment of its
+//    column and k-slot; activations: its own piece of the shared tile), so a
+//    wavefront only waits on its own load counter, and one barrier per stage
+//    publishes the activation tile and frees the oldest slot.
+//  * The activation tile is stored unpadded with the 16-byte chunks of row r
+//    XOR-permuted by r mod 16, so the 16 rows of an MFMA fragment hit 16
+//    distinct bank groups.
 //  * Per scale group of 32 k the raw codes enter the MFMA as BF16 values
 //    128 + q (one mask/OR per two weights).  The accumulator input of that
 //    MFMA is -136 * (group sum of the activations), itself produced by an
@@ -35,8 +39,9 @@
 namespace w4a16 {
 namespace {
 
-constexpr int KT = 128;       // k per stage (4 scale groups, half a superblock)
-constexpr int LDX = KT + 8;   // padded LDS row in BF16 elements (16 rows of a fragment hit distinct banks)
+constexpr int KT = 128;              // k per stage (4 scale groups, half a superblock)
+constexpr int kDecodeThreads = 256;  // four wavefronts, each owning its own columns
+constexpr int kWaves = kDecodeThreads / 64;
 
 struct DecodeParams {
     const uint16_t* A;
@@ -51,14 +56,58 @@ struct DecodeParams {
     unsigned* counters;   // [max_blocks][n_tiles] when KS > 1, zero between calls
 };
 
-constexpr int kDecodeThreads = 256;  // four wavefronts, each owning its own columns
+// 16 zero bytes: the source of activation pieces past the end of K
+__device__ const u32x4 kZero16 = {0u, 0u, 0u, 0u};
 
-template <int MT, int NBW, bool OUT_F32>
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void dma16(const void* g, uint8_t* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_wave_base, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// wait until at most `later` stages of OPS loads each are still in flight (later <= D - 2 <= 4)
+template <int D, int OPS>
+__device__ __forceinline__ void wait_stage(int later) {
+    switch (later) {
+        case 0: wait_vmcnt<0>(); break;
+        case 1: wait_vmcnt<(D - 2 >= 1 ? 1 : 0) * OPS>(); break;
+        case 2: wait_vmcnt<(D - 2 >= 2 ? 2 : 0) * OPS>(); break;
+        case 3: wait_vmcnt<(D - 2 >= 3 ? 3 : 0) * OPS>(); break;
+        default: wait_vmcnt<(D - 2 >= 4 ? 4 : 0) * OPS>(); break;
+    }
+}
+
+// Barrier between stages.  __syncthreads() would also drain every direct load still in flight (the
+// workgroup release fence counts them as pending LDS writes), which would empty the ring; instead each
+// wavefront has already waited for its own loads of the stage, and here only its LDS reads of the previous
+// stage must be complete before another wavefront refills that slot.
+__device__ __forceinline__ void stage_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt untouched
+    __builtin_amdgcn_s_barrier();
+    __asm__ __volatile__("" ::: "memory");  // no LDS access moves across the barrier
+}
+
+template <int MT, int NBW>
+struct DecodeLds {
+    static constexpr int BM = 16 * MT;
+    static constexpr int X_BYTES = BM * KT * 2;                 // one activation stage
+    static constexpr int W_BYTES = NBW * 1024 + 1024;           // one wavefront's codes of one stage + scale rows
+    static constexpr int SLOT = X_BYTES + kWaves * W_BYTES;
+};
+
+template <int MT, int NBW, int D, bool OUT_F32>
 __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_kernel(DecodeParams p) {
-    constexpr int BM = 16 * MT;
-    constexpr int CHUNKS = BM * (KT / 8);        // 16-byte pieces of one activation stage
-    constexpr int XR = CHUNKS / kDecodeThreads;  // pieces per thread (exact: CHUNKS = 256 * MT)
-    __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * LDX];
+    using Lay = DecodeLds<MT, NBW>;
+    constexpr int BM = Lay::BM;
+    constexpr int OPS = MT + NBW + 1;  // direct loads a wavefront issues per stage
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ int srow[BM];
     __shared__ int ssid[BM];
     __shared__ int s_last;
@@ -68,57 +117,67 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_kernel(DecodeParam
     if (e < 0 || e >= p.sh.E) return;  // unowned block (or ids from a larger expert count)
     const Shape sh = p.sh;
     const int K = sh.K;
-    constexpr int WN = kDecodeThreads / 64;
     const int w = threadIdx.x >> 6, L = threadIdx.x & 63;
     const int c = L >> 4, j = L & 15;
-    const int nbw0 = (blockIdx.y * WN + w) * NBW;  // first n-block of this wavefront
+    const int nbw0 = (blockIdx.y * kWaves + w) * NBW;  // first n-block of this wavefront
     const int KS = gridDim.z, ks = blockIdx.z;
     const int nst = (sh.G + 3) / 4;
     const int st_begin = (int)((long)ks * nst / KS), st_end = (int)((long)(ks + 1) * nst / KS);
 
-    for (int m = threadIdx.x; m < BM; m += blockDim.x) {
+    for (int m = threadIdx.x; m < BM; m += kDecodeThreads) {
         const int sid = p.sorted_ids[b * BM + m];
         ssid[m] = sid < p.R ? sid : -1;
         srow[m] = sid < p.R ? sid / p.a_row_div : -1;
     }
     __syncthreads();
 
-    // per-wavefront packed superblock rows (clamped n-blocks compute discarded columns)
+    // per-lane sources of the activation pieces: piece r of this wavefront covers row
+    // m = 4*(w*MT + r) + L/16 and LDS chunk L%16, which holds global chunk (L%16) ^ (m%16).
+    // A sentinel row reads a valid row instead (rows are independent; its results are discarded).
+    const int any_row = srow[0] >= 0 ? srow[0] : 0;
+    const uint16_t* xsrc[MT];
+#pragma unroll
+    for (int r = 0; r < MT; ++r) {
+        const int m = 4 * (w * MT + r) + (L >> 4);
+        const int row = srow[m] >= 0 ? srow[m] : any_row;
+        const int ch = (L & 15) ^ (m & 15);
+        xsrc[r] = p.A + (size_t)row * K + ch * 8;
+    }
     const uint8_t* wbase[NBW];
 #pragma unroll
     for (int q = 0; q < NBW; ++q) {
-        const int nb = nbw0 + q < sh.NB ? nbw0 + q : sh.NB - 1;
+        const int nb = nbw0 + q < sh.NB ? nbw0 + q : sh.NB - 1;  // clamp: result discarded when out of range
         wbase[q] = p.packed + ((size_t)e * sh.NB + nb) * sh.KB * SB_BYTES;
     }
 
-    auto load_x = [&](int st, u32x4* regs) {
+    // this lane's scale row for the gathered scale load (see issue())
+    const uint8_t* sbase;
+    {
+        const int ql = (L >> 4) < NBW ? (L >> 4) : NBW - 1;
+        const int nb = nbw0 + ql < sh.NB ? nbw0 + ql : sh.NB - 1;
+        sbase = p.packed + ((size_t)e * sh.NB + nb) * sh.KB * SB_BYTES + SB_CODE_BYTES + (L & 15) * 16;
+    }
+
+    auto slot_of = [&](int st) { return smem + (size_t)((st - st_begin) % D) * Lay::SLOT; };
+    // issue this wavefront's direct loads of stage st (OPS instructions, in a fixed order)
+    auto issue = [&](int st) {
+        uint8_t* sl = slot_of(st);
 #pragma unroll
-        for (int r = 0; r < XR; ++r) {
-            const int x = threadIdx.x + r * kDecodeThreads;
-            const int m = x >> 4, ch = x & 15;
-            const int k0 = st * KT + ch * 8;
-            const int row = srow[m];
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (row >= 0 && k0 < K) v = *reinterpret_cast<const u32x4*>(p.A + (size_t)row * K + k0);
-            regs[r] = v;
+        for (int r = 0; r < MT; ++r) {
+            const int k0 = st * KT + ((L & 15) ^ ((4 * (w * MT + r) + (L >> 4)) & 15)) * 8;
+            const void* src = k0 < K ? (const void*)(xsrc[r] + st * KT) : (const void*)&kZero16;
+            dma16(src, sl + (4 * (w * MT + r)) * (KT * 2));
         }
-    };
-    auto store_x = [&](uint16_t* buf, const u32x4* regs) {
-#pragma unroll
-        for (int r = 0; r < XR; ++r) {
-            const int x = threadIdx.x + r * kDecodeThreads;
-            const int m = x >> 4, ch = x & 15;
-            *reinterpret_cast<u32x4*>(&buf[m * LDX + ch * 8]) = regs[r];
-        }
-    };
-    auto load_w = [&](int st, u32x4* cw, u32x4* sc) {
         const int kb = st >> 1, h = st & 1;
+        uint8_t* wsl = sl + Lay::X_BYTES + w * Lay::W_BYTES;
 #pragma unroll
         for (int q = 0; q < NBW; ++q) {
             const uint8_t* sbp = wbase[q] + (size_t)kb * SB_BYTES;
-            cw[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sbp + h * 1024 + L * 16));
-            sc[q] = *reinterpret_cast<const u32x4*>(sbp + SB_CODE_BYTES + j * 16);
+            dma16(sbp + h * 1024 + L * 16, wsl + q * 1024);
         }
+        // one full-wavefront load gathers the scale rows of all its n-blocks: lane L takes row L%16 of
+        // n-block L/16 (lanes past NBW*16 repeat the last n-block); rows land at (q*16 + j)*16
+        dma16(sbase + (size_t)kb * SB_BYTES, wsl + NBW * 1024);
     };
 
     f32x4 acc[MT][NBW];
@@ -129,65 +188,52 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_kernel(DecodeParam
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     const bf16x8 m136 = minus136();
 
-    // one scale group: gate the whole group on a uniform predicate only for a ragged last stage
-    auto group = [&](const uint16_t* buf, int g, int gs, const u32x4* cw, const u32x4* sc) {
-        bf16x8 xf[MT];
-        f32x4 xc[MT];
+    // prologue: stages st_begin .. st_begin+D-2 in flight
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            xf[mt] = *reinterpret_cast<const bf16x8*>(&buf[(mt * 16 + j) * LDX + 32 * g + 8 * c]);
-            xc[mt] = mfma16(xf[mt], m136, zero);
-        }
+    for (int d = 0; d < D - 1; ++d)
+        if (st_begin + d < st_end) issue(st_begin + d);
+
+    for (int st = st_begin; st < st_end; ++st) {
+        // wait for this wavefront's loads of stage st: the loads of later stages may stay in flight
+        wait_stage<D, OPS>(min(D - 2, st_end - 1 - st));
+        stage_barrier();  // every wavefront's pieces of the tile have landed; slot of stage st-1 is free
+        if (st + D - 1 < st_end) issue(st + D - 1);
+
+        const uint8_t* sl = slot_of(st);
+        const uint8_t* wsl = sl + Lay::X_BYTES + w * Lay::W_BYTES;
+        u32x4 cw[NBW], sc[NBW];
 #pragma unroll
         for (int q = 0; q < NBW; ++q) {
-            const bf16x8 wf = biased_codes(cw[q][g]);
-            const float s = group_scale(sc[q], gs);
+            cw[q] = *reinterpret_cast<const u32x4*>(wsl + q * 1024 + L * 16);
+            sc[q] = *reinterpret_cast<const u32x4*>(wsl + NBW * 1024 + (q * 16 + j) * 16);
+        }
+        const int g0 = (st & 1) * 4;
+        // a ragged last stage computes its padding groups too: their codes are 8 and scales 0 in the packed
+        // image and their activations are zero, so they add exactly zero
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            bf16x8 xf[MT];
+            f32x4 xc[MT];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const f32x4 d = mfma16(xf[mt], wf, xc[mt]);
-                acc[mt][q] += s * d;
+                const int row = mt * 16 + j;
+                xf[mt] = *reinterpret_cast<const bf16x8*>(sl + row * (KT * 2) + (((4 * g + c) ^ j) * 16));
+                xc[mt] = mfma16(xf[mt], m136, zero);
+            }
+#pragma unroll
+            for (int q = 0; q < NBW; ++q) {
+                const bf16x8 wf = biased_codes(cw[q][g]);
+                const float s = group_scale(sc[q], g0 + g);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const f32x4 d = mfma16(xf[mt], wf, xc[mt]);
+                    acc[mt][q] += s * d;
+                }
             }
         }
-    };
-    // One stage: start the next stage's loads into the other register set, compute this stage, then publish
-    // the next activation tile.  Two named register sets alternate, so no register copy forces the
-    // prefetched loads to complete early.
-    u32x4 xr[XR];
-    auto stage = [&](int st, const u32x4* cw, const u32x4* sc, u32x4* cwn, u32x4* scn) {
-        const bool more = st + 1 < st_end;
-        if (more) {
-            load_x(st + 1, xr);
-            load_w(st + 1, cwn, scn);
-        }
-        const int cur = (st - st_begin) & 1;
-        const uint16_t* buf = xs[cur];
-        const int g0 = (st & 1) * 4;
-        if (st * 4 + 4 <= sh.G) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) group(buf, g, g0 + g, cw, sc);
-        } else {
-            const int ng = sh.G - st * 4;
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-                if (g < ng) group(buf, g, g0 + g, cw, sc);
-        }
-        if (more) store_x(xs[cur ^ 1], xr);
-        __syncthreads();
-    };
-
-    u32x4 cwA[NBW], scA[NBW], cwB[NBW], scB[NBW];
-    if (st_begin < st_end) {
-        load_x(st_begin, xr);
-        load_w(st_begin, cwA, scA);
-        store_x(xs[0], xr);
-    }
-    __syncthreads();
-    for (int st = st_begin; st < st_end; st += 2) {
-        stage(st, cwA, scA, cwB, scB);
-        if (st + 1 < st_end) stage(st + 1, cwB, scB, cwA, scA);
     }
 
-    const int COLS = NBW * 16 * WN;  // columns of the workgroup
+    const int COLS = NBW * 16 * kWaves;  // columns of the workgroup
     if (KS == 1) {
         // lane holds rows 4c + r of each 16-row tile, column j of each of its n-blocks
 #pragma unroll
@@ -247,12 +293,27 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_kernel(DecodeParam
     if (threadIdx.x == 0) __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+#ifndef W4A16_DECODE_LDS_KIB
+#define W4A16_DECODE_LDS_KIB 32
+#endif
+// ring depth per tile shape: as many stages in flight as the LDS budget holds
+template <int MT, int NBW>
+constexpr int ring_depth() {
+    constexpr int d = (W4A16_DECODE_LDS_KIB * 1024) / DecodeLds<MT, NBW>::SLOT;
+    return d > 6 ? 6 : (d < 2 ? 2 : d);
+}
+
 template <int MT, int NBW, bool F32>
 hipError_t launch_t(const GemmArgs& a, const w4a16_plan& pl, hipStream_t s) {
+    constexpr int D = ring_depth<MT, NBW>();
+    constexpr size_t shmem = (size_t)D * DecodeLds<MT, NBW>::SLOT;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_decode_kernel<MT, NBW, D, F32>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    if (attr != hipSuccess) return attr;
     DecodeParams p{a.A, a.a_row_div, static_cast<const uint8_t*>(a.packed), a.sh, a.sorted_ids, a.expert_ids, a.R,
                    a.out, a.partials, a.counters};
     const dim3 grid(a.max_blocks, decode_n_tiles(a.sh, pl), pl.k_split);
-    hipLaunchKernelGGL((gemm_decode_kernel<MT, NBW, F32>), grid, dim3(kDecodeThreads), 0, s, p);
+    hipLaunchKernelGGL((gemm_decode_kernel<MT, NBW, D, F32>), grid, dim3(kDecodeThreads), shmem, s, p);
     return hipGetLastError();
 }
 

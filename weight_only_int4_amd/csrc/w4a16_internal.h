@@ -5,7 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/w4a16.h"
+#include "w4a16.h"
 
 namespace w4a16 {
 
