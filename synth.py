@@ -166,3 +166,22 @@ def integer_exact_case(rng: np.random.Generator, T: int, E: int, k: int, N: int,
     s = np.full((E, N, K // 32), 0x3D80, np.uint16)  # bf16 bits of 2^-4
     ids = uniform_topk(rng, T, E, k)
     return x, c, s, ids
+
+
+def codes_device(seed: int, E: int, N: int, K: int, device):
+    """Seeded codes generated on the GPU (for weight sets too large to draw on the host): uint8 [E,N,K]."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randint(0, 16, (E, N, K), dtype=torch.uint8, device=device, generator=g)
+
+
+def scales_device(seed: int, E: int, N: int, K: int, device, lo: float = 0.005, hi: float = 0.02):
+    """Seeded BF16 scales uniform in [lo, hi] generated on the GPU: bfloat16 [E,N,K/32]."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    u = torch.rand((E, N, K // 32), dtype=torch.float32, device=device, generator=g)
+    return (lo + (hi - lo) * u).to(torch.bfloat16)

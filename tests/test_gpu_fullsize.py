@@ -1,0 +1,169 @@
+"""Parity at the full workload sizes, in the launch configurations the benchmark uses, on sampled rows.
+
+Each test runs the HIP path on the whole workload and checks a sample of output rows against the oracle
+computed row by row: for the grouped GEMMs, up to three routes of every active expert (its first, middle and
+last route, so tile edges are covered) against the oracle's binary64 accumulators, to the 5e-3 per-expert
+bar; for the fused MLP, a sample of tokens against the oracle's binary32 accumulators before the final
+rounding, to the derived fused bar.  Rows of non-local routes must keep their poison bytes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import weight_only_int4_amd as w4
+from gpu_util import POISON, bits, check_gemm, f32, i32, poison_bf16, u16
+
+pytestmark = pytest.mark.gpu
+
+FUSED_TOL = 1e-2  # same derivation as the fused-MLP tests: BF16 output rounding plus two chained GEMMs
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    w4.load()
+
+
+def sample_routes(ids, E, per_expert=3):
+    flat = ids.reshape(-1)
+    rows = []
+    for e in np.unique(flat[(flat >= 0) & (flat < E)]):
+        r = np.nonzero(flat == e)[0]
+        rows.extend(sorted({int(r[0]), int(r[len(r) // 2]), int(r[-1])})[:per_expert])
+    bad = np.nonzero((flat < 0) | (flat >= E))[0]
+    rows.extend(bad[:8].tolist())
+    return np.array(sorted(rows), np.int32)
+
+
+def run_case(orc, label, E, N, K, ids, a_row_div, rows_A, codes, scales, expected_rows=0.0):
+    T = ids.shape[0]
+    k = ids.shape[1]
+    rng = np.random.default_rng(N + K + T)
+    A = synth.activations(rng, rows_A, K)
+    w = w4.pack_weights(torch.from_numpy(codes).cuda(), u16(scales))
+    plan = w4.plan_select(T, k, E, N, K, expected_rows)
+    _say("%s: %r" % (label, plan))
+    route = w4.route_prep(i32(ids), E, plan.block_m)
+    out = poison_bf16(route["R"], N)
+    w4.grouped_gemm(u16(A), a_row_div, w, route, plan, out=out)
+    got = bits(out)
+    rows = sample_routes(ids, E)
+    acc, _ = orc.grouped_gemm(A, a_row_div, codes, scales, ids, acc64=True, rows=rows)
+    worst = check_gemm(got, acc, ids, E, rows=rows, label=label)
+    _say("  %d sampled rows, worst ratio %.2e" % (len(rows), worst))
+
+
+@pytest.fixture(scope="module")
+def qwen3_weights():
+    c13, s13 = synth.expert_weights(2, 128, 1536, 2048, salt=1)
+    c2, s2 = synth.expert_weights(2, 128, 2048, 768, salt=2)
+    return c13, s13, c2, s2
+
+
+@pytest.mark.parametrize("T", [1, 8, 64, 512])
+def test_qwen3_gate_up_and_down(orc, qwen3_weights, T):
+    c13, s13, c2, s2 = qwen3_weights
+    ids = synth.qwen3_routes(T)
+    run_case(orc, "qwen3 T%d gate_up" % T, 128, 1536, 2048, ids, 8, T, c13, s13)
+    run_case(orc, "qwen3 T%d down" % T, 128, 2048, 768, ids, 1, T * 8, c2, s2)
+
+
+def test_qwen3_fused_bench_workload(orc, qwen3_weights):
+    """The benchmark's default step: fused expert MLP, Qwen3-30B-A3B-shaped, 64 tokens."""
+    c13, s13, c2, s2 = qwen3_weights
+    T, k, E = 64, 8, 128
+    ids = synth.qwen3_routes(T)
+    rng = synth.rng_for(2, 7)
+    x = synth.activations(rng, T, 2048)
+    tw = rng.uniform(0.1, 1.0, (T, k)).astype(np.float32)
+    tw /= tw.sum(axis=1, keepdims=True)
+    w13 = w4.pack_weights(torch.from_numpy(c13).cuda(), u16(s13))
+    w2 = w4.pack_weights(torch.from_numpy(c2).cuda(), u16(s2))
+    _say("qwen3 fused plans %r" % (w4.fused_moe_plans(T, k, w13, w2),))
+    got = bits(w4.fused_moe(u16(x), i32(ids), f32(tw), w13, w2))
+    sample = np.arange(0, T, 7)
+    orc.fused_moe(x[sample], ids[sample], tw[sample], c13, s13, c2, s2)
+    ref = orc.last_out_acc
+    g = (got[sample].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    worst = max(np.abs(g[i] - ref[i]).max() / np.abs(ref[i]).max() for i in range(len(sample)))
+    _say("  fused worst ratio %.2e over %d tokens" % (worst, len(sample)))
+    assert worst <= FUSED_TOL
+
+
+@pytest.fixture(scope="module")
+def kimi_weights():
+    return synth.expert_weights(3, 48, 4096, 7168, salt=1)
+
+
+@pytest.mark.parametrize("T", [1, 16, 256])
+def test_kimi_decode_share_gate_up(orc, kimi_weights, T):
+    codes, scales = kimi_weights
+    ids = synth.kimi_decode_routes(T)
+    flat = ids.reshape(-1)
+    rows_e = max(float(((flat >= 0) & (flat < 48)).sum()) / 48.0, 1.0 / 48.0)
+    run_case(orc, "kimi decode T%d gate_up" % T, 48, 4096, 7168, ids, 8, T, codes, scales, expected_rows=rows_e)
+
+
+def test_kimi_decode_share_down(orc):
+    codes, scales = synth.expert_weights(3, 48, 7168, 2048, salt=2)
+    ids = synth.kimi_decode_routes(64)
+    flat = ids.reshape(-1)
+    rows_e = float(((flat >= 0) & (flat < 48)).sum()) / 48.0
+    run_case(orc, "kimi decode T64 down", 48, 7168, 2048, ids, 1, 64 * 8, codes, scales, expected_rows=rows_e)
+
+
+def test_kimi_prefill_share_gate_up(orc, kimi_weights):
+    codes, scales = kimi_weights
+    ids = synth.kimi_prefill_routes(8192)
+    flat = ids.reshape(-1)
+    counts = np.bincount(flat[(flat >= 0) & (flat < 48)], minlength=48)
+    assert (counts == 0).sum() >= 4, "the skewed routing leaves experts empty"
+    rows_e = counts.sum() / 48.0
+    run_case(orc, "kimi prefill T8192 gate_up", 48, 4096, 7168, ids, 8, 8192, codes, scales, expected_rows=rows_e)
+
+
+@pytest.fixture(scope="module")
+def deepseek_weights():
+    dev = torch.device("cuda:0")
+    E, H, I = 256, 7168, 2048
+    c13 = synth.codes_device(5001, E, 2 * I, H, dev)
+    s13 = synth.scales_device(5002, E, 2 * I, H, dev)
+    w13 = w4.pack_weights(c13, s13.contiguous().view(torch.bfloat16))
+    c2 = synth.codes_device(5003, E, H, I, dev)
+    s2 = synth.scales_device(5004, E, H, I, dev)
+    w2 = w4.pack_weights(c2, s2.contiguous().view(torch.bfloat16))
+    torch.cuda.synchronize()
+    return dict(c13=c13, s13=s13, c2=c2, s2=s2, w13=w13, w2=w2, E=E, H=H, I=I)
+
+
+@pytest.mark.parametrize("T", [1, 32, 512, 4096])
+def test_deepseek_fused(orc, deepseek_weights, T):
+    d = deepseek_weights
+    E, H, I = d["E"], d["H"], d["I"]
+    ids, tw = synth.deepseek_router(T)
+    rng = synth.rng_for(5, 7 + T)
+    x = synth.activations(rng, T, H)
+    _say("deepseek T%d fused plans %r" % (T, w4.fused_moe_plans(T, 8, d["w13"], d["w2"])))
+    got = bits(w4.fused_moe(u16(x), i32(ids), f32(tw), d["w13"], d["w2"]))
+    sample = np.unique(np.linspace(0, T - 1, min(T, 6)).astype(int))
+    # the oracle gets only the experts the sampled tokens use (input data copied from the device)
+    used = np.unique(ids[sample])
+    remap = {int(e): i for i, e in enumerate(used)}
+    sub_ids = np.vectorize(lambda e: remap[int(e)])(ids[sample]).astype(np.int32)
+    ue = torch.from_numpy(used).cuda().long()
+    c13 = d["c13"][ue].cpu().numpy()
+    s13 = d["s13"][ue].view(torch.int16).cpu().numpy().view(np.uint16)
+    c2 = d["c2"][ue].cpu().numpy()
+    s2 = d["s2"][ue].view(torch.int16).cpu().numpy().view(np.uint16)
+    orc.fused_moe(x[sample], sub_ids, tw[sample], c13, s13, c2, s2)
+    ref = orc.last_out_acc
+    g = (got[sample].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    worst = max(np.abs(g[i] - ref[i]).max() / np.abs(ref[i]).max() for i in range(len(sample)))
+    _say("  deepseek T%d fused worst ratio %.2e over %d tokens" % (T, worst, len(sample)))
+    assert worst <= FUSED_TOL
