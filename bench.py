@@ -2,8 +2,8 @@
 """Benchmark of the W4A16 MoE hot path on one MI355X.
 
 One step = one fused expert-MLP call on synthetic inputs already resident in
-HBM: routing preparation, gate_up grouped GEMM, SiLU*mul, down grouped GEMM
-and the weighted top-k combine.  The default workload is the
+HBM: routing preparation, gate_up grouped GEMM with SiLU*mul in its epilogue,
+down grouped GEMM and the weighted top-k combine.  The default workload is the
 Qwen3-30B-A3B-shaped layer (128 experts, top-8, hidden 2048, intermediate
 768) at 64 tokens, a decode batch with 4 routed rows per expert.
 
@@ -13,9 +13,11 @@ weights come from HBM as they would in serving.
 
 Prints one JSON line: the metric (effective weight GB/s of the step, i.e.
 packed weight bytes of the experts that received a route divided by the step
-time), the roofline of the dominant kernel (the gate_up GEMM, timed with HIP
-events around its launch inside every timed step), and the CPU oracle timed
-on the host on a bounded sample of the same workload.
+time, from HIP-graph replays of the fused call), the roofline of the dominant
+kernel (the gate_up GEMM, timed with HIP events recorded between the stages of
+as many eager calls of the same step, queued behind a GPU sleep so that the
+events bracket GPU work only), and the CPU oracle timed on the host on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -35,6 +37,7 @@ import numpy as np  # noqa: E402
 METRIC = "us/call + effective weight GB/s (% HBM peak), W4A16 MoE grouped GEMM"
 HBM_PEAK_GBS = 8000.0
 ROTATION_BYTES = 1 << 30
+COPY_CAL_BYTES = 256 << 20
 
 
 def workload_spec(name: str) -> dict:
@@ -121,6 +124,9 @@ def main():
     ap.add_argument("--workload", default="qwen3-moe-t64")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one elementwise copy of 256 MiB (read 256 MiB, write 256 MiB) before the steps: "
+                         "the reference dispatch that scales hardware byte counters to bytes")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -167,6 +173,12 @@ def main():
           % (p13, p2, len(active), Rv, ncopies, per_copy / 1e6), file=sys.stderr, flush=True)
 
     lib = L.load()
+    if args.copy_calibration:
+        src = torch.ones(COPY_CAL_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     def fused_args(c, stream):
         a, b = copies[c]
@@ -209,7 +221,8 @@ def main():
         e.record(stream)  # create the underlying HIP event now
         return e
 
-    events = [[ev() for _ in range(6)] for _ in range(args.steps)]
+    NS = len(L.FUSED_STAGES)
+    events = [[ev() for _ in range(NS + 1)] for _ in range(args.steps)]
     arrays = [ctypes_array(e) for e in events]  # (pointer, keep-alive array)
     for c in range(ncopies):
         check(lib.w4a16_fused_moe_profiled(*fused_args(c, stream), arrays[0][0]))
@@ -218,19 +231,21 @@ def main():
     for i in range(args.steps):
         check(lib.w4a16_fused_moe_profiled(*fused_args(i % ncopies, stream), arrays[i][0]))
     torch.cuda.synchronize()
-    stage = np.array([[events[i][s].elapsed_time(events[i][s + 1]) * 1e3 for s in range(5)] for i in range(args.steps)])
-    gpu_step_us = float(np.mean([events[i][0].elapsed_time(events[i][5]) * 1e3 for i in range(args.steps)]))
+    stage = np.array([[events[i][s].elapsed_time(events[i][s + 1]) * 1e3 for s in range(NS)] for i in range(args.steps)])
+    gpu_step_us = float(np.mean([events[i][0].elapsed_time(events[i][NS]) * 1e3 for i in range(args.steps)]))
     gate_up_us = float(stage[:, 1].mean())
     value = weight_bytes_step / (ms_per_step * 1e-3) / 1e9
 
-    # dominant kernel: gate_up grouped GEMM (decode or prefill kernel by plan)
+    # dominant kernel: gate_up grouped GEMM with the SiLU*mul epilogue (decode or prefill kernel by plan).
+    # Algorithmic bytes: packed weights of the active experts, x once, h written once, routing read once.
     maxP, maxB = L.route_bounds(T, k, E, p13.block_m)
-    alg_bytes = len(active) * wb13 + T * H * 2 + Rv * 2 * I * 4 + (maxP + maxB) * 4
+    alg_bytes = len(active) * wb13 + T * H * 2 + Rv * I * 2 + (maxP + maxB) * 4
     achieved = alg_bytes / (gate_up_us * 1e-6) / 1e9
-    kname = "gemm_%s_kernel<MT=%d,NBW=%d,f32 out> (gate_up, %d waves)" % (
-        "decode" if p13.kernel == L.KERNEL_DECODE else "prefill", p13.block_m // 16, p13.n_blocks, p13.waves)
+    kname = "gemm_%s_kernel<MT=%d,NBW=%d,act out> (gate_up + silu_mul, %d waves, k_split %d)" % (
+        "decode" if p13.kernel == L.KERNEL_DECODE else "prefill", p13.block_m // 16, p13.n_blocks, p13.waves,
+        p13.k_split)
 
-    stages = ["route_prep", "gate_up", "silu_mul", "down", "combine"]
+    stages = list(L.FUSED_STAGES)
     print("[bench] step %.1f us wall (graph replay), %.1f us GPU events; per stage (us): %s" % (
         ms_per_step * 1e3, gpu_step_us, ", ".join("%s %.1f" % (n, v) for n, v in zip(stages, stage.mean(0)))),
         file=sys.stderr, flush=True)

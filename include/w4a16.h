@@ -189,6 +189,23 @@ int w4a16_grouped_gemm_f32(const uint16_t* A, int a_row_div, const w4a16_weights
                            const int32_t* expert_ids, const int32_t* num_tokens_padded, int R,
                            const w4a16_plan* p, float* out, void* ws, size_t ws_bytes, hipStream_t s);
 
+/* Gate/up projection with the expert MLP's activation in its epilogue
+ * (humans& page, "Dedicated warps keep the pipeline busy": FC1 followed by
+ * the activation; SiLU-gated MLP as in the DeepSeek-V3 and Qwen3 MoE layers):
+ * w13 holds [E, 2I, K] weights, gate rows [0, I) then up rows [I, 2I), and
+ *   h[i, c] = bf16( silu(g) * u ),  silu(g) = g / (1 + exp(-g)),  c < I,
+ *   g = sum_k A[i / a_row_div, k] * w13[e, c, k],
+ *   u = sum_k A[i / a_row_div, k] * w13[e, I + c, k],
+ * g and u accumulated in binary32 and never rounded; the activation is formed
+ * in binary32 and rounded once to nearest even.  Exactly
+ * w4a16_grouped_gemm_f32 followed by w4a16_silu_mul_f32, without the [R, 2I]
+ * intermediate.  h device BF16 bits [R, I]; other arguments and the workspace
+ * as for w4a16_grouped_gemm.  Needs 2I a multiple of 32 and
+ * p->n_blocks >= 2 (UNSUPPORTED_SHAPE otherwise). */
+int w4a16_grouped_gemm_silu(const uint16_t* A, int a_row_div, const w4a16_weights* w13, const int32_t* sorted_ids,
+                            const int32_t* expert_ids, const int32_t* num_tokens_padded, int R,
+                            const w4a16_plan* p, uint16_t* h, void* ws, size_t ws_bytes, hipStream_t s);
+
 /* Offsets-form grouped GEMM (nf4 page, "Usage": x sorted by expert, offsets =
  * cumulative rows per expert): rows [expert_offsets[e], expert_offsets[e+1])
  * of A_sorted belong to expert e, and
@@ -221,11 +238,11 @@ int w4a16_silu_mul_f32(const float* gu, int rows, int I, uint16_t* h, hipStream_
 int w4a16_moe_combine(const float* y, const float* topk_w, const int32_t* topk_ids, int T, int k, int E,
                       int H, uint16_t* out, hipStream_t s);
 
-/* Fused expert MLP: route_prep -> gate_up GEMM -> SiLU*mul -> down GEMM ->
+/* Fused expert MLP: route_prep -> gate_up GEMM with SiLU*mul -> down GEMM ->
  * weighted top-k combine.  It is exactly the sequence w4a16_route_prep,
- * w4a16_grouped_gemm_f32 (gate_up, a_row_div = k), w4a16_silu_mul_f32,
- * w4a16_grouped_gemm_f32 (down, a_row_div = 1), w4a16_moe_combine, with the
- * plans of w4a16_fused_moe_plans and the buffers carved from ws.
+ * w4a16_grouped_gemm_silu (a_row_div = k), w4a16_grouped_gemm_f32 (down,
+ * a_row_div = 1), w4a16_moe_combine, with the plans of
+ * w4a16_fused_moe_plans and the buffers carved from ws.
  *   x       device BF16 bits [T,H]
  *   w13     handle of [E, 2I, H] weights, gate rows first then up rows
  *   w2      handle of [E, H, I] weights
@@ -240,7 +257,7 @@ int w4a16_fused_moe_workspace_bytes(int T, int k, const w4a16_weights* w13, cons
                                     size_t* bytes);
 
 /* The two plans w4a16_fused_moe uses (they share block_m, hence one set of
- * routing tensors). */
+ * routing tensors; the gate_up plan has n_blocks >= 2). */
 int w4a16_fused_moe_plans(int T, int k, const w4a16_weights* w13, const w4a16_weights* w2, w4a16_plan* gate_up,
                           w4a16_plan* down);
 
@@ -249,8 +266,8 @@ int w4a16_fused_moe(const uint16_t* x, const int32_t* topk_ids, const float* top
                     size_t ws_bytes, hipStream_t s);
 
 /* w4a16_fused_moe that also records caller-created events on the stream
- * between its stages: stage_events[0] before routing, [1] before gate_up,
- * [2] before the activation, [3] before down, [4] before the combine and [5]
+ * between its stages: stage_events[0] before routing, [1] before gate_up
+ * (with the activation), [2] before down, [3] before the combine and [4]
  * after it (NULL = no events, identical to w4a16_fused_moe).  For per-stage
  * timing of eager calls; nothing else differs. */
 int w4a16_fused_moe_profiled(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, int T, int k,

@@ -68,3 +68,40 @@ def check_gemm(got_bits: np.ndarray, ref_acc: np.ndarray, topk_flat: np.ndarray,
     if inv.size:
         assert np.all(got_bits[inv] == POISON), "%s: a row of a non-local route was written" % label
     return worst
+
+
+def silu(g):
+    return g / (1.0 + np.exp(-g))
+
+
+def check_act(got_bits: np.ndarray, gu_ref: np.ndarray, topk_flat: np.ndarray, E: int, rows=None,
+              tol: float = TOL, label: str = ""):
+    """SiLU*mul output h against the oracle's binary64 gate/up accumulators gu_ref [R, 2I].
+
+    The bar follows from the GEMM bar: per expert block the gate and up values may each be off by
+    dg = tol * max|g| and du = tol * max|u| (max over the block), and silu has slope at most 1.1, so
+        |h - silu(g) u| <= 1.1 |u| dg + (|silu(g)| + 1.1 dg) du + 2^-8 |h|
+    elementwise, the last term being the BF16 rounding of h.  A gate/up column mix-up or a wrong row
+    exceeds it by about 1/tol.  Rows of non-local routes must keep their poison."""
+    ids = np.asarray(topk_flat).reshape(-1)
+    R = ids.size
+    I = gu_ref.shape[1] // 2
+    valid = (ids >= 0) & (ids < E)
+    check_rows = np.arange(R) if rows is None else np.asarray(rows)
+    worst = 0.0
+    for e in np.unique(ids[check_rows][valid[check_rows]]):
+        rr = check_rows[ids[check_rows] == e]
+        g, u = gu_ref[rr, :I], gu_ref[rr, I:]
+        h = bf16_to_f64(got_bits[rr])
+        assert not np.any(np.isnan(h)), "%s expert %d: unwritten (poison) output in a routed row" % (label, e)
+        dg, du = tol * np.abs(g).max(), tol * np.abs(u).max()
+        ref = silu(g) * u
+        bound = 1.1 * np.abs(u) * dg + (np.abs(silu(g)) + 1.1 * dg) * du + 2.0 ** -8 * np.abs(ref) + 1e-30
+        err = np.abs(h - ref)
+        worst = max(worst, float((err / bound).max()))
+        assert np.all(err <= bound), "%s expert %d: activation error beyond the derived bound (worst %.3g x)" % (
+            label, e, (err / bound).max())
+    inv = check_rows[~valid[check_rows]]
+    if inv.size:
+        assert np.all(got_bits[inv] == POISON), "%s: a row of a non-local route was written" % label
+    return worst

@@ -12,7 +12,7 @@ import torch
 
 import synth
 import weight_only_int4_amd as w4
-from gpu_util import POISON, bits, check_gemm, f32, i32, poison_bf16, u16
+from gpu_util import POISON, bits, check_act, check_gemm, f32, i32, poison_bf16, u16
 
 pytestmark = pytest.mark.gpu
 
@@ -57,6 +57,26 @@ def run_case(orc, label, E, N, K, ids, a_row_div, rows_A, codes, scales, expecte
     acc, _ = orc.grouped_gemm(A, a_row_div, codes, scales, ids, acc64=True, rows=rows)
     worst = check_gemm(got, acc, ids, E, rows=rows, label=label)
     _say("  %d sampled rows, worst ratio %.2e" % (len(rows), worst))
+
+
+def run_silu_case(orc, label, E, N, K, ids, a_row_div, rows_A, codes, scales, expected_rows=0.0):
+    """gate_up with the SiLU*mul epilogue on sampled routes, against the oracle's binary64 gate/up values."""
+    T, k = ids.shape
+    rng = np.random.default_rng(N + K + T + 1)
+    A = synth.activations(rng, rows_A, K)
+    w = w4.pack_weights(torch.from_numpy(codes).cuda(), u16(scales))
+    plan = w4.plan_select(T, k, E, N, K, expected_rows)
+    if plan.n_blocks < 2:
+        plan.n_blocks = 2
+    _say("%s: %r" % (label, plan))
+    route = w4.route_prep(i32(ids), E, plan.block_m)
+    h = poison_bf16(route["R"], N // 2)
+    w4.grouped_gemm_silu(u16(A), a_row_div, w, route, plan, out=h)
+    got = bits(h)
+    rows = sample_routes(ids, E)
+    gu, _ = orc.grouped_gemm(A, a_row_div, codes, scales, ids, acc64=True, rows=rows)
+    worst = check_act(got, gu, ids, E, rows=rows, label=label)
+    _say("  %d sampled rows, worst error / bound %.2f" % (len(rows), worst))
 
 
 @pytest.fixture(scope="module")
@@ -108,6 +128,25 @@ def test_kimi_decode_share_gate_up(orc, kimi_weights, T):
     flat = ids.reshape(-1)
     rows_e = max(float(((flat >= 0) & (flat < 48)).sum()) / 48.0, 1.0 / 48.0)
     run_case(orc, "kimi decode T%d gate_up" % T, 48, 4096, 7168, ids, 8, T, codes, scales, expected_rows=rows_e)
+
+
+@pytest.mark.parametrize("T", [1, 64])
+def test_kimi_decode_share_gate_up_silu(orc, kimi_weights, T):
+    codes, scales = kimi_weights
+    ids = synth.kimi_decode_routes(T)
+    flat = ids.reshape(-1)
+    rows_e = max(float(((flat >= 0) & (flat < 48)).sum()) / 48.0, 1.0 / 48.0)
+    run_silu_case(orc, "kimi decode T%d gate_up+silu" % T, 48, 4096, 7168, ids, 8, T, codes, scales,
+                  expected_rows=rows_e)
+
+
+def test_kimi_prefill_share_gate_up_silu(orc, kimi_weights):
+    codes, scales = kimi_weights
+    ids = synth.kimi_prefill_routes(8192)
+    flat = ids.reshape(-1)
+    rows_e = float(((flat >= 0) & (flat < 48)).sum()) / 48.0
+    run_silu_case(orc, "kimi prefill T8192 gate_up+silu", 48, 4096, 7168, ids, 8, 8192, codes, scales,
+                  expected_rows=rows_e)
 
 
 def test_kimi_decode_share_down(orc):

@@ -11,7 +11,7 @@ import torch
 
 import synth
 import weight_only_int4_amd as w4
-from gpu_util import POISON, bits, check_gemm, f32, i32, poison_bf16, u8, u16
+from gpu_util import POISON, bits, check_act, check_gemm, f32, i32, poison_bf16, u8, u16
 
 pytestmark = pytest.mark.gpu
 
@@ -247,6 +247,54 @@ def test_gemm_offsets_form(orc, plan_args):
     check_gemm(got, acc, expert_of_row, E, label="offsets")
 
 
+# ------------------------------------------------------------------ gate_up GEMM with the activation epilogue
+
+ACT_PLANS = [("decode", 16, 2, 4, 1), ("decode", 16, 4, 4, 1), ("decode", 48, 4, 4, 1), ("decode", 32, 4, 4, 2),
+             ("decode", 64, 2, 4, 3), ("prefill", 64, 2, 4, 1), ("prefill", 64, 4, 4, 1), ("prefill", 128, 4, 4, 1),
+             ("prefill", 128, 2, 4, 1)]
+
+
+@pytest.mark.parametrize("plan_args", ACT_PLANS, ids=PLAN_ID)
+@pytest.mark.parametrize("shape", [(40, 6, 2, 256, 128), (33, 5, 2, 288, 48), (7, 3, 1, 96, 16),
+                                   (100, 4, 3, 512, 96)], ids=lambda s: "T%d-E%d-k%d-K%d-I%d" % s)
+def test_gemm_silu(orc, plan_args, shape):
+    """h = bf16(silu(g) * u) straight from the gate/up accumulators: against the oracle's binary64 gate/up
+    values under the bound derived from the GEMM bar, and bit for bit against the two-step path (binary32
+    GEMM output, then silu_mul_f32) with the same plan, whose accumulation order is the same."""
+    T, E, k, K, I = shape
+    _say("gemm_silu %s %s" % (shape, plan_args))
+    rng = np.random.default_rng(31 + T + I)
+    x = synth.activations(rng, T, K)
+    c13, s13 = synth.codes(rng, E, 2 * I, K), synth.scales(rng, E, 2 * I, K)
+    ids = synth.uniform_topk(rng, T, E + 1, k) - 1          # some routes are -1 (not local)
+    w13 = _pack(c13, s13)
+    plan = w4.make_plan(*plan_args)
+    route = w4.route_prep(i32(ids), E, plan.block_m)
+    h = poison_bf16(T * k, I)
+    w4.grouped_gemm_silu(u16(x), k, w13, route, plan, out=h)
+    got = bits(h)
+    gu_ref, _ = orc.grouped_gemm(x, k, c13, s13, ids, acc64=True)
+    worst = check_act(got, gu_ref, ids.reshape(-1), E, label="gemm_silu")
+    _say("  worst error / bound %.2f" % worst)
+    gu = w4.grouped_gemm(u16(x), k, w13, route, plan, out_f32=True)
+    two_step = bits(w4.silu_mul(gu))
+    valid = ids.reshape(-1) >= 0
+    assert np.array_equal(got[valid], two_step[valid]), "fused epilogue differs from GEMM + silu_mul_f32"
+
+
+def test_gemm_silu_rejects_unpaired_plans():
+    rng = np.random.default_rng(2)
+    E, K = 2, 128
+    ids = np.zeros((4, 1), np.int32)
+    x = synth.activations(rng, 4, K)
+    for N, plan_args in ((64, ("decode", 16, 1, 4, 1)), (48, ("decode", 16, 2, 4, 1))):
+        w = _pack(synth.codes(rng, E, N, K), synth.scales(rng, E, N, K))
+        plan = w4.make_plan(*plan_args)
+        route = w4.route_prep(i32(ids), E, plan.block_m)
+        with pytest.raises(w4.W4A16Error, match="n_blocks|multiple of 32"):
+            w4.grouped_gemm_silu(u16(x), 1, w, route, plan)
+
+
 # ------------------------------------------------------------------ activation, combine, fused MLP
 
 def test_silu_mul(orc):
@@ -313,10 +361,9 @@ def test_fused_moe(orc, shape):
     gu_ref, _ = orc.grouped_gemm(x, k, c13, s13, ids, acc64=True)
     gu_bits = (gu.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)  # only for the poison check
     check_gemm_f32(gu, gu_ref, flat, E, "gate_up")
-    gu32 = orc.grouped_gemm(x, k, c13, s13, ids)[0]            # oracle's binary32 gate/up accumulators
-    h_gpu = bits(w4.silu_mul(f32(np.nan_to_num(gu32, nan=0.0).astype(np.float32))))
-    hd = np.abs(orc_bf16_to_f64(h_gpu[valid]) - orc_bf16_to_f64(h_ref[valid]))
-    assert np.all(hd <= np.abs(orc_bf16_to_f64(h_ref[valid])) * 2.0 ** -7 + 1e-30), "activation beyond one ulp"
+    h_gpu = poison_bf16(T * k, I)
+    w4.grouped_gemm_silu(u16(x), k, w13, route, p13, out=h_gpu)  # the gate_up stage of the fused call
+    check_act(bits(h_gpu), gu_ref, flat, E, label="gate_up + silu")
     y = w4.grouped_gemm(u16(h_ref), 1, w2, route, p2, out_f32=True).cpu().numpy().astype(np.float64)
     y_ref64, _ = orc.grouped_gemm(h_ref, 1, c2, s2, ids, acc64=True)
     check_gemm_f32(y, y_ref64, flat, E, "down")

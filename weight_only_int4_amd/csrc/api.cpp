@@ -191,7 +191,7 @@ hipError_t run_gemm(const GemmArgs& a, const w4a16_plan& p, hipStream_t s) {
 // Workspace carve-up of the fused expert MLP.
 struct FusedLayout {
     int maxP, maxB;
-    size_t off_sorted, off_eids, off_ntp, off_offsets, off_counts, off_gu, off_h, off_y, off_split, total;
+    size_t off_sorted, off_eids, off_ntp, off_offsets, off_counts, off_h, off_y, off_split, total;
 };
 
 // The split-K area goes first so its counters sit at a fixed place regardless of the route block.
@@ -206,7 +206,6 @@ FusedLayout fused_layout(int T, int k, int E, int H, int I, int BM, size_t split
     f.off_ntp = o;    o = align_up(o + sizeof(int32_t), 256);
     f.off_offsets = o; o = align_up(o + sizeof(int32_t) * (size_t)(E + 1), 256);
     f.off_counts = o; o = align_up(o + sizeof(int32_t) * (size_t)E, 256);
-    f.off_gu = o;     o = align_up(o + sizeof(float) * R * 2 * I, 256);
     f.off_h = o;      o = align_up(o + sizeof(uint16_t) * R * I, 256);
     f.off_y = o;      o = align_up(o + sizeof(float) * R * H, 256);
     f.total = o;
@@ -363,7 +362,7 @@ int w4a16_gemm_workspace_bytes(const w4a16_plan* p, int R, int E, int N, size_t*
 
 static int grouped_gemm_impl(const char* what, const uint16_t* A, int a_row_div, const w4a16_weights* w,
                              const int32_t* sorted_ids, const int32_t* expert_ids, int R, const w4a16_plan* p,
-                             void* out, int out_f32, void* ws, size_t ws_bytes, hipStream_t s) {
+                             void* out, int out_mode, void* ws, size_t ws_bytes, hipStream_t s) {
     int rc = check_handle(w, what);
     if (rc) return rc;
     rc = validate_plan(p, what);
@@ -373,13 +372,19 @@ static int grouped_gemm_impl(const char* what, const uint16_t* A, int a_row_div,
     if (R % a_row_div) return fail(W4A16_INVALID_ARG, "%s: R=%d not a multiple of a_row_div=%d", what, R, a_row_div);
     if (!A || !sorted_ids || !expert_ids || !out) return fail(W4A16_INVALID_ARG, "%s: NULL pointer argument", what);
     if (!aligned16(A)) return fail(W4A16_INVALID_ARG, "%s: A must be 16-byte aligned", what);
+    if (out_mode == kOutAct) {
+        if (w->shape.N % 32)
+            return fail(W4A16_UNSUPPORTED_SHAPE, "%s: N=%d must be a multiple of 32 (gate and up halves of whole n-blocks)",
+                        what, w->shape.N);
+        if (p->n_blocks < 2) return fail(W4A16_UNSUPPORTED_SHAPE, "%s: plan.n_blocks must be at least 2", what);
+    }
     int maxP, maxB;
     route_bounds(R / a_row_div, a_row_div, w->shape.E, p->block_m, &maxP, &maxB);
     const GemmWs g = gemm_ws(w->shape, *p, maxB);
     if (g.total && (!ws || ws_bytes < g.total))
         return fail(W4A16_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, needs %zu", what, ws_bytes, g.total);
     if (g.total && !aligned16(ws)) return fail(W4A16_INVALID_ARG, "%s: workspace must be 16-byte aligned", what);
-    GemmArgs a{A, a_row_div, w->packed, w->shape, sorted_ids, expert_ids, R, maxB, out, out_f32};
+    GemmArgs a{A, a_row_div, w->packed, w->shape, sorted_ids, expert_ids, R, maxB, out, out_mode};
     bind_ws(a, g, ws, g.counter_bytes);
     return check_launch(run_gemm(a, *p, s), what);
 }
@@ -388,15 +393,23 @@ int w4a16_grouped_gemm(const uint16_t* A, int a_row_div, const w4a16_weights* w,
                        const int32_t* expert_ids, const int32_t* num_tokens_padded, int R, const w4a16_plan* p,
                        uint16_t* out, void* ws, size_t ws_bytes, hipStream_t s) {
     (void)num_tokens_padded;
-    return grouped_gemm_impl("w4a16_grouped_gemm", A, a_row_div, w, sorted_ids, expert_ids, R, p, out, 0, ws, ws_bytes,
-                             s);
+    return grouped_gemm_impl("w4a16_grouped_gemm", A, a_row_div, w, sorted_ids, expert_ids, R, p, out, kOutBf16, ws,
+                             ws_bytes, s);
 }
 
 int w4a16_grouped_gemm_f32(const uint16_t* A, int a_row_div, const w4a16_weights* w, const int32_t* sorted_ids,
                            const int32_t* expert_ids, const int32_t* num_tokens_padded, int R, const w4a16_plan* p,
                            float* out, void* ws, size_t ws_bytes, hipStream_t s) {
     (void)num_tokens_padded;
-    return grouped_gemm_impl("w4a16_grouped_gemm_f32", A, a_row_div, w, sorted_ids, expert_ids, R, p, out, 1, ws,
+    return grouped_gemm_impl("w4a16_grouped_gemm_f32", A, a_row_div, w, sorted_ids, expert_ids, R, p, out, kOutF32, ws,
+                             ws_bytes, s);
+}
+
+int w4a16_grouped_gemm_silu(const uint16_t* A, int a_row_div, const w4a16_weights* w13, const int32_t* sorted_ids,
+                            const int32_t* expert_ids, const int32_t* num_tokens_padded, int R, const w4a16_plan* p,
+                            uint16_t* h, void* ws, size_t ws_bytes, hipStream_t s) {
+    (void)num_tokens_padded;
+    return grouped_gemm_impl("w4a16_grouped_gemm_silu", A, a_row_div, w13, sorted_ids, expert_ids, R, p, h, kOutAct, ws,
                              ws_bytes, s);
 }
 
@@ -450,7 +463,7 @@ int w4a16_grouped_gemm_offsets(const uint16_t* A_sorted, const int32_t* expert_o
                                               expert_ids, s),
                       what);
     if (rc) return rc;
-    GemmArgs a{A_sorted, 1, w->packed, w->shape, sorted_ids, expert_ids, rows_max, maxB, out, 0};
+    GemmArgs a{A_sorted, 1, w->packed, w->shape, sorted_ids, expert_ids, rows_max, maxB, out, kOutBf16};
     bind_ws(a, g, ws, g.counter_bytes);
     return check_launch(run_gemm(a, *p, s), what);
 }
@@ -519,6 +532,7 @@ int w4a16_fused_moe_plans(int T, int k, const w4a16_weights* w13, const w4a16_we
     if (rc) return rc;
     rc = w4a16_plan_select(T, k, E, H, I, 0.f, &p2);
     if (rc) return rc;
+    if (p13.n_blocks < 2) p13.n_blocks = 2;  // the activation epilogue pairs a gate and an up n-block
     p2.block_m = p13.block_m;  // both projections share one set of routing tensors
     p2.kernel = p13.kernel;
     if (p2.kernel == W4A16_KERNEL_PREFILL) {
@@ -575,7 +589,6 @@ int w4a16_fused_moe_profiled(const uint16_t* x, const int32_t* topk_ids, const f
     int32_t* ntp = reinterpret_cast<int32_t*>(base + f.off_ntp);
     int32_t* offsets = reinterpret_cast<int32_t*>(base + f.off_offsets);
     int32_t* counts = reinterpret_cast<int32_t*>(base + f.off_counts);
-    float* gu = reinterpret_cast<float*>(base + f.off_gu);
     uint16_t* h = reinterpret_cast<uint16_t*>(base + f.off_h);
     float* y = reinterpret_cast<float*>(base + f.off_y);
     const int R = T * k;
@@ -594,22 +607,19 @@ int w4a16_fused_moe_profiled(const uint16_t* x, const int32_t* topk_ids, const f
                       "w4a16_fused_moe (route_prep)");
     if (rc) return rc;
     W4A16_STAGE(1);
-    GemmArgs g13{x, k, w13->packed, w13->shape, sorted_ids, expert_ids, R, f.maxB, gu, 1};
+    GemmArgs g13{x, k, w13->packed, w13->shape, sorted_ids, expert_ids, R, f.maxB, h, kOutAct};
     bind_ws(g13, gemm_ws(w13->shape, p13, f.maxB), base + f.off_split, counter_bytes);
-    rc = check_launch(run_gemm(g13, p13, s), "w4a16_fused_moe (gate_up)");
+    rc = check_launch(run_gemm(g13, p13, s), "w4a16_fused_moe (gate_up + silu_mul)");
     if (rc) return rc;
     W4A16_STAGE(2);
-    rc = check_launch(launch_silu_mul_f32(gu, R, I, h, s), "w4a16_fused_moe (silu_mul)");
-    if (rc) return rc;
-    W4A16_STAGE(3);
-    GemmArgs g2{h, 1, w2->packed, w2->shape, sorted_ids, expert_ids, R, f.maxB, y, 1};
+    GemmArgs g2{h, 1, w2->packed, w2->shape, sorted_ids, expert_ids, R, f.maxB, y, kOutF32};
     bind_ws(g2, gemm_ws(w2->shape, p2, f.maxB), base + f.off_split, counter_bytes);
     rc = check_launch(run_gemm(g2, p2, s), "w4a16_fused_moe (down)");
     if (rc) return rc;
-    W4A16_STAGE(4);
+    W4A16_STAGE(3);
     rc = check_launch(launch_combine(y, topk_w, topk_ids, T, k, E, H, out, s), "w4a16_fused_moe (combine)");
     if (rc) return rc;
-    W4A16_STAGE(5);
+    W4A16_STAGE(4);
 #undef W4A16_STAGE
     return ok();
 }

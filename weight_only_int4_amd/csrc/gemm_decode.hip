@@ -102,8 +102,24 @@ struct DecodeLds {
     static constexpr int SLOT = X_BYTES + kWaves * W_BYTES;
 };
 
-template <int MT, int NBW, int D, bool OUT_F32>
+// n-block of weight slot q of wavefront w (see kOutAct for the split of slots between gate and up rows);
+// `o` receives the output n-block index it feeds and `valid` whether that block exists
+template <int NBW, int OM>
+__device__ __forceinline__ int slot_nblock(const Shape& sh, int wave_global, int q, int* o) {
+    if (OM == kOutAct) {
+        constexpr int HB = NBW / 2;
+        const int half = sh.NB / 2;
+        *o = wave_global * HB + (q % HB);
+        const int nb = (q < HB ? 0 : half) + *o;
+        return *o < half ? nb : sh.NB - 1;  // clamp: result discarded when out of range
+    }
+    *o = wave_global * NBW + q;
+    return *o < sh.NB ? *o : sh.NB - 1;
+}
+
+template <int MT, int NBW, int D, int OM>
 __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_kernel(DecodeParams p) {
+    static_assert(OM != kOutAct || NBW % 2 == 0, "the activation epilogue pairs gate and up n-blocks");
     using Lay = DecodeLds<MT, NBW>;
     constexpr int BM = Lay::BM;
     constexpr int OPS = MT + NBW + 1;  // direct loads a wavefront issues per stage
@@ -119,7 +135,7 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_kernel(DecodeParam
     const int K = sh.K;
     const int w = threadIdx.x >> 6, L = threadIdx.x & 63;
     const int c = L >> 4, j = L & 15;
-    const int nbw0 = (blockIdx.y * kWaves + w) * NBW;  // first n-block of this wavefront
+    const int wave_global = blockIdx.y * kWaves + w;  // column group of this wavefront
     const int KS = gridDim.z, ks = blockIdx.z;
     const int nst = (sh.G + 3) / 4;
     const int st_begin = (int)((long)ks * nst / KS), st_end = (int)((long)(ks + 1) * nst / KS);
@@ -146,7 +162,8 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_kernel(DecodeParam
     const uint8_t* wbase[NBW];
 #pragma unroll
     for (int q = 0; q < NBW; ++q) {
-        const int nb = nbw0 + q < sh.NB ? nbw0 + q : sh.NB - 1;  // clamp: result discarded when out of range
+        int o;
+        const int nb = slot_nblock<NBW, OM>(sh, wave_global, q, &o);
         wbase[q] = p.packed + ((size_t)e * sh.NB + nb) * sh.KB * SB_BYTES;
     }
 
@@ -154,7 +171,8 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_kernel(DecodeParam
     const uint8_t* sbase;
     {
         const int ql = (L >> 4) < NBW ? (L >> 4) : NBW - 1;
-        const int nb = nbw0 + ql < sh.NB ? nbw0 + ql : sh.NB - 1;
+        int o;
+        const int nb = slot_nblock<NBW, OM>(sh, wave_global, ql, &o);
         sbase = p.packed + ((size_t)e * sh.NB + nb) * sh.KB * SB_BYTES + SB_CODE_BYTES + (L & 15) * 16;
     }
 
@@ -233,7 +251,7 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_kernel(DecodeParam
         }
     }
 
-    const int COLS = NBW * 16 * kWaves;  // columns of the workgroup
+    const int COLS = NBW * 16 * kWaves;  // weight columns of the workgroup
     if (KS == 1) {
         // lane holds rows 4c + r of each 16-row tile, column j of each of its n-blocks
 #pragma unroll
@@ -242,14 +260,25 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_kernel(DecodeParam
             for (int r = 0; r < 4; ++r) {
                 const int sid = ssid[mt * 16 + 4 * c + r];
                 if (sid < 0) continue;
+                if (OM == kOutAct) {
+                    const int NO = sh.N / 2;
 #pragma unroll
-                for (int q = 0; q < NBW; ++q) {
-                    const int n = (nbw0 + q) * 16 + j;
-                    if (nbw0 + q >= sh.NB || n >= sh.N) continue;
-                    if (OUT_F32)
-                        static_cast<float*>(p.out)[(size_t)sid * sh.N + n] = acc[mt][q][r];
-                    else
-                        static_cast<uint16_t*>(p.out)[(size_t)sid * sh.N + n] = f32_to_bf16_bits(acc[mt][q][r]);
+                    for (int q = 0; q < NBW / 2; ++q) {
+                        const int n = (wave_global * (NBW / 2) + q) * 16 + j;
+                        if (n >= NO) continue;
+                        static_cast<uint16_t*>(p.out)[(size_t)sid * NO + n] =
+                            f32_to_bf16_bits(silu_mul(acc[mt][q][r], acc[mt][q + NBW / 2][r]));
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < NBW; ++q) {
+                        const int n = (wave_global * NBW + q) * 16 + j;
+                        if (n >= sh.N) continue;
+                        if (OM == kOutF32)
+                            static_cast<float*>(p.out)[(size_t)sid * sh.N + n] = acc[mt][q][r];
+                        else
+                            static_cast<uint16_t*>(p.out)[(size_t)sid * sh.N + n] = f32_to_bf16_bits(acc[mt][q][r]);
+                    }
                 }
             }
         return;
@@ -276,19 +305,39 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_kernel(DecodeParam
     __syncthreads();
     if (!s_last) return;
     const float* all = p.partials + tile * KS * (size_t)(BM * COLS);
-    const int n_base = blockIdx.y * COLS;
-    for (int idx = threadIdx.x; idx < BM * COLS; idx += kDecodeThreads) {
-        const int m = idx / COLS, col = idx % COLS;
-        const int sid = ssid[m];
-        const int n = n_base + col;
-        if (sid < 0 || n >= sh.N) continue;
+    auto reduce = [&](int idx) {
         float v = 0.f;
         for (int z = 0; z < KS; ++z)
             v += __hip_atomic_load(&all[(size_t)z * BM * COLS + idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (OUT_F32)
-            static_cast<float*>(p.out)[(size_t)sid * sh.N + n] = v;
-        else
-            static_cast<uint16_t*>(p.out)[(size_t)sid * sh.N + n] = f32_to_bf16_bits(v);
+        return v;
+    };
+    if (OM == kOutAct) {
+        // output column oc of the tile: wavefront oc / (16*HB), its slot (oc / 16) % HB, lane column oc % 16
+        constexpr int HB = NBW / 2, OCOLS = NBW * 16 * kWaves / 2;
+        const int NO = sh.N / 2;
+        for (int idx = threadIdx.x; idx < BM * OCOLS; idx += kDecodeThreads) {
+            const int m = idx / OCOLS, oc = idx % OCOLS;
+            const int sid = ssid[m];
+            const int ww = oc / (16 * HB), q = (oc / 16) % HB, jj = oc % 16;
+            const int n = ((blockIdx.y * kWaves + ww) * HB + q) * 16 + jj;
+            if (sid < 0 || n >= NO) continue;
+            const int gcol = (ww * NBW + q) * 16 + jj;
+            const float g = reduce(m * COLS + gcol), u = reduce(m * COLS + gcol + HB * 16);
+            static_cast<uint16_t*>(p.out)[(size_t)sid * NO + n] = f32_to_bf16_bits(silu_mul(g, u));
+        }
+    } else {
+        const int n_base = blockIdx.y * COLS;
+        for (int idx = threadIdx.x; idx < BM * COLS; idx += kDecodeThreads) {
+            const int m = idx / COLS, col = idx % COLS;
+            const int sid = ssid[m];
+            const int n = n_base + col;
+            if (sid < 0 || n >= sh.N) continue;
+            const float v = reduce(idx);
+            if (OM == kOutF32)
+                static_cast<float*>(p.out)[(size_t)sid * sh.N + n] = v;
+            else
+                static_cast<uint16_t*>(p.out)[(size_t)sid * sh.N + n] = f32_to_bf16_bits(v);
+        }
     }
     if (threadIdx.x == 0) __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -303,37 +352,39 @@ constexpr int ring_depth() {
     return d > 6 ? 6 : (d < 2 ? 2 : d);
 }
 
-template <int MT, int NBW, bool F32>
+template <int MT, int NBW, int OM>
 hipError_t launch_t(const GemmArgs& a, const w4a16_plan& pl, hipStream_t s) {
     constexpr int D = ring_depth<MT, NBW>();
     constexpr size_t shmem = (size_t)D * DecodeLds<MT, NBW>::SLOT;
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_decode_kernel<MT, NBW, D, F32>),
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_decode_kernel<MT, NBW, D, OM>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (attr != hipSuccess) return attr;
     DecodeParams p{a.A, a.a_row_div, static_cast<const uint8_t*>(a.packed), a.sh, a.sorted_ids, a.expert_ids, a.R,
                    a.out, a.partials, a.counters};
     const dim3 grid(a.max_blocks, decode_n_tiles(a.sh, pl), pl.k_split);
-    hipLaunchKernelGGL((gemm_decode_kernel<MT, NBW, D, F32>), grid, dim3(kDecodeThreads), shmem, s, p);
+    hipLaunchKernelGGL((gemm_decode_kernel<MT, NBW, D, OM>), grid, dim3(kDecodeThreads), shmem, s, p);
     return hipGetLastError();
 }
 
-template <int MT, bool F32>
+template <int MT, int OM>
 hipError_t dispatch_nbw(const GemmArgs& a, const w4a16_plan& pl, hipStream_t s) {
     switch (pl.n_blocks) {
-        case 1: return launch_t<MT, 1, F32>(a, pl, s);
-        case 2: return launch_t<MT, 2, F32>(a, pl, s);
-        case 4: return launch_t<MT, 4, F32>(a, pl, s);
+        case 1:
+            if constexpr (OM == kOutAct) return hipErrorInvalidValue;  // gate and up need a slot each
+            else return launch_t<MT, 1, OM>(a, pl, s);
+        case 2: return launch_t<MT, 2, OM>(a, pl, s);
+        case 4: return launch_t<MT, 4, OM>(a, pl, s);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <bool F32>
+template <int OM>
 hipError_t dispatch_mt(const GemmArgs& a, const w4a16_plan& pl, hipStream_t s) {
     switch (pl.block_m / 16) {
-        case 1: return dispatch_nbw<1, F32>(a, pl, s);
-        case 2: return dispatch_nbw<2, F32>(a, pl, s);
-        case 3: return dispatch_nbw<3, F32>(a, pl, s);
-        case 4: return dispatch_nbw<4, F32>(a, pl, s);
+        case 1: return dispatch_nbw<1, OM>(a, pl, s);
+        case 2: return dispatch_nbw<2, OM>(a, pl, s);
+        case 3: return dispatch_nbw<3, OM>(a, pl, s);
+        case 4: return dispatch_nbw<4, OM>(a, pl, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -357,7 +408,12 @@ size_t decode_counters(const Shape& sh, const w4a16_plan& p, int max_blocks) {
 
 hipError_t launch_gemm_decode(const GemmArgs& a, const w4a16_plan& p, hipStream_t s) {
     if (a.max_blocks == 0) return hipSuccess;
-    return a.out_f32 ? dispatch_mt<true>(a, p, s) : dispatch_mt<false>(a, p, s);
+    switch (a.out_mode) {
+        case kOutBf16: return dispatch_mt<kOutBf16>(a, p, s);
+        case kOutF32: return dispatch_mt<kOutF32>(a, p, s);
+        case kOutAct: return dispatch_mt<kOutAct>(a, p, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace w4a16

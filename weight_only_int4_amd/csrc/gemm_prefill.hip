@@ -40,8 +40,9 @@ struct PrefillParams {
     void* out;
 };
 
-template <int MT, int NBW, bool OUT_F32>
+template <int MT, int NBW, int OM>
 __global__ __launch_bounds__(kThreads) void gemm_prefill_kernel(PrefillParams p) {
+    static_assert(OM != kOutAct || NBW % 2 == 0, "the activation epilogue pairs gate and up n-blocks");
     constexpr int BM = 16 * MT;
     constexpr int XR = BM * (KT / 8) / kThreads;  // 16-byte activation pieces per thread per stage
     __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDA];
@@ -56,7 +57,7 @@ __global__ __launch_bounds__(kThreads) void gemm_prefill_kernel(PrefillParams p)
     constexpr int WN = kThreads / 64;
     const int w = threadIdx.x >> 6, L = threadIdx.x & 63;
     const int c = L >> 4, j = L & 15;
-    const int nbw0 = (blockIdx.y * WN + w) * NBW;
+    const int wave_global = blockIdx.y * WN + w;  // column group of this wavefront
     const int nst = (sh.G + 3) / 4;
 
     for (int m = threadIdx.x; m < BM; m += kThreads) {
@@ -69,7 +70,14 @@ __global__ __launch_bounds__(kThreads) void gemm_prefill_kernel(PrefillParams p)
     const uint8_t* wbase[NBW];
 #pragma unroll
     for (int q = 0; q < NBW; ++q) {
-        const int nb = nbw0 + q < sh.NB ? nbw0 + q : sh.NB - 1;  // clamped blocks compute discarded columns
+        int nb;
+        if (OM == kOutAct) {  // slots [0, NBW/2) read gate rows, the rest the matching up rows
+            const int half = sh.NB / 2, o = wave_global * (NBW / 2) + q % (NBW / 2);
+            nb = o < half ? (q < NBW / 2 ? o : half + o) : sh.NB - 1;
+        } else {
+            nb = wave_global * NBW + q < sh.NB ? wave_global * NBW + q : sh.NB - 1;
+        }
+        // clamped blocks compute discarded columns
         wbase[q] = p.packed + ((size_t)e * sh.NB + nb) * sh.KB * SB_BYTES;
     }
 
@@ -158,34 +166,45 @@ __global__ __launch_bounds__(kThreads) void gemm_prefill_kernel(PrefillParams p)
         for (int r = 0; r < 4; ++r) {
             const int sid = ssid[mt * 16 + 4 * c + r];
             if (sid < 0) continue;
+            if (OM == kOutAct) {
+                const int NO = sh.N / 2;
 #pragma unroll
-            for (int q = 0; q < NBW; ++q) {
-                const int n = (nbw0 + q) * 16 + j;
-                if (nbw0 + q >= sh.NB || n >= sh.N) continue;
-                if (OUT_F32)
-                    static_cast<float*>(p.out)[(size_t)sid * sh.N + n] = acc[mt][q][r];
-                else
-                    static_cast<uint16_t*>(p.out)[(size_t)sid * sh.N + n] = f32_to_bf16_bits(acc[mt][q][r]);
+                for (int q = 0; q < NBW / 2; ++q) {
+                    const int n = (wave_global * (NBW / 2) + q) * 16 + j;
+                    if (n >= NO) continue;
+                    static_cast<uint16_t*>(p.out)[(size_t)sid * NO + n] =
+                        f32_to_bf16_bits(silu_mul(acc[mt][q][r], acc[mt][q + NBW / 2][r]));
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < NBW; ++q) {
+                    const int n = (wave_global * NBW + q) * 16 + j;
+                    if (n >= sh.N) continue;
+                    if (OM == kOutF32)
+                        static_cast<float*>(p.out)[(size_t)sid * sh.N + n] = acc[mt][q][r];
+                    else
+                        static_cast<uint16_t*>(p.out)[(size_t)sid * sh.N + n] = f32_to_bf16_bits(acc[mt][q][r]);
+                }
             }
         }
 }
 
-template <int MT, int NBW, bool F32>
+template <int MT, int NBW, int OM>
 hipError_t launch_t(const GemmArgs& a, hipStream_t s) {
     PrefillParams p{a.A, a.a_row_div, static_cast<const uint8_t*>(a.packed), a.sh, a.sorted_ids, a.expert_ids, a.R,
                     a.out};
     constexpr int cols = (kThreads / 64) * NBW;
     const dim3 grid(a.max_blocks, (a.sh.NB + cols - 1) / cols);
-    hipLaunchKernelGGL((gemm_prefill_kernel<MT, NBW, F32>), grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((gemm_prefill_kernel<MT, NBW, OM>), grid, dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 
-template <bool F32>
+template <int OM>
 hipError_t dispatch(const GemmArgs& a, int mt, int nbw, hipStream_t s) {
-    if (nbw == 4 && mt == 4) return launch_t<4, 4, F32>(a, s);
-    if (nbw == 4 && mt == 8) return launch_t<8, 4, F32>(a, s);
-    if (nbw == 2 && mt == 8) return launch_t<8, 2, F32>(a, s);
-    if (nbw == 2 && mt == 4) return launch_t<4, 2, F32>(a, s);
+    if (nbw == 4 && mt == 4) return launch_t<4, 4, OM>(a, s);
+    if (nbw == 4 && mt == 8) return launch_t<8, 4, OM>(a, s);
+    if (nbw == 2 && mt == 8) return launch_t<8, 2, OM>(a, s);
+    if (nbw == 2 && mt == 4) return launch_t<4, 2, OM>(a, s);
     return hipErrorInvalidValue;
 }
 
@@ -194,7 +213,12 @@ hipError_t dispatch(const GemmArgs& a, int mt, int nbw, hipStream_t s) {
 hipError_t launch_gemm_prefill(const GemmArgs& a, const w4a16_plan& p, hipStream_t s) {
     if (a.max_blocks == 0) return hipSuccess;
     const int mt = p.block_m / 16;
-    return a.out_f32 ? dispatch<true>(a, mt, p.n_blocks, s) : dispatch<false>(a, mt, p.n_blocks, s);
+    switch (a.out_mode) {
+        case kOutBf16: return dispatch<kOutBf16>(a, mt, p.n_blocks, s);
+        case kOutF32: return dispatch<kOutF32>(a, mt, p.n_blocks, s);
+        case kOutAct: return dispatch<kOutAct>(a, mt, p.n_blocks, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace w4a16

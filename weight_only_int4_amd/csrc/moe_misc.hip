@@ -19,8 +19,8 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(const uint16_t* __restric
     const uint32_t u2 = *reinterpret_cast<const uint32_t*>(gu + (size_t)r * 2 * I + I + c);
     const float g0 = bf16_to_f32(g2 & 0xFFFFu), g1 = bf16_to_f32(g2 >> 16);
     const float u0 = bf16_to_f32(u2 & 0xFFFFu), u1 = bf16_to_f32(u2 >> 16);
-    const float h0 = g0 / (1.0f + expf(-g0)) * u0;
-    const float h1 = g1 / (1.0f + expf(-g1)) * u1;
+    const float h0 = silu_mul(g0, u0);
+    const float h1 = silu_mul(g1, u1);
     const uint32_t packed = (uint32_t)f32_to_bf16_bits(h0) | ((uint32_t)f32_to_bf16_bits(h1) << 16);
     *reinterpret_cast<uint32_t*>(h + (size_t)r * I + c) = packed;
 }
@@ -35,8 +35,8 @@ __global__ __launch_bounds__(256) void silu_mul_f32_kernel(const float* __restri
     const int r = (int)(idx / pairs), c = 2 * (int)(idx % pairs);
     const float2 g = *reinterpret_cast<const float2*>(gu + (size_t)r * 2 * I + c);
     const float2 u = *reinterpret_cast<const float2*>(gu + (size_t)r * 2 * I + I + c);
-    const float h0 = g.x / (1.0f + expf(-g.x)) * u.x;
-    const float h1 = g.y / (1.0f + expf(-g.y)) * u.y;
+    const float h0 = silu_mul(g.x, u.x);
+    const float h1 = silu_mul(g.y, u.y);
     const uint32_t packed = (uint32_t)f32_to_bf16_bits(h0) | ((uint32_t)f32_to_bf16_bits(h1) << 16);
     *reinterpret_cast<uint32_t*>(h + (size_t)r * I + c) = packed;
 }

@@ -77,6 +77,16 @@ struct w4a16_weights {
 
 namespace w4a16 {
 
+// Output modes of the GEMM kernels.
+//   kOutBf16: out[row, n] = bf16(acc)
+//   kOutF32:  out[row, n] = acc
+//   kOutAct:  the weight rows are [gate (N/2 rows); up (N/2 rows)] and
+//             out[row, n] = bf16(silu(acc_gate[n]) * acc_up[n]), n < N/2;
+//             each wavefront takes half of its n-blocks from the gate rows and
+//             the matching half from the up rows, so both halves of an output
+//             column end in the same lane.
+constexpr int kOutBf16 = 0, kOutF32 = 1, kOutAct = 2;
+
 // Launchers (return hipError_t of the launch).
 hipError_t launch_pack(const uint8_t* codes, const uint16_t* scales, const Shape& sh, void* packed, hipStream_t s);
 hipError_t launch_dequant(const void* packed, const Shape& sh, int expert, float* out_f32, uint16_t* out_bf16,
@@ -96,8 +106,8 @@ struct GemmArgs {
     const int32_t* expert_ids;
     int R;             // sentinel value / number of routes
     int max_blocks;    // route blocks (grid.x)
-    void* out;         // BF16 bits [R,N] or float [R,N]
-    int out_f32;
+    void* out;         // BF16 bits [R,N], float [R,N], or BF16 bits [R,N/2] (activation mode)
+    int out_mode;      // kOutBf16, kOutF32 or kOutAct
     float* partials = nullptr;     // split-K partial tiles (decode, k_split > 1)
     unsigned* counters = nullptr;  // split-K arrival counters, zero between calls
 };

@@ -57,6 +57,7 @@ _SIGS = {
     "w4a16_gemm_workspace_bytes": (_I, [ctypes.POINTER(Plan), _I, _I, _I, ctypes.POINTER(_SZ)]),
     "w4a16_grouped_gemm": (_I, [_P, _I, _P, _P, _P, _P, _I, ctypes.POINTER(Plan), _P, _P, _SZ, _P]),
     "w4a16_grouped_gemm_f32": (_I, [_P, _I, _P, _P, _P, _P, _I, ctypes.POINTER(Plan), _P, _P, _SZ, _P]),
+    "w4a16_grouped_gemm_silu": (_I, [_P, _I, _P, _P, _P, _P, _I, ctypes.POINTER(Plan), _P, _P, _SZ, _P]),
     "w4a16_silu_mul_f32": (_I, [_P, _I, _I, _P, _P]),
     "w4a16_fused_moe_plans": (_I, [_I, _I, _P, _P, ctypes.POINTER(Plan), ctypes.POINTER(Plan)]),
     "w4a16_offsets_workspace_bytes": (_I, [_I, _P, ctypes.POINTER(Plan), ctypes.POINTER(_SZ)]),
@@ -248,6 +249,25 @@ def grouped_gemm(A: torch.Tensor, a_row_div: int, w: Weights, route: dict, plan:
     return out
 
 
+def grouped_gemm_silu(A: torch.Tensor, a_row_div: int, w13: Weights, route: dict, plan: Plan,
+                      out: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Gate/up grouped GEMM with SiLU*mul in the epilogue: h [R, N/2] BF16 from w13 [E, N, K] (gate rows first)."""
+    R = route["R"]
+    if route["block_m"] != plan.block_m:
+        raise ValueError("routing was prepared with block_m=%d but the plan uses %d" % (route["block_m"], plan.block_m))
+    if route["E"] != w13.E:
+        raise ValueError("routing was prepared for %d experts but the weights hold %d" % (route["E"], w13.E))
+    if out is None:
+        out = torch.empty((R, w13.N // 2), dtype=torch.bfloat16, device=A.device)
+    if ws is None:
+        ws = zeroed_workspace(gemm_workspace_bytes(plan, R, w13.E, w13.N), A.device)
+    _check(load().w4a16_grouped_gemm_silu(_ptr(A), a_row_div, w13.handle, ctypes.c_void_p(route["sorted_ids"].data_ptr()),
+                                          ctypes.c_void_p(route["expert_ids"].data_ptr()),
+                                          _ptr(route["num_tokens_padded"]), R, ctypes.byref(plan), _ptr(out), _ptr(ws),
+                                          ws.numel(), _stream(stream)))
+    return out
+
+
 def offsets_workspace_bytes(rows_max: int, w: Weights, plan: Plan) -> int:
     out = _SZ(0)
     _check(load().w4a16_offsets_workspace_bytes(rows_max, w.handle, ctypes.byref(plan), ctypes.byref(out)))
@@ -301,10 +321,15 @@ def fused_moe_workspace_bytes(T: int, k: int, w13: Weights, w2: Weights) -> int:
     return out.value
 
 
+# stage boundaries recorded by w4a16_fused_moe_profiled: routing | gate_up + activation | down | combine
+FUSED_STAGES = ("route_prep", "gate_up_silu", "down", "combine")
+FUSED_STAGE_EVENTS = len(FUSED_STAGES) + 1
+
+
 def fused_moe(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, w13: Weights, w2: Weights,
               out: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None,
               stage_events=None) -> torch.Tensor:
-    """Fused expert MLP.  ``stage_events``: 6 recorded-once torch.cuda.Event objects (timing) or None."""
+    """Fused expert MLP.  ``stage_events``: FUSED_STAGE_EVENTS torch.cuda.Event objects (timing) or None."""
     T, k = topk_ids.shape
     if out is None:
         out = torch.empty((T, w2.N), dtype=torch.bfloat16, device=x.device)
@@ -315,8 +340,8 @@ def fused_moe(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, w13
     if stage_events is None:
         _check(load().w4a16_fused_moe(*args))
     else:
-        if len(stage_events) != 6:
-            raise ValueError("stage_events needs 6 events")
-        arr = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(e.cuda_event) for e in stage_events])
+        if len(stage_events) != FUSED_STAGE_EVENTS:
+            raise ValueError("stage_events needs %d events" % FUSED_STAGE_EVENTS)
+        arr = (ctypes.c_void_p * FUSED_STAGE_EVENTS)(*[ctypes.c_void_p(e.cuda_event) for e in stage_events])
         _check(load().w4a16_fused_moe_profiled(*args, ctypes.cast(arr, ctypes.c_void_p)))
     return out
