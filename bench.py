@@ -71,6 +71,53 @@ def packed_weight_bytes(N: int, K: int) -> int:
     return ((N + 15) // 16) * ((K + 255) // 256) * 2304
 
 
+def gate_up_algorithmic_bytes(spec, block_m: int = 16) -> int:
+    """Bytes the gate_up GEMM (SiLU*mul epilogue) must move at least: the packed weights of every expert that
+    received a route, x once, h written once, and the routing tensors read once."""
+    from weight_only_int4_amd import lib as L
+
+    E, k, H, I, T = spec["E"], spec["k"], spec["H"], spec["I"], spec["T"]
+    flat = spec["routes"]().reshape(-1)
+    valid = (flat >= 0) & (flat < E)
+    active = len(np.unique(flat[valid]))
+    maxP, maxB = L.route_bounds(T, k, E, block_m)
+    return active * packed_weight_bytes(2 * I, H) + T * H * 2 + int(valid.sum()) * I * 2 + (maxP + maxB) * 4
+
+
+KERNEL_SOURCES = ("weight_only_int4_amd/csrc/gemm_decode.hip", "weight_only_int4_amd/csrc/gemm_prefill.hip",
+                  "weight_only_int4_amd/csrc/frag.h", "weight_only_int4_amd/csrc/w4a16_internal.h")
+
+
+def kernel_sources_sha256() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def committed_traffic(workload: str):
+    """HBM bytes per launch of the gate_up kernel from the committed counter summary of this workload, or None
+    when there is none or the kernel sources have changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "gate_up_silu_%s_hbm_traffic.md" % workload)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(("|", "#", "`")):
+                key, _, val = line.partition(":")
+                fields[key.strip()] = val.strip()
+    if fields.get("workload") != workload or fields.get("kernel_sources_sha256") != kernel_sources_sha256():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def make_inputs(spec):
     import synth
 
@@ -238,9 +285,9 @@ def main():
 
     # dominant kernel: gate_up grouped GEMM with the SiLU*mul epilogue (decode or prefill kernel by plan).
     # Algorithmic bytes: packed weights of the active experts, x once, h written once, routing read once.
-    maxP, maxB = L.route_bounds(T, k, E, p13.block_m)
-    alg_bytes = len(active) * wb13 + T * H * 2 + Rv * I * 2 + (maxP + maxB) * 4
+    alg_bytes = gate_up_algorithmic_bytes(spec, p13.block_m)
     achieved = alg_bytes / (gate_up_us * 1e-6) / 1e9
+    traffic = committed_traffic(spec["name"])
     kname = "gemm_%s_kernel<MT=%d,NBW=%d,act out> (gate_up + silu_mul, %d waves, k_split %d)" % (
         "decode" if p13.kernel == L.KERNEL_DECODE else "prefill", p13.block_m // 16, p13.n_blocks, p13.waves,
         p13.k_split)
@@ -262,7 +309,7 @@ def main():
         "stages_us": {n: round(float(v), 2) for n, v in zip(stages, stage.mean(0))},
         "gpu_us_per_step_events": round(gpu_step_us, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": kname,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kname,
                      "bytes_per_launch": int(alg_bytes), "avg_launch_us": round(gate_up_us, 2)},
     }
     if not args.no_cpu_baseline:
