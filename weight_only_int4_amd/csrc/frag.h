@@ -21,6 +21,32 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// A 32-bit constant held in a VGPR that the compiler cannot see through.  gfx9
+// VOP3 encodings take no literal constants, so (x & mask) | bias with literal
+// mask and bias compiles to an AND and an OR with a literal each; with both
+// constants in opaque VGPRs it becomes one v_and_or_b32.  The value is made
+// once, outside the loops; the inline assembly is a plain move, and every
+// instruction that reads its result is ordinary compiled code (so the
+// compiler's hazard checks for the MFMA operands built from it still apply).
+__device__ __forceinline__ uint32_t opaque_vgpr(uint32_t v) {
+    uint32_t r;
+    __asm__ volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
+    return r;
+}
+
+// Eight codes of one packed word as BF16 values 128 + q (exact), in 7 VALU
+// operations when mask and bias are opaque VGPR values (opaque_vgpr of
+// 0x000F000F and 0x43004300): code u = 2p sits in bits [4p, 4p+4) and
+// u = 2p+1 in [16+4p, 20+4p), so a shift and one AND-OR build two operands.
+__device__ __forceinline__ bf16x8 biased_codes_vop3(uint32_t w, uint32_t mask, uint32_t bias) {
+    u32x4 v;
+    v.x = (w & mask) | bias;
+    v.y = ((w >> 4) & mask) | bias;
+    v.z = ((w >> 8) & mask) | bias;
+    v.w = ((w >> 12) & mask) | bias;
+    return __builtin_bit_cast(bf16x8, v);
+}
+
 // Eight codes of one packed word as BF16 values 128 + q (exact).  Code u = 2p
 // sits in bits [4p, 4p+4) and u = 2p+1 in [16+4p, 20+4p), so one shift, mask
 // and OR with the BF16 pattern of 128 (0x4300) builds two operands.

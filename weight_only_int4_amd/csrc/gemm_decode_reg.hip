@@ -1,0 +1,245 @@
+// Decode grouped GEMM for one 16-row tile per workgroup (a few routed rows per
+// expert: the common decode case), with every operand streamed straight into
+// registers.
+//
+// Design (MI355X-first):
+//  * Grid, dequantisation and epilogue as in the LDS-staged decode kernel
+//    (gemm_decode.hip): one workgroup per (route block, 64*NBW columns, K
+//    slice), four independent wavefronts with disjoint columns, the raw codes
+//    fed to the MFMA as BF16 128 + q with a -136 * sum(x) correction, one FMA
+//    per output and group for the scale.
+//  * Each wavefront keeps a ring of D register sets; per stage of 128 k a set
+//    holds its NBW 1 KiB code halves, 8 bytes of scales per row, and its
+//    16-byte activation fragments of the four scale groups (lane (c, j): row j,
+//    k-slot c).  D-1 stages are in flight per wavefront, with no LDS and no
+//    barrier.  The register file (512 KiB per CU) holds more bytes in flight
+//    than an LDS ring can at this tile height, and every ring slot being its
+//    own registers lets the compiler wait for exactly the loads a stage uses.
+//  * Loads are buffer loads: a scalar resource, a per-lane offset fixed for the
+//    whole K loop and the stage offset as a scalar, so issuing a load costs no
+//    vector instruction.  Sentinel rows, and groups past K in a ragged last
+//    stage, read past the resource's extent and get zeros.
+//  * The instruction stream is held to about 12 vector operations per 8
+//    weights per lane (7 to build the BF16 operands with AND-OR, 4 scale FMAs,
+//    1 scale extraction): at 16 lanes per SIMD that is the work that has to
+//    hide under the weight stream.  MFMA results go to VGPRs (compiled with
+//    the VGPR MFMA form, see build.py), saving a register move per element.
+#include <type_traits>
+
+#include "decode_common.h"
+
+namespace w4a16 {
+using namespace decode;
+namespace {
+
+// Buffer resource word 3 for raw (unformatted, unswizzled) buffers on gfx9-family chips; cache policy bit of a
+// non-temporal load; an offset that no resource reaches (a load from it returns zeros).
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kBufferNonTemporal = 2;
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+template <int NBW>
+struct RegStage {
+    u32x4 cw[NBW];  // codes of half h of the superblock, per n-block
+    uint32_t sc[NBW][2];  // scales of groups 4h .. 4h+3 of row j, per n-block
+    u32x4 xa[4];    // activation fragment of each of the 4 groups
+};
+
+#ifndef W4A16_DECODE_REG_WAVES
+#define W4A16_DECODE_REG_WAVES 1
+#endif
+
+template <int NBW, int D, int OM>
+__global__ __launch_bounds__(kDecodeThreads, W4A16_DECODE_REG_WAVES) void gemm_decode_reg_kernel(DecodeParams p) {
+    static_assert(OM != kOutAct || NBW % 2 == 0, "the activation epilogue pairs gate and up n-blocks");
+    static_assert(D >= 2 && D <= 6, "ring depth");
+    __shared__ int ssid[16];
+    __shared__ int s_last;
+
+    const int b = blockIdx.x;
+    const int e = p.expert_ids[b];
+    if (e < 0 || e >= p.sh.E) return;  // unowned block (or ids from a larger expert count)
+    const Shape sh = p.sh;
+    const int K = sh.K;
+    // the wavefront index is uniform: as a scalar it keeps every per-stage offset in scalar registers
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), L = threadIdx.x & 63;
+    const int c = L >> 4, j = L & 15;
+    const int wave_global = blockIdx.y * kWaves + w;
+    const int KS = gridDim.z, ks = blockIdx.z;
+    const int nst = (sh.G + 3) / 4;
+    const int st_begin = (int)((long)ks * nst / KS), st_end = (int)((long)(ks + 1) * nst / KS);
+
+    if (threadIdx.x < 16) {
+        const int sid = p.sorted_ids[b * 16 + threadIdx.x];
+        ssid[threadIdx.x] = sid < p.R ? sid : -1;
+    }
+
+    // Buffer loads: a scalar resource, a per-lane offset fixed for the whole K loop, and the stage's offset as a
+    // scalar, so a load costs no vector arithmetic.  Offsets at or past a resource's extent read zeros.
+    const uint32_t expert_bytes = (uint32_t)sh.NB * sh.KB * SB_BYTES;
+    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.packed + (size_t)e * expert_bytes), (short)0, (int)expert_bytes, kBufferWord3);
+    uint32_t cw_off[NBW], sc_off[NBW];
+#pragma unroll
+    for (int q = 0; q < NBW; ++q) {
+        int o;
+        const uint32_t nb = (uint32_t)slot_nblock<NBW, OM>(sh, wave_global, q, &o);
+        cw_off[q] = nb * sh.KB * SB_BYTES + (uint32_t)L * 16u;
+        sc_off[q] = nb * sh.KB * SB_BYTES + SB_CODE_BYTES + (uint32_t)j * 16u;
+    }
+    // activations: lane (c, j) reads row j of the tile at k-slot c; sentinel rows read past the end (zeros)
+    const uint32_t a_bytes = (uint32_t)(p.R / p.a_row_div) * (uint32_t)K * 2u;
+    const __amdgpu_buffer_rsrc_t xres =
+        __builtin_amdgcn_make_buffer_rsrc((void*)p.A, (short)0, (int)a_bytes, kBufferWord3);
+    const int sid_j = p.sorted_ids[b * 16 + j];
+    const uint32_t x_off = sid_j < p.R ? (uint32_t)(sid_j / p.a_row_div) * (uint32_t)K * 2u + (uint32_t)c * 16u
+                                       : kOutOfRange;
+
+    // RAGGED: the stage may reach past K (only the last stage of K can); its groups past K are skipped by
+    // reading zeros (the test is uniform per group since K is a multiple of 32)
+    auto load = [&](int st, RegStage<NBW>& S, auto ragged) {
+        const int kb = st >> 1, h = st & 1;
+        const int soff_code = kb * SB_BYTES + h * 1024, soff_scale = kb * SB_BYTES + h * 8;
+#pragma unroll
+        for (int q = 0; q < NBW; ++q) {
+            S.cw[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, cw_off[q], soff_code,
+                                                                                      kBufferNonTemporal));
+            const auto sv = __builtin_amdgcn_raw_buffer_load_b64(wres, sc_off[q], soff_scale, 0);
+            S.sc[q][0] = sv[0];
+            S.sc[q][1] = sv[1];
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            uint32_t off = x_off + (uint32_t)g * 64u;
+            int soff = st * KT * 2;
+            if constexpr (decltype(ragged)::value) {
+                if (st * KT + g * 32 >= K) off = kOutOfRange;
+            }
+            S.xa[g] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, off, soff, 0));
+        }
+    };
+    const std::false_type full{};
+    const std::true_type ragged{};
+
+    f32x4 acc[1][NBW];
+#pragma unroll
+    for (int q = 0; q < NBW; ++q) acc[0][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const bf16x8 m136 = minus136();
+
+    const uint32_t kMask = opaque_vgpr(0x000F000Fu), kBias = opaque_vgpr(0x43004300u);
+    auto compute = [&](const RegStage<NBW>& S) {
+        // a ragged last stage computes its padding groups too: their codes are 8 and scales 0 in the packed
+        // image and their activations are zero, so they add exactly zero
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const bf16x8 xf = __builtin_bit_cast(bf16x8, S.xa[g]);
+            const f32x4 xc = mfma16(xf, m136, zero);
+            // all MFMAs of the group first (distinct results), then the scale FMAs: the FMAs of one n-block then
+            // never wait on the MFMA that produced them while the others are still to be issued
+            f32x4 d[NBW];
+#pragma unroll
+            for (int q = 0; q < NBW; ++q) d[q] = mfma16(xf, biased_codes_vop3(S.cw[q][g], kMask, kBias), xc);
+            __builtin_amdgcn_sched_group_barrier(0x008, NBW + 1, 0);  // the group's MFMAs ...
+            __builtin_amdgcn_sched_group_barrier(0x002, 1000, 0);     // ... before its VALU work
+#pragma unroll
+            for (int q = 0; q < NBW; ++q) {
+                const uint32_t word = S.sc[q][g >> 1];
+                const float sc = __uint_as_float((g & 1) ? (word & 0xFFFF0000u) : (word << 16));
+                acc[0][q] += sc * d[q];
+            }
+        }
+    };
+
+    // The ring slot of stage st is (st - st_begin) % D; unrolling by D keeps every slot index static.  The steady
+    // state (every stage issues the load D-1 stages ahead, none of them ragged) has no branches; the last stages
+    // drain with guarded issues.
+    const int full_end = min(st_end, K / KT);  // stages below this one lie entirely inside K
+    RegStage<NBW> ring[D];
+    int st = st_begin;
+    if (full_end - st_begin >= 2 * D - 1) {
+        // the prologue issues its stages in order too, so that at the loop head every slot's loads are as old
+        // on entry as on the back edge (else the compiler's wait counts take the younger, stricter view)
+#pragma unroll
+        for (int d = 0; d < D - 1; ++d) {
+            __builtin_amdgcn_sched_barrier(0);
+            load(st_begin + d, ring[d], full);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        for (; st + 2 * D - 2 < full_end; st += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                // keep the issue order: the loads of stage st+d+D-1 go out before stage st+d is computed (the
+                // scheduler would otherwise gather all loads of the unrolled body in one place)
+                __builtin_amdgcn_sched_barrier(0);
+                load(st + d + D - 1, ring[(d + D - 1) % D], full);
+                __builtin_amdgcn_sched_barrier(0);
+                compute(ring[d]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int d = 0; d < D - 1; ++d)
+            if (st_begin + d < st_end) load(st_begin + d, ring[d], ragged);
+    }
+    // drain: at most 2D-1 stages are left; their loads for stages past st_begin + D - 2 are issued here
+#pragma unroll
+    for (int d = 0; d < 2 * D - 1; ++d) {
+        const int sd = st + d;
+        if (sd < st_end) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (sd + D - 1 < st_end) load(sd + D - 1, ring[(d + D - 1) % D], ragged);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(ring[d % D]);
+        }
+    }
+
+    __syncthreads();  // ssid is complete
+    decode_epilogue<1, NBW, OM>(p, acc, ssid, &s_last, wave_global, w, c, j);
+}
+
+#ifndef W4A16_DECODE_REG_DEPTH
+#define W4A16_DECODE_REG_DEPTH 2
+#endif
+
+template <int NBW, int OM>
+hipError_t launch_reg(const GemmArgs& a, const w4a16_plan& pl, hipStream_t s) {
+    DecodeParams p{a.A, a.a_row_div, static_cast<const uint8_t*>(a.packed), a.sh, a.sorted_ids, a.expert_ids, a.R,
+                   a.out, a.partials, a.counters};
+    const dim3 grid(a.max_blocks, decode_n_tiles(a.sh, pl), pl.k_split);
+    constexpr int D = W4A16_DECODE_REG_DEPTH >= 2 ? W4A16_DECODE_REG_DEPTH : 2;  // 0 switches the kernel off
+    hipLaunchKernelGGL((gemm_decode_reg_kernel<NBW, D, OM>), grid, dim3(kDecodeThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int OM>
+hipError_t dispatch_reg(const GemmArgs& a, const w4a16_plan& pl, hipStream_t s) {
+    switch (pl.n_blocks) {
+        case 1:
+            if constexpr (OM == kOutAct) return hipErrorInvalidValue;  // gate and up need a slot each
+            else return launch_reg<1, OM>(a, pl, s);
+        case 2: return launch_reg<2, OM>(a, pl, s);
+        case 4: return launch_reg<4, OM>(a, pl, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool decode_reg_supported(const GemmArgs& a, const w4a16_plan& p) {
+    // one 16-row tile; the buffer resources address below 2 GiB (one expert's packed weights, the activations)
+    return W4A16_DECODE_REG_DEPTH > 0 && p.block_m == 16 && (size_t)a.sh.NB * a.sh.KB * SB_BYTES < (1u << 31) &&
+           (size_t)(a.R / a.a_row_div) * a.sh.K * 2 < (1u << 31);
+}
+
+hipError_t launch_gemm_decode_reg(const GemmArgs& a, const w4a16_plan& p, hipStream_t s) {
+    if (a.max_blocks == 0) return hipSuccess;
+    switch (a.out_mode) {
+        case kOutBf16: return dispatch_reg<kOutBf16>(a, p, s);
+        case kOutF32: return dispatch_reg<kOutF32>(a, p, s);
+        case kOutAct: return dispatch_reg<kOutAct>(a, p, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace w4a16

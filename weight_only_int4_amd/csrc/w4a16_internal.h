@@ -117,6 +117,8 @@ size_t decode_partial_floats(const Shape& sh, const w4a16_plan& p, int max_block
 size_t decode_counters(const Shape& sh, const w4a16_plan& p, int max_blocks);
 
 hipError_t launch_gemm_decode(const GemmArgs& a, const w4a16_plan& p, hipStream_t s);
+bool decode_reg_supported(const GemmArgs& a, const w4a16_plan& p);
+hipError_t launch_gemm_decode_reg(const GemmArgs& a, const w4a16_plan& p, hipStream_t s);
 hipError_t launch_gemm_prefill(const GemmArgs& a, const w4a16_plan& p, hipStream_t s);
 hipError_t launch_silu_mul(const uint16_t* gu, int rows, int I, uint16_t* h, hipStream_t s);
 hipError_t launch_silu_mul_f32(const float* gu, int rows, int I, uint16_t* h, hipStream_t s);
