@@ -167,7 +167,11 @@ int w4a16_plan_select(int T, int k, int E, int N, int K, float expected_rows_per
  *   A          device BF16 bits [*, K] (x [T,K] with a_row_div = k, or
  *              h [R,K] with a_row_div = 1)
  *   routing    as produced by w4a16_route_prep with p->block_m for R routes
- *              and the handle's E experts
+ *              and the handle's E experts; the kernels read
+ *              num_tokens_padded on the device to find the valid route
+ *              blocks (NULL: every block up to the bound of
+ *              w4a16_route_bounds is visited, and blocks with expert_ids -1
+ *              are skipped)
  *   out        device BF16 bits [R, N]; rows of invalid routes untouched
  *   ws         workspace of w4a16_gemm_workspace_bytes (may be NULL if 0).  A
  *              plan with k_split > 1 keeps per-tile arrival counters in it:
@@ -175,7 +179,9 @@ int w4a16_plan_select(int T, int k, int E, int N, int K, float expected_rows_per
  *              and every call leaves the counters at zero again.  Calls that
  *              share a workspace must not run concurrently.
  * Errors: INVALID_ARG, LAYOUT_MISMATCH (bad handle), UNSUPPORTED_SHAPE (plan
- * values outside the supported set), WORKSPACE_TOO_SMALL, HIP_ERROR. */
+ * values outside the supported set; a prefill plan with one expert's packed
+ * weights or the activation matrix of 2 GiB or more), WORKSPACE_TOO_SMALL,
+ * HIP_ERROR. */
 int w4a16_gemm_workspace_bytes(const w4a16_plan* p, int R, int E, int N, size_t* bytes);
 
 int w4a16_grouped_gemm(const uint16_t* A, int a_row_div, const w4a16_weights* w, const int32_t* sorted_ids,

@@ -126,8 +126,10 @@ w4a16_plan select_plan(int T, int k, int E, int N, int K, float rows) {
         const int max_ks = nst / 2 > 1 ? nst / 2 : 1;
         p.k_split = ks < 1 ? 1 : (ks > max_ks ? max_ks : (ks > 16 ? 16 : ks));
     } else {
+        // 128-row tiles amortise dequantisation over more rows; their wavefront tile is 128 x 32 (two
+        // wavefronts per SIMD fit), the 64-row tile's is 64 x 64
         p.block_m = rows >= 96.0f ? 128 : 64;
-        p.n_blocks = 4;
+        p.n_blocks = p.block_m == 128 ? 2 : 4;
         p.waves = 4;
     }
     if (ov.block_m) p.block_m = ov.block_m;
@@ -360,9 +362,19 @@ int w4a16_gemm_workspace_bytes(const w4a16_plan* p, int R, int E, int N, size_t*
     return ok();
 }
 
+// Shapes the prefill kernel cannot address (its buffer resources reach below 2 GiB).
+static int check_prefill_shape(const char* what, const GemmArgs& a, const w4a16_plan& p) {
+    if (p.kernel == W4A16_KERNEL_PREFILL && !prefill_supported(a))
+        return fail(W4A16_UNSUPPORTED_SHAPE,
+                    "%s: the prefill kernel needs one expert's packed weights and the activation matrix below 2 GiB",
+                    what);
+    return W4A16_OK;
+}
+
 static int grouped_gemm_impl(const char* what, const uint16_t* A, int a_row_div, const w4a16_weights* w,
-                             const int32_t* sorted_ids, const int32_t* expert_ids, int R, const w4a16_plan* p,
-                             void* out, int out_mode, void* ws, size_t ws_bytes, hipStream_t s) {
+                             const int32_t* sorted_ids, const int32_t* expert_ids, const int32_t* ntp, int R,
+                             const w4a16_plan* p, void* out, int out_mode, void* ws, size_t ws_bytes,
+                             hipStream_t s) {
     int rc = check_handle(w, what);
     if (rc) return rc;
     rc = validate_plan(p, what);
@@ -385,6 +397,9 @@ static int grouped_gemm_impl(const char* what, const uint16_t* A, int a_row_div,
         return fail(W4A16_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, needs %zu", what, ws_bytes, g.total);
     if (g.total && !aligned16(ws)) return fail(W4A16_INVALID_ARG, "%s: workspace must be 16-byte aligned", what);
     GemmArgs a{A, a_row_div, w->packed, w->shape, sorted_ids, expert_ids, R, maxB, out, out_mode};
+    a.ntp = ntp;
+    rc = check_prefill_shape(what, a, *p);
+    if (rc) return rc;
     bind_ws(a, g, ws, g.counter_bytes);
     return check_launch(run_gemm(a, *p, s), what);
 }
@@ -392,35 +407,33 @@ static int grouped_gemm_impl(const char* what, const uint16_t* A, int a_row_div,
 int w4a16_grouped_gemm(const uint16_t* A, int a_row_div, const w4a16_weights* w, const int32_t* sorted_ids,
                        const int32_t* expert_ids, const int32_t* num_tokens_padded, int R, const w4a16_plan* p,
                        uint16_t* out, void* ws, size_t ws_bytes, hipStream_t s) {
-    (void)num_tokens_padded;
-    return grouped_gemm_impl("w4a16_grouped_gemm", A, a_row_div, w, sorted_ids, expert_ids, R, p, out, kOutBf16, ws,
-                             ws_bytes, s);
+    return grouped_gemm_impl("w4a16_grouped_gemm", A, a_row_div, w, sorted_ids, expert_ids, num_tokens_padded, R, p,
+                             out, kOutBf16, ws, ws_bytes, s);
 }
 
 int w4a16_grouped_gemm_f32(const uint16_t* A, int a_row_div, const w4a16_weights* w, const int32_t* sorted_ids,
                            const int32_t* expert_ids, const int32_t* num_tokens_padded, int R, const w4a16_plan* p,
                            float* out, void* ws, size_t ws_bytes, hipStream_t s) {
-    (void)num_tokens_padded;
-    return grouped_gemm_impl("w4a16_grouped_gemm_f32", A, a_row_div, w, sorted_ids, expert_ids, R, p, out, kOutF32, ws,
-                             ws_bytes, s);
+    return grouped_gemm_impl("w4a16_grouped_gemm_f32", A, a_row_div, w, sorted_ids, expert_ids, num_tokens_padded, R,
+                             p, out, kOutF32, ws, ws_bytes, s);
 }
 
 int w4a16_grouped_gemm_silu(const uint16_t* A, int a_row_div, const w4a16_weights* w13, const int32_t* sorted_ids,
                             const int32_t* expert_ids, const int32_t* num_tokens_padded, int R, const w4a16_plan* p,
                             uint16_t* h, void* ws, size_t ws_bytes, hipStream_t s) {
-    (void)num_tokens_padded;
-    return grouped_gemm_impl("w4a16_grouped_gemm_silu", A, a_row_div, w13, sorted_ids, expert_ids, R, p, h, kOutAct, ws,
-                             ws_bytes, s);
+    return grouped_gemm_impl("w4a16_grouped_gemm_silu", A, a_row_div, w13, sorted_ids, expert_ids, num_tokens_padded,
+                             R, p, h, kOutAct, ws, ws_bytes, s);
 }
 
-// Offsets-form workspace: [split-K area][sorted_ids][expert_ids].
+// Offsets-form workspace: [split-K area][sorted_ids][expert_ids][num_tokens_padded].
 static size_t offsets_layout(int rows_max, const w4a16_weights* w, const w4a16_plan* p, size_t* off_sorted,
-                             size_t* off_eids, int* maxP, int* maxB, GemmWs* g) {
+                             size_t* off_eids, size_t* off_ntp, int* maxP, int* maxB, GemmWs* g) {
     route_bounds(rows_max, 1, w->shape.E, p->block_m, maxP, maxB);
     *g = gemm_ws(w->shape, *p, *maxB);
     *off_sorted = g->total;
     *off_eids = *off_sorted + align_up(sizeof(int32_t) * (size_t)*maxP, 256);
-    return *off_eids + align_up(sizeof(int32_t) * (size_t)*maxB, 256);
+    *off_ntp = *off_eids + align_up(sizeof(int32_t) * (size_t)*maxB, 256);
+    return *off_ntp + 256;
 }
 
 int w4a16_offsets_workspace_bytes(int rows_max, const w4a16_weights* w, const w4a16_plan* p, size_t* bytes) {
@@ -430,10 +443,10 @@ int w4a16_offsets_workspace_bytes(int rows_max, const w4a16_weights* w, const w4
     rc = validate_plan(p, what);
     if (rc) return rc;
     if (!bytes || rows_max < 0) return fail(W4A16_INVALID_ARG, "%s: bad argument", what);
-    size_t a, b;
+    size_t a, b, c;
     int maxP, maxB;
     GemmWs g;
-    *bytes = offsets_layout(rows_max, w, p, &a, &b, &maxP, &maxB, &g);
+    *bytes = offsets_layout(rows_max, w, p, &a, &b, &c, &maxP, &maxB, &g);
     return ok();
 }
 
@@ -448,10 +461,10 @@ int w4a16_grouped_gemm_offsets(const uint16_t* A_sorted, const int32_t* expert_o
     if (rows_max < 0) return fail(W4A16_INVALID_ARG, "%s: rows_max=%d", what, rows_max);
     if (w->shape.E > W4A16_MAX_EXPERTS) return fail(W4A16_UNSUPPORTED_SHAPE, "%s: too many experts", what);
     if (rows_max == 0) return ok();
-    size_t off_sorted, off_eids;
+    size_t off_sorted, off_eids, off_ntp;
     int maxP, maxB;
     GemmWs g;
-    const size_t need = offsets_layout(rows_max, w, p, &off_sorted, &off_eids, &maxP, &maxB, &g);
+    const size_t need = offsets_layout(rows_max, w, p, &off_sorted, &off_eids, &off_ntp, &maxP, &maxB, &g);
     if (!ws || ws_bytes < need)
         return fail(W4A16_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, needs %zu", what, ws_bytes, need);
     if (!aligned16(ws)) return fail(W4A16_INVALID_ARG, "%s: workspace must be 16-byte aligned", what);
@@ -459,11 +472,15 @@ int w4a16_grouped_gemm_offsets(const uint16_t* A_sorted, const int32_t* expert_o
     if (!aligned16(A_sorted)) return fail(W4A16_INVALID_ARG, "%s: A_sorted must be 16-byte aligned", what);
     int32_t* sorted_ids = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + off_sorted);
     int32_t* expert_ids = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + off_eids);
+    int32_t* ntp = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + off_ntp);
+    GemmArgs a{A_sorted, 1, w->packed, w->shape, sorted_ids, expert_ids, rows_max, maxB, out, kOutBf16};
+    a.ntp = ntp;
+    rc = check_prefill_shape(what, a, *p);
+    if (rc) return rc;
     rc = check_launch(launch_offsets_to_route(expert_offsets, w->shape.E, rows_max, p->block_m, maxP, maxB, sorted_ids,
-                                              expert_ids, s),
+                                              expert_ids, ntp, s),
                       what);
     if (rc) return rc;
-    GemmArgs a{A_sorted, 1, w->packed, w->shape, sorted_ids, expert_ids, rows_max, maxB, out, kOutBf16};
     bind_ws(a, g, ws, g.counter_bytes);
     return check_launch(run_gemm(a, *p, s), what);
 }
@@ -592,6 +609,13 @@ int w4a16_fused_moe_profiled(const uint16_t* x, const int32_t* topk_ids, const f
     uint16_t* h = reinterpret_cast<uint16_t*>(base + f.off_h);
     float* y = reinterpret_cast<float*>(base + f.off_y);
     const int R = T * k;
+    GemmArgs g13{x, k, w13->packed, w13->shape, sorted_ids, expert_ids, R, f.maxB, h, kOutAct};
+    g13.ntp = ntp;
+    GemmArgs g2{h, 1, w2->packed, w2->shape, sorted_ids, expert_ids, R, f.maxB, y, kOutF32};
+    g2.ntp = ntp;
+    rc = check_prefill_shape(what, g13, p13);
+    if (!rc) rc = check_prefill_shape(what, g2, p2);
+    if (rc) return rc;
 
 #define W4A16_STAGE(i)                                                                     \
     do {                                                                                   \
@@ -607,12 +631,10 @@ int w4a16_fused_moe_profiled(const uint16_t* x, const int32_t* topk_ids, const f
                       "w4a16_fused_moe (route_prep)");
     if (rc) return rc;
     W4A16_STAGE(1);
-    GemmArgs g13{x, k, w13->packed, w13->shape, sorted_ids, expert_ids, R, f.maxB, h, kOutAct};
     bind_ws(g13, gemm_ws(w13->shape, p13, f.maxB), base + f.off_split, counter_bytes);
     rc = check_launch(run_gemm(g13, p13, s), "w4a16_fused_moe (gate_up + silu_mul)");
     if (rc) return rc;
     W4A16_STAGE(2);
-    GemmArgs g2{h, 1, w2->packed, w2->shape, sorted_ids, expert_ids, R, f.maxB, y, kOutF32};
     bind_ws(g2, gemm_ws(w2->shape, p2, f.maxB), base + f.off_split, counter_bytes);
     rc = check_launch(run_gemm(g2, p2, s), "w4a16_fused_moe (down)");
     if (rc) return rc;

@@ -97,6 +97,17 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t w, float s, float neg8s) {
     return r;
 }
 
+// Buffer resources (raw, unformatted, unswizzled) on gfx9-family chips: word 3 of the descriptor, the cache
+// policy bit of a non-temporal load, and an offset no resource reaches (a load from it returns zeros; a direct
+// load to LDS from it writes zeros).
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kBufferNonTemporal = 2;
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_resource(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
     __bf16 b = (__bf16)f;
     return __builtin_bit_cast(uint16_t, b);

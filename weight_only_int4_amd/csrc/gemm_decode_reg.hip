@@ -32,11 +32,6 @@ namespace w4a16 {
 using namespace decode;
 namespace {
 
-// Buffer resource word 3 for raw (unformatted, unswizzled) buffers on gfx9-family chips; cache policy bit of a
-// non-temporal load; an offset that no resource reaches (a load from it returns zeros).
-constexpr int kBufferWord3 = 0x00020000;
-constexpr int kBufferNonTemporal = 2;
-constexpr uint32_t kOutOfRange = 0x80000000u;
 
 template <int NBW>
 struct RegStage {
@@ -77,8 +72,7 @@ __global__ __launch_bounds__(kDecodeThreads, W4A16_DECODE_REG_WAVES) void gemm_d
     // Buffer loads: a scalar resource, a per-lane offset fixed for the whole K loop, and the stage's offset as a
     // scalar, so a load costs no vector arithmetic.  Offsets at or past a resource's extent read zeros.
     const uint32_t expert_bytes = (uint32_t)sh.NB * sh.KB * SB_BYTES;
-    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.packed + (size_t)e * expert_bytes), (short)0, (int)expert_bytes, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t wres = buffer_resource(p.packed + (size_t)e * expert_bytes, expert_bytes);
     uint32_t cw_off[NBW], sc_off[NBW];
 #pragma unroll
     for (int q = 0; q < NBW; ++q) {
@@ -89,8 +83,7 @@ __global__ __launch_bounds__(kDecodeThreads, W4A16_DECODE_REG_WAVES) void gemm_d
     }
     // activations: lane (c, j) reads row j of the tile at k-slot c; sentinel rows read past the end (zeros)
     const uint32_t a_bytes = (uint32_t)(p.R / p.a_row_div) * (uint32_t)K * 2u;
-    const __amdgpu_buffer_rsrc_t xres =
-        __builtin_amdgcn_make_buffer_rsrc((void*)p.A, (short)0, (int)a_bytes, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t xres = buffer_resource(p.A, a_bytes);
     const int sid_j = p.sorted_ids[b * 16 + j];
     const uint32_t x_off = sid_j < p.R ? (uint32_t)(sid_j / p.a_row_div) * (uint32_t)K * 2u + (uint32_t)c * 16u
                                        : kOutOfRange;

@@ -1,33 +1,48 @@
 // Prefill grouped GEMM: many routed rows per expert, bound by the matrix cores.
 //
 // Design (MI355X-first):
-//  * One workgroup per (route block of BM rows of one expert, 4*NBW
-//    n-blocks).  The owning expert comes from expert_ids[block] in-kernel, so
-//    no host synchronisation is needed (Chord page, "Two kernel families";
-//    nf4 page, "How it works", finds tiles in-kernel the same way).
-//  * The BM activation rows, gathered through sorted_ids, are staged in LDS
-//    128 k at a time, double-buffered: the next stage's rows are loaded while
-//    the current stage is multiplied, one barrier per stage.  Rows are padded
-//    by 16 bytes so the 16 rows read by one MFMA fragment fall in distinct
-//    banks.
-//  * The four wavefronts split the workgroup's columns, so every weight is
-//    loaded from HBM and dequantised exactly once per workgroup, in
-//    registers, and fed straight to v_mfma_f32_16x16x32_bf16; the next
-//    stage's packed weights are in flight in a second register set while the
-//    current one is used.  Dequantisation (about 2.9 VALU operations per
-//    weight) is amortised over BM rows (Chord page, "Grouped SM90 kernels": a
-//    taller M tile amortises the INT4 dequantisation) and overlaps the MFMAs
-//    of the neighbouring group.
-//  * The MFMA operand is bf16((q - 8) * s), the product rounded once.
+//  * One workgroup of four wavefronts per (route block of BM = 16*MT rows of
+//    one expert, 64*NBW weight columns).  The owning expert comes from
+//    expert_ids[block] in-kernel, so no host synchronisation is needed (Chord
+//    page, "Two kernel families"; the nf4 page, "How it works", finds its
+//    tiles in-kernel the same way).
+//  * Tile order is XCD-aware.  Consecutive workgroup ids go to the eight XCDs
+//    in turn, so id -> (XCD, position) is remapped to give every XCD one
+//    contiguous run of tiles, route block major: the ~64 workgroups an XCD
+//    runs at a time then cover a few route blocks across all column tiles.
+//    They share those rows of activations and, for blocks of the same expert,
+//    its weight slices in the XCD's L2.  Only valid tiles (from the routed
+//    row count num_tokens_padded, read on the device) are spread, so the XCDs
+//    stay balanced.
+//  * The BM gathered activation rows are streamed HBM -> LDS by direct loads
+//    (buffer_load ... lds) into a two-slot ring of 128-k stages, stored
+//    unpadded with each row's 16-byte chunks XOR-permuted by the row, so the
+//    16 rows of an MFMA fragment hit 16 distinct bank groups.  Sentinel rows
+//    and k past K read zeros (an offset past the resource).  No registers hold
+//    activations in flight.
+//  * Each wavefront owns NBW n-blocks across all BM rows.  Its packed weights
+//    for the next stage are in flight in a second register set (buffer loads,
+//    scalar stage offsets) while the current stage is multiplied.  Every
+//    weight is dequantised once per workgroup, to bf16((q - 8) * s) (one FMA,
+//    exact, then one rounding), and feeds MT MFMAs (v_mfma_f32_16x16x32_bf16):
+//    a taller M tile amortises the INT4 conversion (Chord page, "Grouped SM90
+//    kernels").  The dequantisation of group g+1 is independent of the MFMAs
+//    of group g, so the two interleave.
+//  * At most 256 registers per lane for the 128x32 and 64x64 wavefront tiles,
+//    so two wavefronts share each SIMD: one issues VALU dequantisation while
+//    the other's MFMAs run.
+#include <type_traits>
+
 #include "frag.h"
 #include "w4a16_internal.h"
 
 namespace w4a16 {
 namespace {
 
-constexpr int KT = 128;       // k per stage (4 scale groups, half a superblock)
-constexpr int LDA = KT + 8;   // padded LDS row in BF16 elements
-constexpr int kThreads = 256; // four wavefronts, each owning its own columns
+constexpr int KT = 128;        // k per stage (4 scale groups, half a superblock)
+constexpr int kThreads = 256;  // four wavefronts, each owning its own columns
+constexpr int kWaves = kThreads / 64;
+constexpr int kXcds = 8;       // XCDs of the chip; workgroup i runs on XCD i % 8
 
 struct PrefillParams {
     const uint16_t* A;
@@ -36,38 +51,122 @@ struct PrefillParams {
     Shape sh;
     const int32_t* sorted_ids;
     const int32_t* expert_ids;
+    const int32_t* ntp;  // num_tokens_padded (device) or NULL: every block of the grid may be valid
     int R;
+    int max_blocks;
+    int n_tiles;
     void* out;
 };
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Barrier between stages that leaves direct loads in flight (__syncthreads would drain them): each wavefront has
+// waited for its own loads of the stage; its LDS reads of the previous stage complete before the barrier.
+__device__ __forceinline__ void stage_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt untouched
+    __builtin_amdgcn_s_barrier();
+    __asm__ __volatile__("" ::: "memory");
+}
+
+template <int NBW>
+struct WStage {
+    u32x4 cw[NBW];        // codes of half h of the superblock, per n-block
+    uint32_t sc[NBW][2];  // scales of groups 4h .. 4h+3 of row j, per n-block
+};
+
+// Wavefronts per SIMD a tile shape is built for: two, except the 128 x 64 wavefront tile, whose 128 accumulators
+// plus operands need more than half the register file.
+template <int MT, int NBW>
+constexpr int prefill_waves_per_simd() {
+    return MT * NBW >= 32 ? 1 : 2;
+}
+
 template <int MT, int NBW, int OM>
-__global__ __launch_bounds__(kThreads) void gemm_prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<MT, NBW>())) void gemm_prefill_kernel(PrefillParams p) {
     static_assert(OM != kOutAct || NBW % 2 == 0, "the activation epilogue pairs gate and up n-blocks");
+    if constexpr (prefill_waves_per_simd<MT, NBW>() == 1) {
+        // at one wavefront per SIMD the accumulators go to AGPRs (VGPRs alone stop at 256); naming an AGPR tells
+        // the compiler they may be used
+        __asm__ __volatile__("" ::: "a0");
+    }
     constexpr int BM = 16 * MT;
-    constexpr int XR = BM * (KT / 8) / kThreads;  // 16-byte activation pieces per thread per stage
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDA];
-    __shared__ int srow[BM];
+    constexpr int SLOT = BM * KT * 2;          // bytes of one activation stage
+    constexpr int ROWS_PER_WAVE = BM / kWaves;  // activation rows each wavefront streams
+    constexpr int DMA = ROWS_PER_WAVE / 4;      // direct loads per wavefront per stage (4 rows of 256 B each)
+    static_assert(ROWS_PER_WAVE % 16 == 0, "row permutation assumes 16-row groups per wavefront");
+    // the two ring slots are separate arrays, so the compiler can tell the reads of one from the direct loads
+    // into the other (with one array it would wait for every direct load before any read of the ring)
+    __shared__ __attribute__((aligned(16))) uint8_t slot0[SLOT];
+    __shared__ __attribute__((aligned(16))) uint8_t slot1[SLOT];
     __shared__ int ssid[BM];
 
-    const int b = blockIdx.x;
+    // ---- tile (XCD-aware order over the valid tiles only)
+    const int nblk = p.ntp ? min(__builtin_amdgcn_readfirstlane(*p.ntp) / BM, p.max_blocks) : p.max_blocks;
+    const int V = nblk * p.n_tiles;
+    const int per_xcd = (V + kXcds - 1) / kXcds;
+    const int pos = blockIdx.x / kXcds;
+    const int tile = (blockIdx.x % kXcds) * per_xcd + pos;
+    if (pos >= per_xcd || tile >= V) return;
+    const int b = tile / p.n_tiles, nt = tile % p.n_tiles;
     const int e = p.expert_ids[b];
-    if (e < 0 || e >= p.sh.E) return;  // unowned block (or ids from a larger expert count)
+    if (e < 0 || e >= p.sh.E) return;
+
     const Shape sh = p.sh;
     const int K = sh.K;
-    constexpr int WN = kThreads / 64;
-    const int w = threadIdx.x >> 6, L = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), L = threadIdx.x & 63;
     const int c = L >> 4, j = L & 15;
-    const int wave_global = blockIdx.y * WN + w;  // column group of this wavefront
+    const int wave_global = nt * kWaves + w;
     const int nst = (sh.G + 3) / 4;
 
     for (int m = threadIdx.x; m < BM; m += kThreads) {
         const int sid = p.sorted_ids[b * BM + m];
         ssid[m] = sid < p.R ? sid : -1;
-        srow[m] = sid < p.R ? sid / p.a_row_div : -1;
     }
-    __syncthreads();
 
-    const uint8_t* wbase[NBW];
+    // ---- activation stream: wavefront w fills rows [w*RPW, (w+1)*RPW) of each slot, 4 rows per direct load;
+    // lane L of load r writes row w*RPW + 4r + L/16, physical chunk L%16, which holds chunk (L%16) ^ (row%16)
+    const uint32_t a_bytes = (uint32_t)(p.R / p.a_row_div) * (uint32_t)K * 2u;
+    const __amdgpu_buffer_rsrc_t ares = buffer_resource(p.A, a_bytes);
+    uint32_t a_off[DMA];
+#pragma unroll
+    for (int r = 0; r < DMA; ++r) {
+        const int row = w * ROWS_PER_WAVE + 4 * r + (L >> 4);
+        const int sid = p.sorted_ids[b * BM + row];
+        const int ch = (L & 15) ^ (row & 15);
+        a_off[r] = sid < p.R ? (uint32_t)(sid / p.a_row_div) * (uint32_t)K * 2u + (uint32_t)ch * 16u : kOutOfRange;
+    }
+    // RAGGED: the stage may reach past K (only the last stage of K can); its chunks past K read zeros, with the
+    // whole offset going through the resource's range check
+    auto issue_a = [&](int st, uint8_t* slot_base, auto ragged) {
+        uint8_t* slot = slot_base + w * ROWS_PER_WAVE * KT * 2;
+#pragma unroll
+        for (int r = 0; r < DMA; ++r) {
+            uint32_t off = a_off[r];
+            int soff = st * KT * 2;
+            if constexpr (decltype(ragged)::value) {
+                const int ch = (L & 15) ^ ((4 * r + (L >> 4)) & 15);
+                off = (st * KT + ch * 8 < K && off != kOutOfRange) ? off + (uint32_t)soff : kOutOfRange;
+                soff = 0;
+            }
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ares, (lds_void*)(slot + r * 4 * KT * 2), 16, off, soff, 0, 0);
+        }
+    };
+    auto issue_a_last = [&](int st, uint8_t* slot_base) {  // the last stage of K: ragged or not
+        if ((st + 1) * KT > K) issue_a(st, slot_base, std::true_type{});
+        else issue_a(st, slot_base, std::false_type{});
+    };
+
+    // ---- weight stream: one expert's packed image, per-lane offsets fixed for the whole K loop
+    const uint32_t expert_bytes = (uint32_t)sh.NB * sh.KB * SB_BYTES;
+    const __amdgpu_buffer_rsrc_t wres = buffer_resource(p.packed + (size_t)e * expert_bytes, expert_bytes);
+    uint32_t cw_off[NBW], sc_off[NBW];
 #pragma unroll
     for (int q = 0; q < NBW; ++q) {
         int nb;
@@ -78,36 +177,18 @@ __global__ __launch_bounds__(kThreads) void gemm_prefill_kernel(PrefillParams p)
             nb = wave_global * NBW + q < sh.NB ? wave_global * NBW + q : sh.NB - 1;
         }
         // clamped blocks compute discarded columns
-        wbase[q] = p.packed + ((size_t)e * sh.NB + nb) * sh.KB * SB_BYTES;
+        cw_off[q] = (uint32_t)nb * sh.KB * SB_BYTES + (uint32_t)L * 16u;
+        sc_off[q] = (uint32_t)nb * sh.KB * SB_BYTES + SB_CODE_BYTES + (uint32_t)j * 16u;
     }
-
-    auto load_x = [&](int st, u32x4* regs) {
-#pragma unroll
-        for (int r = 0; r < XR; ++r) {
-            const int x = threadIdx.x + r * kThreads;
-            const int m = x >> 4, ch = x & 15;
-            const int k0 = st * KT + ch * 8;
-            const int row = srow[m];
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (row >= 0 && k0 < K) v = *reinterpret_cast<const u32x4*>(p.A + (size_t)row * K + k0);
-            regs[r] = v;
-        }
-    };
-    auto store_x = [&](uint16_t* buf, const u32x4* regs) {
-#pragma unroll
-        for (int r = 0; r < XR; ++r) {
-            const int x = threadIdx.x + r * kThreads;
-            const int m = x >> 4, ch = x & 15;
-            *reinterpret_cast<u32x4*>(&buf[m * LDA + ch * 8]) = regs[r];
-        }
-    };
-    auto load_w = [&](int st, u32x4* cw, u32x4* sc) {
+    auto load_w = [&](int st, WStage<NBW>& W) {
         const int kb = st >> 1, h = st & 1;
 #pragma unroll
         for (int q = 0; q < NBW; ++q) {
-            const uint8_t* sbp = wbase[q] + (size_t)kb * SB_BYTES;
-            cw[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sbp + h * 1024 + L * 16));
-            sc[q] = *reinterpret_cast<const u32x4*>(sbp + SB_CODE_BYTES + j * 16);
+            W.cw[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    wres, cw_off[q], kb * SB_BYTES + h * 1024, kBufferNonTemporal));
+            const auto sv = __builtin_amdgcn_raw_buffer_load_b64(wres, sc_off[q], kb * SB_BYTES + h * 8, 0);
+            W.sc[q][0] = sv[0];
+            W.sc[q][1] = sv[1];
         }
     };
 
@@ -117,49 +198,87 @@ __global__ __launch_bounds__(kThreads) void gemm_prefill_kernel(PrefillParams p)
 #pragma unroll
         for (int q = 0; q < NBW; ++q) acc[mt][q] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto group = [&](const uint16_t* buf, int g, int gs, const u32x4* cw, const u32x4* sc) {
-        bf16x8 wf[NBW];
+    auto dequant_group = [&](const WStage<NBW>& W, int g, bf16x8* wf) {
 #pragma unroll
         for (int q = 0; q < NBW; ++q) {
-            const float s = group_scale(sc[q], gs);
-            wf[q] = dequant8(cw[q][g], s, -8.0f * s);
-        }
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const bf16x8 af = *reinterpret_cast<const bf16x8*>(&buf[(mt * 16 + j) * LDA + 32 * g + 8 * c]);
-#pragma unroll
-            for (int q = 0; q < NBW; ++q) acc[mt][q] = mfma16(af, wf[q], acc[mt][q]);
+            const uint32_t word = W.sc[q][g >> 1];
+            const float s = __uint_as_float((g & 1) ? (word & 0xFFFF0000u) : (word << 16));
+            wf[q] = dequant8(W.cw[q][g], s, -8.0f * s);
         }
     };
-    u32x4 xr[XR];
-    auto stage = [&](int st, const u32x4* cw, const u32x4* sc, u32x4* cwn, u32x4* scn) {
-        const bool more = st + 1 < nst;
-        if (more) {
-            load_x(st + 1, xr);
-            load_w(st + 1, cwn, scn);
-        }
-        const uint16_t* buf = As[st & 1];
-        const int g0 = (st & 1) * 4;
-        // a ragged last stage computes its padding groups too: their codes are 8 and scales 0 in the packed
-        // image and their activations are zero in LDS, so they add exactly zero
+    // multiply the stage in LDS slot `slot` with the weights W.  A ragged last stage computes its padding groups
+    // too: their codes are 8 and scales 0 in the packed image (weight 0) and their activations are zero.
+    // Software-pipelined by scale group: while the MFMAs of group g run, the activation fragments of group g+1
+    // are read from LDS and its weights dequantised, so neither the LDS latency nor the conversion stalls them.
+    auto compute = [&](const uint8_t* slot, const WStage<NBW>& W) {
+        bf16x8 af[2][MT];
+        bf16x8 wf[2][NBW];
+        auto read_a = [&](int g, bf16x8* out) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) group(buf, g, g0 + g, cw, sc);
-        if (more) store_x(As[(st + 1) & 1], xr);
-        __syncthreads();
+            for (int mt = 0; mt < MT; ++mt)
+                out[mt] = *reinterpret_cast<const bf16x8*>(slot + (mt * 16 + j) * (KT * 2) + (((4 * g + c) ^ j) * 16));
+        };
+        read_a(0, af[0]);
+        dequant_group(W, 0, wf[0]);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            if (g < 3) {
+                read_a(g + 1, af[(g + 1) & 1]);
+                dequant_group(W, g + 1, wf[(g + 1) & 1]);
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int q = 0; q < NBW; ++q) acc[mt][q] = mfma16(af[g & 1][mt], wf[g & 1][q], acc[mt][q]);
+        }
     };
+    // one stage: wait for this wavefront's activation loads of stage st, barrier (all pieces landed; the other
+    // slot is no longer read), start stage st+1's loads into the other slot and register set, multiply stage st
+    // NEXT: 0 = stage st is the last, 1 = stage st+1 is a full stage, 2 = stage st+1 is the last stage of K
+    auto stage = [&](int st, const uint8_t* cur, uint8_t* next, const WStage<NBW>& W, WStage<NBW>& Wn, auto next_kind) {
+        constexpr int NEXT = decltype(next_kind)::value;
+        // The wait counts on the issue order pinned below: a stage's activation loads, then its 2*NBW weight
+        // loads, so once at most 2*NBW loads are pending the activation loads of stage st have landed.
+        wait_vmcnt<2 * NBW>();
+        stage_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (NEXT == 1) issue_a(st + 1, next, std::false_type{});
+        if constexpr (NEXT == 2) issue_a_last(st + 1, next);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (NEXT != 0) load_w(st + 1, Wn);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(cur, W);
+    };
+    using none = std::integral_constant<int, 0>;
+    using full = std::integral_constant<int, 1>;
+    using last = std::integral_constant<int, 2>;
 
-    u32x4 cwA[NBW], scA[NBW], cwB[NBW], scB[NBW];
-    load_x(0, xr);
-    load_w(0, cwA, scA);
-    store_x(As[0], xr);
-    __syncthreads();
-    // pairs of stages alternate the two register sets (no copies between them)
-    for (int st = 0; st < nst; st += 2) {
-        stage(st, cwA, scA, cwB, scB);
-        if (st + 1 < nst) stage(st + 1, cwB, scB, cwA, scA);
+    // Pairs of stages alternate the two slots and the two weight register sets (no copies between them).  The
+    // loop's loads are never for the last stage, so it has no branches (a branch around loads would make the
+    // compiler assume the worst count of loads in flight and drain them); the last one to three stages are peeled.
+    WStage<NBW> WA, WB;
+    if (nst == 1) issue_a_last(0, slot0);
+    else issue_a(0, slot0, std::false_type{});
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(0, WA);
+    __builtin_amdgcn_sched_barrier(0);
+    int st = 0;
+    for (; st + 3 < nst; st += 2) {
+        stage(st, slot0, slot1, WA, WB, full{});
+        stage(st + 1, slot1, slot0, WB, WA, full{});
+    }
+    if (st + 3 == nst) {
+        stage(st, slot0, slot1, WA, WB, full{});
+        stage(st + 1, slot1, slot0, WB, WA, last{});
+        stage(st + 2, slot0, slot1, WA, WB, none{});
+    } else if (st + 2 == nst) {
+        stage(st, slot0, slot1, WA, WB, last{});
+        stage(st + 1, slot1, slot0, WB, WA, none{});
+    } else {
+        stage(st, slot0, slot1, WA, WB, none{});
     }
 
-    // epilogue: lane holds rows 4c + r of each 16-row tile, column j of each n-block
+    // ---- epilogue: lane holds rows 4c + r of each 16-row tile, column j of each n-block
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -191,10 +310,14 @@ __global__ __launch_bounds__(kThreads) void gemm_prefill_kernel(PrefillParams p)
 
 template <int MT, int NBW, int OM>
 hipError_t launch_t(const GemmArgs& a, hipStream_t s) {
-    PrefillParams p{a.A, a.a_row_div, static_cast<const uint8_t*>(a.packed), a.sh, a.sorted_ids, a.expert_ids, a.R,
-                    a.out};
-    constexpr int cols = (kThreads / 64) * NBW;
-    const dim3 grid(a.max_blocks, (a.sh.NB + cols - 1) / cols);
+    constexpr int cols = kWaves * NBW;  // n-blocks of weight columns per workgroup
+    const int n_tiles = (a.sh.NB + cols - 1) / cols;
+    PrefillParams p{a.A,          a.a_row_div, static_cast<const uint8_t*>(a.packed), a.sh, a.sorted_ids,
+                    a.expert_ids, a.ntp,       a.R,  a.max_blocks, n_tiles, a.out};
+    // a multiple of the XCD count: tile t runs on workgroup (t % per_xcd) * 8 + t / per_xcd, which can reach
+    // 8 * ceil(tiles / 8) - 1
+    const unsigned tiles = (unsigned)a.max_blocks * (unsigned)n_tiles;
+    const dim3 grid((tiles + kXcds - 1) / kXcds * kXcds);
     hipLaunchKernelGGL((gemm_prefill_kernel<MT, NBW, OM>), grid, dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
@@ -209,6 +332,11 @@ hipError_t dispatch(const GemmArgs& a, int mt, int nbw, hipStream_t s) {
 }
 
 }  // namespace
+
+bool prefill_supported(const GemmArgs& a) {
+    // the buffer resources address below 2 GiB: one expert's packed weights, and the activation matrix
+    return (size_t)a.sh.NB * a.sh.KB * SB_BYTES < (1u << 31) && (size_t)(a.R / a.a_row_div) * a.sh.K * 2 < (1u << 31);
+}
 
 hipError_t launch_gemm_prefill(const GemmArgs& a, const w4a16_plan& p, hipStream_t s) {
     if (a.max_blocks == 0) return hipSuccess;

@@ -144,7 +144,8 @@ __global__ __launch_bounds__(kThreads) void route_prep_kernel(const int32_t* __r
 __global__ __launch_bounds__(kThreads) void offsets_to_route_kernel(const int32_t* __restrict__ off, int E,
                                                                     int rows_max, int BM, int max_padded,
                                                                     int max_blocks, int32_t* __restrict__ sorted_ids,
-                                                                    int32_t* __restrict__ expert_ids) {
+                                                                    int32_t* __restrict__ expert_ids,
+                                                                    int32_t* __restrict__ ntp) {
     extern __shared__ int smem[];
     int* pad_off = smem;            // E+1
     int* wave_tot = pad_off + E + 1;  // kWaves+1
@@ -158,7 +159,10 @@ __global__ __launch_bounds__(kThreads) void offsets_to_route_kernel(const int32_
     int tot_p;
     const int off_p = block_exclusive_scan(padded, wave_tot, &tot_p);
     if (tid < E) pad_off[tid] = off_p;
-    if (tid == 0) pad_off[E] = tot_p;
+    if (tid == 0) {
+        pad_off[E] = tot_p;
+        *ntp = tot_p < max_padded ? tot_p : max_padded;
+    }
     __syncthreads();
     for (int p = tid; p < max_padded; p += kThreads) {
         int v = rows_max;
@@ -204,10 +208,11 @@ hipError_t launch_route_prep(const int32_t* topk_ids, int R, int E, int block_m,
 }
 
 hipError_t launch_offsets_to_route(const int32_t* offsets, int E, int rows_max, int block_m, int max_padded,
-                                   int max_blocks, int32_t* sorted_ids, int32_t* expert_ids, hipStream_t s) {
+                                   int max_blocks, int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntp,
+                                   hipStream_t s) {
     const size_t shmem = sizeof(int) * ((size_t)E + 1 + kWaves + 1);
     hipLaunchKernelGGL(offsets_to_route_kernel, dim3(1), dim3(kThreads), shmem, s, offsets, E, rows_max, block_m,
-                       max_padded, max_blocks, sorted_ids, expert_ids);
+                       max_padded, max_blocks, sorted_ids, expert_ids, ntp);
     return hipGetLastError();
 }
 

@@ -95,7 +95,8 @@ hipError_t launch_route_prep(const int32_t* topk_ids, int R, int E, int block_m,
                              int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntp, int32_t* offsets,
                              int32_t* counts, hipStream_t s);
 hipError_t launch_offsets_to_route(const int32_t* offsets, int E, int rows_max, int block_m, int max_padded,
-                                   int max_blocks, int32_t* sorted_ids, int32_t* expert_ids, hipStream_t s);
+                                   int max_blocks, int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntp,
+                                   hipStream_t s);
 
 struct GemmArgs {
     const uint16_t* A;
@@ -108,6 +109,7 @@ struct GemmArgs {
     int max_blocks;    // route blocks (grid.x)
     void* out;         // BF16 bits [R,N], float [R,N], or BF16 bits [R,N/2] (activation mode)
     int out_mode;      // kOutBf16, kOutF32 or kOutAct
+    const int32_t* ntp = nullptr;  // num_tokens_padded (device) when known: bounds the valid route blocks
     float* partials = nullptr;     // split-K partial tiles (decode, k_split > 1)
     unsigned* counters = nullptr;  // split-K arrival counters, zero between calls
 };
@@ -120,6 +122,7 @@ hipError_t launch_gemm_decode(const GemmArgs& a, const w4a16_plan& p, hipStream_
 bool decode_reg_supported(const GemmArgs& a, const w4a16_plan& p);
 hipError_t launch_gemm_decode_reg(const GemmArgs& a, const w4a16_plan& p, hipStream_t s);
 hipError_t launch_gemm_prefill(const GemmArgs& a, const w4a16_plan& p, hipStream_t s);
+bool prefill_supported(const GemmArgs& a);
 hipError_t launch_silu_mul(const uint16_t* gu, int rows, int I, uint16_t* h, hipStream_t s);
 hipError_t launch_silu_mul_f32(const float* gu, int rows, int I, uint16_t* h, hipStream_t s);
 hipError_t launch_combine(const float* y, const float* tw, const int32_t* ids, int T, int k, int E, int H,
