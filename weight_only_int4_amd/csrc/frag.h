@@ -74,27 +74,42 @@ __device__ __forceinline__ float group_scale(u32x4 sc, int g) {
     return __uint_as_float((g & 1) ? (word & 0xFFFF0000u) : (word << 16));
 }
 
-// Eight fully dequantised weights bf16((q - 8) * s) of one packed word.
-// (q - 8) * s is formed exactly by one fused multiply-add, q * s + (-8 s)
-// (the product needs at most 12 significant bits), then rounded once to BF16
-// with round-to-nearest-even.
+// Hides a value from the optimiser (no instruction is emitted).  Used on the
+// byte-masked code words below: otherwise LLVM folds "(w & 0x0F0F0F0F) then
+// byte i" into a separate shift-and-mask per code, losing the one-instruction
+// byte conversions v_cvt_f32_ubyte1..3.
+__device__ __forceinline__ uint32_t opaque_u32(uint32_t x) {
+    __asm__("" : "+v"(x));
+    return x;
+}
+
+// Two floats to a packed pair of BF16 values, round to nearest even (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+// Eight fully dequantised weights bf16((q - 8) * s) of one packed word, in 23
+// VALU operations: two byte masks split the word into the codes 0, 4, 1, 5
+// and 2, 6, 3, 7 (one per byte), v_cvt_f32_ubyte0..3 convert them, one fused
+// multiply-add q * s + (-8 s) forms (q - 8) * s exactly (the product needs at
+// most 12 significant bits), and each pair is rounded once to BF16 (round to
+// nearest even).
 __device__ __forceinline__ bf16x8 dequant8(uint32_t w, float s, float neg8s) {
-    const uint32_t lo = w & 0x0F0F0F0Fu;         // codes 0, 4, 1, 5 in bytes 0..3
-    const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // codes 2, 6, 3, 7 in bytes 0..3
+    const uint32_t lo = opaque_u32(w & 0x0F0F0F0Fu);         // codes 0, 4, 1, 5 in bytes 0..3
+    const uint32_t hi = opaque_u32((w >> 4) & 0x0F0F0F0Fu);  // codes 2, 6, 3, 7 in bytes 0..3
     const float q0 = (float)(lo & 0xFFu), q4 = (float)((lo >> 8) & 0xFFu);
     const float q1 = (float)((lo >> 16) & 0xFFu), q5 = (float)(lo >> 24);
     const float q2 = (float)(hi & 0xFFu), q6 = (float)((hi >> 8) & 0xFFu);
     const float q3 = (float)((hi >> 16) & 0xFFu), q7 = (float)(hi >> 24);
-    bf16x8 r;
-    r[0] = (__bf16)__builtin_fmaf(q0, s, neg8s);
-    r[1] = (__bf16)__builtin_fmaf(q1, s, neg8s);
-    r[2] = (__bf16)__builtin_fmaf(q2, s, neg8s);
-    r[3] = (__bf16)__builtin_fmaf(q3, s, neg8s);
-    r[4] = (__bf16)__builtin_fmaf(q4, s, neg8s);
-    r[5] = (__bf16)__builtin_fmaf(q5, s, neg8s);
-    r[6] = (__bf16)__builtin_fmaf(q6, s, neg8s);
-    r[7] = (__bf16)__builtin_fmaf(q7, s, neg8s);
-    return r;
+    u32x4 v;
+    v.x = pack_bf16x2(__builtin_fmaf(q0, s, neg8s), __builtin_fmaf(q1, s, neg8s));
+    v.y = pack_bf16x2(__builtin_fmaf(q2, s, neg8s), __builtin_fmaf(q3, s, neg8s));
+    v.z = pack_bf16x2(__builtin_fmaf(q4, s, neg8s), __builtin_fmaf(q5, s, neg8s));
+    v.w = pack_bf16x2(__builtin_fmaf(q6, s, neg8s), __builtin_fmaf(q7, s, neg8s));
+    return __builtin_bit_cast(bf16x8, v);
 }
 
 // Buffer resources (raw, unformatted, unswizzled) on gfx9-family chips: word 3 of the descriptor, the cache
