@@ -65,7 +65,9 @@ enum { W4A16_KERNEL_DECODE = 1, W4A16_KERNEL_PREFILL = 2 };
  * for the routing tensors passed with it. */
 typedef struct w4a16_plan {
     int32_t kernel;        /* W4A16_KERNEL_DECODE or W4A16_KERNEL_PREFILL */
-    int32_t block_m;       /* rows per route block: 16, 32, 48 or 64 (decode); 64 or 128 (prefill) */
+    int32_t block_m;       /* rows per route block: 16, 32, 48 or 64 (decode); 32, 64 or 128 (prefill;
+                              with 32, a workgroup takes up to 128 rows (n_blocks 2) or 64 rows
+                              (n_blocks 4) of consecutive blocks of one expert) */
     int32_t n_blocks;      /* 16-column blocks per wavefront: 1, 2 or 4 */
     int32_t waves;         /* wavefronts per workgroup, each owning its own columns: 4 */
     int32_t k_split;       /* decode: workgroups sharing one output tile along K (1..64); prefill: 1 */
@@ -174,6 +176,7 @@ int w4a16_plan_select(int T, int k, int E, int N, int K, float expected_rows_per
  *              are skipped)
  *   out        device BF16 bits [R, N]; rows of invalid routes untouched
  *   ws         workspace of w4a16_gemm_workspace_bytes (may be NULL if 0).  A
+ *              prefill plan with block_m 32 builds its tile list there.  A
  *              plan with k_split > 1 keeps per-tile arrival counters in it:
  *              the workspace must be zero-filled once before its first use,
  *              and every call leaves the counters at zero again.  Calls that

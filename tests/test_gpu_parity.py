@@ -108,7 +108,8 @@ def test_route_prep_bit_exact(orc, name, gen, E, BM):
 DECODE_PLANS = ([("decode", bm, nbw, 4, 1) for bm in (16, 32, 48, 64) for nbw in (1, 2, 4)]
                 + [("decode", 16, 4, 4, 2), ("decode", 32, 2, 4, 2), ("decode", 64, 1, 4, 2),
                    ("decode", 16, 1, 4, 3)])  # 3 slices of a 2-stage K: one slice is empty
-PREFILL_PLANS = [("prefill", bm, nbw, 4, 1) for bm in (64, 128) for nbw in (2, 4)]
+PREFILL_PLANS = ([("prefill", bm, nbw, 4, 1) for bm in (64, 128) for nbw in (2, 4)]
+                 + [("prefill", 32, 2, 4, 1), ("prefill", 32, 4, 4, 1)])  # 32-row blocks in 128- / 64-row tiles
 PLAN_ID = lambda p: "%s-bm%d-nb%d-w%d-ks%d" % p  # noqa: E731
 
 
@@ -133,7 +134,8 @@ def test_gemm_tiny_all_plans(orc, plan_args):
 
 
 @pytest.mark.parametrize("plan_args", [("decode", 16, 4, 4, 1), ("decode", 64, 2, 4, 1), ("decode", 16, 4, 4, 3),
-                                       ("decode", 32, 2, 4, 7), ("prefill", 64, 4, 4, 1), ("prefill", 128, 2, 4, 1)],
+                                       ("decode", 32, 2, 4, 7), ("prefill", 64, 4, 4, 1), ("prefill", 128, 2, 4, 1),
+                                       ("prefill", 32, 2, 4, 1)],
                          ids=PLAN_ID)
 @pytest.mark.parametrize("shape", [(24, 6, 2, 40, 512), (9, 4, 3, 64, 96), (70, 3, 2, 16, 2048),
                                    (5, 10, 8, 4096, 7168)], ids=lambda s: "T%d-E%d-k%d-N%d-K%d" % s)
@@ -184,7 +186,8 @@ EDGE = ["E1", "one hot expert", "empty and single", "ragged N and K", "tile edge
 
 
 @pytest.mark.parametrize("plan_args", [("decode", 16, 1, 4, 1), ("decode", 32, 4, 4, 1), ("decode", 64, 2, 4, 1),
-                                       ("decode", 16, 2, 4, 2), ("prefill", 64, 2, 4, 1), ("prefill", 128, 4, 4, 1)],
+                                       ("decode", 16, 2, 4, 2), ("prefill", 64, 2, 4, 1), ("prefill", 128, 4, 4, 1),
+                                       ("prefill", 32, 2, 4, 1), ("prefill", 32, 4, 4, 1)],
                          ids=PLAN_ID)
 @pytest.mark.parametrize("kind", EDGE)
 def test_gemm_edge_cases(orc, kind, plan_args):
@@ -225,9 +228,32 @@ def test_gemm_is_deterministic_and_permutation_equivariant(orc):
         assert np.array_equal(c, a[route_perm])
 
 
+@pytest.mark.parametrize("plan_args", [("prefill", 32, 2, 4, 1), ("prefill", 32, 4, 4, 1)], ids=PLAN_ID)
+def test_gemm_prefill_tile_list(orc, plan_args):
+    # 32-row route blocks gathered into taller tiles: experts whose block runs are 1 .. 9 blocks long (every
+    # tile height, runs cut into several tiles, empty experts) and more than 1024 valid blocks, so runs and tiles
+    # cross the 1024-block chunks of the tile-list scan
+    _say("gemm prefill tile list %s" % (plan_args,))
+    rng = np.random.default_rng(4242)
+    E, N, K = 420, 32, 64
+    runs = rng.integers(0, 10, E)                              # route blocks per expert, 0 .. 9
+    counts = np.where(runs > 0, 32 * runs - rng.integers(0, 32, E), 0)
+    ids = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(counts)])
+    ids = ids[rng.permutation(ids.size)].reshape(-1, 1)
+    assert int(runs.sum()) > 1100
+    x = synth.activations(rng, ids.shape[0], K)
+    case = synth.GemmCase("tile list", x, 1, synth.codes(rng, E, N, K), synth.scales(rng, E, N, K), ids)
+    plan = w4.make_plan(*plan_args)
+    got = _run_gemm(case, plan)
+    acc, _ = orc.grouped_gemm(case.A, 1, case.codes, case.scales, case.topk_ids, acc64=True)
+    worst = check_gemm(got, acc, case.topk_ids, case.E, label="tile list")
+    _say("  worst ratio %.2e" % worst)
+
+
 # ------------------------------------------------------------------ offsets form
 
-@pytest.mark.parametrize("plan_args", [("decode", 16, 4, 4, 1), ("decode", 16, 2, 4, 2), ("prefill", 64, 4, 4, 1)],
+@pytest.mark.parametrize("plan_args", [("decode", 16, 4, 4, 1), ("decode", 16, 2, 4, 2), ("prefill", 64, 4, 4, 1),
+                                       ("prefill", 32, 2, 4, 1)],
                          ids=PLAN_ID)
 def test_gemm_offsets_form(orc, plan_args):
     rng = np.random.default_rng(99)
@@ -251,7 +277,7 @@ def test_gemm_offsets_form(orc, plan_args):
 
 ACT_PLANS = [("decode", 16, 2, 4, 1), ("decode", 16, 4, 4, 1), ("decode", 48, 4, 4, 1), ("decode", 32, 4, 4, 2),
              ("decode", 64, 2, 4, 3), ("prefill", 64, 2, 4, 1), ("prefill", 64, 4, 4, 1), ("prefill", 128, 4, 4, 1),
-             ("prefill", 128, 2, 4, 1)]
+             ("prefill", 128, 2, 4, 1), ("prefill", 32, 2, 4, 1), ("prefill", 32, 4, 4, 1)]
 
 
 @pytest.mark.parametrize("plan_args", ACT_PLANS, ids=PLAN_ID)

@@ -153,8 +153,8 @@ int validate_plan(const w4a16_plan* p, const char* what) {
             return fail(W4A16_UNSUPPORTED_SHAPE, "%s: decode k_split %d not in 1..64", what, p->k_split);
         if (p->waves != 4) return fail(W4A16_UNSUPPORTED_SHAPE, "%s: decode waves must be 4", what);
     } else if (p->kernel == W4A16_KERNEL_PREFILL) {
-        if (p->block_m != 64 && p->block_m != 128)
-            return fail(W4A16_UNSUPPORTED_SHAPE, "%s: prefill block_m %d not in {64,128}", what, p->block_m);
+        if (p->block_m != 32 && p->block_m != 64 && p->block_m != 128)
+            return fail(W4A16_UNSUPPORTED_SHAPE, "%s: prefill block_m %d not in {32,64,128}", what, p->block_m);
         if (p->n_blocks != 2 && p->n_blocks != 4)
             return fail(W4A16_UNSUPPORTED_SHAPE, "%s: prefill n_blocks %d not in {2,4}", what, p->n_blocks);
         if (p->k_split != 1) return fail(W4A16_UNSUPPORTED_SHAPE, "%s: prefill k_split must be 1", what);
@@ -167,23 +167,40 @@ int validate_plan(const w4a16_plan* p, const char* what) {
 
 // Split-K workspace of one GEMM: arrival counters first (so that GEMMs sharing a
 // workspace find them at the same place, all zero), then the partial tiles.
+// A prefill plan whose workgroup tile spans several route blocks also needs a tile list after the split-K area:
+// its length (one int, padded to 16 bytes), then (first block, blocks) per tile, at most one tile per block.
 struct GemmWs {
-    size_t counter_bytes, partial_bytes, total;
+    size_t counter_bytes, partial_bytes, tile_bytes, total;
 };
+
+bool tiled_prefill(const w4a16_plan& p) {
+    return p.kernel == W4A16_KERNEL_PREFILL && prefill_tile_rows(p) != p.block_m;
+}
 
 GemmWs gemm_ws(const Shape& sh, const w4a16_plan& p, int max_blocks) {
     GemmWs g;
     g.counter_bytes = align_up(sizeof(unsigned) * decode_counters(sh, p, max_blocks), 256);
     g.partial_bytes = align_up(sizeof(float) * decode_partial_floats(sh, p, max_blocks), 256);
-    g.total = g.counter_bytes + g.partial_bytes;
+    g.tile_bytes = tiled_prefill(p) ? align_up(sizeof(int32_t) * (4 + 2 * (size_t)max_blocks), 256) : 0;
+    g.total = g.counter_bytes + g.partial_bytes + g.tile_bytes;
     return g;
 }
 
-// counters at ws, partials at ws + partial_offset
-void bind_ws(GemmArgs& a, const GemmWs& g, void* ws, size_t partial_offset) {
-    if (g.total == 0) return;
-    a.counters = static_cast<unsigned*>(ws);
-    a.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + partial_offset);
+// counters at ws, partials at ws + partial_offset, the tile list at tiles
+void bind_ws(GemmArgs& a, const GemmWs& g, void* ws, size_t partial_offset, void* tiles) {
+    if (g.counter_bytes + g.partial_bytes) {
+        a.counters = static_cast<unsigned*>(ws);
+        a.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + partial_offset);
+    }
+    if (g.tile_bytes) {
+        a.tile_count = static_cast<int32_t*>(tiles);
+        a.tiles = static_cast<int32_t*>(tiles) + 4;
+    }
+}
+
+// standalone layout: counters | partials | tile list
+void bind_ws(GemmArgs& a, const GemmWs& g, void* ws) {
+    bind_ws(a, g, ws, g.counter_bytes, static_cast<char*>(ws) + g.counter_bytes + g.partial_bytes);
 }
 
 hipError_t run_gemm(const GemmArgs& a, const w4a16_plan& p, hipStream_t s) {
@@ -193,16 +210,18 @@ hipError_t run_gemm(const GemmArgs& a, const w4a16_plan& p, hipStream_t s) {
 // Workspace carve-up of the fused expert MLP.
 struct FusedLayout {
     int maxP, maxB;
-    size_t off_sorted, off_eids, off_ntp, off_offsets, off_counts, off_h, off_y, off_split, total;
+    size_t off_sorted, off_eids, off_ntp, off_offsets, off_counts, off_h, off_y, off_split, off_tiles, total;
 };
 
 // The split-K area goes first so its counters sit at a fixed place regardless of the route block.
-FusedLayout fused_layout(int T, int k, int E, int H, int I, int BM, size_t split_bytes) {
+// The two GEMMs run one after the other on one stream, so they share one tile-list area.
+FusedLayout fused_layout(int T, int k, int E, int H, int I, int BM, size_t split_bytes, size_t tile_bytes) {
     FusedLayout f;
     route_bounds(T, k, E, BM, &f.maxP, &f.maxB);
     const size_t R = (size_t)T * k;
     size_t o = 0;
     f.off_split = o;  o = align_up(o + split_bytes, 256);
+    f.off_tiles = o;  o = align_up(o + tile_bytes, 256);
     f.off_sorted = o; o = align_up(o + sizeof(int32_t) * (size_t)f.maxP, 256);
     f.off_eids = o;   o = align_up(o + sizeof(int32_t) * (size_t)f.maxB, 256);
     f.off_ntp = o;    o = align_up(o + sizeof(int32_t), 256);
@@ -400,7 +419,7 @@ static int grouped_gemm_impl(const char* what, const uint16_t* A, int a_row_div,
     a.ntp = ntp;
     rc = check_prefill_shape(what, a, *p);
     if (rc) return rc;
-    bind_ws(a, g, ws, g.counter_bytes);
+    bind_ws(a, g, ws);
     return check_launch(run_gemm(a, *p, s), what);
 }
 
@@ -481,7 +500,7 @@ int w4a16_grouped_gemm_offsets(const uint16_t* A_sorted, const int32_t* expert_o
                                               expert_ids, ntp, s),
                       what);
     if (rc) return rc;
-    bind_ws(a, g, ws, g.counter_bytes);
+    bind_ws(a, g, ws);
     return check_launch(run_gemm(a, *p, s), what);
 }
 
@@ -521,7 +540,8 @@ static FusedLayout fused_full_layout(int T, int k, const w4a16_weights* w13, con
     const GemmWs a = gemm_ws(w13->shape, p13, maxB), b = gemm_ws(w2->shape, p2, maxB);
     *counter_bytes = a.counter_bytes > b.counter_bytes ? a.counter_bytes : b.counter_bytes;
     const size_t partial_bytes = a.partial_bytes > b.partial_bytes ? a.partial_bytes : b.partial_bytes;
-    return fused_layout(T, k, E, H, I, p13.block_m, *counter_bytes + partial_bytes);
+    const size_t tile_bytes = a.tile_bytes > b.tile_bytes ? a.tile_bytes : b.tile_bytes;
+    return fused_layout(T, k, E, H, I, p13.block_m, *counter_bytes + partial_bytes, tile_bytes);
 }
 
 int w4a16_fused_moe_workspace_bytes(int T, int k, const w4a16_weights* w13, const w4a16_weights* w2, size_t* bytes) {
@@ -631,11 +651,11 @@ int w4a16_fused_moe_profiled(const uint16_t* x, const int32_t* topk_ids, const f
                       "w4a16_fused_moe (route_prep)");
     if (rc) return rc;
     W4A16_STAGE(1);
-    bind_ws(g13, gemm_ws(w13->shape, p13, f.maxB), base + f.off_split, counter_bytes);
+    bind_ws(g13, gemm_ws(w13->shape, p13, f.maxB), base + f.off_split, counter_bytes, base + f.off_tiles);
     rc = check_launch(run_gemm(g13, p13, s), "w4a16_fused_moe (gate_up + silu_mul)");
     if (rc) return rc;
     W4A16_STAGE(2);
-    bind_ws(g2, gemm_ws(w2->shape, p2, f.maxB), base + f.off_split, counter_bytes);
+    bind_ws(g2, gemm_ws(w2->shape, p2, f.maxB), base + f.off_split, counter_bytes, base + f.off_tiles);
     rc = check_launch(run_gemm(g2, p2, s), "w4a16_fused_moe (down)");
     if (rc) return rc;
     W4A16_STAGE(3);

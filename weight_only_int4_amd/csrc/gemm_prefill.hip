@@ -6,6 +6,11 @@
 //    expert_ids[block] in-kernel, so no host synchronisation is needed (Chord
 //    page, "Two kernel families"; the nf4 page, "How it works", finds its
 //    tiles in-kernel the same way).
+//  * With 32-row route blocks, a workgroup takes a tile of up to BM/32
+//    consecutive blocks of one expert from a tile list built on the device,
+//    and runs a body specialised for the tile's height.  Padding then costs
+//    at most 31 rows per expert instead of BM-1, while the dequantisation is
+//    still shared by all rows of the tile.
 //  * Tile order is XCD-aware.  Consecutive workgroup ids go to the eight XCDs
 //    in turn, so id -> (XCD, position) is remapped to give every XCD one
 //    contiguous run of tiles, route block major: the ~64 workgroups an XCD
@@ -56,6 +61,8 @@ struct PrefillParams {
     int max_blocks;
     int n_tiles;
     void* out;
+    const int32_t* tiles;       // tile list (first route block, blocks), or NULL: one route block of BM rows per tile
+    const int32_t* tile_count;  // its length (device)
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -88,36 +95,15 @@ constexpr int prefill_waves_per_simd() {
     return MT * NBW >= 32 ? 1 : 2;
 }
 
-template <int MT, int NBW, int OM>
-__global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<MT, NBW>())) void gemm_prefill_kernel(PrefillParams p) {
-    static_assert(OM != kOutAct || NBW % 2 == 0, "the activation epilogue pairs gate and up n-blocks");
-    if constexpr (prefill_waves_per_simd<MT, NBW>() == 1) {
-        // at one wavefront per SIMD the accumulators go to AGPRs (VGPRs alone stop at 256); naming an AGPR tells
-        // the compiler they may be used
-        __asm__ __volatile__("" ::: "a0");
-    }
-    constexpr int BM = 16 * MT;
-    constexpr int SLOT = BM * KT * 2;          // bytes of one activation stage
+// One tile: 16*MTA rows starting at route slot row0, all of them of expert e, times the column tile nt.  The
+// LDS ring and the row table are the kernel's (sized for its largest tile).
+template <int MTA, int NBW, int OM>
+__device__ __forceinline__ void prefill_tile(const PrefillParams& p, uint8_t* slot0, uint8_t* slot1, int* ssid,
+                                             int row0, int e, int nt) {
+    constexpr int BM = 16 * MTA;                // rows of this tile
     constexpr int ROWS_PER_WAVE = BM / kWaves;  // activation rows each wavefront streams
     constexpr int DMA = ROWS_PER_WAVE / 4;      // direct loads per wavefront per stage (4 rows of 256 B each)
-    static_assert(ROWS_PER_WAVE % 16 == 0, "row permutation assumes 16-row groups per wavefront");
-    // the two ring slots are separate arrays, so the compiler can tell the reads of one from the direct loads
-    // into the other (with one array it would wait for every direct load before any read of the ring)
-    __shared__ __attribute__((aligned(16))) uint8_t slot0[SLOT];
-    __shared__ __attribute__((aligned(16))) uint8_t slot1[SLOT];
-    __shared__ int ssid[BM];
-
-    // ---- tile (XCD-aware order over the valid tiles only)
-    const int nblk = p.ntp ? min(__builtin_amdgcn_readfirstlane(*p.ntp) / BM, p.max_blocks) : p.max_blocks;
-    const int V = nblk * p.n_tiles;
-    const int per_xcd = (V + kXcds - 1) / kXcds;
-    const int pos = blockIdx.x / kXcds;
-    const int tile = (blockIdx.x % kXcds) * per_xcd + pos;
-    if (pos >= per_xcd || tile >= V) return;
-    const int b = tile / p.n_tiles, nt = tile % p.n_tiles;
-    const int e = p.expert_ids[b];
-    if (e < 0 || e >= p.sh.E) return;
-
+    static_assert(ROWS_PER_WAVE % 4 == 0, "a direct load fills four rows");
     const Shape sh = p.sh;
     const int K = sh.K;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), L = threadIdx.x & 63;
@@ -126,7 +112,7 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<MT, NBW>())) void
     const int nst = (sh.G + 3) / 4;
 
     for (int m = threadIdx.x; m < BM; m += kThreads) {
-        const int sid = p.sorted_ids[b * BM + m];
+        const int sid = p.sorted_ids[row0 + m];
         ssid[m] = sid < p.R ? sid : -1;
     }
 
@@ -138,7 +124,7 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<MT, NBW>())) void
 #pragma unroll
     for (int r = 0; r < DMA; ++r) {
         const int row = w * ROWS_PER_WAVE + 4 * r + (L >> 4);
-        const int sid = p.sorted_ids[b * BM + row];
+        const int sid = p.sorted_ids[row0 + row];
         const int ch = (L & 15) ^ (row & 15);
         a_off[r] = sid < p.R ? (uint32_t)(sid / p.a_row_div) * (uint32_t)K * 2u + (uint32_t)ch * 16u : kOutOfRange;
     }
@@ -151,7 +137,7 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<MT, NBW>())) void
             uint32_t off = a_off[r];
             int soff = st * KT * 2;
             if constexpr (decltype(ragged)::value) {
-                const int ch = (L & 15) ^ ((4 * r + (L >> 4)) & 15);
+                const int ch = (L & 15) ^ ((w * ROWS_PER_WAVE + 4 * r + (L >> 4)) & 15);
                 off = (st * KT + ch * 8 < K && off != kOutOfRange) ? off + (uint32_t)soff : kOutOfRange;
                 soff = 0;
             }
@@ -192,9 +178,9 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<MT, NBW>())) void
         }
     };
 
-    f32x4 acc[MT][NBW];
+    f32x4 acc[MTA][NBW];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < MTA; ++mt)
 #pragma unroll
         for (int q = 0; q < NBW; ++q) acc[mt][q] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -211,11 +197,11 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<MT, NBW>())) void
     // Software-pipelined by scale group: while the MFMAs of group g run, the activation fragments of group g+1
     // are read from LDS and its weights dequantised, so neither the LDS latency nor the conversion stalls them.
     auto compute = [&](const uint8_t* slot, const WStage<NBW>& W) {
-        bf16x8 af[2][MT];
+        bf16x8 af[2][MTA];
         bf16x8 wf[2][NBW];
         auto read_a = [&](int g, bf16x8* out) {
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+            for (int mt = 0; mt < MTA; ++mt)
                 out[mt] = *reinterpret_cast<const bf16x8*>(slot + (mt * 16 + j) * (KT * 2) + (((4 * g + c) ^ j) * 16));
         };
         read_a(0, af[0]);
@@ -227,7 +213,7 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<MT, NBW>())) void
                 dequant_group(W, g + 1, wf[(g + 1) & 1]);
             }
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+            for (int mt = 0; mt < MTA; ++mt)
 #pragma unroll
                 for (int q = 0; q < NBW; ++q) acc[mt][q] = mfma16(af[g & 1][mt], wf[g & 1][q], acc[mt][q]);
         }
@@ -280,7 +266,7 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<MT, NBW>())) void
 
     // ---- epilogue: lane holds rows 4c + r of each 16-row tile, column j of each n-block
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < MTA; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int sid = ssid[mt * 16 + 4 * c + r];
@@ -308,26 +294,86 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<MT, NBW>())) void
         }
 }
 
-template <int MT, int NBW, int OM>
+// Tiles of c route blocks of RB16 * 16 rows: the body for height c * RB16 (c <= MT / RB16)
+template <int MT, int NBW, int OM, int RB16, int C = 1>
+__device__ __forceinline__ void run_tile(int c, const PrefillParams& p, uint8_t* slot0, uint8_t* slot1, int* ssid,
+                                         int row0, int e, int nt) {
+    if constexpr (C * RB16 <= MT) {
+        if (c == C) prefill_tile<C * RB16, NBW, OM>(p, slot0, slot1, ssid, row0, e, nt);
+        else run_tile<MT, NBW, OM, RB16, C + 1>(c, p, slot0, slot1, ssid, row0, e, nt);
+    }
+}
+
+// RB16: route block height in 16-row units; MT (= the tile's largest height) when every route block is a tile.
+template <int MT, int NBW, int OM, int RB16>
+__global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<MT, NBW>())) void gemm_prefill_kernel(PrefillParams p) {
+    static_assert(OM != kOutAct || NBW % 2 == 0, "the activation epilogue pairs gate and up n-blocks");
+    static_assert(MT % RB16 == 0, "a tile is a whole number of route blocks");
+    constexpr bool TILED = RB16 < MT;
+    if constexpr (prefill_waves_per_simd<MT, NBW>() == 1) {
+        // at one wavefront per SIMD the accumulators go to AGPRs (VGPRs alone stop at 256); naming an AGPR tells
+        // the compiler they may be used
+        __asm__ __volatile__("" ::: "a0");
+    }
+    constexpr int BM = 16 * MT;
+    constexpr int SLOT = BM * KT * 2;  // bytes of one activation stage
+    // the two ring slots are separate arrays, so the compiler can tell the reads of one from the direct loads
+    // into the other (with one array it would wait for every direct load before any read of the ring)
+    __shared__ __attribute__((aligned(16))) uint8_t slot0[SLOT];
+    __shared__ __attribute__((aligned(16))) uint8_t slot1[SLOT];
+    __shared__ int ssid[BM];
+
+    // ---- tile (XCD-aware order over the valid tiles only)
+    int ntl;
+    if constexpr (TILED) ntl = __builtin_amdgcn_readfirstlane(*p.tile_count);
+    else ntl = p.ntp ? min(__builtin_amdgcn_readfirstlane(*p.ntp) / BM, p.max_blocks) : p.max_blocks;
+    const int V = ntl * p.n_tiles;
+    const int per_xcd = (V + kXcds - 1) / kXcds;
+    const int pos = blockIdx.x / kXcds;
+    const int tile = (blockIdx.x % kXcds) * per_xcd + pos;
+    if (pos >= per_xcd || tile >= V) return;
+    const int t = tile / p.n_tiles, nt = tile % p.n_tiles;
+    if constexpr (TILED) {
+        const int b0 = p.tiles[2 * t], c = p.tiles[2 * t + 1];
+        const int e = p.expert_ids[b0];
+        if (e < 0 || e >= p.sh.E) return;
+        run_tile<MT, NBW, OM, RB16>(c, p, slot0, slot1, ssid, b0 * RB16 * 16, e, nt);
+    } else {
+        const int e = p.expert_ids[t];
+        if (e < 0 || e >= p.sh.E) return;
+        prefill_tile<MT, NBW, OM>(p, slot0, slot1, ssid, t * BM, e, nt);
+    }
+}
+
+template <int MT, int NBW, int OM, int RB16>
 hipError_t launch_t(const GemmArgs& a, hipStream_t s) {
     constexpr int cols = kWaves * NBW;  // n-blocks of weight columns per workgroup
     const int n_tiles = (a.sh.NB + cols - 1) / cols;
     PrefillParams p{a.A,          a.a_row_div, static_cast<const uint8_t*>(a.packed), a.sh, a.sorted_ids,
-                    a.expert_ids, a.ntp,       a.R,  a.max_blocks, n_tiles, a.out};
+                    a.expert_ids, a.ntp,       a.R,  a.max_blocks, n_tiles, a.out, a.tiles, a.tile_count};
     // a multiple of the XCD count: tile t runs on workgroup (t % per_xcd) * 8 + t / per_xcd, which can reach
-    // 8 * ceil(tiles / 8) - 1
+    // 8 * ceil(tiles / 8) - 1.  A tile list holds at most one tile per route block.
     const unsigned tiles = (unsigned)a.max_blocks * (unsigned)n_tiles;
     const dim3 grid((tiles + kXcds - 1) / kXcds * kXcds);
-    hipLaunchKernelGGL((gemm_prefill_kernel<MT, NBW, OM>), grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((gemm_prefill_kernel<MT, NBW, OM, RB16>), grid, dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 
+// route blocks of 16*mt rows are tiles; 32-row route blocks (rb16 = 2) are gathered into 128-row tiles of a
+// 128 x 32 wavefront tile, or 64-row tiles of a 64 x 64 one
 template <int OM>
-hipError_t dispatch(const GemmArgs& a, int mt, int nbw, hipStream_t s) {
-    if (nbw == 4 && mt == 4) return launch_t<4, 4, OM>(a, s);
-    if (nbw == 4 && mt == 8) return launch_t<8, 4, OM>(a, s);
-    if (nbw == 2 && mt == 8) return launch_t<8, 2, OM>(a, s);
-    if (nbw == 2 && mt == 4) return launch_t<4, 2, OM>(a, s);
+hipError_t dispatch(const GemmArgs& a, int mt, int nbw, int rb16, hipStream_t s) {
+    if (rb16 == 2) {
+        if (a.tiles == nullptr || a.tile_count == nullptr) return hipErrorInvalidValue;
+        if (nbw == 2) return launch_t<8, 2, OM, 2>(a, s);
+        if (nbw == 4) return launch_t<4, 4, OM, 2>(a, s);
+        return hipErrorInvalidValue;
+    }
+    if (rb16 != mt) return hipErrorInvalidValue;
+    if (nbw == 4 && mt == 4) return launch_t<4, 4, OM, 4>(a, s);
+    if (nbw == 4 && mt == 8) return launch_t<8, 4, OM, 8>(a, s);
+    if (nbw == 2 && mt == 8) return launch_t<8, 2, OM, 8>(a, s);
+    if (nbw == 2 && mt == 4) return launch_t<4, 2, OM, 4>(a, s);
     return hipErrorInvalidValue;
 }
 
@@ -338,13 +384,23 @@ bool prefill_supported(const GemmArgs& a) {
     return (size_t)a.sh.NB * a.sh.KB * SB_BYTES < (1u << 31) && (size_t)(a.R / a.a_row_div) * a.sh.K * 2 < (1u << 31);
 }
 
+int prefill_tile_rows(const w4a16_plan& p) {
+    if (p.block_m != 32) return p.block_m;
+    return p.n_blocks == 2 ? 128 : 64;
+}
+
 hipError_t launch_gemm_prefill(const GemmArgs& a, const w4a16_plan& p, hipStream_t s) {
     if (a.max_blocks == 0) return hipSuccess;
-    const int mt = p.block_m / 16;
+    const int mt = prefill_tile_rows(p) / 16, rb16 = p.block_m / 16;
+    if (rb16 < mt) {
+        hipError_t err = launch_tile_map(a.expert_ids, a.ntp, p.block_m, a.max_blocks, mt / rb16, a.tiles,
+                                         a.tile_count, s);
+        if (err != hipSuccess) return err;
+    }
     switch (a.out_mode) {
-        case kOutBf16: return dispatch<kOutBf16>(a, mt, p.n_blocks, s);
-        case kOutF32: return dispatch<kOutF32>(a, mt, p.n_blocks, s);
-        case kOutAct: return dispatch<kOutAct>(a, mt, p.n_blocks, s);
+        case kOutBf16: return dispatch<kOutBf16>(a, mt, p.n_blocks, rb16, s);
+        case kOutF32: return dispatch<kOutF32>(a, mt, p.n_blocks, rb16, s);
+        case kOutAct: return dispatch<kOutAct>(a, mt, p.n_blocks, rb16, s);
         default: return hipErrorInvalidValue;
     }
 }

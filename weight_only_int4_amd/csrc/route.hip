@@ -10,6 +10,8 @@
 // is ranked by (earlier chunks) + (earlier wavefronts of this chunk) + (lower
 // lanes of this wavefront with the same expert).  The last term comes from a
 // lane-match mask built from one ballot per bit of the expert id.
+#include <climits>
+
 #include "w4a16_internal.h"
 
 namespace w4a16 {
@@ -139,6 +141,77 @@ __global__ __launch_bounds__(kThreads) void route_prep_kernel(const int32_t* __r
     }
 }
 
+// Inclusive max-scan of one int per thread across the workgroup.
+__device__ int block_inclusive_max(int v, int* wave_tot) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off, 64);
+        if (lane >= off && o > incl) incl = o;
+    }
+    if (lane == 63) wave_tot[wave] = incl;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int run = INT_MIN;
+        for (int w = 0; w < kWaves; ++w) {
+            const int t = wave_tot[w];
+            wave_tot[w] = run;
+            run = t > run ? t : run;
+        }
+    }
+    __syncthreads();
+    const int r = wave_tot[wave] > incl ? wave_tot[wave] : incl;
+    __syncthreads();
+    return r;
+}
+
+// Tiles of up to `group` consecutive route blocks of one expert, for GEMM kernels whose workgroup covers more
+// rows than a route block: routing keeps fine blocks (little padding) while the kernel amortises the weight
+// dequantisation over up to group * BM rows.  A tile starts at every group-th block of each run of equal
+// expert_ids (a run's start comes from a max-scan of run starts, so no thread walks a run) and takes the blocks
+// of the run that follow, up to group.  tiles[2t] = first block, tiles[2t+1] = blocks; *count = tiles, at most
+// the number of valid blocks.  Blocks with a negative expert id get no tile.
+__global__ __launch_bounds__(kThreads) void tile_map_kernel(const int32_t* __restrict__ expert_ids,
+                                                            const int32_t* __restrict__ ntp, int BM, int max_blocks,
+                                                            int group, int32_t* __restrict__ tiles,
+                                                            int32_t* __restrict__ count) {
+    __shared__ int wave_tot[kWaves + 1];
+    __shared__ int carry[2];  // tiles written by earlier chunks; start of the run open at the chunk boundary
+    const int tid = threadIdx.x;
+    int nvalid = ntp ? *ntp / BM : max_blocks;
+    if (nvalid > max_blocks) nvalid = max_blocks;
+    if (tid == 0) carry[0] = carry[1] = 0;
+    __syncthreads();
+    for (int base = 0; base < nvalid; base += kThreads) {
+        const int b = base + tid;
+        const bool in = b < nvalid;
+        const int e = in ? expert_ids[b] : -1;
+        const bool start = in && (b == 0 || expert_ids[b - 1] != e);
+        int run0 = block_inclusive_max(start ? b : -1, wave_tot);
+        if (run0 < carry[1]) run0 = carry[1];
+        const bool anchor = in && e >= 0 && (b - run0) % group == 0;
+        int n = 0;
+        if (anchor) {
+            n = 1;
+            while (n < group && b + n < nvalid && expert_ids[b + n] == e) ++n;
+        }
+        int total;
+        const int excl = block_exclusive_scan(anchor ? 1 : 0, wave_tot, &total);
+        if (anchor) {
+            tiles[2 * (carry[0] + excl)] = b;
+            tiles[2 * (carry[0] + excl) + 1] = n;
+        }
+        __syncthreads();
+        if (tid == kThreads - 1) {
+            carry[0] += total;
+            carry[1] = run0;
+        }
+        __syncthreads();
+    }
+    if (tid == 0) *count = carry[0];
+}
+
 // Offsets form -> indexed form: rows [off[e], off[e+1]) of expert e become
 // slots of e's padded segment; the sentinel is rows_max.
 __global__ __launch_bounds__(kThreads) void offsets_to_route_kernel(const int32_t* __restrict__ off, int E,
@@ -213,6 +286,13 @@ hipError_t launch_offsets_to_route(const int32_t* offsets, int E, int rows_max, 
     const size_t shmem = sizeof(int) * ((size_t)E + 1 + kWaves + 1);
     hipLaunchKernelGGL(offsets_to_route_kernel, dim3(1), dim3(kThreads), shmem, s, offsets, E, rows_max, block_m,
                        max_padded, max_blocks, sorted_ids, expert_ids, ntp);
+    return hipGetLastError();
+}
+
+hipError_t launch_tile_map(const int32_t* expert_ids, const int32_t* ntp, int block_m, int max_blocks, int group,
+                           int32_t* tiles, int32_t* count, hipStream_t s) {
+    hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(kThreads), 0, s, expert_ids, ntp, block_m, max_blocks, group,
+                       tiles, count);
     return hipGetLastError();
 }
 

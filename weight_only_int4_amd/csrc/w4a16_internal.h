@@ -94,6 +94,8 @@ hipError_t launch_dequant(const void* packed, const Shape& sh, int expert, float
 hipError_t launch_route_prep(const int32_t* topk_ids, int R, int E, int block_m, int max_padded, int max_blocks,
                              int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntp, int32_t* offsets,
                              int32_t* counts, hipStream_t s);
+hipError_t launch_tile_map(const int32_t* expert_ids, const int32_t* ntp, int block_m, int max_blocks, int group,
+                           int32_t* tiles, int32_t* count, hipStream_t s);
 hipError_t launch_offsets_to_route(const int32_t* offsets, int E, int rows_max, int block_m, int max_padded,
                                    int max_blocks, int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntp,
                                    hipStream_t s);
@@ -110,6 +112,8 @@ struct GemmArgs {
     void* out;         // BF16 bits [R,N], float [R,N], or BF16 bits [R,N/2] (activation mode)
     int out_mode;      // kOutBf16, kOutF32 or kOutAct
     const int32_t* ntp = nullptr;  // num_tokens_padded (device) when known: bounds the valid route blocks
+    int32_t* tiles = nullptr;      // prefill with 32-row route blocks: tile list (first block, blocks) pairs
+    int32_t* tile_count = nullptr; // ... and its length (device)
     float* partials = nullptr;     // split-K partial tiles (decode, k_split > 1)
     unsigned* counters = nullptr;  // split-K arrival counters, zero between calls
 };
@@ -123,6 +127,9 @@ bool decode_reg_supported(const GemmArgs& a, const w4a16_plan& p);
 hipError_t launch_gemm_decode_reg(const GemmArgs& a, const w4a16_plan& p, hipStream_t s);
 hipError_t launch_gemm_prefill(const GemmArgs& a, const w4a16_plan& p, hipStream_t s);
 bool prefill_supported(const GemmArgs& a);
+// Rows per prefill workgroup tile: block_m, except 32-row route blocks, which are gathered into tiles of 128
+// rows (n_blocks 2) or 64 rows (n_blocks 4) through a tile list.
+int prefill_tile_rows(const w4a16_plan& p);
 hipError_t launch_silu_mul(const uint16_t* gu, int rows, int I, uint16_t* h, hipStream_t s);
 hipError_t launch_silu_mul_f32(const float* gu, int rows, int I, uint16_t* h, hipStream_t s);
 hipError_t launch_combine(const float* y, const float* tw, const int32_t* ids, int T, int k, int E, int H,
