@@ -316,8 +316,9 @@ def main():
         kname = "gemm_decode_reg_kernel<NBW=%d,D=2,act out> (gate_up + silu_mul, k_split %d)" % (p13.n_blocks,
                                                                                                p13.k_split)
     else:
-        kname = "gemm_%s_kernel<MT=%d,NBW=%d,act out> (gate_up + silu_mul, k_split %d)" % (
-            "decode" if p13.kernel == L.KERNEL_DECODE else "prefill", p13.block_m // 16, p13.n_blocks, p13.k_split)
+        kname = "gemm_%s_kernel<MT=%d,NBW=%d,act out> (gate_up + silu_mul, route blocks of %d rows, k_split %d)" % (
+            "decode" if p13.kernel == L.KERNEL_DECODE else "prefill", (p13.tile_m or p13.block_m) // 16,
+            p13.n_blocks, p13.block_m, p13.k_split)
 
     stages = list(L.FUSED_STAGES)
     print("[bench] step %.1f us wall (graph replay), %.1f us GPU events; per stage (us): %s" % (

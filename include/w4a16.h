@@ -65,13 +65,14 @@ enum { W4A16_KERNEL_DECODE = 1, W4A16_KERNEL_PREFILL = 2 };
  * for the routing tensors passed with it. */
 typedef struct w4a16_plan {
     int32_t kernel;        /* W4A16_KERNEL_DECODE or W4A16_KERNEL_PREFILL */
-    int32_t block_m;       /* rows per route block: 16, 32, 48 or 64 (decode); 32, 64 or 128 (prefill;
-                              with 32, a workgroup takes up to 128 rows (n_blocks 2) or 64 rows
-                              (n_blocks 4) of consecutive blocks of one expert) */
-    int32_t n_blocks;      /* 16-column blocks per wavefront: 1, 2 or 4 */
+    int32_t block_m;       /* rows per route block: 16, 32, 48 or 64 (decode); 32, 64 or 128 (prefill) */
+    int32_t n_blocks;      /* 16-column blocks per wavefront: 1, 2 or 4 (prefill: 2 or 4) */
     int32_t waves;         /* wavefronts per workgroup, each owning its own columns: 4 */
     int32_t k_split;       /* decode: workgroups sharing one output tile along K (1..64); prefill: 1 */
-    int32_t reserved[3];   /* must be zero */
+    int32_t tile_m;        /* prefill: rows per workgroup tile, 64 or 128 (0: block_m).  With block_m
+                              32 a workgroup takes up to tile_m / 32 consecutive route blocks of one
+                              expert; otherwise tile_m equals block_m.  decode: 0 */
+    int32_t reserved[2];   /* must be zero */
 } w4a16_plan;
 
 /* Host handle describing one packed weight set (E experts of N x K). */
@@ -155,8 +156,9 @@ int w4a16_route_prep(const int32_t* topk_ids, int T, int k, int E, int block_m, 
 /* Choose a plan from the routed rows per expert, not the token count (Chord
  * page, "TL;DR" and "Indexed kernels").  expected_rows_per_expert <= 0 means
  * T*k/E.  Host only and memoised; environment overrides W4A16_FORCE_KERNEL
- * (decode|prefill), W4A16_BLOCK_M, W4A16_N_BLOCKS and W4A16_WAVES are read
- * once and are part of the memo key. */
+ * (decode|prefill), W4A16_BLOCK_M, W4A16_N_BLOCKS, W4A16_WAVES,
+ * W4A16_K_SPLIT and W4A16_TILE_M are read once and are part of the memo
+ * key. */
 int w4a16_plan_select(int T, int k, int E, int N, int K, float expected_rows_per_expert, w4a16_plan* out);
 
 /* ---------------------------------------------------------------- GEMM */
@@ -176,7 +178,8 @@ int w4a16_plan_select(int T, int k, int E, int N, int K, float expected_rows_per
  *              are skipped)
  *   out        device BF16 bits [R, N]; rows of invalid routes untouched
  *   ws         workspace of w4a16_gemm_workspace_bytes (may be NULL if 0).  A
- *              prefill plan with block_m 32 builds its tile list there.  A
+ *              prefill plan with tile_m above block_m builds its tile list
+ *              there.  A
  *              plan with k_split > 1 keeps per-tile arrival counters in it:
  *              the workspace must be zero-filled once before its first use,
  *              and every call leaves the counters at zero again.  Calls that

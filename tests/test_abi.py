@@ -98,19 +98,25 @@ def test_plan_selector_keys_on_rows_per_expert(lib):
     # Qwen3-like decode: 64 tokens x 8 / 128 experts = 4 rows per expert
     p = L.plan_select(64, 8, 128, 1536, 2048)
     assert p.kernel == L.KERNEL_DECODE and p.block_m == 16
-    # same token count, far fewer experts: 64 x 8 / 4 = 128 rows per expert -> prefill
+    # same token count, far fewer experts: 64 x 8 / 4 = 128 rows per expert -> prefill, 32-row route blocks
+    # gathered into 128-row tiles
     p = L.plan_select(64, 8, 4, 1536, 2048)
-    assert p.kernel == L.KERNEL_PREFILL and p.block_m == 128
-    # an explicit expectation overrides T*k/E
+    assert p.kernel == L.KERNEL_PREFILL and (p.block_m, p.tile_m) == (32, 128)
+    # an explicit expectation overrides T*k/E: 10 rows stay on the decode kernel, 30 rows take 64-row tiles of
+    # 32-row blocks, 48 rows plain 64-row blocks
+    p = L.plan_select(64, 8, 128, 1536, 2048, expected_rows_per_expert=10.0)
+    assert p.kernel == L.KERNEL_DECODE and (p.block_m, p.tile_m) == (16, 0)
     p = L.plan_select(64, 8, 128, 1536, 2048, expected_rows_per_expert=30.0)
-    assert p.kernel == L.KERNEL_DECODE and p.block_m == 48
+    assert p.kernel == L.KERNEL_PREFILL and (p.block_m, p.tile_m) == (32, 64)
+    p = L.plan_select(64, 8, 128, 1536, 2048, expected_rows_per_expert=48.0)
+    assert p.kernel == L.KERNEL_PREFILL and (p.block_m, p.tile_m) == (64, 0)
     # one token on a Kimi-K2-like expert share: few workgroups, so K is split across workgroups
     p = L.plan_select(1, 8, 48, 4096, 7168, expected_rows_per_expert=1.0 / 48)
     assert p.kernel == L.KERNEL_DECODE and p.k_split > 1
     # memoised: same answer twice
     a = L.plan_select(256, 8, 48, 4096, 7168)
     b = L.plan_select(256, 8, 48, 4096, 7168)
-    assert (a.kernel, a.block_m, a.n_blocks, a.waves) == (b.kernel, b.block_m, b.n_blocks, b.waves)
+    assert (a.kernel, a.block_m, a.n_blocks, a.waves, a.tile_m) == (b.kernel, b.block_m, b.n_blocks, b.waves, b.tile_m)
 
 
 def test_plan_validation(lib):
@@ -126,6 +132,17 @@ def test_plan_validation(lib):
     good = L.make_plan("decode", 16, 4, 4)
     assert lib.w4a16_gemm_workspace_bytes(ctypes.byref(good), 32, 8, 512, ctypes.byref(sz)) == 0
     assert sz.value == 0
+    # prefill tiles: 64 or 128 rows, taller than the route block only for 32-row blocks; decode has none
+    for args in (("prefill", 32, 2, 4, 1, 96), ("prefill", 64, 2, 4, 1, 128), ("prefill", 128, 2, 4, 1, 64),
+                 ("prefill", 32, 2, 4, 1, 0), ("decode", 16, 4, 4, 1, 64)):
+        bad = L.make_plan(*args)
+        assert lib.w4a16_gemm_workspace_bytes(ctypes.byref(bad), 32, 8, 512, ctypes.byref(sz)) == -2, args
+    # a tile list: its length padded to 16 bytes, then two ints per 32-row route block (R=32, E=8: at most 9 blocks),
+    # rounded up to 256 bytes
+    tiled = L.make_plan("prefill", 32, 2, 4, 1, 128)
+    assert L.gemm_workspace_bytes(tiled, 32, 8, 512) == 256
+    assert L.gemm_workspace_bytes(tiled, 32 * 100, 8, 512) == ((4 + 2 * 108) * 4 + 255) // 256 * 256
+    assert L.gemm_workspace_bytes(L.make_plan("prefill", 64, 2, 4, 1, 64), 32, 8, 512) == 0
     # split K: counters (one per route block and column tile) then fp32 partial tiles
     split = L.make_plan("decode", 16, 4, 4, k_split=4)
     # 10 route blocks x 2 column tiles of 256: 20 counters (one 256-byte line), 10*2*4 partial tiles of 16x256

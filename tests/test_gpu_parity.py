@@ -109,8 +109,8 @@ DECODE_PLANS = ([("decode", bm, nbw, 4, 1) for bm in (16, 32, 48, 64) for nbw in
                 + [("decode", 16, 4, 4, 2), ("decode", 32, 2, 4, 2), ("decode", 64, 1, 4, 2),
                    ("decode", 16, 1, 4, 3)])  # 3 slices of a 2-stage K: one slice is empty
 PREFILL_PLANS = ([("prefill", bm, nbw, 4, 1) for bm in (64, 128) for nbw in (2, 4)]
-                 + [("prefill", 32, 2, 4, 1), ("prefill", 32, 4, 4, 1)])  # 32-row blocks in 128- / 64-row tiles
-PLAN_ID = lambda p: "%s-bm%d-nb%d-w%d-ks%d" % p  # noqa: E731
+                 + [("prefill", 32, nbw, 4, 1, tile) for tile in (64, 128) for nbw in (2, 4)])  # tiles of 32-row blocks
+PLAN_ID = lambda p: "%s-bm%d-nb%d-w%d-ks%d" % p[:5] + ("-t%d" % p[5] if len(p) > 5 else "")  # noqa: E731
 
 
 def _run_gemm(case, plan, a_row_div=None):
@@ -135,7 +135,7 @@ def test_gemm_tiny_all_plans(orc, plan_args):
 
 @pytest.mark.parametrize("plan_args", [("decode", 16, 4, 4, 1), ("decode", 64, 2, 4, 1), ("decode", 16, 4, 4, 3),
                                        ("decode", 32, 2, 4, 7), ("prefill", 64, 4, 4, 1), ("prefill", 128, 2, 4, 1),
-                                       ("prefill", 32, 2, 4, 1)],
+                                       ("prefill", 32, 2, 4, 1, 128), ("prefill", 32, 2, 4, 1, 64)],
                          ids=PLAN_ID)
 @pytest.mark.parametrize("shape", [(24, 6, 2, 40, 512), (9, 4, 3, 64, 96), (70, 3, 2, 16, 2048),
                                    (5, 10, 8, 4096, 7168)], ids=lambda s: "T%d-E%d-k%d-N%d-K%d" % s)
@@ -187,7 +187,7 @@ EDGE = ["E1", "one hot expert", "empty and single", "ragged N and K", "tile edge
 
 @pytest.mark.parametrize("plan_args", [("decode", 16, 1, 4, 1), ("decode", 32, 4, 4, 1), ("decode", 64, 2, 4, 1),
                                        ("decode", 16, 2, 4, 2), ("prefill", 64, 2, 4, 1), ("prefill", 128, 4, 4, 1),
-                                       ("prefill", 32, 2, 4, 1), ("prefill", 32, 4, 4, 1)],
+                                       ("prefill", 32, 2, 4, 1, 128), ("prefill", 32, 2, 4, 1, 64)],
                          ids=PLAN_ID)
 @pytest.mark.parametrize("kind", EDGE)
 def test_gemm_edge_cases(orc, kind, plan_args):
@@ -228,7 +228,8 @@ def test_gemm_is_deterministic_and_permutation_equivariant(orc):
         assert np.array_equal(c, a[route_perm])
 
 
-@pytest.mark.parametrize("plan_args", [("prefill", 32, 2, 4, 1), ("prefill", 32, 4, 4, 1)], ids=PLAN_ID)
+@pytest.mark.parametrize("plan_args", [("prefill", 32, 2, 4, 1, 128), ("prefill", 32, 4, 4, 1, 128),
+                                       ("prefill", 32, 2, 4, 1, 64)], ids=PLAN_ID)
 def test_gemm_prefill_tile_list(orc, plan_args):
     # 32-row route blocks gathered into taller tiles: experts whose block runs are 1 .. 9 blocks long (every
     # tile height, runs cut into several tiles, empty experts) and more than 1024 valid blocks, so runs and tiles
@@ -253,7 +254,7 @@ def test_gemm_prefill_tile_list(orc, plan_args):
 # ------------------------------------------------------------------ offsets form
 
 @pytest.mark.parametrize("plan_args", [("decode", 16, 4, 4, 1), ("decode", 16, 2, 4, 2), ("prefill", 64, 4, 4, 1),
-                                       ("prefill", 32, 2, 4, 1)],
+                                       ("prefill", 32, 2, 4, 1, 64)],
                          ids=PLAN_ID)
 def test_gemm_offsets_form(orc, plan_args):
     rng = np.random.default_rng(99)
@@ -277,7 +278,8 @@ def test_gemm_offsets_form(orc, plan_args):
 
 ACT_PLANS = [("decode", 16, 2, 4, 1), ("decode", 16, 4, 4, 1), ("decode", 48, 4, 4, 1), ("decode", 32, 4, 4, 2),
              ("decode", 64, 2, 4, 3), ("prefill", 64, 2, 4, 1), ("prefill", 64, 4, 4, 1), ("prefill", 128, 4, 4, 1),
-             ("prefill", 128, 2, 4, 1), ("prefill", 32, 2, 4, 1), ("prefill", 32, 4, 4, 1)]
+             ("prefill", 128, 2, 4, 1), ("prefill", 32, 2, 4, 1, 128), ("prefill", 32, 4, 4, 1, 128),
+             ("prefill", 32, 2, 4, 1, 64), ("prefill", 32, 4, 4, 1, 64)]
 
 
 @pytest.mark.parametrize("plan_args", ACT_PLANS, ids=PLAN_ID)

@@ -74,7 +74,7 @@ int env_int(const char* name, int dflt) {
 
 struct Overrides {
     int force_kernel = 0;  // 0 auto, else W4A16_KERNEL_*
-    int block_m = 0, n_blocks = 0, waves = 0, k_split = 0;
+    int block_m = 0, n_blocks = 0, waves = 0, k_split = 0, tile_m = -1;
 };
 
 const Overrides& overrides() {
@@ -87,16 +87,18 @@ const Overrides& overrides() {
         r.n_blocks = env_int("W4A16_N_BLOCKS", 0);
         r.waves = env_int("W4A16_WAVES", 0);
         r.k_split = env_int("W4A16_K_SPLIT", 0);
+        r.tile_m = env_int("W4A16_TILE_M", -1);
         return r;
     }();
     return o;
 }
 
-// Decode wins while the per-group scale FMAs (4 per output per group) cost
-// less than a full dequantisation of every weight, i.e. below about 60 rows
-// per expert; above that the prefill kernel amortises dequantisation over a
-// tall M tile.
-constexpr float kDecodeMaxRows = 48.0f;
+// Decode streams each weight once per route block and applies the scales per
+// output row; the prefill kernel dequantises each weight once per tile and
+// shares it over the tile's rows.  Measured on the Qwen3-, Kimi- and
+// DeepSeek-shaped projections, decode is faster up to about 12 routed rows per
+// expert and the prefill kernel from 16 rows on.
+constexpr float kDecodeMaxRows = 12.0f;
 
 w4a16_plan select_plan(int T, int k, int E, int N, int K, float rows) {
     const Overrides& ov = overrides();
@@ -126,23 +128,35 @@ w4a16_plan select_plan(int T, int k, int E, int N, int K, float rows) {
         const int max_ks = nst / 2 > 1 ? nst / 2 : 1;
         p.k_split = ks < 1 ? 1 : (ks > max_ks ? max_ks : (ks > 16 ? 16 : ks));
     } else {
-        // 128-row tiles amortise dequantisation over more rows; their wavefront tile is 128 x 32 (two
-        // wavefronts per SIMD fit), the 64-row tile's is 64 x 64
-        p.block_m = rows >= 96.0f ? 128 : 64;
-        p.n_blocks = p.block_m == 128 ? 2 : 4;
+        // 32-row route blocks keep the padding below 32 rows per expert; the workgroup tile gathers up to four
+        // of them so that each dequantised weight feeds up to 128 rows.  Below ~56 rows per expert a 64-row tile
+        // is faster (twice the workgroups; a 128-row tile would mostly hold one or two blocks), and between 40
+        // and 56 rows plain 64-row blocks are (measured; the tile list costs a launch and the padding saved is
+        // small there).
         p.waves = 4;
+        p.n_blocks = 2;
+        if (rows >= 56.0f) {
+            p.block_m = 32;
+            p.tile_m = 128;
+        } else if (rows >= 40.0f) {
+            p.block_m = 64;
+        } else {
+            p.block_m = 32;
+            p.tile_m = 64;
+        }
     }
     if (ov.block_m) p.block_m = ov.block_m;
     if (ov.n_blocks) p.n_blocks = ov.n_blocks;
     if (ov.waves) p.waves = ov.waves;
     if (ov.k_split && p.kernel == W4A16_KERNEL_DECODE) p.k_split = ov.k_split;
+    if (ov.tile_m >= 0 && p.kernel == W4A16_KERNEL_PREFILL) p.tile_m = ov.tile_m;
     (void)T; (void)k;
     return p;
 }
 
 int validate_plan(const w4a16_plan* p, const char* what) {
     if (!p) return fail(W4A16_INVALID_ARG, "%s: plan is NULL", what);
-    for (int i = 0; i < 3; ++i)
+    for (int i = 0; i < 2; ++i)
         if (p->reserved[i]) return fail(W4A16_INVALID_ARG, "%s: plan.reserved must be zero", what);
     if (p->kernel == W4A16_KERNEL_DECODE) {
         if (p->block_m % 16 || p->block_m < 16 || p->block_m > 64)
@@ -152,9 +166,16 @@ int validate_plan(const w4a16_plan* p, const char* what) {
         if (p->k_split < 1 || p->k_split > 64)
             return fail(W4A16_UNSUPPORTED_SHAPE, "%s: decode k_split %d not in 1..64", what, p->k_split);
         if (p->waves != 4) return fail(W4A16_UNSUPPORTED_SHAPE, "%s: decode waves must be 4", what);
+        if (p->tile_m != 0) return fail(W4A16_UNSUPPORTED_SHAPE, "%s: decode tile_m must be 0", what);
     } else if (p->kernel == W4A16_KERNEL_PREFILL) {
         if (p->block_m != 32 && p->block_m != 64 && p->block_m != 128)
             return fail(W4A16_UNSUPPORTED_SHAPE, "%s: prefill block_m %d not in {32,64,128}", what, p->block_m);
+        const int tile = p->tile_m ? p->tile_m : p->block_m;
+        if (tile != 64 && tile != 128)
+            return fail(W4A16_UNSUPPORTED_SHAPE, "%s: prefill tile_m %d not in {64,128}", what, tile);
+        if (tile != p->block_m && p->block_m != 32)
+            return fail(W4A16_UNSUPPORTED_SHAPE, "%s: prefill tile_m %d must equal block_m %d unless block_m is 32",
+                        what, tile, p->block_m);
         if (p->n_blocks != 2 && p->n_blocks != 4)
             return fail(W4A16_UNSUPPORTED_SHAPE, "%s: prefill n_blocks %d not in {2,4}", what, p->n_blocks);
         if (p->k_split != 1) return fail(W4A16_UNSUPPORTED_SHAPE, "%s: prefill k_split must be 1", what);
@@ -575,8 +596,10 @@ int w4a16_fused_moe_plans(int T, int k, const w4a16_weights* w13, const w4a16_we
     if (p2.kernel == W4A16_KERNEL_PREFILL) {
         if (p2.n_blocks != 2 && p2.n_blocks != 4) p2.n_blocks = 4;
         p2.k_split = 1;
-    } else if (p2.k_split < 1) {
-        p2.k_split = 1;
+        p2.tile_m = p13.tile_m;
+    } else {
+        if (p2.k_split < 1) p2.k_split = 1;
+        p2.tile_m = 0;
     }
     rc = validate_plan(&p2, what);
     if (rc) return rc;

@@ -359,14 +359,15 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-// route blocks of 16*mt rows are tiles; 32-row route blocks (rb16 = 2) are gathered into 128-row tiles of a
-// 128 x 32 wavefront tile, or 64-row tiles of a 64 x 64 one
+// route blocks of 16*mt rows are tiles; 32-row route blocks (rb16 = 2) are gathered into tiles of 16*mt rows
 template <int OM>
 hipError_t dispatch(const GemmArgs& a, int mt, int nbw, int rb16, hipStream_t s) {
-    if (rb16 == 2) {
+    if (rb16 == 2 && mt > 2) {
         if (a.tiles == nullptr || a.tile_count == nullptr) return hipErrorInvalidValue;
-        if (nbw == 2) return launch_t<8, 2, OM, 2>(a, s);
-        if (nbw == 4) return launch_t<4, 4, OM, 2>(a, s);
+        if (nbw == 2 && mt == 8) return launch_t<8, 2, OM, 2>(a, s);
+        if (nbw == 4 && mt == 8) return launch_t<8, 4, OM, 2>(a, s);
+        if (nbw == 2 && mt == 4) return launch_t<4, 2, OM, 2>(a, s);
+        if (nbw == 4 && mt == 4) return launch_t<4, 4, OM, 2>(a, s);
         return hipErrorInvalidValue;
     }
     if (rb16 != mt) return hipErrorInvalidValue;
@@ -384,10 +385,7 @@ bool prefill_supported(const GemmArgs& a) {
     return (size_t)a.sh.NB * a.sh.KB * SB_BYTES < (1u << 31) && (size_t)(a.R / a.a_row_div) * a.sh.K * 2 < (1u << 31);
 }
 
-int prefill_tile_rows(const w4a16_plan& p) {
-    if (p.block_m != 32) return p.block_m;
-    return p.n_blocks == 2 ? 128 : 64;
-}
+int prefill_tile_rows(const w4a16_plan& p) { return p.tile_m ? p.tile_m : p.block_m; }
 
 hipError_t launch_gemm_prefill(const GemmArgs& a, const w4a16_plan& p, hipStream_t s) {
     if (a.max_blocks == 0) return hipSuccess;

@@ -127,8 +127,8 @@ bool decode_reg_supported(const GemmArgs& a, const w4a16_plan& p);
 hipError_t launch_gemm_decode_reg(const GemmArgs& a, const w4a16_plan& p, hipStream_t s);
 hipError_t launch_gemm_prefill(const GemmArgs& a, const w4a16_plan& p, hipStream_t s);
 bool prefill_supported(const GemmArgs& a);
-// Rows per prefill workgroup tile: block_m, except 32-row route blocks, which are gathered into tiles of 128
-// rows (n_blocks 2) or 64 rows (n_blocks 4) through a tile list.
+// Rows per prefill workgroup tile (plan.tile_m, else block_m); 32-row route blocks are gathered into taller
+// tiles through a tile list.
 int prefill_tile_rows(const w4a16_plan& p);
 hipError_t launch_silu_mul(const uint16_t* gu, int rows, int I, uint16_t* h, hipStream_t s);
 hipError_t launch_silu_mul_f32(const float* gu, int rows, int I, uint16_t* h, hipStream_t s);

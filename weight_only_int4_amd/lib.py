@@ -32,12 +32,14 @@ class W4A16Error(RuntimeError):
 
 class Plan(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("block_m", ctypes.c_int32), ("n_blocks", ctypes.c_int32),
-                ("waves", ctypes.c_int32), ("k_split", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
+                ("waves", ctypes.c_int32), ("k_split", ctypes.c_int32), ("tile_m", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 2)]
 
     def __repr__(self):
         kind = {KERNEL_DECODE: "decode", KERNEL_PREFILL: "prefill"}.get(self.kernel, str(self.kernel))
-        return "Plan(%s, block_m=%d, n_blocks=%d, waves=%d, k_split=%d)" % (kind, self.block_m, self.n_blocks,
-                                                                          self.waves, self.k_split)
+        tile = ", tile_m=%d" % self.tile_m if self.tile_m else ""
+        return "Plan(%s, block_m=%d, n_blocks=%d, waves=%d, k_split=%d%s)" % (kind, self.block_m, self.n_blocks,
+                                                                            self.waves, self.k_split, tile)
 
 
 # name -> (restype, argtypes)
@@ -210,10 +212,10 @@ def plan_select(T: int, k: int, E: int, N: int, K: int, expected_rows_per_expert
     return p
 
 
-def make_plan(kernel: str, block_m: int, n_blocks: int, waves: int, k_split: int = 1) -> Plan:
+def make_plan(kernel: str, block_m: int, n_blocks: int, waves: int, k_split: int = 1, tile_m: int = 0) -> Plan:
     p = Plan()
     p.kernel = KERNEL_DECODE if kernel == "decode" else KERNEL_PREFILL
-    p.block_m, p.n_blocks, p.waves, p.k_split = block_m, n_blocks, waves, k_split
+    p.block_m, p.n_blocks, p.waves, p.k_split, p.tile_m = block_m, n_blocks, waves, k_split, tile_m
     return p
 
 
