@@ -137,11 +137,11 @@ def test_plan_validation(lib):
                  ("prefill", 32, 2, 4, 1, 0), ("decode", 16, 4, 4, 1, 64)):
         bad = L.make_plan(*args)
         assert lib.w4a16_gemm_workspace_bytes(ctypes.byref(bad), 32, 8, 512, ctypes.byref(sz)) == -2, args
-    # a tile list: its length padded to 16 bytes, then two ints per 32-row route block (R=32, E=8: at most 9 blocks),
-    # rounded up to 256 bytes
+    # a tile list: its length padded to 16 bytes, then two ints per 32-row route block for the tiles and two for
+    # the scratch they are built with (R=32, E=8: at most 9 blocks), rounded up to 256 bytes
     tiled = L.make_plan("prefill", 32, 2, 4, 1, 128)
     assert L.gemm_workspace_bytes(tiled, 32, 8, 512) == 256
-    assert L.gemm_workspace_bytes(tiled, 32 * 100, 8, 512) == ((4 + 2 * 108) * 4 + 255) // 256 * 256
+    assert L.gemm_workspace_bytes(tiled, 32 * 100, 8, 512) == ((4 + 4 * 108) * 4 + 255) // 256 * 256
     assert L.gemm_workspace_bytes(L.make_plan("prefill", 64, 2, 4, 1, 64), 32, 8, 512) == 0
     # split K: counters (one per route block and column tile) then fp32 partial tiles
     split = L.make_plan("decode", 16, 4, 4, k_split=4)

@@ -189,7 +189,8 @@ int validate_plan(const w4a16_plan* p, const char* what) {
 // Split-K workspace of one GEMM: arrival counters first (so that GEMMs sharing a
 // workspace find them at the same place, all zero), then the partial tiles.
 // A prefill plan whose workgroup tile spans several route blocks also needs a tile list after the split-K area:
-// its length (one int, padded to 16 bytes), then (first block, blocks) per tile, at most one tile per block.
+// its length (one int, padded to 16 bytes), then (first block, blocks) per tile, at most one tile per block,
+// then two ints per block of scratch the list is built with.
 struct GemmWs {
     size_t counter_bytes, partial_bytes, tile_bytes, total;
 };
@@ -202,7 +203,7 @@ GemmWs gemm_ws(const Shape& sh, const w4a16_plan& p, int max_blocks) {
     GemmWs g;
     g.counter_bytes = align_up(sizeof(unsigned) * decode_counters(sh, p, max_blocks), 256);
     g.partial_bytes = align_up(sizeof(float) * decode_partial_floats(sh, p, max_blocks), 256);
-    g.tile_bytes = tiled_prefill(p) ? align_up(sizeof(int32_t) * (4 + 2 * (size_t)max_blocks), 256) : 0;
+    g.tile_bytes = tiled_prefill(p) ? align_up(sizeof(int32_t) * (4 + 4 * (size_t)max_blocks), 256) : 0;
     g.total = g.counter_bytes + g.partial_bytes + g.tile_bytes;
     return g;
 }
@@ -216,6 +217,7 @@ void bind_ws(GemmArgs& a, const GemmWs& g, void* ws, size_t partial_offset, void
     if (g.tile_bytes) {
         a.tile_count = static_cast<int32_t*>(tiles);
         a.tiles = static_cast<int32_t*>(tiles) + 4;
+        a.tile_scratch = a.tiles + 2 * (size_t)a.max_blocks;
     }
 }
 

@@ -363,7 +363,7 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t s) {
 template <int OM>
 hipError_t dispatch(const GemmArgs& a, int mt, int nbw, int rb16, hipStream_t s) {
     if (rb16 == 2 && mt > 2) {
-        if (a.tiles == nullptr || a.tile_count == nullptr) return hipErrorInvalidValue;
+        if (a.tiles == nullptr || a.tile_count == nullptr || a.tile_scratch == nullptr) return hipErrorInvalidValue;
         if (nbw == 2 && mt == 8) return launch_t<8, 2, OM, 2>(a, s);
         if (nbw == 4 && mt == 8) return launch_t<8, 4, OM, 2>(a, s);
         if (nbw == 2 && mt == 4) return launch_t<4, 2, OM, 2>(a, s);
@@ -392,7 +392,7 @@ hipError_t launch_gemm_prefill(const GemmArgs& a, const w4a16_plan& p, hipStream
     const int mt = prefill_tile_rows(p) / 16, rb16 = p.block_m / 16;
     if (rb16 < mt) {
         hipError_t err = launch_tile_map(a.expert_ids, a.ntp, p.block_m, a.max_blocks, mt / rb16, a.tiles,
-                                         a.tile_count, s);
+                                         a.tile_count, a.tile_scratch, s);
         if (err != hipSuccess) return err;
     }
     switch (a.out_mode) {

@@ -166,50 +166,112 @@ __device__ int block_inclusive_max(int v, int* wave_tot) {
     return r;
 }
 
-// Tiles of up to `group` consecutive route blocks of one expert, for GEMM kernels whose workgroup covers more
-// rows than a route block: routing keeps fine blocks (little padding) while the kernel amortises the weight
-// dequantisation over up to group * BM rows.  A tile starts at every group-th block of each run of equal
-// expert_ids (a run's start comes from a max-scan of run starts, so no thread walks a run) and takes the blocks
-// of the run that follow, up to group.  tiles[2t] = first block, tiles[2t+1] = blocks; *count = tiles, at most
-// the number of valid blocks.  Blocks with a negative expert id get no tile.
+// Inclusive min-scan from the right (suffix minimum) of one int per thread across the workgroup.
+__device__ int block_suffix_min(int v, int* wave_tot) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_down(incl, off, 64);
+        if (lane + off < 64 && o < incl) incl = o;
+    }
+    if (lane == 0) wave_tot[wave] = incl;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int run = INT_MAX;
+        for (int w = kWaves - 1; w >= 0; --w) {
+            const int t = wave_tot[w];
+            wave_tot[w] = run;
+            run = t < run ? t : run;
+        }
+    }
+    __syncthreads();
+    const int r = wave_tot[wave] < incl ? wave_tot[wave] : incl;
+    __syncthreads();
+    return r;
+}
+
+// Tiles of consecutive route blocks of one expert, for GEMM kernels whose workgroup covers more rows than a
+// route block: routing keeps fine blocks (little padding) while the kernel amortises the weight dequantisation
+// over the tile's rows.  A run of L equal expert_ids is cut into n = ceil(L / group) tiles of as equal a size as
+// possible (the first L % n take one block more): a kernel whose cost per tile is mostly the dequantisation
+// gains nothing from a full tile beside a one-block one.  Run starts come from a max-scan of start flags and run
+// ends from a suffix min-scan of end flags, both kept per block in `scratch` (2 * max_blocks ints), so no thread
+// walks a run.  tiles[2t] = first block, tiles[2t+1] = blocks; *count = tiles, at most the number of valid
+// blocks.  Blocks with a negative expert id get no tile.
 __global__ __launch_bounds__(kThreads) void tile_map_kernel(const int32_t* __restrict__ expert_ids,
                                                             const int32_t* __restrict__ ntp, int BM, int max_blocks,
                                                             int group, int32_t* __restrict__ tiles,
-                                                            int32_t* __restrict__ count) {
+                                                            int32_t* __restrict__ count,
+                                                            int32_t* __restrict__ scratch) {
     __shared__ int wave_tot[kWaves + 1];
-    __shared__ int carry[2];  // tiles written by earlier chunks; start of the run open at the chunk boundary
+    __shared__ int carry[2];
     const int tid = threadIdx.x;
     int nvalid = ntp ? *ntp / BM : max_blocks;
     if (nvalid > max_blocks) nvalid = max_blocks;
-    if (tid == 0) carry[0] = carry[1] = 0;
+    int32_t* run_first = scratch;
+    int32_t* run_last = scratch + max_blocks;
+    const int nchunks = (nvalid + kThreads - 1) / kThreads;
+
+    // run starts, first chunk to last (the start of a run open at a chunk's end is carried into the next)
+    if (tid == 0) carry[0] = 0;
     __syncthreads();
-    for (int base = 0; base < nvalid; base += kThreads) {
-        const int b = base + tid;
+    for (int ch = 0; ch < nchunks; ++ch) {
+        const int b = ch * kThreads + tid;
         const bool in = b < nvalid;
-        const int e = in ? expert_ids[b] : -1;
-        const bool start = in && (b == 0 || expert_ids[b - 1] != e);
-        int run0 = block_inclusive_max(start ? b : -1, wave_tot);
-        if (run0 < carry[1]) run0 = carry[1];
-        const bool anchor = in && e >= 0 && (b - run0) % group == 0;
+        const bool start = in && (b == 0 || expert_ids[b - 1] != expert_ids[b]);
+        int r0 = block_inclusive_max(start ? b : -1, wave_tot);
+        if (r0 < carry[0]) r0 = carry[0];
+        if (in) run_first[b] = r0;
+        __syncthreads();
+        if (tid == kThreads - 1) carry[0] = r0;
+        __syncthreads();
+    }
+    // run ends, last chunk to first
+    if (tid == 0) carry[0] = INT_MAX;
+    __syncthreads();
+    for (int ch = nchunks - 1; ch >= 0; --ch) {
+        const int b = ch * kThreads + tid;
+        const bool in = b < nvalid;
+        const bool end = in && (b == nvalid - 1 || expert_ids[b + 1] != expert_ids[b]);
+        int r1 = block_suffix_min(end ? b : INT_MAX, wave_tot);
+        if (r1 > carry[0]) r1 = carry[0];
+        if (in) run_last[b] = r1;
+        __syncthreads();
+        if (tid == 0) carry[0] = r1;
+        __syncthreads();
+    }
+    __threadfence_block();
+    // tile starts, compacted in block order
+    if (tid == 0) carry[1] = 0;
+    __syncthreads();
+    for (int ch = 0; ch < nchunks; ++ch) {
+        const int b = ch * kThreads + tid;
+        bool anchor = false;
         int n = 0;
-        if (anchor) {
-            n = 1;
-            while (n < group && b + n < nvalid && expert_ids[b + n] == e) ++n;
+        if (b < nvalid && expert_ids[b] >= 0) {
+            const int r0 = run_first[b], L = run_last[b] - r0 + 1, pos = b - r0;
+            const int nt = (L + group - 1) / group, base = L / nt, rem = L % nt;
+            const int big = rem * (base + 1);  // blocks in the first rem tiles, of base + 1 blocks each
+            if (pos < big) {
+                anchor = pos % (base + 1) == 0;
+                n = base + 1;
+            } else {
+                anchor = (pos - big) % base == 0;
+                n = base;
+            }
         }
         int total;
         const int excl = block_exclusive_scan(anchor ? 1 : 0, wave_tot, &total);
         if (anchor) {
-            tiles[2 * (carry[0] + excl)] = b;
-            tiles[2 * (carry[0] + excl) + 1] = n;
+            tiles[2 * (carry[1] + excl)] = b;
+            tiles[2 * (carry[1] + excl) + 1] = n;
         }
         __syncthreads();
-        if (tid == kThreads - 1) {
-            carry[0] += total;
-            carry[1] = run0;
-        }
+        if (tid == 0) carry[1] += total;
         __syncthreads();
     }
-    if (tid == 0) *count = carry[0];
+    if (tid == 0) *count = carry[1];
 }
 
 // Offsets form -> indexed form: rows [off[e], off[e+1]) of expert e become
@@ -290,9 +352,9 @@ hipError_t launch_offsets_to_route(const int32_t* offsets, int E, int rows_max, 
 }
 
 hipError_t launch_tile_map(const int32_t* expert_ids, const int32_t* ntp, int block_m, int max_blocks, int group,
-                           int32_t* tiles, int32_t* count, hipStream_t s) {
+                           int32_t* tiles, int32_t* count, int32_t* scratch, hipStream_t s) {
     hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(kThreads), 0, s, expert_ids, ntp, block_m, max_blocks, group,
-                       tiles, count);
+                       tiles, count, scratch);
     return hipGetLastError();
 }
 

@@ -95,7 +95,7 @@ hipError_t launch_route_prep(const int32_t* topk_ids, int R, int E, int block_m,
                              int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntp, int32_t* offsets,
                              int32_t* counts, hipStream_t s);
 hipError_t launch_tile_map(const int32_t* expert_ids, const int32_t* ntp, int block_m, int max_blocks, int group,
-                           int32_t* tiles, int32_t* count, hipStream_t s);
+                           int32_t* tiles, int32_t* count, int32_t* scratch, hipStream_t s);
 hipError_t launch_offsets_to_route(const int32_t* offsets, int E, int rows_max, int block_m, int max_padded,
                                    int max_blocks, int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntp,
                                    hipStream_t s);
@@ -114,6 +114,7 @@ struct GemmArgs {
     const int32_t* ntp = nullptr;  // num_tokens_padded (device) when known: bounds the valid route blocks
     int32_t* tiles = nullptr;      // prefill with 32-row route blocks: tile list (first block, blocks) pairs
     int32_t* tile_count = nullptr; // ... and its length (device)
+    int32_t* tile_scratch = nullptr; // 2 * max_blocks ints the tile list is built with
     float* partials = nullptr;     // split-K partial tiles (decode, k_split > 1)
     unsigned* counters = nullptr;  // split-K arrival counters, zero between calls
 };
