@@ -36,6 +36,7 @@ import numpy as np  # noqa: E402
 
 METRIC = "us/call + effective weight GB/s (% HBM peak), W4A16 MoE grouped GEMM"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense BF16 matrix peak of the MI355X
 ROTATION_BYTES = 1 << 30
 COPY_CAL_BYTES = 256 << 20
 
@@ -54,11 +55,35 @@ def workload_spec(name: str) -> dict:
                     desc="Kimi-K2-shaped one-GPU expert share: 48 local of 384 experts, top-8 uniform "
                          "(about 1/8 of routes local), hidden 7168, intermediate 2048, %d tokens" % T)
 
+    def deepseek(T):
+        # the router's ids and weights come from one draw
+        r = {}
+
+        def draw():
+            if not r:
+                r["ids"], r["tw"] = synth.deepseek_router(T)
+            return r
+
+        return dict(E=256, k=8, H=7168, I=2048, T=T, cfg=5, device_weights=True, routes=lambda: draw()["ids"],
+                    router_weights=lambda: draw()["tw"],
+                    desc="DeepSeek-V3-shaped fused expert MLP on one GPU: 256 experts, top-8 of a softmax "
+                         "router over seeded BF16 logits, hidden 7168, intermediate 2048, %d tokens" % T)
+
+    def kimi_prefill(T):
+        return dict(E=48, k=8, H=7168, I=2048, T=T, cfg=4, device_weights=True,
+                    routes=lambda: synth.kimi_prefill_routes(T),
+                    desc="Kimi-K2-shaped one-GPU prefill share: 48 local of 384 experts, top-8 with Zipf(1.1) "
+                         "expert popularity (about 1/8 of routes local, some local experts empty), hidden 7168, "
+                         "intermediate 2048, %d tokens" % T)
+
     table = {}
     for T in (1, 8, 64, 512):
         table["qwen3-moe-t%d" % T] = qwen3(T)
     for T in (1, 2, 4, 8, 16, 32, 64, 128, 256):
         table["kimi-moe-t%d" % T] = kimi(T)
+    for T in (1, 32, 512, 4096):
+        table["deepseek-moe-t%d" % T] = deepseek(T)
+    table["kimi-prefill-t8192"] = kimi_prefill(8192)
     if name not in table:
         raise SystemExit("unknown workload %s; choose from %s" % (name, ", ".join(sorted(table))))
     spec = table[name]
@@ -118,18 +143,52 @@ def committed_traffic(workload: str):
         return None
 
 
-def make_inputs(spec):
+def make_inputs(spec, dev=None):
+    """x, ids, topk weights and the two weight sets: numpy arrays (codes uint8, scales BF16 bits), or, for
+    weight sets of gigabytes, torch tensors drawn on the GPU (codes uint8, scales bfloat16)."""
     import synth
 
     E, k, H, I, T = spec["E"], spec["k"], spec["H"], spec["I"], spec["T"]
     rng = synth.rng_for(spec["cfg"], 7)
     x = synth.activations(rng, T, H)
-    c13, s13 = synth.expert_weights(spec["cfg"], E, 2 * I, H, salt=1)
-    c2, s2 = synth.expert_weights(spec["cfg"], E, H, I, salt=2)
+    if spec.get("device_weights"):
+        base = 1000 * spec["cfg"]
+        c13, s13 = synth.codes_device(base + 1, E, 2 * I, H, dev), synth.scales_device(base + 2, E, 2 * I, H, dev)
+        c2, s2 = synth.codes_device(base + 3, E, H, I, dev), synth.scales_device(base + 4, E, H, I, dev)
+    else:
+        c13, s13 = synth.expert_weights(spec["cfg"], E, 2 * I, H, salt=1)
+        c2, s2 = synth.expert_weights(spec["cfg"], E, H, I, salt=2)
     ids = spec["routes"]()
-    tw = rng.uniform(0.1, 1.0, (T, k)).astype(np.float32)
-    tw /= tw.sum(axis=1, keepdims=True)
+    if "router_weights" in spec:
+        tw = spec["router_weights"]()
+    else:
+        tw = rng.uniform(0.1, 1.0, (T, k)).astype(np.float32)
+        tw /= tw.sum(axis=1, keepdims=True)
     return x, ids, tw, c13, s13, c2, s2
+
+
+def host_expert_subset(ids, E, weights, max_experts):
+    """For an oracle run on weights held on the GPU: the longest prefix of tokens whose local experts number
+    at most ``max_experts``, those experts' weights copied to the host, and the ids renumbered to them."""
+    import torch
+
+    Ts, seen = 0, set()
+    for t in range(ids.shape[0]):
+        row = {int(e) for e in ids[t] if 0 <= e < E}
+        if len(seen | row) > max_experts and Ts > 0:
+            break
+        seen |= row
+        Ts += 1
+    used = np.array(sorted(seen), np.int64)
+    remap = np.full(E, -1, np.int32)
+    remap[used] = np.arange(used.size, dtype=np.int32)
+    sub_ids = np.where((ids[:Ts] >= 0) & (ids[:Ts] < E), remap[np.clip(ids[:Ts], 0, E - 1)], -1).astype(np.int32)
+    idx = torch.from_numpy(used).to(weights[0].device)
+    host = []
+    for w in weights:
+        t = w.index_select(0, idx).cpu()
+        host.append(t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy())
+    return Ts, sub_ids, host
 
 
 def cpu_baseline(spec, inputs, weight_bytes_step, budget_s=10.0):
@@ -140,11 +199,16 @@ def cpu_baseline(spec, inputs, weight_bytes_step, budget_s=10.0):
     o = oracle.Oracle(oracle.build())
     threads = min(16, os.cpu_count() or 1)
     T = spec["T"]
+    if spec.get("device_weights"):
+        # weights live on the GPU: the oracle gets the tokens whose experts fit a host copy of 24 experts
+        Tmax, ids, (c13, s13, c2, s2) = host_expert_subset(ids, spec["E"], (c13, s13, c2, s2), 24)
+        x, tw = x[:Tmax], tw[:Tmax]
     # whole steps when one fits the budget, else the first Ts tokens, extrapolated linearly in tokens
     t0 = time.perf_counter()
     o.fused_moe(x[:1], ids[:1], tw[:1], c13, s13, c2, s2, nthreads=threads)
     one_tok = max(time.perf_counter() - t0, 1e-3)
     Ts = T if one_tok * T <= 3 * budget_s else max(1, int(budget_s / one_tok))
+    Ts = min(Ts, ids.shape[0])
     times = []
     start = time.perf_counter()
     while True:
@@ -191,7 +255,7 @@ def main():
     spec = workload_spec(args.workload)
     E, k, H, I, T = spec["E"], spec["k"], spec["H"], spec["I"], spec["T"]
     print("[bench] %s" % spec["desc"], file=sys.stderr, flush=True)
-    inputs = make_inputs(spec)
+    inputs = make_inputs(spec, dev)
     x, ids, tw, c13, s13, c2, s2 = inputs
     flat = ids.reshape(-1)
     valid = (flat >= 0) & (flat < E)
@@ -203,8 +267,14 @@ def main():
     def u16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
 
-    w13 = w4.pack_weights(torch.from_numpy(c13).to(dev), u16(s13))
-    w2 = w4.pack_weights(torch.from_numpy(c2).to(dev), u16(s2))
+    def codes_dev(c):
+        return c if isinstance(c, torch.Tensor) else torch.from_numpy(c).to(dev)
+
+    def scales_dev(sc):
+        return sc.view(torch.int16) if isinstance(sc, torch.Tensor) else u16(sc)
+
+    w13 = w4.pack_weights(codes_dev(c13), scales_dev(s13))
+    w2 = w4.pack_weights(codes_dev(c2), scales_dev(s2))
     per_copy = w13.packed.numel() + w2.packed.numel()
     ncopies = max(2, math.ceil(ROTATION_BYTES / per_copy) + 1)
     copies = [(w13, w2)]
@@ -285,10 +355,13 @@ def main():
     # ---- the dominant kernel alone: its launch as in the fused call (same plan, routing and workspace layout
     # rules), captured back to back in one HIP graph that cycles through the weight copies; HIP events on the
     # launch stream around the replays give the average launch duration without host gaps
+    prefill_plan = p13.kernel == L.KERNEL_PREFILL
     route = w4.route_prep(idsd, E, p13.block_m)
     h_out = torch.empty((T * k, I), dtype=torch.bfloat16, device=dev)
     gws = w4.zeroed_workspace(w4.gemm_workspace_bytes(p13, T * k, E, 2 * I), dev)
     reps = max(ncopies, 20 // ncopies * ncopies)
+    if prefill_plan:
+        reps = ncopies  # launches of milliseconds: one per weight copy is enough
     for c in range(ncopies):
         w4.grouped_gemm_silu(xd, k, copies[c][0], route, p13, out=h_out, ws=gws)
     torch.cuda.synchronize()
@@ -308,9 +381,15 @@ def main():
     gate_up_us = e0.elapsed_time(e1) * 1e3 / (n_replay * reps)
 
     # dominant kernel: gate_up grouped GEMM with the SiLU*mul epilogue (decode or prefill kernel by plan).
-    # Algorithmic bytes: packed weights of the active experts, x once, h written once, routing read once.
-    alg_bytes = gate_up_algorithmic_bytes(spec, p13.block_m)
-    achieved = alg_bytes / (gate_up_us * 1e-6) / 1e9
+    # Decode is bound by HBM: algorithmic bytes = packed weights of the active experts, x once, h written once,
+    # routing read once.  Prefill is bound by the matrix cores: algorithmic flops = 2 * valid routes * 2I * H.
+    prefill = p13.kernel == L.KERNEL_PREFILL
+    if prefill:
+        alg_flops = 2.0 * Rv * (2 * I) * H
+        achieved = alg_flops / (gate_up_us * 1e-6) / 1e12
+    else:
+        alg_bytes = gate_up_algorithmic_bytes(spec, p13.block_m)
+        achieved = alg_bytes / (gate_up_us * 1e-6) / 1e9
     traffic = committed_traffic(spec["name"])
     if p13.kernel == L.KERNEL_DECODE and p13.block_m == 16:
         kname = "gemm_decode_reg_kernel<NBW=%d,D=2,act out> (gate_up + silu_mul, k_split %d)" % (p13.n_blocks,
@@ -336,11 +415,16 @@ def main():
                    "weight_rotation_copies": ncopies, "parallelism": "none (one GPU)"},
         "stages_us": {n: round(float(v), 2) for n, v in zip(stages, stage.mean(0))},
         "gpu_us_per_step_events": round(gpu_step_us, 2),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kname,
-                     "bytes_per_launch": int(alg_bytes), "avg_launch_us": round(gate_up_us, 2),
-                     "timing": "HIP events around %d graph-captured back-to-back launches" % (n_replay * reps)},
+        "roofline": ({"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                      "kernel": kname, "flops_per_launch": alg_flops} if prefill else
+                     {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kname,
+                      "bytes_per_launch": int(alg_bytes)}),
     }
+    result["roofline"].update({"avg_launch_us": round(gate_up_us, 2),
+                               "timing": "HIP events around %d graph-captured back-to-back launches"
+                                         % (n_replay * reps)})
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(spec, inputs, weight_bytes_step, args.cpu_budget)
     print(json.dumps(result), flush=True)

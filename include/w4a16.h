@@ -151,6 +151,23 @@ int w4a16_route_prep(const int32_t* topk_ids, int T, int k, int E, int block_m, 
                      int32_t* expert_ids, int32_t* num_tokens_padded, int32_t* expert_offsets,
                      int32_t* counts, hipStream_t s);
 
+/* Same outputs, bit for bit, as w4a16_route_prep, from several workgroups
+ * when T*k exceeds 8192 routes (else from one, as above).  The routes are
+ * cut into chunks of 4096: each chunk is counted per expert, one workgroup
+ * turns the counts into offsets and each chunk's first slot per expert, and
+ * each chunk is then scattered from there with the same in-chunk ranking,
+ * so the order inside an expert stays ascending route index (Chord page,
+ * "Two kernel families": the indexed layout; no host readback).
+ *   ws   device scratch of w4a16_route_prep_workspace_bytes(T, k, E) bytes
+ *        (ceil(T*k / 4096) * E ints when more than two chunks, else 0; may
+ *        then be NULL), 4-byte aligned, owned by the caller, contents on
+ *        entry ignored.  Calls sharing ws must not run concurrently.
+ * Errors: as w4a16_route_prep, plus WORKSPACE_TOO_SMALL. */
+int w4a16_route_prep_workspace_bytes(int T, int k, int E, size_t* bytes);
+int w4a16_route_prep_ws(const int32_t* topk_ids, int T, int k, int E, int block_m, int32_t* sorted_ids,
+                        int32_t* expert_ids, int32_t* num_tokens_padded, int32_t* expert_offsets,
+                        int32_t* counts, void* ws, size_t ws_bytes, hipStream_t s);
+
 /* ---------------------------------------------------------------- planning */
 
 /* Choose a plan from the routed rows per expert, not the token count (Chord

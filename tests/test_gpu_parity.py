@@ -89,6 +89,30 @@ ROUTE_CASES = [
 ]
 
 
+MULTI_ROUTE_CASES = [
+    ("deepseek T4096", lambda: synth.deepseek_router(4096)[0], 256, 32),
+    ("kimi prefill T8192", lambda: synth.kimi_prefill_routes(8192), 48, 32),
+    ("one expert R=20000", lambda: np.full((10000, 2), 5, np.int32), 8, 128),
+    ("E1024 R=12289", lambda: np.random.default_rng(6).integers(-3, 1030, (12289, 1)).astype(np.int32), 1024, 16),
+]
+
+
+@pytest.mark.parametrize("name,gen,E,BM", MULTI_ROUTE_CASES, ids=[c[0] for c in MULTI_ROUTE_CASES])
+def test_route_prep_multi_workgroup_bit_exact(orc, name, gen, E, BM):
+    # the several-workgroup routing (more than two chunks of 4096 routes) against the oracle, field by field
+    _say("route_prep_ws %s" % name)
+    ids = np.ascontiguousarray(gen(), np.int32)
+    assert w4.route_prep_workspace_bytes(ids.shape[0], ids.shape[1], E) > 0
+    ref = orc.route_prep(ids, E, BM)
+    got = w4.route_prep(i32(ids), E, BM, multi=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(got["sorted_ids"].cpu().numpy(), ref["sorted_ids"]), "sorted_ids"
+    assert np.array_equal(got["expert_ids"].cpu().numpy(), ref["expert_ids"]), "expert_ids"
+    assert int(got["num_tokens_padded"].cpu()[0]) == ref["num_tokens_padded"]
+    assert np.array_equal(got["expert_offsets"].cpu().numpy(), ref["expert_offsets"]), "expert_offsets"
+    assert np.array_equal(got["counts"].cpu().numpy(), ref["counts"]), "counts"
+
+
 @pytest.mark.parametrize("name,gen,E,BM", ROUTE_CASES, ids=[c[0] for c in ROUTE_CASES])
 def test_route_prep_bit_exact(orc, name, gen, E, BM):
     _say("route_prep %s" % name)
@@ -341,9 +365,12 @@ def orc_bf16_to_f64(b):
     return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def test_moe_combine(orc):
-    rng = np.random.default_rng(8)
-    T, k, H, E = 21, 4, 128, 6
+@pytest.mark.parametrize("T,k,H,E", [(21, 4, 128, 6), (5, 8, 7168, 9), (7, 10, 2056, 12), (9, 3, 130, 4)],
+                         ids=lambda v: str(v))
+def test_moe_combine(orc, T, k, H, E):
+    # eight columns per lane when H % 8 == 0 (with a partial last column group, and more routes than one unrolled
+    # pass), two per lane otherwise
+    rng = np.random.default_rng(8 + H)
     y = rng.standard_normal((T * k, H)).astype(np.float32)
     tw = rng.uniform(0, 1, (T, k)).astype(np.float32)
     ids = rng.integers(-2, E + 2, (T, k)).astype(np.int32)
@@ -362,8 +389,10 @@ FUSED_TOL = 1e-2
 
 
 @pytest.mark.parametrize("shape", [(16, 8, 2, 256, 128), (64, 16, 4, 512, 256), (300, 8, 2, 256, 128),
-                                   (3, 4, 2, 128, 64)], ids=lambda s: "T%d-E%d-k%d-H%d-I%d" % s)
+                                   (3, 4, 2, 128, 64), (2100, 16, 4, 128, 64)],
+                         ids=lambda s: "T%d-E%d-k%d-H%d-I%d" % s)
 def test_fused_moe(orc, shape):
+    # the last shape has 8400 routes: the routing runs on several workgroups
     T, E, k, H, I = shape
     _say("fused %s" % (shape,))
     rng = np.random.default_rng(T * 7 + E)

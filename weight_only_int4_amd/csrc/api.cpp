@@ -3,6 +3,7 @@
 // allocated or read here; every device operation is a launch on the caller's
 // stream.
 #include <math.h>
+#include <stdint.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -233,7 +234,8 @@ hipError_t run_gemm(const GemmArgs& a, const w4a16_plan& p, hipStream_t s) {
 // Workspace carve-up of the fused expert MLP.
 struct FusedLayout {
     int maxP, maxB;
-    size_t off_sorted, off_eids, off_ntp, off_offsets, off_counts, off_h, off_y, off_split, off_tiles, total;
+    size_t off_sorted, off_eids, off_ntp, off_offsets, off_counts, off_h, off_y, off_split, off_tiles, off_route,
+        total;
 };
 
 // The split-K area goes first so its counters sit at a fixed place regardless of the route block.
@@ -245,6 +247,7 @@ FusedLayout fused_layout(int T, int k, int E, int H, int I, int BM, size_t split
     size_t o = 0;
     f.off_split = o;  o = align_up(o + split_bytes, 256);
     f.off_tiles = o;  o = align_up(o + tile_bytes, 256);
+    f.off_route = o;  o = align_up(o + sizeof(int32_t) * route_prep_scratch_ints((int)R, E), 256);
     f.off_sorted = o; o = align_up(o + sizeof(int32_t) * (size_t)f.maxP, 256);
     f.off_eids = o;   o = align_up(o + sizeof(int32_t) * (size_t)f.maxB, 256);
     f.off_ntp = o;    o = align_up(o + sizeof(int32_t), 256);
@@ -362,6 +365,34 @@ int w4a16_route_prep(const int32_t* topk_ids, int T, int k, int E, int block_m, 
         return fail(W4A16_INVALID_ARG, "%s: NULL pointer argument", what);
     return check_launch(launch_route_prep(topk_ids, T * k, E, block_m, maxP, maxB, sorted_ids, expert_ids,
                                           num_tokens_padded, expert_offsets, counts, s),
+                        what);
+}
+
+int w4a16_route_prep_workspace_bytes(int T, int k, int E, size_t* bytes) {
+    if (!bytes || T < 0 || k < 1 || E < 1 || (long)T * k > INT32_MAX)
+        return fail(W4A16_INVALID_ARG, "w4a16_route_prep_workspace_bytes: T=%d k=%d E=%d", T, k, E);
+    *bytes = sizeof(int32_t) * route_prep_scratch_ints(T * k, E);
+    return ok();
+}
+
+int w4a16_route_prep_ws(const int32_t* topk_ids, int T, int k, int E, int block_m, int32_t* sorted_ids,
+                        int32_t* expert_ids, int32_t* num_tokens_padded, int32_t* expert_offsets, int32_t* counts,
+                        void* ws, size_t ws_bytes, hipStream_t s) {
+    const char* what = "w4a16_route_prep_ws";
+    int maxP, maxB;
+    int rc = w4a16_route_bounds(T, k, E, block_m, &maxP, &maxB);
+    if (rc) return rc;
+    if (E > W4A16_MAX_EXPERTS) return fail(W4A16_UNSUPPORTED_SHAPE, "%s: E=%d exceeds %d", what, E, W4A16_MAX_EXPERTS);
+    if ((T > 0 && !topk_ids) || (maxP > 0 && !sorted_ids) || (maxB > 0 && !expert_ids) || !num_tokens_padded ||
+        !expert_offsets || !counts)
+        return fail(W4A16_INVALID_ARG, "%s: NULL pointer argument", what);
+    const size_t need = sizeof(int32_t) * route_prep_scratch_ints(T * k, E);
+    if (need && (!ws || ws_bytes < need))
+        return fail(W4A16_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, needs %zu", what, ws_bytes, need);
+    if (need && ((uintptr_t)ws & 3u)) return fail(W4A16_INVALID_ARG, "%s: workspace must be 4-byte aligned", what);
+    return check_launch(launch_route_prep_scratch(topk_ids, T * k, E, block_m, maxP, maxB, sorted_ids, expert_ids,
+                                                  num_tokens_padded, expert_offsets, counts,
+                                                  need ? static_cast<int32_t*>(ws) : nullptr, s),
                         what);
 }
 
@@ -671,8 +702,8 @@ int w4a16_fused_moe_profiled(const uint16_t* x, const int32_t* topk_ids, const f
         }                                                                                  \
     } while (0)
     W4A16_STAGE(0);
-    rc = check_launch(launch_route_prep(topk_ids, R, E, p13.block_m, f.maxP, f.maxB, sorted_ids, expert_ids, ntp, offsets,
-                                        counts, s),
+    rc = check_launch(launch_route_prep_scratch(topk_ids, R, E, p13.block_m, f.maxP, f.maxB, sorted_ids, expert_ids, ntp,
+                                                offsets, counts, reinterpret_cast<int32_t*>(base + f.off_route), s),
                       "w4a16_fused_moe (route_prep)");
     if (rc) return rc;
     W4A16_STAGE(1);

@@ -62,6 +62,56 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     *reinterpret_cast<uint32_t*>(out + (size_t)t * H + n) = packed;
 }
 
+// The same sum, eight columns per lane: one workgroup per (token, 2048 columns).  The token's ids and weights
+// are uniform across the workgroup; the y rows of up to eight routes are in flight together (two 16-byte loads
+// per route and lane) before any is accumulated, in route order as above.  Needs H % 8 == 0.
+constexpr int kCombineCols = 8;
+constexpr int kCombineUnroll = 8;
+
+__global__ __launch_bounds__(256) void combine8_kernel(const float* __restrict__ y, const float* __restrict__ tw,
+                                                       const int32_t* __restrict__ ids, int T, int k, int E, int H,
+                                                       uint16_t* __restrict__ out) {
+    const int t = blockIdx.x;
+    const int n = (blockIdx.y * 256 + threadIdx.x) * kCombineCols;
+    if (n >= H) return;
+    const int32_t* tid = ids + (size_t)t * k;
+    const float* tww = tw + (size_t)t * k;
+    float acc[kCombineCols];
+#pragma unroll
+    for (int c = 0; c < kCombineCols; ++c) acc[c] = 0.f;
+    for (int j0 = 0; j0 < k; j0 += kCombineUnroll) {
+        float4 v[kCombineUnroll][2];
+        float wt[kCombineUnroll];
+        bool ok[kCombineUnroll];
+#pragma unroll
+        for (int u = 0; u < kCombineUnroll; ++u) {
+            const int j = j0 + u;
+            const int e = j < k ? tid[j] : -1;
+            ok[u] = e >= 0 && e < E;
+            wt[u] = ok[u] ? tww[j] : 0.f;
+            if (ok[u]) {
+                const float4* row = reinterpret_cast<const float4*>(y + ((size_t)t * k + j) * H + n);
+                v[u][0] = row[0];
+                v[u][1] = row[1];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kCombineUnroll; ++u) {
+            if (!ok[u]) continue;
+            const float vv[kCombineCols] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w,
+                                            v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
+#pragma unroll
+            for (int c = 0; c < kCombineCols; ++c) acc[c] = acc[c] + wt[u] * vv[c];
+        }
+    }
+    uint4 o;
+    o.x = (uint32_t)f32_to_bf16_bits(acc[0]) | ((uint32_t)f32_to_bf16_bits(acc[1]) << 16);
+    o.y = (uint32_t)f32_to_bf16_bits(acc[2]) | ((uint32_t)f32_to_bf16_bits(acc[3]) << 16);
+    o.z = (uint32_t)f32_to_bf16_bits(acc[4]) | ((uint32_t)f32_to_bf16_bits(acc[5]) << 16);
+    o.w = (uint32_t)f32_to_bf16_bits(acc[6]) | ((uint32_t)f32_to_bf16_bits(acc[7]) << 16);
+    *reinterpret_cast<uint4*>(out + (size_t)t * H + n) = o;
+}
+
 }  // namespace
 
 hipError_t launch_silu_mul(const uint16_t* gu, int rows, int I, uint16_t* h, hipStream_t s) {
@@ -82,6 +132,12 @@ hipError_t launch_combine(const float* y, const float* tw, const int32_t* ids, i
                           uint16_t* out, hipStream_t s) {
     const long work = (long)T * (H / 2);
     if (work == 0) return hipSuccess;
+    if (H % kCombineCols == 0 && ((uintptr_t)y & 15u) == 0 && ((uintptr_t)out & 15u) == 0) {
+        const unsigned col_groups = (unsigned)((H / kCombineCols + 255) / 256);
+        hipLaunchKernelGGL(combine8_kernel, dim3((unsigned)T, col_groups), dim3(256), 0, s, y, tw, ids, T, k, E, H,
+                           out);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, y, tw, ids, T, k, E, H,
                        out);
     return hipGetLastError();

@@ -141,6 +141,124 @@ __global__ __launch_bounds__(kThreads) void route_prep_kernel(const int32_t* __r
     }
 }
 
+// ---- the same routing tensors from several workgroups, for many routes (needs scratch)
+//
+// Routes are cut into chunks of kChunk.  (1) Each chunk's workgroup counts its routes per expert.  (2) One
+// workgroup turns the counts into per-expert totals, offsets and padded offsets (as above), and each chunk's
+// first slot per expert: the expert's padded offset plus the routes of that expert in earlier chunks; it also
+// writes the sentinels and expert_ids.  (3) Each chunk's workgroup scatters its routes from those bases with the
+// same in-chunk ranking as above, so the order inside an expert is again ascending route index.
+constexpr int kChunk = 4 * kThreads;
+
+__global__ __launch_bounds__(kThreads) void route_count_kernel(const int32_t* __restrict__ ids, int R, int E,
+                                                               int32_t* __restrict__ chunk_counts) {
+    extern __shared__ int cnt[];
+    const int tid = threadIdx.x, c = blockIdx.x;
+    for (int e = tid; e < E; e += kThreads) cnt[e] = 0;
+    __syncthreads();
+    const int end = min(R, (c + 1) * kChunk);
+    for (int i = c * kChunk + tid; i < end; i += kThreads) {
+        const int e = ids[i];
+        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += kThreads) chunk_counts[(size_t)c * E + e] = cnt[e];
+}
+
+// Shared memory (ints): pad_off[E+1] | wave_tot[kWaves+1]
+__global__ __launch_bounds__(kThreads) void route_scan_kernel(int R, int E, int BM, int max_padded, int max_blocks,
+                                                              int nchunks, int32_t* __restrict__ chunk_base,
+                                                              int32_t* __restrict__ sorted_ids,
+                                                              int32_t* __restrict__ expert_ids,
+                                                              int32_t* __restrict__ ntp_out,
+                                                              int32_t* __restrict__ offsets_out,
+                                                              int32_t* __restrict__ counts_out) {
+    extern __shared__ int smem[];
+    int* pad_off = smem;
+    int* wave_tot = pad_off + E + 1;
+    const int tid = threadIdx.x;
+    // E <= kThreads: thread e owns expert e
+    int c = 0;
+    if (tid < E)
+        for (int ch = 0; ch < nchunks; ++ch) {
+            const int v = chunk_base[(size_t)ch * E + tid];
+            chunk_base[(size_t)ch * E + tid] = c;  // routes of expert tid in earlier chunks
+            c += v;
+        }
+    const int padded = tid < E ? ceil_div(c, BM) * BM : 0;
+    int tot_c, tot_p;
+    const int off_c = block_exclusive_scan(c, wave_tot, &tot_c);
+    const int off_p = block_exclusive_scan(padded, wave_tot, &tot_p);
+    if (tid < E) {
+        counts_out[tid] = c;
+        offsets_out[tid] = off_c;
+        pad_off[tid] = off_p;
+        for (int ch = 0; ch < nchunks; ++ch) chunk_base[(size_t)ch * E + tid] += off_p;
+    }
+    if (tid == 0) {
+        offsets_out[E] = tot_c;
+        pad_off[E] = tot_p;
+        *ntp_out = tot_p;
+    }
+    __syncthreads();
+    for (int p = tid; p < max_padded; p += kThreads) sorted_ids[p] = R;
+    for (int b = tid; b < max_blocks; b += kThreads) {
+        const int p = b * BM;
+        int owner = -1;
+        if (p < tot_p) {
+            int lo = 0, hi = E - 1;  // last e with pad_off[e] <= p
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (pad_off[mid] <= p) lo = mid; else hi = mid - 1;
+            }
+            owner = lo;
+        }
+        expert_ids[b] = owner;
+    }
+}
+
+// Shared memory (ints): base[E] | wave_cnt[kWaves][E]
+__global__ __launch_bounds__(kThreads) void route_scatter_kernel(const int32_t* __restrict__ ids, int R, int E,
+                                                                 const int32_t* __restrict__ chunk_base,
+                                                                 int32_t* __restrict__ sorted_ids) {
+    extern __shared__ int smem[];
+    int* base = smem;
+    int* wave_cnt = base + E;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = blockIdx.x;
+    for (int e = tid; e < E; e += kThreads) base[e] = chunk_base[(size_t)c * E + e];
+    for (int x = tid; x < kWaves * E; x += kThreads) wave_cnt[x] = 0;
+    int nbits = 1;
+    while ((1 << nbits) < E) ++nbits;
+    __syncthreads();
+    const int end = min(R, (c + 1) * kChunk);
+    for (int sub = c * kChunk; sub < end; sub += kThreads) {
+        const int i = sub + tid;
+        const int e = i < end ? ids[i] : -1;
+        const bool valid = e >= 0 && e < E;
+        uint64_t match = __ballot(valid);
+        for (int bit = 0; bit < nbits; ++bit) {
+            const uint64_t ones = __ballot(valid && ((e >> bit) & 1));
+            match &= ((e >> bit) & 1) ? ones : ~ones;
+        }
+        const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        const int rank_w = __popcll(match & lower);
+        const bool leader = valid && rank_w == 0;
+        if (leader) wave_cnt[wave * E + e] = __popcll(match);
+        __syncthreads();
+        if (valid) {
+            int prior = base[e];
+            for (int w = 0; w < wave; ++w) prior += wave_cnt[w * E + e];
+            sorted_ids[prior + rank_w] = i;
+        }
+        __syncthreads();
+        if (leader) {
+            atomicAdd(&base[e], wave_cnt[wave * E + e]);
+            wave_cnt[wave * E + e] = 0;
+        }
+        __syncthreads();
+    }
+}
+
 // Inclusive max-scan of one int per thread across the workgroup.
 __device__ int block_inclusive_max(int v, int* wave_tot) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -339,6 +457,36 @@ hipError_t launch_route_prep(const int32_t* topk_ids, int R, int E, int block_m,
     if (shmem > 65536 && attr != hipSuccess) return attr;
     hipLaunchKernelGGL(route_prep_kernel, dim3(1), dim3(kThreads), shmem, s, topk_ids, R, E, block_m, max_padded,
                        max_blocks, sorted_ids, expert_ids, ntp, offsets, counts);
+    return hipGetLastError();
+}
+
+size_t route_prep_scratch_ints(int R, int E) {
+    const int nchunks = (R + kChunk - 1) / kChunk;
+    return nchunks > 2 ? (size_t)nchunks * E : 0;
+}
+
+hipError_t launch_route_prep_scratch(const int32_t* topk_ids, int R, int E, int block_m, int max_padded,
+                                     int max_blocks, int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntp,
+                                     int32_t* offsets, int32_t* counts, int32_t* scratch, hipStream_t s) {
+    const int nchunks = (R + kChunk - 1) / kChunk;
+    if (nchunks <= 2 || scratch == nullptr)
+        return launch_route_prep(topk_ids, R, E, block_m, max_padded, max_blocks, sorted_ids, expert_ids, ntp,
+                                 offsets, counts, s);
+    hipLaunchKernelGGL(route_count_kernel, dim3(nchunks), dim3(kThreads), sizeof(int) * (size_t)E, s, topk_ids, R,
+                       E, scratch);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kThreads), sizeof(int) * ((size_t)E + 1 + kWaves + 1), s, R, E,
+                       block_m, max_padded, max_blocks, nchunks, scratch, sorted_ids, expert_ids, ntp, offsets,
+                       counts);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const size_t scatter_lds = sizeof(int) * ((size_t)E + (size_t)kWaves * E);
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(route_scatter_kernel),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (scatter_lds > 65536 && attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(route_scatter_kernel, dim3(nchunks), dim3(kThreads), scatter_lds, s, topk_ids, R, E, scratch,
+                       sorted_ids);
     return hipGetLastError();
 }
 

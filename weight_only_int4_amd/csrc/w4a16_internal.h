@@ -94,6 +94,11 @@ hipError_t launch_dequant(const void* packed, const Shape& sh, int expert, float
 hipError_t launch_route_prep(const int32_t* topk_ids, int R, int E, int block_m, int max_padded, int max_blocks,
                              int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntp, int32_t* offsets,
                              int32_t* counts, hipStream_t s);
+// Ints of scratch the routing of R routes uses when spread over several workgroups (0: one workgroup does it).
+size_t route_prep_scratch_ints(int R, int E);
+hipError_t launch_route_prep_scratch(const int32_t* topk_ids, int R, int E, int block_m, int max_padded,
+                                     int max_blocks, int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntp,
+                                     int32_t* offsets, int32_t* counts, int32_t* scratch, hipStream_t s);
 hipError_t launch_tile_map(const int32_t* expert_ids, const int32_t* ntp, int block_m, int max_blocks, int group,
                            int32_t* tiles, int32_t* count, int32_t* scratch, hipStream_t s);
 hipError_t launch_offsets_to_route(const int32_t* offsets, int E, int rows_max, int block_m, int max_padded,

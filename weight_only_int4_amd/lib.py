@@ -55,6 +55,8 @@ _SIGS = {
     "w4a16_dequant": (_I, [_P, _I, _P, _P, _P]),
     "w4a16_route_bounds": (_I, [_I, _I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
     "w4a16_route_prep": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
+    "w4a16_route_prep_workspace_bytes": (_I, [_I, _I, _I, ctypes.POINTER(_SZ)]),
+    "w4a16_route_prep_ws": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "w4a16_plan_select": (_I, [_I, _I, _I, _I, _I, ctypes.c_float, ctypes.POINTER(Plan)]),
     "w4a16_gemm_workspace_bytes": (_I, [ctypes.POINTER(Plan), _I, _I, _I, ctypes.POINTER(_SZ)]),
     "w4a16_grouped_gemm": (_I, [_P, _I, _P, _P, _P, _P, _I, ctypes.POINTER(Plan), _P, _P, _SZ, _P]),
@@ -181,8 +183,15 @@ def route_bounds(T: int, k: int, E: int, block_m: int):
     return mp.value, mb.value
 
 
-def route_prep(topk_ids: torch.Tensor, E: int, block_m: int, stream=None) -> dict:
-    """topk_ids int32 [T,k] on the GPU -> routing tensors (all on the GPU)."""
+def route_prep_workspace_bytes(T: int, k: int, E: int) -> int:
+    out = _SZ(0)
+    _check(load().w4a16_route_prep_workspace_bytes(T, k, E, ctypes.byref(out)))
+    return out.value
+
+
+def route_prep(topk_ids: torch.Tensor, E: int, block_m: int, stream=None, multi: bool = False) -> dict:
+    """topk_ids int32 [T,k] on the GPU -> routing tensors (all on the GPU).  ``multi``: the several-workgroup
+    form with its scratch (w4a16_route_prep_ws)."""
     T, k = topk_ids.shape
     maxP, maxB = route_bounds(T, k, E, block_m)
     dev = topk_ids.device
@@ -191,6 +200,16 @@ def route_prep(topk_ids: torch.Tensor, E: int, block_m: int, stream=None) -> dic
                num_tokens_padded=torch.empty(1, dtype=torch.int32, device=dev),
                expert_offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
                counts=torch.empty(E, dtype=torch.int32, device=dev), block_m=block_m, R=T * k, E=E)
+    if multi:
+        nbytes = route_prep_workspace_bytes(T, k, E)
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+        _check(load().w4a16_route_prep_ws(_ptr(topk_ids) if T else None, T, k, E, block_m,
+                                          ctypes.c_void_p(out["sorted_ids"].data_ptr()),
+                                          ctypes.c_void_p(out["expert_ids"].data_ptr()),
+                                          _ptr(out["num_tokens_padded"]), _ptr(out["expert_offsets"]),
+                                          _ptr(out["counts"]), _ptr(ws), ws.numel(), _stream(stream)))
+        out["_ws"] = ws
+        return out
     route_prep_into(topk_ids, E, block_m, out, stream)
     return out
 
