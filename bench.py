@@ -109,21 +109,27 @@ def gate_up_algorithmic_bytes(spec, block_m: int = 16) -> int:
     return active * packed_weight_bytes(2 * I, H) + T * H * 2 + int(valid.sum()) * I * 2 + (maxP + maxB) * 4
 
 
-KERNEL_SOURCES = ("weight_only_int4_amd/csrc/gemm_decode.hip", "weight_only_int4_amd/csrc/gemm_prefill.hip",
-                  "weight_only_int4_amd/csrc/frag.h", "weight_only_int4_amd/csrc/w4a16_internal.h")
+# the sources the gate_up kernel of each family is built from
+KERNEL_SOURCES = {
+    "decode": ("weight_only_int4_amd/csrc/gemm_decode_reg.hip", "weight_only_int4_amd/csrc/gemm_decode.hip",
+               "weight_only_int4_amd/csrc/decode_common.h", "weight_only_int4_amd/csrc/frag.h",
+               "weight_only_int4_amd/csrc/w4a16_internal.h"),
+    "prefill": ("weight_only_int4_amd/csrc/gemm_prefill.hip", "weight_only_int4_amd/csrc/frag.h",
+                "weight_only_int4_amd/csrc/w4a16_internal.h"),
+}
 
 
-def kernel_sources_sha256() -> str:
+def kernel_sources_sha256(family: str) -> str:
     import hashlib
 
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[family]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def committed_traffic(workload: str):
+def committed_traffic(workload: str, family: str):
     """HBM bytes per launch of the gate_up kernel from the committed counter summary of this workload, or None
     when there is none or the kernel sources have changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "gate_up_silu_%s_hbm_traffic.md" % workload)
@@ -135,7 +141,7 @@ def committed_traffic(workload: str):
             if ":" in line and not line.startswith(("|", "#", "`")):
                 key, _, val = line.partition(":")
                 fields[key.strip()] = val.strip()
-    if fields.get("workload") != workload or fields.get("kernel_sources_sha256") != kernel_sources_sha256():
+    if fields.get("workload") != workload or fields.get("kernel_sources_sha256") != kernel_sources_sha256(family):
         return None
     try:
         return int(fields["traffic_bytes_per_launch"])
@@ -390,7 +396,7 @@ def main():
     else:
         alg_bytes = gate_up_algorithmic_bytes(spec, p13.block_m)
         achieved = alg_bytes / (gate_up_us * 1e-6) / 1e9
-    traffic = committed_traffic(spec["name"])
+    traffic = committed_traffic(spec["name"], "prefill" if prefill else "decode")
     if p13.kernel == L.KERNEL_DECODE and p13.block_m == 16:
         kname = "gemm_decode_reg_kernel<NBW=%d,D=2,act out> (gate_up + silu_mul, k_split %d)" % (p13.n_blocks,
                                                                                                p13.k_split)
