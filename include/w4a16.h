@@ -250,6 +250,42 @@ int w4a16_grouped_gemm_offsets(const uint16_t* A_sorted, const int32_t* expert_o
                                const w4a16_weights* w, const w4a16_plan* p, uint16_t* out, void* ws,
                                size_t ws_bytes, hipStream_t s);
 
+/* Contiguous-form grouped GEMM (Chord page, "Grouped SM90 kernels": rows
+ * concatenated by expert, each expert padded to 128 rows, with m_indices
+ * giving each row's expert and -1 on padding rows):
+ *   out[r, n] = bf16( sum_k A[r, k] * w[m_indices[r], n, k] )
+ * for every r < m with 0 <= m_indices[r] < E; other rows of out are untouched.
+ *   A          device BF16 bits [m, K], 16-byte aligned
+ *   m_indices  device int32 [m]
+ *   out        device BF16 bits [m, N]
+ *   ws         >= w4a16_contiguous_workspace_bytes(m, w, p), 16-byte aligned,
+ *              zero-filled once before its first use when p->k_split > 1
+ * The rows are grouped by expert on the device (the routing of
+ * w4a16_route_prep with one route per row), so the 128-row padding and even
+ * the grouping itself are accepted but not required.  The same kernels as
+ * w4a16_grouped_gemm; p->block_m is the route block of that grouping.
+ * Errors: INVALID_ARG, LAYOUT_MISMATCH, UNSUPPORTED_SHAPE, WORKSPACE_TOO_SMALL,
+ * HIP_ERROR. */
+int w4a16_contiguous_workspace_bytes(int m, const w4a16_weights* w, const w4a16_plan* p, size_t* bytes);
+int w4a16_grouped_gemm_contiguous(const uint16_t* A, const int32_t* m_indices, int m, const w4a16_weights* w,
+                                  const w4a16_plan* p, uint16_t* out, void* ws, size_t ws_bytes, hipStream_t s);
+
+/* Masked-form grouped GEMM (Chord page, "Grouped SM90 kernels": a fixed
+ * per-expert row budget max_m, the valid count per expert in masked_m, a
+ * flat output whose rows past each expert's count are to be ignored):
+ *   out[e*max_m + r, n] = bf16( sum_k A[e*max_m + r, k] * w[e, n, k] )
+ * for r < min(masked_m[e], max_m); the other rows of out are untouched.
+ *   A          device BF16 bits [E, max_m, K] (flat [E*max_m, K]), 16-byte aligned
+ *   masked_m   device int32 [E] (negative counts as 0, above max_m as max_m)
+ *   out        device BF16 bits [E*max_m, N]
+ *   ws         >= w4a16_masked_workspace_bytes(max_m, w, p), as above
+ * The pages' host-side expected_m is a planning input: pass it to
+ * w4a16_plan_select as the expected rows per expert.  E*max_m must fit int32.
+ * Errors: as the contiguous form. */
+int w4a16_masked_workspace_bytes(int max_m, const w4a16_weights* w, const w4a16_plan* p, size_t* bytes);
+int w4a16_grouped_gemm_masked(const uint16_t* A, const int32_t* masked_m, int max_m, const w4a16_weights* w,
+                              const w4a16_plan* p, uint16_t* out, void* ws, size_t ws_bytes, hipStream_t s);
+
 /* ---------------------------------------------------------------- expert MLP */
 
 /* h[r, c] = bf16( silu(gu[r, c]) * gu[r, I + c] ), silu(g) = g / (1 + exp(-g)),

@@ -298,6 +298,58 @@ def test_gemm_offsets_form(orc, plan_args):
     check_gemm(got, acc, expert_of_row, E, label="offsets")
 
 
+# ------------------------------------------------------------------ contiguous and masked forms
+
+CM_PLANS = [("decode", 16, 4, 4, 1), ("decode", 32, 2, 4, 2), ("prefill", 64, 4, 4, 1), ("prefill", 32, 2, 4, 1, 128)]
+
+
+@pytest.mark.parametrize("plan_args", CM_PLANS, ids=PLAN_ID)
+@pytest.mark.parametrize("layout", ["padded to 128", "interleaved"])
+def test_gemm_contiguous_form(orc, plan_args, layout):
+    # rows concatenated by expert and padded to 128 rows with -1 (the pages' layout), or the same rows in an
+    # arbitrary order with ids out of range among them: the rows are grouped on the device either way
+    _say("gemm contiguous %s %s" % (layout, plan_args))
+    rng = np.random.default_rng(31)
+    E, N, K = 7, 80, 288
+    counts = np.array([130, 0, 1, 127, 128, 300, 5])
+    parts = []
+    for e, c in enumerate(counts):
+        parts.append(np.full(c, e, np.int32))
+        parts.append(np.full((-c) % 128, -1, np.int32))
+    m_idx = np.concatenate(parts)
+    if layout == "interleaved":
+        m_idx = m_idx[rng.permutation(m_idx.size)]
+        m_idx[::37] = E + 3                               # also out of range: untouched
+    A = synth.activations(rng, m_idx.size, K)
+    codes, scales = synth.codes(rng, E, N, K), synth.scales(rng, E, N, K)
+    w = _pack(codes, scales)
+    plan = w4.make_plan(*plan_args)
+    out = poison_bf16(m_idx.size, N)
+    w4.grouped_gemm_contiguous(u16(A), i32(m_idx), w, plan, out=out)
+    acc, _ = orc.grouped_gemm(A, 1, codes, scales, m_idx, acc64=True)
+    check_gemm(bits(out), acc, m_idx, E, label="contiguous")
+
+
+@pytest.mark.parametrize("plan_args", CM_PLANS, ids=PLAN_ID)
+def test_gemm_masked_form(orc, plan_args):
+    # per-expert row budget with empty, partial, full and over-full (clamped) experts; rows past each count keep
+    # their poison
+    _say("gemm masked %s" % (plan_args,))
+    rng = np.random.default_rng(32)
+    E, max_m, N, K = 6, 96, 64, 256
+    masked = np.array([0, 1, 96, 40, 200, -3], np.int32)
+    A = synth.activations(rng, E * max_m, K)
+    codes, scales = synth.codes(rng, E, N, K), synth.scales(rng, E, N, K)
+    w = _pack(codes, scales)
+    plan = w4.make_plan(*plan_args)
+    out = poison_bf16(E * max_m, N)
+    w4.grouped_gemm_masked(u16(A).view(E, max_m, K), i32(masked), w, plan, out=out)
+    r = np.arange(max_m)
+    expert_of_row = np.concatenate([np.where(r < min(max(c, 0), max_m), e, -1) for e, c in enumerate(masked)])
+    acc, _ = orc.grouped_gemm(A, 1, codes, scales, expert_of_row.astype(np.int32), acc64=True)
+    check_gemm(bits(out), acc, expert_of_row, E, label="masked")
+
+
 # ------------------------------------------------------------------ gate_up GEMM with the activation epilogue
 
 ACT_PLANS = [("decode", 16, 2, 4, 1), ("decode", 16, 4, 4, 1), ("decode", 48, 4, 4, 1), ("decode", 32, 4, 4, 2),

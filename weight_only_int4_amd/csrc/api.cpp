@@ -558,6 +558,122 @@ int w4a16_grouped_gemm_offsets(const uint16_t* A_sorted, const int32_t* expert_o
     return check_launch(run_gemm(a, *p, s), what);
 }
 
+// Masked form: rows [e*max_m, e*max_m + masked_m[e]) of a [E*max_m, K] activation block belong to expert e; the
+// routing tensors are built on the device in the offsets-form workspace layout.
+int w4a16_masked_workspace_bytes(int max_m, const w4a16_weights* w, const w4a16_plan* p, size_t* bytes) {
+    const char* what = "w4a16_masked_workspace_bytes";
+    int rc = check_handle(w, what);
+    if (rc) return rc;
+    if (max_m < 0 || (long)max_m * w->shape.E > INT32_MAX)
+        return fail(W4A16_INVALID_ARG, "%s: max_m=%d", what, max_m);
+    return w4a16_offsets_workspace_bytes(max_m * w->shape.E, w, p, bytes);
+}
+
+int w4a16_grouped_gemm_masked(const uint16_t* A, const int32_t* masked_m, int max_m, const w4a16_weights* w,
+                              const w4a16_plan* p, uint16_t* out, void* ws, size_t ws_bytes, hipStream_t s) {
+    const char* what = "w4a16_grouped_gemm_masked";
+    int rc = check_handle(w, what);
+    if (rc) return rc;
+    rc = validate_plan(p, what);
+    if (rc) return rc;
+    const int E = w->shape.E;
+    if (max_m < 0 || (long)max_m * E > INT32_MAX) return fail(W4A16_INVALID_ARG, "%s: max_m=%d", what, max_m);
+    if (E > W4A16_MAX_EXPERTS) return fail(W4A16_UNSUPPORTED_SHAPE, "%s: too many experts", what);
+    if (max_m == 0) return ok();
+    const int rows = max_m * E;
+    size_t off_sorted, off_eids, off_ntp;
+    int maxP, maxB;
+    GemmWs g;
+    const size_t need = offsets_layout(rows, w, p, &off_sorted, &off_eids, &off_ntp, &maxP, &maxB, &g);
+    if (!ws || ws_bytes < need)
+        return fail(W4A16_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, needs %zu", what, ws_bytes, need);
+    if (!aligned16(ws)) return fail(W4A16_INVALID_ARG, "%s: workspace must be 16-byte aligned", what);
+    if (!A || !masked_m || !out) return fail(W4A16_INVALID_ARG, "%s: NULL pointer argument", what);
+    if (!aligned16(A)) return fail(W4A16_INVALID_ARG, "%s: A must be 16-byte aligned", what);
+    int32_t* sorted_ids = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + off_sorted);
+    int32_t* expert_ids = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + off_eids);
+    int32_t* ntp = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + off_ntp);
+    GemmArgs a{A, 1, w->packed, w->shape, sorted_ids, expert_ids, rows, maxB, out, kOutBf16};
+    a.ntp = ntp;
+    rc = check_prefill_shape(what, a, *p);
+    if (rc) return rc;
+    rc = check_launch(launch_masked_to_route(masked_m, E, max_m, p->block_m, maxP, maxB, sorted_ids, expert_ids, ntp, s),
+                      what);
+    if (rc) return rc;
+    bind_ws(a, g, ws);
+    return check_launch(run_gemm(a, *p, s), what);
+}
+
+// Contiguous form: row r of A belongs to expert m_indices[r] (-1, or any id outside [0,E): a padding row).  The
+// rows are sorted by expert on the device exactly as routes are (one route per row), so neither the grouping nor
+// the padding of the rows matters.  Workspace: [GEMM workspace][sorted_ids][expert_ids][num_tokens_padded]
+// [expert_offsets][counts][routing scratch].
+static size_t contiguous_layout(int m, const w4a16_weights* w, const w4a16_plan* p, size_t* off, int* maxP, int* maxB,
+                                GemmWs* g) {
+    const int E = w->shape.E;
+    route_bounds(m, 1, E, p->block_m, maxP, maxB);
+    *g = gemm_ws(w->shape, *p, *maxB);
+    off[0] = g->total;                                                          // sorted_ids
+    off[1] = off[0] + align_up(sizeof(int32_t) * (size_t)*maxP, 256);          // expert_ids
+    off[2] = off[1] + align_up(sizeof(int32_t) * (size_t)*maxB, 256);          // num_tokens_padded
+    off[3] = off[2] + 256;                                                      // expert_offsets
+    off[4] = off[3] + align_up(sizeof(int32_t) * (size_t)(E + 1), 256);        // counts
+    off[5] = off[4] + align_up(sizeof(int32_t) * (size_t)E, 256);              // routing scratch
+    return off[5] + align_up(sizeof(int32_t) * route_prep_scratch_ints(m, E), 256);
+}
+
+int w4a16_contiguous_workspace_bytes(int m, const w4a16_weights* w, const w4a16_plan* p, size_t* bytes) {
+    const char* what = "w4a16_contiguous_workspace_bytes";
+    int rc = check_handle(w, what);
+    if (rc) return rc;
+    rc = validate_plan(p, what);
+    if (rc) return rc;
+    if (!bytes || m < 0) return fail(W4A16_INVALID_ARG, "%s: bad argument", what);
+    size_t off[6];
+    int maxP, maxB;
+    GemmWs g;
+    *bytes = contiguous_layout(m, w, p, off, &maxP, &maxB, &g);
+    return ok();
+}
+
+int w4a16_grouped_gemm_contiguous(const uint16_t* A, const int32_t* m_indices, int m, const w4a16_weights* w,
+                                  const w4a16_plan* p, uint16_t* out, void* ws, size_t ws_bytes, hipStream_t s) {
+    const char* what = "w4a16_grouped_gemm_contiguous";
+    int rc = check_handle(w, what);
+    if (rc) return rc;
+    rc = validate_plan(p, what);
+    if (rc) return rc;
+    const int E = w->shape.E;
+    if (m < 0) return fail(W4A16_INVALID_ARG, "%s: m=%d", what, m);
+    if (E > W4A16_MAX_EXPERTS) return fail(W4A16_UNSUPPORTED_SHAPE, "%s: too many experts", what);
+    if (m == 0) return ok();
+    size_t off[6];
+    int maxP, maxB;
+    GemmWs g;
+    const size_t need = contiguous_layout(m, w, p, off, &maxP, &maxB, &g);
+    if (!ws || ws_bytes < need)
+        return fail(W4A16_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, needs %zu", what, ws_bytes, need);
+    if (!aligned16(ws)) return fail(W4A16_INVALID_ARG, "%s: workspace must be 16-byte aligned", what);
+    if (!A || !m_indices || !out) return fail(W4A16_INVALID_ARG, "%s: NULL pointer argument", what);
+    if (!aligned16(A)) return fail(W4A16_INVALID_ARG, "%s: A must be 16-byte aligned", what);
+    char* base = static_cast<char*>(ws);
+    int32_t* sorted_ids = reinterpret_cast<int32_t*>(base + off[0]);
+    int32_t* expert_ids = reinterpret_cast<int32_t*>(base + off[1]);
+    int32_t* ntp = reinterpret_cast<int32_t*>(base + off[2]);
+    GemmArgs a{A, 1, w->packed, w->shape, sorted_ids, expert_ids, m, maxB, out, kOutBf16};
+    a.ntp = ntp;
+    rc = check_prefill_shape(what, a, *p);
+    if (rc) return rc;
+    rc = check_launch(launch_route_prep_scratch(m_indices, m, E, p->block_m, maxP, maxB, sorted_ids, expert_ids, ntp,
+                                                reinterpret_cast<int32_t*>(base + off[3]),
+                                                reinterpret_cast<int32_t*>(base + off[4]),
+                                                reinterpret_cast<int32_t*>(base + off[5]), s),
+                      what);
+    if (rc) return rc;
+    bind_ws(a, g, ws);
+    return check_launch(run_gemm(a, *p, s), what);
+}
+
 int w4a16_silu_mul(const uint16_t* gu, int rows, int I, uint16_t* h, hipStream_t s) {
     if (rows < 0 || I < 2 || I % 2) return fail(W4A16_INVALID_ARG, "w4a16_silu_mul: rows=%d I=%d (I must be even)", rows, I);
     if (rows == 0) return ok();

@@ -392,21 +392,32 @@ __global__ __launch_bounds__(kThreads) void tile_map_kernel(const int32_t* __res
     if (tid == 0) *count = carry[1];
 }
 
-// Offsets form -> indexed form: rows [off[e], off[e+1]) of expert e become
-// slots of e's padded segment; the sentinel is rows_max.
-__global__ __launch_bounds__(kThreads) void offsets_to_route_kernel(const int32_t* __restrict__ off, int E,
-                                                                    int rows_max, int BM, int max_padded,
+// Row ranges -> indexed form: rows [start(e), start(e) + count(e)) of expert e become slots of e's padded
+// segment; the sentinel is rows_max.  Offsets form: start(e) = off[e], count(e) = off[e+1] - off[e].  Masked
+// form (off == NULL): start(e) = e * max_m, count(e) = masked_m[e] clamped to [0, max_m].
+__global__ __launch_bounds__(kThreads) void offsets_to_route_kernel(const int32_t* __restrict__ off,
+                                                                    const int32_t* __restrict__ masked_m, int max_m,
+                                                                    int E, int rows_max, int BM, int max_padded,
                                                                     int max_blocks, int32_t* __restrict__ sorted_ids,
                                                                     int32_t* __restrict__ expert_ids,
                                                                     int32_t* __restrict__ ntp) {
     extern __shared__ int smem[];
-    int* pad_off = smem;            // E+1
-    int* wave_tot = pad_off + E + 1;  // kWaves+1
+    int* pad_off = smem;                  // E+1
+    int* start = pad_off + E + 1;         // E
+    int* count = start + E;               // E
+    int* wave_tot = count + E;            // kWaves+1
     const int tid = threadIdx.x;
     int c = 0;
     if (tid < E) {
-        c = off[tid + 1] - off[tid];
+        if (off) {
+            c = off[tid + 1] - off[tid];
+            start[tid] = off[tid];
+        } else {
+            c = masked_m[tid] < max_m ? masked_m[tid] : max_m;
+            start[tid] = tid * max_m;
+        }
         if (c < 0) c = 0;
+        count[tid] = c;
     }
     const int padded = ceil_div(c, BM) * BM;
     int tot_p;
@@ -426,8 +437,8 @@ __global__ __launch_bounds__(kThreads) void offsets_to_route_kernel(const int32_
                 if (pad_off[mid] <= p) lo = mid; else hi = mid - 1;
             }
             const int r = p - pad_off[lo];
-            const int row = off[lo] + r;
-            if (r < off[lo + 1] - off[lo] && row >= 0 && row < rows_max) v = row;
+            const int row = start[lo] + r;
+            if (r < count[lo] && row >= 0 && row < rows_max) v = row;
         }
         sorted_ids[p] = v;
     }
@@ -493,9 +504,18 @@ hipError_t launch_route_prep_scratch(const int32_t* topk_ids, int R, int E, int 
 hipError_t launch_offsets_to_route(const int32_t* offsets, int E, int rows_max, int block_m, int max_padded,
                                    int max_blocks, int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntp,
                                    hipStream_t s) {
-    const size_t shmem = sizeof(int) * ((size_t)E + 1 + kWaves + 1);
-    hipLaunchKernelGGL(offsets_to_route_kernel, dim3(1), dim3(kThreads), shmem, s, offsets, E, rows_max, block_m,
-                       max_padded, max_blocks, sorted_ids, expert_ids, ntp);
+    const size_t shmem = sizeof(int) * ((size_t)E + 1 + 2 * (size_t)E + kWaves + 1);
+    hipLaunchKernelGGL(offsets_to_route_kernel, dim3(1), dim3(kThreads), shmem, s, offsets, nullptr, 0, E, rows_max,
+                       block_m, max_padded, max_blocks, sorted_ids, expert_ids, ntp);
+    return hipGetLastError();
+}
+
+hipError_t launch_masked_to_route(const int32_t* masked_m, int E, int max_m, int block_m, int max_padded,
+                                  int max_blocks, int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntp,
+                                  hipStream_t s) {
+    const size_t shmem = sizeof(int) * ((size_t)E + 1 + 2 * (size_t)E + kWaves + 1);
+    hipLaunchKernelGGL(offsets_to_route_kernel, dim3(1), dim3(kThreads), shmem, s, nullptr, masked_m, max_m, E,
+                       E * max_m, block_m, max_padded, max_blocks, sorted_ids, expert_ids, ntp);
     return hipGetLastError();
 }
 

@@ -56,6 +56,10 @@ _SIGS = {
     "w4a16_route_bounds": (_I, [_I, _I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
     "w4a16_route_prep": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     "w4a16_route_prep_workspace_bytes": (_I, [_I, _I, _I, ctypes.POINTER(_SZ)]),
+    "w4a16_contiguous_workspace_bytes": (_I, [_I, _P, _P, ctypes.POINTER(_SZ)]),
+    "w4a16_grouped_gemm_contiguous": (_I, [_P, _P, _I, _P, _P, _P, _P, _SZ, _P]),
+    "w4a16_masked_workspace_bytes": (_I, [_I, _P, _P, ctypes.POINTER(_SZ)]),
+    "w4a16_grouped_gemm_masked": (_I, [_P, _P, _I, _P, _P, _P, _P, _SZ, _P]),
     "w4a16_route_prep_ws": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "w4a16_plan_select": (_I, [_I, _I, _I, _I, _I, ctypes.c_float, ctypes.POINTER(Plan)]),
     "w4a16_gemm_workspace_bytes": (_I, [ctypes.POINTER(Plan), _I, _I, _I, ctypes.POINTER(_SZ)]),
@@ -304,6 +308,45 @@ def grouped_gemm_offsets(A_sorted: torch.Tensor, expert_offsets: torch.Tensor, w
         ws = zeroed_workspace(offsets_workspace_bytes(rows_max, w, plan), A_sorted.device)
     _check(load().w4a16_grouped_gemm_offsets(_ptr(A_sorted), _ptr(expert_offsets), rows_max, w.handle,
                                              ctypes.byref(plan), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def contiguous_workspace_bytes(m: int, w: Weights, plan: Plan) -> int:
+    out = _SZ(0)
+    _check(load().w4a16_contiguous_workspace_bytes(m, w.handle, ctypes.byref(plan), ctypes.byref(out)))
+    return out.value
+
+
+def grouped_gemm_contiguous(A: torch.Tensor, m_indices: torch.Tensor, w: Weights, plan: Plan,
+                            out: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None):
+    """Contiguous form: row r of A [m, K] belongs to expert m_indices[r] (-1: padding, row of out untouched)."""
+    m = A.shape[0]
+    if out is None:
+        out = torch.empty((m, w.N), dtype=torch.bfloat16, device=A.device)
+    if ws is None:
+        ws = zeroed_workspace(contiguous_workspace_bytes(m, w, plan), A.device)
+    _check(load().w4a16_grouped_gemm_contiguous(_ptr(A), _ptr(m_indices), m, w.handle, ctypes.byref(plan), _ptr(out),
+                                                _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def masked_workspace_bytes(max_m: int, w: Weights, plan: Plan) -> int:
+    out = _SZ(0)
+    _check(load().w4a16_masked_workspace_bytes(max_m, w.handle, ctypes.byref(plan), ctypes.byref(out)))
+    return out.value
+
+
+def grouped_gemm_masked(A: torch.Tensor, masked_m: torch.Tensor, w: Weights, plan: Plan,
+                        out: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None):
+    """Masked form: A [E, max_m, K]; rows r < masked_m[e] of expert e are computed into the flat out
+    [E*max_m, N]; the other rows of out are untouched."""
+    E, max_m, K = A.shape
+    if out is None:
+        out = torch.empty((E * max_m, w.N), dtype=torch.bfloat16, device=A.device)
+    if ws is None:
+        ws = zeroed_workspace(masked_workspace_bytes(max_m, w, plan), A.device)
+    _check(load().w4a16_grouped_gemm_masked(_ptr(A), _ptr(masked_m), max_m, w.handle, ctypes.byref(plan), _ptr(out),
+                                            _ptr(ws), ws.numel(), _stream(stream)))
     return out
 
 
