@@ -9,6 +9,9 @@ accumulation, compiled with ``-O2 -ffp-contract=off`` so no multiply-add is
 fused).  This module only marshals numpy arrays into it.  Definitions and the
 passages they follow are in the C file's header:
 
+* MXFP4 weights ``w = e2m1(c) * 2^(e - 127)`` with one E8M0 scale per 32 k --
+  b12x page ("local-inference-lab/b12x pull 479", "Summary") and humans& page
+  ("BF16 preserves each local product"), value sets of the OCP formats;
 * dequantisation ``w = (q - 8) * s`` with one BF16 scale per 32 k -- Chord page
   ("vLLM x Novita AI: Chord, Faster INT4 MoE for Kimi K2.x"), sections
   "Grouped SM90 kernels" and "H200 and Blackwell indexed decode";
@@ -72,6 +75,18 @@ def _bind(lib):
     lib.orc_combine.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P, _P]
     lib.orc_fused_moe.restype = _I
     lib.orc_fused_moe.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I]
+    lib.orc_e2m1.restype = ctypes.c_float
+    lib.orc_e2m1.argtypes = [ctypes.c_uint8]
+    lib.orc_e8m0.restype = ctypes.c_float
+    lib.orc_e8m0.argtypes = [ctypes.c_uint8]
+    lib.orc_dequant_mxfp4_one.restype = ctypes.c_float
+    lib.orc_dequant_mxfp4_one.argtypes = [ctypes.c_uint8, ctypes.c_uint8]
+    lib.orc_dequant_mxfp4.restype = None
+    lib.orc_dequant_mxfp4.argtypes = [_P, _P, _I, _I, _P, _P]
+    lib.orc_grouped_gemm_fmt.restype = None
+    lib.orc_grouped_gemm_fmt.argtypes = [_P, _I, _P, _P, _I, _I, _I, _I, _P, _I, _I, _P, _P, _P, _I, _I]
+    lib.orc_fused_moe_fmt.restype = _I
+    lib.orc_fused_moe_fmt.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _I]
     return lib
 
 
@@ -112,6 +127,26 @@ class Oracle:
     def silu(self, g: float) -> float:
         return float(self.lib.orc_silu(float(g)))
 
+    def e2m1(self, code: int) -> float:
+        return float(self.lib.orc_e2m1(int(code)))
+
+    def e8m0(self, e: int) -> float:
+        return float(self.lib.orc_e8m0(int(e)))
+
+    def dequant_mxfp4_one(self, code: int, scale_e8m0: int) -> float:
+        return float(self.lib.orc_dequant_mxfp4_one(int(code), int(scale_e8m0)))
+
+    def dequant_mxfp4(self, codes: np.ndarray, scales: np.ndarray):
+        """One MXFP4 expert: codes uint8 [N,K], E8M0 scales uint8 [N,K/32] -> (f32 [N,K], bf16 bits [N,K])."""
+        codes = _c(codes, np.uint8)
+        scales = _c(scales, np.uint8)
+        N, K = codes.shape
+        assert K % 32 == 0 and scales.shape == (N, K // 32)
+        f = np.empty((N, K), np.float32)
+        b = np.empty((N, K), np.uint16)
+        self.lib.orc_dequant_mxfp4(_ptr(codes), _ptr(scales), N, K, _ptr(f), _ptr(b))
+        return f, b
+
     # ------------------------------------------------------------ arrays
     def dequant(self, codes: np.ndarray, scales: np.ndarray):
         """One expert: codes uint8 [N,K], scales bf16 bits [N,K/32] -> (f32 [N,K], bf16 bits [N,K])."""
@@ -147,16 +182,18 @@ class Oracle:
                     num_tokens_padded=int(ntp[0]), expert_offsets=offs, counts=counts[:E])
 
     def grouped_gemm(self, A, a_row_div: int, codes, scales, topk_ids, acc64: bool = False, rows=None,
-                     nthreads: int | None = None):
+                     nthreads: int | None = None, fmt: str = "int4"):
         """out[i,:] = bf16(sum_k A[i//a_row_div,k] * w[e(i),:,k]) for every valid route i.
 
-        A bf16 bits [*,K]; codes uint8 [E,N,K]; scales bf16 bits [E,N,K/32]; topk_ids int32 (any shape,
-        flattened to R).  Returns (acc float64 [R,N], NaN where not computed; out bf16 bits [R,N], 0xFFFF
-        where not computed).  ``rows`` restricts the work to the listed route indices.
+        A bf16 bits [*,K]; codes uint8 [E,N,K]; scales [E,N,K/32]: bf16 bits (fmt "int4") or E8M0 bytes
+        (fmt "mxfp4"); topk_ids int32 (any shape, flattened to R).  Returns (acc float64 [R,N], NaN where not
+        computed; out bf16 bits [R,N], 0xFFFF where not computed).  ``rows`` restricts the work to the listed
+        route indices.
         """
         A = _c(A, np.uint16)
         codes = _c(codes, np.uint8)
-        scales = _c(scales, np.uint16)
+        fcode = {"int4": 0, "mxfp4": 1}[fmt]
+        scales = _c(scales, np.uint16 if fcode == 0 else np.uint8)
         ids = _c(topk_ids, np.int32).reshape(-1)
         E, N, K = codes.shape
         assert A.ndim == 2 and A.shape[1] == K and scales.shape == (E, N, K // 32)
@@ -164,9 +201,9 @@ class Oracle:
         acc = np.full((R, N), np.nan, np.float64)
         out = np.full((R, N), 0xFFFF, np.uint16)
         rows_arr = None if rows is None else _c(rows, np.int32)
-        self.lib.orc_grouped_gemm(_ptr(A), a_row_div, _ptr(codes), _ptr(scales), E, N, K, _ptr(ids), R,
-                                  1 if acc64 else 0, _ptr(acc), _ptr(out), _ptr(rows_arr),
-                                  0 if rows_arr is None else rows_arr.size, nthreads or default_threads())
+        self.lib.orc_grouped_gemm_fmt(_ptr(A), a_row_div, _ptr(codes), _ptr(scales), fcode, E, N, K, _ptr(ids), R,
+                                      1 if acc64 else 0, _ptr(acc), _ptr(out), _ptr(rows_arr),
+                                      0 if rows_arr is None else rows_arr.size, nthreads or default_threads())
         return acc, out
 
     def silu_mul(self, gu: np.ndarray):
@@ -190,15 +227,18 @@ class Oracle:
         self.lib.orc_combine(_ptr(y), _ptr(tw), _ptr(ids), T, k, E, H, _ptr(out), _ptr(acc))
         return (out, acc) if with_acc else out
 
-    def fused_moe(self, x, topk_ids, tw, c13, s13, c2, s2, nthreads: int | None = None):
-        """Fused expert MLP; returns (out bf16 bits [T,H], h bf16 bits [R,I], y float64 [R,H]).
+    def fused_moe(self, x, topk_ids, tw, c13, s13, c2, s2, nthreads: int | None = None, fmt: str = "int4"):
+        """Fused expert MLP; returns (out bf16 bits [T,H], h bf16 bits [R,I], y float64 [R,H]).  Scales as in
+        ``grouped_gemm`` for ``fmt``.
 
         ``self.last_out_acc`` then holds the combine's binary32 accumulators before rounding [T,H]."""
         x = _c(x, np.uint16)
         ids = _c(topk_ids, np.int32)
         tw = _c(tw, np.float32)
-        c13, s13 = _c(c13, np.uint8), _c(s13, np.uint16)
-        c2, s2 = _c(c2, np.uint8), _c(s2, np.uint16)
+        fcode = {"int4": 0, "mxfp4": 1}[fmt]
+        sdt = np.uint16 if fcode == 0 else np.uint8
+        c13, s13 = _c(c13, np.uint8), _c(s13, sdt)
+        c2, s2 = _c(c2, np.uint8), _c(s2, sdt)
         T, k = ids.shape
         E, two_i, H = c13.shape
         I = two_i // 2
@@ -208,9 +248,9 @@ class Oracle:
         out_acc = np.empty((T, H), np.float64)
         h = np.zeros((R, I), np.uint16)
         y = np.zeros((R, H), np.float64)
-        rc = self.lib.orc_fused_moe(_ptr(x), _ptr(ids), _ptr(tw), T, k, E, H, I, _ptr(c13), _ptr(s13),
-                                    _ptr(c2), _ptr(s2), _ptr(out), _ptr(out_acc), _ptr(h), _ptr(y),
-                                    nthreads or default_threads())
+        rc = self.lib.orc_fused_moe_fmt(_ptr(x), _ptr(ids), _ptr(tw), T, k, E, H, I, _ptr(c13), _ptr(s13),
+                                        _ptr(c2), _ptr(s2), fcode, _ptr(out), _ptr(out_acc), _ptr(h), _ptr(y),
+                                        nthreads or default_threads())
         assert rc == 0
         self.last_out_acc = out_acc
         return out, h, y

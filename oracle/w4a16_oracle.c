@@ -21,6 +21,15 @@
  *    (Chord page, "Two kernel families" and Figure 3: activations stay
  *    unpadded and padding lives in the index tensors as sentinels), plus
  *    per-expert offsets (nf4 page, "Usage": cumulative rows per expert).
+ *  - A second weight format, MXFP4: 4-bit E2M1 codes with one E8M0 scale per
+ *    32 consecutive k, w = e2m1(c) * 2^(e - 127).  The b12x page
+ *    ("local-inference-lab/b12x pull 479", section "Summary") runs MXFP4
+ *    routed experts with E8M0 scales; the humans& page (section "BF16
+ *    preserves each local product") dequantises E2M1 values by their block
+ *    scale into BF16, where such products are exact.  The value set of E2M1
+ *    (sign, two exponent bits with bias 1, one mantissa bit) and of E8M0 (a
+ *    bare power of two, 0xFF not a number) are those of the OCP Microscaling
+ *    formats the pages name.
  *  - The fused expert MLP (gate_up, SiLU*mul, down, weighted top-k merge) is
  *    the chain the humans& page describes for its persistent kernel
  *    ("humans& Beats FlashInfer's Best MoE Kernel by 25% on Blackwell GPUs",
@@ -98,6 +107,42 @@ float orc_dequant_one(uint8_t code, uint16_t scale_bf16) {
     return (float)(q - 8) * orc_bf16_to_f32(scale_bf16);
 }
 
+/* MXFP4: E2M1 code c (low nibble): bit 3 sign, bits 2..1 exponent (bias 1), bit 0 mantissa; exponent 0 is
+ * subnormal (0 or 0.5).  Positive values in code order: 0, 0.5, 1, 1.5, 2, 3, 4, 6.  E8M0 scale byte e: 2^(e-127),
+ * 0xFF not a number.  The product has at most 2 significant bits, so binary32 holds it exactly down to 2^-149. */
+float orc_e2m1(uint8_t code) {
+    static const float mag[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+    float v = mag[code & 7];
+    return (code & 8) ? -v : v;
+}
+
+float orc_e8m0(uint8_t e) { return e == 0xFF ? NAN : ldexpf(1.0f, (int)e - 127); }
+
+float orc_dequant_mxfp4_one(uint8_t code, uint8_t scale_e8m0) {
+    return orc_e2m1((uint8_t)(code & 0x0F)) * orc_e8m0(scale_e8m0);
+}
+
+/* One expert, MXFP4: codes [N,K], E8M0 scales [N,K/32] -> out_f32 / out_bf16 [N,K] (either may be NULL). */
+void orc_dequant_mxfp4(const uint8_t* codes, const uint8_t* scales, int N, int K, float* out_f32,
+                       uint16_t* out_bf16) {
+    int G = K / 32;
+    for (int n = 0; n < N; ++n) {
+        const uint8_t* srow = scales + (size_t)n * G;
+        for (int k = 0; k < K; ++k) {
+            float w = orc_dequant_mxfp4_one(codes[(size_t)n * K + k], srow[k / 32]);
+            if (out_f32) out_f32[(size_t)n * K + k] = w;
+            if (out_bf16) out_bf16[(size_t)n * K + k] = orc_bf16_rne(w);
+        }
+    }
+}
+
+/* A weight of either format: fmt 0 = INT4 codes with BF16 scales (uint16 array), 1 = MXFP4 with E8M0 scales
+ * (uint8 array); g indexes the scale array. */
+static float orc_weight(int fmt, const uint8_t* codes, const void* scales, size_t idx, size_t g) {
+    if (fmt == 1) return orc_dequant_mxfp4_one(codes[idx], ((const uint8_t*)scales)[g]);
+    return orc_dequant_one(codes[idx], ((const uint16_t*)scales)[g]);
+}
+
 /* One expert: codes [N,K], scales [N,K/32] -> out_f32 [N,K], out_bf16 [N,K] (either may be NULL). */
 void orc_dequant(const uint8_t* codes, const uint16_t* scales, int N, int K,
                  float* out_f32, uint16_t* out_bf16) {
@@ -173,7 +218,7 @@ int orc_route_prep(const int32_t* topk_ids, int T, int k, int E, int BM,
 
 typedef struct {
     const uint16_t* A; int a_row_div;
-    const uint8_t* codes; const uint16_t* scales;
+    const uint8_t* codes; const void* scales; int fmt;
     int E, N, K;
     const int32_t* topk_ids; int R; int acc64;
     double* out_acc; uint16_t* out;
@@ -187,20 +232,20 @@ static void gemm_row(const gemm_job* j, int i) {
     int N = j->N, K = j->K, G = K / 32;
     const uint16_t* a = j->A + (size_t)(i / j->a_row_div) * K;
     const uint8_t* cw = j->codes + (size_t)e * N * K;
-    const uint16_t* sw = j->scales + (size_t)e * N * G;
+    const size_t sw = (size_t)e * N * G;  /* first scale of expert e */
     for (int n = 0; n < N; ++n) {
         if (j->acc64) {
             double acc = 0.0;
             for (int k = 0; k < K; ++k)
                 acc += (double)orc_bf16_to_f32(a[k]) *
-                       (double)orc_dequant_one(cw[(size_t)n * K + k], sw[(size_t)n * G + k / 32]);
+                       (double)orc_weight(j->fmt, cw, j->scales, (size_t)n * K + k, sw + (size_t)n * G + k / 32);
             if (j->out_acc) j->out_acc[(size_t)i * N + n] = acc;
             if (j->out) j->out[(size_t)i * N + n] = orc_bf16_rne_f64(acc);
         } else {
             float acc = 0.0f;
             for (int k = 0; k < K; ++k) {
                 float prod = orc_bf16_to_f32(a[k]) *
-                             orc_dequant_one(cw[(size_t)n * K + k], sw[(size_t)n * G + k / 32]);
+                             orc_weight(j->fmt, cw, j->scales, (size_t)n * K + k, sw + (size_t)n * G + k / 32);
                 acc = acc + prod;
             }
             if (j->out_acc) j->out_acc[(size_t)i * N + n] = (double)acc;
@@ -223,19 +268,26 @@ static void run_threads(void* (*fn)(void*), void* jobs, size_t job_size, int nth
     free(th);
 }
 
-/* rows == NULL: all R routes; otherwise only the listed route indices. */
-void orc_grouped_gemm(const uint16_t* A, int a_row_div, const uint8_t* codes, const uint16_t* scales,
-                      int E, int N, int K, const int32_t* topk_ids, int R, int acc64,
-                      double* out_acc, uint16_t* out, const int32_t* rows, int nrows, int nthreads) {
+/* rows == NULL: all R routes; otherwise only the listed route indices.  fmt: 0 INT4 / BF16 scales, 1 MXFP4. */
+void orc_grouped_gemm_fmt(const uint16_t* A, int a_row_div, const uint8_t* codes, const void* scales, int fmt,
+                          int E, int N, int K, const int32_t* topk_ids, int R, int acc64,
+                          double* out_acc, uint16_t* out, const int32_t* rows, int nrows, int nthreads) {
     if (nthreads < 1) nthreads = 1;
     gemm_job* jobs = (gemm_job*)malloc(sizeof(gemm_job) * (size_t)nthreads);
     for (int t = 0; t < nthreads; ++t) {
-        gemm_job j = {A, a_row_div, codes, scales, E, N, K, topk_ids, R, acc64,
+        gemm_job j = {A, a_row_div, codes, scales, fmt, E, N, K, topk_ids, R, acc64,
                       out_acc, out, rows, nrows, t, nthreads};
         jobs[t] = j;
     }
     run_threads(gemm_worker, jobs, sizeof(gemm_job), nthreads);
     free(jobs);
+}
+
+void orc_grouped_gemm(const uint16_t* A, int a_row_div, const uint8_t* codes, const uint16_t* scales,
+                      int E, int N, int K, const int32_t* topk_ids, int R, int acc64,
+                      double* out_acc, uint16_t* out, const int32_t* rows, int nrows, int nthreads) {
+    orc_grouped_gemm_fmt(A, a_row_div, codes, scales, 0, E, N, K, topk_ids, R, acc64, out_acc, out, rows, nrows,
+                         nthreads);
 }
 
 /* ------------------------------------------------------------------ */
@@ -285,7 +337,7 @@ void orc_combine(const double* y, const float* tw, const int32_t* topk_ids, int 
 
 typedef struct {
     const uint16_t* x; const int32_t* topk_ids; int T, k, E, H, I;
-    const uint8_t* c13; const uint16_t* s13; const uint8_t* c2; const uint16_t* s2;
+    const uint8_t* c13; const void* s13; const uint8_t* c2; const void* s2; int fmt;
     double* gu; uint16_t* h; double* y;
     int tid, nthreads;
 } moe_job;
@@ -301,10 +353,10 @@ static void* moe_worker(void* p) {
         double* gu = j->gu + (size_t)i * 2 * I;
         for (int n = 0; n < 2 * I; ++n) {
             const uint8_t* cw = j->c13 + ((size_t)e * 2 * I + n) * H;
-            const uint16_t* sw = j->s13 + ((size_t)e * 2 * I + n) * G13;
+            const size_t sw = ((size_t)e * 2 * I + n) * G13;
             float acc = 0.0f;
             for (int kk = 0; kk < H; ++kk)
-                acc = acc + orc_bf16_to_f32(a[kk]) * orc_dequant_one(cw[kk], sw[kk / 32]);
+                acc = acc + orc_bf16_to_f32(a[kk]) * orc_weight(j->fmt, cw, j->s13, (size_t)kk, sw + kk / 32);
             gu[n] = (double)acc;
         }
         uint16_t* h = j->h + (size_t)i * I;
@@ -312,20 +364,20 @@ static void* moe_worker(void* p) {
         double* y = j->y + (size_t)i * H;
         for (int n = 0; n < H; ++n) {
             const uint8_t* cw = j->c2 + ((size_t)e * H + n) * I;
-            const uint16_t* sw = j->s2 + ((size_t)e * H + n) * G2;
+            const size_t sw = ((size_t)e * H + n) * G2;
             float acc = 0.0f;
             for (int kk = 0; kk < I; ++kk)
-                acc = acc + orc_bf16_to_f32(h[kk]) * orc_dequant_one(cw[kk], sw[kk / 32]);
+                acc = acc + orc_bf16_to_f32(h[kk]) * orc_weight(j->fmt, cw, j->s2, (size_t)kk, sw + kk / 32);
             y[n] = (double)acc;
         }
     }
     return NULL;
 }
 
-int orc_fused_moe(const uint16_t* x, const int32_t* topk_ids, const float* tw, int T, int k,
-                  int E, int H, int I,
-                  const uint8_t* c13, const uint16_t* s13, const uint8_t* c2, const uint16_t* s2,
-                  uint16_t* out, double* out_acc, uint16_t* h_out, double* y_out, int nthreads) {
+int orc_fused_moe_fmt(const uint16_t* x, const int32_t* topk_ids, const float* tw, int T, int k,
+                      int E, int H, int I,
+                      const uint8_t* c13, const void* s13, const uint8_t* c2, const void* s2, int fmt,
+                      uint16_t* out, double* out_acc, uint16_t* h_out, double* y_out, int nthreads) {
     size_t R = (size_t)T * k;
     double* gu = (double*)malloc(sizeof(double) * (R ? R : 1) * 2 * (size_t)I);
     uint16_t* h = h_out ? h_out : (uint16_t*)malloc(sizeof(uint16_t) * (R ? R : 1) * (size_t)I);
@@ -334,7 +386,7 @@ int orc_fused_moe(const uint16_t* x, const int32_t* topk_ids, const float* tw, i
     if (nthreads < 1) nthreads = 1;
     moe_job* jobs = (moe_job*)malloc(sizeof(moe_job) * (size_t)nthreads);
     for (int t = 0; t < nthreads; ++t) {
-        moe_job j = {x, topk_ids, T, k, E, H, I, c13, s13, c2, s2, gu, h, y, t, nthreads};
+        moe_job j = {x, topk_ids, T, k, E, H, I, c13, s13, c2, s2, fmt, gu, h, y, t, nthreads};
         jobs[t] = j;
     }
     run_threads(moe_worker, jobs, sizeof(moe_job), nthreads);
@@ -344,4 +396,12 @@ int orc_fused_moe(const uint16_t* x, const int32_t* topk_ids, const float* tw, i
     if (!h_out) free(h);
     if (!y_out) free(y);
     return 0;
+}
+
+int orc_fused_moe(const uint16_t* x, const int32_t* topk_ids, const float* tw, int T, int k,
+                  int E, int H, int I,
+                  const uint8_t* c13, const uint16_t* s13, const uint8_t* c2, const uint16_t* s2,
+                  uint16_t* out, double* out_acc, uint16_t* h_out, double* y_out, int nthreads) {
+    return orc_fused_moe_fmt(x, topk_ids, tw, T, k, E, H, I, c13, s13, c2, s2, 0, out, out_acc, h_out, y_out,
+                             nthreads);
 }

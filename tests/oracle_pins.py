@@ -11,7 +11,8 @@ Sources of truth used here:
 * exact rational arithmetic (``exact_rational.py``) on tiny inputs;
 * closed forms (constant codes, one-hot activations, SiLU identities);
 * an integer-exact regime where every binary32 partial sum is exact;
-* library routines: torch's BF16 cast, numpy's matmul and bincount;
+* library routines: torch's BF16 cast, its float8 (E4M3, E8M0) decoders for the MXFP4 value sets, numpy's
+  matmul and bincount;
 * invariants (token permutation, power-of-two scaling, empty experts) and the
   properties that fully determine the routing tensors.
 """
@@ -425,6 +426,140 @@ def pin_fused_composition(o):
     del e
 
 
+# ------------------------------------------------------------------ MXFP4
+
+def e2m1_via_e4m3():
+    """The 16 E2M1 values, each re-encoded bit-wise as the E4M3 value it equals and decoded by torch's float8
+    cast (a library routine).  E2M1: bit 3 sign, bits 2..1 exponent with bias 1 (0: subnormal, value m/2),
+    bit 0 mantissa; E4M3 has bias 7 and three mantissa bits, so a normal E2M1 (e, m) is E4M3 (e + 6, 4m) and
+    the subnormal 0.5 is 2^-1 = E4M3 exponent 6."""
+    import torch
+
+    codes = []
+    for c in range(16):
+        sgn, ex, m = c >> 3, (c >> 1) & 3, c & 1
+        if ex == 0:
+            mag = 0x30 if m else 0x00
+        else:
+            mag = ((ex + 6) << 3) | (m << 2)
+        codes.append((sgn << 7) | mag)
+    t = torch.tensor(codes, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float32)
+    return t.numpy().astype(np.float64)
+
+
+def e8m0_via_torch():
+    import torch
+
+    return torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e8m0fnu).to(torch.float32).numpy()
+
+
+def mxfp4_exact(table, c, e):
+    return Fraction(float(table[c & 15])) * Fraction(2) ** (int(e) - 127)
+
+
+def pin_mxfp4_values(o):
+    table = e2m1_via_e4m3()
+    for c in range(16):
+        got = o.e2m1(c)
+        assert got == table[c] and math.copysign(1.0, got) == math.copysign(1.0, table[c]), ("e2m1", c, got)
+    scale = e8m0_via_torch()
+    for e in range(255):
+        assert o.e8m0(e) == float(scale[e]), ("e8m0", e)
+    assert math.isnan(o.e8m0(255)) and math.isnan(float(scale[255]))
+    # every code at every scale from 2^-127 to 2^125 (above, 6 * 2^126 leaves binary32): the weight is the exact
+    # product
+    for e in range(0, 253):
+        for c in range(16):
+            assert Fraction(o.dequant_mxfp4_one(c | 0xA0, e)) == mxfp4_exact(table, c, e), ("product", c, e)
+
+
+def pin_mxfp4_dequant_groups(o):
+    # group g covers k in [32g, 32g+32) of its row; the BF16 image is the same value (at most 2 significant bits)
+    table = e2m1_via_e4m3()
+    r = _rng(61)
+    N, K = 5, 160
+    codes = r.integers(0, 256, (N, K), dtype=np.uint8)          # upper nibble must be ignored
+    scales = r.integers(100, 150, (N, K // 32), dtype=np.uint8)
+    f, b = o.dequant_mxfp4(codes, scales)
+    for n in range(N):
+        for k in range(K):
+            want = mxfp4_exact(table, codes[n, k], scales[n, k // 32])
+            assert Fraction(float(f[n, k])) == want, ("f32", n, k)
+            assert Fraction(float(_bits_f32(np.array([b[n, k]], np.uint16))[0])) == want, ("bf16", n, k)
+
+
+def _mx_draw(seed, T, E, k, N, K):
+    r = _rng(seed)
+    A = _bf16_of(r.standard_normal((T, K))).reshape(T, K)
+    codes = r.integers(0, 16, (E, N, K), dtype=np.uint8)
+    scales = r.integers(118, 130, (E, N, K // 32), dtype=np.uint8)
+    ids = np.argsort(r.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    return A, codes, scales, ids
+
+
+def pin_mxfp4_gemm_exact_rational(o):
+    table = e2m1_via_e4m3()
+    u = 2.0 ** -24
+    for seed, (T, E, k, N, K) in enumerate([(2, 3, 2, 6, 32), (3, 2, 2, 4, 96)]):
+        A, codes, scales, ids = _mx_draw(300 + seed, T, E, k, N, K)
+        acc32, out = o.grouped_gemm(A, k, codes, scales, ids, fmt="mxfp4", nthreads=2)
+        acc64, _ = o.grouped_gemm(A, k, codes, scales, ids, acc64=True, fmt="mxfp4", nthreads=2)
+        gamma = K * u / (1 - K * u)
+        for i in range(T * k):
+            e = int(ids.reshape(-1)[i])
+            for n in range(N):
+                terms = [X.bf16_bits_to_fraction(A[i // k][kk]) * mxfp4_exact(table, codes[e, n, kk],
+                                                                              scales[e, n, kk // 32])
+                         for kk in range(K)]
+                exact = sum(terms, Fraction(0))
+                if X.binary_span_bits(terms) <= 53:
+                    assert Fraction(acc64[i, n]) == exact, ("fp64 accumulation not exact", i, n)
+                bound = gamma * float(sum(abs(t) for t in terms))
+                assert abs(Fraction(acc32[i, n]) - exact) <= Fraction(bound), ("fp32 error bound", i, n)
+                lo, hi = X.round_bf16(exact - Fraction(bound)), X.round_bf16(exact + Fraction(bound))
+                if lo == hi:
+                    assert out[i, n] == X.fraction_to_bf16_bits(X.round_bf16(exact)), ("bf16 output", i, n)
+
+
+def pin_mxfp4_gemm_library_matmul(o):
+    # one expert, every route valid: x @ W^T with W from the library-decoded value tables (numpy, binary64)
+    table = e2m1_via_e4m3()
+    scale = e8m0_via_torch().astype(np.float64)
+    r = _rng(62)
+    T, N, K = 5, 20, 192
+    A = _bf16_of(r.standard_normal((T, K))).reshape(T, K)
+    codes = r.integers(0, 16, (1, N, K), dtype=np.uint8)
+    scales = r.integers(110, 140, (1, N, K // 32), dtype=np.uint8)
+    W = table[codes[0]] * np.repeat(scale[scales[0]], 32, axis=1)
+    ref = _bits_f32(A).astype(np.float64) @ W.T
+    acc64, _ = o.grouped_gemm(A, 1, codes, scales, np.zeros((T, 1), np.int32), acc64=True, fmt="mxfp4")
+    assert np.allclose(acc64, ref, rtol=1e-12, atol=1e-30), "fp64 accumulation vs numpy matmul"
+
+
+def pin_mxfp4_fused_composition(o):
+    r = _rng(63)
+    T, E, k, H, I = 4, 3, 2, 64, 32
+    x = _bf16_of(r.standard_normal((T, H))).reshape(T, H)
+    c13 = r.integers(0, 16, (E, 2 * I, H), dtype=np.uint8)
+    s13 = r.integers(120, 128, (E, 2 * I, H // 32), dtype=np.uint8)
+    c2 = r.integers(0, 16, (E, H, I), dtype=np.uint8)
+    s2 = r.integers(120, 128, (E, H, I // 32), dtype=np.uint8)
+    ids = np.argsort(r.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    ids[3, 0] = -1
+    tw = r.uniform(0.1, 1.0, (T, k)).astype(np.float32)
+    out, h, y = o.fused_moe(x, ids, tw, c13, s13, c2, s2, nthreads=2, fmt="mxfp4")
+    gu, _ = o.grouped_gemm(x, k, c13, s13, ids, nthreads=2, fmt="mxfp4")
+    valid = (ids.reshape(-1) >= 0) & (ids.reshape(-1) < E)
+    h_ref = o.silu_mul(np.nan_to_num(gu, nan=0.0))
+    assert np.array_equal(h[valid], h_ref[valid]), "h"
+    y_ref, _ = o.grouped_gemm(h_ref, 1, c2, s2, ids, nthreads=2, fmt="mxfp4")
+    assert np.array_equal(y[valid], y_ref[valid]), "y"
+    out_ref, _ = o.combine(np.nan_to_num(y_ref, nan=0.0), tw, ids, E, with_acc=True)
+    assert np.array_equal(out, out_ref), "combine"
+
+
 ALL_PINS = [pin_dequant_table, pin_dequant_groups, pin_bf16_rounding, pin_gemm_hand_cases,
             pin_gemm_exact_rational, pin_gemm_integer_exact, pin_gemm_library_matmul, pin_gemm_invariants,
-            pin_route_prep, pin_silu, pin_combine, pin_fused_composition]
+            pin_route_prep, pin_silu, pin_combine, pin_fused_composition, pin_mxfp4_values,
+            pin_mxfp4_dequant_groups, pin_mxfp4_gemm_exact_rational, pin_mxfp4_gemm_library_matmul,
+            pin_mxfp4_fused_composition]

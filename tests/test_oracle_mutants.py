@@ -19,15 +19,15 @@ MUTANTS = {
     "zero point 7": ("(float)(q - 8)", "(float)(q - 7)"),
     "nibble mask drops a bit": ("int q = (int)(code & 0x0F);", "int q = (int)(code & 0x07);"),
     "group of 16 in dequant": ("scales[(size_t)n * G + k / 32]", "scales[(size_t)n * G + k / 16 % G]"),
-    "group of 64 in gemm": ("sw[(size_t)n * G + k / 32]);\n                acc = acc + prod;",
-                            "sw[(size_t)n * G + k / 64]);\n                acc = acc + prod;"),
+    "group of 64 in gemm": ("sw + (size_t)n * G + k / 32);\n                acc = acc + prod;",
+                            "sw + (size_t)n * G + k / 64);\n                acc = acc + prod;"),
     "ties away from zero": ("(lower == 0x8000u && (upper & 1u))", "(lower == 0x8000u)"),
     "truncating bf16": ("if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) upper += 1u;", ""),
     "dropped last k": ("for (int k = 0; k < K; ++k) {\n                float prod",
                        "for (int k = 0; k < K - 1; ++k) {\n                float prod"),
     "wrong A row": ("j->A + (size_t)(i / j->a_row_div) * K", "j->A + (size_t)(i % j->a_row_div) * K"),
-    "transposed weight index": ("float prod = orc_bf16_to_f32(a[k]) *\n                             orc_dequant_one(cw[(size_t)n * K + k]",
-                                "float prod = orc_bf16_to_f32(a[k]) *\n                             orc_dequant_one(cw[(size_t)(k % N) * K + (n % K)]"),
+    "transposed weight index": ("float prod = orc_bf16_to_f32(a[k]) *\n                             orc_weight(j->fmt, cw, j->scales, (size_t)n * K + k,",
+                                "float prod = orc_bf16_to_f32(a[k]) *\n                             orc_weight(j->fmt, cw, j->scales, (size_t)(k % N) * K + (n % K),"),
     "sentinel R-1": ("for (int p = 0; p < maxP; ++p) sorted_ids[p] = R;", "for (int p = 0; p < maxP; ++p) sorted_ids[p] = R - 1;"),
     "no per-expert padding": ("int padded = (cnt[e] + BM - 1) / BM * BM;", "int padded = cnt[e];"),
     "non-local id kept": ("if (e >= 0 && e < E) cnt[e] += 1;", "if (e >= 0 && e <= E) cnt[e < E ? e : 0] += 1;"),
@@ -36,8 +36,13 @@ MUTANTS = {
     "combine keeps non-local": ("                if (e < 0 || e >= E) continue;\n                acc = acc + tw",
                                 "                acc = acc + tw"),
     "combine weight index": ("acc = acc + tw[(size_t)t * k + j] *", "acc = acc + tw[(size_t)t * k] *"),
-    "down uses unrounded h": ("acc = acc + orc_bf16_to_f32(h[kk]) * orc_dequant_one(cw[kk], sw[kk / 32]);",
-                              "acc = acc + (float)(orc_silu(gu[kk]) * gu[I + kk]) * orc_dequant_one(cw[kk], sw[kk / 32]);"),
+    "down uses unrounded h": ("acc = acc + orc_bf16_to_f32(h[kk]) * orc_weight(j->fmt, cw, j->s2, (size_t)kk, sw + kk / 32);",
+                              "acc = acc + (float)(orc_silu(gu[kk]) * gu[I + kk]) * orc_weight(j->fmt, cw, j->s2, (size_t)kk, sw + kk / 32);"),
+    "e2m1 3 and 4 swapped": ("{0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f}", "{0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 4.0f, 3.0f, 6.0f}"),
+    "e2m1 sign ignored": ("return (code & 8) ? -v : v;", "return v;"),
+    "e8m0 bias 128": ("ldexpf(1.0f, (int)e - 127)", "ldexpf(1.0f, (int)e - 128)"),
+    "mxfp4 scale of the next group": ("srow[k / 32]", "srow[(k / 32 + 1) % G]"),
+    "mxfp4 scales read as bf16": ("if (fmt == 1) return orc_dequant_mxfp4_one", "if (fmt == 2) return orc_dequant_mxfp4_one"),
 }
 
 RUNNER = textwrap.dedent("""
