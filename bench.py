@@ -84,6 +84,12 @@ def workload_spec(name: str) -> dict:
     for T in (1, 32, 512, 4096):
         table["deepseek-moe-t%d" % T] = deepseek(T)
     table["kimi-prefill-t8192"] = kimi_prefill(8192)
+    # the same layers with MXFP4 weights (E2M1 codes, E8M0 scales per 32 k)
+    for key in list(table):
+        mx = dict(table[key])
+        mx["fmt"] = "mxfp4"
+        mx["desc"] = mx["desc"] + "; MXFP4 weights"
+        table[key + "-mxfp4"] = mx
     if name not in table:
         raise SystemExit("unknown workload %s; choose from %s" % (name, ", ".join(sorted(table))))
     spec = table[name]
@@ -91,9 +97,10 @@ def workload_spec(name: str) -> dict:
     return spec
 
 
-def packed_weight_bytes(N: int, K: int) -> int:
-    # 16-row x 256-k superblocks of 2304 bytes: 4.5 bits per weight when N % 16 == 0 and K % 256 == 0
-    return ((N + 15) // 16) * ((K + 255) // 256) * 2304
+def packed_weight_bytes(N: int, K: int, fmt: str = "int4") -> int:
+    # 16-row x 256-k superblocks: 2304 bytes with BF16 scales (4.5 bits per weight), 2176 with E8M0 scales
+    # (4.25 bits per weight), when N % 16 == 0 and K % 256 == 0
+    return ((N + 15) // 16) * ((K + 255) // 256) * (2176 if fmt == "mxfp4" else 2304)
 
 
 def gate_up_algorithmic_bytes(spec, block_m: int = 16) -> int:
@@ -106,7 +113,7 @@ def gate_up_algorithmic_bytes(spec, block_m: int = 16) -> int:
     valid = (flat >= 0) & (flat < E)
     active = len(np.unique(flat[valid]))
     maxP, maxB = L.route_bounds(T, k, E, block_m)
-    return active * packed_weight_bytes(2 * I, H) + T * H * 2 + int(valid.sum()) * I * 2 + (maxP + maxB) * 4
+    return active * packed_weight_bytes(2 * I, H, spec.get("fmt", "int4")) + T * H * 2 + int(valid.sum()) * I * 2 + (maxP + maxB) * 4
 
 
 # the sources the gate_up kernel of each family is built from
@@ -150,20 +157,26 @@ def committed_traffic(workload: str, family: str):
 
 
 def make_inputs(spec, dev=None):
-    """x, ids, topk weights and the two weight sets: numpy arrays (codes uint8, scales BF16 bits), or, for
-    weight sets of gigabytes, torch tensors drawn on the GPU (codes uint8, scales bfloat16)."""
+    """x, ids, topk weights and the two weight sets: numpy arrays (codes uint8, scales BF16 bits or E8M0
+    bytes), or, for weight sets of gigabytes, torch tensors drawn on the GPU (codes uint8, scales bfloat16 or
+    uint8)."""
     import synth
 
     E, k, H, I, T = spec["E"], spec["k"], spec["H"], spec["I"], spec["T"]
+    mx = spec.get("fmt") == "mxfp4"
     rng = synth.rng_for(spec["cfg"], 7)
     x = synth.activations(rng, T, H)
     if spec.get("device_weights"):
         base = 1000 * spec["cfg"]
-        c13, s13 = synth.codes_device(base + 1, E, 2 * I, H, dev), synth.scales_device(base + 2, E, 2 * I, H, dev)
-        c2, s2 = synth.codes_device(base + 3, E, H, I, dev), synth.scales_device(base + 4, E, H, I, dev)
+        sdev = synth.mxfp4_scales_device if mx else synth.scales_device
+        c13, s13 = synth.codes_device(base + 1, E, 2 * I, H, dev), sdev(base + 2, E, 2 * I, H, dev)
+        c2, s2 = synth.codes_device(base + 3, E, H, I, dev), sdev(base + 4, E, H, I, dev)
     else:
         c13, s13 = synth.expert_weights(spec["cfg"], E, 2 * I, H, salt=1)
         c2, s2 = synth.expert_weights(spec["cfg"], E, H, I, salt=2)
+        if mx:
+            s13 = synth.mxfp4_scales(synth.rng_for(spec["cfg"], 201), E, 2 * I, H)
+            s2 = synth.mxfp4_scales(synth.rng_for(spec["cfg"], 202), E, H, I)
     ids = spec["routes"]()
     if "router_weights" in spec:
         tw = spec["router_weights"]()
@@ -211,7 +224,8 @@ def cpu_baseline(spec, inputs, weight_bytes_step, budget_s=10.0):
         x, tw = x[:Tmax], tw[:Tmax]
     # whole steps when one fits the budget, else the first Ts tokens, extrapolated linearly in tokens
     t0 = time.perf_counter()
-    o.fused_moe(x[:1], ids[:1], tw[:1], c13, s13, c2, s2, nthreads=threads)
+    fmt = spec.get("fmt", "int4")
+    o.fused_moe(x[:1], ids[:1], tw[:1], c13, s13, c2, s2, nthreads=threads, fmt=fmt)
     one_tok = max(time.perf_counter() - t0, 1e-3)
     Ts = T if one_tok * T <= 3 * budget_s else max(1, int(budget_s / one_tok))
     Ts = min(Ts, ids.shape[0])
@@ -219,7 +233,7 @@ def cpu_baseline(spec, inputs, weight_bytes_step, budget_s=10.0):
     start = time.perf_counter()
     while True:
         t0 = time.perf_counter()
-        o.fused_moe(x[:Ts], ids[:Ts], tw[:Ts], c13, s13, c2, s2, nthreads=threads)
+        o.fused_moe(x[:Ts], ids[:Ts], tw[:Ts], c13, s13, c2, s2, nthreads=threads, fmt=fmt)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - start >= budget_s or len(times) >= 5:
             break
@@ -267,7 +281,8 @@ def main():
     valid = (flat >= 0) & (flat < E)
     active = np.unique(flat[valid])
     Rv = int(valid.sum())
-    wb13, wb2 = packed_weight_bytes(2 * I, H), packed_weight_bytes(H, I)
+    fmt = spec.get("fmt", "int4")
+    wb13, wb2 = packed_weight_bytes(2 * I, H, fmt), packed_weight_bytes(H, I, fmt)
     weight_bytes_step = len(active) * (wb13 + wb2)
 
     def u16(a):
@@ -277,10 +292,13 @@ def main():
         return c if isinstance(c, torch.Tensor) else torch.from_numpy(c).to(dev)
 
     def scales_dev(sc):
+        if fmt == "mxfp4":
+            return codes_dev(sc)
         return sc.view(torch.int16) if isinstance(sc, torch.Tensor) else u16(sc)
 
-    w13 = w4.pack_weights(codes_dev(c13), scales_dev(s13))
-    w2 = w4.pack_weights(codes_dev(c2), scales_dev(s2))
+    pack = w4.pack_weights_mxfp4 if fmt == "mxfp4" else w4.pack_weights
+    w13 = pack(codes_dev(c13), scales_dev(s13))
+    w2 = pack(codes_dev(c2), scales_dev(s2))
     per_copy = w13.packed.numel() + w2.packed.numel()
     ncopies = max(2, math.ceil(ROTATION_BYTES / per_copy) + 1)
     copies = [(w13, w2)]
@@ -407,12 +425,12 @@ def main():
         achieved = alg_bytes / (gate_up_us * 1e-6) / 1e9
     traffic = committed_traffic(spec["name"], "prefill" if prefill else "decode")
     if p13.kernel == L.KERNEL_DECODE and p13.block_m == 16:
-        kname = "gemm_decode_reg_kernel<NBW=%d,D=2,act out> (gate_up + silu_mul, k_split %d)" % (p13.n_blocks,
-                                                                                               p13.k_split)
+        kname = "gemm_decode_reg_kernel<NBW=%d,D=2,act out,%s> (gate_up + silu_mul, k_split %d)" % (
+            p13.n_blocks, fmt, p13.k_split)
     else:
-        kname = "gemm_%s_kernel<MT=%d,NBW=%d,act out> (gate_up + silu_mul, route blocks of %d rows, k_split %d)" % (
-            "decode" if p13.kernel == L.KERNEL_DECODE else "prefill", (p13.tile_m or p13.block_m) // 16,
-            p13.n_blocks, p13.block_m, p13.k_split)
+        kname = "gemm_%s_kernel<MT=%d,NBW=%d,act out,%s> (gate_up + silu_mul, route blocks of %d rows, " \
+                "k_split %d)" % ("decode" if p13.kernel == L.KERNEL_DECODE else "prefill",
+                                 (p13.tile_m or p13.block_m) // 16, p13.n_blocks, fmt, p13.block_m, p13.k_split)
 
     stages = list(L.FUSED_STAGES)
     print("[bench] step %.1f us wall (graph replay), %.1f us GPU events; per stage (us): %s" % (
@@ -425,7 +443,8 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": spec["name"], "description": spec["desc"], "experts": E, "top_k": k,
-                   "tokens": T, "hidden": H, "intermediate": I, "active_experts": int(len(active)),
+                   "tokens": T, "hidden": H, "intermediate": I, "weight_format": fmt,
+                   "active_experts": int(len(active)),
                    "local_routes": Rv, "weight_bytes_per_step": int(weight_bytes_step),
                    "weight_rotation_copies": ncopies, "parallelism": "none (one GPU)"},
         "stages_us": {n: round(float(v), 2) for n, v in zip(stages, stage.mean(0))},

@@ -57,6 +57,9 @@ enum {
 
 enum { W4A16_KERNEL_DECODE = 1, W4A16_KERNEL_PREFILL = 2 };
 
+/* Weight formats of a packed weight set. */
+enum { W4A16_FORMAT_INT4 = 0, W4A16_FORMAT_MXFP4 = 1 };
+
 /* Largest expert count the routing kernel accepts. */
 #define W4A16_MAX_EXPERTS 1024
 
@@ -105,6 +108,27 @@ int w4a16_packed_bytes(int E, int N, int K, size_t* bytes);
 int w4a16_pack_weights(const uint8_t* codes, const uint16_t* scales, int E, int N, int K,
                        void* packed, size_t packed_bytes, hipStream_t s, w4a16_weights** out);
 
+/* MXFP4 weight sets: w = e2m1(c) * 2^(e - 127), with c the E2M1 code in the
+ * low nibble of codes[e,n,k] (bit 3 sign, bits 2..1 exponent with bias 1,
+ * bit 0 mantissa: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) and e the E8M0
+ * byte scales[e,n,k/32] (b12x page, "Summary": MXFP4 experts with E8M0
+ * scales; humans& page, "BF16 preserves each local product": E2M1 values
+ * times their block scale are exact in BF16).  Same kernels, plans and
+ * calls as INT4 weights, except decode plans need block_m 16.  Scale bytes
+ * 1..252 are supported (0 puts products below the normal range, 255 is not
+ * a number, 253 and 254 overflow binary32 for the largest magnitudes).
+ *   codes   device, uint8 [E,N,K] (upper nibble ignored)
+ *   scales  device, uint8 [E,N,K/32] (E8M0)
+ *   packed  device, >= w4a16_packed_bytes_mxfp4(E,N,K) bytes
+ * Errors: as w4a16_pack_weights. */
+int w4a16_packed_bytes_mxfp4(int E, int N, int K, size_t* bytes);
+int w4a16_pack_weights_mxfp4(const uint8_t* codes, const uint8_t* scales, int E, int N, int K,
+                             void* packed, size_t packed_bytes, hipStream_t s, w4a16_weights** out);
+
+/* Format of a handle: W4A16_FORMAT_INT4 or W4A16_FORMAT_MXFP4 (negative: an
+ * error code). */
+int w4a16_weights_format(const w4a16_weights* w);
+
 /* A second handle for another device buffer that holds a byte-identical copy
  * of w's packed image (for example a copy made with hipMemcpy).  Nothing is
  * launched. */
@@ -116,7 +140,8 @@ int w4a16_weights_info(const w4a16_weights* w, int* E, int* N, int* K, void** pa
 void w4a16_weights_destroy(w4a16_weights* w);
 
 /* Dequantise one expert from the packed buffer (verification path).
- *   out_f32  device float [N,K] or NULL: (q - 8) * s, exact in binary32.
+ *   out_f32  device float [N,K] or NULL: (q - 8) * s (MXFP4: e2m1(c) *
+ *            2^(e-127)), exact in binary32.
  *   out_bf16 device BF16 bits [N,K] or NULL: that value rounded to nearest
  *            even, the operand the tensor-core path multiplies.
  * Errors: INVALID_ARG (expert out of range, both outputs NULL), HIP_ERROR. */

@@ -48,6 +48,11 @@ def scales(rng: np.random.Generator, E: int, N: int, K: int, lo: float = 0.005, 
     return to_bf16_bits(rng.uniform(lo, hi, size=(E, N, K // 32)).astype(np.float32))
 
 
+def mxfp4_scales(rng: np.random.Generator, E: int, N: int, K: int, lo: int = 118, hi: int = 126) -> np.ndarray:
+    """E8M0 scale bytes uniform in [lo, hi] (2^-9 .. 2^-1 by default): uint8 [E,N,K/32]."""
+    return rng.integers(lo, hi + 1, (E, N, K // 32), dtype=np.uint8)
+
+
 def uniform_topk(rng: np.random.Generator, T: int, E: int, k: int) -> np.ndarray:
     """Distinct experts per token, uniform without replacement: int32 [T, k]."""
     if T == 0:
@@ -175,6 +180,15 @@ def codes_device(seed: int, E: int, N: int, K: int, device):
     g = torch.Generator(device=device)
     g.manual_seed(seed)
     return torch.randint(0, 16, (E, N, K), dtype=torch.uint8, device=device, generator=g)
+
+
+def mxfp4_scales_device(seed: int, E: int, N: int, K: int, device, lo: int = 118, hi: int = 126):
+    """Seeded E8M0 scale bytes uniform in [lo, hi] generated on the GPU: uint8 [E,N,K/32]."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randint(lo, hi + 1, (E, N, K // 32), dtype=torch.uint8, device=device, generator=g)
 
 
 def scales_device(seed: int, E: int, N: int, K: int, device, lo: float = 0.005, hi: float = 0.02):

@@ -206,3 +206,66 @@ def test_deepseek_fused(orc, deepseek_weights, T):
     worst = max(np.abs(g[i] - ref[i]).max() / np.abs(ref[i]).max() for i in range(len(sample)))
     _say("  deepseek T%d fused worst ratio %.2e over %d tokens" % (T, worst, len(sample)))
     assert worst <= FUSED_TOL
+
+
+# ------------------------------------------------------------------ MXFP4 weights at the benchmark's sizes
+
+def _fused_sampled(orc, label, x, ids, tw, w13, w2, host_weights, sample, fmt):
+    got = bits(w4.fused_moe(u16(x), i32(ids), f32(tw), w13, w2))
+    c13, s13, c2, s2 = host_weights
+    orc.fused_moe(x[sample], ids[sample], tw[sample], c13, s13, c2, s2, fmt=fmt)
+    ref = orc.last_out_acc
+    g = (got[sample].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    worst = max(np.abs(g[i] - ref[i]).max() / np.abs(ref[i]).max() for i in range(len(sample)))
+    _say("  %s worst ratio %.2e over %d tokens" % (label, worst, len(sample)))
+    assert worst <= FUSED_TOL
+
+
+def test_qwen3_fused_bench_workload_mxfp4(orc, qwen3_weights):
+    """The Qwen3-30B-A3B-shaped 64-token step with MXFP4 weights (E2M1 codes, E8M0 scales per 32 k), drawn as
+    the benchmark draws them."""
+    c13, _, c2, _ = qwen3_weights
+    T, k, E = 64, 8, 128
+    s13 = synth.mxfp4_scales(synth.rng_for(2, 201), E, 1536, 2048)
+    s2 = synth.mxfp4_scales(synth.rng_for(2, 202), E, 2048, 768)
+    ids = synth.qwen3_routes(T)
+    rng = synth.rng_for(2, 7)
+    x = synth.activations(rng, T, 2048)
+    tw = rng.uniform(0.1, 1.0, (T, k)).astype(np.float32)
+    tw /= tw.sum(axis=1, keepdims=True)
+    w13 = w4.pack_weights_mxfp4(torch.from_numpy(c13).cuda(), torch.from_numpy(s13).cuda())
+    w2 = w4.pack_weights_mxfp4(torch.from_numpy(c2).cuda(), torch.from_numpy(s2).cuda())
+    _say("qwen3 mxfp4 fused plans %r" % (w4.fused_moe_plans(T, k, w13, w2),))
+    _fused_sampled(orc, "qwen3 T64 mxfp4 fused", x, ids, tw, w13, w2, (c13, s13, c2, s2), np.arange(0, T, 7),
+                   "mxfp4")
+
+
+def test_deepseek_fused_mxfp4_t4096(orc):
+    """DeepSeek-V3-shaped 4096-token fused step with MXFP4 weights generated on the device (prefill plans with
+    tile lists), on sampled tokens; the oracle gets the experts those tokens use."""
+    dev = torch.device("cuda:0")
+    E, H, I, T = 256, 7168, 2048, 4096
+    c13 = synth.codes_device(5101, E, 2 * I, H, dev)
+    s13 = synth.mxfp4_scales_device(5102, E, 2 * I, H, dev)
+    c2 = synth.codes_device(5103, E, H, I, dev)
+    s2 = synth.mxfp4_scales_device(5104, E, H, I, dev)
+    w13 = w4.pack_weights_mxfp4(c13, s13)
+    w2 = w4.pack_weights_mxfp4(c2, s2)
+    ids, tw = synth.deepseek_router(T)
+    x = synth.activations(synth.rng_for(5, 7 + T), T, H)
+    _say("deepseek T%d mxfp4 fused plans %r" % (T, w4.fused_moe_plans(T, 8, w13, w2)))
+    sample = np.unique(np.linspace(0, T - 1, 5).astype(int))
+    used = np.unique(ids[sample])
+    remap = np.full(E, -1, np.int32)
+    remap[used] = np.arange(used.size, dtype=np.int32)
+    ue = torch.from_numpy(used).cuda().long()
+    host = tuple(t[ue].cpu().numpy() for t in (c13, s13, c2, s2))
+    got = bits(w4.fused_moe(u16(x), i32(ids), f32(tw), w13, w2))
+    orc.fused_moe(x[sample], remap[ids[sample]], tw[sample], *host, fmt="mxfp4")
+    ref = orc.last_out_acc
+    g = (got[sample].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    worst = max(np.abs(g[i] - ref[i]).max() / np.abs(ref[i]).max() for i in range(len(sample)))
+    _say("  deepseek T%d mxfp4 fused worst ratio %.2e over %d tokens" % (T, worst, len(sample)))
+    assert worst <= FUSED_TOL
+    del w13, w2, c13, s13, c2, s2
+    torch.cuda.empty_cache()

@@ -350,6 +350,137 @@ def test_gemm_masked_form(orc, plan_args):
     check_gemm(bits(out), acc, expert_of_row, E, label="masked")
 
 
+# ------------------------------------------------------------------ MXFP4 weights
+
+def _pack_mx(codes, scales):
+    return w4.pack_weights_mxfp4(u8(codes), u8(scales))
+
+
+@pytest.mark.parametrize("E,N,K", [(3, 64, 256), (2, 40, 96), (1, 17, 288)])
+def test_mxfp4_dequant_bit_exact(orc, E, N, K):
+    _say("mxfp4 dequant E=%d N=%d K=%d" % (E, N, K))
+    rng = np.random.default_rng(2000 + N + K)
+    codes = synth.codes(rng, E, N, K) | np.uint8(0x30)   # the upper nibble must be ignored
+    scales = rng.integers(1, 253, (E, N, K // 32), dtype=np.uint8)
+    w = _pack_mx(codes, scales)
+    assert w.fmt == "mxfp4"
+    for e in range(E):
+        f, b = w4.dequant(w, e)
+        ref_f, ref_b = orc.dequant_mxfp4(codes[e], scales[e])
+        assert np.array_equal(f.cpu().numpy().view(np.uint32), ref_f.view(np.uint32)), "fp32 image, expert %d" % e
+        assert np.array_equal(bits(b), ref_b), "bf16 image, expert %d" % e
+
+
+MX_PLANS = ([("decode", 16, nbw, 4, ks) for nbw in (1, 2, 4) for ks in (1, 2)] + [("decode", 16, 4, 4, 3)]
+            + PREFILL_PLANS)
+
+
+@pytest.mark.parametrize("plan_args", MX_PLANS, ids=PLAN_ID)
+def test_mxfp4_gemm(orc, plan_args):
+    _say("mxfp4 gemm %s" % (plan_args,))
+    rng = np.random.default_rng(2100)
+    T, E, k, N, K = 40, 6, 2, 96, 544                      # ragged last stage of K
+    x = synth.activations(rng, T, K)
+    codes, scales = synth.codes(rng, E, N, K), synth.mxfp4_scales(rng, E, N, K)
+    ids = synth.uniform_topk(rng, T, E, k)
+    ids[3, 1] = -1
+    w = _pack_mx(codes, scales)
+    plan = w4.make_plan(*plan_args)
+    route = w4.route_prep(i32(ids), E, plan.block_m)
+    out = poison_bf16(T * k, N)
+    w4.grouped_gemm(u16(x), k, w, route, plan, out=out)
+    acc, _ = orc.grouped_gemm(x, k, codes, scales, ids, acc64=True, fmt="mxfp4")
+    check_gemm(bits(out), acc, ids, E, label="mxfp4 %s" % (plan_args,))
+
+
+@pytest.mark.parametrize("plan_args", [("decode", 16, 4, 4, 1), ("decode", 16, 2, 4, 3), ("prefill", 64, 4, 4, 1),
+                                       ("prefill", 32, 2, 4, 1, 128)], ids=PLAN_ID)
+def test_mxfp4_gemm_integer_exact(orc, plan_args):
+    # scale 1 and x in {-2..2}: every product is a multiple of 0.5 and every partial sum is exact in binary32
+    rng = np.random.default_rng(2200)
+    T, E, k, N, K = 30, 4, 2, 48, 1024
+    x = synth.to_bf16_bits(rng.integers(-2, 3, (T, K)).astype(np.float32))
+    codes = synth.codes(rng, E, N, K)
+    scales = np.full((E, N, K // 32), 127, np.uint8)
+    ids = synth.uniform_topk(rng, T, E, k)
+    w = _pack_mx(codes, scales)
+    plan = w4.make_plan(*plan_args)
+    route = w4.route_prep(i32(ids), E, plan.block_m)
+    out = poison_bf16(T * k, N)
+    w4.grouped_gemm(u16(x), k, w, route, plan, out=out)
+    _, ref_bits = orc.grouped_gemm(x, k, codes, scales, ids, fmt="mxfp4")
+    assert np.array_equal(bits(out), ref_bits), "integer regime must be bit-exact"
+
+
+@pytest.mark.parametrize("plan_args", [("decode", 16, 4, 4, 1), ("prefill", 32, 2, 4, 1, 64)], ids=PLAN_ID)
+@pytest.mark.parametrize("kind", EDGE)
+def test_mxfp4_edge_cases(orc, kind, plan_args):
+    case = _edge_case(kind)
+    rng = np.random.default_rng(2300 + EDGE.index(kind))
+    scales = synth.mxfp4_scales(rng, case.E, case.N, case.K)
+    w = _pack_mx(case.codes, scales)
+    plan = w4.make_plan(*plan_args)
+    route = w4.route_prep(i32(case.topk_ids), case.E, plan.block_m)
+    out = poison_bf16(route["R"], case.N)
+    w4.grouped_gemm(u16(case.A), case.topk_ids.shape[1], w, route, plan, out=out)
+    acc, _ = orc.grouped_gemm(case.A, case.topk_ids.shape[1], case.codes, scales, case.topk_ids, acc64=True,
+                              fmt="mxfp4")
+    check_gemm(bits(out), acc, case.topk_ids, case.E, label="mxfp4 " + kind)
+
+
+@pytest.mark.parametrize("plan_args", [("decode", 16, 2, 4, 1), ("decode", 16, 4, 4, 2), ("prefill", 32, 2, 4, 1, 128)],
+                         ids=PLAN_ID)
+def test_mxfp4_gemm_silu(orc, plan_args):
+    rng = np.random.default_rng(2400)
+    T, E, k, K, I = 50, 5, 2, 256, 96
+    x = synth.activations(rng, T, K)
+    codes, scales = synth.codes(rng, E, 2 * I, K), synth.mxfp4_scales(rng, E, 2 * I, K)
+    ids = synth.uniform_topk(rng, T, E, k)
+    w = _pack_mx(codes, scales)
+    plan = w4.make_plan(*plan_args)
+    route = w4.route_prep(i32(ids), E, plan.block_m)
+    h = poison_bf16(T * k, I)
+    w4.grouped_gemm_silu(u16(x), k, w, route, plan, out=h)
+    gu, _ = orc.grouped_gemm(x, k, codes, scales, ids, acc64=True, fmt="mxfp4")
+    check_act(bits(h), gu, ids, E, label="mxfp4 silu")
+
+
+def test_mxfp4_rejects_wide_decode_blocks():
+    rng = np.random.default_rng(2500)
+    codes, scales = synth.codes(rng, 2, 32, 64), synth.mxfp4_scales(rng, 2, 32, 64)
+    w = _pack_mx(codes, scales)
+    ids = np.zeros((4, 1), np.int32)
+    plan = w4.make_plan("decode", 32, 2, 4, 1)
+    route = w4.route_prep(i32(ids), 2, 32)
+    with pytest.raises(w4.W4A16Error) as ei:
+        w4.grouped_gemm(u16(synth.activations(rng, 4, 64)), 1, w, route, plan)
+    assert ei.value.code == -2
+
+
+@pytest.mark.parametrize("shape", [(16, 8, 2, 256, 128), (200, 8, 2, 256, 128)], ids=lambda s: "T%d-E%d-k%d-H%d-I%d" % s)
+def test_mxfp4_fused_moe(orc, shape):
+    T, E, k, H, I = shape
+    _say("mxfp4 fused %s" % (shape,))
+    rng = np.random.default_rng(2600 + T)
+    x = synth.activations(rng, T, H)
+    c13, s13 = synth.codes(rng, E, 2 * I, H), synth.mxfp4_scales(rng, E, 2 * I, H, 120, 124)
+    c2, s2 = synth.codes(rng, E, H, I), synth.mxfp4_scales(rng, E, H, I, 120, 124)
+    ids = synth.uniform_topk(rng, T, E, k)
+    ids[0, :] = -1
+    tw = rng.uniform(0.1, 1.0, (T, k)).astype(np.float32)
+    w13, w2 = _pack_mx(c13, s13), _pack_mx(c2, s2)
+    out = torch.full((T, H), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    w4.fused_moe(u16(x), i32(ids), f32(tw), w13, w2, out=out)
+    got = bits(out)
+    orc.fused_moe(x, ids, tw, c13, s13, c2, s2, fmt="mxfp4")
+    out_acc = orc.last_out_acc
+    g = orc_bf16_to_f64(got)
+    assert np.all(got[0] == 0)
+    for t in range(1, T):
+        den = np.abs(out_acc[t]).max()
+        assert np.abs(g[t] - out_acc[t]).max() <= FUSED_TOL * den, "token %d" % t
+
+
 # ------------------------------------------------------------------ gate_up GEMM with the activation epilogue
 
 ACT_PLANS = [("decode", 16, 2, 4, 1), ("decode", 16, 4, 4, 1), ("decode", 48, 4, 4, 1), ("decode", 32, 4, 4, 2),

@@ -302,6 +302,48 @@ int w4a16_pack_weights(const uint8_t* codes, const uint16_t* scales, int E, int 
     return ok();
 }
 
+int w4a16_packed_bytes_mxfp4(int E, int N, int K, size_t* bytes) {
+    if (!bytes) return fail(W4A16_INVALID_ARG, "w4a16_packed_bytes_mxfp4: bytes is NULL");
+    if (E < 1 || N < 1) return fail(W4A16_INVALID_ARG, "w4a16_packed_bytes_mxfp4: E=%d N=%d must be >= 1", E, N);
+    if (K < 32 || K % 32)
+        return fail(W4A16_UNSUPPORTED_SHAPE, "w4a16_packed_bytes_mxfp4: K=%d must be a positive multiple of 32", K);
+    *bytes = packed_bytes(make_shape(E, N, K, kFmtMxfp4));
+    return ok();
+}
+
+int w4a16_pack_weights_mxfp4(const uint8_t* codes, const uint8_t* scales, int E, int N, int K, void* packed,
+                             size_t packed_bytes_avail, hipStream_t s, w4a16_weights** out) {
+    const char* what = "w4a16_pack_weights_mxfp4";
+    if (!codes || !scales || !packed || !out) return fail(W4A16_INVALID_ARG, "%s: NULL pointer argument", what);
+    size_t need = 0;
+    int rc = w4a16_packed_bytes_mxfp4(E, N, K, &need);
+    if (rc) return rc;
+    if (packed_bytes_avail < need)
+        return fail(W4A16_WORKSPACE_TOO_SMALL, "%s: packed buffer has %zu bytes, needs %zu", what, packed_bytes_avail, need);
+    if (!aligned16(packed)) return fail(W4A16_INVALID_ARG, "%s: packed buffer must be 16-byte aligned", what);
+    if (((uintptr_t)codes & 7u) != 0) return fail(W4A16_INVALID_ARG, "%s: codes must be 8-byte aligned", what);
+    w4a16_weights* w = new (std::nothrow) w4a16_weights;
+    if (!w) return fail(W4A16_INVALID_ARG, "%s: out of host memory", what);
+    w->magic = kHandleMagic;
+    w->layout_version = kLayoutVersion;
+    w->shape = make_shape(E, N, K, kFmtMxfp4);
+    w->packed = packed;
+    w->bytes = need;
+    rc = check_launch(launch_pack_mxfp4(codes, scales, w->shape, packed, s), what);
+    if (rc) {
+        delete w;
+        return rc;
+    }
+    *out = w;
+    return ok();
+}
+
+int w4a16_weights_format(const w4a16_weights* w) {
+    int rc = check_handle(w, "w4a16_weights_format");
+    if (rc) return rc;
+    return w->shape.fmt;
+}
+
 int w4a16_weights_rebind(const w4a16_weights* w, void* packed, w4a16_weights** out) {
     int rc = check_handle(w, "w4a16_weights_rebind");
     if (rc) return rc;
@@ -444,6 +486,14 @@ static int check_prefill_shape(const char* what, const GemmArgs& a, const w4a16_
     return W4A16_OK;
 }
 
+// MXFP4 weights run on the 16-row register-streaming decode kernel and on the prefill kernel.
+static int check_format_plan(const char* what, const w4a16_weights* w, const w4a16_plan& p) {
+    if (w->shape.fmt == kFmtMxfp4 && p.kernel == W4A16_KERNEL_DECODE && p.block_m != 16)
+        return fail(W4A16_UNSUPPORTED_SHAPE, "%s: MXFP4 weights need decode block_m 16 (plan has %d)", what,
+                    p.block_m);
+    return W4A16_OK;
+}
+
 static int grouped_gemm_impl(const char* what, const uint16_t* A, int a_row_div, const w4a16_weights* w,
                              const int32_t* sorted_ids, const int32_t* expert_ids, const int32_t* ntp, int R,
                              const w4a16_plan* p, void* out, int out_mode, void* ws, size_t ws_bytes,
@@ -451,6 +501,8 @@ static int grouped_gemm_impl(const char* what, const uint16_t* A, int a_row_div,
     int rc = check_handle(w, what);
     if (rc) return rc;
     rc = validate_plan(p, what);
+    if (rc) return rc;
+    rc = check_format_plan(what, w, *p);
     if (rc) return rc;
     if (R < 0 || a_row_div < 1) return fail(W4A16_INVALID_ARG, "%s: R=%d a_row_div=%d", what, R, a_row_div);
     if (R == 0) return ok();
@@ -531,6 +583,8 @@ int w4a16_grouped_gemm_offsets(const uint16_t* A_sorted, const int32_t* expert_o
     if (rc) return rc;
     rc = validate_plan(p, what);
     if (rc) return rc;
+    rc = check_format_plan(what, w, *p);
+    if (rc) return rc;
     if (rows_max < 0) return fail(W4A16_INVALID_ARG, "%s: rows_max=%d", what, rows_max);
     if (w->shape.E > W4A16_MAX_EXPERTS) return fail(W4A16_UNSUPPORTED_SHAPE, "%s: too many experts", what);
     if (rows_max == 0) return ok();
@@ -575,6 +629,8 @@ int w4a16_grouped_gemm_masked(const uint16_t* A, const int32_t* masked_m, int ma
     int rc = check_handle(w, what);
     if (rc) return rc;
     rc = validate_plan(p, what);
+    if (rc) return rc;
+    rc = check_format_plan(what, w, *p);
     if (rc) return rc;
     const int E = w->shape.E;
     if (max_m < 0 || (long)max_m * E > INT32_MAX) return fail(W4A16_INVALID_ARG, "%s: max_m=%d", what, max_m);
@@ -642,6 +698,8 @@ int w4a16_grouped_gemm_contiguous(const uint16_t* A, const int32_t* m_indices, i
     int rc = check_handle(w, what);
     if (rc) return rc;
     rc = validate_plan(p, what);
+    if (rc) return rc;
+    rc = check_format_plan(what, w, *p);
     if (rc) return rc;
     const int E = w->shape.E;
     if (m < 0) return fail(W4A16_INVALID_ARG, "%s: m=%d", what, m);
@@ -807,6 +865,8 @@ int w4a16_fused_moe_profiled(const uint16_t* x, const int32_t* topk_ids, const f
     g2.ntp = ntp;
     rc = check_prefill_shape(what, g13, p13);
     if (!rc) rc = check_prefill_shape(what, g2, p2);
+    if (!rc) rc = check_format_plan(what, w13, p13);
+    if (!rc) rc = check_format_plan(what, w2, p2);
     if (rc) return rc;
 
 #define W4A16_STAGE(i)                                                                     \

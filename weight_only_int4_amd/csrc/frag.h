@@ -112,6 +112,57 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t w, float s, float neg8s) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
+// The same eight weights bf16((q - 8) * s) with the code-to-float conversion
+// folded into the multiply-add, in 17 VALU operations: one shift and four
+// AND-ORs place each code in a binary16 bit pattern whose value is affine in
+// the code (0x6400 | q is 1024 + q for a code in bits 0..3 of a half,
+// 0x5400 | (q << 4) is 64 + q for a code in bits 4..7), one mixed-precision
+// fused multiply-add per weight reads that half as binary32 and forms
+// (1024 + q) * s - 1032 s or (64 + q) * s - 72 s, which is (q - 8) * s exactly,
+// and each pair is rounded once to BF16 (round to nearest even).  The masks and
+// patterns come in as opaque VGPR values (0x000F000F, 0x00F000F0, 0x64006400,
+// 0x54005400) so that each AND-OR is one VOP3 instruction; neg1032s = -1032 s,
+// neg72s = -72 s.
+struct MixConsts {
+    uint32_t mask_lo, mask_hi, magic_lo, magic_hi;
+};
+__device__ __forceinline__ MixConsts mix_consts() {
+    return {opaque_vgpr(0x000F000Fu), opaque_vgpr(0x00F000F0u), opaque_vgpr(0x64006400u), opaque_vgpr(0x54005400u)};
+}
+__device__ __forceinline__ bf16x8 dequant8_mix(uint32_t w, float s, float neg1032s, float neg72s, const MixConsts& k) {
+    typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+    const uint32_t w8 = w >> 8;
+    const f16x2_t p0 = __builtin_bit_cast(f16x2_t, (w & k.mask_lo) | k.magic_lo);   // codes 0, 1
+    const f16x2_t p1 = __builtin_bit_cast(f16x2_t, (w & k.mask_hi) | k.magic_hi);   // codes 2, 3
+    const f16x2_t p2 = __builtin_bit_cast(f16x2_t, (w8 & k.mask_lo) | k.magic_lo);  // codes 4, 5
+    const f16x2_t p3 = __builtin_bit_cast(f16x2_t, (w8 & k.mask_hi) | k.magic_hi);  // codes 6, 7
+    u32x4 v;
+    v.x = pack_bf16x2(__builtin_fmaf((float)p0.x, s, neg1032s), __builtin_fmaf((float)p0.y, s, neg1032s));
+    v.y = pack_bf16x2(__builtin_fmaf((float)p1.x, s, neg72s), __builtin_fmaf((float)p1.y, s, neg72s));
+    v.z = pack_bf16x2(__builtin_fmaf((float)p2.x, s, neg1032s), __builtin_fmaf((float)p2.y, s, neg1032s));
+    v.w = pack_bf16x2(__builtin_fmaf((float)p3.x, s, neg72s), __builtin_fmaf((float)p3.y, s, neg72s));
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// MXFP4: eight E2M1 codes of one 32-bit word (code u in bits [4u, 4u+4)) to the BF16 fragment
+// e2m1(code) * 2^(e - 127), where e is the exponent field of `scale` (an E8M0 byte shifted into a binary32
+// exponent).  The hardware conversion takes one byte -- two neighbouring k -- per instruction and applies the
+// scale's power of two; E2M1 times a power of two has at most 2 significant bits, so the result is exact.
+__device__ __forceinline__ bf16x8 mxfp4_dequant8(uint32_t w, float scale) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    u32x4 v;
+    v.x = __builtin_bit_cast(uint32_t, (bf16x2_t)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+    v.y = __builtin_bit_cast(uint32_t, (bf16x2_t)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+    v.z = __builtin_bit_cast(uint32_t, (bf16x2_t)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+    v.w = __builtin_bit_cast(uint32_t, (bf16x2_t)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// The E8M0 scale of group d (0..3) from four scale bytes as a binary32 power of two.
+__device__ __forceinline__ float e8m0_scale(uint32_t four_bytes, int d) {
+    return __uint_as_float(((four_bytes >> (8 * d)) & 0xFFu) << 23);
+}
+
 // Buffer resources (raw, unformatted, unswizzled) on gfx9-family chips: word 3 of the descriptor, the cache
 // policy bit of a non-temporal load, and an offset no resource reaches (a load from it returns zeros; a direct
 // load to LDS from it writes zeros).

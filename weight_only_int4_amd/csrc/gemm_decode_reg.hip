@@ -24,6 +24,12 @@
 //    1 scale extraction): at 16 lanes per SIMD that is the work that has to
 //    hide under the weight stream.  MFMA results go to VGPRs (compiled with
 //    the VGPR MFMA form, see build.py), saving a register move per element.
+//  * MXFP4 weights (FMT = kFmtMxfp4) need none of that: the hardware converts
+//    two E2M1 codes with their E8M0 scale to exact BF16 per instruction (at
+//    the full VALU rate), so each group is 4 conversions per n-block and its
+//    MFMAs accumulate directly.  That leaves registers for a ring of three
+//    stages instead of two: two stages in flight per wavefront, which the
+//    smaller per-stage compute needs to keep the weight stream busy.
 #include <type_traits>
 
 #include "decode_common.h"
@@ -44,8 +50,10 @@ struct RegStage {
 #define W4A16_DECODE_REG_WAVES 1
 #endif
 
-template <int NBW, int D, int OM>
+template <int NBW, int D, int OM, int FMT>
 __global__ __launch_bounds__(kDecodeThreads, W4A16_DECODE_REG_WAVES) void gemm_decode_reg_kernel(DecodeParams p) {
+    constexpr int SB = sb_bytes(FMT);
+    constexpr bool MX = FMT == kFmtMxfp4;
     static_assert(OM != kOutAct || NBW % 2 == 0, "the activation epilogue pairs gate and up n-blocks");
     static_assert(D >= 2 && D <= 6, "ring depth");
     __shared__ int ssid[16];
@@ -71,15 +79,15 @@ __global__ __launch_bounds__(kDecodeThreads, W4A16_DECODE_REG_WAVES) void gemm_d
 
     // Buffer loads: a scalar resource, a per-lane offset fixed for the whole K loop, and the stage's offset as a
     // scalar, so a load costs no vector arithmetic.  Offsets at or past a resource's extent read zeros.
-    const uint32_t expert_bytes = (uint32_t)sh.NB * sh.KB * SB_BYTES;
+    const uint32_t expert_bytes = (uint32_t)sh.NB * sh.KB * SB;
     const __amdgpu_buffer_rsrc_t wres = buffer_resource(p.packed + (size_t)e * expert_bytes, expert_bytes);
     uint32_t cw_off[NBW], sc_off[NBW];
 #pragma unroll
     for (int q = 0; q < NBW; ++q) {
         int o;
         const uint32_t nb = (uint32_t)slot_nblock<NBW, OM>(sh, wave_global, q, &o);
-        cw_off[q] = nb * sh.KB * SB_BYTES + (uint32_t)L * 16u;
-        sc_off[q] = nb * sh.KB * SB_BYTES + SB_CODE_BYTES + (uint32_t)j * 16u;
+        cw_off[q] = nb * sh.KB * SB + (uint32_t)L * 16u;
+        sc_off[q] = nb * sh.KB * SB + SB_CODE_BYTES + (uint32_t)j * (MX ? 8u : 16u);
     }
     // activations: lane (c, j) reads row j of the tile at k-slot c; sentinel rows read past the end (zeros)
     const uint32_t a_bytes = (uint32_t)(p.R / p.a_row_div) * (uint32_t)K * 2u;
@@ -92,14 +100,18 @@ __global__ __launch_bounds__(kDecodeThreads, W4A16_DECODE_REG_WAVES) void gemm_d
     // reading zeros (the test is uniform per group since K is a multiple of 32)
     auto load = [&](int st, RegStage<NBW>& S, auto ragged) {
         const int kb = st >> 1, h = st & 1;
-        const int soff_code = kb * SB_BYTES + h * 1024, soff_scale = kb * SB_BYTES + h * 8;
+        const int soff_code = kb * SB + h * 1024, soff_scale = kb * SB + h * (MX ? 4 : 8);
 #pragma unroll
         for (int q = 0; q < NBW; ++q) {
             S.cw[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, cw_off[q], soff_code,
                                                                                       kBufferNonTemporal));
-            const auto sv = __builtin_amdgcn_raw_buffer_load_b64(wres, sc_off[q], soff_scale, 0);
-            S.sc[q][0] = sv[0];
-            S.sc[q][1] = sv[1];
+            if constexpr (MX) {
+                S.sc[q][0] = __builtin_amdgcn_raw_buffer_load_b32(wres, sc_off[q], soff_scale, 0);
+            } else {
+                const auto sv = __builtin_amdgcn_raw_buffer_load_b64(wres, sc_off[q], soff_scale, 0);
+                S.sc[q][0] = sv[0];
+                S.sc[q][1] = sv[1];
+            }
         }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -122,6 +134,17 @@ __global__ __launch_bounds__(kDecodeThreads, W4A16_DECODE_REG_WAVES) void gemm_d
 
     const uint32_t kMask = opaque_vgpr(0x000F000Fu), kBias = opaque_vgpr(0x43004300u);
     auto compute = [&](const RegStage<NBW>& S) {
+        if constexpr (MX) {
+            // exact BF16 weights from the hardware conversion, accumulated directly
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const bf16x8 xf = __builtin_bit_cast(bf16x8, S.xa[g]);
+#pragma unroll
+                for (int q = 0; q < NBW; ++q)
+                    acc[0][q] = mfma16(xf, mxfp4_dequant8(S.cw[q][g], e8m0_scale(S.sc[q][0], g)), acc[0][q]);
+            }
+            return;
+        }
         // a ragged last stage computes its padding groups too: their codes are 8 and scales 0 in the packed
         // image and their activations are zero, so they add exactly zero
 #pragma unroll
@@ -194,6 +217,9 @@ __global__ __launch_bounds__(kDecodeThreads, W4A16_DECODE_REG_WAVES) void gemm_d
 #ifndef W4A16_DECODE_REG_DEPTH
 #define W4A16_DECODE_REG_DEPTH 2
 #endif
+#ifndef W4A16_DECODE_REG_DEPTH_MX
+#define W4A16_DECODE_REG_DEPTH_MX 3
+#endif
 
 template <int NBW, int OM>
 hipError_t launch_reg(const GemmArgs& a, const w4a16_plan& pl, hipStream_t s) {
@@ -201,7 +227,11 @@ hipError_t launch_reg(const GemmArgs& a, const w4a16_plan& pl, hipStream_t s) {
                    a.out, a.partials, a.counters};
     const dim3 grid(a.max_blocks, decode_n_tiles(a.sh, pl), pl.k_split);
     constexpr int D = W4A16_DECODE_REG_DEPTH >= 2 ? W4A16_DECODE_REG_DEPTH : 2;  // 0 switches the kernel off
-    hipLaunchKernelGGL((gemm_decode_reg_kernel<NBW, D, OM>), grid, dim3(kDecodeThreads), 0, s, p);
+    constexpr int DMX = W4A16_DECODE_REG_DEPTH_MX >= 2 ? W4A16_DECODE_REG_DEPTH_MX : 2;
+    if (a.sh.fmt == kFmtMxfp4)
+        hipLaunchKernelGGL((gemm_decode_reg_kernel<NBW, DMX, OM, kFmtMxfp4>), grid, dim3(kDecodeThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((gemm_decode_reg_kernel<NBW, D, OM, kFmtInt4>), grid, dim3(kDecodeThreads), 0, s, p);
     return hipGetLastError();
 }
 
@@ -221,7 +251,8 @@ hipError_t dispatch_reg(const GemmArgs& a, const w4a16_plan& pl, hipStream_t s) 
 
 bool decode_reg_supported(const GemmArgs& a, const w4a16_plan& p) {
     // one 16-row tile; the buffer resources address below 2 GiB (one expert's packed weights, the activations)
-    return W4A16_DECODE_REG_DEPTH > 0 && p.block_m == 16 && (size_t)a.sh.NB * a.sh.KB * SB_BYTES < (1u << 31) &&
+    return W4A16_DECODE_REG_DEPTH > 0 && p.block_m == 16 &&
+           (size_t)a.sh.NB * a.sh.KB * sb_bytes(a.sh.fmt) < (1u << 31) &&
            (size_t)(a.R / a.a_row_div) * a.sh.K * 2 < (1u << 31);
 }
 

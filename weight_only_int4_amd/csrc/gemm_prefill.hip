@@ -33,6 +33,9 @@
 //    a taller M tile amortises the INT4 conversion (Chord page, "Grouped SM90
 //    kernels").  The dequantisation of group g+1 is independent of the MFMAs
 //    of group g, so the two interleave.
+//  * MXFP4 weights (FMT = kFmtMxfp4) convert in hardware: two E2M1 codes and
+//    their E8M0 scale to exact BF16 per instruction, 4 instructions per 8
+//    weights instead of about 23.
 //  * At most 256 registers per lane for the 128x32 and 64x64 wavefront tiles,
 //    so two wavefronts share each SIMD: one issues VALU dequantisation while
 //    the other's MFMAs run.
@@ -43,6 +46,10 @@
 
 namespace w4a16 {
 namespace {
+
+#ifndef W4A16_PREFILL_MIX
+#define W4A16_PREFILL_MIX 1
+#endif
 
 constexpr int KT = 128;        // k per stage (4 scale groups, half a superblock)
 constexpr int kThreads = 256;  // four wavefronts, each owning its own columns
@@ -97,7 +104,7 @@ constexpr int prefill_waves_per_simd() {
 
 // One tile: 16*MTA rows starting at route slot row0, all of them of expert e, times the column tile nt.  The
 // LDS ring and the row table are the kernel's (sized for its largest tile).
-template <int MTA, int NBW, int OM>
+template <int MTA, int NBW, int OM, int FMT>
 __device__ __forceinline__ void prefill_tile(const PrefillParams& p, uint8_t* slot0, uint8_t* slot1, int* ssid,
                                              int row0, int e, int nt) {
     constexpr int BM = 16 * MTA;                // rows of this tile
@@ -150,7 +157,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, uint8_t* sl
     };
 
     // ---- weight stream: one expert's packed image, per-lane offsets fixed for the whole K loop
-    const uint32_t expert_bytes = (uint32_t)sh.NB * sh.KB * SB_BYTES;
+    constexpr int SB = sb_bytes(FMT);
+    constexpr bool MX = FMT == kFmtMxfp4;
+    const uint32_t expert_bytes = (uint32_t)sh.NB * sh.KB * SB;
     const __amdgpu_buffer_rsrc_t wres = buffer_resource(p.packed + (size_t)e * expert_bytes, expert_bytes);
     uint32_t cw_off[NBW], sc_off[NBW];
 #pragma unroll
@@ -163,18 +172,22 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, uint8_t* sl
             nb = wave_global * NBW + q < sh.NB ? wave_global * NBW + q : sh.NB - 1;
         }
         // clamped blocks compute discarded columns
-        cw_off[q] = (uint32_t)nb * sh.KB * SB_BYTES + (uint32_t)L * 16u;
-        sc_off[q] = (uint32_t)nb * sh.KB * SB_BYTES + SB_CODE_BYTES + (uint32_t)j * 16u;
+        cw_off[q] = (uint32_t)nb * sh.KB * SB + (uint32_t)L * 16u;
+        sc_off[q] = (uint32_t)nb * sh.KB * SB + SB_CODE_BYTES + (uint32_t)j * (MX ? 8u : 16u);
     }
     auto load_w = [&](int st, WStage<NBW>& W) {
         const int kb = st >> 1, h = st & 1;
 #pragma unroll
         for (int q = 0; q < NBW; ++q) {
             W.cw[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                    wres, cw_off[q], kb * SB_BYTES + h * 1024, kBufferNonTemporal));
-            const auto sv = __builtin_amdgcn_raw_buffer_load_b64(wres, sc_off[q], kb * SB_BYTES + h * 8, 0);
-            W.sc[q][0] = sv[0];
-            W.sc[q][1] = sv[1];
+                                                    wres, cw_off[q], kb * SB + h * 1024, kBufferNonTemporal));
+            if constexpr (MX) {
+                W.sc[q][0] = __builtin_amdgcn_raw_buffer_load_b32(wres, sc_off[q], kb * SB + h * 4, 0);
+            } else {
+                const auto sv = __builtin_amdgcn_raw_buffer_load_b64(wres, sc_off[q], kb * SB + h * 8, 0);
+                W.sc[q][0] = sv[0];
+                W.sc[q][1] = sv[1];
+            }
         }
     };
 
@@ -184,12 +197,24 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, uint8_t* sl
 #pragma unroll
         for (int q = 0; q < NBW; ++q) acc[mt][q] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+#if W4A16_PREFILL_MIX
+    const MixConsts mixk = mix_consts();
+#endif
     auto dequant_group = [&](const WStage<NBW>& W, int g, bf16x8* wf) {
+        if constexpr (MX) {
+#pragma unroll
+            for (int q = 0; q < NBW; ++q) wf[q] = mxfp4_dequant8(W.cw[q][g], e8m0_scale(W.sc[q][0], g));
+            return;
+        }
 #pragma unroll
         for (int q = 0; q < NBW; ++q) {
             const uint32_t word = W.sc[q][g >> 1];
             const float s = __uint_as_float((g & 1) ? (word & 0xFFFF0000u) : (word << 16));
+#if W4A16_PREFILL_MIX
+            wf[q] = dequant8_mix(W.cw[q][g], s, -1032.0f * s, -72.0f * s, mixk);
+#else
             wf[q] = dequant8(W.cw[q][g], s, -8.0f * s);
+#endif
         }
     };
     // multiply the stage in LDS slot `slot` with the weights W.  A ragged last stage computes its padding groups
@@ -295,17 +320,17 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, uint8_t* sl
 }
 
 // Tiles of c route blocks of RB16 * 16 rows: the body for height c * RB16 (c <= MT / RB16)
-template <int MT, int NBW, int OM, int RB16, int C = 1>
+template <int MT, int NBW, int OM, int RB16, int FMT, int C = 1>
 __device__ __forceinline__ void run_tile(int c, const PrefillParams& p, uint8_t* slot0, uint8_t* slot1, int* ssid,
                                          int row0, int e, int nt) {
     if constexpr (C * RB16 <= MT) {
-        if (c == C) prefill_tile<C * RB16, NBW, OM>(p, slot0, slot1, ssid, row0, e, nt);
-        else run_tile<MT, NBW, OM, RB16, C + 1>(c, p, slot0, slot1, ssid, row0, e, nt);
+        if (c == C) prefill_tile<C * RB16, NBW, OM, FMT>(p, slot0, slot1, ssid, row0, e, nt);
+        else run_tile<MT, NBW, OM, RB16, FMT, C + 1>(c, p, slot0, slot1, ssid, row0, e, nt);
     }
 }
 
 // RB16: route block height in 16-row units; MT (= the tile's largest height) when every route block is a tile.
-template <int MT, int NBW, int OM, int RB16>
+template <int MT, int NBW, int OM, int RB16, int FMT>
 __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<MT, NBW>())) void gemm_prefill_kernel(PrefillParams p) {
     static_assert(OM != kOutAct || NBW % 2 == 0, "the activation epilogue pairs gate and up n-blocks");
     static_assert(MT % RB16 == 0, "a tile is a whole number of route blocks");
@@ -337,11 +362,11 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<MT, NBW>())) void
         const int b0 = p.tiles[2 * t], c = p.tiles[2 * t + 1];
         const int e = p.expert_ids[b0];
         if (e < 0 || e >= p.sh.E) return;
-        run_tile<MT, NBW, OM, RB16>(c, p, slot0, slot1, ssid, b0 * RB16 * 16, e, nt);
+        run_tile<MT, NBW, OM, RB16, FMT>(c, p, slot0, slot1, ssid, b0 * RB16 * 16, e, nt);
     } else {
         const int e = p.expert_ids[t];
         if (e < 0 || e >= p.sh.E) return;
-        prefill_tile<MT, NBW, OM>(p, slot0, slot1, ssid, t * BM, e, nt);
+        prefill_tile<MT, NBW, OM, FMT>(p, slot0, slot1, ssid, t * BM, e, nt);
     }
 }
 
@@ -355,7 +380,10 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t s) {
     // 8 * ceil(tiles / 8) - 1.  A tile list holds at most one tile per route block.
     const unsigned tiles = (unsigned)a.max_blocks * (unsigned)n_tiles;
     const dim3 grid((tiles + kXcds - 1) / kXcds * kXcds);
-    hipLaunchKernelGGL((gemm_prefill_kernel<MT, NBW, OM, RB16>), grid, dim3(kThreads), 0, s, p);
+    if (a.sh.fmt == kFmtMxfp4)
+        hipLaunchKernelGGL((gemm_prefill_kernel<MT, NBW, OM, RB16, kFmtMxfp4>), grid, dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((gemm_prefill_kernel<MT, NBW, OM, RB16, kFmtInt4>), grid, dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 
@@ -382,7 +410,8 @@ hipError_t dispatch(const GemmArgs& a, int mt, int nbw, int rb16, hipStream_t s)
 
 bool prefill_supported(const GemmArgs& a) {
     // the buffer resources address below 2 GiB: one expert's packed weights, and the activation matrix
-    return (size_t)a.sh.NB * a.sh.KB * SB_BYTES < (1u << 31) && (size_t)(a.R / a.a_row_div) * a.sh.K * 2 < (1u << 31);
+    return (size_t)a.sh.NB * a.sh.KB * sb_bytes(a.sh.fmt) < (1u << 31) &&
+           (size_t)(a.R / a.a_row_div) * a.sh.K * 2 < (1u << 31);
 }
 
 int prefill_tile_rows(const w4a16_plan& p) { return p.tile_m ? p.tile_m : p.block_m; }

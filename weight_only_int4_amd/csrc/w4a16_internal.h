@@ -29,6 +29,13 @@ namespace w4a16 {
 // Rows n >= N carry code 8 and scale 0 (weight 0); groups past K carry code 8
 // and scale 0 and are never read by the GEMM kernels.
 //
+// MXFP4 weight sets (E2M1 codes, one E8M0 scale byte per 32 k) use the same
+// superblock geometry with two differences: word d carries code u in bits
+// [4u, 4u+4) (each byte holds two neighbouring k, the pair the hardware
+// FP4 -> BF16 conversion takes), and the scales are one byte per group, 8
+// bytes per row j at 2048 + 8*j, so a superblock is 2176 bytes.  Padding is
+// code 0 (+0) with scale 127 (1.0).
+//
 // Why this order: one wavefront of 64 lanes loading 16 contiguous bytes per
 // lane reads exactly one half (1024 bytes, fully coalesced), and lane
 // L = c*16 + j then holds, for each of four groups, the eight codes that the
@@ -44,24 +51,34 @@ constexpr int SB_GROUPS = 8;    // scale groups per superblock
 constexpr int SB_CODE_BYTES = 2048;
 constexpr int SB_SCALE_BYTES = 256;
 constexpr int SB_BYTES = SB_CODE_BYTES + SB_SCALE_BYTES;
+constexpr int SB_BYTES_MXFP4 = SB_CODE_BYTES + NB_ROWS * SB_GROUPS;
 constexpr uint32_t kHandleMagic = 0x34413136u;  // "41A6"
+
+// Weight formats (the value is the public W4A16_FORMAT_* constant).
+constexpr int kFmtInt4 = W4A16_FORMAT_INT4;
+constexpr int kFmtMxfp4 = W4A16_FORMAT_MXFP4;
+
+// Superblock bytes of a format.
+__host__ __device__ constexpr int sb_bytes(int fmt) { return fmt == kFmtMxfp4 ? SB_BYTES_MXFP4 : SB_BYTES; }
 
 struct Shape {
     int E, N, K;
     int NB, KB, G;  // n-blocks, superblocks along K, scale groups (K/32)
+    int fmt;        // kFmtInt4 or kFmtMxfp4
 };
 
-inline Shape make_shape(int E, int N, int K) {
+inline Shape make_shape(int E, int N, int K, int fmt = kFmtInt4) {
     Shape s;
     s.E = E; s.N = N; s.K = K;
     s.NB = (N + NB_ROWS - 1) / NB_ROWS;
     s.KB = (K + SB_K - 1) / SB_K;
     s.G = K / 32;
+    s.fmt = fmt;
     return s;
 }
 
 inline size_t packed_bytes(const Shape& s) {
-    return (size_t)s.E * s.NB * s.KB * SB_BYTES;
+    return (size_t)s.E * s.NB * s.KB * sb_bytes(s.fmt);
 }
 
 }  // namespace w4a16
@@ -89,6 +106,8 @@ constexpr int kOutBf16 = 0, kOutF32 = 1, kOutAct = 2;
 
 // Launchers (return hipError_t of the launch).
 hipError_t launch_pack(const uint8_t* codes, const uint16_t* scales, const Shape& sh, void* packed, hipStream_t s);
+hipError_t launch_pack_mxfp4(const uint8_t* codes, const uint8_t* scales, const Shape& sh, void* packed,
+                             hipStream_t s);
 hipError_t launch_dequant(const void* packed, const Shape& sh, int expert, float* out_f32, uint16_t* out_bf16,
                           hipStream_t s);
 hipError_t launch_route_prep(const int32_t* topk_ids, int R, int E, int block_m, int max_padded, int max_blocks,

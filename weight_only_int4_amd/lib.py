@@ -20,6 +20,8 @@ _P = ctypes.c_void_p
 _I = ctypes.c_int
 _SZ = ctypes.c_size_t
 
+FORMAT_INT4 = 0
+FORMAT_MXFP4 = 1
 KERNEL_DECODE = 1
 KERNEL_PREFILL = 2
 
@@ -48,6 +50,9 @@ _SIGS = {
     "w4a16_version": (ctypes.c_char_p, []),
     "w4a16_packed_bytes": (_I, [_I, _I, _I, ctypes.POINTER(_SZ)]),
     "w4a16_pack_weights": (_I, [_P, _P, _I, _I, _I, _P, _SZ, _P, ctypes.POINTER(_P)]),
+    "w4a16_packed_bytes_mxfp4": (_I, [_I, _I, _I, ctypes.POINTER(_SZ)]),
+    "w4a16_pack_weights_mxfp4": (_I, [_P, _P, _I, _I, _I, _P, _SZ, _P, ctypes.POINTER(_P)]),
+    "w4a16_weights_format": (_I, [_P]),
     "w4a16_weights_rebind": (_I, [_P, _P, ctypes.POINTER(_P)]),
     "w4a16_weights_info": (_I, [_P, ctypes.POINTER(_I), ctypes.POINTER(_I), ctypes.POINTER(_I),
                                 ctypes.POINTER(_P), ctypes.POINTER(_SZ)]),
@@ -125,9 +130,10 @@ def symbol_names():
 
 # ---------------------------------------------------------------- weights
 
-def packed_bytes(E: int, N: int, K: int) -> int:
+def packed_bytes(E: int, N: int, K: int, fmt: str = "int4") -> int:
     out = _SZ(0)
-    _check(load().w4a16_packed_bytes(E, N, K, ctypes.byref(out)))
+    fn = load().w4a16_packed_bytes_mxfp4 if fmt == "mxfp4" else load().w4a16_packed_bytes
+    _check(fn(E, N, K, ctypes.byref(out)))
     return out.value
 
 
@@ -144,6 +150,12 @@ class Weights:
         h = ctypes.c_void_p()
         _check(load().w4a16_weights_rebind(self.handle, _ptr(packed), ctypes.byref(h)))
         return Weights(h.value, packed, self.E, self.N, self.K)
+
+    @property
+    def fmt(self) -> str:
+        rc = load().w4a16_weights_format(self.handle)
+        _check(min(rc, 0))
+        return "mxfp4" if rc == FORMAT_MXFP4 else "int4"
 
     def info(self):
         E, N, K = _I(), _I(), _I()
@@ -168,6 +180,18 @@ def pack_weights(codes: torch.Tensor, scales: torch.Tensor, packed: torch.Tensor
     h = ctypes.c_void_p()
     _check(load().w4a16_pack_weights(_ptr(codes), _ptr(scales), E, N, K, _ptr(packed), packed.numel(),
                                      _stream(stream), ctypes.byref(h)))
+    return Weights(h.value, packed, E, N, K)
+
+def pack_weights_mxfp4(codes: torch.Tensor, scales: torch.Tensor, packed: torch.Tensor | None = None,
+                       stream=None) -> Weights:
+    """MXFP4: codes uint8 [E,N,K] (low nibble: E2M1), scales uint8 [E,N,K/32] (E8M0) -> Weights."""
+    E, N, K = codes.shape
+    nbytes = packed_bytes(E, N, K, "mxfp4")
+    if packed is None:
+        packed = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
+    h = ctypes.c_void_p()
+    _check(load().w4a16_pack_weights_mxfp4(_ptr(codes), _ptr(scales), E, N, K, _ptr(packed), packed.numel(),
+                                           _stream(stream), ctypes.byref(h)))
     return Weights(h.value, packed, E, N, K)
 
 
