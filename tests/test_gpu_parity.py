@@ -629,11 +629,50 @@ def check_gemm_f32(got, ref, flat, E, label, tol=5e-3):
         assert ratio <= tol, "%s expert %d ratio %.3g" % (label, e, ratio)
 
 
-def test_fused_moe_graph_replays(orc):
+@pytest.mark.parametrize("shape", [(32, 64, 4, 512, 256), (5, 8, 2, 2016, 256), (64, 16, 4, 512, 256),
+                                   (2, 48, 8, 512, 2048)],
+                         ids=["T32-E64-decode", "T5-E8-H2016-decode", "T64-E16-prefill", "T2-E48-splitK"])
+def test_fused_moe_equals_sequence(orc, shape):
+    """The fused call is the sequence route_prep, gate_up with SiLU*mul, down (binary32), combine, with the same
+    plans, bit for bit (decode, prefill and split-K plans; a token without a local route, one routed twice to
+    the same expert, a non-local route, a ragged last column tile)."""
+    T, E, k, H, I = shape
+    _say("fused = sequence %s" % (shape,))
+    rng = np.random.default_rng(T * 13 + E)
+    x = synth.activations(rng, T, H)
+    c13, s13 = synth.codes(rng, E, 2 * I, H), synth.scales(rng, E, 2 * I, H)
+    c2, s2 = synth.codes(rng, E, H, I), synth.scales(rng, E, H, I)
+    ids = synth.uniform_topk(rng, T, E, k)
+    ids[0, :] = -1                                    # no local route: zero row
+    ids[1, 1] = ids[1, 0]                             # one token routed twice to the same expert
+    ids[T - 1, 0] = E + 3                             # a non-local route
+    tw = rng.uniform(0.1, 1.0, (T, k)).astype(np.float32)
+    w13, w2 = _pack(c13, s13), _pack(c2, s2)
+    p13, p2 = w4.fused_moe_plans(T, k, w13, w2)
+    _say("  plans %r %r" % (p13, p2))
+    out = torch.full((T, H), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    w4.fused_moe(u16(x), i32(ids), f32(tw), w13, w2, out=out)
+    route = w4.route_prep(i32(ids), E, p13.block_m)
+    h = poison_bf16(T * k, I)
+    w4.grouped_gemm_silu(u16(x), k, w13, route, p13, out=h)
+    y = w4.grouped_gemm(h, 1, w2, route, p2, out_f32=True)
+    seq = bits(w4.moe_combine(y, f32(tw), i32(ids), E))
+    got = bits(out)
+    assert np.all(got[0] == 0)
+    assert np.array_equal(got, seq), "fused differs from the sequence in %d values" % int((got != seq).sum())
+    orc.fused_moe(x, ids, tw, c13, s13, c2, s2)
+    ref = orc.last_out_acc
+    for t in range(1, T):
+        assert np.abs(orc_bf16_to_f64(got[t]) - ref[t]).max() <= FUSED_TOL * np.abs(ref[t]).max()
+
+
+@pytest.mark.parametrize("shape", [(2, 48, 8, 512, 256), (2, 48, 8, 512, 2048), (32, 64, 4, 512, 256)],
+                         ids=["T2-E48-gate-up-splitK", "T2-E48-both-splitK", "T32-E64-decode"])
+def test_fused_moe_graph_replays(orc, shape):
     """The fused call captured in a HIP graph: every replay (with eager work and synchronisations in between)
     must equal the eager result bit for bit, including plans that split K (their counters reset each call)."""
     rng = np.random.default_rng(77)
-    T, E, k, H, I = 2, 48, 8, 512, 256               # few routes: the planner splits K
+    T, E, k, H, I = shape
     x = synth.activations(rng, T, H)
     c13, s13 = synth.codes(rng, E, 2 * I, H), synth.scales(rng, E, 2 * I, H)
     c2, s2 = synth.codes(rng, E, H, I), synth.scales(rng, E, H, I)

@@ -55,8 +55,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         if (e < 0 || e >= E) continue;
         const float wt = tw[(size_t)t * k + jj];
         const float2 v = *reinterpret_cast<const float2*>(y + ((size_t)t * k + jj) * H + n);
-        a0 = a0 + wt * v.x;
-        a1 = a1 + wt * v.y;
+        a0 = __builtin_fmaf(wt, v.x, a0);  // one rounding per route, as in every combine of this library
+        a1 = __builtin_fmaf(wt, v.y, a1);
     }
     const uint32_t packed = (uint32_t)f32_to_bf16_bits(a0) | ((uint32_t)f32_to_bf16_bits(a1) << 16);
     *reinterpret_cast<uint32_t*>(out + (size_t)t * H + n) = packed;
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) void combine8_kernel(const float* __restrict__
             const float vv[kCombineCols] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w,
                                             v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
 #pragma unroll
-            for (int c = 0; c < kCombineCols; ++c) acc[c] = acc[c] + wt[u] * vv[c];
+            for (int c = 0; c < kCombineCols; ++c) acc[c] = __builtin_fmaf(wt[u], vv[c], acc[c]);
         }
     }
     uint4 o;
