@@ -127,7 +127,7 @@ def test_plan_validation(lib):
     assert lib.w4a16_gemm_workspace_bytes(ctypes.byref(bad), 32, 8, 512, ctypes.byref(sz)) == -2
     bad = L.make_plan("prefill", 96, 4, 4)
     assert lib.w4a16_gemm_workspace_bytes(ctypes.byref(bad), 32, 8, 512, ctypes.byref(sz)) == -2
-    bad = L.make_plan("prefill", 64, 4, 4, k_split=2)
+    bad = L.make_plan("prefill", 64, 4, 4, k_split=17)
     assert lib.w4a16_gemm_workspace_bytes(ctypes.byref(bad), 32, 8, 512, ctypes.byref(sz)) == -2
     good = L.make_plan("decode", 16, 4, 4)
     assert lib.w4a16_gemm_workspace_bytes(ctypes.byref(good), 32, 8, 512, ctypes.byref(sz)) == 0
@@ -143,6 +143,15 @@ def test_plan_validation(lib):
     assert L.gemm_workspace_bytes(tiled, 32, 8, 512) == 256
     assert L.gemm_workspace_bytes(tiled, 32 * 100, 8, 512) == ((4 + 4 * 108) * 4 + 255) // 256 * 256
     assert L.gemm_workspace_bytes(L.make_plan("prefill", 64, 2, 4, 1, 64), 32, 8, 512) == 0
+    # prefill split K: one counter per (tile, column tile), then fp32 partial tiles of the tallest tile.  Plain
+    # 64-row blocks: one tile per route block (R=32, E=8, 64-row blocks: 32 + 8*63 slots -> 9 blocks); n_blocks 4
+    # -> 256 columns, N=512 -> 2 column tiles
+    ps = L.make_plan("prefill", 64, 4, 4, k_split=3)
+    assert L.gemm_workspace_bytes(ps, 32, 8, 512) == 256 + 9 * 2 * 3 * 64 * 256 * 4
+    # 32-row blocks in 128-row tiles: at most ceil(blocks / 4) + owners tiles (R=32, E=8: 9 blocks -> 3 + 8)
+    pt = L.make_plan("prefill", 32, 2, 4, 2, 128)
+    tl = ((4 + 4 * 9) * 4 + 255) // 256 * 256
+    assert L.gemm_workspace_bytes(pt, 32, 8, 512) == 256 + 11 * 4 * 2 * 128 * 128 * 4 + tl
     # split K: counters (one per route block and column tile) then fp32 partial tiles
     split = L.make_plan("decode", 16, 4, 4, k_split=4)
     # 10 route blocks x 2 column tiles of 256: 20 counters (one 256-byte line), 10*2*4 partial tiles of 16x256

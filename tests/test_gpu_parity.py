@@ -133,7 +133,8 @@ DECODE_PLANS = ([("decode", bm, nbw, 4, 1) for bm in (16, 32, 48, 64) for nbw in
                 + [("decode", 16, 4, 4, 2), ("decode", 32, 2, 4, 2), ("decode", 64, 1, 4, 2),
                    ("decode", 16, 1, 4, 3)])  # 3 slices of a 2-stage K: one slice is empty
 PREFILL_PLANS = ([("prefill", bm, nbw, 4, 1) for bm in (64, 128) for nbw in (2, 4)]
-                 + [("prefill", 32, nbw, 4, 1, tile) for tile in (64, 128) for nbw in (2, 4)])  # tiles of 32-row blocks
+                 + [("prefill", 32, nbw, 4, 1, tile) for tile in (64, 128) for nbw in (2, 4)]  # tiles of 32-row blocks
+                 + [("prefill", 64, 2, 4, 2), ("prefill", 32, 2, 4, 3, 128)])  # K split across workgroups
 PLAN_ID = lambda p: "%s-bm%d-nb%d-w%d-ks%d" % p[:5] + ("-t%d" % p[5] if len(p) > 5 else "")  # noqa: E731
 
 
@@ -159,7 +160,8 @@ def test_gemm_tiny_all_plans(orc, plan_args):
 
 @pytest.mark.parametrize("plan_args", [("decode", 16, 4, 4, 1), ("decode", 64, 2, 4, 1), ("decode", 16, 4, 4, 3),
                                        ("decode", 32, 2, 4, 7), ("prefill", 64, 4, 4, 1), ("prefill", 128, 2, 4, 1),
-                                       ("prefill", 32, 2, 4, 1, 128), ("prefill", 32, 2, 4, 1, 64)],
+                                       ("prefill", 32, 2, 4, 1, 128), ("prefill", 32, 2, 4, 1, 64),
+                                       ("prefill", 64, 4, 4, 3), ("prefill", 32, 2, 4, 2, 128)],
                          ids=PLAN_ID)
 @pytest.mark.parametrize("shape", [(24, 6, 2, 40, 512), (9, 4, 3, 64, 96), (70, 3, 2, 16, 2048),
                                    (5, 10, 8, 4096, 7168)], ids=lambda s: "T%d-E%d-k%d-N%d-K%d" % s)
@@ -211,7 +213,8 @@ EDGE = ["E1", "one hot expert", "empty and single", "ragged N and K", "tile edge
 
 @pytest.mark.parametrize("plan_args", [("decode", 16, 1, 4, 1), ("decode", 32, 4, 4, 1), ("decode", 64, 2, 4, 1),
                                        ("decode", 16, 2, 4, 2), ("prefill", 64, 2, 4, 1), ("prefill", 128, 4, 4, 1),
-                                       ("prefill", 32, 2, 4, 1, 128), ("prefill", 32, 2, 4, 1, 64)],
+                                       ("prefill", 32, 2, 4, 1, 128), ("prefill", 32, 2, 4, 1, 64),
+                                       ("prefill", 32, 2, 4, 2, 64)],
                          ids=PLAN_ID)
 @pytest.mark.parametrize("kind", EDGE)
 def test_gemm_edge_cases(orc, kind, plan_args):
@@ -222,6 +225,47 @@ def test_gemm_edge_cases(orc, kind, plan_args):
     acc, _ = orc.grouped_gemm(case.A, case.topk_ids.shape[1], case.codes, case.scales, case.topk_ids, acc64=True)
     worst = check_gemm(got, acc, case.topk_ids, case.E, label=kind)
     _say("  worst ratio %.2e" % worst)
+
+
+@pytest.mark.parametrize("plan_args", [("prefill", 64, 2, 4, 2), ("prefill", 64, 4, 4, 5), ("prefill", 128, 2, 4, 3),
+                                       ("prefill", 32, 2, 4, 3, 128), ("prefill", 32, 4, 4, 16, 64)],
+                         ids=PLAN_ID)
+def test_gemm_prefill_split_k(orc, plan_args):
+    """K split across workgroups on the prefill kernel: slices of 1-2 stages over a ragged K (16 slices over 5
+    stages leaves 11 empty), every output mode, deterministic across calls and graph replays (the arrival
+    counters return to zero)."""
+    _say("prefill split-K %s" % (plan_args,))
+    rng = np.random.default_rng(3100 + plan_args[4])
+    T, E, k, N, K = 150, 5, 2, 96, 544
+    x = synth.activations(rng, T, K)
+    codes, scales = synth.codes(rng, E, N, K), synth.scales(rng, E, N, K)
+    ids = synth.uniform_topk(rng, T, E, k)
+    ids[7, 1] = -1
+    w = _pack(codes, scales)
+    plan = w4.make_plan(*plan_args)
+    route = w4.route_prep(i32(ids), E, plan.block_m)
+    ws = w4.zeroed_workspace(w4.gemm_workspace_bytes(plan, T * k, E, N), "cuda")
+    acc, _ = orc.grouped_gemm(x, k, codes, scales, ids, acc64=True)
+    out = poison_bf16(T * k, N)
+    w4.grouped_gemm(u16(x), k, w, route, plan, out=out, ws=ws)
+    first = bits(out)
+    check_gemm(first, acc, ids, E, label="split-K bf16 %s" % (plan_args,))
+    f = w4.grouped_gemm(u16(x), k, w, route, plan, out_f32=True, ws=ws).cpu().numpy().astype(np.float64)
+    check_gemm_f32(f, acc, ids.reshape(-1), E, "split-K f32")
+    h = poison_bf16(T * k, N // 2)
+    w4.grouped_gemm_silu(u16(x), k, w, route, plan, out=h, ws=ws)
+    check_act(bits(h), acc, ids, E, label="split-K silu")
+    xd = u16(x)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        w4.grouped_gemm(xd, k, w, route, plan, out=out, ws=ws)
+    for rep in range(3):
+        out.view(torch.int16).fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out), first), "replay %d differs" % rep
 
 
 def test_gemm_zero_tokens():

@@ -101,6 +101,7 @@ const Overrides& overrides() {
 // expert and the prefill kernel from 16 rows on.
 constexpr float kDecodeMaxRows = 12.0f;
 
+
 w4a16_plan select_plan(int T, int k, int E, int N, int K, float rows) {
     const Overrides& ov = overrides();
     w4a16_plan p;
@@ -145,11 +146,15 @@ w4a16_plan select_plan(int T, int k, int E, int N, int K, float rows) {
             p.block_m = 32;
             p.tile_m = 64;
         }
+        // The prefill kernel can split K across workgroups (explicit plans), but the planner does not: on an
+        // 8-expert, 4096 x 14336 projection whose grid holds about one workgroup per CU, two to eight slices
+        // were 2-75% slower at 32 to 256 rows per expert (measured), so more workgroups per CU do not help
+        // there and the partial tiles cost their traffic.
     }
     if (ov.block_m) p.block_m = ov.block_m;
     if (ov.n_blocks) p.n_blocks = ov.n_blocks;
     if (ov.waves) p.waves = ov.waves;
-    if (ov.k_split && p.kernel == W4A16_KERNEL_DECODE) p.k_split = ov.k_split;
+    if (ov.k_split) p.k_split = ov.k_split;
     if (ov.tile_m >= 0 && p.kernel == W4A16_KERNEL_PREFILL) p.tile_m = ov.tile_m;
     (void)T; (void)k;
     return p;
@@ -179,7 +184,8 @@ int validate_plan(const w4a16_plan* p, const char* what) {
                         what, tile, p->block_m);
         if (p->n_blocks != 2 && p->n_blocks != 4)
             return fail(W4A16_UNSUPPORTED_SHAPE, "%s: prefill n_blocks %d not in {2,4}", what, p->n_blocks);
-        if (p->k_split != 1) return fail(W4A16_UNSUPPORTED_SHAPE, "%s: prefill k_split must be 1", what);
+        if (p->k_split < 1 || p->k_split > 16)
+            return fail(W4A16_UNSUPPORTED_SHAPE, "%s: prefill k_split %d not in 1..16", what, p->k_split);
         if (p->waves != 4) return fail(W4A16_UNSUPPORTED_SHAPE, "%s: prefill waves must be 4", what);
     } else {
         return fail(W4A16_INVALID_ARG, "%s: unknown kernel %d", what, p->kernel);
@@ -202,8 +208,10 @@ bool tiled_prefill(const w4a16_plan& p) {
 
 GemmWs gemm_ws(const Shape& sh, const w4a16_plan& p, int max_blocks) {
     GemmWs g;
-    g.counter_bytes = align_up(sizeof(unsigned) * decode_counters(sh, p, max_blocks), 256);
-    g.partial_bytes = align_up(sizeof(float) * decode_partial_floats(sh, p, max_blocks), 256);
+    g.counter_bytes = align_up(sizeof(unsigned) * (decode_counters(sh, p, max_blocks) +
+                                                   prefill_counters(sh, p, max_blocks)), 256);
+    g.partial_bytes = align_up(sizeof(float) * (decode_partial_floats(sh, p, max_blocks) +
+                                                prefill_partial_floats(sh, p, max_blocks)), 256);
     g.tile_bytes = tiled_prefill(p) ? align_up(sizeof(int32_t) * (4 + 4 * (size_t)max_blocks), 256) : 0;
     g.total = g.counter_bytes + g.partial_bytes + g.tile_bytes;
     return g;
@@ -802,8 +810,8 @@ int w4a16_fused_moe_plans(int T, int k, const w4a16_weights* w13, const w4a16_we
     p2.kernel = p13.kernel;
     if (p2.kernel == W4A16_KERNEL_PREFILL) {
         if (p2.n_blocks != 2 && p2.n_blocks != 4) p2.n_blocks = 4;
-        p2.k_split = 1;
         p2.tile_m = p13.tile_m;
+        p2.k_split = overrides().k_split ? overrides().k_split : 1;
     } else {
         if (p2.k_split < 1) p2.k_split = 1;
         p2.tile_m = 0;

@@ -70,6 +70,10 @@ struct PrefillParams {
     void* out;
     const int32_t* tiles;       // tile list (first route block, blocks), or NULL: one route block of BM rows per tile
     const int32_t* tile_count;  // its length (device)
+    // split K (grid.y slices): fp32 partial tiles [tile][n_tiles][KS][BM][COLS] and one arrival counter per
+    // (tile, column tile), zero between calls
+    float* partials;
+    unsigned* counters;
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -102,11 +106,79 @@ constexpr int prefill_waves_per_simd() {
     return MT * NBW >= 32 ? 1 : 2;
 }
 
+// Split K: every slice publishes its fp32 partial tile with device-coherent stores and bumps the (tile, column
+// tile) counter; the last to arrive adds the KS partials in slice order, writes the output in its mode and resets
+// the counter.  Partial tiles are BM = 16*MT rows (the kernel's tallest tile) by COLS columns; a tile of MTA < MT
+// row groups uses the first 16*MTA rows.
+template <int MTA, int NBW, int OM, int MT>
+__device__ __forceinline__ void prefill_split_epilogue(const PrefillParams& p, const f32x4 (&acc)[MTA][NBW],
+                                                       const int* ssid, int* s_last, int nt, int t, int ks, int KS,
+                                                       int w, int c, int j) {
+    constexpr int BM = 16 * MT, ROWS = 16 * MTA;
+    constexpr int COLS = NBW * 16 * kWaves;
+    const Shape& sh = p.sh;
+    const size_t tile = (size_t)t * p.n_tiles + nt;
+    float* mine = p.partials + (tile * KS + ks) * (size_t)(BM * COLS);
+#pragma unroll
+    for (int mt = 0; mt < MTA; ++mt)
+#pragma unroll
+        for (int q = 0; q < NBW; ++q)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                __hip_atomic_store(&mine[(mt * 16 + 4 * c + r) * COLS + (w * NBW + q) * 16 + j], acc[mt][q][r],
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // the stores above are device-coherent; wait until they have completed before signalling
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned prev = __hip_atomic_fetch_add(&p.counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_last = prev == (unsigned)(KS - 1);
+    }
+    __syncthreads();
+    if (!*s_last) return;
+    const float* all = p.partials + tile * KS * (size_t)(BM * COLS);
+    auto reduce = [&](int idx) {
+        float v = 0.f;
+        for (int z = 0; z < KS; ++z)
+            v += __hip_atomic_load(&all[(size_t)z * BM * COLS + idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return v;
+    };
+    if (OM == kOutAct) {
+        // output column oc of the tile: wavefront oc / (16*HB), its slot (oc / 16) % HB, lane column oc % 16
+        constexpr int HB = NBW / 2, OCOLS = COLS / 2;
+        const int NO = sh.N / 2;
+        for (int idx = threadIdx.x; idx < ROWS * OCOLS; idx += kThreads) {
+            const int m = idx / OCOLS, oc = idx % OCOLS;
+            const int sid = ssid[m];
+            const int ww = oc / (16 * HB), q = (oc / 16) % HB, jj = oc % 16;
+            const int n = ((nt * kWaves + ww) * HB + q) * 16 + jj;
+            if (sid < 0 || n >= NO) continue;
+            const int gcol = (ww * NBW + q) * 16 + jj;
+            const float g = reduce(m * COLS + gcol), u = reduce(m * COLS + gcol + HB * 16);
+            static_cast<uint16_t*>(p.out)[(size_t)sid * NO + n] = f32_to_bf16_bits(silu_mul(g, u));
+        }
+    } else {
+        const int n_base = nt * COLS;
+        for (int idx = threadIdx.x; idx < ROWS * COLS; idx += kThreads) {
+            const int m = idx / COLS, col = idx % COLS;
+            const int sid = ssid[m];
+            const int n = n_base + col;
+            if (sid < 0 || n >= sh.N) continue;
+            const float v = reduce(idx);
+            if (OM == kOutF32)
+                static_cast<float*>(p.out)[(size_t)sid * sh.N + n] = v;
+            else
+                static_cast<uint16_t*>(p.out)[(size_t)sid * sh.N + n] = f32_to_bf16_bits(v);
+        }
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // One tile: 16*MTA rows starting at route slot row0, all of them of expert e, times the column tile nt.  The
 // LDS ring and the row table are the kernel's (sized for its largest tile).
-template <int MTA, int NBW, int OM, int FMT>
+template <int MTA, int NBW, int OM, int FMT, int MT>
 __device__ __forceinline__ void prefill_tile(const PrefillParams& p, uint8_t* slot0, uint8_t* slot1, int* ssid,
-                                             int row0, int e, int nt) {
+                                             int* s_last, int row0, int e, int nt, int t) {
     constexpr int BM = 16 * MTA;                // rows of this tile
     constexpr int ROWS_PER_WAVE = BM / kWaves;  // activation rows each wavefront streams
     constexpr int DMA = ROWS_PER_WAVE / 4;      // direct loads per wavefront per stage (4 rows of 256 B each)
@@ -117,6 +189,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, uint8_t* sl
     const int c = L >> 4, j = L & 15;
     const int wave_global = nt * kWaves + w;
     const int nst = (sh.G + 3) / 4;
+    // this workgroup's K slice: stages [st_begin, st_end) of nst (all of them without split K)
+    const int KS = gridDim.y, ks = blockIdx.y;
+    const int st_begin = (int)((long)ks * nst / KS), st_end = (int)((long)(ks + 1) * nst / KS);
 
     for (int m = threadIdx.x; m < BM; m += kThreads) {
         const int sid = p.sorted_ids[row0 + m];
@@ -267,26 +342,34 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, uint8_t* sl
     // Pairs of stages alternate the two slots and the two weight register sets (no copies between them).  The
     // loop's loads are never for the last stage, so it has no branches (a branch around loads would make the
     // compiler assume the worst count of loads in flight and drain them); the last one to three stages are peeled.
+    // (the last stage of a slice goes through issue_a_last, which reads a ragged stage only at the end of K)
     WStage<NBW> WA, WB;
-    if (nst == 1) issue_a_last(0, slot0);
-    else issue_a(0, slot0, std::false_type{});
-    __builtin_amdgcn_sched_barrier(0);
-    load_w(0, WA);
-    __builtin_amdgcn_sched_barrier(0);
-    int st = 0;
-    for (; st + 3 < nst; st += 2) {
-        stage(st, slot0, slot1, WA, WB, full{});
-        stage(st + 1, slot1, slot0, WB, WA, full{});
+    if (st_end > st_begin) {
+        if (st_end - st_begin == 1) issue_a_last(st_begin, slot0);
+        else issue_a(st_begin, slot0, std::false_type{});
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(st_begin, WA);
+        __builtin_amdgcn_sched_barrier(0);
+        int st = st_begin;
+        for (; st + 3 < st_end; st += 2) {
+            stage(st, slot0, slot1, WA, WB, full{});
+            stage(st + 1, slot1, slot0, WB, WA, full{});
+        }
+        if (st + 3 == st_end) {
+            stage(st, slot0, slot1, WA, WB, full{});
+            stage(st + 1, slot1, slot0, WB, WA, last{});
+            stage(st + 2, slot0, slot1, WA, WB, none{});
+        } else if (st + 2 == st_end) {
+            stage(st, slot0, slot1, WA, WB, last{});
+            stage(st + 1, slot1, slot0, WB, WA, none{});
+        } else {
+            stage(st, slot0, slot1, WA, WB, none{});
+        }
     }
-    if (st + 3 == nst) {
-        stage(st, slot0, slot1, WA, WB, full{});
-        stage(st + 1, slot1, slot0, WB, WA, last{});
-        stage(st + 2, slot0, slot1, WA, WB, none{});
-    } else if (st + 2 == nst) {
-        stage(st, slot0, slot1, WA, WB, last{});
-        stage(st + 1, slot1, slot0, WB, WA, none{});
-    } else {
-        stage(st, slot0, slot1, WA, WB, none{});
+
+    if (KS > 1) {
+        prefill_split_epilogue<MTA, NBW, OM, MT>(p, acc, ssid, s_last, nt, t, ks, KS, w, c, j);
+        return;
     }
 
     // ---- epilogue: lane holds rows 4c + r of each 16-row tile, column j of each n-block
@@ -322,10 +405,10 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, uint8_t* sl
 // Tiles of c route blocks of RB16 * 16 rows: the body for height c * RB16 (c <= MT / RB16)
 template <int MT, int NBW, int OM, int RB16, int FMT, int C = 1>
 __device__ __forceinline__ void run_tile(int c, const PrefillParams& p, uint8_t* slot0, uint8_t* slot1, int* ssid,
-                                         int row0, int e, int nt) {
+                                         int* s_last, int row0, int e, int nt, int t) {
     if constexpr (C * RB16 <= MT) {
-        if (c == C) prefill_tile<C * RB16, NBW, OM, FMT>(p, slot0, slot1, ssid, row0, e, nt);
-        else run_tile<MT, NBW, OM, RB16, FMT, C + 1>(c, p, slot0, slot1, ssid, row0, e, nt);
+        if (c == C) prefill_tile<C * RB16, NBW, OM, FMT, MT>(p, slot0, slot1, ssid, s_last, row0, e, nt, t);
+        else run_tile<MT, NBW, OM, RB16, FMT, C + 1>(c, p, slot0, slot1, ssid, s_last, row0, e, nt, t);
     }
 }
 
@@ -347,6 +430,7 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<MT, NBW>())) void
     __shared__ __attribute__((aligned(16))) uint8_t slot0[SLOT];
     __shared__ __attribute__((aligned(16))) uint8_t slot1[SLOT];
     __shared__ int ssid[BM];
+    __shared__ int s_last;
 
     // ---- tile (XCD-aware order over the valid tiles only)
     int ntl;
@@ -362,24 +446,26 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<MT, NBW>())) void
         const int b0 = p.tiles[2 * t], c = p.tiles[2 * t + 1];
         const int e = p.expert_ids[b0];
         if (e < 0 || e >= p.sh.E) return;
-        run_tile<MT, NBW, OM, RB16, FMT>(c, p, slot0, slot1, ssid, b0 * RB16 * 16, e, nt);
+        run_tile<MT, NBW, OM, RB16, FMT>(c, p, slot0, slot1, ssid, &s_last, b0 * RB16 * 16, e, nt, t);
     } else {
         const int e = p.expert_ids[t];
         if (e < 0 || e >= p.sh.E) return;
-        prefill_tile<MT, NBW, OM, FMT>(p, slot0, slot1, ssid, t * BM, e, nt);
+        prefill_tile<MT, NBW, OM, FMT, MT>(p, slot0, slot1, ssid, &s_last, t * BM, e, nt, t);
     }
 }
 
 template <int MT, int NBW, int OM, int RB16>
-hipError_t launch_t(const GemmArgs& a, hipStream_t s) {
+hipError_t launch_t(const GemmArgs& a, int ks, hipStream_t s) {
     constexpr int cols = kWaves * NBW;  // n-blocks of weight columns per workgroup
     const int n_tiles = (a.sh.NB + cols - 1) / cols;
+    if (ks > 1 && (a.partials == nullptr || a.counters == nullptr)) return hipErrorInvalidValue;
     PrefillParams p{a.A,          a.a_row_div, static_cast<const uint8_t*>(a.packed), a.sh, a.sorted_ids,
-                    a.expert_ids, a.ntp,       a.R,  a.max_blocks, n_tiles, a.out, a.tiles, a.tile_count};
+                    a.expert_ids, a.ntp,       a.R,  a.max_blocks, n_tiles, a.out, a.tiles, a.tile_count,
+                    a.partials,   a.counters};
     // a multiple of the XCD count: tile t runs on workgroup (t % per_xcd) * 8 + t / per_xcd, which can reach
-    // 8 * ceil(tiles / 8) - 1.  A tile list holds at most one tile per route block.
+    // 8 * ceil(tiles / 8) - 1.  A tile list holds at most one tile per route block.  grid.y: the K slices.
     const unsigned tiles = (unsigned)a.max_blocks * (unsigned)n_tiles;
-    const dim3 grid((tiles + kXcds - 1) / kXcds * kXcds);
+    const dim3 grid((tiles + kXcds - 1) / kXcds * kXcds, (unsigned)ks);
     if (a.sh.fmt == kFmtMxfp4)
         hipLaunchKernelGGL((gemm_prefill_kernel<MT, NBW, OM, RB16, kFmtMxfp4>), grid, dim3(kThreads), 0, s, p);
     else
@@ -389,20 +475,20 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t s) {
 
 // route blocks of 16*mt rows are tiles; 32-row route blocks (rb16 = 2) are gathered into tiles of 16*mt rows
 template <int OM>
-hipError_t dispatch(const GemmArgs& a, int mt, int nbw, int rb16, hipStream_t s) {
+hipError_t dispatch(const GemmArgs& a, int mt, int nbw, int rb16, int ks, hipStream_t s) {
     if (rb16 == 2 && mt > 2) {
         if (a.tiles == nullptr || a.tile_count == nullptr || a.tile_scratch == nullptr) return hipErrorInvalidValue;
-        if (nbw == 2 && mt == 8) return launch_t<8, 2, OM, 2>(a, s);
-        if (nbw == 4 && mt == 8) return launch_t<8, 4, OM, 2>(a, s);
-        if (nbw == 2 && mt == 4) return launch_t<4, 2, OM, 2>(a, s);
-        if (nbw == 4 && mt == 4) return launch_t<4, 4, OM, 2>(a, s);
+        if (nbw == 2 && mt == 8) return launch_t<8, 2, OM, 2>(a, ks, s);
+        if (nbw == 4 && mt == 8) return launch_t<8, 4, OM, 2>(a, ks, s);
+        if (nbw == 2 && mt == 4) return launch_t<4, 2, OM, 2>(a, ks, s);
+        if (nbw == 4 && mt == 4) return launch_t<4, 4, OM, 2>(a, ks, s);
         return hipErrorInvalidValue;
     }
     if (rb16 != mt) return hipErrorInvalidValue;
-    if (nbw == 4 && mt == 4) return launch_t<4, 4, OM, 4>(a, s);
-    if (nbw == 4 && mt == 8) return launch_t<8, 4, OM, 8>(a, s);
-    if (nbw == 2 && mt == 8) return launch_t<8, 2, OM, 8>(a, s);
-    if (nbw == 2 && mt == 4) return launch_t<4, 2, OM, 4>(a, s);
+    if (nbw == 4 && mt == 4) return launch_t<4, 4, OM, 4>(a, ks, s);
+    if (nbw == 4 && mt == 8) return launch_t<8, 4, OM, 8>(a, ks, s);
+    if (nbw == 2 && mt == 8) return launch_t<8, 2, OM, 8>(a, ks, s);
+    if (nbw == 2 && mt == 4) return launch_t<4, 2, OM, 4>(a, ks, s);
     return hipErrorInvalidValue;
 }
 
@@ -416,6 +502,31 @@ bool prefill_supported(const GemmArgs& a) {
 
 int prefill_tile_rows(const w4a16_plan& p) { return p.tile_m ? p.tile_m : p.block_m; }
 
+int prefill_n_tiles(const Shape& sh, const w4a16_plan& p) {
+    const int cols = kWaves * p.n_blocks;
+    return (sh.NB + cols - 1) / cols;
+}
+
+// Tiles a grid can hold: one per route block, or with G route blocks per tile at most ceil(L/G) per expert run
+// of L blocks, which sums to at most ceil(max_blocks / G) + (experts owning a block).
+size_t prefill_max_tiles(const Shape& sh, const w4a16_plan& p, int max_blocks) {
+    const int G = prefill_tile_rows(p) / p.block_m;
+    if (G <= 1) return (size_t)max_blocks;
+    const int owners = sh.E < max_blocks ? sh.E : max_blocks;
+    return (size_t)((max_blocks + G - 1) / G) + (size_t)owners;
+}
+
+size_t prefill_partial_floats(const Shape& sh, const w4a16_plan& p, int max_blocks) {
+    if (p.kernel != W4A16_KERNEL_PREFILL || p.k_split <= 1) return 0;
+    return prefill_max_tiles(sh, p, max_blocks) * prefill_n_tiles(sh, p) * p.k_split * prefill_tile_rows(p) *
+           (size_t)(p.n_blocks * 16 * kWaves);
+}
+
+size_t prefill_counters(const Shape& sh, const w4a16_plan& p, int max_blocks) {
+    if (p.kernel != W4A16_KERNEL_PREFILL || p.k_split <= 1) return 0;
+    return prefill_max_tiles(sh, p, max_blocks) * prefill_n_tiles(sh, p);
+}
+
 hipError_t launch_gemm_prefill(const GemmArgs& a, const w4a16_plan& p, hipStream_t s) {
     if (a.max_blocks == 0) return hipSuccess;
     const int mt = prefill_tile_rows(p) / 16, rb16 = p.block_m / 16;
@@ -425,9 +536,9 @@ hipError_t launch_gemm_prefill(const GemmArgs& a, const w4a16_plan& p, hipStream
         if (err != hipSuccess) return err;
     }
     switch (a.out_mode) {
-        case kOutBf16: return dispatch<kOutBf16>(a, mt, p.n_blocks, rb16, s);
-        case kOutF32: return dispatch<kOutF32>(a, mt, p.n_blocks, rb16, s);
-        case kOutAct: return dispatch<kOutAct>(a, mt, p.n_blocks, rb16, s);
+        case kOutBf16: return dispatch<kOutBf16>(a, mt, p.n_blocks, rb16, p.k_split, s);
+        case kOutF32: return dispatch<kOutF32>(a, mt, p.n_blocks, rb16, p.k_split, s);
+        case kOutAct: return dispatch<kOutAct>(a, mt, p.n_blocks, rb16, p.k_split, s);
         default: return hipErrorInvalidValue;
     }
 }

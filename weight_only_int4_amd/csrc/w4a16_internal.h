@@ -158,6 +158,11 @@ bool prefill_supported(const GemmArgs& a);
 // Rows per prefill workgroup tile (plan.tile_m, else block_m); 32-row route blocks are gathered into taller
 // tiles through a tile list.
 int prefill_tile_rows(const w4a16_plan& p);
+// Split-K workspace of a prefill plan (k_split > 1): fp32 partial tiles and (tile, column tile) counters.
+int prefill_n_tiles(const Shape& sh, const w4a16_plan& p);
+size_t prefill_max_tiles(const Shape& sh, const w4a16_plan& p, int max_blocks);
+size_t prefill_partial_floats(const Shape& sh, const w4a16_plan& p, int max_blocks);
+size_t prefill_counters(const Shape& sh, const w4a16_plan& p, int max_blocks);
 hipError_t launch_silu_mul(const uint16_t* gu, int rows, int I, uint16_t* h, hipStream_t s);
 hipError_t launch_silu_mul_f32(const float* gu, int rows, int I, uint16_t* h, hipStream_t s);
 hipError_t launch_combine(const float* y, const float* tw, const int32_t* ids, int T, int k, int E, int H,
