@@ -22,6 +22,7 @@ bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import math
 import os
@@ -51,7 +52,7 @@ def workload_spec(name: str) -> dict:
                          "intermediate 768, %d tokens" % T)
 
     def kimi(T):
-        return dict(E=48, k=8, H=7168, I=2048, T=T, cfg=3, routes=lambda: synth.kimi_decode_routes(T),
+        return dict(E=48, k=8, H=7168, I=2048, T=T, cfg=3, global_experts=384, routes=lambda: synth.kimi_decode_routes(T),
                     desc="Kimi-K2-shaped one-GPU expert share: 48 local of 384 experts, top-8 uniform "
                          "(about 1/8 of routes local), hidden 7168, intermediate 2048, %d tokens" % T)
 
@@ -70,7 +71,7 @@ def workload_spec(name: str) -> dict:
                          "router over seeded BF16 logits, hidden 7168, intermediate 2048, %d tokens" % T)
 
     def kimi_prefill(T):
-        return dict(E=48, k=8, H=7168, I=2048, T=T, cfg=4, device_weights=True,
+        return dict(E=48, k=8, H=7168, I=2048, T=T, cfg=4, global_experts=384, device_weights=True,
                     routes=lambda: synth.kimi_prefill_routes(T),
                     desc="Kimi-K2-shaped one-GPU prefill share: 48 local of 384 experts, top-8 with Zipf(1.1) "
                          "expert popularity (about 1/8 of routes local, some local experts empty), hidden 7168, "
@@ -308,10 +309,15 @@ def main():
     idsd = torch.from_numpy(ids).to(dev)
     twd = torch.from_numpy(tw).to(dev)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    ws = w4.zeroed_workspace(w4.fused_moe_workspace_bytes(T, k, w13, w2), dev)
-    p13, p2 = w4.fused_moe_plans(T, k, w13, w2)
-    print("[bench] plans: gate_up %r, down %r; %d active experts, %d local routes; weight pool %d copies x %.1f MB"
-          % (p13, p2, len(active), Rv, ncopies, per_copy / 1e6), file=sys.stderr, flush=True)
+    # an expert-parallel share plans for the rows a local expert expects, T*k / (global experts), which is what
+    # the caller knows before routing; a whole-model layer uses the call's own estimate T*k/E
+    hint = T * k / spec["global_experts"] if "global_experts" in spec else 0.0
+    p13, p2 = w4.fused_moe_plans(T, k, w13, w2, expected_rows_per_expert=hint)
+    plans = (p13, p2)
+    ws = w4.zeroed_workspace(w4.fused_moe_workspace_bytes(T, k, w13, w2, plans), dev)
+    print("[bench] plans: gate_up %r, down %r%s; %d active experts, %d local routes; weight pool %d copies x %.1f MB"
+          % (p13, p2, " (for %.2f rows per local expert)" % hint if hint else "", len(active), Rv, ncopies,
+             per_copy / 1e6), file=sys.stderr, flush=True)
 
     lib = L.load()
     if args.copy_calibration:
@@ -321,10 +327,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def fused_args(c, stream):
+    def fused_args(c, stream, events=None):
         a, b = copies[c]
-        return (L._ptr(xd), L._ptr(idsd), L._ptr(twd), T, k, a.handle, b.handle, L._ptr(out), L._ptr(ws),
-                ws.numel(), L._stream(stream))
+        return (L._ptr(xd), L._ptr(idsd), L._ptr(twd), T, k, a.handle, b.handle, ctypes.byref(p13), ctypes.byref(p2),
+                L._ptr(out), L._ptr(ws), ws.numel(), L._stream(stream), events)
 
     def check(rc):
         if rc:
@@ -333,13 +339,13 @@ def main():
     # ---- timed steps: HIP-graph replays of the fused call, one graph per weight copy
     stream = torch.cuda.current_stream()
     for c in range(ncopies):  # eager warm-up of every copy (also initialises the library's launch state)
-        check(lib.w4a16_fused_moe(*fused_args(c, stream)))
+        check(lib.w4a16_fused_moe_planned(*fused_args(c, stream)))
     torch.cuda.synchronize()
     graphs = []
     for c in range(ncopies):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            check(lib.w4a16_fused_moe(*fused_args(c, torch.cuda.current_stream())))
+            check(lib.w4a16_fused_moe_planned(*fused_args(c, torch.cuda.current_stream())))
         graphs.append(g)
     for i in range(args.warmup):
         graphs[i % ncopies].replay()
@@ -366,11 +372,11 @@ def main():
     events = [[ev() for _ in range(NS + 1)] for _ in range(args.steps)]
     arrays = [ctypes_array(e) for e in events]  # (pointer, keep-alive array)
     for c in range(ncopies):
-        check(lib.w4a16_fused_moe_profiled(*fused_args(c, stream), arrays[0][0]))
+        check(lib.w4a16_fused_moe_planned(*fused_args(c, stream, arrays[0][0])))
     torch.cuda.synchronize()
     torch.cuda._sleep(int(2.4e9 * max(0.02, 400e-6 * args.steps)))  # ~clock rate x seconds of host enqueue
     for i in range(args.steps):
-        check(lib.w4a16_fused_moe_profiled(*fused_args(i % ncopies, stream), arrays[i][0]))
+        check(lib.w4a16_fused_moe_planned(*fused_args(i % ncopies, stream, arrays[i][0])))
     torch.cuda.synchronize()
     stage = np.array([[events[i][s].elapsed_time(events[i][s + 1]) * 1e3 for s in range(NS)] for i in range(args.steps)])
     gpu_step_us = float(np.mean([events[i][0].elapsed_time(events[i][NS]) * 1e3 for i in range(args.steps)]))

@@ -366,6 +366,31 @@ int w4a16_fused_moe_profiled(const uint16_t* x, const int32_t* topk_ids, const f
                              const w4a16_weights* w13, const w4a16_weights* w2, uint16_t* out, void* ws,
                              size_t ws_bytes, hipStream_t s, hipEvent_t* stage_events);
 
+/* The fused plans for an expected number of routed rows per expert (as in
+ * w4a16_plan_select; <= 0 means T*k/E).  An expert-parallel share of
+ * E local experts out of G receives about T*k/G rows per local expert: the
+ * default T*k/E overstates that G/E times and can pick prefill plans where
+ * the decode kernel is faster (Chord page, "TL;DR": the schedule follows
+ * routed rows per expert). */
+int w4a16_fused_moe_plans_hint(int T, int k, const w4a16_weights* w13, const w4a16_weights* w2,
+                               float expected_rows_per_expert, w4a16_plan* gate_up, w4a16_plan* down);
+
+/* w4a16_fused_moe with caller-chosen plans (for example from
+ * w4a16_fused_moe_plans_hint).  The plans must be valid on their own, share
+ * kernel and block_m (one set of routing tensors), the gate_up plan needs
+ * n_blocks >= 2, prefill plans share their tile height, and MXFP4 weights
+ * take decode plans of block_m 16 only; otherwise INVALID_ARG or
+ * UNSUPPORTED_SHAPE before anything is launched.  ws holds at least
+ * w4a16_fused_moe_planned_workspace_bytes for the same plans, zero-filled
+ * once before its first use.  stage_events: NULL or five events, as in
+ * w4a16_fused_moe_profiled. */
+int w4a16_fused_moe_planned_workspace_bytes(int T, int k, const w4a16_weights* w13, const w4a16_weights* w2,
+                                            const w4a16_plan* gate_up, const w4a16_plan* down, size_t* bytes);
+int w4a16_fused_moe_planned(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, int T, int k,
+                            const w4a16_weights* w13, const w4a16_weights* w2, const w4a16_plan* gate_up,
+                            const w4a16_plan* down, uint16_t* out, void* ws, size_t ws_bytes, hipStream_t s,
+                            hipEvent_t* stage_events);
+
 #ifdef __cplusplus
 }
 #endif

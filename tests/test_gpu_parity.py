@@ -710,6 +710,44 @@ def test_fused_moe_equals_sequence(orc, shape):
         assert np.abs(orc_bf16_to_f64(got[t]) - ref[t]).max() <= FUSED_TOL * np.abs(ref[t]).max()
 
 
+def test_fused_moe_planned_and_hint(orc):
+    """Caller-chosen plans: the call's own plans give the same bits as the plain call; an expert-parallel share
+    (48 local experts of 384, about 1/8 of routes local) gets decode plans from the rows-per-expert hint where
+    the default T*k/E estimate picks prefill, and the result still meets the fused bar; inconsistent plan pairs
+    are rejected before any launch."""
+    rng = np.random.default_rng(91)
+    T, E, k, H, I, G = 256, 48, 8, 512, 256, 384
+    x = synth.activations(rng, T, H)
+    c13, s13 = synth.codes(rng, E, 2 * I, H), synth.scales(rng, E, 2 * I, H)
+    c2, s2 = synth.codes(rng, E, H, I), synth.scales(rng, E, H, I)
+    ids = synth.uniform_topk(rng, T, G, k)
+    ids = np.where(ids < E, ids, -1).astype(np.int32)  # routes to the other experts are not local
+    tw = rng.uniform(0.1, 1.0, (T, k)).astype(np.float32)
+    w13, w2 = _pack(c13, s13), _pack(c2, s2)
+    xd, idsd, twd = u16(x), i32(ids), f32(tw)
+    own = w4.fused_moe_plans(T, k, w13, w2)
+    hinted = w4.fused_moe_plans(T, k, w13, w2, expected_rows_per_expert=T * k / G)
+    _say("default plans %r\nhinted plans %r" % (own, hinted))
+    assert own[0].kernel == w4.KERNEL_PREFILL and hinted[0].kernel == w4.KERNEL_DECODE
+    plain = bits(w4.fused_moe(xd, idsd, twd, w13, w2))
+    assert np.array_equal(bits(w4.fused_moe(xd, idsd, twd, w13, w2, plans=own)), plain)
+    got = bits(w4.fused_moe(xd, idsd, twd, w13, w2, plans=hinted))
+    orc.fused_moe(x, ids, tw, c13, s13, c2, s2)
+    ref = orc.last_out_acc
+    for t in range(T):
+        if (ids[t] < 0).all():
+            assert np.all(got[t] == 0)
+            continue
+        assert np.abs(orc_bf16_to_f64(got[t]) - ref[t]).max() <= FUSED_TOL * np.abs(ref[t]).max()
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    for bad in [(hinted[0], own[1]),                                                   # kernel and block_m differ
+                (w4.make_plan("decode", 16, 1, 4, 1), w4.make_plan("decode", 16, 4, 4, 1)),  # gate_up n_blocks 1
+                (w4.make_plan("prefill", 32, 2, 4, 1, 128), w4.make_plan("prefill", 32, 2, 4, 1, 64))]:  # tiles
+        with pytest.raises(w4.W4A16Error) as ei:
+            w4.fused_moe(xd, idsd, twd, w13, w2, out=out, plans=bad)
+        assert ei.value.code == -1
+
+
 @pytest.mark.parametrize("shape", [(2, 48, 8, 512, 256), (2, 48, 8, 512, 2048), (32, 64, 4, 512, 256)],
                          ids=["T2-E48-gate-up-splitK", "T2-E48-both-splitK", "T32-E64-decode"])
 def test_fused_moe_graph_replays(orc, shape):

@@ -780,19 +780,60 @@ static FusedLayout fused_full_layout(int T, int k, const w4a16_weights* w13, con
     return fused_layout(T, k, E, H, I, p13.block_m, *counter_bytes + partial_bytes, tile_bytes);
 }
 
-int w4a16_fused_moe_workspace_bytes(int T, int k, const w4a16_weights* w13, const w4a16_weights* w2, size_t* bytes) {
+// The two weight handles form an expert MLP and the two plans can run it: each valid on its own, one route block
+// height (one set of routing tensors), one kernel family, n-blocks in pairs for the gate_up activation, one tile
+// height for prefill, and decode plans of MXFP4 weights on 16-row blocks.
+static int check_fused_plans(int T, int k, const w4a16_weights* w13, const w4a16_weights* w2,
+                             const w4a16_plan* p13, const w4a16_plan* p2, const char* what) {
+    int rc = check_handle(w13, what);
+    if (rc) return rc;
+    rc = check_handle(w2, what);
+    if (rc) return rc;
+    if (T < 0 || k < 1) return fail(W4A16_INVALID_ARG, "%s: T=%d k=%d", what, T, k);
+    const int E = w13->shape.E, H = w13->shape.K, I = w2->shape.K;
+    if (w2->shape.E != E || w13->shape.N != 2 * I || w2->shape.N != H)
+        return fail(W4A16_LAYOUT_MISMATCH, "%s: w13 is [%d,%d,%d] and w2 is [%d,%d,%d]; need [E,2I,H] and [E,H,I]", what,
+                    w13->shape.E, w13->shape.N, w13->shape.K, w2->shape.E, w2->shape.N, w2->shape.K);
+    if (E > W4A16_MAX_EXPERTS) return fail(W4A16_UNSUPPORTED_SHAPE, "%s: E=%d exceeds %d", what, E, W4A16_MAX_EXPERTS);
+    if (!p13 || !p2) return fail(W4A16_INVALID_ARG, "%s: plan is NULL", what);
+    rc = validate_plan(p13, what);
+    if (!rc) rc = validate_plan(p2, what);
+    if (rc) return rc;
+    if (p13->kernel != p2->kernel || p13->block_m != p2->block_m)
+        return fail(W4A16_INVALID_ARG, "%s: gate_up and down plans must share kernel and block_m (one routing)", what);
+    if (p13->n_blocks < 2) return fail(W4A16_INVALID_ARG, "%s: gate_up plan needs n_blocks >= 2", what);
+    if (p13->kernel == W4A16_KERNEL_PREFILL && prefill_tile_rows(*p13) != prefill_tile_rows(*p2))
+        return fail(W4A16_INVALID_ARG, "%s: prefill plans must share tile_m (one tile list)", what);
+    rc = check_format_plan(what, w13, *p13);
+    if (!rc) rc = check_format_plan(what, w2, *p2);
+    return rc;
+}
+
+int w4a16_fused_moe_planned_workspace_bytes(int T, int k, const w4a16_weights* w13, const w4a16_weights* w2,
+                                            const w4a16_plan* gate_up, const w4a16_plan* down, size_t* bytes) {
     const char* what = "w4a16_fused_moe_workspace_bytes";
     if (!bytes) return fail(W4A16_INVALID_ARG, "%s: bytes is NULL", what);
+    int rc = check_fused_plans(T, k, w13, w2, gate_up, down, what);
+    if (rc) return rc;
+    size_t cb;
+    *bytes = fused_full_layout(T, k, w13, w2, *gate_up, *down, &cb).total;
+    return ok();
+}
+
+int w4a16_fused_moe_workspace_bytes(int T, int k, const w4a16_weights* w13, const w4a16_weights* w2, size_t* bytes) {
     w4a16_plan p13, p2;
     int rc = w4a16_fused_moe_plans(T, k, w13, w2, &p13, &p2);
     if (rc) return rc;
-    size_t cb;
-    *bytes = fused_full_layout(T, k, w13, w2, p13, p2, &cb).total;
-    return ok();
+    return w4a16_fused_moe_planned_workspace_bytes(T, k, w13, w2, &p13, &p2, bytes);
 }
 
 int w4a16_fused_moe_plans(int T, int k, const w4a16_weights* w13, const w4a16_weights* w2, w4a16_plan* gate_up,
                           w4a16_plan* down) {
+    return w4a16_fused_moe_plans_hint(T, k, w13, w2, 0.f, gate_up, down);
+}
+
+int w4a16_fused_moe_plans_hint(int T, int k, const w4a16_weights* w13, const w4a16_weights* w2,
+                               float expected_rows_per_expert, w4a16_plan* gate_up, w4a16_plan* down) {
     const char* what = "w4a16_fused_moe_plans";
     int rc = check_handle(w13, what);
     if (rc) return rc;
@@ -801,9 +842,9 @@ int w4a16_fused_moe_plans(int T, int k, const w4a16_weights* w13, const w4a16_we
     if (!gate_up || !down || k < 1 || T < 0) return fail(W4A16_INVALID_ARG, "%s: bad argument", what);
     const int E = w13->shape.E, H = w13->shape.K, I = w2->shape.K;
     w4a16_plan p13, p2;
-    rc = w4a16_plan_select(T, k, E, 2 * I, H, 0.f, &p13);
+    rc = w4a16_plan_select(T, k, E, 2 * I, H, expected_rows_per_expert, &p13);
     if (rc) return rc;
-    rc = w4a16_plan_select(T, k, E, H, I, 0.f, &p2);
+    rc = w4a16_plan_select(T, k, E, H, I, expected_rows_per_expert, &p2);
     if (rc) return rc;
     if (p13.n_blocks < 2) p13.n_blocks = 2;  // the activation epilogue pairs a gate and an up n-block
     p2.block_m = p13.block_m;  // both projections share one set of routing tensors
@@ -832,31 +873,29 @@ int w4a16_fused_moe(const uint16_t* x, const int32_t* topk_ids, const float* top
 int w4a16_fused_moe_profiled(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, int T, int k,
                              const w4a16_weights* w13, const w4a16_weights* w2, uint16_t* out, void* ws,
                              size_t ws_bytes, hipStream_t s, hipEvent_t* ev) {
+    w4a16_plan p13, p2;
+    int rc = w4a16_fused_moe_plans(T, k, w13, w2, &p13, &p2);
+    if (rc) return rc;
+    return w4a16_fused_moe_planned(x, topk_ids, topk_w, T, k, w13, w2, &p13, &p2, out, ws, ws_bytes, s, ev);
+}
+
+int w4a16_fused_moe_planned(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, int T, int k,
+                            const w4a16_weights* w13, const w4a16_weights* w2, const w4a16_plan* gate_up,
+                            const w4a16_plan* down, uint16_t* out, void* ws, size_t ws_bytes, hipStream_t s,
+                            hipEvent_t* ev) {
     const char* what = "w4a16_fused_moe";
-    int rc = check_handle(w13, what);
+    int rc = check_fused_plans(T, k, w13, w2, gate_up, down, what);
     if (rc) return rc;
-    rc = check_handle(w2, what);
-    if (rc) return rc;
-    if (T < 0 || k < 1) return fail(W4A16_INVALID_ARG, "%s: T=%d k=%d", what, T, k);
     const int E = w13->shape.E, H = w13->shape.K, I = w2->shape.K;
-    if (w2->shape.E != E || w13->shape.N != 2 * I || w2->shape.N != H)
-        return fail(W4A16_LAYOUT_MISMATCH, "%s: w13 is [%d,%d,%d] and w2 is [%d,%d,%d]; need [E,2I,H] and [E,H,I]", what,
-                    w13->shape.E, w13->shape.N, w13->shape.K, w2->shape.E, w2->shape.N, w2->shape.K);
-    if (E > W4A16_MAX_EXPERTS) return fail(W4A16_UNSUPPORTED_SHAPE, "%s: E=%d exceeds %d", what, E, W4A16_MAX_EXPERTS);
     if (T == 0) return ok();
     if (!x || !topk_ids || !topk_w || !out) return fail(W4A16_INVALID_ARG, "%s: NULL pointer argument", what);
     if (!aligned16(x) || ((uintptr_t)out & 3u)) return fail(W4A16_INVALID_ARG, "%s: x must be 16-byte aligned", what);
-    size_t need = 0;
-    rc = w4a16_fused_moe_workspace_bytes(T, k, w13, w2, &need);
-    if (rc) return rc;
+    const w4a16_plan p13 = *gate_up, p2 = *down;
+    size_t counter_bytes;
+    const size_t need = fused_full_layout(T, k, w13, w2, p13, p2, &counter_bytes).total;
     if (!ws || ws_bytes < need) return fail(W4A16_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, needs %zu", what, ws_bytes, need);
     if (!aligned16(ws)) return fail(W4A16_INVALID_ARG, "%s: workspace must be 16-byte aligned", what);
 
-    w4a16_plan p13, p2;
-    rc = w4a16_fused_moe_plans(T, k, w13, w2, &p13, &p2);
-    if (rc) return rc;
-
-    size_t counter_bytes;
     const FusedLayout f = fused_full_layout(T, k, w13, w2, p13, p2, &counter_bytes);
     char* base = static_cast<char*>(ws);
     int32_t* sorted_ids = reinterpret_cast<int32_t*>(base + f.off_sorted);

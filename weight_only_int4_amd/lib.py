@@ -80,6 +80,11 @@ _SIGS = {
     "w4a16_fused_moe_workspace_bytes": (_I, [_I, _I, _P, _P, ctypes.POINTER(_SZ)]),
     "w4a16_fused_moe": (_I, [_P, _P, _P, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "w4a16_fused_moe_profiled": (_I, [_P, _P, _P, _I, _I, _P, _P, _P, _P, _SZ, _P, _P]),
+    "w4a16_fused_moe_plans_hint": (_I, [_I, _I, _P, _P, ctypes.c_float, ctypes.POINTER(Plan), ctypes.POINTER(Plan)]),
+    "w4a16_fused_moe_planned_workspace_bytes": (_I, [_I, _I, _P, _P, ctypes.POINTER(Plan), ctypes.POINTER(Plan),
+                                                     ctypes.POINTER(_SZ)]),
+    "w4a16_fused_moe_planned": (_I, [_P, _P, _P, _I, _I, _P, _P, ctypes.POINTER(Plan), ctypes.POINTER(Plan), _P, _P,
+                                     _SZ, _P, _P]),
 }
 
 _lib = None
@@ -397,15 +402,25 @@ def moe_combine(y: torch.Tensor, topk_w: torch.Tensor, topk_ids: torch.Tensor, E
     return out
 
 
-def fused_moe_plans(T: int, k: int, w13: Weights, w2: Weights):
+def fused_moe_plans(T: int, k: int, w13: Weights, w2: Weights, expected_rows_per_expert: float = 0.0):
+    """The fused call's plans; ``expected_rows_per_expert`` > 0 replaces the default T*k/E estimate."""
     p13, p2 = Plan(), Plan()
-    _check(load().w4a16_fused_moe_plans(T, k, w13.handle, w2.handle, ctypes.byref(p13), ctypes.byref(p2)))
+    if expected_rows_per_expert > 0:
+        _check(load().w4a16_fused_moe_plans_hint(T, k, w13.handle, w2.handle, float(expected_rows_per_expert),
+                                                 ctypes.byref(p13), ctypes.byref(p2)))
+    else:
+        _check(load().w4a16_fused_moe_plans(T, k, w13.handle, w2.handle, ctypes.byref(p13), ctypes.byref(p2)))
     return p13, p2
 
 
-def fused_moe_workspace_bytes(T: int, k: int, w13: Weights, w2: Weights) -> int:
+def fused_moe_workspace_bytes(T: int, k: int, w13: Weights, w2: Weights, plans=None) -> int:
+    """Workspace of the fused call, for its own plans or for ``plans`` = (gate_up, down)."""
     out = _SZ(0)
-    _check(load().w4a16_fused_moe_workspace_bytes(T, k, w13.handle, w2.handle, ctypes.byref(out)))
+    if plans is None:
+        _check(load().w4a16_fused_moe_workspace_bytes(T, k, w13.handle, w2.handle, ctypes.byref(out)))
+    else:
+        _check(load().w4a16_fused_moe_planned_workspace_bytes(T, k, w13.handle, w2.handle, ctypes.byref(plans[0]),
+                                                              ctypes.byref(plans[1]), ctypes.byref(out)))
     return out.value
 
 
@@ -416,20 +431,27 @@ FUSED_STAGE_EVENTS = len(FUSED_STAGES) + 1
 
 def fused_moe(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, w13: Weights, w2: Weights,
               out: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None,
-              stage_events=None) -> torch.Tensor:
-    """Fused expert MLP.  ``stage_events``: FUSED_STAGE_EVENTS torch.cuda.Event objects (timing) or None."""
+              stage_events=None, plans=None) -> torch.Tensor:
+    """Fused expert MLP.  ``stage_events``: FUSED_STAGE_EVENTS torch.cuda.Event objects (timing) or None;
+    ``plans``: (gate_up, down) plans to use instead of the call's own (w4a16_fused_moe_planned)."""
     T, k = topk_ids.shape
     if out is None:
         out = torch.empty((T, w2.N), dtype=torch.bfloat16, device=x.device)
     if ws is None:
-        ws = zeroed_workspace(fused_moe_workspace_bytes(T, k, w13, w2), x.device)
-    args = (_ptr(x) if T else None, _ptr(topk_ids) if T else None, _ptr(topk_w) if T else None, T, k, w13.handle,
-            w2.handle, _ptr(out) if T else None, _ptr(ws), ws.numel(), _stream(stream))
-    if stage_events is None:
-        _check(load().w4a16_fused_moe(*args))
-    else:
+        ws = zeroed_workspace(fused_moe_workspace_bytes(T, k, w13, w2, plans), x.device)
+    ev = None
+    if stage_events is not None:
         if len(stage_events) != FUSED_STAGE_EVENTS:
             raise ValueError("stage_events needs %d events" % FUSED_STAGE_EVENTS)
         arr = (ctypes.c_void_p * FUSED_STAGE_EVENTS)(*[ctypes.c_void_p(e.cuda_event) for e in stage_events])
-        _check(load().w4a16_fused_moe_profiled(*args, ctypes.cast(arr, ctypes.c_void_p)))
+        ev = ctypes.cast(arr, ctypes.c_void_p)
+    head = (_ptr(x) if T else None, _ptr(topk_ids) if T else None, _ptr(topk_w) if T else None, T, k, w13.handle,
+            w2.handle)
+    tail = (_ptr(out) if T else None, _ptr(ws), ws.numel(), _stream(stream))
+    if plans is not None:
+        _check(load().w4a16_fused_moe_planned(*head, ctypes.byref(plans[0]), ctypes.byref(plans[1]), *tail, ev))
+    elif ev is None:
+        _check(load().w4a16_fused_moe(*head, *tail))
+    else:
+        _check(load().w4a16_fused_moe_profiled(*head, *tail, ev))
     return out
