@@ -269,3 +269,30 @@ def test_deepseek_fused_mxfp4_t4096(orc):
     assert worst <= FUSED_TOL
     del w13, w2, c13, s13, c2, s2
     torch.cuda.empty_cache()
+
+
+def test_kimi_decode_share_fused_bench_workload(orc, kimi_weights):
+    """The Kimi-K2 share's fused step as the benchmark runs it (256 tokens, about 1/8 of routes local, plans for
+    T*k/384 rows per local expert), on sampled tokens with at least one local route."""
+    codes13, scales13 = kimi_weights
+    c2, s2 = synth.expert_weights(3, 48, 7168, 2048, salt=2)
+    T, k, E, G = 256, 8, 48, 384
+    ids = synth.kimi_decode_routes(T)
+    rng = synth.rng_for(3, 7)
+    x = synth.activations(rng, T, 7168)
+    tw = rng.uniform(0.1, 1.0, (T, k)).astype(np.float32)
+    tw /= tw.sum(axis=1, keepdims=True)
+    w13 = w4.pack_weights(torch.from_numpy(codes13).cuda(), u16(scales13))
+    w2 = w4.pack_weights(torch.from_numpy(c2).cuda(), u16(s2))
+    plans = w4.fused_moe_plans(T, k, w13, w2, expected_rows_per_expert=T * k / G)
+    _say("kimi T%d fused plans %r" % (T, plans))
+    got = bits(w4.fused_moe(u16(x), i32(ids), f32(tw), w13, w2, plans=plans))
+    local = ((ids >= 0) & (ids < E)).any(axis=1)
+    assert np.all(got[~local] == 0), "tokens without a local route must be zero"
+    sample = np.nonzero(local)[0][::23][:8]
+    orc.fused_moe(x[sample], ids[sample], tw[sample], codes13, scales13, c2, s2)
+    ref = orc.last_out_acc
+    g = (got[sample].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    worst = max(np.abs(g[i] - ref[i]).max() / np.abs(ref[i]).max() for i in range(len(sample)))
+    _say("  kimi T%d fused worst ratio %.2e over %d tokens" % (T, worst, len(sample)))
+    assert worst <= FUSED_TOL
