@@ -268,6 +268,36 @@ def test_gemm_prefill_split_k(orc, plan_args):
         assert np.array_equal(bits(out), first), "replay %d differs" % rep
 
 
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+@pytest.mark.parametrize("plan_args", [("decode", 16, 4, 4, 1), ("decode", 16, 2, 4, 3), ("prefill", 64, 2, 4, 1),
+                                       ("prefill", 32, 2, 4, 1, 128), ("prefill", 32, 4, 4, 2, 64)],
+                         ids=PLAN_ID)
+def test_gemm_many_experts_ragged(orc, plan_args, fmt):
+    """512 experts with a skewed load (a few hot experts, many with one or two rows, many empty), N = 72 (a
+    ragged last n-block) and K = 1056 (33 groups: a ragged last stage)."""
+    if fmt == "mxfp4" and plan_args[0] == "decode" and plan_args[1] != 16:
+        pytest.skip("MXFP4 decode plans use 16-row blocks")
+    _say("gemm many experts %s %s" % (fmt, plan_args))
+    rng = np.random.default_rng(4100)
+    T, E, k, N, K = 300, 512, 8, 72, 1056
+    x = synth.activations(rng, T, K)
+    codes = synth.codes(rng, E, N, K)
+    scales = synth.mxfp4_scales(rng, E, N, K) if fmt == "mxfp4" else synth.scales(rng, E, N, K)
+    popularity = 1.0 / (1.0 + np.arange(E)) ** 1.2
+    ids = np.stack([rng.choice(E, size=k, replace=False, p=popularity / popularity.sum()) for _ in range(T)])
+    ids = ids.astype(np.int32)
+    w = _pack_mx(codes, scales) if fmt == "mxfp4" else _pack(codes, scales)
+    plan = w4.make_plan(*plan_args)
+    route = w4.route_prep(i32(ids), E, plan.block_m)
+    out = poison_bf16(T * k, N)
+    w4.grouped_gemm(u16(x), k, w, route, plan, out=out)
+    acc, _ = orc.grouped_gemm(x, k, codes, scales, ids, acc64=True, fmt=fmt)
+    counts = np.bincount(ids.reshape(-1), minlength=E)
+    assert counts.max() > 100 and (counts == 0).sum() > 50 and (counts == 1).sum() > 10
+    worst = check_gemm(bits(out), acc, ids, E, label="many experts %s" % fmt)
+    _say("  worst ratio %.2e" % worst)
+
+
 def test_gemm_zero_tokens():
     case = synth.tiny_case()
     w = _pack(case.codes, case.scales)
