@@ -74,15 +74,6 @@ __device__ __forceinline__ float group_scale(u32x4 sc, int g) {
     return __uint_as_float((g & 1) ? (word & 0xFFFF0000u) : (word << 16));
 }
 
-// Hides a value from the optimiser (no instruction is emitted).  Used on the
-// byte-masked code words below: otherwise LLVM folds "(w & 0x0F0F0F0F) then
-// byte i" into a separate shift-and-mask per code, losing the one-instruction
-// byte conversions v_cvt_f32_ubyte1..3.
-__device__ __forceinline__ uint32_t opaque_u32(uint32_t x) {
-    __asm__("" : "+v"(x));
-    return x;
-}
-
 // Two floats to a packed pair of BF16 values, round to nearest even (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -91,29 +82,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
-// Eight fully dequantised weights bf16((q - 8) * s) of one packed word, in 23
-// VALU operations: two byte masks split the word into the codes 0, 4, 1, 5
-// and 2, 6, 3, 7 (one per byte), v_cvt_f32_ubyte0..3 convert them, one fused
-// multiply-add q * s + (-8 s) forms (q - 8) * s exactly (the product needs at
-// most 12 significant bits), and each pair is rounded once to BF16 (round to
-// nearest even).
-__device__ __forceinline__ bf16x8 dequant8(uint32_t w, float s, float neg8s) {
-    const uint32_t lo = opaque_u32(w & 0x0F0F0F0Fu);         // codes 0, 4, 1, 5 in bytes 0..3
-    const uint32_t hi = opaque_u32((w >> 4) & 0x0F0F0F0Fu);  // codes 2, 6, 3, 7 in bytes 0..3
-    const float q0 = (float)(lo & 0xFFu), q4 = (float)((lo >> 8) & 0xFFu);
-    const float q1 = (float)((lo >> 16) & 0xFFu), q5 = (float)(lo >> 24);
-    const float q2 = (float)(hi & 0xFFu), q6 = (float)((hi >> 8) & 0xFFu);
-    const float q3 = (float)((hi >> 16) & 0xFFu), q7 = (float)(hi >> 24);
-    u32x4 v;
-    v.x = pack_bf16x2(__builtin_fmaf(q0, s, neg8s), __builtin_fmaf(q1, s, neg8s));
-    v.y = pack_bf16x2(__builtin_fmaf(q2, s, neg8s), __builtin_fmaf(q3, s, neg8s));
-    v.z = pack_bf16x2(__builtin_fmaf(q4, s, neg8s), __builtin_fmaf(q5, s, neg8s));
-    v.w = pack_bf16x2(__builtin_fmaf(q6, s, neg8s), __builtin_fmaf(q7, s, neg8s));
-    return __builtin_bit_cast(bf16x8, v);
-}
-
-// The same eight weights bf16((q - 8) * s) with the code-to-float conversion
-// folded into the multiply-add, in 17 VALU operations: one shift and four
+// Eight fully dequantised weights bf16((q - 8) * s) of one packed word, with the
+// code-to-float conversion folded into the multiply-add, in 17 VALU operations: one shift and four
 // AND-ORs place each code in a binary16 bit pattern whose value is affine in
 // the code (0x6400 | q is 1024 + q for a code in bits 0..3 of a half,
 // 0x5400 | (q << 4) is 64 + q for a code in bits 4..7), one mixed-precision

@@ -28,14 +28,16 @@
 //  * Each wavefront owns NBW n-blocks across all BM rows.  Its packed weights
 //    for the next stage are in flight in a second register set (buffer loads,
 //    scalar stage offsets) while the current stage is multiplied.  Every
-//    weight is dequantised once per workgroup, to bf16((q - 8) * s) (one FMA,
-//    exact, then one rounding), and feeds MT MFMAs (v_mfma_f32_16x16x32_bf16):
+//    weight is dequantised once per workgroup, to bf16((q - 8) * s) (one
+//    mixed-precision FMA on a binary16 pattern of the code, exact, then one
+//    rounding; 17 operations per 8 weights and 3 per scale group), and feeds
+//    MT MFMAs (v_mfma_f32_16x16x32_bf16):
 //    a taller M tile amortises the INT4 conversion (Chord page, "Grouped SM90
 //    kernels").  The dequantisation of group g+1 is independent of the MFMAs
 //    of group g, so the two interleave.
 //  * MXFP4 weights (FMT = kFmtMxfp4) convert in hardware: two E2M1 codes and
 //    their E8M0 scale to exact BF16 per instruction, 4 instructions per 8
-//    weights instead of about 23.
+//    weights instead of about 20.
 //  * At most 256 registers per lane for the 128x32 and 64x64 wavefront tiles,
 //    so two wavefronts share each SIMD: one issues VALU dequantisation while
 //    the other's MFMAs run.
@@ -46,10 +48,6 @@
 
 namespace w4a16 {
 namespace {
-
-#ifndef W4A16_PREFILL_MIX
-#define W4A16_PREFILL_MIX 1
-#endif
 
 constexpr int KT = 128;        // k per stage (4 scale groups, half a superblock)
 constexpr int kThreads = 256;  // four wavefronts, each owning its own columns
@@ -272,9 +270,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, uint8_t* sl
 #pragma unroll
         for (int q = 0; q < NBW; ++q) acc[mt][q] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-#if W4A16_PREFILL_MIX
     const MixConsts mixk = mix_consts();
-#endif
     auto dequant_group = [&](const WStage<NBW>& W, int g, bf16x8* wf) {
         if constexpr (MX) {
 #pragma unroll
@@ -285,11 +281,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, uint8_t* sl
         for (int q = 0; q < NBW; ++q) {
             const uint32_t word = W.sc[q][g >> 1];
             const float s = __uint_as_float((g & 1) ? (word & 0xFFFF0000u) : (word << 16));
-#if W4A16_PREFILL_MIX
             wf[q] = dequant8_mix(W.cw[q][g], s, -1032.0f * s, -72.0f * s, mixk);
-#else
-            wf[q] = dequant8(W.cw[q][g], s, -8.0f * s);
-#endif
         }
     };
     // multiply the stage in LDS slot `slot` with the weights W.  A ragged last stage computes its padding groups
