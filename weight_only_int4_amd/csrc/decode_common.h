@@ -23,6 +23,8 @@ struct DecodeParams {
     void* out;
     float* partials;      // [max_blocks][n_tiles][KS][BM][COLS] when KS > 1
     unsigned* counters;   // [max_blocks][n_tiles] when KS > 1, zero between calls
+    const int32_t* ntp = nullptr;  // num_tokens_padded (device) or NULL: bounds the valid route blocks
+    int route_blocks = 0;          // route blocks of the grid (grid.x may be rounded up)
 };
 
 // n-block of weight slot q of wavefront w (see kOutAct for the split of slots between gate and up rows);
@@ -46,7 +48,8 @@ __device__ __forceinline__ int slot_nblock(const Shape& sh, int wave_global, int
 // the last to arrive adds the KS partials in slice order, writes the output and resets the counter.
 template <int MT, int NBW, int OM>
 __device__ __forceinline__ void decode_epilogue(const DecodeParams& p, const f32x4 (&acc)[MT][NBW], const int* ssid,
-                                                int* s_last, int wave_global, int w, int c, int j) {
+                                                int* s_last, int b, int nt, int n_tiles, int wave_global, int w,
+                                                int c, int j) {
     constexpr int BM = 16 * MT;
     constexpr int COLS = NBW * 16 * kWaves;  // weight columns of the workgroup
     const Shape& sh = p.sh;
@@ -84,7 +87,7 @@ __device__ __forceinline__ void decode_epilogue(const DecodeParams& p, const f32
     }
 
     // split K: publish the partial tile, the last workgroup of the tile reduces in ks order
-    const size_t tile = (size_t)blockIdx.x * gridDim.y + blockIdx.y;
+    const size_t tile = (size_t)b * n_tiles + nt;
     float* mine = p.partials + (tile * KS + ks) * (size_t)(BM * COLS);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -118,14 +121,14 @@ __device__ __forceinline__ void decode_epilogue(const DecodeParams& p, const f32
             const int m = idx / OCOLS, oc = idx % OCOLS;
             const int sid = ssid[m];
             const int ww = oc / (16 * HB), q = (oc / 16) % HB, jj = oc % 16;
-            const int n = ((blockIdx.y * kWaves + ww) * HB + q) * 16 + jj;
+            const int n = ((nt * kWaves + ww) * HB + q) * 16 + jj;
             if (sid < 0 || n >= NO) continue;
             const int gcol = (ww * NBW + q) * 16 + jj;
             const float g = reduce(m * COLS + gcol), u = reduce(m * COLS + gcol + HB * 16);
             static_cast<uint16_t*>(p.out)[(size_t)sid * NO + n] = f32_to_bf16_bits(silu_mul(g, u));
         }
     } else {
-        const int n_base = blockIdx.y * COLS;
+        const int n_base = nt * COLS;
         for (int idx = threadIdx.x; idx < BM * COLS; idx += kDecodeThreads) {
             const int m = idx / COLS, col = idx % COLS;
             const int sid = ssid[m];

@@ -5,7 +5,10 @@
 // Design (MI355X-first):
 //  * Grid, dequantisation and epilogue as in the LDS-staged decode kernel
 //    (gemm_decode.hip): one workgroup per (route block, 64*NBW columns, K
-//    slice), four independent wavefronts with disjoint columns, the raw codes
+//    slice), the (route block, column tile) pairs laid over the XCDs in
+//    contiguous runs so that each XCD's L2 holds only its own route blocks'
+//    activation rows (Kimi-K2 share at 256 tokens: 76% of HBM instead of
+//    65%), four independent wavefronts with disjoint columns, the raw codes
 //    fed to the MFMA as BF16 128 + q with a -136 * sum(x) correction, one FMA
 //    per output and group for the scale.
 //  * Each wavefront keeps a ring of D register sets; per stage of 128 k a set
@@ -49,6 +52,7 @@ struct RegStage {
 #ifndef W4A16_DECODE_REG_WAVES
 #define W4A16_DECODE_REG_WAVES 1
 #endif
+constexpr int kXcds = 8;  // XCDs of the chip; workgroup i runs on XCD i % 8
 
 template <int NBW, int D, int OM, int FMT>
 __global__ __launch_bounds__(kDecodeThreads, W4A16_DECODE_REG_WAVES) void gemm_decode_reg_kernel(DecodeParams p) {
@@ -59,7 +63,18 @@ __global__ __launch_bounds__(kDecodeThreads, W4A16_DECODE_REG_WAVES) void gemm_d
     __shared__ int ssid[16];
     __shared__ int s_last;
 
-    const int b = blockIdx.x;
+    // (route block, column tile) of this workgroup.  XCD-aware: consecutive workgroup ids go to the eight XCDs
+    // in turn, so id -> (XCD, position) is remapped to give every XCD a contiguous run of the valid (route
+    // block, column tile) pairs, route block major; an XCD then gathers the activation rows of its own route
+    // blocks only, and its L2 holds them while its weight streams pass through.
+    const int n_tiles = gridDim.y;
+    const int valid = p.ntp ? min(__builtin_amdgcn_readfirstlane(*p.ntp) / 16, p.route_blocks) : p.route_blocks;
+    const int V = valid * n_tiles;
+    const int id = blockIdx.x + gridDim.x * blockIdx.y;  // gridDim.x * gridDim.y is a multiple of 8
+    const int per_xcd = (V + kXcds - 1) / kXcds;
+    const int pos = id / kXcds, slot = (id % kXcds) * per_xcd + pos;
+    if (pos >= per_xcd || slot >= V) return;
+    const int b = slot / n_tiles, nt = slot % n_tiles;
     const int e = p.expert_ids[b];
     if (e < 0 || e >= p.sh.E) return;  // unowned block (or ids from a larger expert count)
     const Shape sh = p.sh;
@@ -67,7 +82,7 @@ __global__ __launch_bounds__(kDecodeThreads, W4A16_DECODE_REG_WAVES) void gemm_d
     // the wavefront index is uniform: as a scalar it keeps every per-stage offset in scalar registers
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), L = threadIdx.x & 63;
     const int c = L >> 4, j = L & 15;
-    const int wave_global = blockIdx.y * kWaves + w;
+    const int wave_global = nt * kWaves + w;
     const int KS = gridDim.z, ks = blockIdx.z;
     const int nst = (sh.G + 3) / 4;
     const int st_begin = (int)((long)ks * nst / KS), st_end = (int)((long)(ks + 1) * nst / KS);
@@ -211,7 +226,7 @@ __global__ __launch_bounds__(kDecodeThreads, W4A16_DECODE_REG_WAVES) void gemm_d
     }
 
     __syncthreads();  // ssid is complete
-    decode_epilogue<1, NBW, OM>(p, acc, ssid, &s_last, wave_global, w, c, j);
+    decode_epilogue<1, NBW, OM>(p, acc, ssid, &s_last, b, nt, n_tiles, wave_global, w, c, j);
 }
 
 #ifndef W4A16_DECODE_REG_DEPTH
@@ -225,7 +240,11 @@ template <int NBW, int OM>
 hipError_t launch_reg(const GemmArgs& a, const w4a16_plan& pl, hipStream_t s) {
     DecodeParams p{a.A, a.a_row_div, static_cast<const uint8_t*>(a.packed), a.sh, a.sorted_ids, a.expert_ids, a.R,
                    a.out, a.partials, a.counters};
-    const dim3 grid(a.max_blocks, decode_n_tiles(a.sh, pl), pl.k_split);
+    p.ntp = a.ntp;
+    p.route_blocks = a.max_blocks;
+    // grid.x a multiple of the XCD count, so that the remap above is onto the valid pairs
+    const unsigned gx = (unsigned)(a.max_blocks + kXcds - 1) / kXcds * kXcds;
+    const dim3 grid(gx, decode_n_tiles(a.sh, pl), pl.k_split);
     constexpr int D = W4A16_DECODE_REG_DEPTH >= 2 ? W4A16_DECODE_REG_DEPTH : 2;  // 0 switches the kernel off
     constexpr int DMX = W4A16_DECODE_REG_DEPTH_MX >= 2 ? W4A16_DECODE_REG_DEPTH_MX : 2;
     if (a.sh.fmt == kFmtMxfp4)
