@@ -223,8 +223,8 @@ int w4a16_plan_select(int T, int k, int E, int N, int K, float expected_rows_per
  *   out        device BF16 bits [R, N]; rows of invalid routes untouched
  *   ws         workspace of w4a16_gemm_workspace_bytes (may be NULL if 0).  A
  *              prefill plan with tile_m above block_m builds its tile list
- *              there.  A
- *              plan with k_split > 1 keeps per-tile arrival counters in it:
+ *              there.  A plan with k_split > 1 (decode or prefill) keeps
+ *              partial tiles and per-tile arrival counters in it:
  *              the workspace must be zero-filled once before its first use,
  *              and every call leaves the counters at zero again.  Calls that
  *              share a workspace must not run concurrently.
