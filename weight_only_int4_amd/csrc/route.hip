@@ -19,12 +19,17 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
+#ifndef W4A16_ROUTE_SMALL_THREADS
+#define W4A16_ROUTE_SMALL_THREADS 512
+#endif
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // Exclusive scan of one int per thread across the workgroup; returns the
 // thread's exclusive prefix and writes the total to *total (all threads).
+template <int NT = kThreads>
 __device__ int block_exclusive_scan(int v, int* wave_tot, int* total) {
+    constexpr int kW = NT / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int incl = v;
 #pragma unroll
@@ -36,22 +41,23 @@ __device__ int block_exclusive_scan(int v, int* wave_tot, int* total) {
     __syncthreads();
     if (threadIdx.x == 0) {
         int run = 0;
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = 0; w < kW; ++w) {
             const int t = wave_tot[w];
             wave_tot[w] = run;
             run += t;
         }
-        wave_tot[kWaves] = run;
+        wave_tot[kW] = run;
     }
     __syncthreads();
     const int excl = wave_tot[wave] + incl - v;
-    *total = wave_tot[kWaves];
+    *total = wave_tot[kW];
     __syncthreads();
     return excl;
 }
 
-// Shared memory layout (ints): cnt[E] | pad_off[E+1] | base[E] | wave_cnt[kWaves][E] | wave_tot[kWaves+1]
-__global__ __launch_bounds__(kThreads) void route_prep_kernel(const int32_t* __restrict__ ids, int R, int E, int BM,
+// Shared memory layout (ints): cnt[E] | pad_off[E+1] | base[E] | wave_cnt[(NT / 64)][E] | wave_tot[(NT / 64)+1]
+template <int NT>
+__global__ __launch_bounds__(NT) void route_prep_kernel(const int32_t* __restrict__ ids, int R, int E, int BM,
                                                               int max_padded, int max_blocks,
                                                               int32_t* __restrict__ sorted_ids,
                                                               int32_t* __restrict__ expert_ids,
@@ -63,24 +69,24 @@ __global__ __launch_bounds__(kThreads) void route_prep_kernel(const int32_t* __r
     int* pad_off = cnt + E;
     int* base = pad_off + E + 1;
     int* wave_cnt = base + E;
-    int* wave_tot = wave_cnt + kWaves * E;
+    int* wave_tot = wave_cnt + (NT / 64) * E;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-    for (int e = tid; e < E; e += kThreads) cnt[e] = 0;
-    for (int x = tid; x < kWaves * E; x += kThreads) wave_cnt[x] = 0;
+    for (int e = tid; e < E; e += NT) cnt[e] = 0;
+    for (int x = tid; x < (NT / 64) * E; x += NT) wave_cnt[x] = 0;
     __syncthreads();
-    for (int i = tid; i < R; i += kThreads) {
+    for (int i = tid; i < R; i += NT) {
         const int e = ids[i];
         if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
     }
     __syncthreads();
 
-    // scans of counts (unpadded offsets) and padded sizes, E <= kThreads
+    // scans of counts (unpadded offsets) and padded sizes, E <= NT
     const int c = tid < E ? cnt[tid] : 0;
     const int padded = tid < E ? ceil_div(c, BM) * BM : 0;
     int tot_c, tot_p;
-    const int off_c = block_exclusive_scan(c, wave_tot, &tot_c);
-    const int off_p = block_exclusive_scan(padded, wave_tot, &tot_p);
+    const int off_c = block_exclusive_scan<NT>(c, wave_tot, &tot_c);
+    const int off_p = block_exclusive_scan<NT>(padded, wave_tot, &tot_p);
     if (tid < E) {
         counts_out[tid] = c;
         offsets_out[tid] = off_c;
@@ -95,8 +101,8 @@ __global__ __launch_bounds__(kThreads) void route_prep_kernel(const int32_t* __r
     __syncthreads();
 
     // every slot starts as the sentinel; the scatter below overwrites valid ones
-    for (int p = tid; p < max_padded; p += kThreads) sorted_ids[p] = R;
-    for (int b = tid; b < max_blocks; b += kThreads) {
+    for (int p = tid; p < max_padded; p += NT) sorted_ids[p] = R;
+    for (int b = tid; b < max_blocks; b += NT) {
         const int p = b * BM;
         int owner = -1;
         if (p < tot_p) {
@@ -113,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void route_prep_kernel(const int32_t* __r
     while ((1 << nbits) < E) ++nbits;
     __syncthreads();  // sentinel stores complete before any scatter store
 
-    for (int chunk = 0; chunk < R; chunk += kThreads) {
+    for (int chunk = 0; chunk < R; chunk += NT) {
         const int i = chunk + tid;
         const int e = i < R ? ids[i] : -1;
         const bool valid = e >= 0 && e < E;
@@ -462,12 +468,25 @@ __global__ __launch_bounds__(kThreads) void offsets_to_route_kernel(const int32_
 hipError_t launch_route_prep(const int32_t* topk_ids, int R, int E, int block_m, int max_padded, int max_blocks,
                              int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntp, int32_t* offsets,
                              int32_t* counts, hipStream_t s) {
+#if W4A16_ROUTE_SMALL_THREADS >= 64
+    {
+        if (E <= W4A16_ROUTE_SMALL_THREADS && R <= W4A16_ROUTE_SMALL_THREADS) {
+            // few routes and experts (decode steps): half the workgroup, half the barrier cost and LDS to clear;
+            // thread e still owns expert e (measured: 0.5-0.7 us less at up to 512 routes, slower beyond)
+            constexpr int NT = W4A16_ROUTE_SMALL_THREADS, NW = NT / 64;
+            const size_t shmem = sizeof(int) * ((size_t)E + (E + 1) + E + (size_t)NW * E + (NW + 1));
+            hipLaunchKernelGGL(route_prep_kernel<NT>, dim3(1), dim3(NT), shmem, s, topk_ids, R, E, block_m,
+                               max_padded, max_blocks, sorted_ids, expert_ids, ntp, offsets, counts);
+            return hipGetLastError();
+        }
+    }
+#endif
     const size_t shmem = sizeof(int) * ((size_t)E + (E + 1) + E + (size_t)kWaves * E + (kWaves + 1));
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(route_prep_kernel),
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(route_prep_kernel<kThreads>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (shmem > 65536 && attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(route_prep_kernel, dim3(1), dim3(kThreads), shmem, s, topk_ids, R, E, block_m, max_padded,
-                       max_blocks, sorted_ids, expert_ids, ntp, offsets, counts);
+    hipLaunchKernelGGL(route_prep_kernel<kThreads>, dim3(1), dim3(kThreads), shmem, s, topk_ids, R, E, block_m,
+                       max_padded, max_blocks, sorted_ids, expert_ids, ntp, offsets, counts);
     return hipGetLastError();
 }
 
