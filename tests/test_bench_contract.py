@@ -1,0 +1,62 @@
+"""The benchmark's host-side contract, without a GPU: workload table, algorithmic byte counts, the committed
+HBM-traffic summaries it reads, and the refusal of more than one GPU."""
+import glob
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_workload_table():
+    names = ["qwen3-moe-t%d" % t for t in (1, 8, 64, 512)] + ["kimi-moe-t%d" % t for t in (1, 64, 256)] + \
+            ["deepseek-moe-t%d" % t for t in (1, 32, 512, 4096)] + ["kimi-prefill-t8192"]
+    for name in names:
+        spec = bench.workload_spec(name)
+        assert spec["name"] == name and spec.get("fmt", "int4") == "int4"
+        mx = bench.workload_spec(name + "-mxfp4")
+        assert mx["fmt"] == "mxfp4" and (mx["E"], mx["H"], mx["I"], mx["T"]) == (spec["E"], spec["H"], spec["I"],
+                                                                                spec["T"])
+    # expert-parallel shares state the global expert count their plans are hinted with
+    assert bench.workload_spec("kimi-moe-t256")["global_experts"] == 384
+    assert "global_experts" not in bench.workload_spec("qwen3-moe-t64")
+    with pytest.raises(SystemExit):
+        bench.workload_spec("no-such-workload")
+
+
+def test_packed_weight_bytes():
+    # 16-row x 256-k superblocks: 2304 bytes (INT4 codes + BF16 scales), 2176 (E2M1 codes + E8M0 scales)
+    assert bench.packed_weight_bytes(16, 256) == 2304
+    assert bench.packed_weight_bytes(16, 256, "mxfp4") == 2176
+    assert bench.packed_weight_bytes(4096, 7168) == 4096 * 7168 * 9 // 16
+    assert bench.packed_weight_bytes(4096, 7168, "mxfp4") == 4096 * 7168 * 17 // 32
+    assert bench.packed_weight_bytes(17, 288) == 2 * 2 * 2304  # ragged shapes pad to whole superblocks
+
+
+def test_committed_traffic_summaries_match_the_sources():
+    """Every committed HBM-traffic summary names its workload and the hash of the kernel sources it was taken
+    with; bench.py reports the figure only while they match, so a stale summary shows up here first."""
+    paths = sorted(glob.glob(os.path.join(ROOT, "profiles", "gate_up_silu_*_hbm_traffic.md")))
+    assert paths
+    for path in paths:
+        workload = os.path.basename(path)[len("gate_up_silu_"):-len("_hbm_traffic.md")]
+        spec = bench.workload_spec(workload)
+        family = "prefill" if workload in ("deepseek-moe-t4096", "deepseek-moe-t4096-mxfp4",
+                                           "kimi-prefill-t8192", "kimi-prefill-t8192-mxfp4") else "decode"
+        traffic = bench.committed_traffic(workload, family)
+        assert traffic is not None, "%s was taken with other kernel sources" % os.path.basename(path)
+        if family == "decode":
+            alg = bench.gate_up_algorithmic_bytes(spec)
+            assert 0.95 * alg <= traffic <= 1.2 * alg, (workload, traffic, alg)
+
+
+def test_more_than_one_gpu_is_refused():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=60)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr
