@@ -68,15 +68,16 @@ enum { W4A16_FORMAT_INT4 = 0, W4A16_FORMAT_MXFP4 = 1 };
  * for the routing tensors passed with it. */
 typedef struct w4a16_plan {
     int32_t kernel;        /* W4A16_KERNEL_DECODE or W4A16_KERNEL_PREFILL */
-    int32_t block_m;       /* rows per route block: 16, 32, 48 or 64 (decode); 32, 64 or 128 (prefill) */
-    int32_t n_blocks;      /* 16-column blocks per wavefront: 1, 2 or 4 (prefill: 2 or 4) */
+    int32_t block_m;       /* rows per route block: 16, 32, 48 or 64 (decode); 16, 32, 64 or 128 (prefill) */
+    int32_t n_blocks;      /* 16-column blocks per wavefront: 1, 2 or 4 (prefill: 2 or 4; 2 with block_m 16) */
     int32_t waves;         /* wavefronts per workgroup, each owning its own columns: 4 */
     int32_t k_split;       /* workgroups sharing one output tile along K: decode 1..64, prefill 1..16
                               (the planner splits decode K for grids with few workgroups, and prefill
                               K never) */
-    int32_t tile_m;        /* prefill: rows per workgroup tile, 64 or 128 (0: block_m).  With block_m
-                              32 a workgroup takes up to tile_m / 32 consecutive route blocks of one
-                              expert; otherwise tile_m equals block_m.  decode: 0 */
+    int32_t tile_m;        /* prefill: rows per workgroup tile (0: block_m).  With block_m 16 it is 64
+                              or 144, with block_m 32 64 or 128, and a workgroup takes up to
+                              tile_m / block_m consecutive route blocks of one expert; otherwise
+                              tile_m equals block_m (64 or 128).  decode: 0 */
     int32_t reserved[2];   /* must be zero */
 } w4a16_plan;
 

@@ -98,16 +98,16 @@ def test_plan_selector_keys_on_rows_per_expert(lib):
     # Qwen3-like decode: 64 tokens x 8 / 128 experts = 4 rows per expert
     p = L.plan_select(64, 8, 128, 1536, 2048)
     assert p.kernel == L.KERNEL_DECODE and p.block_m == 16
-    # same token count, far fewer experts: 64 x 8 / 4 = 128 rows per expert -> prefill, 32-row route blocks
-    # gathered into 128-row tiles
+    # same token count, far fewer experts: 64 x 8 / 4 = 128 rows per expert -> prefill, 16-row route blocks
+    # gathered into tiles of up to 144 rows
     p = L.plan_select(64, 8, 4, 1536, 2048)
-    assert p.kernel == L.KERNEL_PREFILL and (p.block_m, p.tile_m) == (32, 128)
+    assert p.kernel == L.KERNEL_PREFILL and (p.block_m, p.tile_m) == (16, 144)
     # an explicit expectation overrides T*k/E: 10 rows stay on the decode kernel, 30 rows take 64-row tiles of
-    # 32-row blocks, 48 rows plain 64-row blocks
+    # 16-row blocks, 48 rows plain 64-row blocks
     p = L.plan_select(64, 8, 128, 1536, 2048, expected_rows_per_expert=10.0)
     assert p.kernel == L.KERNEL_DECODE and (p.block_m, p.tile_m) == (16, 0)
     p = L.plan_select(64, 8, 128, 1536, 2048, expected_rows_per_expert=30.0)
-    assert p.kernel == L.KERNEL_PREFILL and (p.block_m, p.tile_m) == (32, 64)
+    assert p.kernel == L.KERNEL_PREFILL and (p.block_m, p.tile_m) == (16, 64)
     p = L.plan_select(64, 8, 128, 1536, 2048, expected_rows_per_expert=48.0)
     assert p.kernel == L.KERNEL_PREFILL and (p.block_m, p.tile_m) == (64, 0)
     # one token on a Kimi-K2-like expert share: few workgroups, so K is split across workgroups
@@ -132,9 +132,11 @@ def test_plan_validation(lib):
     good = L.make_plan("decode", 16, 4, 4)
     assert lib.w4a16_gemm_workspace_bytes(ctypes.byref(good), 32, 8, 512, ctypes.byref(sz)) == 0
     assert sz.value == 0
-    # prefill tiles: 64 or 128 rows, taller than the route block only for 32-row blocks; decode has none
+    # prefill tiles: 64 or 128 rows, taller than the route block only for 32-row blocks; 16-row blocks take
+    # tiles of 64 or 144 rows and two n-blocks per wavefront; decode has none
     for args in (("prefill", 32, 2, 4, 1, 96), ("prefill", 64, 2, 4, 1, 128), ("prefill", 128, 2, 4, 1, 64),
-                 ("prefill", 32, 2, 4, 1, 0), ("decode", 16, 4, 4, 1, 64)):
+                 ("prefill", 32, 2, 4, 1, 0), ("decode", 16, 4, 4, 1, 64), ("prefill", 16, 2, 4, 1, 0),
+                 ("prefill", 16, 2, 4, 1, 128), ("prefill", 16, 4, 4, 1, 144), ("prefill", 32, 2, 4, 1, 144)):
         bad = L.make_plan(*args)
         assert lib.w4a16_gemm_workspace_bytes(ctypes.byref(bad), 32, 8, 512, ctypes.byref(sz)) == -2, args
     # a tile list: its length padded to 16 bytes, then two ints per 32-row route block for the tiles and two for
@@ -152,6 +154,12 @@ def test_plan_validation(lib):
     pt = L.make_plan("prefill", 32, 2, 4, 2, 128)
     tl = ((4 + 4 * 9) * 4 + 255) // 256 * 256
     assert L.gemm_workspace_bytes(pt, 32, 8, 512) == 256 + 11 * 4 * 2 * 128 * 128 * 4 + tl
+    # 16-row blocks in 144-row tiles (R=32, E=8: 32 + 8*15 slots -> 10 blocks; at most ceil(10 / 9) + 8 tiles),
+    # two n-blocks per wavefront -> 128 columns, N=512 -> 4 column tiles
+    pt16 = L.make_plan("prefill", 16, 2, 4, 2, 144)
+    tl16 = ((4 + 4 * 10) * 4 + 255) // 256 * 256
+    assert L.gemm_workspace_bytes(pt16, 32, 8, 512) == 256 + 10 * 4 * 2 * 144 * 128 * 4 + tl16
+    assert L.gemm_workspace_bytes(L.make_plan("prefill", 16, 2, 4, 1, 144), 32, 8, 512) == tl16
     # split K: counters (one per route block and column tile) then fp32 partial tiles
     split = L.make_plan("decode", 16, 4, 4, k_split=4)
     # 10 route blocks x 2 column tiles of 256: 20 counters (one 256-byte line), 10*2*4 partial tiles of 16x256

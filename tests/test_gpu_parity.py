@@ -134,7 +134,9 @@ DECODE_PLANS = ([("decode", bm, nbw, 4, 1) for bm in (16, 32, 48, 64) for nbw in
                    ("decode", 16, 1, 4, 3)])  # 3 slices of a 2-stage K: one slice is empty
 PREFILL_PLANS = ([("prefill", bm, nbw, 4, 1) for bm in (64, 128) for nbw in (2, 4)]
                  + [("prefill", 32, nbw, 4, 1, tile) for tile in (64, 128) for nbw in (2, 4)]  # tiles of 32-row blocks
-                 + [("prefill", 64, 2, 4, 2), ("prefill", 32, 2, 4, 3, 128)])  # K split across workgroups
+                 + [("prefill", 16, 2, 4, 1, tile) for tile in (64, 144)]  # tiles of 16-row blocks
+                 + [("prefill", 64, 2, 4, 2), ("prefill", 32, 2, 4, 3, 128),
+                    ("prefill", 16, 2, 4, 3, 144)])  # K split across workgroups
 PLAN_ID = lambda p: "%s-bm%d-nb%d-w%d-ks%d" % p[:5] + ("-t%d" % p[5] if len(p) > 5 else "")  # noqa: E731
 
 
@@ -161,7 +163,8 @@ def test_gemm_tiny_all_plans(orc, plan_args):
 @pytest.mark.parametrize("plan_args", [("decode", 16, 4, 4, 1), ("decode", 64, 2, 4, 1), ("decode", 16, 4, 4, 3),
                                        ("decode", 32, 2, 4, 7), ("prefill", 64, 4, 4, 1), ("prefill", 128, 2, 4, 1),
                                        ("prefill", 32, 2, 4, 1, 128), ("prefill", 32, 2, 4, 1, 64),
-                                       ("prefill", 64, 4, 4, 3), ("prefill", 32, 2, 4, 2, 128)],
+                                       ("prefill", 64, 4, 4, 3), ("prefill", 32, 2, 4, 2, 128),
+                                       ("prefill", 16, 2, 4, 1, 144), ("prefill", 16, 2, 4, 1, 64)],
                          ids=PLAN_ID)
 @pytest.mark.parametrize("shape", [(24, 6, 2, 40, 512), (9, 4, 3, 64, 96), (70, 3, 2, 16, 2048),
                                    (5, 10, 8, 4096, 7168)], ids=lambda s: "T%d-E%d-k%d-N%d-K%d" % s)
@@ -214,7 +217,8 @@ EDGE = ["E1", "one hot expert", "empty and single", "ragged N and K", "tile edge
 @pytest.mark.parametrize("plan_args", [("decode", 16, 1, 4, 1), ("decode", 32, 4, 4, 1), ("decode", 64, 2, 4, 1),
                                        ("decode", 16, 2, 4, 2), ("prefill", 64, 2, 4, 1), ("prefill", 128, 4, 4, 1),
                                        ("prefill", 32, 2, 4, 1, 128), ("prefill", 32, 2, 4, 1, 64),
-                                       ("prefill", 32, 2, 4, 2, 64)],
+                                       ("prefill", 32, 2, 4, 2, 64), ("prefill", 16, 2, 4, 1, 144),
+                                       ("prefill", 16, 2, 4, 1, 64)],
                          ids=PLAN_ID)
 @pytest.mark.parametrize("kind", EDGE)
 def test_gemm_edge_cases(orc, kind, plan_args):
@@ -228,7 +232,8 @@ def test_gemm_edge_cases(orc, kind, plan_args):
 
 
 @pytest.mark.parametrize("plan_args", [("prefill", 64, 2, 4, 2), ("prefill", 64, 4, 4, 5), ("prefill", 128, 2, 4, 3),
-                                       ("prefill", 32, 2, 4, 3, 128), ("prefill", 32, 4, 4, 16, 64)],
+                                       ("prefill", 32, 2, 4, 3, 128), ("prefill", 32, 4, 4, 16, 64),
+                                       ("prefill", 16, 2, 4, 2, 144)],
                          ids=PLAN_ID)
 def test_gemm_prefill_split_k(orc, plan_args):
     """K split across workgroups on the prefill kernel: slices of 1-2 stages over a ragged K (16 slices over 5
@@ -270,7 +275,8 @@ def test_gemm_prefill_split_k(orc, plan_args):
 
 @pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
 @pytest.mark.parametrize("plan_args", [("decode", 16, 4, 4, 1), ("decode", 16, 2, 4, 3), ("prefill", 64, 2, 4, 1),
-                                       ("prefill", 32, 2, 4, 1, 128), ("prefill", 32, 4, 4, 2, 64)],
+                                       ("prefill", 32, 2, 4, 1, 128), ("prefill", 32, 4, 4, 2, 64),
+                                       ("prefill", 16, 2, 4, 1, 144)],
                          ids=PLAN_ID)
 def test_gemm_many_experts_ragged(orc, plan_args, fmt):
     """512 experts with a skewed load (a few hot experts, many with one or two rows, many empty), N = 72 (a
@@ -327,11 +333,12 @@ def test_gemm_is_deterministic_and_permutation_equivariant(orc):
 
 
 @pytest.mark.parametrize("plan_args", [("prefill", 32, 2, 4, 1, 128), ("prefill", 32, 4, 4, 1, 128),
-                                       ("prefill", 32, 2, 4, 1, 64)], ids=PLAN_ID)
+                                       ("prefill", 32, 2, 4, 1, 64), ("prefill", 16, 2, 4, 1, 144),
+                                       ("prefill", 16, 2, 4, 1, 64)], ids=PLAN_ID)
 def test_gemm_prefill_tile_list(orc, plan_args):
-    # 32-row route blocks gathered into taller tiles: experts whose block runs are 1 .. 9 blocks long (every
-    # tile height, runs cut into several tiles, empty experts) and more than 1024 valid blocks, so runs and tiles
-    # cross the 1024-block chunks of the tile-list scan
+    # route blocks gathered into taller tiles: experts of 0 .. 288 rows, whose runs are 1 .. 9 blocks of 32 rows or
+    # 1 .. 18 blocks of 16 rows long (every tile height, runs cut into several tiles, empty experts) and more than
+    # 1024 valid blocks, so runs and tiles cross the 1024-block chunks of the tile-list scan
     _say("gemm prefill tile list %s" % (plan_args,))
     rng = np.random.default_rng(4242)
     E, N, K = 420, 32, 64

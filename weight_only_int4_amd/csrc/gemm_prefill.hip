@@ -12,13 +12,15 @@
 //    at most 31 rows per expert instead of BM-1, while the dequantisation is
 //    still shared by all rows of the tile.
 //  * Tile order is XCD-aware.  Consecutive workgroup ids go to the eight XCDs
-//    in turn, so id -> (XCD, position) is remapped to give every XCD one
-//    contiguous run of tiles, route block major: the ~64 workgroups an XCD
-//    runs at a time then cover a few route blocks across all column tiles.
-//    They share those rows of activations and, for blocks of the same expert,
-//    its weight slices in the XCD's L2.  Only valid tiles (from the routed
-//    row count num_tokens_padded, read on the device) are spread, so the XCDs
-//    stay balanced.
+//    in turn, so id -> (XCD, position) is remapped to give every XCD runs of
+//    consecutive (tile, column tile) pairs, tile major: the ~64 workgroups an
+//    XCD runs at a time then cover one or two tiles across all column tiles,
+//    sharing those rows of activations and the expert's weight slices in the
+//    XCD's L2.  The runs are chunks of the valid pairs only (from the routed
+//    row count num_tokens_padded, read on the device), about six per XCD and
+//    dealt to the XCDs in turn: with skewed routing the tall tiles of the
+//    busiest experts come first, and one contiguous range per XCD would leave
+//    the first XCDs with most of the work.
 //  * The BM gathered activation rows are streamed HBM -> LDS by direct loads
 //    (buffer_load ... lds) into a two-slot ring of 128-k stages, stored
 //    unpadded with each row's 16-byte chunks XOR-permuted by the row, so the
@@ -53,6 +55,10 @@ constexpr int KT = 128;        // k per stage (4 scale groups, half a superblock
 constexpr int kThreads = 256;  // four wavefronts, each owning its own columns
 constexpr int kWaves = kThreads / 64;
 constexpr int kXcds = 8;       // XCDs of the chip; workgroup i runs on XCD i % 8
+// XCD order: the valid (tile, column tile) pairs are cut into chunks of consecutive pairs, at least kChunkMin long
+// and about kChunkRounds per XCD, and chunk j runs on XCD j % 8
+constexpr int kChunkMin = 32;
+constexpr int kChunkRounds = 6;
 
 struct PrefillParams {
     const uint16_t* A;
@@ -429,11 +435,11 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<MT, NBW>())) void
     if constexpr (TILED) ntl = __builtin_amdgcn_readfirstlane(*p.tile_count);
     else ntl = p.ntp ? min(__builtin_amdgcn_readfirstlane(*p.ntp) / BM, p.max_blocks) : p.max_blocks;
     const int V = ntl * p.n_tiles;
-    const int per_xcd = (V + kXcds - 1) / kXcds;
+    const int chunk = max(kChunkMin, (V + kXcds * kChunkRounds - 1) / (kXcds * kChunkRounds));
     const int pos = blockIdx.x / kXcds;
-    const int tile = (blockIdx.x % kXcds) * per_xcd + pos;
-    if (pos >= per_xcd || tile >= V) return;
-    const int t = tile / p.n_tiles, nt = tile % p.n_tiles;
+    const int pair = ((pos / chunk) * kXcds + (int)(blockIdx.x % kXcds)) * chunk + pos % chunk;
+    if (pair >= V) return;
+    const int t = pair / p.n_tiles, nt = pair % p.n_tiles;
     if constexpr (TILED) {
         const int b0 = p.tiles[2 * t], c = p.tiles[2 * t + 1];
         const int e = p.expert_ids[b0];
@@ -454,10 +460,19 @@ hipError_t launch_t(const GemmArgs& a, int ks, hipStream_t s) {
     PrefillParams p{a.A,          a.a_row_div, static_cast<const uint8_t*>(a.packed), a.sh, a.sorted_ids,
                     a.expert_ids, a.ntp,       a.R,  a.max_blocks, n_tiles, a.out, a.tiles, a.tile_count,
                     a.partials,   a.counters};
-    // a multiple of the XCD count: tile t runs on workgroup (t % per_xcd) * 8 + t / per_xcd, which can reach
-    // 8 * ceil(tiles / 8) - 1.  A tile list holds at most one tile per route block.  grid.y: the K slices.
-    const unsigned tiles = (unsigned)a.max_blocks * (unsigned)n_tiles;
-    const dim3 grid((tiles + kXcds - 1) / kXcds * kXcds, (unsigned)ks);
+    // V <= tiles: a tile list of G-block tiles holds at most ceil(max_blocks / G) + min(E, max_blocks) tiles (each
+    // expert's run of L blocks is cut into ceil(L / G) <= L / G + 1), plain route blocks are one tile each.  The
+    // bound is every route landing on these experts; the grid's workgroups past V exit at once but still cost
+    // their dispatch (about 0.3 us per thousand, measured), which matters where only a share of the routes is
+    // local.  XCD x takes chunks x, x + 8, ... of c pairs each, so it needs ceil(ceil(V / c) / 8) * c workgroups:
+    // at most V/8 + kChunkRounds when c is ceil(V / (8 * kChunkRounds)), and at most V/8 + kChunkMin when c is
+    // kChunkMin.  grid.y: the K slices.
+    constexpr int G = MT / RB16;
+    const unsigned max_tiles = G > 1 ? (unsigned)((a.max_blocks + G - 1) / G + (a.sh.E < a.max_blocks ? a.sh.E : a.max_blocks))
+                                     : (unsigned)a.max_blocks;
+    const unsigned tiles = max_tiles * (unsigned)n_tiles;
+    constexpr unsigned kSlack = kChunkMin > kChunkRounds ? kChunkMin : kChunkRounds;
+    const dim3 grid(((tiles + kXcds - 1) / kXcds + kSlack) * kXcds, (unsigned)ks);
     if (a.sh.fmt == kFmtMxfp4)
         hipLaunchKernelGGL((gemm_prefill_kernel<MT, NBW, OM, RB16, kFmtMxfp4>), grid, dim3(kThreads), 0, s, p);
     else
@@ -468,12 +483,18 @@ hipError_t launch_t(const GemmArgs& a, int ks, hipStream_t s) {
 // route blocks of 16*mt rows are tiles; 32-row route blocks (rb16 = 2) are gathered into tiles of 16*mt rows
 template <int OM>
 hipError_t dispatch(const GemmArgs& a, int mt, int nbw, int rb16, int ks, hipStream_t s) {
-    if (rb16 == 2 && mt > 2) {
+    if (rb16 < mt) {
         if (a.tiles == nullptr || a.tile_count == nullptr || a.tile_scratch == nullptr) return hipErrorInvalidValue;
-        if (nbw == 2 && mt == 8) return launch_t<8, 2, OM, 2>(a, ks, s);
-        if (nbw == 4 && mt == 8) return launch_t<8, 4, OM, 2>(a, ks, s);
-        if (nbw == 2 && mt == 4) return launch_t<4, 2, OM, 2>(a, ks, s);
-        if (nbw == 4 && mt == 4) return launch_t<4, 4, OM, 2>(a, ks, s);
+        if (rb16 == 2) {
+            if (nbw == 2 && mt == 8) return launch_t<8, 2, OM, 2>(a, ks, s);
+            if (nbw == 4 && mt == 8) return launch_t<8, 4, OM, 2>(a, ks, s);
+            if (nbw == 2 && mt == 4) return launch_t<4, 2, OM, 2>(a, ks, s);
+            if (nbw == 4 && mt == 4) return launch_t<4, 4, OM, 2>(a, ks, s);
+        }
+        if (rb16 == 1 && nbw == 2) {
+            if (mt == 9) return launch_t<9, 2, OM, 1>(a, ks, s);
+            if (mt == 4) return launch_t<4, 2, OM, 1>(a, ks, s);
+        }
         return hipErrorInvalidValue;
     }
     if (rb16 != mt) return hipErrorInvalidValue;
