@@ -6,11 +6,12 @@
 //    expert_ids[block] in-kernel, so no host synchronisation is needed (Chord
 //    page, "Two kernel families"; the nf4 page, "How it works", finds its
 //    tiles in-kernel the same way).
-//  * With 32-row route blocks, a workgroup takes a tile of up to BM/32
-//    consecutive blocks of one expert from a tile list built on the device,
-//    and runs a body specialised for the tile's height.  Padding then costs
-//    at most 31 rows per expert instead of BM-1, while the dequantisation is
-//    still shared by all rows of the tile.
+//  * With route blocks of 16 or 32 rows, a workgroup takes a tile of up to
+//    BM/16 or BM/32 consecutive blocks of one expert from a tile list built
+//    on the device, and runs a body specialised for the tile's height.
+//    Padding then costs less than one route block per expert instead of up
+//    to BM-1 rows, while the dequantisation is still shared by all rows of
+//    the tile (up to 144 of them).
 //  * Tile order is XCD-aware.  Consecutive workgroup ids go to the eight XCDs
 //    in turn, so id -> (XCD, position) is remapped to give every XCD runs of
 //    consecutive (tile, column tile) pairs, tile major: the ~64 workgroups an
@@ -480,7 +481,8 @@ hipError_t launch_t(const GemmArgs& a, int ks, hipStream_t s) {
     return hipGetLastError();
 }
 
-// route blocks of 16*mt rows are tiles; 32-row route blocks (rb16 = 2) are gathered into tiles of 16*mt rows
+// route blocks of 16*mt rows are tiles; 16- and 32-row route blocks (rb16 = 1, 2) are gathered into tiles of up to
+// 16*mt rows
 template <int OM>
 hipError_t dispatch(const GemmArgs& a, int mt, int nbw, int rb16, int ks, hipStream_t s) {
     if (rb16 < mt) {

@@ -75,7 +75,11 @@ __global__ __launch_bounds__(NT) void route_prep_kernel(const int32_t* __restric
     for (int e = tid; e < E; e += NT) cnt[e] = 0;
     for (int x = tid; x < (NT / 64) * E; x += NT) wave_cnt[x] = 0;
     __syncthreads();
-    for (int i = tid; i < R; i += NT) {
+    // the first chunk's ids stay in registers for the scatter below (one load fewer on the critical path when
+    // there are at most NT routes)
+    const int e_first = tid < R ? ids[tid] : -1;
+    if (e_first >= 0 && e_first < E) atomicAdd(&cnt[e_first], 1);
+    for (int i = tid + NT; i < R; i += NT) {
         const int e = ids[i];
         if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
     }
@@ -121,7 +125,7 @@ __global__ __launch_bounds__(NT) void route_prep_kernel(const int32_t* __restric
 
     for (int chunk = 0; chunk < R; chunk += NT) {
         const int i = chunk + tid;
-        const int e = i < R ? ids[i] : -1;
+        const int e = chunk == 0 ? e_first : (i < R ? ids[i] : -1);
         const bool valid = e >= 0 && e < E;
         uint64_t match = __ballot(valid);
         for (int bit = 0; bit < nbits; ++bit) {

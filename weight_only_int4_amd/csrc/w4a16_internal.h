@@ -139,7 +139,7 @@ struct GemmArgs {
     void* out;         // BF16 bits [R,N], float [R,N], or BF16 bits [R,N/2] (activation mode)
     int out_mode;      // kOutBf16, kOutF32 or kOutAct
     const int32_t* ntp = nullptr;  // num_tokens_padded (device) when known: bounds the valid route blocks
-    int32_t* tiles = nullptr;      // prefill with 32-row route blocks: tile list (first block, blocks) pairs
+    int32_t* tiles = nullptr;      // prefill tiles of several route blocks: tile list (first block, blocks) pairs
     int32_t* tile_count = nullptr; // ... and its length (device)
     int32_t* tile_scratch = nullptr; // 2 * max_blocks ints the tile list is built with
     float* partials = nullptr;     // split-K partial tiles (decode, k_split > 1)
@@ -155,8 +155,8 @@ bool decode_reg_supported(const GemmArgs& a, const w4a16_plan& p);
 hipError_t launch_gemm_decode_reg(const GemmArgs& a, const w4a16_plan& p, hipStream_t s);
 hipError_t launch_gemm_prefill(const GemmArgs& a, const w4a16_plan& p, hipStream_t s);
 bool prefill_supported(const GemmArgs& a);
-// Rows per prefill workgroup tile (plan.tile_m, else block_m); 32-row route blocks are gathered into taller
-// tiles through a tile list.
+// Rows per prefill workgroup tile (plan.tile_m, else block_m); 16- and 32-row route blocks are gathered into
+// taller tiles through a tile list.
 int prefill_tile_rows(const w4a16_plan& p);
 // Split-K workspace of a prefill plan (k_split > 1): fp32 partial tiles and (tile, column tile) counters.
 int prefill_n_tiles(const Shape& sh, const w4a16_plan& p);
