@@ -117,6 +117,20 @@ def gate_up_algorithmic_bytes(spec, block_m: int = 16) -> int:
     return active * packed_weight_bytes(2 * I, H, spec.get("fmt", "int4")) + T * H * 2 + int(valid.sum()) * I * 2 + (maxP + maxB) * 4
 
 
+def roofline_bound(spec, block_m: int = 16):
+    """The roofline that bounds the gate_up launch: "hbm" or "mfma", whichever of its minimum HBM time
+    (algorithmic bytes at the HBM peak) and its minimum matrix time (2 * valid routes * 2I * H flops at the
+    dense BF16 peak) is longer, with both figures.  The kernel that runs does not decide it: a prefill plan at
+    16 rows per expert streams its weights at a few flops per byte and is HBM-bound."""
+    E, H, I = spec["E"], spec["H"], spec["I"]
+    flat = spec["routes"]().reshape(-1)
+    Rv = int(((flat >= 0) & (flat < E)).sum())
+    alg_bytes = gate_up_algorithmic_bytes(spec, block_m)
+    alg_flops = 2.0 * Rv * (2 * I) * H
+    mfma = alg_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > alg_bytes / (HBM_PEAK_GBS * 1e9)
+    return ("mfma" if mfma else "hbm"), alg_bytes, alg_flops
+
+
 # the sources the gate_up kernel of each family is built from
 KERNEL_SOURCES = {
     "decode": ("weight_only_int4_amd/csrc/gemm_decode_reg.hip", "weight_only_int4_amd/csrc/gemm_decode.hip",
@@ -420,14 +434,15 @@ def main():
     gate_up_us = statistics.median(trials)
 
     # dominant kernel: gate_up grouped GEMM with the SiLU*mul epilogue (decode or prefill kernel by plan).
-    # Decode is bound by HBM: algorithmic bytes = packed weights of the active experts, x once, h written once,
-    # routing read once.  Prefill is bound by the matrix cores: algorithmic flops = 2 * valid routes * 2I * H.
+    # Its roofline is the longer of two minimum times: algorithmic bytes (packed weights of the active experts,
+    # x once, h written once, routing read once) at the HBM peak, and algorithmic flops (2 * valid routes * 2I *
+    # H) at the dense BF16 matrix peak.
     prefill = p13.kernel == L.KERNEL_PREFILL
-    if prefill:
-        alg_flops = 2.0 * Rv * (2 * I) * H
+    bound, alg_bytes, alg_flops = roofline_bound(spec, p13.block_m)
+    mfma_bound = bound == "mfma"
+    if mfma_bound:
         achieved = alg_flops / (gate_up_us * 1e-6) / 1e12
     else:
-        alg_bytes = gate_up_algorithmic_bytes(spec, p13.block_m)
         achieved = alg_bytes / (gate_up_us * 1e-6) / 1e9
     traffic = committed_traffic(spec["name"], "prefill" if prefill else "decode")
     if p13.kernel == L.KERNEL_DECODE and p13.block_m == 16:
@@ -457,7 +472,7 @@ def main():
         "gpu_us_per_step_events": round(gpu_step_us, 2),
         "roofline": ({"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                       "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
-                      "kernel": kname, "flops_per_launch": alg_flops} if prefill else
+                      "kernel": kname, "flops_per_launch": alg_flops} if mfma_bound else
                      {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                       "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kname,
                       "bytes_per_launch": int(alg_bytes)}),

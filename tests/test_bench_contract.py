@@ -60,3 +60,14 @@ def test_more_than_one_gpu_is_refused():
                          text=True, timeout=60)
     assert res.returncode == 2
     assert "one GPU" in res.stderr
+
+
+def test_roofline_bound_follows_arithmetic_intensity():
+    """The reported roofline is the longer minimum time, bytes at the HBM peak or flops at the matrix peak (the
+    ridge sits near 88 routed rows per expert), whichever kernel the plan runs: decode at 4 rows per expert
+    and the prefill kernel at 16 rows stream weights, 128 rows per expert and the Kimi-K2 prefill share are
+    matrix-bound."""
+    for name, want in (("qwen3-moe-t64", "hbm"), ("deepseek-moe-t512", "hbm"), ("deepseek-moe-t512-mxfp4", "hbm"),
+                       ("deepseek-moe-t4096", "mfma"), ("kimi-prefill-t8192", "mfma")):
+        bound, nbytes, flops = bench.roofline_bound(bench.workload_spec(name))
+        assert bound == want, (name, nbytes, flops)
