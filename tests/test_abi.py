@@ -110,9 +110,17 @@ def test_plan_selector_keys_on_rows_per_expert(lib):
     assert p.kernel == L.KERNEL_PREFILL and (p.block_m, p.tile_m) == (16, 64)
     p = L.plan_select(64, 8, 128, 1536, 2048, expected_rows_per_expert=48.0)
     assert p.kernel == L.KERNEL_PREFILL and (p.block_m, p.tile_m) == (64, 0)
-    # one token on a Kimi-K2-like expert share: few workgroups, so K is split across workgroups
+    # one token on a Kimi-K2-like expert share: few workgroups, so K is split across workgroups, in slices of at
+    # least 8 stages of 128 k (at most 7 of K = 7168), and the workgroups are narrowed to 2 n-blocks
     p = L.plan_select(1, 8, 48, 4096, 7168, expected_rows_per_expert=1.0 / 48)
-    assert p.kernel == L.KERNEL_DECODE and p.k_split > 1
+    assert p.kernel == L.KERNEL_DECODE and 1 < p.k_split <= 7 and p.n_blocks == 2
+    # a short K is never split below 8 stages per slice: K = 768 (6 stages) stays whole
+    p = L.plan_select(1, 8, 128, 2048, 768)
+    assert p.kernel == L.KERNEL_DECODE and p.k_split == 1
+    # the 64-token Qwen3-like step fills the machine as it is: 4 n-blocks, K whole
+    for N, K in ((1536, 2048), (2048, 768)):
+        p = L.plan_select(64, 8, 128, N, K)
+        assert (p.kernel, p.n_blocks, p.k_split) == (L.KERNEL_DECODE, 4, 1)
     # memoised: same answer twice
     a = L.plan_select(256, 8, 48, 4096, 7168)
     b = L.plan_select(256, 8, 48, 4096, 7168)
