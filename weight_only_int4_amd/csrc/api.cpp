@@ -124,18 +124,26 @@ w4a16_plan select_plan(int T, int k, int E, int N, int K, float rows) {
         const double active = (double)E * (1.0 - exp(-(double)rows));
         const double blocks = active * ceil((double)rows / p.block_m > 1.0 ? (double)rows / p.block_m : 1.0);
         auto waves_of = [&](int nbw) { return blocks * (double)((NB + nbw * p.waves - 1) / (nbw * p.waves)) * p.waves; };
-        // a grid of fewer than ~2 wavefronts per CU streams better from narrower workgroups (twice the column
-        // tiles): on 1-4 tokens, gate_up and down 10-40% faster (measured on the Qwen3-, Kimi-K2-share and
-        // DeepSeek-V3-shaped steps)
-        if (p.n_blocks == 4 && waves_of(4) < 512.0) p.n_blocks = 2;
-        const double waves_total = waves_of(p.n_blocks);
-        // fill the machine with ~8 wavefronts per CU by splitting K, but keep >= 8 stages of 128 k per slice
-        // and at most 16 slices: shorter slices cost more in partial tiles and their reduction than they gain
-        // (measured: one token on the Kimi-K2 share, 28 slices 38 us, 7 slices 24 us)
-        int ks = (int)ceil(2048.0 / (waves_total > 1.0 ? waves_total : 1.0));
-        int max_ks = nst / 8 > 1 ? nst / 8 : 1;
+        int max_ks = nst / 8 > 1 ? nst / 8 : 1;  // slices of at least 8 stages of 128 k
         if (max_ks > 16) max_ks = 16;
-        p.k_split = ks < 1 ? 1 : (ks > max_ks ? max_ks : ks);
+        if (p.n_blocks < 4 || waves_of(4) < 512.0) {
+            // A grid of fewer than ~2 wavefronts per CU streams better from narrower workgroups (twice the
+            // column tiles), and with K split until ~8 wavefronts per CU: on 1-4 tokens, gate_up and down
+            // 10-40% faster (measured on the Qwen3-, Kimi-K2-share and DeepSeek-V3-shaped steps).  Slices
+            // shorter than 8 stages cost more in partial tiles and their reduction than they gain (one token
+            // on the Kimi-K2 share: 28 slices 38 us, 7 slices 24 us).
+            if (p.n_blocks == 4) p.n_blocks = 2;
+            const double waves_total = waves_of(p.n_blocks);
+            const int ks = (int)ceil(2048.0 / (waves_total > 1.0 ? waves_total : 1.0));
+            p.k_split = ks < 1 ? 1 : (ks > max_ks ? max_ks : ks);
+        } else {
+            // From ~2 wavefronts per CU on, K whole is fastest (measured on 2-32 tokens: 8-20% faster than 2 or
+            // 3 slices), except where 257-384 workgroups leave a second round less than half full and K is
+            // long enough (>= 32 stages) for half-length slices to fill it (Kimi-K2 share, 32 tokens: 66.7 us
+            // with 2 slices, 73.9 with K whole)
+            const double waves_total = waves_of(4);
+            p.k_split = (waves_total > 1024.0 && waves_total <= 1536.0 && nst >= 32 && max_ks >= 2) ? 2 : 1;
+        }
     } else {
         // 16-row route blocks keep the padding below 16 rows per expert; the workgroup tile gathers up to nine
         // of them so that each dequantised weight feeds up to 144 rows, and an expert of 129-144 rows is one tile
