@@ -111,9 +111,12 @@ def test_plan_selector_keys_on_rows_per_expert(lib):
     p = L.plan_select(64, 8, 128, 1536, 2048, expected_rows_per_expert=48.0)
     assert p.kernel == L.KERNEL_PREFILL and (p.block_m, p.tile_m) == (64, 0)
     # one token on a Kimi-K2-like expert share: few workgroups, so K is split across workgroups, in slices of at
-    # least 8 stages of 128 k (at most 7 of K = 7168), and the workgroups are narrowed to 2 n-blocks
+    # least 4 stages of 128 k (at most 14 of K = 7168), and the workgroups are narrowed to 2 n-blocks
     p = L.plan_select(1, 8, 48, 4096, 7168, expected_rows_per_expert=1.0 / 48)
-    assert p.kernel == L.KERNEL_DECODE and 1 < p.k_split <= 7 and p.n_blocks == 2
+    assert p.kernel == L.KERNEL_DECODE and 1 < p.k_split <= 14 and p.n_blocks == 2
+    # a Mixtral-like down projection (K = 14336): K split at most 16 ways, workgroups kept at 4 n-blocks
+    p = L.plan_select(1, 2, 8, 4096, 14336)
+    assert p.kernel == L.KERNEL_DECODE and p.k_split == 16 and p.n_blocks == 4
     # a short K is never split below 8 stages per slice: K = 768 (6 stages) stays whole
     p = L.plan_select(1, 8, 128, 2048, 768)
     assert p.kernel == L.KERNEL_DECODE and p.k_split == 1

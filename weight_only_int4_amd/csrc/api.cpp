@@ -124,15 +124,19 @@ w4a16_plan select_plan(int T, int k, int E, int N, int K, float rows) {
         const double active = (double)E * (1.0 - exp(-(double)rows));
         const double blocks = active * ceil((double)rows / p.block_m > 1.0 ? (double)rows / p.block_m : 1.0);
         auto waves_of = [&](int nbw) { return blocks * (double)((NB + nbw * p.waves - 1) / (nbw * p.waves)) * p.waves; };
-        int max_ks = nst / 8 > 1 ? nst / 8 : 1;  // slices of at least 8 stages of 128 k
+        // slices of at least 8 stages of 128 k over K up to 32 stages (at K = 2048 one or two slices beat four
+        // or eight), of at least 4 over longer K (one token on the Kimi-K2 share, K = 7168: 14 slices 21.6 us,
+        // 7 slices 23.7, 28 slices 28.3), and at most 16 slices
+        int max_ks = nst <= 32 ? nst / 8 : nst / 4;
+        if (max_ks < 1) max_ks = 1;
         if (max_ks > 16) max_ks = 16;
         if (p.n_blocks < 4 || waves_of(4) < 512.0) {
             // A grid of fewer than ~2 wavefronts per CU streams better from narrower workgroups (twice the
             // column tiles), and with K split until ~8 wavefronts per CU: on 1-4 tokens, gate_up and down
-            // 10-40% faster (measured on the Qwen3-, Kimi-K2-share and DeepSeek-V3-shaped steps).  Slices
-            // shorter than 8 stages cost more in partial tiles and their reduction than they gain (one token
-            // on the Kimi-K2 share: 28 slices 38 us, 7 slices 24 us).
-            if (p.n_blocks == 4) p.n_blocks = 2;
+            // 10-40% faster (measured on the Qwen3-, Kimi-K2-share and DeepSeek-V3-shaped steps).  With a long
+            // K (more than 64 stages, a Mixtral-8x7B-shaped down projection) the slices of 4 n-blocks stream
+            // better than narrower workgroups (one token: 25.6 us against 30.5).
+            if (p.n_blocks == 4 && nst <= 64) p.n_blocks = 2;
             const double waves_total = waves_of(p.n_blocks);
             const int ks = (int)ceil(2048.0 / (waves_total > 1.0 ? waves_total : 1.0));
             p.k_split = ks < 1 ? 1 : (ks > max_ks ? max_ks : ks);
