@@ -332,10 +332,13 @@ int w4a16_moe_combine(const float* y, const float* topk_w, const int32_t* topk_i
                       int H, uint16_t* out, hipStream_t s);
 
 /* Fused expert MLP: route_prep -> gate_up GEMM with SiLU*mul -> down GEMM ->
- * weighted top-k combine.  It is exactly the sequence w4a16_route_prep,
- * w4a16_grouped_gemm_silu (a_row_div = k), w4a16_grouped_gemm_f32 (down,
- * a_row_div = 1), w4a16_moe_combine, with the plans of
- * w4a16_fused_moe_plans and the buffers carved from ws.
+ * weighted top-k combine.  Its output is exactly that of the sequence
+ * w4a16_route_prep, w4a16_grouped_gemm_silu (a_row_div = k),
+ * w4a16_grouped_gemm_f32 (down, a_row_div = 1), w4a16_moe_combine, with the
+ * plans of w4a16_fused_moe_plans and the buffers carved from ws.  A decode
+ * step (decode plans of 16-row blocks, at most 4096 routes) routes its rows
+ * inside the gate_up kernel instead of a separate launch: the same routing
+ * tensors and outputs, one launch fewer.
  *   x       device BF16 bits [T,H]
  *   w13     handle of [E, 2I, H] weights, gate rows first then up rows
  *   w2      handle of [E, H, I] weights
@@ -361,7 +364,8 @@ int w4a16_fused_moe(const uint16_t* x, const int32_t* topk_ids, const float* top
 /* w4a16_fused_moe that also records caller-created events on the stream
  * between its stages: stage_events[0] before routing, [1] before gate_up
  * (with the activation), [2] before down, [3] before the combine and [4]
- * after it (NULL = no events, identical to w4a16_fused_moe).  For per-stage
+ * after it (NULL = no events, identical to w4a16_fused_moe).  When gate_up
+ * routes its own rows the routing stage is empty.  For per-stage
  * timing of eager calls; nothing else differs. */
 int w4a16_fused_moe_profiled(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, int T, int k,
                              const w4a16_weights* w13, const w4a16_weights* w2, uint16_t* out, void* ws,

@@ -711,19 +711,23 @@ def check_gemm_f32(got, ref, flat, E, label, tol=5e-3):
 
 
 @pytest.mark.parametrize("shape", [(32, 64, 4, 512, 256), (5, 8, 2, 2016, 256), (64, 16, 4, 512, 256),
-                                   (2, 48, 8, 512, 2048)],
-                         ids=["T32-E64-decode", "T5-E8-H2016-decode", "T64-E16-prefill", "T2-E48-splitK"])
+                                   (2, 48, 8, 512, 2048), (512, 1024, 8, 256, 128), (40, 300, 3, 256, 128),
+                                   (5, 1, 2, 256, 64)],
+                         ids=["T32-E64-decode", "T5-E8-H2016-decode", "T64-E16-prefill", "T2-E48-splitK",
+                              "T512-E1024-decode-4096-routes", "T40-E300-decode", "T5-E1-decode"])
 def test_fused_moe_equals_sequence(orc, shape):
     """The fused call is the sequence route_prep, gate_up with SiLU*mul, down (binary32), combine, with the same
     plans, bit for bit (decode, prefill and split-K plans; a token without a local route, one routed twice to
-    the same expert, a non-local route, a ragged last column tile)."""
+    the same expert, a non-local route, a ragged last column tile).  Decode steps of up to 4096 routes route their
+    rows inside the gate_up kernel: the largest such step over the most experts, more experts than the kernel has
+    threads, and a single expert are among the shapes."""
     T, E, k, H, I = shape
     _say("fused = sequence %s" % (shape,))
     rng = np.random.default_rng(T * 13 + E)
     x = synth.activations(rng, T, H)
     c13, s13 = synth.codes(rng, E, 2 * I, H), synth.scales(rng, E, 2 * I, H)
     c2, s2 = synth.codes(rng, E, H, I), synth.scales(rng, E, H, I)
-    ids = synth.uniform_topk(rng, T, E, k)
+    ids = synth.uniform_topk(rng, T, E, k) if E >= k else np.zeros((T, k), np.int32)  # k distinct experts a token
     ids[0, :] = -1                                    # no local route: zero row
     ids[1, 1] = ids[1, 0]                             # one token routed twice to the same expert
     ids[T - 1, 0] = E + 3                             # a non-local route

@@ -953,11 +953,22 @@ int w4a16_fused_moe_planned(const uint16_t* x, const int32_t* topk_ids, const fl
                 return fail(W4A16_HIP_ERROR, "%s: event record failed: %s", what, hipGetErrorString(e_)); \
         }                                                                                  \
     } while (0)
+    // A decode step of up to kSelfRouteMaxRoutes routes on the register-streaming kernel routes its rows inside
+    // the gate_up kernel (which then writes the routing tensors down reads): one launch and its gap fewer.
+    // Every gate_up workgroup reads all the ids twice, so larger steps keep the routing preparation.
+    constexpr int kSelfRouteMaxRoutes = 4096;
+    const bool self_route = p13.kernel == W4A16_KERNEL_DECODE && p13.block_m == 16 && R <= kSelfRouteMaxRoutes &&
+                            E <= W4A16_MAX_EXPERTS && decode_reg_supported(g13, p13);
     W4A16_STAGE(0);
-    rc = check_launch(launch_route_prep_scratch(topk_ids, R, E, p13.block_m, f.maxP, f.maxB, sorted_ids, expert_ids, ntp,
-                                                offsets, counts, reinterpret_cast<int32_t*>(base + f.off_route), s),
-                      "w4a16_fused_moe (route_prep)");
-    if (rc) return rc;
+    if (self_route) {
+        g13.self_route_ids = topk_ids;
+    } else {
+        rc = check_launch(launch_route_prep_scratch(topk_ids, R, E, p13.block_m, f.maxP, f.maxB, sorted_ids, expert_ids,
+                                                    ntp, offsets, counts, reinterpret_cast<int32_t*>(base + f.off_route),
+                                                    s),
+                          "w4a16_fused_moe (route_prep)");
+        if (rc) return rc;
+    }
     W4A16_STAGE(1);
     bind_ws(g13, gemm_ws(w13->shape, p13, f.maxB), base + f.off_split, counter_bytes, base + f.off_tiles);
     rc = check_launch(run_gemm(g13, p13, s), "w4a16_fused_moe (gate_up + silu_mul)");

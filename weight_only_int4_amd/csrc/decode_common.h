@@ -25,6 +25,11 @@ struct DecodeParams {
     unsigned* counters;   // [max_blocks][n_tiles] when KS > 1, zero between calls
     const int32_t* ntp = nullptr;  // num_tokens_padded (device) or NULL: bounds the valid route blocks
     int route_blocks = 0;          // route blocks of the grid (grid.x may be rounded up)
+    // in-kernel routing (gate_up of the fused decode step): top-k ids [R] in, the routing tensors out
+    const int32_t* topk = nullptr;
+    int32_t* sorted_out = nullptr;
+    int32_t* eids_out = nullptr;
+    int32_t* ntp_out = nullptr;
 };
 
 // n-block of weight slot q of wavefront w (see kOutAct for the split of slots between gate and up rows);

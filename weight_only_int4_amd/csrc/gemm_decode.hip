@@ -295,6 +295,7 @@ size_t decode_counters(const Shape& sh, const w4a16_plan& p, int max_blocks) {
 hipError_t launch_gemm_decode(const GemmArgs& a, const w4a16_plan& p, hipStream_t s) {
     if (a.max_blocks == 0) return hipSuccess;
     if (decode_reg_supported(a, p)) return launch_gemm_decode_reg(a, p, s);
+    if (a.self_route_ids) return hipErrorInvalidValue;      // in-kernel routing is on the register kernel only
     if (a.sh.fmt != kFmtInt4) return hipErrorInvalidValue;  // the LDS-staged kernel reads INT4 images only
     switch (a.out_mode) {
         case kOutBf16: return dispatch_mt<kOutBf16>(a, p, s);

@@ -54,7 +54,37 @@ struct RegStage {
 #endif
 constexpr int kXcds = 8;  // XCDs of the chip; workgroup i runs on XCD i % 8
 
-template <int NBW, int D, int OM, int FMT>
+// Exclusive prefix sum of v over the workgroup's threads (uniform call site); *total receives the sum.
+__device__ __forceinline__ int wg_exclusive_scan(int v, int* wt, int* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+    }
+    if (lane == 63) wt[wave] = incl;
+    __syncthreads();
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const int x = wt[w];
+        if (w < wave) before += x;
+        tot += x;
+    }
+    __syncthreads();  // wt is rewritten by the next call
+    *total = tot;
+    return before + incl - v;
+}
+
+// SR: in-kernel routing (gate_up of the fused decode step).  Instead of reading the routing tensors, every
+// workgroup counts the top-k ids per expert in LDS, lays the experts' 16-row blocks out in expert order (the
+// order the counting sort of the routing preparation gives), finds the expert of its own block and ranks that
+// expert's routes by route index to pick its 16 rows, exactly the rows the routing preparation would put there.
+// The workgroups of column tile 0 (first K slice) write their block's sorted_ids and expert_ids, and workgroup 0
+// num_tokens_padded, for the GEMMs that follow; decode rows are independent of their slot, so the outputs are
+// those of the routed path bit for bit.
+template <int NBW, int D, int OM, int FMT, bool SR = false>
 __global__ __launch_bounds__(kDecodeThreads, W4A16_DECODE_REG_WAVES) void gemm_decode_reg_kernel(DecodeParams p) {
     constexpr int SB = sb_bytes(FMT);
     constexpr bool MX = FMT == kFmtMxfp4;
@@ -62,21 +92,88 @@ __global__ __launch_bounds__(kDecodeThreads, W4A16_DECODE_REG_WAVES) void gemm_d
     static_assert(D >= 2 && D <= 6, "ring depth");
     __shared__ int ssid[16];
     __shared__ int s_last;
+    // SR: per-expert counts [E], first block of each expert [E + 1], wavefront totals of the scans
+    __shared__ int sr_lds[SR ? 2 * W4A16_MAX_EXPERTS + 8 : 1];
+    int* const cnt = sr_lds;
+    int* const boff = sr_lds + W4A16_MAX_EXPERTS;
+    int* const wt = sr_lds + 2 * W4A16_MAX_EXPERTS + 2;
 
     // (route block, column tile) of this workgroup.  XCD-aware: consecutive workgroup ids go to the eight XCDs
     // in turn, so id -> (XCD, position) is remapped to give every XCD a contiguous run of the valid (route
     // block, column tile) pairs, route block major; an XCD then gathers the activation rows of its own route
     // blocks only, and its L2 holds them while its weight streams pass through.
     const int n_tiles = gridDim.y;
-    const int valid = p.ntp ? min(__builtin_amdgcn_readfirstlane(*p.ntp) / 16, p.route_blocks) : p.route_blocks;
+    int valid;
+    if constexpr (SR) {
+        const int E = p.sh.E, tid = threadIdx.x;
+        for (int x = tid; x < E; x += kDecodeThreads) cnt[x] = 0;
+        __syncthreads();
+        for (int i = tid; i < p.R; i += kDecodeThreads) {
+            const int ee = p.topk[i];
+            if (ee >= 0 && ee < E) atomicAdd(&cnt[ee], 1);
+        }
+        __syncthreads();
+        const int per = (E + kDecodeThreads - 1) / kDecodeThreads;
+        int local = 0;
+        for (int q = 0; q < per; ++q) {
+            const int x = tid * per + q;
+            if (x < E) local += (cnt[x] + 15) >> 4;
+        }
+        int tot;
+        int run = wg_exclusive_scan(local, wt, &tot);
+        for (int q = 0; q < per; ++q) {
+            const int x = tid * per + q;
+            if (x < E) {
+                boff[x] = run;
+                run += (cnt[x] + 15) >> 4;
+            }
+        }
+        if (tid == 0) boff[E] = tot;
+        __syncthreads();
+        tot = __builtin_amdgcn_readfirstlane(tot);
+        if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0) *p.ntp_out = tot * 16;
+        valid = min(tot, p.route_blocks);
+    } else {
+        valid = p.ntp ? min(__builtin_amdgcn_readfirstlane(*p.ntp) / 16, p.route_blocks) : p.route_blocks;
+    }
     const int V = valid * n_tiles;
     const int id = blockIdx.x + gridDim.x * blockIdx.y;  // gridDim.x * gridDim.y is a multiple of 8
     const int per_xcd = (V + kXcds - 1) / kXcds;
     const int pos = id / kXcds, slot = (id % kXcds) * per_xcd + pos;
     if (pos >= per_xcd || slot >= V) return;
     const int b = slot / n_tiles, nt = slot % n_tiles;
-    const int e = p.expert_ids[b];
-    if (e < 0 || e >= p.sh.E) return;  // unowned block (or ids from a larger expert count)
+    int e;
+    if constexpr (SR) {
+        // owner: the last expert whose first block is at or before b (empty experts share their successor's)
+        int lo = 0, hi = p.sh.E - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (boff[mid] <= b) lo = mid;
+            else hi = mid - 1;
+        }
+        e = __builtin_amdgcn_readfirstlane(lo);
+        const int first = 16 * (b - __builtin_amdgcn_readfirstlane(boff[e]));  // rank of the block's first row
+        if (threadIdx.x < 16) ssid[threadIdx.x] = -1;
+        __syncthreads();
+        int carry = 0;
+        for (int ch = 0; ch < p.R; ch += kDecodeThreads) {
+            const int i = ch + threadIdx.x;
+            const bool m = i < p.R && p.topk[i] == e;
+            int n;
+            const int r = carry + wg_exclusive_scan(m ? 1 : 0, wt, &n);
+            if (m && r >= first && r < first + 16) ssid[r - first] = i;
+            carry += __builtin_amdgcn_readfirstlane(n);
+            if (carry >= first + 16) break;  // uniform: every later route of e ranks past this block
+        }
+        __syncthreads();
+        if (nt == 0 && blockIdx.z == 0) {
+            if (threadIdx.x < 16) p.sorted_out[b * 16 + threadIdx.x] = ssid[threadIdx.x] >= 0 ? ssid[threadIdx.x] : p.R;
+            if (threadIdx.x == 0) p.eids_out[b] = e;
+        }
+    } else {
+        e = p.expert_ids[b];
+        if (e < 0 || e >= p.sh.E) return;  // unowned block (or ids from a larger expert count)
+    }
     const Shape sh = p.sh;
     const int K = sh.K;
     // the wavefront index is uniform: as a scalar it keeps every per-stage offset in scalar registers
@@ -87,7 +184,7 @@ __global__ __launch_bounds__(kDecodeThreads, W4A16_DECODE_REG_WAVES) void gemm_d
     const int nst = (sh.G + 3) / 4;
     const int st_begin = (int)((long)ks * nst / KS), st_end = (int)((long)(ks + 1) * nst / KS);
 
-    if (threadIdx.x < 16) {
+    if (!SR && threadIdx.x < 16) {
         const int sid = p.sorted_ids[b * 16 + threadIdx.x];
         ssid[threadIdx.x] = sid < p.R ? sid : -1;
     }
@@ -107,7 +204,7 @@ __global__ __launch_bounds__(kDecodeThreads, W4A16_DECODE_REG_WAVES) void gemm_d
     // activations: lane (c, j) reads row j of the tile at k-slot c; sentinel rows read past the end (zeros)
     const uint32_t a_bytes = (uint32_t)(p.R / p.a_row_div) * (uint32_t)K * 2u;
     const __amdgpu_buffer_rsrc_t xres = buffer_resource(p.A, a_bytes);
-    const int sid_j = p.sorted_ids[b * 16 + j];
+    const int sid_j = SR ? (ssid[j] >= 0 ? ssid[j] : p.R) : p.sorted_ids[b * 16 + j];
     const uint32_t x_off = sid_j < p.R ? (uint32_t)(sid_j / p.a_row_div) * (uint32_t)K * 2u + (uint32_t)c * 16u
                                        : kOutOfRange;
 
@@ -247,6 +344,23 @@ hipError_t launch_reg(const GemmArgs& a, const w4a16_plan& pl, hipStream_t s) {
     const dim3 grid(gx, decode_n_tiles(a.sh, pl), pl.k_split);
     constexpr int D = W4A16_DECODE_REG_DEPTH >= 2 ? W4A16_DECODE_REG_DEPTH : 2;  // 0 switches the kernel off
     constexpr int DMX = W4A16_DECODE_REG_DEPTH_MX >= 2 ? W4A16_DECODE_REG_DEPTH_MX : 2;
+    if constexpr (OM == kOutAct) {
+        if (a.self_route_ids) {
+            if (a.sh.E > W4A16_MAX_EXPERTS || a.ntp == nullptr) return hipErrorInvalidValue;
+            p.topk = a.self_route_ids;
+            p.sorted_out = const_cast<int32_t*>(a.sorted_ids);
+            p.eids_out = const_cast<int32_t*>(a.expert_ids);
+            p.ntp_out = const_cast<int32_t*>(a.ntp);
+            if (a.sh.fmt == kFmtMxfp4)
+                hipLaunchKernelGGL((gemm_decode_reg_kernel<NBW, DMX, OM, kFmtMxfp4, true>), grid, dim3(kDecodeThreads),
+                                   0, s, p);
+            else
+                hipLaunchKernelGGL((gemm_decode_reg_kernel<NBW, D, OM, kFmtInt4, true>), grid, dim3(kDecodeThreads), 0,
+                                   s, p);
+            return hipGetLastError();
+        }
+    }
+    if (a.self_route_ids) return hipErrorInvalidValue;  // in-kernel routing is for the gate_up GEMM only
     if (a.sh.fmt == kFmtMxfp4)
         hipLaunchKernelGGL((gemm_decode_reg_kernel<NBW, DMX, OM, kFmtMxfp4>), grid, dim3(kDecodeThreads), 0, s, p);
     else

@@ -144,6 +144,9 @@ struct GemmArgs {
     int32_t* tile_scratch = nullptr; // 2 * max_blocks ints the tile list is built with
     float* partials = nullptr;     // split-K partial tiles (decode, k_split > 1)
     unsigned* counters = nullptr;  // split-K arrival counters, zero between calls
+    // decode gate_up only: route the rows in-kernel from these top-k ids [R] and write sorted_ids, expert_ids and
+    // num_tokens_padded (the buffers above, which must then be writable) for the GEMMs that follow
+    const int32_t* self_route_ids = nullptr;
 };
 
 int decode_n_tiles(const Shape& sh, const w4a16_plan& p);
