@@ -4,8 +4,11 @@
 One step = one fused expert-MLP call on synthetic inputs already resident in
 HBM: routing preparation, gate_up grouped GEMM with SiLU*mul in its epilogue,
 down grouped GEMM and the weighted top-k combine.  The default workload is the
-Qwen3-30B-A3B-shaped layer (128 experts, top-8, hidden 2048, intermediate
-768) at 64 tokens, a decode batch with 4 routed rows per expert.
+largest one-GPU configuration: the DeepSeek-V3-shaped layer (256 experts,
+top-8 of a softmax router, hidden 7168, intermediate 2048) at 4096 tokens,
+128 routed rows per expert, whose gate_up GEMM is bound by the matrix cores.
+Decode workloads (e.g. the Qwen3-30B-A3B-shaped layer at 64 tokens) are
+selected with --workload.
 
 Every step reads a different copy of the packed weights from a rotation pool
 of at least 1 GiB, larger than the 256 MiB Infinity Cache plus the L2s, so the
@@ -225,13 +228,30 @@ def host_expert_subset(ids, E, weights, max_experts):
     return Ts, sub_ids, host
 
 
+# Host threads one GPU's job may keep busy on the GPU machine: its CPU share is 16 threads whatever the
+# machine's count of CPUs shows, so the oracle's pool is capped there.
+CPU_SHARE_THREADS = 16
+
+
+def available_cpus() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
+
+
+def oracle_threads() -> int:
+    """Threads of the oracle's pool: every CPU this process may run on, up to the GPU job's CPU share."""
+    return max(1, min(CPU_SHARE_THREADS, available_cpus()))
+
+
 def cpu_baseline(spec, inputs, weight_bytes_step, budget_s=10.0):
     """The oracle (test infrastructure, never the product) timed on the host's cores on this workload."""
     import oracle
 
     x, ids, tw, c13, s13, c2, s2 = inputs
     o = oracle.Oracle(oracle.build())
-    threads = min(16, os.cpu_count() or 1)
+    threads = oracle_threads()
     T = spec["T"]
     if spec.get("device_weights"):
         # weights live on the GPU: the oracle gets the tokens whose experts fit a host copy of 24 experts
@@ -258,8 +278,9 @@ def cpu_baseline(spec, inputs, weight_bytes_step, budget_s=10.0):
               "median of %d runs of %.2f s" % ("the full step of %d tokens" % T if Ts == T else
                                                  "the first %d of %d tokens, scaled to the step" % (Ts, T),
                                                  len(times), med))
-    return {"value": weight_bytes_step / step_s / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": sample, "us_per_step": step_s * 1e6}
+    return {"value": weight_bytes_step / step_s / 1e9, "unit": "GB/s", "cores": threads, "threads": threads,
+            "host_cpus": os.cpu_count(), "cpus_available": available_cpus(), "kind": "oracle",
+            "cpu_share_cap": CPU_SHARE_THREADS, "sample": sample, "us_per_step": step_s * 1e6}
 
 
 def main():
@@ -267,7 +288,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="qwen3-moe-t64")
+    ap.add_argument("--workload", default="deepseek-moe-t4096")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing")
     ap.add_argument("--copy-calibration", action="store_true",

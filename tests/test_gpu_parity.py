@@ -710,19 +710,29 @@ def check_gemm_f32(got, ref, flat, E, label, tol=5e-3):
         assert ratio <= tol, "%s expert %d ratio %.3g" % (label, e, ratio)
 
 
-@pytest.mark.parametrize("shape", [(32, 64, 4, 512, 256), (5, 8, 2, 2016, 256), (64, 16, 4, 512, 256),
-                                   (2, 48, 8, 512, 2048), (512, 1024, 8, 256, 128), (40, 300, 3, 256, 128),
-                                   (5, 1, 2, 256, 64)],
-                         ids=["T32-E64-decode", "T5-E8-H2016-decode", "T64-E16-prefill", "T2-E48-splitK",
-                              "T512-E1024-decode-4096-routes", "T40-E300-decode", "T5-E1-decode"])
-def test_fused_moe_equals_sequence(orc, shape):
+# explicit decode plans whose gate_up splits K (4 stages of 128 k at H = 512: slices of 1-2 stages; 16 stages at
+# H = 2048), with the down projection split too or whole
+SPLIT_GU = (("decode", 16, 2, 4, 3), ("decode", 16, 4, 4, 2))
+SPLIT_GU_ONLY = (("decode", 16, 2, 4, 4), ("decode", 16, 4, 4, 1))
+
+
+@pytest.mark.parametrize("shape,plans", [((32, 64, 4, 512, 256), None), ((5, 8, 2, 2016, 256), None),
+                                         ((64, 16, 4, 512, 256), None), ((2, 48, 8, 512, 2048), None),
+                                         ((2, 48, 8, 512, 256), SPLIT_GU), ((3, 48, 8, 2048, 256), SPLIT_GU_ONLY),
+                                         ((512, 1024, 8, 256, 128), None), ((600, 512, 8, 256, 128), None),
+                                         ((40, 300, 3, 256, 128), None), ((5, 1, 2, 256, 64), None)],
+                         ids=["T32-E64-decode", "T5-E8-H2016-decode", "T64-E16-prefill", "T2-E48-down-splitK",
+                              "T2-E48-both-splitK", "T3-E48-H2048-gate-up-splitK", "T512-E1024-decode-4096-routes",
+                              "T600-E512-decode-4800-routes", "T40-E300-decode", "T5-E1-decode"])
+def test_fused_moe_equals_sequence(orc, shape, plans):
     """The fused call is the sequence route_prep, gate_up with SiLU*mul, down (binary32), combine, with the same
     plans, bit for bit (decode, prefill and split-K plans; a token without a local route, one routed twice to
     the same expert, a non-local route, a ragged last column tile).  Decode steps of up to 4096 routes route their
     rows inside the gate_up kernel: the largest such step over the most experts, more experts than the kernel has
-    threads, and a single expert are among the shapes."""
+    threads, a single expert, and gate_up plans that split K (every slice routes its rows) are among the shapes;
+    a decode step of 4800 routes takes the separate routing launch."""
     T, E, k, H, I = shape
-    _say("fused = sequence %s" % (shape,))
+    _say("fused = sequence %s plans %r" % (shape, plans))
     rng = np.random.default_rng(T * 13 + E)
     x = synth.activations(rng, T, H)
     c13, s13 = synth.codes(rng, E, 2 * I, H), synth.scales(rng, E, 2 * I, H)
@@ -733,10 +743,16 @@ def test_fused_moe_equals_sequence(orc, shape):
     ids[T - 1, 0] = E + 3                             # a non-local route
     tw = rng.uniform(0.1, 1.0, (T, k)).astype(np.float32)
     w13, w2 = _pack(c13, s13), _pack(c2, s2)
-    p13, p2 = w4.fused_moe_plans(T, k, w13, w2)
+    if plans is None:
+        p13, p2 = w4.fused_moe_plans(T, k, w13, w2)
+    else:
+        p13, p2 = w4.make_plan(*plans[0]), w4.make_plan(*plans[1])
+        assert p13.k_split > 1, "the case exists to split gate_up's K"
+    if T * k > 4096:
+        assert p13.kernel == w4.KERNEL_DECODE, "past 4096 routes on a decode plan: the separate routing launch"
     _say("  plans %r %r" % (p13, p2))
     out = torch.full((T, H), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
-    w4.fused_moe(u16(x), i32(ids), f32(tw), w13, w2, out=out)
+    w4.fused_moe(u16(x), i32(ids), f32(tw), w13, w2, out=out, plans=(p13, p2))
     route = w4.route_prep(i32(ids), E, p13.block_m)
     h = poison_bf16(T * k, I)
     w4.grouped_gemm_silu(u16(x), k, w13, route, p13, out=h)
@@ -789,11 +805,13 @@ def test_fused_moe_planned_and_hint(orc):
         assert ei.value.code == -1
 
 
-@pytest.mark.parametrize("shape", [(2, 48, 8, 512, 256), (2, 48, 8, 512, 2048), (32, 64, 4, 512, 256)],
-                         ids=["T2-E48-gate-up-splitK", "T2-E48-both-splitK", "T32-E64-decode"])
-def test_fused_moe_graph_replays(orc, shape):
+@pytest.mark.parametrize("shape,plans", [((2, 48, 8, 512, 256), SPLIT_GU), ((3, 48, 8, 2048, 256), SPLIT_GU_ONLY),
+                                         ((2, 48, 8, 512, 2048), None), ((32, 64, 4, 512, 256), None)],
+                         ids=["T2-E48-both-splitK", "T3-E48-gate-up-splitK", "T2-E48-down-splitK", "T32-E64-decode"])
+def test_fused_moe_graph_replays(orc, shape, plans):
     """The fused call captured in a HIP graph: every replay (with eager work and synchronisations in between)
-    must equal the eager result bit for bit, including plans that split K (their counters reset each call)."""
+    must equal the eager result bit for bit, including plans that split K (their counters reset each call; the
+    split gate_up also routes its rows in every slice)."""
     rng = np.random.default_rng(77)
     T, E, k, H, I = shape
     x = synth.activations(rng, T, H)
@@ -802,12 +820,17 @@ def test_fused_moe_graph_replays(orc, shape):
     ids = synth.uniform_topk(rng, T, E, k)
     tw = rng.uniform(0.1, 1.0, (T, k)).astype(np.float32)
     w13, w2 = _pack(c13, s13), _pack(c2, s2)
-    p13, p2 = w4.fused_moe_plans(T, k, w13, w2)
-    _say("graph replay plans %r %r" % (p13, p2))
+    if plans is None:
+        p13, p2 = w4.fused_moe_plans(T, k, w13, w2)
+    else:
+        p13, p2 = w4.make_plan(*plans[0]), w4.make_plan(*plans[1])
+        assert p13.k_split > 1
+    pl = (p13, p2)
+    _say("graph replay plans %r %r" % pl)
     xd, idsd, twd = u16(x), i32(ids), f32(tw)
-    ws = w4.zeroed_workspace(w4.fused_moe_workspace_bytes(T, k, w13, w2), xd.device)
+    ws = w4.zeroed_workspace(w4.fused_moe_workspace_bytes(T, k, w13, w2, pl), xd.device)
     out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
-    w4.fused_moe(xd, idsd, twd, w13, w2, out=out, ws=ws)
+    w4.fused_moe(xd, idsd, twd, w13, w2, out=out, ws=ws, plans=pl)
     eager = bits(out)
     orc.fused_moe(x, ids, tw, c13, s13, c2, s2)
     ref = orc.last_out_acc
@@ -815,13 +838,13 @@ def test_fused_moe_graph_replays(orc, shape):
         assert np.abs(orc_bf16_to_f64(eager[t]) - ref[t]).max() <= FUSED_TOL * np.abs(ref[t]).max()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        w4.fused_moe(xd, idsd, twd, w13, w2, out=out, ws=ws)
+        w4.fused_moe(xd, idsd, twd, w13, w2, out=out, ws=ws, plans=pl)
     for rep in range(4):
         out.fill_(0)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(bits(out), eager), "replay %d differs from the eager call" % rep
-        w4.fused_moe(xd, idsd, twd, w13, w2, out=out, ws=ws)  # eager work between replays
+        w4.fused_moe(xd, idsd, twd, w13, w2, out=out, ws=ws, plans=pl)  # eager work between replays
         torch.cuda.synchronize()
         assert np.array_equal(bits(out), eager)

@@ -102,8 +102,9 @@ __device__ __forceinline__ void decode_epilogue(const DecodeParams& p, const f32
             for (int r = 0; r < 4; ++r)
                 __hip_atomic_store(&mine[(mt * 16 + 4 * c + r) * COLS + (w * NBW + q) * 16 + j], acc[mt][q][r],
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // the stores above are device-coherent; wait until they have completed before signalling
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    // the stores above are device-coherent: every wavefront waits until its own have completed, then the
+    // barrier orders all of them before the arrival below
+    wait_own_stores();
     __syncthreads();
     if (threadIdx.x == 0) {
         const unsigned prev = __hip_atomic_fetch_add(&p.counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

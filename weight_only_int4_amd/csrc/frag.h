@@ -144,6 +144,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_resource(const void* ba
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
 }
 
+// s_waitcnt vmcnt(0), the other counters left alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in 6:4,
+// lgkmcnt in 11:8).  On gfx9 the vector memory counter also counts stores, which it releases once the store has
+// been acknowledged at the coherence level its cache policy names, so after this wait the wavefront's
+// device-coherent stores are visible to every workgroup of the device.  A workgroup-scope release fence does not
+// wait for them (the workgroup's wavefronts share the CU's path to memory).
+__device__ __forceinline__ void wait_own_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
     __bf16 b = (__bf16)f;
     return __builtin_bit_cast(uint16_t, b);

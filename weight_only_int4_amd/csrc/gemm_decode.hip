@@ -228,13 +228,12 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_kernel(DecodeParam
 }
 
 
-#ifndef W4A16_DECODE_LDS_KIB
-#define W4A16_DECODE_LDS_KIB 32
-#endif
+// LDS budget of the ring per workgroup
+constexpr int kRingLdsBytes = 32 * 1024;
 // ring depth per tile shape: as many stages in flight as the LDS budget holds
 template <int MT, int NBW>
 constexpr int ring_depth() {
-    constexpr int d = (W4A16_DECODE_LDS_KIB * 1024) / DecodeLds<MT, NBW>::SLOT;
+    constexpr int d = kRingLdsBytes / DecodeLds<MT, NBW>::SLOT;
     return d > 6 ? 6 : (d < 2 ? 2 : d);
 }
 

@@ -49,9 +49,6 @@ struct RegStage {
     u32x4 xa[4];    // activation fragment of each of the 4 groups
 };
 
-#ifndef W4A16_DECODE_REG_WAVES
-#define W4A16_DECODE_REG_WAVES 1
-#endif
 constexpr int kXcds = 8;  // XCDs of the chip; workgroup i runs on XCD i % 8
 
 // Exclusive prefix sum of v over the workgroup's threads (uniform call site); *total receives the sum.
@@ -85,7 +82,7 @@ __device__ __forceinline__ int wg_exclusive_scan(int v, int* wt, int* total) {
 // num_tokens_padded, for the GEMMs that follow; decode rows are independent of their slot, so the outputs are
 // those of the routed path bit for bit.
 template <int NBW, int D, int OM, int FMT, bool SR = false>
-__global__ __launch_bounds__(kDecodeThreads, W4A16_DECODE_REG_WAVES) void gemm_decode_reg_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kDecodeThreads, 1) void gemm_decode_reg_kernel(DecodeParams p) {
     constexpr int SB = sb_bytes(FMT);
     constexpr bool MX = FMT == kFmtMxfp4;
     static_assert(OM != kOutAct || NBW % 2 == 0, "the activation epilogue pairs gate and up n-blocks");
@@ -326,12 +323,10 @@ __global__ __launch_bounds__(kDecodeThreads, W4A16_DECODE_REG_WAVES) void gemm_d
     decode_epilogue<1, NBW, OM>(p, acc, ssid, &s_last, b, nt, n_tiles, wave_global, w, c, j);
 }
 
-#ifndef W4A16_DECODE_REG_DEPTH
-#define W4A16_DECODE_REG_DEPTH 2
-#endif
-#ifndef W4A16_DECODE_REG_DEPTH_MX
-#define W4A16_DECODE_REG_DEPTH_MX 3
-#endif
+// ring depths: two stages of INT4 weights (three wavefronts per SIMD fit), three of MXFP4 (its conversion leaves the
+// registers for a third stage at the same occupancy)
+constexpr int kRingDepth = 2;
+constexpr int kRingDepthMx = 3;
 
 template <int NBW, int OM>
 hipError_t launch_reg(const GemmArgs& a, const w4a16_plan& pl, hipStream_t s) {
@@ -342,8 +337,7 @@ hipError_t launch_reg(const GemmArgs& a, const w4a16_plan& pl, hipStream_t s) {
     // grid.x a multiple of the XCD count, so that the remap above is onto the valid pairs
     const unsigned gx = (unsigned)(a.max_blocks + kXcds - 1) / kXcds * kXcds;
     const dim3 grid(gx, decode_n_tiles(a.sh, pl), pl.k_split);
-    constexpr int D = W4A16_DECODE_REG_DEPTH >= 2 ? W4A16_DECODE_REG_DEPTH : 2;  // 0 switches the kernel off
-    constexpr int DMX = W4A16_DECODE_REG_DEPTH_MX >= 2 ? W4A16_DECODE_REG_DEPTH_MX : 2;
+    constexpr int D = kRingDepth, DMX = kRingDepthMx;
     if constexpr (OM == kOutAct) {
         if (a.self_route_ids) {
             if (a.sh.E > W4A16_MAX_EXPERTS || a.ntp == nullptr) return hipErrorInvalidValue;
@@ -384,7 +378,7 @@ hipError_t dispatch_reg(const GemmArgs& a, const w4a16_plan& pl, hipStream_t s) 
 
 bool decode_reg_supported(const GemmArgs& a, const w4a16_plan& p) {
     // one 16-row tile; the buffer resources address below 2 GiB (one expert's packed weights, the activations)
-    return W4A16_DECODE_REG_DEPTH > 0 && p.block_m == 16 &&
+    return p.block_m == 16 &&
            (size_t)a.sh.NB * a.sh.KB * sb_bytes(a.sh.fmt) < (1u << 31) &&
            (size_t)(a.R / a.a_row_div) * a.sh.K * 2 < (1u << 31);
 }

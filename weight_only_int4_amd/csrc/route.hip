@@ -19,9 +19,7 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-#ifndef W4A16_ROUTE_SMALL_THREADS
-#define W4A16_ROUTE_SMALL_THREADS 512
-#endif
+constexpr int kSmallThreads = 512;  // workgroup of the routing of few routes and experts
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
@@ -472,19 +470,15 @@ __global__ __launch_bounds__(kThreads) void offsets_to_route_kernel(const int32_
 hipError_t launch_route_prep(const int32_t* topk_ids, int R, int E, int block_m, int max_padded, int max_blocks,
                              int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntp, int32_t* offsets,
                              int32_t* counts, hipStream_t s) {
-#if W4A16_ROUTE_SMALL_THREADS >= 64
-    {
-        if (E <= W4A16_ROUTE_SMALL_THREADS && R <= W4A16_ROUTE_SMALL_THREADS) {
-            // few routes and experts (decode steps): half the workgroup, half the barrier cost and LDS to clear;
-            // thread e still owns expert e (measured: 0.5-0.7 us less at up to 512 routes, slower beyond)
-            constexpr int NT = W4A16_ROUTE_SMALL_THREADS, NW = NT / 64;
-            const size_t shmem = sizeof(int) * ((size_t)E + (E + 1) + E + (size_t)NW * E + (NW + 1));
-            hipLaunchKernelGGL(route_prep_kernel<NT>, dim3(1), dim3(NT), shmem, s, topk_ids, R, E, block_m,
-                               max_padded, max_blocks, sorted_ids, expert_ids, ntp, offsets, counts);
-            return hipGetLastError();
-        }
+    if (E <= kSmallThreads && R <= kSmallThreads) {
+        // few routes and experts (decode steps): half the workgroup, half the barrier cost and LDS to clear;
+        // thread e still owns expert e (measured: 0.5-0.7 us less at up to 512 routes, slower beyond)
+        constexpr int NT = kSmallThreads, NW = NT / 64;
+        const size_t shmem = sizeof(int) * ((size_t)E + (E + 1) + E + (size_t)NW * E + (NW + 1));
+        hipLaunchKernelGGL(route_prep_kernel<NT>, dim3(1), dim3(NT), shmem, s, topk_ids, R, E, block_m,
+                           max_padded, max_blocks, sorted_ids, expert_ids, ntp, offsets, counts);
+        return hipGetLastError();
     }
-#endif
     const size_t shmem = sizeof(int) * ((size_t)E + (E + 1) + E + (size_t)kWaves * E + (kWaves + 1));
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(route_prep_kernel<kThreads>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
