@@ -22,8 +22,10 @@
  *  - Returns W4A16_OK (0) or a negative status; the message of the last
  *    failure on the calling thread is w4a16_last_error().
  *  - Device buffers are allocated and owned by the caller and passed as raw
- *    device pointers; the library never allocates device memory, never
- *    synchronises and never reads device memory from the host.  Work is
+ *    device pointers; the library never allocates device memory (its one
+ *    static scratch, used by w4a16_fused_moe_noalloc only, is reserved when
+ *    its code loads), never synchronises and never reads device memory from
+ *    the host.  Work is
  *    enqueued on the given HIP stream (NULL = the null stream) and may be
  *    captured into a HIP graph.
  *  - All checks happen on the host before any launch; a failed check
@@ -395,6 +397,31 @@ int w4a16_fused_moe_planned(const uint16_t* x, const int32_t* topk_ids, const fl
                             const w4a16_weights* w13, const w4a16_weights* w2, const w4a16_plan* gate_up,
                             const w4a16_plan* down, uint16_t* out, void* ws, size_t ws_bytes, hipStream_t s,
                             hipEvent_t* stage_events);
+
+/* Bytes of the library's static device scratch, the only device memory the
+ * library itself holds: one copy per GPU the library runs on, reserved when
+ * the library's code is loaded there and kept until the process ends. */
+#define W4A16_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+
+/* w4a16_fused_moe for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same plans (w4a16_fused_moe_plans), kernels and results bit for bit,
+ * with every intermediate (routing tensors, split-K partials and counters,
+ * tile list, h, y) in the library's static scratch of
+ * W4A16_NOALLOC_SCRATCH_BYTES instead of a caller workspace.  It calls no
+ * allocating routine; the caller still passes inputs and the output.
+ *   x, topk_ids, topk_w, T, k, w13, w2, out: as in w4a16_fused_moe.
+ * A call whose workspace (w4a16_fused_moe_workspace_bytes) exceeds the
+ * scratch fails with WORKSPACE_TOO_SMALL before anything is launched; that
+ * covers decode steps up to about R*(4H + 2I) bytes of intermediates, e.g.
+ * 256 tokens of the Kimi-K2 one-GPU share or 512 of a Qwen3-30B-A3B layer.
+ * Every call on one GPU shares that GPU's scratch and leaves its contents
+ * behind; the split-K counters are cleared on the stream before use.  Calls
+ * that overlap on one GPU (other streams, other threads) race.
+ * Errors: as w4a16_fused_moe, plus HIP_ERROR when the scratch's device address
+ * cannot be obtained. */
+int w4a16_fused_moe_noalloc(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, int T, int k,
+                            const w4a16_weights* w13, const w4a16_weights* w2, uint16_t* out, hipStream_t s);
 
 #ifdef __cplusplus
 }

@@ -986,3 +986,64 @@ int w4a16_fused_moe_planned(const uint16_t* x, const int32_t* topk_ids, const fl
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------------ no-allocation fused call
+
+// The static scratch of w4a16_fused_moe_noalloc.  Each GPU holds its own copy at its own address; in host code the
+// name is only a host-side stand-in, so host code uses the per-device address from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[W4A16_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of scratch per device, set once
+
+// Address of scratch on the current device, looked up once per device.
+int scratch_address(void** out, const char* what) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return fail(W4A16_HIP_ERROR, "%s: hipGetDevice failed: %s", what, hipGetErrorString(err));
+    if (dev < 0 || dev >= kMaxDevices) return fail(W4A16_HIP_ERROR, "%s: device %d beyond %d", what, dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess || p == nullptr)
+            return fail(W4A16_HIP_ERROR, "%s: hipGetSymbolAddress of the scratch failed: %s", what,
+                        hipGetErrorString(err));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return W4A16_OK;
+}
+}  // namespace
+
+extern "C" int w4a16_fused_moe_noalloc(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, int T, int k,
+                                       const w4a16_weights* w13, const w4a16_weights* w2, uint16_t* out,
+                                       hipStream_t s) {
+    const char* what = "w4a16_fused_moe_noalloc";
+    w4a16_plan p13, p2;
+    int rc = w4a16_fused_moe_plans(T, k, w13, w2, &p13, &p2);
+    if (rc) return rc;
+    rc = check_fused_plans(T, k, w13, w2, &p13, &p2, what);
+    if (rc) return rc;
+    if (T == 0) return ok();
+    size_t counter_bytes;
+    const FusedLayout f = fused_full_layout(T, k, w13, w2, p13, p2, &counter_bytes);
+    if (f.total > W4A16_NOALLOC_SCRATCH_BYTES)
+        return fail(W4A16_WORKSPACE_TOO_SMALL,
+                    "%s: T=%d k=%d needs %zu bytes of intermediates, the static scratch holds %zu; use "
+                    "w4a16_fused_moe with a workspace",
+                    what, T, k, f.total, (size_t)W4A16_NOALLOC_SCRATCH_BYTES);
+    if (!x || !topk_ids || !topk_w || !out) return fail(W4A16_INVALID_ARG, "%s: NULL pointer argument", what);
+    void* ws = nullptr;
+    rc = scratch_address(&ws, what);
+    if (rc) return rc;
+    // the split-K counters start at zero: the scratch keeps whatever the last call left there
+    if (counter_bytes) {
+        rc = check_launch(launch_zero_words(static_cast<uint32_t*>(ws), counter_bytes / 4, s), what);
+        if (rc) return rc;
+    }
+    return w4a16_fused_moe_planned(x, topk_ids, topk_w, T, k, w13, w2, &p13, &p2, out, ws,
+                                   W4A16_NOALLOC_SCRATCH_BYTES, s, nullptr);
+}

@@ -112,7 +112,19 @@ __global__ __launch_bounds__(256) void combine8_kernel(const float* __restrict__
     *reinterpret_cast<uint4*>(out + (size_t)t * H + n) = o;
 }
 
+// Zero-fills n 32-bit words (used where a caller may capture the call in a graph).
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* __restrict__ p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
+}
+
 }  // namespace
+
+hipError_t launch_zero_words(uint32_t* p, size_t n, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    const size_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
 
 hipError_t launch_silu_mul(const uint16_t* gu, int rows, int I, uint16_t* h, hipStream_t s) {
     const long work = (long)rows * (I / 2);

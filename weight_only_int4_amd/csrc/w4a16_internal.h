@@ -168,6 +168,7 @@ size_t prefill_partial_floats(const Shape& sh, const w4a16_plan& p, int max_bloc
 size_t prefill_counters(const Shape& sh, const w4a16_plan& p, int max_blocks);
 hipError_t launch_silu_mul(const uint16_t* gu, int rows, int I, uint16_t* h, hipStream_t s);
 hipError_t launch_silu_mul_f32(const float* gu, int rows, int I, uint16_t* h, hipStream_t s);
+hipError_t launch_zero_words(uint32_t* p, size_t n, hipStream_t s);
 hipError_t launch_combine(const float* y, const float* tw, const int32_t* ids, int T, int k, int E, int H,
                           uint16_t* out, hipStream_t s);
 

@@ -85,6 +85,7 @@ _SIGS = {
                                                      ctypes.POINTER(_SZ)]),
     "w4a16_fused_moe_planned": (_I, [_P, _P, _P, _I, _I, _P, _P, ctypes.POINTER(Plan), ctypes.POINTER(Plan), _P, _P,
                                      _SZ, _P, _P]),
+    "w4a16_fused_moe_noalloc": (_I, [_P, _P, _P, _I, _I, _P, _P, _P, _P]),
 }
 
 _lib = None
@@ -454,4 +455,18 @@ def fused_moe(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, w13
         _check(load().w4a16_fused_moe(*head, *tail))
     else:
         _check(load().w4a16_fused_moe_profiled(*head, *tail, ev))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 96 << 20  # W4A16_NOALLOC_SCRATCH_BYTES
+
+
+def fused_moe_noalloc(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, w13: Weights, w2: Weights,
+                      out: torch.Tensor, stream=None) -> torch.Tensor:
+    """Fused expert MLP with every intermediate in the library's static device scratch (w4a16_fused_moe_noalloc):
+    no workspace, no allocation; ``out`` is the caller's."""
+    T, k = topk_ids.shape
+    _check(load().w4a16_fused_moe_noalloc(_ptr(x) if T else None, _ptr(topk_ids) if T else None,
+                                          _ptr(topk_w) if T else None, T, k, w13.handle, w2.handle,
+                                          _ptr(out) if T else None, _stream(stream)))
     return out
