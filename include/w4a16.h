@@ -198,12 +198,46 @@ int w4a16_route_prep_ws(const int32_t* topk_ids, int T, int k, int E, int block_
                         int32_t* expert_ids, int32_t* num_tokens_padded, int32_t* expert_offsets,
                         int32_t* counts, void* ws, size_t ws_bytes, hipStream_t s);
 
+/* Routing validation, for routing tensors built outside this library (for
+ * example a serving engine's over-allocated alignment buffers).  The GEMM
+ * calls trust their routing tensors, as the Chord page's indexed fast path
+ * does with its routing validation switched off so that it stays
+ * graph-capturable ("vLLM integration").  This call checks them on the
+ * device, without a host read-back (capturable), and writes a status word:
+ * 0 when valid, else a bitmask of
+ *   W4A16_ROUTE_BAD_COUNT     num_tokens_padded < 0, > max_padded, or not a
+ *                             multiple of block_m
+ *   W4A16_ROUTE_BAD_EXPERT    a block below num_tokens_padded whose
+ *                             expert_ids entry is outside [0, E)
+ *   W4A16_ROUTE_BAD_SLOT      a slot below num_tokens_padded holding an id
+ *                             outside [0, R] (R = T*k is the sentinel)
+ *   W4A16_ROUTE_WRONG_EXPERT  (topk_ids given) a slot holding route i whose
+ *                             topk_ids[i] is not its block's expert
+ *   topk_ids  device int32 [R] or NULL (skip the last check)
+ *   sorted_ids, expert_ids, num_tokens_padded: device tensors as produced by
+ *             w4a16_route_prep for block_m, with max_padded slots
+ *   status    device int32 [1], written
+ * With the environment variable W4A16_VALIDATE=1 every grouped GEMM call
+ * that takes routing tensors runs this check first, synchronises the stream
+ * and fails with INVALID_ARG on a non-zero status (a debugging mode: it
+ * synchronises, so it cannot be captured).
+ * Errors: INVALID_ARG, UNSUPPORTED_SHAPE, HIP_ERROR. */
+enum {
+    W4A16_ROUTE_BAD_COUNT = 1,
+    W4A16_ROUTE_BAD_EXPERT = 2,
+    W4A16_ROUTE_BAD_SLOT = 4,
+    W4A16_ROUTE_WRONG_EXPERT = 8
+};
+int w4a16_validate_routing(const int32_t* topk_ids, int R, int E, int block_m, const int32_t* sorted_ids,
+                           const int32_t* expert_ids, const int32_t* num_tokens_padded, int max_padded,
+                           int32_t* status, hipStream_t s);
+
 /* ---------------------------------------------------------------- planning */
 
 /* Choose a plan from the routed rows per expert, not the token count (Chord
  * page, "TL;DR" and "Indexed kernels").  expected_rows_per_expert <= 0 means
  * T*k/E.  Host only and memoised; environment overrides W4A16_FORCE_KERNEL
- * (decode|prefill), W4A16_BLOCK_M, W4A16_N_BLOCKS, W4A16_WAVES,
+ * (decode|prefill; also read as W4A16_FORCE_SCHEDULE), W4A16_BLOCK_M, W4A16_N_BLOCKS, W4A16_WAVES,
  * W4A16_K_SPLIT and W4A16_TILE_M are read once and are part of the memo
  * key. */
 int w4a16_plan_select(int T, int k, int E, int N, int K, float expected_rows_per_expert, w4a16_plan* out);
@@ -236,6 +270,9 @@ int w4a16_plan_select(int T, int k, int E, int N, int K, float expected_rows_per
  * weights or the activation matrix of 2 GiB or more), WORKSPACE_TOO_SMALL,
  * HIP_ERROR. */
 int w4a16_gemm_workspace_bytes(const w4a16_plan* p, int R, int E, int N, size_t* bytes);
+/* The same size for R = T*k routes, in the argument order of the planning
+ * calls (T tokens, top-k). */
+int w4a16_workspace_bytes(const w4a16_plan* p, int T, int k, int E, int N, size_t* bytes);
 
 int w4a16_grouped_gemm(const uint16_t* A, int a_row_div, const w4a16_weights* w, const int32_t* sorted_ids,
                        const int32_t* expert_ids, const int32_t* num_tokens_padded, int R,

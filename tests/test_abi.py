@@ -184,3 +184,36 @@ def test_bad_handle_is_rejected(lib):
     rc = lib.w4a16_dequant(ctypes.cast(junk, ctypes.c_void_p), 0, f, None, None)
     assert rc == -3 and b"not a w4a16 weight handle" in lib.w4a16_last_error()
     assert lib.w4a16_dequant(None, 0, f, None, None) == -1
+
+
+def test_workspace_bytes_in_token_terms(lib):
+    """w4a16_workspace_bytes(plan, T, k, E, N) is the GEMM workspace of R = T*k routes."""
+    from weight_only_int4_amd import lib as L
+
+    split = L.make_plan("decode", 16, 4, 4, k_split=4)
+    sz = ctypes.c_size_t(0)
+    assert lib.w4a16_workspace_bytes(ctypes.byref(split), 16, 2, 8, 512, ctypes.byref(sz)) == 0
+    assert sz.value == L.gemm_workspace_bytes(split, 32, 8, 512)
+    assert lib.w4a16_workspace_bytes(ctypes.byref(split), -1, 2, 8, 512, ctypes.byref(sz)) == -1
+
+
+def test_validate_routing_argument_checks(lib):
+    """Argument errors of the device-side routing check are caught on the host, before any launch (the device
+    pointers below are never dereferenced)."""
+    st = ctypes.c_void_p(0x4000)
+    p = ctypes.c_void_p(0x1000)
+    assert lib.w4a16_validate_routing(None, 32, 8, 24, p, p, p, 160, st, None) == -2   # block_m not a multiple of 16
+    assert lib.w4a16_validate_routing(None, 32, 8, 16, p, p, p, 150, st, None) == -1   # max_padded not whole blocks
+    assert lib.w4a16_validate_routing(None, 32, 8, 16, p, p, None, 160, st, None) == -1
+    assert lib.w4a16_validate_routing(None, 32, 8, 16, p, p, p, 160, None, None) == -1
+    assert lib.w4a16_validate_routing(None, -1, 8, 16, p, p, p, 160, st, None) == -1
+    assert b"w4a16_validate_routing" in lib.w4a16_last_error()
+
+
+def test_noalloc_checks_before_launch(lib):
+    """The no-allocation fused call refuses bad arguments on the host (the handle check comes first)."""
+    junk = (ctypes.c_uint32 * 16)()
+    h = ctypes.cast(junk, ctypes.c_void_p)
+    p = ctypes.c_void_p(0x1000)
+    assert lib.w4a16_fused_moe_noalloc(p, p, p, 4, 2, h, h, p, None) == -3
+    assert lib.w4a16_fused_moe_noalloc(p, p, p, 4, 2, None, None, p, None) == -1

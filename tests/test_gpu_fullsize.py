@@ -121,7 +121,7 @@ def kimi_weights():
     return synth.expert_weights(3, 48, 4096, 7168, salt=1)
 
 
-@pytest.mark.parametrize("T", [1, 16, 256])
+@pytest.mark.parametrize("T", [1, 2, 4, 8, 16, 32, 64, 128, 256])
 def test_kimi_decode_share_gate_up(orc, kimi_weights, T):
     codes, scales = kimi_weights
     ids = synth.kimi_decode_routes(T)
@@ -181,8 +181,22 @@ def deepseek_weights():
     return dict(c13=c13, s13=s13, c2=c2, s2=s2, w13=w13, w2=w2, E=E, H=H, I=I)
 
 
+def _deepseek_host_weights(d, used):
+    """Codes and scales of the experts ``used`` copied from the device, and the id remap onto them."""
+    ue = torch.from_numpy(np.asarray(used)).cuda().long()
+    c13 = d["c13"][ue].cpu().numpy()
+    s13 = d["s13"][ue].view(torch.int16).cpu().numpy().view(np.uint16)
+    c2 = d["c2"][ue].cpu().numpy()
+    s2 = d["s2"][ue].view(torch.int16).cpu().numpy().view(np.uint16)
+    remap = np.full(d["E"], -1, np.int32)
+    remap[np.asarray(used)] = np.arange(len(used), dtype=np.int32)
+    return c13, s13, c2, s2, remap
+
+
 @pytest.mark.parametrize("T", [1, 32, 512, 4096])
 def test_deepseek_fused(orc, deepseek_weights, T):
+    """The DeepSeek-V3-shaped fused step on up to 64 sampled tokens (every token below 64), against the oracle
+    on the experts those tokens use."""
     d = deepseek_weights
     E, H, I = d["E"], d["H"], d["I"]
     ids, tw = synth.deepseek_router(T)
@@ -190,22 +204,50 @@ def test_deepseek_fused(orc, deepseek_weights, T):
     x = synth.activations(rng, T, H)
     _say("deepseek T%d fused plans %r" % (T, w4.fused_moe_plans(T, 8, d["w13"], d["w2"])))
     got = bits(w4.fused_moe(u16(x), i32(ids), f32(tw), d["w13"], d["w2"]))
-    sample = np.unique(np.linspace(0, T - 1, min(T, 6)).astype(int))
-    # the oracle gets only the experts the sampled tokens use (input data copied from the device)
+    sample = np.unique(np.linspace(0, T - 1, min(T, 64)).astype(int))
     used = np.unique(ids[sample])
-    remap = {int(e): i for i, e in enumerate(used)}
-    sub_ids = np.vectorize(lambda e: remap[int(e)])(ids[sample]).astype(np.int32)
-    ue = torch.from_numpy(used).cuda().long()
-    c13 = d["c13"][ue].cpu().numpy()
-    s13 = d["s13"][ue].view(torch.int16).cpu().numpy().view(np.uint16)
-    c2 = d["c2"][ue].cpu().numpy()
-    s2 = d["s2"][ue].view(torch.int16).cpu().numpy().view(np.uint16)
-    orc.fused_moe(x[sample], sub_ids, tw[sample], c13, s13, c2, s2)
+    c13, s13, c2, s2, remap = _deepseek_host_weights(d, used)
+    orc.fused_moe(x[sample], remap[ids[sample]], tw[sample], c13, s13, c2, s2)
     ref = orc.last_out_acc
     g = (got[sample].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     worst = max(np.abs(g[i] - ref[i]).max() / np.abs(ref[i]).max() for i in range(len(sample)))
     _say("  deepseek T%d fused worst ratio %.2e over %d tokens" % (T, worst, len(sample)))
     assert worst <= FUSED_TOL
+
+
+def test_deepseek_t4096_stages(orc, deepseek_weights):
+    """Stage by stage at the benchmark's size and plans (prefill, tile lists): gate_up with SiLU*mul and the
+    down projection (binary32 output) on the first, middle and last route of every one of the 256 experts,
+    against the oracle's binary64 accumulators."""
+    d = deepseek_weights
+    E, H, I, T, k = d["E"], d["H"], d["I"], 4096, 8
+    ids, _ = synth.deepseek_router(T)
+    x = synth.activations(synth.rng_for(5, 7 + T), T, H)
+    p13, p2 = w4.fused_moe_plans(T, k, d["w13"], d["w2"])
+    _say("deepseek T4096 stage plans %r %r" % (p13, p2))
+    assert p13.kernel == w4.KERNEL_PREFILL
+    route = w4.route_prep(i32(ids), E, p13.block_m)
+    h = poison_bf16(T * k, I)
+    w4.grouped_gemm_silu(u16(x), k, d["w13"], route, p13, out=h)
+    hin = synth.activations(synth.rng_for(5, 99), T * k, I)
+    y = w4.grouped_gemm(u16(hin), 1, d["w2"], route, p2, out_f32=True).cpu().numpy().astype(np.float64)
+    got_h = bits(h)
+    rows = sample_routes(ids, E)
+    assert len(rows) >= 3 * E - 2
+    c13, s13, c2, s2, _ = _deepseek_host_weights(d, np.arange(E))
+    gu, _ = orc.grouped_gemm(x, k, c13, s13, ids, acc64=True, rows=rows)
+    worst = check_act(got_h, gu, ids, E, rows=rows, label="deepseek T4096 gate_up+silu")
+    _say("  gate_up+silu: %d sampled routes, worst error / bound %.2f" % (len(rows), worst))
+    del gu
+    yr, _ = orc.grouped_gemm(hin, 1, c2, s2, ids, acc64=True, rows=rows)
+    flat = ids.reshape(-1)
+    worst = 0.0
+    for e in range(E):
+        rr = rows[flat[rows] == e]
+        ratio = np.abs(y[rr] - yr[rr]).max() / np.abs(yr[rr]).max()
+        worst = max(worst, ratio)
+        assert ratio <= 5e-3, "down expert %d ratio %.3g" % (e, ratio)
+    _say("  down: %d sampled routes, worst ratio %.2e" % (len(rows), worst))
 
 
 # ------------------------------------------------------------------ MXFP4 weights at the benchmark's sizes

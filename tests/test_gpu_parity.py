@@ -127,6 +127,72 @@ def test_route_prep_bit_exact(orc, name, gen, E, BM):
     assert np.array_equal(got["counts"].cpu().numpy(), ref["counts"]), "counts"
 
 
+def test_validate_routing_flags_each_fault():
+    """The device-side routing check: valid tensors give 0; each planted fault sets its own bit, with no host
+    read-back by the call itself."""
+    rng = np.random.default_rng(4242)
+    T, k, E, BM = 50, 4, 12, 16
+    ids = synth.uniform_topk(rng, T, E, k)
+    ids[3, 1] = -1
+    idsd = i32(ids)
+    route = w4.route_prep(idsd, E, BM)
+    assert int(w4.validate_routing(route, idsd).item()) == 0
+    assert int(w4.validate_routing(route).item()) == 0
+    ntp = int(route["num_tokens_padded"].item())
+
+    def flagged(mutate, with_ids=True):
+        r = {key: (v.clone() if isinstance(v, torch.Tensor) else v) for key, v in route.items()}
+        mutate(r)
+        return int(w4.validate_routing(r, idsd if with_ids else None).item())
+
+    assert flagged(lambda r: r["num_tokens_padded"].fill_(ntp + 1)) & w4.lib.ROUTE_BAD_COUNT
+    assert flagged(lambda r: r["num_tokens_padded"].fill_(r["sorted_ids"].numel() + BM)) & w4.lib.ROUTE_BAD_COUNT
+    assert flagged(lambda r: r["expert_ids"][0].fill_(E)) & w4.lib.ROUTE_BAD_EXPERT
+    assert flagged(lambda r: r["expert_ids"][0].fill_(-1)) & w4.lib.ROUTE_BAD_EXPERT
+    assert flagged(lambda r: r["sorted_ids"][1].fill_(T * k + 1)) & w4.lib.ROUTE_BAD_SLOT
+    assert flagged(lambda r: r["sorted_ids"][1].fill_(-5)) & w4.lib.ROUTE_BAD_SLOT
+    # a route of another expert placed in block 0: only the check with topk_ids sees it
+    other = int(np.nonzero(ids.reshape(-1) != int(route["expert_ids"][0].item()))[0][0])
+    assert flagged(lambda r: r["sorted_ids"][0].fill_(other)) == w4.lib.ROUTE_WRONG_EXPERT
+    assert flagged(lambda r: r["sorted_ids"][0].fill_(other), with_ids=False) == 0
+    # slots past num_tokens_padded are not read
+    assert flagged(lambda r: r["sorted_ids"][ntp:].fill_(-7)) == 0
+
+
+def test_validate_mode_rejects_bad_routing_before_the_gemm():
+    """W4A16_VALIDATE=1 (read once per process, so in a child process): a GEMM call with a corrupted expert id
+    fails with INVALID_ARG and writes nothing; good routing still runs."""
+    import os
+    import subprocess
+    import sys
+    code = """
+import numpy as np, torch, sys
+sys.path.insert(0, %r)
+import synth, weight_only_int4_amd as w4
+rng = np.random.default_rng(5)
+T, k, E, N, K = 20, 2, 4, 64, 64
+ids = synth.uniform_topk(rng, T, E, k)
+x = torch.from_numpy(synth.activations(rng, T, K).view(np.int16)).cuda().view(torch.bfloat16)
+w = w4.pack_weights(torch.from_numpy(synth.codes(rng, E, N, K)).cuda(),
+                    torch.from_numpy(synth.scales(rng, E, N, K).view(np.int16)).cuda().view(torch.bfloat16))
+plan = w4.make_plan("decode", 16, 1, 4, 1)
+route = w4.route_prep(torch.from_numpy(ids).cuda(), E, 16)
+w4.grouped_gemm(x, k, w, route, plan)
+route["expert_ids"][0].fill_(E + 3)
+out = torch.full((T * k, N), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+try:
+    w4.grouped_gemm(x, k, w, route, plan, out=out)
+except w4.W4A16Error as e:
+    assert e.code == -1 and "W4A16_VALIDATE" in str(e), str(e)
+    assert bool((out.view(torch.int16) == -1).all())
+    print("rejected")
+""" % os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, W4A16_VALIDATE="1")
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=300)
+    assert res.returncode == 0, res.stderr[-2000:]
+    assert "rejected" in res.stdout
+
+
 # ------------------------------------------------------------------ GEMM, tiny config, both kernels
 
 DECODE_PLANS = ([("decode", bm, nbw, 4, 1) for bm in (16, 32, 48, 64) for nbw in (1, 2, 4)]

@@ -10,4 +10,4 @@ from .lib import (FORMAT_INT4, FORMAT_MXFP4, FUSED_STAGE_EVENTS, FUSED_STAGES, K
                   grouped_gemm_offsets, grouped_gemm_silu, load, make_plan, masked_workspace_bytes, moe_combine,
                   pack_weights, pack_weights_mxfp4,
                   packed_bytes, plan_select, route_bounds, route_prep, route_prep_into, route_prep_workspace_bytes,
-                  silu_mul, version, zeroed_workspace)
+                  silu_mul, validate_routing, version, zeroed_workspace)

@@ -82,6 +82,7 @@ const Overrides& overrides() {
     static Overrides o = [] {
         Overrides r;
         const char* fk = getenv("W4A16_FORCE_KERNEL");
+        if (!fk || !*fk) fk = getenv("W4A16_FORCE_SCHEDULE");  // the same switch under its other name
         if (fk && !strcmp(fk, "decode")) r.force_kernel = W4A16_KERNEL_DECODE;
         if (fk && !strcmp(fk, "prefill")) r.force_kernel = W4A16_KERNEL_PREFILL;
         r.block_m = env_int("W4A16_BLOCK_M", 0);
@@ -477,6 +478,21 @@ int w4a16_route_prep_ws(const int32_t* topk_ids, int T, int k, int E, int block_
                         what);
 }
 
+int w4a16_validate_routing(const int32_t* topk_ids, int R, int E, int block_m, const int32_t* sorted_ids,
+                           const int32_t* expert_ids, const int32_t* num_tokens_padded, int max_padded,
+                           int32_t* status, hipStream_t s) {
+    const char* what = "w4a16_validate_routing";
+    if (R < 0 || E < 1 || max_padded < 0) return fail(W4A16_INVALID_ARG, "%s: R=%d E=%d max_padded=%d", what, R, E, max_padded);
+    if (block_m < 16 || block_m % 16)
+        return fail(W4A16_UNSUPPORTED_SHAPE, "%s: block_m %d must be a positive multiple of 16", what, block_m);
+    if (max_padded % block_m) return fail(W4A16_INVALID_ARG, "%s: max_padded %d not a multiple of block_m", what, max_padded);
+    if (!num_tokens_padded || !status || (max_padded > 0 && (!sorted_ids || !expert_ids)))
+        return fail(W4A16_INVALID_ARG, "%s: NULL pointer argument", what);
+    return check_launch(launch_route_validate(topk_ids, R, E, block_m, sorted_ids, expert_ids, num_tokens_padded,
+                                              max_padded, status, s),
+                        what);
+}
+
 int w4a16_plan_select(int T, int k, int E, int N, int K, float expected_rows_per_expert, w4a16_plan* out) {
     if (!out) return fail(W4A16_INVALID_ARG, "w4a16_plan_select: out is NULL");
     if (T < 0 || k < 1 || E < 1 || N < 1 || K < 32 || K % 32)
@@ -516,6 +532,12 @@ int w4a16_gemm_workspace_bytes(const w4a16_plan* p, int R, int E, int N, size_t*
     return ok();
 }
 
+int w4a16_workspace_bytes(const w4a16_plan* p, int T, int k, int E, int N, size_t* bytes) {
+    if (T < 0 || k < 1 || (long)T * k > INT32_MAX)
+        return fail(W4A16_INVALID_ARG, "w4a16_workspace_bytes: T=%d k=%d", T, k);
+    return w4a16_gemm_workspace_bytes(p, T * k, E, N, bytes);
+}
+
 // Shapes the prefill kernel cannot address (its buffer resources reach below 2 GiB).
 static int check_prefill_shape(const char* what, const GemmArgs& a, const w4a16_plan& p) {
     if (p.kernel == W4A16_KERNEL_PREFILL && !prefill_supported(a))
@@ -530,6 +552,34 @@ static int check_format_plan(const char* what, const w4a16_weights* w, const w4a
     if (w->shape.fmt == kFmtMxfp4 && p.kernel == W4A16_KERNEL_DECODE && p.block_m != 16)
         return fail(W4A16_UNSUPPORTED_SHAPE, "%s: MXFP4 weights need decode block_m 16 (plan has %d)", what,
                     p.block_m);
+    return W4A16_OK;
+}
+
+// W4A16_VALIDATE=1: the GEMM calls that take routing tensors check them on the device first and synchronise to
+// read the status (a debugging mode).  The status word lives in a small static device array.
+static __device__ int32_t validate_status[1];
+
+static bool validate_mode() {
+    static const bool on = [] {
+        const char* v = getenv("W4A16_VALIDATE");
+        return v && *v && strcmp(v, "0") != 0;
+    }();
+    return on;
+}
+
+static int validate_now(const char* what, const int32_t* sorted_ids, const int32_t* expert_ids, const int32_t* ntp,
+                        int R, int E, int block_m, int max_padded, hipStream_t s) {
+    void* st = nullptr;
+    hipError_t err = hipGetSymbolAddress(&st, HIP_SYMBOL(validate_status));
+    if (err == hipSuccess)
+        err = launch_route_validate(nullptr, R, E, block_m, sorted_ids, expert_ids, ntp, max_padded,
+                                    static_cast<int32_t*>(st), s);
+    int32_t status = 0;
+    if (err == hipSuccess) err = hipStreamSynchronize(s);
+    if (err == hipSuccess) err = hipMemcpy(&status, st, sizeof(status), hipMemcpyDeviceToHost);
+    if (err != hipSuccess) return fail(W4A16_HIP_ERROR, "%s: routing validation failed: %s", what, hipGetErrorString(err));
+    if (status)
+        return fail(W4A16_INVALID_ARG, "%s: routing tensors invalid (W4A16_VALIDATE status 0x%x)", what, (unsigned)status);
     return W4A16_OK;
 }
 
@@ -564,6 +614,10 @@ static int grouped_gemm_impl(const char* what, const uint16_t* A, int a_row_div,
     a.ntp = ntp;
     rc = check_prefill_shape(what, a, *p);
     if (rc) return rc;
+    if (validate_mode() && ntp) {
+        rc = validate_now(what, sorted_ids, expert_ids, ntp, R, w->shape.E, p->block_m, maxP, s);
+        if (rc) return rc;
+    }
     bind_ws(a, g, ws);
     return check_launch(run_gemm(a, *p, s), what);
 }

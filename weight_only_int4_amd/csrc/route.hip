@@ -543,4 +543,41 @@ hipError_t launch_tile_map(const int32_t* expert_ids, const int32_t* ntp, int bl
     return hipGetLastError();
 }
 
+// Checks caller-provided routing tensors on the device (one workgroup, no host read-back) and writes a status
+// bitmask: kRouteBadCount (num_tokens_padded negative, above max_padded or not a multiple of block_m),
+// kRouteBadExpert (a block below num_tokens_padded owned by no expert in [0, E)), kRouteBadSlot (a slot below
+// num_tokens_padded holding an id outside [0, R]; R is the sentinel), kRouteWrongExpert (with topk_ids: a slot
+// holding route i of another expert than its block's).
+__global__ __launch_bounds__(1024) void route_validate_kernel(const int32_t* __restrict__ topk, int R, int E,
+                                                               int block_m, const int32_t* __restrict__ sorted_ids,
+                                                               const int32_t* __restrict__ expert_ids,
+                                                               const int32_t* __restrict__ ntp, int max_padded,
+                                                               int32_t* __restrict__ status) {
+    __shared__ int flags;
+    if (threadIdx.x == 0) flags = 0;
+    __syncthreads();
+    const int n = *ntp;
+    int f = 0;
+    if (n < 0 || n > max_padded || n % block_m) f |= W4A16_ROUTE_BAD_COUNT;
+    const int used = (n < 0 ? 0 : (n > max_padded ? max_padded : n));
+    for (int slot = threadIdx.x; slot < used; slot += blockDim.x) {
+        const int e = expert_ids[slot / block_m];
+        const int sid = sorted_ids[slot];
+        if (e < 0 || e >= E) f |= W4A16_ROUTE_BAD_EXPERT;
+        if (sid < 0 || sid > R) f |= W4A16_ROUTE_BAD_SLOT;
+        else if (topk && sid < R && topk[sid] != e) f |= W4A16_ROUTE_WRONG_EXPERT;
+    }
+    if (f) atomicOr(&flags, f);
+    __syncthreads();
+    if (threadIdx.x == 0) *status = flags;
+}
+
+hipError_t launch_route_validate(const int32_t* topk_ids, int R, int E, int block_m, const int32_t* sorted_ids,
+                                 const int32_t* expert_ids, const int32_t* ntp, int max_padded, int32_t* status,
+                                 hipStream_t s) {
+    hipLaunchKernelGGL(route_validate_kernel, dim3(1), dim3(1024), 0, s, topk_ids, R, E, block_m, sorted_ids,
+                       expert_ids, ntp, max_padded, status);
+    return hipGetLastError();
+}
+
 }  // namespace w4a16

@@ -118,6 +118,9 @@ size_t route_prep_scratch_ints(int R, int E);
 hipError_t launch_route_prep_scratch(const int32_t* topk_ids, int R, int E, int block_m, int max_padded,
                                      int max_blocks, int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntp,
                                      int32_t* offsets, int32_t* counts, int32_t* scratch, hipStream_t s);
+hipError_t launch_route_validate(const int32_t* topk_ids, int R, int E, int block_m, const int32_t* sorted_ids,
+                                 const int32_t* expert_ids, const int32_t* ntp, int max_padded, int32_t* status,
+                                 hipStream_t s);
 hipError_t launch_tile_map(const int32_t* expert_ids, const int32_t* ntp, int block_m, int max_blocks, int group,
                            int32_t* tiles, int32_t* count, int32_t* scratch, hipStream_t s);
 hipError_t launch_masked_to_route(const int32_t* masked_m, int E, int max_m, int block_m, int max_padded,

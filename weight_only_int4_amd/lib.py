@@ -86,7 +86,11 @@ _SIGS = {
     "w4a16_fused_moe_planned": (_I, [_P, _P, _P, _I, _I, _P, _P, ctypes.POINTER(Plan), ctypes.POINTER(Plan), _P, _P,
                                      _SZ, _P, _P]),
     "w4a16_fused_moe_noalloc": (_I, [_P, _P, _P, _I, _I, _P, _P, _P, _P]),
+    "w4a16_validate_routing": (_I, [_P, _I, _I, _I, _P, _P, _P, _I, _P, _P]),
+    "w4a16_workspace_bytes": (_I, [ctypes.POINTER(Plan), _I, _I, _I, _I, ctypes.POINTER(_SZ)]),
 }
+
+ROUTE_BAD_COUNT, ROUTE_BAD_EXPERT, ROUTE_BAD_SLOT, ROUTE_WRONG_EXPERT = 1, 2, 4, 8
 
 _lib = None
 
@@ -258,6 +262,20 @@ def route_prep_into(topk_ids: torch.Tensor, E: int, block_m: int, out: dict, str
 
 
 # ---------------------------------------------------------------- planning and GEMM
+
+def validate_routing(route: dict, topk_ids: torch.Tensor | None = None, status: torch.Tensor | None = None,
+                     stream=None) -> torch.Tensor:
+    """Device-side check of routing tensors (w4a16_validate_routing); returns the int32 status tensor [1] (0 =
+    valid, else a bitmask of ROUTE_*), written on the stream without a host read-back."""
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=route["sorted_ids"].device)
+    _check(load().w4a16_validate_routing(_ptr(topk_ids) if topk_ids is not None else None, route["R"], route["E"],
+                                         route["block_m"], ctypes.c_void_p(route["sorted_ids"].data_ptr()),
+                                         ctypes.c_void_p(route["expert_ids"].data_ptr()),
+                                         _ptr(route["num_tokens_padded"]), route["sorted_ids"].numel(),
+                                         _ptr(status), _stream(stream)))
+    return status
+
 
 def plan_select(T: int, k: int, E: int, N: int, K: int, expected_rows_per_expert: float = 0.0) -> Plan:
     p = Plan()
