@@ -105,3 +105,39 @@ def check_act(got_bits: np.ndarray, gu_ref: np.ndarray, topk_flat: np.ndarray, E
     if inv.size:
         assert np.all(got_bits[inv] == POISON), "%s: a row of a non-local route was written" % label
     return worst
+
+
+# Fused expert MLP bar, per token t: max|gpu - oracle| <= FUSED_TOL * S_t with S_t = sum_j |tw[t,j]| * max|y_j|
+# over the token's valid routes j (y_j: the oracle's binary32 down-projection row of route t*k + j).  S_t is the
+# scale the token's weighted sum is built from: a route's y_j may be off by the GEMM bar times max|y_j|, and the
+# combine adds those errors with weights tw.  Normalising by max|out_t| instead would make the bar depend on how
+# far the k weighted rows cancel.  The BF16 rounding of the output (at most 2^-9 of |out_t| <= S_t) is inside.
+FUSED_TOL = 5e-3
+
+
+def check_fused(got_bits: np.ndarray, out_acc: np.ndarray, y: np.ndarray, tw: np.ndarray, ids: np.ndarray, E: int,
+                tol: float = FUSED_TOL, label: str = ""):
+    """Fused MLP output [T,H] (BF16 bits) against the oracle's combine accumulators out_acc [T,H] (before the
+    final rounding) to the bar above; tokens without a valid route must be all zero.  Returns (worst error /
+    S_t, worst error / max|out_t|), the second only reported."""
+    ids = np.asarray(ids)
+    T, k = ids.shape
+    g = bf16_to_f64(got_bits)
+    worst, worst_plain = 0.0, 0.0
+    for t in range(T):
+        valid = (ids[t] >= 0) & (ids[t] < E)
+        if not valid.any():
+            assert np.all(got_bits[t] == 0), "%s token %d without a local route must be zero" % (label, t)
+            continue
+        scale = sum(abs(float(tw[t, j])) * np.abs(y[t * k + j]).max() for j in range(k) if valid[j])
+        err = np.abs(g[t] - out_acc[t]).max()
+        if scale == 0.0:
+            assert err == 0.0, "%s token %d" % (label, t)
+            continue
+        ratio = err / scale
+        worst = max(worst, ratio)
+        den = np.abs(out_acc[t]).max()
+        if den > 0:
+            worst_plain = max(worst_plain, err / den)
+        assert ratio <= tol, "%s token %d: error %.3g of S_t (bar %.3g)" % (label, t, ratio, tol)
+    return worst, worst_plain
