@@ -80,8 +80,21 @@ typedef struct w4a16_plan {
                               or 144, with block_m 32 64 or 128, and a workgroup takes up to
                               tile_m / block_m consecutive route blocks of one expert; otherwise
                               tile_m equals block_m (64 or 128).  decode: 0 */
-    int32_t reserved[2];   /* must be zero */
+    int32_t flags;         /* 0, or W4A16_PLAN_ONE_LAUNCH on the gate_up plan of a fused call */
+    int32_t reserved[1];   /* must be zero */
 } w4a16_plan;
+
+/* Plan flag, read on the gate_up plan of w4a16_fused_moe_planned: run a decode
+ * step's gate_up and down GEMMs in one launch, down's workgroups of a route
+ * block starting once gate_up has stored that block's rows of h (humans& page,
+ * "Blackwell hides the conversion work").  Applies when both plans are decode
+ * plans of 16-row blocks on the register-streaming kernel, the step has at
+ * most 4096 routes and both weight sets share a format; otherwise ignored.
+ * Outputs are bit-identical either way.  The planner never sets it: on the
+ * Qwen3-, Kimi-K2- and DeepSeek-V3-shaped decode steps the two launches were
+ * faster (one kernel's register budget for both GEMMs, and no tail of gate_up
+ * for down to fill). */
+#define W4A16_PLAN_ONE_LAUNCH 1
 
 /* Host handle describing one packed weight set (E experts of N x K). */
 typedef struct w4a16_weights w4a16_weights;

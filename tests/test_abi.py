@@ -142,6 +142,14 @@ def test_plan_validation(lib):
     assert lib.w4a16_gemm_workspace_bytes(ctypes.byref(bad), 32, 8, 512, ctypes.byref(sz)) == -2
     good = L.make_plan("decode", 16, 4, 4)
     assert lib.w4a16_gemm_workspace_bytes(ctypes.byref(good), 32, 8, 512, ctypes.byref(sz)) == 0
+    # plan flags: W4A16_PLAN_ONE_LAUNCH is the only one; the reserved word stays zero
+    assert lib.w4a16_gemm_workspace_bytes(ctypes.byref(L.make_plan("decode", 16, 4, 4, flags=1)), 32, 8, 512,
+                                          ctypes.byref(sz)) == 0
+    assert lib.w4a16_gemm_workspace_bytes(ctypes.byref(L.make_plan("decode", 16, 4, 4, flags=2)), 32, 8, 512,
+                                          ctypes.byref(sz)) == -1
+    bad = L.make_plan("decode", 16, 4, 4)
+    bad.reserved[0] = 1
+    assert lib.w4a16_gemm_workspace_bytes(ctypes.byref(bad), 32, 8, 512, ctypes.byref(sz)) == -1
     assert sz.value == 0
     # prefill tiles: 64 or 128 rows, taller than the route block only for 32-row blocks; 16-row blocks take
     # tiles of 64 or 144 rows and two n-blocks per wavefront; decode has none

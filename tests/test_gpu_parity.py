@@ -817,6 +817,60 @@ def test_fused_moe_equals_sequence(orc, shape, plans):
     _say("  fused worst %.2e of S_t (%.2e of max|out|)" % (worst, plain))
 
 
+@pytest.mark.parametrize("shape,plans,fmt", [((32, 64, 4, 512, 256), None, "int4"), ((2, 48, 8, 512, 256), SPLIT_GU, "int4"),
+                                             ((3, 48, 8, 2048, 256), SPLIT_GU_ONLY, "int4"),
+                                             ((2, 48, 8, 512, 2048), None, "int4"), ((5, 1, 2, 256, 64), None, "int4"),
+                                             ((512, 1024, 8, 256, 128), None, "int4"),
+                                             ((40, 300, 3, 256, 128), None, "mxfp4"),
+                                             ((600, 512, 8, 256, 128), None, "int4")],
+                         ids=["T32-E64", "T2-E48-both-splitK", "T3-E48-gate-up-splitK", "T2-E48-down-splitK", "T5-E1",
+                              "T512-E1024-4096-routes", "T40-E300-mxfp4", "T600-E512-flag-ignored"])
+def test_fused_moe_one_launch(orc, shape, plans, fmt):
+    """W4A16_PLAN_ONE_LAUNCH: gate_up and down of a decode step in one launch, down's workgroups of a route block
+    waiting for that block's rows of h.  Bit for bit the two-launch call with the same plans, every graph replay
+    too (the wait counters reset themselves); past 4096 routes the flag is ignored."""
+    T, E, k, H, I = shape
+    _say("one launch %s %s" % (shape, fmt))
+    rng = np.random.default_rng(T * 17 + E)
+    x = synth.activations(rng, T, H)
+    c13, c2 = synth.codes(rng, E, 2 * I, H), synth.codes(rng, E, H, I)
+    if fmt == "mxfp4":
+        s13, s2 = synth.mxfp4_scales(rng, E, 2 * I, H, 120, 124), synth.mxfp4_scales(rng, E, H, I, 120, 124)
+        w13, w2 = _pack_mx(c13, s13), _pack_mx(c2, s2)
+    else:
+        s13, s2 = synth.scales(rng, E, 2 * I, H), synth.scales(rng, E, H, I)
+        w13, w2 = _pack(c13, s13), _pack(c2, s2)
+    ids = synth.uniform_topk(rng, T, E, k) if E >= k else np.zeros((T, k), np.int32)
+    ids[0, :] = -1
+    ids[T - 1, 0] = E + 3
+    tw = rng.uniform(0.1, 1.0, (T, k)).astype(np.float32)
+    two = w4.fused_moe_plans(T, k, w13, w2) if plans is None else (w4.make_plan(*plans[0]), w4.make_plan(*plans[1]))
+    one = w4.lib.one_launch(two)
+    assert one[0].flags == w4.lib.PLAN_ONE_LAUNCH and two[0].flags == 0
+    xd, idsd, twd = u16(x), i32(ids), f32(tw)
+    ref = bits(w4.fused_moe(xd, idsd, twd, w13, w2, plans=two))
+    ws = w4.zeroed_workspace(w4.fused_moe_workspace_bytes(T, k, w13, w2, one), xd.device)
+    out = torch.full((T, H), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    w4.fused_moe(xd, idsd, twd, w13, w2, out=out, ws=ws, plans=one)
+    got = bits(out)
+    assert np.array_equal(got, ref), "one launch differs from two in %d values" % int((got != ref).sum())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        w4.fused_moe(xd, idsd, twd, w13, w2, out=out, ws=ws, plans=one)
+    for rep in range(3):
+        out.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out), ref), "replay %d differs" % rep
+        w4.fused_moe(xd, idsd, twd, w13, w2, out=out, ws=ws, plans=one)  # eager work between replays
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out), ref)
+    _, _, y_ref = orc.fused_moe(x, ids, tw, c13, s13, c2, s2, fmt=fmt)
+    worst, plain = check_fused(got, orc.last_out_acc, y_ref, tw, ids, E, label="one launch")
+    _say("  fused worst %.2e of S_t (%.2e of max|out|)" % (worst, plain))
+
+
 def test_fused_moe_planned_and_hint(orc):
     """Caller-chosen plans: the call's own plans give the same bits as the plain call; an expert-parallel share
     (48 local experts of 384, about 1/8 of routes local) gets decode plans from the rows-per-expert hint where

@@ -184,8 +184,8 @@ w4a16_plan select_plan(int T, int k, int E, int N, int K, float rows) {
 
 int validate_plan(const w4a16_plan* p, const char* what) {
     if (!p) return fail(W4A16_INVALID_ARG, "%s: plan is NULL", what);
-    for (int i = 0; i < 2; ++i)
-        if (p->reserved[i]) return fail(W4A16_INVALID_ARG, "%s: plan.reserved must be zero", what);
+    if (p->reserved[0]) return fail(W4A16_INVALID_ARG, "%s: plan.reserved must be zero", what);
+    if (p->flags & ~W4A16_PLAN_ONE_LAUNCH) return fail(W4A16_INVALID_ARG, "%s: unknown plan flags 0x%x", what, p->flags);
     if (p->kernel == W4A16_KERNEL_DECODE) {
         if (p->block_m % 16 || p->block_m < 16 || p->block_m > 64)
             return fail(W4A16_UNSUPPORTED_SHAPE, "%s: decode block_m %d not in {16,32,48,64}", what, p->block_m);
@@ -851,18 +851,61 @@ int w4a16_moe_combine(const float* y, const float* topk_w, const int32_t* topk_i
     return check_launch(launch_combine(y, topk_w, topk_ids, T, k, E, H, out, s), "w4a16_moe_combine");
 }
 
-// Fused workspace: split-K area shared by both GEMMs (counters at the start, sized for the larger of the two),
-// then routing tensors and intermediates.
-static FusedLayout fused_full_layout(int T, int k, const w4a16_weights* w13, const w4a16_weights* w2,
-                                     const w4a16_plan& p13, const w4a16_plan& p2, size_t* counter_bytes) {
+// A decode step of 16-row blocks on the register-streaming kernel with at most kSelfRouteMaxRoutes routes routes its
+// rows inside the gate_up kernel (every gate_up workgroup reads all the ids twice, so larger steps keep the routing
+// launch).  With W4A16_PLAN_ONE_LAUNCH on the gate_up plan such a step also runs down in the same launch (down's
+// workgroups of a route block start once gate_up has stored that block's rows of h; both route in-kernel) when
+// down's plan is one too and both weight sets have one format.
+constexpr int kSelfRouteMaxRoutes = 4096;
+
+static bool fused_self_route(int R, int E, const GemmArgs& g13, const w4a16_plan& p13) {
+    return p13.kernel == W4A16_KERNEL_DECODE && p13.block_m == 16 && R <= kSelfRouteMaxRoutes &&
+           E <= W4A16_MAX_EXPERTS && decode_reg_supported(g13, p13);
+}
+
+// Fused workspace.  Zero at rest, from offset 0: the sync words of the one-launch step (if it runs as one launch)
+// and the split-K counters.  Two GEMMs in one launch each get their own split-K area; two GEMMs in consecutive
+// launches share one (counters at the start, sized for the larger).  Then the routing tensors and intermediates.
+struct FusedPlan {
+    FusedLayout f;
+    bool one_launch;
+    size_t off_sync, off_c13, off_p13, off_c2, off_p2;  // one launch: both split areas; else off_c13/off_p13 shared
+    size_t zero_bytes;                                   // [0, zero_bytes) holds everything that is zero at rest
+};
+
+static FusedPlan fused_full_layout(int T, int k, const w4a16_weights* w13, const w4a16_weights* w2,
+                                   const w4a16_plan& p13, const w4a16_plan& p2) {
     const int E = w13->shape.E, H = w13->shape.K, I = w2->shape.K;
+    const int R = T * k;
     int maxP, maxB;
     route_bounds(T, k, E, p13.block_m, &maxP, &maxB);
     const GemmWs a = gemm_ws(w13->shape, p13, maxB), b = gemm_ws(w2->shape, p2, maxB);
-    *counter_bytes = a.counter_bytes > b.counter_bytes ? a.counter_bytes : b.counter_bytes;
-    const size_t partial_bytes = a.partial_bytes > b.partial_bytes ? a.partial_bytes : b.partial_bytes;
+    GemmArgs g13{nullptr, k, nullptr, w13->shape, nullptr, nullptr, R, maxB, nullptr, kOutAct};
+    GemmArgs g2{nullptr, 1, nullptr, w2->shape, nullptr, nullptr, R, maxB, nullptr, kOutF32};
+    FusedPlan fp;
+    fp.one_launch = (p13.flags & W4A16_PLAN_ONE_LAUNCH) && fused_self_route(R, E, g13, p13) &&
+                    decode_fused_supported(g13, p13, g2, p2);
+    size_t head;
+    if (fp.one_launch) {
+        fp.off_sync = 0;
+        fp.off_c13 = align_up(sizeof(unsigned) * (2 * (size_t)maxB + 1), 256);
+        fp.off_c2 = fp.off_c13 + a.counter_bytes;
+        fp.zero_bytes = fp.off_c2 + b.counter_bytes;
+        fp.off_p13 = fp.zero_bytes;
+        fp.off_p2 = fp.off_p13 + a.partial_bytes;
+        head = fp.off_p2 + b.partial_bytes;
+    } else {
+        const size_t cb = a.counter_bytes > b.counter_bytes ? a.counter_bytes : b.counter_bytes;
+        const size_t pb = a.partial_bytes > b.partial_bytes ? a.partial_bytes : b.partial_bytes;
+        fp.off_sync = 0;
+        fp.off_c13 = fp.off_c2 = 0;
+        fp.off_p13 = fp.off_p2 = cb;
+        fp.zero_bytes = cb;
+        head = cb + pb;
+    }
     const size_t tile_bytes = a.tile_bytes > b.tile_bytes ? a.tile_bytes : b.tile_bytes;
-    return fused_layout(T, k, E, H, I, p13.block_m, *counter_bytes + partial_bytes, tile_bytes);
+    fp.f = fused_layout(T, k, E, H, I, p13.block_m, head, tile_bytes);
+    return fp;
 }
 
 // The two weight handles form an expert MLP and the two plans can run it: each valid on its own, one route block
@@ -900,8 +943,7 @@ int w4a16_fused_moe_planned_workspace_bytes(int T, int k, const w4a16_weights* w
     if (!bytes) return fail(W4A16_INVALID_ARG, "%s: bytes is NULL", what);
     int rc = check_fused_plans(T, k, w13, w2, gate_up, down, what);
     if (rc) return rc;
-    size_t cb;
-    *bytes = fused_full_layout(T, k, w13, w2, *gate_up, *down, &cb).total;
+    *bytes = fused_full_layout(T, k, w13, w2, *gate_up, *down).f.total;
     return ok();
 }
 
@@ -976,8 +1018,8 @@ int w4a16_fused_moe_planned(const uint16_t* x, const int32_t* topk_ids, const fl
     if (!x || !topk_ids || !topk_w || !out) return fail(W4A16_INVALID_ARG, "%s: NULL pointer argument", what);
     if (!aligned16(x) || ((uintptr_t)out & 3u)) return fail(W4A16_INVALID_ARG, "%s: x must be 16-byte aligned", what);
     const w4a16_plan p13 = *gate_up, p2 = *down;
-    size_t counter_bytes;
-    const FusedLayout f = fused_full_layout(T, k, w13, w2, p13, p2, &counter_bytes);
+    const FusedPlan fp = fused_full_layout(T, k, w13, w2, p13, p2);
+    const FusedLayout& f = fp.f;
     if (!ws || ws_bytes < f.total)
         return fail(W4A16_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, needs %zu", what, ws_bytes, f.total);
     if (!aligned16(ws)) return fail(W4A16_INVALID_ARG, "%s: workspace must be 16-byte aligned", what);
@@ -1007,12 +1049,7 @@ int w4a16_fused_moe_planned(const uint16_t* x, const int32_t* topk_ids, const fl
                 return fail(W4A16_HIP_ERROR, "%s: event record failed: %s", what, hipGetErrorString(e_)); \
         }                                                                                  \
     } while (0)
-    // A decode step of up to kSelfRouteMaxRoutes routes on the register-streaming kernel routes its rows inside
-    // the gate_up kernel (which then writes the routing tensors down reads): one launch and its gap fewer.
-    // Every gate_up workgroup reads all the ids twice, so larger steps keep the routing preparation.
-    constexpr int kSelfRouteMaxRoutes = 4096;
-    const bool self_route = p13.kernel == W4A16_KERNEL_DECODE && p13.block_m == 16 && R <= kSelfRouteMaxRoutes &&
-                            E <= W4A16_MAX_EXPERTS && decode_reg_supported(g13, p13);
+    const bool self_route = fused_self_route(R, E, g13, p13);
     W4A16_STAGE(0);
     if (self_route) {
         g13.self_route_ids = topk_ids;
@@ -1024,13 +1061,28 @@ int w4a16_fused_moe_planned(const uint16_t* x, const int32_t* topk_ids, const fl
         if (rc) return rc;
     }
     W4A16_STAGE(1);
-    bind_ws(g13, gemm_ws(w13->shape, p13, f.maxB), base + f.off_split, counter_bytes, base + f.off_tiles);
-    rc = check_launch(run_gemm(g13, p13, s), "w4a16_fused_moe (gate_up + silu_mul)");
-    if (rc) return rc;
-    W4A16_STAGE(2);
-    bind_ws(g2, gemm_ws(w2->shape, p2, f.maxB), base + f.off_split, counter_bytes, base + f.off_tiles);
-    rc = check_launch(run_gemm(g2, p2, s), "w4a16_fused_moe (down)");
-    if (rc) return rc;
+    const GemmWs w13ws = gemm_ws(w13->shape, p13, f.maxB), w2ws = gemm_ws(w2->shape, p2, f.maxB);
+    bind_ws(g13, w13ws, base + f.off_split + fp.off_c13, fp.off_p13 - fp.off_c13, base + f.off_tiles);
+    bind_ws(g2, w2ws, base + f.off_split + fp.off_c2, fp.off_p2 - fp.off_c2, base + f.off_tiles);
+    if (fp.one_launch) {
+        // gate_up and down in one launch: down's workgroups of a route block start once gate_up has stored that
+        // block's rows of h (humans& page, "Blackwell hides the conversion work": the second GEMM's work begins
+        // before the first one ends); both route their rows in-kernel, nothing writes the routing tensors
+        g2.self_route_ids = topk_ids;
+        g13.sorted_ids = g13.expert_ids = g2.sorted_ids = g2.expert_ids = nullptr;
+        g13.ntp = g2.ntp = nullptr;
+        rc = check_launch(launch_gemm_decode_fused(g13, p13, g2, p2,
+                                                   reinterpret_cast<unsigned*>(base + f.off_split + fp.off_sync), s),
+                          "w4a16_fused_moe (gate_up + silu_mul + down, one launch)");
+        if (rc) return rc;
+        W4A16_STAGE(2);
+    } else {
+        rc = check_launch(run_gemm(g13, p13, s), "w4a16_fused_moe (gate_up + silu_mul)");
+        if (rc) return rc;
+        W4A16_STAGE(2);
+        rc = check_launch(run_gemm(g2, p2, s), "w4a16_fused_moe (down)");
+        if (rc) return rc;
+    }
     W4A16_STAGE(3);
     rc = check_launch(launch_combine(y, topk_w, topk_ids, T, k, E, H, out, s), "w4a16_fused_moe (combine)");
     if (rc) return rc;
@@ -1082,8 +1134,8 @@ extern "C" int w4a16_fused_moe_noalloc(const uint16_t* x, const int32_t* topk_id
     rc = check_fused_plans(T, k, w13, w2, &p13, &p2, what);
     if (rc) return rc;
     if (T == 0) return ok();
-    size_t counter_bytes;
-    const FusedLayout f = fused_full_layout(T, k, w13, w2, p13, p2, &counter_bytes);
+    const FusedPlan fp = fused_full_layout(T, k, w13, w2, p13, p2);
+    const FusedLayout& f = fp.f;
     if (f.total > W4A16_NOALLOC_SCRATCH_BYTES)
         return fail(W4A16_WORKSPACE_TOO_SMALL,
                     "%s: T=%d k=%d needs %zu bytes of intermediates, the static scratch holds %zu; use "
@@ -1093,9 +1145,10 @@ extern "C" int w4a16_fused_moe_noalloc(const uint16_t* x, const int32_t* topk_id
     void* ws = nullptr;
     rc = scratch_address(&ws, what);
     if (rc) return rc;
-    // the split-K counters start at zero: the scratch keeps whatever the last call left there
-    if (counter_bytes) {
-        rc = check_launch(launch_zero_words(static_cast<uint32_t*>(ws), counter_bytes / 4, s), what);
+    // the split-K counters and the one-launch step's sync words start at zero: the scratch keeps whatever the
+    // last call left there
+    if (fp.zero_bytes) {
+        rc = check_launch(launch_zero_words(static_cast<uint32_t*>(ws), fp.zero_bytes / 4, s), what);
         if (rc) return rc;
     }
     return w4a16_fused_moe_planned(x, topk_ids, topk_w, T, k, w13, w2, &p13, &p2, out, ws,

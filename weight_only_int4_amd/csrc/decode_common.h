@@ -47,18 +47,26 @@ __device__ __forceinline__ int slot_nblock(const Shape& sh, int wave_global, int
     return *o < sh.NB ? *o : sh.NB - 1;
 }
 
+// A BF16 output element; COH: device-coherent (visible to workgroups on other XCDs once the store completes).
+template <bool COH>
+__device__ __forceinline__ void store_bf16(uint16_t* dst, uint16_t v) {
+    if constexpr (COH) __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *dst = v;
+}
+
 // Epilogue shared by the decode kernels.  Lane (c, j) of wavefront w holds rows 4c + r of each 16-row tile and
-// column j of each of its NBW n-blocks.  With one K slice the results go straight to the output; with KS slices
-// every workgroup publishes its fp32 partial tile with device-coherent stores and bumps the tile's counter, and
-// the last to arrive adds the KS partials in slice order, writes the output and resets the counter.
-template <int MT, int NBW, int OM>
-__device__ __forceinline__ void decode_epilogue(const DecodeParams& p, const f32x4 (&acc)[MT][NBW], const int* ssid,
-                                                int* s_last, int b, int nt, int n_tiles, int wave_global, int w,
-                                                int c, int j) {
+// column j of each of its NBW n-blocks.  With one K slice (KS == 1) the results go straight to the output; with KS
+// slices every workgroup publishes its fp32 partial tile with device-coherent stores and bumps the tile's
+// counter, and the last to arrive adds the KS partials in slice order, writes the output and resets the counter.
+// Returns whether this workgroup wrote the output tile.  COH: BF16 and activation outputs are stored
+// device-coherently (read by other workgroups of the same launch).
+template <int MT, int NBW, int OM, bool COH = false>
+__device__ __forceinline__ bool decode_epilogue(const DecodeParams& p, const f32x4 (&acc)[MT][NBW], const int* ssid,
+                                                int* s_last, int b, int nt, int n_tiles, int KS, int ks,
+                                                int wave_global, int w, int c, int j) {
     constexpr int BM = 16 * MT;
     constexpr int COLS = NBW * 16 * kWaves;  // weight columns of the workgroup
     const Shape& sh = p.sh;
-    const int KS = gridDim.z, ks = blockIdx.z;
     if (KS == 1) {
         // lane holds rows 4c + r of each 16-row tile, column j of each of its n-blocks
 #pragma unroll
@@ -73,8 +81,8 @@ __device__ __forceinline__ void decode_epilogue(const DecodeParams& p, const f32
                     for (int q = 0; q < NBW / 2; ++q) {
                         const int n = (wave_global * (NBW / 2) + q) * 16 + j;
                         if (n >= NO) continue;
-                        static_cast<uint16_t*>(p.out)[(size_t)sid * NO + n] =
-                            f32_to_bf16_bits(silu_mul(acc[mt][q][r], acc[mt][q + NBW / 2][r]));
+                        store_bf16<COH>(static_cast<uint16_t*>(p.out) + (size_t)sid * NO + n,
+                                        f32_to_bf16_bits(silu_mul(acc[mt][q][r], acc[mt][q + NBW / 2][r])));
                     }
                 } else {
 #pragma unroll
@@ -84,11 +92,12 @@ __device__ __forceinline__ void decode_epilogue(const DecodeParams& p, const f32
                         if (OM == kOutF32)
                             static_cast<float*>(p.out)[(size_t)sid * sh.N + n] = acc[mt][q][r];
                         else
-                            static_cast<uint16_t*>(p.out)[(size_t)sid * sh.N + n] = f32_to_bf16_bits(acc[mt][q][r]);
+                            store_bf16<COH>(static_cast<uint16_t*>(p.out) + (size_t)sid * sh.N + n,
+                                            f32_to_bf16_bits(acc[mt][q][r]));
                     }
                 }
             }
-        return;
+        return true;
     }
 
     // split K: publish the partial tile, the last workgroup of the tile reduces in ks order
@@ -111,7 +120,7 @@ __device__ __forceinline__ void decode_epilogue(const DecodeParams& p, const f32
         *s_last = prev == (unsigned)(KS - 1);
     }
     __syncthreads();
-    if (!*s_last) return;
+    if (!*s_last) return false;
     const float* all = p.partials + tile * KS * (size_t)(BM * COLS);
     auto reduce = [&](int idx) {
         float v = 0.f;
@@ -131,7 +140,7 @@ __device__ __forceinline__ void decode_epilogue(const DecodeParams& p, const f32
             if (sid < 0 || n >= NO) continue;
             const int gcol = (ww * NBW + q) * 16 + jj;
             const float g = reduce(m * COLS + gcol), u = reduce(m * COLS + gcol + HB * 16);
-            static_cast<uint16_t*>(p.out)[(size_t)sid * NO + n] = f32_to_bf16_bits(silu_mul(g, u));
+            store_bf16<COH>(static_cast<uint16_t*>(p.out) + (size_t)sid * NO + n, f32_to_bf16_bits(silu_mul(g, u)));
         }
     } else {
         const int n_base = nt * COLS;
@@ -144,10 +153,11 @@ __device__ __forceinline__ void decode_epilogue(const DecodeParams& p, const f32
             if (OM == kOutF32)
                 static_cast<float*>(p.out)[(size_t)sid * sh.N + n] = v;
             else
-                static_cast<uint16_t*>(p.out)[(size_t)sid * sh.N + n] = f32_to_bf16_bits(v);
+                store_bf16<COH>(static_cast<uint16_t*>(p.out) + (size_t)sid * sh.N + n, f32_to_bf16_bits(v));
         }
     }
     if (threadIdx.x == 0) __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
 }
 
 }  // namespace decode

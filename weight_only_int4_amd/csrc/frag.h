@@ -134,10 +134,11 @@ __device__ __forceinline__ float e8m0_scale(uint32_t four_bytes, int d) {
 }
 
 // Buffer resources (raw, unformatted, unswizzled) on gfx9-family chips: word 3 of the descriptor, the cache
-// policy bit of a non-temporal load, and an offset no resource reaches (a load from it returns zeros; a direct
+// policy bits of a non-temporal and of a device-coherent load, and an offset no resource reaches (a load from it returns zeros; a direct
 // load to LDS from it writes zeros).
 constexpr int kBufferWord3 = 0x00020000;
 constexpr int kBufferNonTemporal = 2;
+constexpr int kBufferDeviceCoherent = 16;  // the sc1 bit: the load is coherent at device scope
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_resource(const void* base, uint32_t bytes) {

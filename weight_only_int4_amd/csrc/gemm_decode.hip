@@ -224,7 +224,8 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_kernel(DecodeParam
         }
     }
 
-    decode_epilogue<MT, NBW, OM>(p, acc, ssid, &s_last, b, blockIdx.y, gridDim.y, wave_global, w, c, j);
+    decode_epilogue<MT, NBW, OM>(p, acc, ssid, &s_last, b, blockIdx.y, gridDim.y, gridDim.z, blockIdx.z, wave_global,
+                                 w, c, j);
 }
 
 

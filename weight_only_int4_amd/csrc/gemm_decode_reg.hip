@@ -81,16 +81,32 @@ __device__ __forceinline__ int wg_exclusive_scan(int v, int* wt, int* total) {
 // The workgroups of column tile 0 (first K slice) write their block's sorted_ids and expert_ids, and workgroup 0
 // num_tokens_padded, for the GEMMs that follow; decode rows are independent of their slot, so the outputs are
 // those of the routed path bit for bit.
-template <int NBW, int D, int OM, int FMT, bool SR = false>
-__global__ __launch_bounds__(kDecodeThreads, 1) void gemm_decode_reg_kernel(DecodeParams p) {
+// The two GEMMs of the fused decode step in one launch (gate_up workgroups first, then down workgroups): a route
+// block's down workgroups wait until every gate_up column tile of that block has stored its rows of h, so down's
+// work starts while gate_up's last workgroups still run, with no launch boundary between them.
+struct FusedSync {
+    unsigned* ready;     // [route blocks]: gate_up column tiles whose rows of h are stored; zero at rest
+    unsigned* done;      // [route blocks]: down workgroups finished; the last one resets both; zero at rest
+    unsigned* timeouts;  // counts down workgroups that stopped waiting (never in a correct launch)
+    unsigned ready_target, done_target;
+};
+constexpr int kRolePlain = 0, kRoleGateUp = 1, kRoleDown = 2;
+// bounded wait of a down workgroup: about a second of polling (the gate_up workgroups it waits for were dispatched
+// before it and wait on nothing, so this bound is never reached in a correct launch; it only guarantees an end)
+constexpr unsigned kMaxPolls = 1u << 24;
+
+// One workgroup of the kernel: route block x column tile x K slice (ks of KS), from the workgroup's index id
+// among the n_tiles * route-block positions of its slice.
+template <int NBW, int D, int OM, int FMT, bool SR, int ROLE>
+__device__ __forceinline__ void decode_reg_body(const DecodeParams& p, const int id, const int n_tiles, const int KS,
+                                                const int ks, int* ssid, int* s_last, int* sr_lds,
+                                                const FusedSync& fs) {
     constexpr int SB = sb_bytes(FMT);
     constexpr bool MX = FMT == kFmtMxfp4;
     static_assert(OM != kOutAct || NBW % 2 == 0, "the activation epilogue pairs gate and up n-blocks");
     static_assert(D >= 2 && D <= 6, "ring depth");
-    __shared__ int ssid[16];
-    __shared__ int s_last;
-    // SR: per-expert counts [E], first block of each expert [E + 1], wavefront totals of the scans
-    __shared__ int sr_lds[SR ? 2 * W4A16_MAX_EXPERTS + 8 : 1];
+    // activation loads of the down role read h that other workgroups of this launch stored: device-coherent
+    constexpr int kActAux = ROLE == kRoleDown ? kBufferDeviceCoherent : 0;
     int* const cnt = sr_lds;
     int* const boff = sr_lds + W4A16_MAX_EXPERTS;
     int* const wt = sr_lds + 2 * W4A16_MAX_EXPERTS + 2;
@@ -99,7 +115,6 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void gemm_decode_reg_kernel(Deco
     // in turn, so id -> (XCD, position) is remapped to give every XCD a contiguous run of the valid (route
     // block, column tile) pairs, route block major; an XCD then gathers the activation rows of its own route
     // blocks only, and its L2 holds them while its weight streams pass through.
-    const int n_tiles = gridDim.y;
     int valid;
     if constexpr (SR) {
         const int E = p.sh.E, tid = threadIdx.x;
@@ -128,13 +143,13 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void gemm_decode_reg_kernel(Deco
         if (tid == 0) boff[E] = tot;
         __syncthreads();
         tot = __builtin_amdgcn_readfirstlane(tot);
-        if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0) *p.ntp_out = tot * 16;
+        if (p.ntp_out && id == 0 && ks == 0 && tid == 0) *p.ntp_out = tot * 16;
         valid = min(tot, p.route_blocks);
     } else {
         valid = p.ntp ? min(__builtin_amdgcn_readfirstlane(*p.ntp) / 16, p.route_blocks) : p.route_blocks;
     }
     const int V = valid * n_tiles;
-    const int id = blockIdx.x + gridDim.x * blockIdx.y;  // gridDim.x * gridDim.y is a multiple of 8
+    // id: the number of positions per slice is a multiple of 8, so id % 8 is the workgroup's XCD
     const int per_xcd = (V + kXcds - 1) / kXcds;
     const int pos = id / kXcds, slot = (id % kXcds) * per_xcd + pos;
     if (pos >= per_xcd || slot >= V) return;
@@ -163,7 +178,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void gemm_decode_reg_kernel(Deco
             if (carry >= first + 16) break;  // uniform: every later route of e ranks past this block
         }
         __syncthreads();
-        if (nt == 0 && blockIdx.z == 0) {
+        if (p.sorted_out && nt == 0 && ks == 0) {
             if (threadIdx.x < 16) p.sorted_out[b * 16 + threadIdx.x] = ssid[threadIdx.x] >= 0 ? ssid[threadIdx.x] : p.R;
             if (threadIdx.x == 0) p.eids_out[b] = e;
         }
@@ -177,7 +192,6 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void gemm_decode_reg_kernel(Deco
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), L = threadIdx.x & 63;
     const int c = L >> 4, j = L & 15;
     const int wave_global = nt * kWaves + w;
-    const int KS = gridDim.z, ks = blockIdx.z;
     const int nst = (sh.G + 3) / 4;
     const int st_begin = (int)((long)ks * nst / KS), st_end = (int)((long)(ks + 1) * nst / KS);
 
@@ -197,6 +211,20 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void gemm_decode_reg_kernel(Deco
         const uint32_t nb = (uint32_t)slot_nblock<NBW, OM>(sh, wave_global, q, &o);
         cw_off[q] = nb * sh.KB * SB + (uint32_t)L * 16u;
         sc_off[q] = nb * sh.KB * SB + SB_CODE_BYTES + (uint32_t)j * (MX ? 8u : 16u);
+    }
+    if constexpr (ROLE == kRoleDown) {
+        // every gate_up column tile of route block b has stored its rows of h
+        if (threadIdx.x == 0) {
+            unsigned polls = 0;
+            while (__hip_atomic_load(&fs.ready[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < fs.ready_target) {
+                __builtin_amdgcn_s_sleep(2);
+                if (++polls == kMaxPolls) {
+                    __hip_atomic_fetch_add(fs.timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+            }
+        }
+        __syncthreads();
     }
     // activations: lane (c, j) reads row j of the tile at k-slot c; sentinel rows read past the end (zeros)
     const uint32_t a_bytes = (uint32_t)(p.R / p.a_row_div) * (uint32_t)K * 2u;
@@ -229,7 +257,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void gemm_decode_reg_kernel(Deco
             if constexpr (decltype(ragged)::value) {
                 if (st * KT + g * 32 >= K) off = kOutOfRange;
             }
-            S.xa[g] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, off, soff, 0));
+            S.xa[g] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, off, soff, kActAux));
         }
     };
     const std::false_type full{};
@@ -320,7 +348,57 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void gemm_decode_reg_kernel(Deco
     }
 
     __syncthreads();  // ssid is complete
-    decode_epilogue<1, NBW, OM>(p, acc, ssid, &s_last, b, nt, n_tiles, wave_global, w, c, j);
+    const bool wrote = decode_epilogue<1, NBW, OM, ROLE == kRoleGateUp>(p, acc, ssid, s_last, b, nt, n_tiles, KS, ks,
+                                                                        wave_global, w, c, j);
+    if constexpr (ROLE == kRoleGateUp) {
+        // this workgroup's rows of h are stored device-coherently: once every wavefront's stores have completed,
+        // count the column tile as ready for the block's down workgroups
+        if (wrote) {
+            wait_own_stores();
+            __syncthreads();
+            if (threadIdx.x == 0) __hip_atomic_fetch_add(&fs.ready[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    if constexpr (ROLE == kRoleDown) {
+        // the last down workgroup of the block resets both counters: every other one has passed its wait
+        if (threadIdx.x == 0) {
+            const unsigned prev = __hip_atomic_fetch_add(&fs.done[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (prev == fs.done_target - 1) {
+                __hip_atomic_store(&fs.ready[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(&fs.done[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+}
+
+template <int NBW, int D, int OM, int FMT, bool SR = false>
+__global__ __launch_bounds__(kDecodeThreads, 1) void gemm_decode_reg_kernel(DecodeParams p) {
+    __shared__ int ssid[16];
+    __shared__ int s_last;
+    // SR: per-expert counts [E], first block of each expert [E + 1], wavefront totals of the scans
+    __shared__ int sr_lds[SR ? 2 * W4A16_MAX_EXPERTS + 8 : 1];
+    // gridDim.x * gridDim.y is a multiple of 8
+    decode_reg_body<NBW, D, OM, FMT, SR, kRolePlain>(p, blockIdx.x + gridDim.x * blockIdx.y, gridDim.y, gridDim.z,
+                                                     blockIdx.z, ssid, &s_last, sr_lds, FusedSync{});
+}
+
+// gate_up (SiLU*mul into h) and down (binary32 y) of one decode step in one launch; both route their rows in-kernel.
+// Workgroups [0, ng) are gate_up's (pos_gu positions per K slice), the rest down's.
+template <int NBW1, int NBW2, int D, int FMT>
+__global__ __launch_bounds__(kDecodeThreads, 1) void gemm_decode_fused_kernel(DecodeParams gu, DecodeParams dn,
+                                                                              FusedSync fs, int ng, int pos_gu,
+                                                                              int nt_gu, int ks_gu, int pos_dn,
+                                                                              int nt_dn, int ks_dn) {
+    __shared__ int ssid[16];
+    __shared__ int s_last;
+    __shared__ int sr_lds[2 * W4A16_MAX_EXPERTS + 8];
+    const int x = blockIdx.x;
+    if (x < ng)
+        decode_reg_body<NBW1, D, kOutAct, FMT, true, kRoleGateUp>(gu, x % pos_gu, nt_gu, ks_gu, x / pos_gu, ssid, &s_last,
+                                                                  sr_lds, fs);
+    else
+        decode_reg_body<NBW2, D, kOutF32, FMT, true, kRoleDown>(dn, (x - ng) % pos_dn, nt_dn, ks_dn, (x - ng) / pos_dn,
+                                                                ssid, &s_last, sr_lds, fs);
 }
 
 // ring depths: two stages of INT4 weights (three wavefronts per SIMD fit), three of MXFP4 (its conversion leaves the
@@ -374,7 +452,69 @@ hipError_t dispatch_reg(const GemmArgs& a, const w4a16_plan& pl, hipStream_t s) 
     }
 }
 
+template <int NBW1, int NBW2, int FMT>
+hipError_t launch_fused_t(const GemmArgs& a13, const w4a16_plan& p13, const GemmArgs& a2, const w4a16_plan& p2,
+                          unsigned* sync, hipStream_t s) {
+    constexpr int D = FMT == kFmtMxfp4 ? kRingDepthMx : kRingDepth;
+    auto params = [](const GemmArgs& a) {
+        DecodeParams p{a.A, a.a_row_div, static_cast<const uint8_t*>(a.packed), a.sh, a.sorted_ids, a.expert_ids, a.R,
+                       a.out, a.partials, a.counters};
+        p.route_blocks = a.max_blocks;
+        p.topk = a.self_route_ids;  // both GEMMs route their rows in-kernel; nothing writes the routing tensors
+        return p;
+    };
+    const int gx = (a13.max_blocks + kXcds - 1) / kXcds * kXcds;
+    const int nt_gu = decode_n_tiles(a13.sh, p13), nt_dn = decode_n_tiles(a2.sh, p2);
+    const int pos_gu = gx * nt_gu, pos_dn = gx * nt_dn;
+    const int ng = pos_gu * p13.k_split;
+    FusedSync fs{sync, sync + a13.max_blocks, sync + 2 * a13.max_blocks, (unsigned)nt_gu, (unsigned)(nt_dn * p2.k_split)};
+    const unsigned grid = (unsigned)(ng + pos_dn * p2.k_split);
+    hipLaunchKernelGGL((gemm_decode_fused_kernel<NBW1, NBW2, D, FMT>), dim3(grid), dim3(kDecodeThreads), 0, s,
+                       params(a13), params(a2), fs, ng, pos_gu, nt_gu, p13.k_split, pos_dn, nt_dn, p2.k_split);
+    return hipGetLastError();
+}
+
+template <int NBW1, int FMT>
+hipError_t launch_fused_n2(const GemmArgs& a13, const w4a16_plan& p13, const GemmArgs& a2, const w4a16_plan& p2,
+                           unsigned* sync, hipStream_t s) {
+    switch (p2.n_blocks) {
+        case 2: return launch_fused_t<NBW1, 2, FMT>(a13, p13, a2, p2, sync, s);
+        case 4: return launch_fused_t<NBW1, 4, FMT>(a13, p13, a2, p2, sync, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int FMT>
+hipError_t launch_fused_fmt(const GemmArgs& a13, const w4a16_plan& p13, const GemmArgs& a2, const w4a16_plan& p2,
+                            unsigned* sync, hipStream_t s) {
+    switch (p13.n_blocks) {
+        case 2: return launch_fused_n2<2, FMT>(a13, p13, a2, p2, sync, s);
+        case 4: return launch_fused_n2<4, FMT>(a13, p13, a2, p2, sync, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
+
+bool decode_fused_supported(const GemmArgs& a13, const w4a16_plan& p13, const GemmArgs& a2, const w4a16_plan& p2) {
+    return p13.kernel == W4A16_KERNEL_DECODE && p2.kernel == W4A16_KERNEL_DECODE && decode_reg_supported(a13, p13) &&
+           decode_reg_supported(a2, p2) && a13.sh.fmt == a2.sh.fmt && a13.max_blocks == a2.max_blocks &&
+           (p13.n_blocks == 2 || p13.n_blocks == 4) && (p2.n_blocks == 2 || p2.n_blocks == 4) &&
+           a13.sh.E <= W4A16_MAX_EXPERTS;
+}
+
+hipError_t launch_gemm_decode_fused(const GemmArgs& a13, const w4a16_plan& p13, const GemmArgs& a2,
+                                    const w4a16_plan& p2, unsigned* sync, hipStream_t s) {
+    if (a13.max_blocks == 0) return hipSuccess;
+    if (!decode_fused_supported(a13, p13, a2, p2) || a13.self_route_ids == nullptr || a2.self_route_ids == nullptr ||
+        a13.out_mode != kOutAct || a2.out_mode != kOutF32 || sync == nullptr)
+        return hipErrorInvalidValue;
+    if ((p13.k_split > 1 && (a13.partials == nullptr || a13.counters == nullptr)) ||
+        (p2.k_split > 1 && (a2.partials == nullptr || a2.counters == nullptr)))
+        return hipErrorInvalidValue;
+    return a13.sh.fmt == kFmtMxfp4 ? launch_fused_fmt<kFmtMxfp4>(a13, p13, a2, p2, sync, s)
+                                   : launch_fused_fmt<kFmtInt4>(a13, p13, a2, p2, sync, s);
+}
 
 bool decode_reg_supported(const GemmArgs& a, const w4a16_plan& p) {
     // one 16-row tile; the buffer resources address below 2 GiB (one expert's packed weights, the activations)

@@ -159,6 +159,13 @@ size_t decode_counters(const Shape& sh, const w4a16_plan& p, int max_blocks);
 hipError_t launch_gemm_decode(const GemmArgs& a, const w4a16_plan& p, hipStream_t s);
 bool decode_reg_supported(const GemmArgs& a, const w4a16_plan& p);
 hipError_t launch_gemm_decode_reg(const GemmArgs& a, const w4a16_plan& p, hipStream_t s);
+// The decode step's gate_up (SiLU*mul into h) and down (binary32 y) in one launch, both on the register-streaming
+// kernel with in-kernel routing (self_route_ids set in both), down's workgroups of a route block starting once
+// gate_up's column tiles of that block have stored h.  sync: 2 * max_blocks + 1 words, zero at rest; each
+// GEMM's split-K area its own.
+bool decode_fused_supported(const GemmArgs& a13, const w4a16_plan& p13, const GemmArgs& a2, const w4a16_plan& p2);
+hipError_t launch_gemm_decode_fused(const GemmArgs& a13, const w4a16_plan& p13, const GemmArgs& a2,
+                                    const w4a16_plan& p2, unsigned* sync, hipStream_t s);
 hipError_t launch_gemm_prefill(const GemmArgs& a, const w4a16_plan& p, hipStream_t s);
 bool prefill_supported(const GemmArgs& a);
 // Rows per prefill workgroup tile (plan.tile_m, else block_m); 16- and 32-row route blocks are gathered into

@@ -35,11 +35,13 @@ class W4A16Error(RuntimeError):
 class Plan(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("block_m", ctypes.c_int32), ("n_blocks", ctypes.c_int32),
                 ("waves", ctypes.c_int32), ("k_split", ctypes.c_int32), ("tile_m", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 2)]
+                ("flags", ctypes.c_int32), ("reserved", ctypes.c_int32 * 1)]
 
     def __repr__(self):
         kind = {KERNEL_DECODE: "decode", KERNEL_PREFILL: "prefill"}.get(self.kernel, str(self.kernel))
         tile = ", tile_m=%d" % self.tile_m if self.tile_m else ""
+        if self.flags:
+            tile += ", flags=%d" % self.flags
         return "Plan(%s, block_m=%d, n_blocks=%d, waves=%d, k_split=%d%s)" % (kind, self.block_m, self.n_blocks,
                                                                             self.waves, self.k_split, tile)
 
@@ -283,11 +285,24 @@ def plan_select(T: int, k: int, E: int, N: int, K: int, expected_rows_per_expert
     return p
 
 
-def make_plan(kernel: str, block_m: int, n_blocks: int, waves: int, k_split: int = 1, tile_m: int = 0) -> Plan:
+PLAN_ONE_LAUNCH = 1  # W4A16_PLAN_ONE_LAUNCH
+
+
+def make_plan(kernel: str, block_m: int, n_blocks: int, waves: int, k_split: int = 1, tile_m: int = 0,
+              flags: int = 0) -> Plan:
     p = Plan()
     p.kernel = KERNEL_DECODE if kernel == "decode" else KERNEL_PREFILL
     p.block_m, p.n_blocks, p.waves, p.k_split, p.tile_m = block_m, n_blocks, waves, k_split, tile_m
+    p.flags = flags
     return p
+
+
+def one_launch(plans):
+    """The fused call's (gate_up, down) plans with W4A16_PLAN_ONE_LAUNCH set on the gate_up plan."""
+    p13, p2 = plans
+    q = Plan.from_buffer_copy(p13)
+    q.flags |= PLAN_ONE_LAUNCH
+    return q, p2
 
 
 def gemm_workspace_bytes(plan: Plan, R: int, E: int, N: int) -> int:
