@@ -503,6 +503,17 @@ def main():
                                "timing": "median of 5 trials, each HIP events around %d graph-captured "
                                          "back-to-back launches, after about 30 ms of the same launches"
                                          % (n_replay * reps)})
+    if p13.kernel == L.KERNEL_DECODE and p13.block_m == 16 and T * k <= 4096:
+        # inside the fused step this gate_up routes its rows itself (no routing launch): its stage time from the
+        # per-stage events, a launch gap included, against the same roofline
+        st = float(stage.mean(0)[stages.index("gate_up_silu")])
+        ach = (alg_flops / (st * 1e-6) / 1e12) if mfma_bound else (alg_bytes / (st * 1e-6) / 1e9)
+        result["roofline"]["step_form"] = {
+            "kernel": kname.replace("act out,", "act out, routes its rows in-kernel,"),
+            "stage_us": round(st, 2), "achieved": round(ach, 1),
+            "frac": round(ach / (MFMA_BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBS), 4),
+            "timing": "mean over the timed steps of HIP events around the gate_up stage of eager fused calls "
+                      "(includes the gap between launches)"}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(spec, inputs, weight_bytes_step, args.cpu_budget)
     print(json.dumps(result), flush=True)

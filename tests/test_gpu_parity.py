@@ -420,6 +420,15 @@ def test_gemm_prefill_tile_list(orc, plan_args):
     acc, _ = orc.grouped_gemm(case.A, 1, case.codes, case.scales, case.topk_ids, acc64=True)
     worst = check_gemm(got, acc, case.topk_ids, case.E, label="tile list")
     _say("  worst ratio %.2e" % worst)
+    # the same routing over N = 288 (two or three column tiles, the last one partial) in the integer regime,
+    # bit-exact
+    N2 = 288
+    xi = synth.to_bf16_bits(rng.integers(-2, 3, size=(ids.shape[0], K)).astype(np.float32))
+    ci = synth.codes(rng, E, N2, K)
+    si = np.full((E, N2, K // 32), 0x3D80, np.uint16)  # 2^-4
+    gi = _run_gemm(synth.GemmCase("tile list int", xi, 1, ci, si, ids), plan)
+    _, ref_bits = orc.grouped_gemm(xi, 1, ci, si, ids)
+    assert np.array_equal(gi, ref_bits), "tile list, integer regime over several column tiles: must be bit-exact"
 
 
 # ------------------------------------------------------------------ offsets form
