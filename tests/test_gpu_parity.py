@@ -780,14 +780,17 @@ SPLIT_GU_ONLY = (("decode", 16, 2, 4, 4), ("decode", 16, 4, 4, 1))
                                          ((64, 16, 4, 512, 256), None), ((2, 48, 8, 512, 2048), None),
                                          ((2, 48, 8, 512, 256), SPLIT_GU), ((3, 48, 8, 2048, 256), SPLIT_GU_ONLY),
                                          ((512, 1024, 8, 256, 128), None), ((600, 512, 8, 256, 128), None),
-                                         ((40, 300, 3, 256, 128), None), ((5, 1, 2, 256, 64), None)],
+                                         ((40, 300, 3, 256, 128), None), ((5, 1, 2, 256, 64), None),
+                                         ((1024, 8, 2, 256, 128), None)],
                          ids=["T32-E64-decode", "T5-E8-H2016-decode", "T64-E16-prefill", "T2-E48-down-splitK",
                               "T2-E48-both-splitK", "T3-E48-H2048-gate-up-splitK", "T512-E1024-decode-4096-routes",
-                              "T600-E512-decode-4800-routes", "T40-E300-decode", "T5-E1-decode"])
+                              "T600-E512-decode-4800-routes", "T40-E300-decode", "T5-E1-decode",
+                              "T1024-E8-prefill-shared-tile-list"])
 def test_fused_moe_equals_sequence(orc, shape, plans):
     """The fused call is the sequence route_prep, gate_up with SiLU*mul, down (binary32), combine, with the same
     plans, bit for bit (decode, prefill and split-K plans; a token without a local route, one routed twice to
-    the same expert, a non-local route, a ragged last column tile).  Decode steps of up to 4096 routes route their
+    the same expert, a non-local route, a ragged last column tile; with prefill plans down reuses the tile list
+    gate_up built, including experts cut into two tiles).  Decode steps of up to 4096 routes route their
     rows inside the gate_up kernel: the largest such step over the most experts, more experts than the kernel has
     threads, a single expert, and gate_up plans that split K (every slice routes its rows) are among the shapes;
     a decode step of 4800 routes takes the separate routing launch."""

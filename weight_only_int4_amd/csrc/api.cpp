@@ -1064,6 +1064,10 @@ int w4a16_fused_moe_planned(const uint16_t* x, const int32_t* topk_ids, const fl
     const GemmWs w13ws = gemm_ws(w13->shape, p13, f.maxB), w2ws = gemm_ws(w2->shape, p2, f.maxB);
     bind_ws(g13, w13ws, base + f.off_split + fp.off_c13, fp.off_p13 - fp.off_c13, base + f.off_tiles);
     bind_ws(g2, w2ws, base + f.off_split + fp.off_c2, fp.off_p2 - fp.off_c2, base + f.off_tiles);
+    // both GEMMs tile the same routing the same way: down reuses the tile list gate_up builds (one area, same
+    // route blocks and tile height)
+    g2.tiles_ready = tiled_prefill(p13) && tiled_prefill(p2) && p13.block_m == p2.block_m &&
+                     prefill_tile_rows(p13) == prefill_tile_rows(p2);
     if (fp.one_launch) {
         // gate_up and down in one launch: down's workgroups of a route block start once gate_up has stored that
         // block's rows of h (humans& page, "Blackwell hides the conversion work": the second GEMM's work begins

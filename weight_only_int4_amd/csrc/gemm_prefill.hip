@@ -546,7 +546,7 @@ size_t prefill_counters(const Shape& sh, const w4a16_plan& p, int max_blocks) {
 hipError_t launch_gemm_prefill(const GemmArgs& a, const w4a16_plan& p, hipStream_t s) {
     if (a.max_blocks == 0) return hipSuccess;
     const int mt = prefill_tile_rows(p) / 16, rb16 = p.block_m / 16;
-    if (rb16 < mt) {
+    if (rb16 < mt && !a.tiles_ready) {
         hipError_t err = launch_tile_map(a.expert_ids, a.ntp, p.block_m, a.max_blocks, mt / rb16, a.tiles,
                                          a.tile_count, a.tile_scratch, s);
         if (err != hipSuccess) return err;

@@ -145,6 +145,7 @@ struct GemmArgs {
     int32_t* tiles = nullptr;      // prefill tiles of several route blocks: tile list (first block, blocks) pairs
     int32_t* tile_count = nullptr; // ... and its length (device)
     int32_t* tile_scratch = nullptr; // 2 * max_blocks ints the tile list is built with
+    bool tiles_ready = false;        // the tile list already holds this routing's tiles (built by an earlier GEMM)
     float* partials = nullptr;     // split-K partial tiles (decode, k_split > 1)
     unsigned* counters = nullptr;  // split-K arrival counters, zero between calls
     // decode gate_up only: route the rows in-kernel from these top-k ids [R] and write sorted_ids, expert_ids and
