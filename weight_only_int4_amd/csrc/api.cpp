@@ -852,11 +852,10 @@ int w4a16_moe_combine(const float* y, const float* topk_w, const int32_t* topk_i
 }
 
 // A decode step of 16-row blocks on the register-streaming kernel with at most kSelfRouteMaxRoutes routes routes its
-// rows inside the gate_up kernel (every gate_up workgroup reads all the ids twice, so larger steps keep the routing
-// launch).  With W4A16_PLAN_ONE_LAUNCH on the gate_up plan such a step also runs down in the same launch (down's
+// rows inside the gate_up kernel (every gate_up workgroup reads all the ids into LDS, so larger steps keep the
+// routing launch).  With W4A16_PLAN_ONE_LAUNCH on the gate_up plan such a step also runs down in the same launch (down's
 // workgroups of a route block start once gate_up has stored that block's rows of h; both route in-kernel) when
 // down's plan is one too and both weight sets have one format.
-constexpr int kSelfRouteMaxRoutes = 4096;
 
 static bool fused_self_route(int R, int E, const GemmArgs& g13, const w4a16_plan& p13) {
     return p13.kernel == W4A16_KERNEL_DECODE && p13.block_m == 16 && R <= kSelfRouteMaxRoutes &&

@@ -75,8 +75,9 @@ __device__ __forceinline__ int wg_exclusive_scan(int v, int* wt, int* total) {
 }
 
 // SR: in-kernel routing (gate_up of the fused decode step).  Instead of reading the routing tensors, every
-// workgroup counts the top-k ids per expert in LDS, lays the experts' 16-row blocks out in expert order (the
-// order the counting sort of the routing preparation gives), finds the expert of its own block and ranks that
+// workgroup copies the top-k ids to LDS and counts them per expert, lays the experts' 16-row blocks out in expert
+// order (the order the counting sort of the routing preparation gives), finds the expert of its own block, issues
+// the first stages' weight loads (they depend only on the expert and the column tile), and meanwhile ranks that
 // expert's routes by route index to pick its 16 rows, exactly the rows the routing preparation would put there.
 // The workgroups of column tile 0 (first K slice) write their block's sorted_ids and expert_ids, and workgroup 0
 // num_tokens_padded, for the GEMMs that follow; decode rows are independent of their slot, so the outputs are
@@ -110,6 +111,7 @@ __device__ __forceinline__ void decode_reg_body(const DecodeParams& p, const int
     int* const cnt = sr_lds;
     int* const boff = sr_lds + W4A16_MAX_EXPERTS;
     int* const wt = sr_lds + 2 * W4A16_MAX_EXPERTS + 2;
+    int* const ids = sr_lds + 2 * W4A16_MAX_EXPERTS + 8;  // the top-k ids, R <= kSelfRouteMaxRoutes
 
     // (route block, column tile) of this workgroup.  XCD-aware: consecutive workgroup ids go to the eight XCDs
     // in turn, so id -> (XCD, position) is remapped to give every XCD a contiguous run of the valid (route
@@ -122,6 +124,7 @@ __device__ __forceinline__ void decode_reg_body(const DecodeParams& p, const int
         __syncthreads();
         for (int i = tid; i < p.R; i += kDecodeThreads) {
             const int ee = p.topk[i];
+            ids[i] = ee;
             if (ee >= 0 && ee < E) atomicAdd(&cnt[ee], 1);
         }
         __syncthreads();
@@ -154,7 +157,7 @@ __device__ __forceinline__ void decode_reg_body(const DecodeParams& p, const int
     const int pos = id / kXcds, slot = (id % kXcds) * per_xcd + pos;
     if (pos >= per_xcd || slot >= V) return;
     const int b = slot / n_tiles, nt = slot % n_tiles;
-    int e;
+    int e, first = 0;
     if constexpr (SR) {
         // owner: the last expert whose first block is at or before b (empty experts share their successor's)
         int lo = 0, hi = p.sh.E - 1;
@@ -164,24 +167,7 @@ __device__ __forceinline__ void decode_reg_body(const DecodeParams& p, const int
             else hi = mid - 1;
         }
         e = __builtin_amdgcn_readfirstlane(lo);
-        const int first = 16 * (b - __builtin_amdgcn_readfirstlane(boff[e]));  // rank of the block's first row
-        if (threadIdx.x < 16) ssid[threadIdx.x] = -1;
-        __syncthreads();
-        int carry = 0;
-        for (int ch = 0; ch < p.R; ch += kDecodeThreads) {
-            const int i = ch + threadIdx.x;
-            const bool m = i < p.R && p.topk[i] == e;
-            int n;
-            const int r = carry + wg_exclusive_scan(m ? 1 : 0, wt, &n);
-            if (m && r >= first && r < first + 16) ssid[r - first] = i;
-            carry += __builtin_amdgcn_readfirstlane(n);
-            if (carry >= first + 16) break;  // uniform: every later route of e ranks past this block
-        }
-        __syncthreads();
-        if (p.sorted_out && nt == 0 && ks == 0) {
-            if (threadIdx.x < 16) p.sorted_out[b * 16 + threadIdx.x] = ssid[threadIdx.x] >= 0 ? ssid[threadIdx.x] : p.R;
-            if (threadIdx.x == 0) p.eids_out[b] = e;
-        }
+        first = 16 * (b - __builtin_amdgcn_readfirstlane(boff[e]));  // rank of the block's first row
     } else {
         e = p.expert_ids[b];
         if (e < 0 || e >= p.sh.E) return;  // unowned block (or ids from a larger expert count)
@@ -212,6 +198,48 @@ __device__ __forceinline__ void decode_reg_body(const DecodeParams& p, const int
         cw_off[q] = nb * sh.KB * SB + (uint32_t)L * 16u;
         sc_off[q] = nb * sh.KB * SB + SB_CODE_BYTES + (uint32_t)j * (MX ? 8u : 16u);
     }
+    // weight half of a stage's loads (the other half, the activations, needs the block's rows)
+    auto load_w = [&](int st, RegStage<NBW>& S) {
+        const int kb = st >> 1, h = st & 1;
+        const int soff_code = kb * SB + h * 1024, soff_scale = kb * SB + h * (MX ? 4 : 8);
+#pragma unroll
+        for (int q = 0; q < NBW; ++q) {
+            S.cw[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, cw_off[q], soff_code,
+                                                                                      kBufferNonTemporal));
+            if constexpr (MX) {
+                S.sc[q][0] = __builtin_amdgcn_raw_buffer_load_b32(wres, sc_off[q], soff_scale, 0);
+            } else {
+                const auto sv = __builtin_amdgcn_raw_buffer_load_b64(wres, sc_off[q], soff_scale, 0);
+                S.sc[q][0] = sv[0];
+                S.sc[q][1] = sv[1];
+            }
+        }
+    };
+    RegStage<NBW> ring[D];
+    if constexpr (SR) {
+        // the first stages' weights depend only on the expert and the column tile: they are in flight while the
+        // workgroup ranks the expert's routes to find its rows
+#pragma unroll
+        for (int d = 0; d < D - 1; ++d)
+            if (st_begin + d < st_end) load_w(st_begin + d, ring[d]);
+        if (threadIdx.x < 16) ssid[threadIdx.x] = -1;
+        __syncthreads();
+        int carry = 0;
+        for (int ch = 0; ch < p.R; ch += kDecodeThreads) {
+            const int i = ch + threadIdx.x;
+            const bool m = i < p.R && ids[i] == e;
+            int n;
+            const int r = carry + wg_exclusive_scan(m ? 1 : 0, wt, &n);
+            if (m && r >= first && r < first + 16) ssid[r - first] = i;
+            carry += __builtin_amdgcn_readfirstlane(n);
+            if (carry >= first + 16) break;  // uniform: every later route of e ranks past this block
+        }
+        __syncthreads();
+        if (p.sorted_out && nt == 0 && ks == 0) {
+            if (threadIdx.x < 16) p.sorted_out[b * 16 + threadIdx.x] = ssid[threadIdx.x] >= 0 ? ssid[threadIdx.x] : p.R;
+            if (threadIdx.x == 0) p.eids_out[b] = e;
+        }
+    }
     if constexpr (ROLE == kRoleDown) {
         // every gate_up column tile of route block b has stored its rows of h
         if (threadIdx.x == 0) {
@@ -235,21 +263,7 @@ __device__ __forceinline__ void decode_reg_body(const DecodeParams& p, const int
 
     // RAGGED: the stage may reach past K (only the last stage of K can); its groups past K are skipped by
     // reading zeros (the test is uniform per group since K is a multiple of 32)
-    auto load = [&](int st, RegStage<NBW>& S, auto ragged) {
-        const int kb = st >> 1, h = st & 1;
-        const int soff_code = kb * SB + h * 1024, soff_scale = kb * SB + h * (MX ? 4 : 8);
-#pragma unroll
-        for (int q = 0; q < NBW; ++q) {
-            S.cw[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, cw_off[q], soff_code,
-                                                                                      kBufferNonTemporal));
-            if constexpr (MX) {
-                S.sc[q][0] = __builtin_amdgcn_raw_buffer_load_b32(wres, sc_off[q], soff_scale, 0);
-            } else {
-                const auto sv = __builtin_amdgcn_raw_buffer_load_b64(wres, sc_off[q], soff_scale, 0);
-                S.sc[q][0] = sv[0];
-                S.sc[q][1] = sv[1];
-            }
-        }
+    auto load_a = [&](int st, RegStage<NBW>& S, auto ragged) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             uint32_t off = x_off + (uint32_t)g * 64u;
@@ -259,6 +273,10 @@ __device__ __forceinline__ void decode_reg_body(const DecodeParams& p, const int
             }
             S.xa[g] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, off, soff, kActAux));
         }
+    };
+    auto load = [&](int st, RegStage<NBW>& S, auto ragged) {
+        load_w(st, S);
+        load_a(st, S, ragged);
     };
     const std::false_type full{};
     const std::true_type ragged{};
@@ -308,7 +326,6 @@ __device__ __forceinline__ void decode_reg_body(const DecodeParams& p, const int
     // state (every stage issues the load D-1 stages ahead, none of them ragged) has no branches; the last stages
     // drain with guarded issues.
     const int full_end = min(st_end, K / KT);  // stages below this one lie entirely inside K
-    RegStage<NBW> ring[D];
     int st = st_begin;
     if (full_end - st_begin >= 2 * D - 1) {
         // the prologue issues its stages in order too, so that at the loop head every slot's loads are as old
@@ -316,7 +333,8 @@ __device__ __forceinline__ void decode_reg_body(const DecodeParams& p, const int
 #pragma unroll
         for (int d = 0; d < D - 1; ++d) {
             __builtin_amdgcn_sched_barrier(0);
-            load(st_begin + d, ring[d], full);
+            if constexpr (SR) load_a(st_begin + d, ring[d], full);
+            else load(st_begin + d, ring[d], full);
         }
         __builtin_amdgcn_sched_barrier(0);
         for (; st + 2 * D - 2 < full_end; st += D) {
@@ -333,7 +351,10 @@ __device__ __forceinline__ void decode_reg_body(const DecodeParams& p, const int
     } else {
 #pragma unroll
         for (int d = 0; d < D - 1; ++d)
-            if (st_begin + d < st_end) load(st_begin + d, ring[d], ragged);
+            if (st_begin + d < st_end) {
+                if constexpr (SR) load_a(st_begin + d, ring[d], ragged);
+                else load(st_begin + d, ring[d], ragged);
+            }
     }
     // drain: at most 2D-1 stages are left; their loads for stages past st_begin + D - 2 are issued here
 #pragma unroll
@@ -376,7 +397,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void gemm_decode_reg_kernel(Deco
     __shared__ int ssid[16];
     __shared__ int s_last;
     // SR: per-expert counts [E], first block of each expert [E + 1], wavefront totals of the scans
-    __shared__ int sr_lds[SR ? 2 * W4A16_MAX_EXPERTS + 8 : 1];
+    __shared__ int sr_lds[SR ? kSelfRouteLdsInts : 1];
     // gridDim.x * gridDim.y is a multiple of 8
     decode_reg_body<NBW, D, OM, FMT, SR, kRolePlain>(p, blockIdx.x + gridDim.x * blockIdx.y, gridDim.y, gridDim.z,
                                                      blockIdx.z, ssid, &s_last, sr_lds, FusedSync{});
@@ -391,7 +412,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void gemm_decode_fused_kernel(De
                                                                               int nt_dn, int ks_dn) {
     __shared__ int ssid[16];
     __shared__ int s_last;
-    __shared__ int sr_lds[2 * W4A16_MAX_EXPERTS + 8];
+    __shared__ int sr_lds[kSelfRouteLdsInts];
     const int x = blockIdx.x;
     if (x < ng)
         decode_reg_body<NBW1, D, kOutAct, FMT, true, kRoleGateUp>(gu, x % pos_gu, nt_gu, ks_gu, x / pos_gu, ssid, &s_last,
@@ -418,7 +439,8 @@ hipError_t launch_reg(const GemmArgs& a, const w4a16_plan& pl, hipStream_t s) {
     constexpr int D = kRingDepth, DMX = kRingDepthMx;
     if constexpr (OM == kOutAct) {
         if (a.self_route_ids) {
-            if (a.sh.E > W4A16_MAX_EXPERTS || a.ntp == nullptr) return hipErrorInvalidValue;
+            // the routing stages the ids and per-expert tables in LDS
+            if (a.sh.E > W4A16_MAX_EXPERTS || a.R > kSelfRouteMaxRoutes || a.ntp == nullptr) return hipErrorInvalidValue;
             p.topk = a.self_route_ids;
             p.sorted_out = const_cast<int32_t*>(a.sorted_ids);
             p.eids_out = const_cast<int32_t*>(a.expert_ids);
@@ -507,7 +529,8 @@ hipError_t launch_gemm_decode_fused(const GemmArgs& a13, const w4a16_plan& p13, 
                                     const w4a16_plan& p2, unsigned* sync, hipStream_t s) {
     if (a13.max_blocks == 0) return hipSuccess;
     if (!decode_fused_supported(a13, p13, a2, p2) || a13.self_route_ids == nullptr || a2.self_route_ids == nullptr ||
-        a13.out_mode != kOutAct || a2.out_mode != kOutF32 || sync == nullptr)
+        a13.out_mode != kOutAct || a2.out_mode != kOutF32 || sync == nullptr || a13.R > kSelfRouteMaxRoutes ||
+        a2.R > kSelfRouteMaxRoutes || a13.sh.E > W4A16_MAX_EXPERTS)
         return hipErrorInvalidValue;
     if ((p13.k_split > 1 && (a13.partials == nullptr || a13.counters == nullptr)) ||
         (p2.k_split > 1 && (a2.partials == nullptr || a2.counters == nullptr)))

@@ -130,6 +130,12 @@ hipError_t launch_offsets_to_route(const int32_t* offsets, int E, int rows_max, 
                                    int max_blocks, int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntp,
                                    hipStream_t s);
 
+// Routes up to which a decode gate_up routes its rows in-kernel (the top-k ids are staged in LDS).
+constexpr int kSelfRouteMaxRoutes = 4096;
+// LDS ints of that routing: per-expert counts [E], first block of each expert [E + 1], wavefront totals of the
+// scans, then the top-k ids [R]
+constexpr int kSelfRouteLdsInts = 2 * W4A16_MAX_EXPERTS + 8 + kSelfRouteMaxRoutes;
+
 struct GemmArgs {
     const uint16_t* A;
     int a_row_div;
