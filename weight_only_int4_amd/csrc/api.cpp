@@ -1049,13 +1049,21 @@ int w4a16_fused_moe_planned(const uint16_t* x, const int32_t* topk_ids, const fl
         }                                                                                  \
     } while (0)
     const bool self_route = fused_self_route(R, E, g13, p13);
+    // prefill plans that gather route blocks into tiles: the routing writes the tile list too (from the per-expert
+    // counts), and both GEMMs use it as it is
+    TileOut to;
+    if (!self_route && tiled_prefill(p13)) {
+        to.group = prefill_tile_rows(p13) / p13.block_m;
+        to.count = reinterpret_cast<int32_t*>(base + f.off_tiles);
+        to.tiles = to.count + 4;
+    }
     W4A16_STAGE(0);
     if (self_route) {
         g13.self_route_ids = topk_ids;
     } else {
         rc = check_launch(launch_route_prep_scratch(topk_ids, R, E, p13.block_m, f.maxP, f.maxB, sorted_ids, expert_ids,
                                                     ntp, offsets, counts, reinterpret_cast<int32_t*>(base + f.off_route),
-                                                    s),
+                                                    s, to),
                           "w4a16_fused_moe (route_prep)");
         if (rc) return rc;
     }
@@ -1063,9 +1071,10 @@ int w4a16_fused_moe_planned(const uint16_t* x, const int32_t* topk_ids, const fl
     const GemmWs w13ws = gemm_ws(w13->shape, p13, f.maxB), w2ws = gemm_ws(w2->shape, p2, f.maxB);
     bind_ws(g13, w13ws, base + f.off_split + fp.off_c13, fp.off_p13 - fp.off_c13, base + f.off_tiles);
     bind_ws(g2, w2ws, base + f.off_split + fp.off_c2, fp.off_p2 - fp.off_c2, base + f.off_tiles);
-    // both GEMMs tile the same routing the same way: down reuses the tile list gate_up builds (one area, same
-    // route blocks and tile height)
-    g2.tiles_ready = tiled_prefill(p13) && tiled_prefill(p2) && p13.block_m == p2.block_m &&
+    // both GEMMs tile the same routing the same way (one area, same route blocks and tile height): the tile list
+    // the routing wrote serves both
+    g13.tiles_ready = to.tiles != nullptr;
+    g2.tiles_ready = to.tiles != nullptr && tiled_prefill(p2) && p13.block_m == p2.block_m &&
                      prefill_tile_rows(p13) == prefill_tile_rows(p2);
     if (fp.one_launch) {
         // gate_up and down in one launch: down's workgroups of a route block start once gate_up has stored that

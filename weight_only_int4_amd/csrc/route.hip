@@ -53,6 +53,25 @@ __device__ int block_exclusive_scan(int v, int* wave_tot, int* total) {
     return excl;
 }
 
+// The tile list of the prefill GEMMs (the same records as tile_map_kernel builds from expert_ids), written by the
+// routing itself when the caller asks for it: thread e owns expert e, whose L route blocks start at block b0e, and
+// cuts them into ceil(L / group) tiles of as equal a size as possible (the first L % n one block larger).  The
+// scan is uniform: every thread of the workgroup calls this.
+template <int NT>
+__device__ void emit_tiles(const TileOut& to, int L, int b0e, int* wave_tot) {
+    const int n = L > 0 ? (L + to.group - 1) / to.group : 0;
+    int total;
+    const int t0 = block_exclusive_scan<NT>(n, wave_tot, &total);
+    if (n > 0) {
+        const int base = L / n, rem = L % n;
+        for (int i = 0; i < n; ++i) {
+            to.tiles[2 * (t0 + i)] = b0e + (i < rem ? i * (base + 1) : rem * (base + 1) + (i - rem) * base);
+            to.tiles[2 * (t0 + i) + 1] = i < rem ? base + 1 : base;
+        }
+    }
+    if (threadIdx.x == 0) *to.count = total;
+}
+
 // Shared memory layout (ints): cnt[E] | pad_off[E+1] | base[E] | wave_cnt[(NT / 64)][E] | wave_tot[(NT / 64)+1]
 template <int NT>
 __global__ __launch_bounds__(NT) void route_prep_kernel(const int32_t* __restrict__ ids, int R, int E, int BM,
@@ -61,7 +80,7 @@ __global__ __launch_bounds__(NT) void route_prep_kernel(const int32_t* __restric
                                                               int32_t* __restrict__ expert_ids,
                                                               int32_t* __restrict__ ntp_out,
                                                               int32_t* __restrict__ offsets_out,
-                                                              int32_t* __restrict__ counts_out) {
+                                                              int32_t* __restrict__ counts_out, TileOut to) {
     extern __shared__ int smem[];
     int* cnt = smem;
     int* pad_off = cnt + E;
@@ -100,6 +119,7 @@ __global__ __launch_bounds__(NT) void route_prep_kernel(const int32_t* __restric
         pad_off[E] = tot_p;
         *ntp_out = tot_p;
     }
+    if (to.tiles) emit_tiles<NT>(to, padded / BM, off_p / BM, wave_tot);
     __syncthreads();
 
     // every slot starts as the sentinel; the scatter below overwrites valid ones
@@ -180,7 +200,7 @@ __global__ __launch_bounds__(kThreads) void route_scan_kernel(int R, int E, int 
                                                               int32_t* __restrict__ expert_ids,
                                                               int32_t* __restrict__ ntp_out,
                                                               int32_t* __restrict__ offsets_out,
-                                                              int32_t* __restrict__ counts_out) {
+                                                              int32_t* __restrict__ counts_out, TileOut to) {
     extern __shared__ int smem[];
     int* pad_off = smem;
     int* wave_tot = pad_off + E + 1;
@@ -208,6 +228,7 @@ __global__ __launch_bounds__(kThreads) void route_scan_kernel(int R, int E, int 
         pad_off[E] = tot_p;
         *ntp_out = tot_p;
     }
+    if (to.tiles) emit_tiles<kThreads>(to, padded / BM, off_p / BM, wave_tot);
     __syncthreads();
     for (int p = tid; p < max_padded; p += kThreads) sorted_ids[p] = R;
     for (int b = tid; b < max_blocks; b += kThreads) {
@@ -469,14 +490,14 @@ __global__ __launch_bounds__(kThreads) void offsets_to_route_kernel(const int32_
 
 hipError_t launch_route_prep(const int32_t* topk_ids, int R, int E, int block_m, int max_padded, int max_blocks,
                              int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntp, int32_t* offsets,
-                             int32_t* counts, hipStream_t s) {
+                             int32_t* counts, hipStream_t s, TileOut to) {
     if (E <= kSmallThreads && R <= kSmallThreads) {
         // few routes and experts (decode steps): half the workgroup, half the barrier cost and LDS to clear;
         // thread e still owns expert e (measured: 0.5-0.7 us less at up to 512 routes, slower beyond)
         constexpr int NT = kSmallThreads, NW = NT / 64;
         const size_t shmem = sizeof(int) * ((size_t)E + (E + 1) + E + (size_t)NW * E + (NW + 1));
         hipLaunchKernelGGL(route_prep_kernel<NT>, dim3(1), dim3(NT), shmem, s, topk_ids, R, E, block_m,
-                           max_padded, max_blocks, sorted_ids, expert_ids, ntp, offsets, counts);
+                           max_padded, max_blocks, sorted_ids, expert_ids, ntp, offsets, counts, to);
         return hipGetLastError();
     }
     const size_t shmem = sizeof(int) * ((size_t)E + (E + 1) + E + (size_t)kWaves * E + (kWaves + 1));
@@ -484,7 +505,7 @@ hipError_t launch_route_prep(const int32_t* topk_ids, int R, int E, int block_m,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (shmem > 65536 && attr != hipSuccess) return attr;
     hipLaunchKernelGGL(route_prep_kernel<kThreads>, dim3(1), dim3(kThreads), shmem, s, topk_ids, R, E, block_m,
-                       max_padded, max_blocks, sorted_ids, expert_ids, ntp, offsets, counts);
+                       max_padded, max_blocks, sorted_ids, expert_ids, ntp, offsets, counts, to);
     return hipGetLastError();
 }
 
@@ -495,18 +516,18 @@ size_t route_prep_scratch_ints(int R, int E) {
 
 hipError_t launch_route_prep_scratch(const int32_t* topk_ids, int R, int E, int block_m, int max_padded,
                                      int max_blocks, int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntp,
-                                     int32_t* offsets, int32_t* counts, int32_t* scratch, hipStream_t s) {
+                                     int32_t* offsets, int32_t* counts, int32_t* scratch, hipStream_t s, TileOut to) {
     const int nchunks = (R + kChunk - 1) / kChunk;
     if (nchunks <= 2 || scratch == nullptr)
         return launch_route_prep(topk_ids, R, E, block_m, max_padded, max_blocks, sorted_ids, expert_ids, ntp,
-                                 offsets, counts, s);
+                                 offsets, counts, s, to);
     hipLaunchKernelGGL(route_count_kernel, dim3(nchunks), dim3(kThreads), sizeof(int) * (size_t)E, s, topk_ids, R,
                        E, scratch);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kThreads), sizeof(int) * ((size_t)E + 1 + kWaves + 1), s, R, E,
                        block_m, max_padded, max_blocks, nchunks, scratch, sorted_ids, expert_ids, ntp, offsets,
-                       counts);
+                       counts, to);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     const size_t scatter_lds = sizeof(int) * ((size_t)E + (size_t)kWaves * E);

@@ -110,14 +110,22 @@ hipError_t launch_pack_mxfp4(const uint8_t* codes, const uint8_t* scales, const 
                              hipStream_t s);
 hipError_t launch_dequant(const void* packed, const Shape& sh, int expert, float* out_f32, uint16_t* out_bf16,
                           hipStream_t s);
+// Optional output of the routing: the tile list of a prefill GEMM whose tiles gather `group` route blocks (the
+// records tile_map_kernel builds), written from the per-expert counts; tiles == nullptr: none.
+struct TileOut {
+    int group = 0;
+    int32_t* tiles = nullptr;
+    int32_t* count = nullptr;
+};
 hipError_t launch_route_prep(const int32_t* topk_ids, int R, int E, int block_m, int max_padded, int max_blocks,
                              int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntp, int32_t* offsets,
-                             int32_t* counts, hipStream_t s);
+                             int32_t* counts, hipStream_t s, TileOut to = TileOut{});
 // Ints of scratch the routing of R routes uses when spread over several workgroups (0: one workgroup does it).
 size_t route_prep_scratch_ints(int R, int E);
 hipError_t launch_route_prep_scratch(const int32_t* topk_ids, int R, int E, int block_m, int max_padded,
                                      int max_blocks, int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntp,
-                                     int32_t* offsets, int32_t* counts, int32_t* scratch, hipStream_t s);
+                                     int32_t* offsets, int32_t* counts, int32_t* scratch, hipStream_t s,
+                                     TileOut to = TileOut{});
 hipError_t launch_route_validate(const int32_t* topk_ids, int R, int E, int block_m, const int32_t* sorted_ids,
                                  const int32_t* expert_ids, const int32_t* ntp, int max_padded, int32_t* status,
                                  hipStream_t s);
