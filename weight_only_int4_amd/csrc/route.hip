@@ -20,6 +20,7 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kSmallThreads = 512;  // workgroup of the routing of few routes and experts
+constexpr int kRegChunks = 4;       // chunks of routes the one-workgroup routing keeps in registers
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
@@ -92,11 +93,15 @@ __global__ __launch_bounds__(NT) void route_prep_kernel(const int32_t* __restric
     for (int e = tid; e < E; e += NT) cnt[e] = 0;
     for (int x = tid; x < (NT / 64) * E; x += NT) wave_cnt[x] = 0;
     __syncthreads();
-    // the first chunk's ids stay in registers for the scatter below (one load fewer on the critical path when
-    // there are at most NT routes)
-    const int e_first = tid < R ? ids[tid] : -1;
-    if (e_first >= 0 && e_first < E) atomicAdd(&cnt[e_first], 1);
-    for (int i = tid + NT; i < R; i += NT) {
+    // the ids of the first kRegChunks chunks are loaded together and stay in registers for the scatter below, so
+    // neither pass waits on a load per chunk (later chunks, past kRegChunks * NT routes, are read again)
+    int e_reg[kRegChunks];
+#pragma unroll
+    for (int ci = 0; ci < kRegChunks; ++ci) e_reg[ci] = ci * NT + tid < R ? ids[ci * NT + tid] : -1;
+#pragma unroll
+    for (int ci = 0; ci < kRegChunks; ++ci)
+        if (e_reg[ci] >= 0 && e_reg[ci] < E) atomicAdd(&cnt[e_reg[ci]], 1);
+    for (int i = tid + kRegChunks * NT; i < R; i += NT) {
         const int e = ids[i];
         if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
     }
@@ -141,9 +146,10 @@ __global__ __launch_bounds__(NT) void route_prep_kernel(const int32_t* __restric
     while ((1 << nbits) < E) ++nbits;
     __syncthreads();  // sentinel stores complete before any scatter store
 
-    for (int chunk = 0; chunk < R; chunk += NT) {
+    // one chunk of NT routes, ranked in route order: earlier chunks (base), earlier wavefronts (wave_cnt), lower
+    // lanes with the same expert (a lane-match mask from one ballot per bit of the expert id)
+    auto scatter_chunk = [&](int chunk, int e) {
         const int i = chunk + tid;
-        const int e = chunk == 0 ? e_first : (i < R ? ids[i] : -1);
         const bool valid = e >= 0 && e < E;
         uint64_t match = __ballot(valid);
         for (int bit = 0; bit < nbits; ++bit) {
@@ -166,7 +172,12 @@ __global__ __launch_bounds__(NT) void route_prep_kernel(const int32_t* __restric
             wave_cnt[wave * E + e] = 0;
         }
         __syncthreads();
-    }
+    };
+#pragma unroll
+    for (int ci = 0; ci < kRegChunks; ++ci)
+        if (ci * NT < R) scatter_chunk(ci * NT, e_reg[ci]);  // uniform
+    for (int chunk = kRegChunks * NT; chunk < R; chunk += NT)
+        scatter_chunk(chunk, chunk + tid < R ? ids[chunk + tid] : -1);
 }
 
 // ---- the same routing tensors from several workgroups, for many routes (needs scratch)
