@@ -188,18 +188,24 @@ __global__ __launch_bounds__(NT) void route_prep_kernel(const int32_t* __restric
 // writes the sentinels and expert_ids.  (3) Each chunk's workgroup scatters its routes from those bases with the
 // same in-chunk ranking as above, so the order inside an expert is again ascending route index.
 constexpr int kChunk = 4 * kThreads;
+constexpr int kScanRegChunks = 16;  // chunk counts per expert the scan holds in registers (65536 routes)
 
 __global__ __launch_bounds__(kThreads) void route_count_kernel(const int32_t* __restrict__ ids, int R, int E,
                                                                int32_t* __restrict__ chunk_counts) {
     extern __shared__ int cnt[];
     const int tid = threadIdx.x, c = blockIdx.x;
+    const int end = min(R, (c + 1) * kChunk);
+    int e_reg[kChunk / kThreads];  // the chunk's ids, loaded together before the counter is cleared
+#pragma unroll
+    for (int u = 0; u < kChunk / kThreads; ++u) {
+        const int i = c * kChunk + u * kThreads + tid;
+        e_reg[u] = i < end ? ids[i] : -1;
+    }
     for (int e = tid; e < E; e += kThreads) cnt[e] = 0;
     __syncthreads();
-    const int end = min(R, (c + 1) * kChunk);
-    for (int i = c * kChunk + tid; i < end; i += kThreads) {
-        const int e = ids[i];
-        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
-    }
+#pragma unroll
+    for (int u = 0; u < kChunk / kThreads; ++u)
+        if (e_reg[u] >= 0 && e_reg[u] < E) atomicAdd(&cnt[e_reg[u]], 1);
     __syncthreads();
     for (int e = tid; e < E; e += kThreads) chunk_counts[(size_t)c * E + e] = cnt[e];
 }
@@ -216,14 +222,24 @@ __global__ __launch_bounds__(kThreads) void route_scan_kernel(int R, int E, int 
     int* pad_off = smem;
     int* wave_tot = pad_off + E + 1;
     const int tid = threadIdx.x;
-    // E <= kThreads: thread e owns expert e
+    // E <= kThreads: thread e owns expert e.  The first kScanRegChunks chunk counts are loaded together (no load
+    // waits behind the previous chunk's store), then replaced by the routes of expert e in earlier chunks.
     int c = 0;
-    if (tid < E)
-        for (int ch = 0; ch < nchunks; ++ch) {
-            const int v = chunk_base[(size_t)ch * E + tid];
-            chunk_base[(size_t)ch * E + tid] = c;  // routes of expert tid in earlier chunks
-            c += v;
+    if (tid < E) {
+        int v[kScanRegChunks];
+#pragma unroll
+        for (int ch = 0; ch < kScanRegChunks; ++ch) v[ch] = ch < nchunks ? chunk_base[(size_t)ch * E + tid] : 0;
+#pragma unroll
+        for (int ch = 0; ch < kScanRegChunks; ++ch) {
+            if (ch < nchunks) chunk_base[(size_t)ch * E + tid] = c;
+            c += v[ch];
         }
+        for (int ch = kScanRegChunks; ch < nchunks; ++ch) {
+            const int x = chunk_base[(size_t)ch * E + tid];
+            chunk_base[(size_t)ch * E + tid] = c;
+            c += x;
+        }
+    }
     const int padded = tid < E ? ceil_div(c, BM) * BM : 0;
     int tot_c, tot_p;
     const int off_c = block_exclusive_scan(c, wave_tot, &tot_c);
@@ -265,15 +281,26 @@ __global__ __launch_bounds__(kThreads) void route_scatter_kernel(const int32_t* 
     int* base = smem;
     int* wave_cnt = base + E;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = blockIdx.x;
+    const int end = min(R, (c + 1) * kChunk);
+    // the chunk's ids, loaded together up front
+    constexpr int kSubs = kChunk / kThreads;
+    int e_reg[kSubs];
+#pragma unroll
+    for (int u = 0; u < kSubs; ++u) {
+        const int i = c * kChunk + u * kThreads + tid;
+        e_reg[u] = i < end ? ids[i] : -1;
+    }
     for (int e = tid; e < E; e += kThreads) base[e] = chunk_base[(size_t)c * E + e];
     for (int x = tid; x < kWaves * E; x += kThreads) wave_cnt[x] = 0;
     int nbits = 1;
     while ((1 << nbits) < E) ++nbits;
     __syncthreads();
-    const int end = min(R, (c + 1) * kChunk);
-    for (int sub = c * kChunk; sub < end; sub += kThreads) {
+#pragma unroll
+    for (int u = 0; u < kSubs; ++u) {
+        const int sub = c * kChunk + u * kThreads;
+        if (sub >= end) break;  // uniform
         const int i = sub + tid;
-        const int e = i < end ? ids[i] : -1;
+        const int e = e_reg[u];
         const bool valid = e >= 0 && e < E;
         uint64_t match = __ballot(valid);
         for (int bit = 0; bit < nbits; ++bit) {
