@@ -68,11 +68,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 constexpr int kCombineCols = 8;
 constexpr int kCombineUnroll = 8;
 
+// COLS_FAST: the column group is grid.x, so the workgroups of one token run next to each other and read its
+// rows of y together (grid.y then holds the tokens, at most 65535)
+template <bool COLS_FAST>
 __global__ __launch_bounds__(256) void combine8_kernel(const float* __restrict__ y, const float* __restrict__ tw,
                                                        const int32_t* __restrict__ ids, int T, int k, int E, int H,
                                                        uint16_t* __restrict__ out) {
-    const int t = blockIdx.x;
-    const int n = (blockIdx.y * 256 + threadIdx.x) * kCombineCols;
+    const int t = COLS_FAST ? blockIdx.y : blockIdx.x;
+    const int n = ((COLS_FAST ? blockIdx.x : blockIdx.y) * 256 + threadIdx.x) * kCombineCols;
     if (n >= H) return;
     const int32_t* tid = ids + (size_t)t * k;
     const float* tww = tw + (size_t)t * k;
@@ -146,8 +149,12 @@ hipError_t launch_combine(const float* y, const float* tw, const int32_t* ids, i
     if (work == 0) return hipSuccess;
     if (H % kCombineCols == 0 && ((uintptr_t)y & 15u) == 0 && ((uintptr_t)out & 15u) == 0) {
         const unsigned col_groups = (unsigned)((H / kCombineCols + 255) / 256);
-        hipLaunchKernelGGL(combine8_kernel, dim3((unsigned)T, col_groups), dim3(256), 0, s, y, tw, ids, T, k, E, H,
-                           out);
+        if (T <= 65535)
+            hipLaunchKernelGGL(combine8_kernel<true>, dim3(col_groups, (unsigned)T), dim3(256), 0, s, y, tw, ids, T, k,
+                               E, H, out);
+        else
+            hipLaunchKernelGGL(combine8_kernel<false>, dim3((unsigned)T, col_groups), dim3(256), 0, s, y, tw, ids, T, k,
+                               E, H, out);
         return hipGetLastError();
     }
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, y, tw, ids, T, k, E, H,
