@@ -701,11 +701,12 @@ def orc_bf16_to_f64(b):
     return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-@pytest.mark.parametrize("T,k,H,E", [(21, 4, 128, 6), (5, 8, 7168, 9), (7, 10, 2056, 12), (9, 3, 130, 4)],
+@pytest.mark.parametrize("T,k,H,E", [(21, 4, 128, 6), (5, 8, 7168, 9), (7, 10, 2056, 12), (9, 3, 130, 4),
+                                     (70000, 2, 16, 5)],
                          ids=lambda v: str(v))
 def test_moe_combine(orc, T, k, H, E):
     # eight columns per lane when H % 8 == 0 (with a partial last column group, and more routes than one unrolled
-    # pass), two per lane otherwise
+    # pass), two per lane otherwise; past 65535 tokens the tokens go in grid.x
     rng = np.random.default_rng(8 + H)
     y = rng.standard_normal((T * k, H)).astype(np.float32)
     tw = rng.uniform(0, 1, (T, k)).astype(np.float32)
