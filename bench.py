@@ -503,6 +503,16 @@ def main():
                                "timing": "median of 5 trials, each HIP events around %d graph-captured "
                                          "back-to-back launches, after about 30 ms of the same launches"
                                          % (n_replay * reps)})
+    # references measured on the same box: a device-to-device copy of 1 GiB (read + write bytes per second), and
+    # for a matrix-bound workload a dense BF16 GEMM of the gate_up shape on the valid rows (torch, i.e. the
+    # platform's BLAS, no dequantisation, no gather)
+    ref = {"copy_gbs": round(measured_copy_gbs(dev), 1)}
+    if mfma_bound:
+        ref["dense_bf16_gemm_tflops"] = round(measured_dense_gemm_tflops(Rv, 2 * I, H, dev), 1)
+        ref["kernel_vs_dense_gemm"] = round(achieved / ref["dense_bf16_gemm_tflops"], 4)
+    else:
+        ref["kernel_vs_copy"] = round(achieved / ref["copy_gbs"], 4)
+    result["roofline"]["measured_references"] = ref
     if p13.kernel == L.KERNEL_DECODE and p13.block_m == 16 and T * k <= 4096:
         # inside the fused step this gate_up routes its rows itself (no routing launch): its stage time from the
         # per-stage events, a launch gap included, against the same roofline
@@ -517,6 +527,48 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(spec, inputs, weight_bytes_step, args.cpu_budget)
     print(json.dumps(result), flush=True)
+
+
+def _event_median_us(fn, reps=10, trials=5):
+    import torch
+
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(trials):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3 / reps)
+    return statistics.median(ts)
+
+
+def measured_copy_gbs(dev, nbytes=1 << 30):
+    """Device-to-device copy bandwidth on this machine (bytes read plus bytes written per second, GB/s)."""
+    import torch
+
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    us = _event_median_us(lambda: dst.copy_(src))
+    del src, dst
+    return 2 * nbytes / (us * 1e-6) / 1e9
+
+
+def measured_dense_gemm_tflops(M, N, K, dev):
+    """A dense BF16 GEMM [M,K] x [K,N] through torch on this machine (TFLOP/s): the matrix-core rate the platform's
+    BLAS reaches on the same shape with nothing to dequantise or gather."""
+    import torch
+
+    a = torch.randn((M, K), device=dev).to(torch.bfloat16)
+    b = torch.randn((K, N), device=dev).to(torch.bfloat16)  # contiguous, not a transposed view
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    us = _event_median_us(lambda: torch.mm(a, b, out=c))
+    del a, b, c
+    return 2.0 * M * N * K / (us * 1e-6) / 1e12
 
 
 def ctypes_array(evs):
