@@ -960,3 +960,60 @@ def test_fused_moe_graph_replays(orc, shape, plans):
         w4.fused_moe(xd, idsd, twd, w13, w2, out=out, ws=ws, plans=pl)  # eager work between replays
         torch.cuda.synchronize()
         assert np.array_equal(bits(out), eager)
+
+
+# ------------------------------------------------------------------ seeded random shapes
+
+def _random_fused_case(seed):
+    """One seeded random fused-MLP case: shape, routing (uniform, skewed or with non-local ids) and plans (the
+    planner's, or an explicit decode or prefill plan of any supported tiling)."""
+    rng = np.random.default_rng(seed)
+    E = int(rng.integers(1, 300))
+    k = int(rng.integers(1, min(8, E) + 1))
+    T = int(rng.integers(1, 700))
+    H = 32 * int(rng.integers(2, 17))      # 64 .. 512
+    I = 32 * int(rng.integers(1, 9))       # 32 .. 256 (2I a multiple of 16)
+    kind = int(rng.integers(0, 3))
+    if kind == 0:
+        ids = synth.uniform_topk(rng, T, E, k)
+    elif kind == 1:  # skewed: a few experts take most routes (repeats within a token allowed)
+        p = (1.0 + np.arange(E)) ** -1.5
+        ids = rng.choice(E, size=(T, k), p=p / p.sum()).astype(np.int32)
+    else:            # an expert-parallel share: about half the ids are not local
+        ids = rng.integers(-1, 2 * E, (T, k)).astype(np.int32)
+        ids[ids >= E] = -1
+    plan_pick = int(rng.integers(0, 6))
+    plans = [None, ("decode", 16, 2, 4, 1), ("decode", 16, 4, 4, 2), ("prefill", 16, 2, 4, 1, 144),
+             ("prefill", 16, 2, 4, 1, 64), ("prefill", 64, 4, 4, 1)][plan_pick]
+    return rng, T, E, k, H, I, ids, plans
+
+
+@pytest.mark.parametrize("seed", list(range(24)))
+def test_fused_moe_random_shapes(orc, seed):
+    """Seeded random shapes, routings and plans through the fused call, against the oracle (R18's bar) and, bit
+    for bit, against the routed sequence with the same plans."""
+    rng, T, E, k, H, I, ids, plans = _random_fused_case(1000 + seed)
+    _say("random fused seed %d: T=%d E=%d k=%d H=%d I=%d plans=%r" % (seed, T, E, k, H, I, plans))
+    x = synth.activations(rng, T, H)
+    c13, s13 = synth.codes(rng, E, 2 * I, H), synth.scales(rng, E, 2 * I, H)
+    c2, s2 = synth.codes(rng, E, H, I), synth.scales(rng, E, H, I)
+    tw = rng.uniform(0.1, 1.0, (T, k)).astype(np.float32)
+    w13, w2 = _pack(c13, s13), _pack(c2, s2)
+    if plans is None:
+        p13, p2 = w4.fused_moe_plans(T, k, w13, w2)
+    else:
+        p13, p2 = w4.make_plan(*plans), w4.make_plan(*plans)
+        if p13.kernel == w4.KERNEL_DECODE and p2.k_split > 1:
+            p2 = w4.make_plan("decode", 16, 4, 4, 1)
+    out = torch.full((T, H), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    w4.fused_moe(u16(x), i32(ids), f32(tw), w13, w2, out=out, plans=(p13, p2))
+    got = bits(out)
+    route = w4.route_prep(i32(ids), E, p13.block_m)
+    h = poison_bf16(T * k, I)
+    w4.grouped_gemm_silu(u16(x), k, w13, route, p13, out=h)
+    y = w4.grouped_gemm(h, 1, w2, route, p2, out_f32=True)
+    seq = bits(w4.moe_combine(y, f32(tw), i32(ids), E))
+    assert np.array_equal(got, seq), "fused differs from the sequence in %d values" % int((got != seq).sum())
+    _, _, y_ref = orc.fused_moe(x, ids, tw, c13, s13, c2, s2)
+    worst, plain = check_fused(got, orc.last_out_acc, y_ref, tw, ids, E, label="random fused %d" % seed)
+    _say("  fused worst %.2e of S_t (%.2e of max|out|)" % (worst, plain))
