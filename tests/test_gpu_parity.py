@@ -968,11 +968,11 @@ def _random_fused_case(seed):
     """One seeded random fused-MLP case: shape, routing (uniform, skewed or with non-local ids) and plans (the
     planner's, or an explicit decode or prefill plan of any supported tiling)."""
     rng = np.random.default_rng(seed)
-    E = int(rng.integers(1, 300))
+    E = int(rng.integers(1, 300)) if seed % 5 else int(rng.integers(512, 1025))
     k = int(rng.integers(1, min(8, E) + 1))
     T = int(rng.integers(1, 700))
     H = 32 * int(rng.integers(2, 17))      # 64 .. 512
-    I = 32 * int(rng.integers(1, 9))       # 32 .. 256 (2I a multiple of 16)
+    I = 32 * int(rng.integers(2, 9))       # 64 .. 256: down sums of at least two scale groups (see R18)
     kind = int(rng.integers(0, 3))
     if kind == 0:
         ids = synth.uniform_topk(rng, T, E, k)
@@ -988,17 +988,22 @@ def _random_fused_case(seed):
     return rng, T, E, k, H, I, ids, plans
 
 
-@pytest.mark.parametrize("seed", list(range(24)))
-def test_fused_moe_random_shapes(orc, seed):
+@pytest.mark.parametrize("seed,fmt", [(s, "int4") for s in range(24)] + [(s, "mxfp4") for s in range(24, 32)])
+def test_fused_moe_random_shapes(orc, seed, fmt):
     """Seeded random shapes, routings and plans through the fused call, against the oracle (R18's bar) and, bit
-    for bit, against the routed sequence with the same plans."""
+    for bit, against the routed sequence with the same plans; the last seeds with MXFP4 weights."""
     rng, T, E, k, H, I, ids, plans = _random_fused_case(1000 + seed)
-    _say("random fused seed %d: T=%d E=%d k=%d H=%d I=%d plans=%r" % (seed, T, E, k, H, I, plans))
+    _say("random fused seed %d (%s): T=%d E=%d k=%d H=%d I=%d plans=%r" % (seed, fmt, T, E, k, H, I, plans))
     x = synth.activations(rng, T, H)
-    c13, s13 = synth.codes(rng, E, 2 * I, H), synth.scales(rng, E, 2 * I, H)
-    c2, s2 = synth.codes(rng, E, H, I), synth.scales(rng, E, H, I)
+    if fmt == "mxfp4":
+        c13, s13 = synth.codes(rng, E, 2 * I, H), synth.mxfp4_scales(rng, E, 2 * I, H)
+        c2, s2 = synth.codes(rng, E, H, I), synth.mxfp4_scales(rng, E, H, I)
+        w13, w2 = _pack_mx(c13, s13), _pack_mx(c2, s2)
+    else:
+        c13, s13 = synth.codes(rng, E, 2 * I, H), synth.scales(rng, E, 2 * I, H)
+        c2, s2 = synth.codes(rng, E, H, I), synth.scales(rng, E, H, I)
+        w13, w2 = _pack(c13, s13), _pack(c2, s2)
     tw = rng.uniform(0.1, 1.0, (T, k)).astype(np.float32)
-    w13, w2 = _pack(c13, s13), _pack(c2, s2)
     if plans is None:
         p13, p2 = w4.fused_moe_plans(T, k, w13, w2)
     else:
@@ -1014,6 +1019,6 @@ def test_fused_moe_random_shapes(orc, seed):
     y = w4.grouped_gemm(h, 1, w2, route, p2, out_f32=True)
     seq = bits(w4.moe_combine(y, f32(tw), i32(ids), E))
     assert np.array_equal(got, seq), "fused differs from the sequence in %d values" % int((got != seq).sum())
-    _, _, y_ref = orc.fused_moe(x, ids, tw, c13, s13, c2, s2)
+    _, _, y_ref = orc.fused_moe(x, ids, tw, c13, s13, c2, s2, fmt=fmt)
     worst, plain = check_fused(got, orc.last_out_acc, y_ref, tw, ids, E, label="random fused %d" % seed)
     _say("  fused worst %.2e of S_t (%.2e of max|out|)" % (worst, plain))
