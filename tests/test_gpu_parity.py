@@ -835,13 +835,25 @@ def test_fused_moe_equals_sequence(orc, shape, plans):
                                              ((2, 48, 8, 512, 2048), None, "int4"), ((5, 1, 2, 256, 64), None, "int4"),
                                              ((512, 1024, 8, 256, 128), None, "int4"),
                                              ((40, 300, 3, 256, 128), None, "mxfp4"),
-                                             ((600, 512, 8, 256, 128), None, "int4")],
+                                             ((600, 512, 8, 256, 128), None, "int4"),
+                                             ((1024, 8, 2, 256, 128), None, "int4"),
+                                             ((2100, 16, 4, 128, 64), None, "int4"),
+                                             ((512, 128, 8, 256, 128), (("prefill", 16, 2, 4, 1, 64),
+                                                                        ("prefill", 16, 2, 4, 1, 64)), "int4"),
+                                             ((700, 40, 3, 256, 96), (("prefill", 16, 2, 4, 1, 144),
+                                                                      ("prefill", 16, 2, 4, 1, 144)), "mxfp4"),
+                                             ((300, 6, 2, 512, 256), (("prefill", 64, 4, 4, 1),
+                                                                      ("prefill", 64, 4, 4, 1)), "int4")],
                          ids=["T32-E64", "T2-E48-both-splitK", "T3-E48-gate-up-splitK", "T2-E48-down-splitK", "T5-E1",
-                              "T512-E1024-4096-routes", "T40-E300-mxfp4", "T600-E512-flag-ignored"])
+                              "T512-E1024-4096-routes", "T40-E300-mxfp4", "T600-E512-flag-ignored",
+                              "prefill-T1024-E8-tiles-144", "prefill-T2100-E16-8400-routes", "prefill-T512-E128-tiles-64",
+                              "prefill-T700-E40-mxfp4", "prefill-T300-E6-plain-blocks-flag-ignored"])
 def test_fused_moe_one_launch(orc, shape, plans, fmt):
     """W4A16_PLAN_ONE_LAUNCH: gate_up and down of a decode step in one launch, down's workgroups of a route block
-    waiting for that block's rows of h.  Bit for bit the two-launch call with the same plans, every graph replay
-    too (the wait counters reset themselves); past 4096 routes the flag is ignored."""
+    waiting for that block's rows of h; of a prefill step of tiled 16-row blocks, down's workgroups of a tile
+    waiting for that tile's rows of h.  Bit for bit the two-launch call with the same plans, every graph replay
+    too (the wait counters reset themselves); past 4096 routes of a decode plan, and on plain prefill blocks, the
+    flag is ignored."""
     T, E, k, H, I = shape
     _say("one launch %s %s" % (shape, fmt))
     rng = np.random.default_rng(T * 17 + E)
@@ -857,7 +869,15 @@ def test_fused_moe_one_launch(orc, shape, plans, fmt):
     ids[0, :] = -1
     ids[T - 1, 0] = E + 3
     tw = rng.uniform(0.1, 1.0, (T, k)).astype(np.float32)
-    two = w4.fused_moe_plans(T, k, w13, w2) if plans is None else (w4.make_plan(*plans[0]), w4.make_plan(*plans[1]))
+    if plans is None:
+        dflt = w4.fused_moe_plans(T, k, w13, w2)
+        # the planner turns one launch on for prefill steps of tiled 16-row blocks whose down GEMM reads h again
+        # below 0.85 GB (every shape here), never for decode steps
+        small = all(q.kernel == w4.lib.KERNEL_PREFILL and q.tile_m in (64, 144) and q.block_m == 16 and
+                    q.n_blocks == 2 and q.k_split == 1 for q in dflt)
+        assert dflt[0].flags == (w4.lib.PLAN_ONE_LAUNCH if small else 0), dflt
+    two = w4.lib.two_launches(w4.fused_moe_plans(T, k, w13, w2) if plans is None else
+                              (w4.make_plan(*plans[0]), w4.make_plan(*plans[1])))
     one = w4.lib.one_launch(two)
     assert one[0].flags == w4.lib.PLAN_ONE_LAUNCH and two[0].flags == 0
     xd, idsd, twd = u16(x), i32(ids), f32(tw)

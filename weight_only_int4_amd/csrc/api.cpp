@@ -882,8 +882,9 @@ static FusedPlan fused_full_layout(int T, int k, const w4a16_weights* w13, const
     GemmArgs g13{nullptr, k, nullptr, w13->shape, nullptr, nullptr, R, maxB, nullptr, kOutAct};
     GemmArgs g2{nullptr, 1, nullptr, w2->shape, nullptr, nullptr, R, maxB, nullptr, kOutF32};
     FusedPlan fp;
-    fp.one_launch = (p13.flags & W4A16_PLAN_ONE_LAUNCH) && fused_self_route(R, E, g13, p13) &&
-                    decode_fused_supported(g13, p13, g2, p2);
+    fp.one_launch = (p13.flags & W4A16_PLAN_ONE_LAUNCH) &&
+                    ((fused_self_route(R, E, g13, p13) && decode_fused_supported(g13, p13, g2, p2)) ||
+                     prefill_fused_supported(g13, p13, g2, p2));
     size_t head;
     if (fp.one_launch) {
         fp.off_sync = 0;
@@ -985,6 +986,20 @@ int w4a16_fused_moe_plans_hint(int T, int k, const w4a16_weights* w13, const w4a
     }
     rc = validate_plan(&p2, what);
     if (rc) return rc;
+    // Prefill steps of tiled 16-row blocks run gate_up and down in one launch when down's device-coherent reads of
+    // h stay small: h is stored by workgroups on other XCDs in the same launch, so each of down's column tiles reads
+    // its tile's rows past the L2, n_tiles(down) x R x I x 2 bytes in all.  Measured, fused step in one launch
+    // against two: Qwen3-30B-A3B-shaped steps of 256 .. 4096 tokens 1.2 .. 6% faster (0.1 .. 0.8 GB read again),
+    // DeepSeek-V3-shaped steps of 512 and 1024 tokens the same (0.9, 1.9 GB), of 2048 and 4096 tokens 1.4% and
+    // 1.7% slower (3.8, 7.5 GB).  W4A16_ONE_LAUNCH=0 or 1 forces the choice where the plans allow it.
+    if (p13.kernel == W4A16_KERNEL_PREFILL) {
+        GemmArgs g13{nullptr, k, nullptr, w13->shape, nullptr, nullptr, T * k, 0, nullptr, kOutAct};
+        GemmArgs g2{nullptr, 1, nullptr, w2->shape, nullptr, nullptr, T * k, 0, nullptr, kOutF32};
+        const double reread = (double)prefill_n_tiles(w2->shape, p2) * T * k * I * 2.0;
+        const char* force = getenv("W4A16_ONE_LAUNCH");
+        const bool want = force && *force ? atoi(force) != 0 : reread < 0.85e9;
+        if (want && prefill_fused_supported(g13, p13, g2, p2)) p13.flags |= W4A16_PLAN_ONE_LAUNCH;
+    }
     *gate_up = p13;
     *down = p2;
     return ok();
@@ -1076,7 +1091,16 @@ int w4a16_fused_moe_planned(const uint16_t* x, const int32_t* topk_ids, const fl
     g13.tiles_ready = to.tiles != nullptr;
     g2.tiles_ready = to.tiles != nullptr && tiled_prefill(p2) && p13.block_m == p2.block_m &&
                      prefill_tile_rows(p13) == prefill_tile_rows(p2);
-    if (fp.one_launch) {
+    if (fp.one_launch && p13.kernel == W4A16_KERNEL_PREFILL) {
+        // gate_up and down in one launch: down's workgroups of a tile start once every gate_up column tile of that
+        // tile has stored its rows of h, so down fills the chip while gate_up's last workgroups run (humans& page,
+        // "Blackwell hides the conversion work")
+        rc = check_launch(launch_gemm_prefill_fused(g13, p13, g2, p2,
+                                                    reinterpret_cast<unsigned*>(base + f.off_split + fp.off_sync), s),
+                          "w4a16_fused_moe (gate_up + silu_mul + down, one launch)");
+        if (rc) return rc;
+        W4A16_STAGE(2);
+    } else if (fp.one_launch) {
         // gate_up and down in one launch: down's workgroups of a route block start once gate_up has stored that
         // block's rows of h (humans& page, "Blackwell hides the conversion work": the second GEMM's work begins
         // before the first one ends); both route their rows in-kernel, nothing writes the routing tensors

@@ -81,6 +81,19 @@ struct PrefillParams {
     unsigned* counters;
 };
 
+// gate_up and down of a fused step in one launch (gate_up workgroups first, then down workgroups): a tile's down
+// workgroups wait until every gate_up column tile of that tile has stored its rows of h.
+struct PrefillSync {
+    unsigned* ready;     // [tiles]: gate_up column tiles whose rows of h are stored; zero at rest
+    unsigned* done;      // [tiles]: down workgroups finished; the last one resets both; zero at rest
+    unsigned* timeouts;  // counts down workgroups that stopped waiting (never in a correct launch)
+    unsigned ready_target, done_target;
+};
+constexpr int kRolePlain = 0, kRoleGateUp = 1, kRoleDown = 2;
+// bounded wait of a down workgroup: about a second of polling (the gate_up workgroups it waits for were dispatched
+// before it and wait on nothing, so this bound is never reached in a correct launch; it only guarantees an end)
+constexpr unsigned kMaxPolls = 1u << 24;
+
 typedef __attribute__((address_space(3))) void lds_void;
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14)
@@ -182,9 +195,9 @@ __device__ __forceinline__ void prefill_split_epilogue(const PrefillParams& p, c
 
 // One tile: 16*MTA rows starting at route slot row0, all of them of expert e, times the column tile nt.  The
 // LDS ring and the row table are the kernel's (sized for its largest tile).
-template <int MTA, int NBW, int OM, int FMT, int MT>
+template <int MTA, int NBW, int OM, int FMT, int MT, int ROLE = kRolePlain>
 __device__ __forceinline__ void prefill_tile(const PrefillParams& p, uint8_t* slot0, uint8_t* slot1, int* ssid,
-                                             int* s_last, int row0, int e, int nt, int t) {
+                                             int* s_last, int row0, int e, int nt, int t, const PrefillSync* fs) {
     constexpr int BM = 16 * MTA;                // rows of this tile
     constexpr int ROWS_PER_WAVE = BM / kWaves;  // activation rows each wavefront streams
     constexpr int DMA = ROWS_PER_WAVE / 4;      // direct loads per wavefront per stage (4 rows of 256 B each)
@@ -229,7 +242,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, uint8_t* sl
                 off = (st * KT + ch * 8 < K && off != kOutOfRange) ? off + (uint32_t)soff : kOutOfRange;
                 soff = 0;
             }
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ares, (lds_void*)(slot + r * 4 * KT * 2), 16, off, soff, 0, 0);
+            // the down role reads h that gate_up workgroups of the same launch stored: device-coherent loads
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ares, (lds_void*)(slot + r * 4 * KT * 2), 16, off, soff, 0,
+                                                     ROLE == kRoleDown ? kBufferDeviceCoherent : 0);
         }
     };
     auto issue_a_last = [&](int st, uint8_t* slot_base) {  // the last stage of K: ragged or not
@@ -344,6 +359,20 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, uint8_t* sl
     // compiler assume the worst count of loads in flight and drain them); the last one to three stages are peeled.
     // (the last stage of a slice goes through issue_a_last, which reads a ragged stage only at the end of K)
     WStage<NBW> WA, WB;
+    if constexpr (ROLE == kRoleDown) {
+        // every gate_up column tile of tile t has stored its rows of h
+        if (threadIdx.x == 0) {
+            unsigned polls = 0;
+            while (__hip_atomic_load(&fs->ready[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < fs->ready_target) {
+                __builtin_amdgcn_s_sleep(2);
+                if (++polls == kMaxPolls) {
+                    __hip_atomic_fetch_add(fs->timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+            }
+        }
+        __syncthreads();
+    }
     if (st_end > st_begin) {
         if (st_end - st_begin == 1) issue_a_last(st_begin, slot0);
         else issue_a(st_begin, slot0, std::false_type{});
@@ -385,8 +414,12 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, uint8_t* sl
                 for (int q = 0; q < NBW / 2; ++q) {
                     const int n = (wave_global * (NBW / 2) + q) * 16 + j;
                     if (n >= NO) continue;
-                    static_cast<uint16_t*>(p.out)[(size_t)sid * NO + n] =
-                        f32_to_bf16_bits(silu_mul(acc[mt][q][r], acc[mt][q + NBW / 2][r]));
+                    uint16_t* dst = static_cast<uint16_t*>(p.out) + (size_t)sid * NO + n;
+                    const uint16_t v = f32_to_bf16_bits(silu_mul(acc[mt][q][r], acc[mt][q + NBW / 2][r]));
+                    // gate_up role: h is read by down workgroups of the same launch, so it is stored
+                    // device-coherently
+                    if constexpr (ROLE == kRoleGateUp) __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    else *dst = v;
                 }
             } else {
 #pragma unroll
@@ -400,15 +433,60 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, uint8_t* sl
                 }
             }
         }
+    if constexpr (ROLE == kRoleGateUp) {
+        // this workgroup's rows of h are stored device-coherently: once every wavefront's stores have completed,
+        // count the column tile as ready for the tile's down workgroups
+        wait_own_stores();
+        __syncthreads();
+        if (threadIdx.x == 0) __hip_atomic_fetch_add(&fs->ready[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if constexpr (ROLE == kRoleDown) {
+        // the last down workgroup of the tile resets both counters: every other one has passed its wait
+        if (threadIdx.x == 0) {
+            const unsigned prev = __hip_atomic_fetch_add(&fs->done[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (prev == fs->done_target - 1) {
+                __hip_atomic_store(&fs->ready[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(&fs->done[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
 }
 
 // Tiles of c route blocks of RB16 * 16 rows: the body for height c * RB16 (c <= MT / RB16)
-template <int MT, int NBW, int OM, int RB16, int FMT, int C = 1>
+template <int MT, int NBW, int OM, int RB16, int FMT, int ROLE, int C = 1>
 __device__ __forceinline__ void run_tile(int c, const PrefillParams& p, uint8_t* slot0, uint8_t* slot1, int* ssid,
-                                         int* s_last, int row0, int e, int nt, int t) {
+                                         int* s_last, int row0, int e, int nt, int t, const PrefillSync* fs) {
     if constexpr (C * RB16 <= MT) {
-        if (c == C) prefill_tile<C * RB16, NBW, OM, FMT, MT>(p, slot0, slot1, ssid, s_last, row0, e, nt, t);
-        else run_tile<MT, NBW, OM, RB16, FMT, C + 1>(c, p, slot0, slot1, ssid, s_last, row0, e, nt, t);
+        if (c == C) prefill_tile<C * RB16, NBW, OM, FMT, MT, ROLE>(p, slot0, slot1, ssid, s_last, row0, e, nt, t, fs);
+        else run_tile<MT, NBW, OM, RB16, FMT, ROLE, C + 1>(c, p, slot0, slot1, ssid, s_last, row0, e, nt, t, fs);
+    }
+}
+
+// One workgroup of the GEMM: (tile, column tile) pair of position id among the launch's positions (XCD-aware order
+// over the valid tiles only; id % 8 is the workgroup's XCD).
+template <int MT, int NBW, int OM, int RB16, int FMT, int ROLE>
+__device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, uint8_t* slot0, uint8_t* slot1, int* ssid,
+                                             int* s_last, const PrefillSync* fs) {
+    constexpr bool TILED = RB16 < MT;
+    constexpr int BM = 16 * MT;
+    int ntl;
+    if constexpr (TILED) ntl = __builtin_amdgcn_readfirstlane(*p.tile_count);
+    else ntl = p.ntp ? min(__builtin_amdgcn_readfirstlane(*p.ntp) / BM, p.max_blocks) : p.max_blocks;
+    const int V = ntl * p.n_tiles;
+    const int chunk = max(kChunkMin, (V + kXcds * kChunkRounds - 1) / (kXcds * kChunkRounds));
+    const int pos = id / kXcds;
+    const int pair = ((pos / chunk) * kXcds + id % kXcds) * chunk + pos % chunk;
+    if (pair >= V) return;
+    const int t = pair / p.n_tiles, nt = pair % p.n_tiles;
+    if constexpr (TILED) {
+        const int b0 = p.tiles[2 * t], c = p.tiles[2 * t + 1];
+        const int e = p.expert_ids[b0];
+        if (e < 0 || e >= p.sh.E) return;
+        run_tile<MT, NBW, OM, RB16, FMT, ROLE>(c, p, slot0, slot1, ssid, s_last, b0 * RB16 * 16, e, nt, t, fs);
+    } else {
+        const int e = p.expert_ids[t];
+        if (e < 0 || e >= p.sh.E) return;
+        prefill_tile<MT, NBW, OM, FMT, MT, ROLE>(p, slot0, slot1, ssid, s_last, t * BM, e, nt, t, fs);
     }
 }
 
@@ -417,41 +495,38 @@ template <int MT, int NBW, int OM, int RB16, int FMT>
 __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<MT, NBW>())) void gemm_prefill_kernel(PrefillParams p) {
     static_assert(OM != kOutAct || NBW % 2 == 0, "the activation epilogue pairs gate and up n-blocks");
     static_assert(MT % RB16 == 0, "a tile is a whole number of route blocks");
-    constexpr bool TILED = RB16 < MT;
     if constexpr (prefill_waves_per_simd<MT, NBW>() == 1) {
         // at one wavefront per SIMD the accumulators go to AGPRs (VGPRs alone stop at 256); naming an AGPR tells
         // the compiler they may be used
         __asm__ __volatile__("" ::: "a0");
     }
-    constexpr int BM = 16 * MT;
-    constexpr int SLOT = BM * KT * 2;  // bytes of one activation stage
+    constexpr int SLOT = 16 * MT * KT * 2;  // bytes of one activation stage
     // the two ring slots are separate arrays, so the compiler can tell the reads of one from the direct loads
     // into the other (with one array it would wait for every direct load before any read of the ring)
     __shared__ __attribute__((aligned(16))) uint8_t slot0[SLOT];
     __shared__ __attribute__((aligned(16))) uint8_t slot1[SLOT];
-    __shared__ int ssid[BM];
+    __shared__ int ssid[16 * MT];
     __shared__ int s_last;
+    prefill_body<MT, NBW, OM, RB16, FMT, kRolePlain>(p, (int)blockIdx.x, slot0, slot1, ssid, &s_last, nullptr);
+}
 
-    // ---- tile (XCD-aware order over the valid tiles only)
-    int ntl;
-    if constexpr (TILED) ntl = __builtin_amdgcn_readfirstlane(*p.tile_count);
-    else ntl = p.ntp ? min(__builtin_amdgcn_readfirstlane(*p.ntp) / BM, p.max_blocks) : p.max_blocks;
-    const int V = ntl * p.n_tiles;
-    const int chunk = max(kChunkMin, (V + kXcds * kChunkRounds - 1) / (kXcds * kChunkRounds));
-    const int pos = blockIdx.x / kXcds;
-    const int pair = ((pos / chunk) * kXcds + (int)(blockIdx.x % kXcds)) * chunk + pos % chunk;
-    if (pair >= V) return;
-    const int t = pair / p.n_tiles, nt = pair % p.n_tiles;
-    if constexpr (TILED) {
-        const int b0 = p.tiles[2 * t], c = p.tiles[2 * t + 1];
-        const int e = p.expert_ids[b0];
-        if (e < 0 || e >= p.sh.E) return;
-        run_tile<MT, NBW, OM, RB16, FMT>(c, p, slot0, slot1, ssid, &s_last, b0 * RB16 * 16, e, nt, t);
-    } else {
-        const int e = p.expert_ids[t];
-        if (e < 0 || e >= p.sh.E) return;
-        prefill_tile<MT, NBW, OM, FMT, MT>(p, slot0, slot1, ssid, &s_last, t * BM, e, nt, t);
-    }
+// gate_up (SiLU*mul into h) and down (binary32 y) of a fused step in one launch: workgroups [0, ng) are gate_up's,
+// the rest down's.  Every gate_up workgroup of an XCD is dispatched before that XCD's first down workgroup and
+// waits on nothing, so a down workgroup's wait for its tile always ends.  ng is a multiple of 8, so the XCD of a
+// workgroup is the XCD its role's position maps to.
+template <int MT, int NBW, int RB16, int FMT>
+__global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<MT, NBW>())) void gemm_prefill_fused_kernel(
+    PrefillParams gu, PrefillParams dn, PrefillSync fs, int ng) {
+    static_assert(NBW % 2 == 0 && MT % RB16 == 0, "prefill tile shape");
+    static_assert(prefill_waves_per_simd<MT, NBW>() == 2, "two wavefronts per SIMD");
+    constexpr int SLOT = 16 * MT * KT * 2;
+    __shared__ __attribute__((aligned(16))) uint8_t slot0[SLOT];
+    __shared__ __attribute__((aligned(16))) uint8_t slot1[SLOT];
+    __shared__ int ssid[16 * MT];
+    __shared__ int s_last;
+    const int id = (int)blockIdx.x;
+    if (id < ng) prefill_body<MT, NBW, kOutAct, RB16, FMT, kRoleGateUp>(gu, id, slot0, slot1, ssid, &s_last, &fs);
+    else prefill_body<MT, NBW, kOutF32, RB16, FMT, kRoleDown>(dn, id - ng, slot0, slot1, ssid, &s_last, &fs);
 }
 
 template <int MT, int NBW, int OM, int RB16>
@@ -479,6 +554,38 @@ hipError_t launch_t(const GemmArgs& a, int ks, hipStream_t s) {
         hipLaunchKernelGGL((gemm_prefill_kernel<MT, NBW, OM, RB16, kFmtMxfp4>), grid, dim3(kThreads), 0, s, p);
     else
         hipLaunchKernelGGL((gemm_prefill_kernel<MT, NBW, OM, RB16, kFmtInt4>), grid, dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+// Workgroups a role needs for its (tile, column tile) pairs (see launch_t).
+unsigned prefill_role_workgroups(const GemmArgs& a, int G, int n_tiles) {
+    const unsigned max_tiles = G > 1 ? (unsigned)((a.max_blocks + G - 1) / G + (a.sh.E < a.max_blocks ? a.sh.E : a.max_blocks))
+                                     : (unsigned)a.max_blocks;
+    const unsigned tiles = max_tiles * (unsigned)n_tiles;
+    constexpr unsigned kSlack = kChunkMin > kChunkRounds ? kChunkMin : kChunkRounds;
+    return ((tiles + kXcds - 1) / kXcds + kSlack) * kXcds;
+}
+
+template <int MT, int NBW, int RB16>
+hipError_t launch_fused_t(const GemmArgs& a13, const GemmArgs& a2, unsigned* sync, hipStream_t s) {
+    constexpr int cols = kWaves * NBW;
+    const int nt13 = (a13.sh.NB + cols - 1) / cols, nt2 = (a2.sh.NB + cols - 1) / cols;
+    auto params = [](const GemmArgs& a, int n_tiles) {
+        return PrefillParams{a.A,      a.a_row_div, static_cast<const uint8_t*>(a.packed), a.sh, a.sorted_ids,
+                             a.expert_ids, a.ntp,   a.R, a.max_blocks, n_tiles, a.out, a.tiles, a.tile_count,
+                             nullptr,  nullptr};
+    };
+    const PrefillParams gu = params(a13, nt13), dn = params(a2, nt2);
+    constexpr int G = MT / RB16;
+    const unsigned ng = prefill_role_workgroups(a13, G, nt13), nd = prefill_role_workgroups(a2, G, nt2);
+    const PrefillSync fs{sync, sync + a13.max_blocks, sync + 2 * (size_t)a13.max_blocks, (unsigned)nt13,
+                         (unsigned)nt2};
+    if (a13.sh.fmt == kFmtMxfp4)
+        hipLaunchKernelGGL((gemm_prefill_fused_kernel<MT, NBW, RB16, kFmtMxfp4>), dim3(ng + nd), dim3(kThreads), 0, s,
+                           gu, dn, fs, (int)ng);
+    else
+        hipLaunchKernelGGL((gemm_prefill_fused_kernel<MT, NBW, RB16, kFmtInt4>), dim3(ng + nd), dim3(kThreads), 0, s,
+                           gu, dn, fs, (int)ng);
     return hipGetLastError();
 }
 
@@ -541,6 +648,32 @@ size_t prefill_partial_floats(const Shape& sh, const w4a16_plan& p, int max_bloc
 size_t prefill_counters(const Shape& sh, const w4a16_plan& p, int max_blocks) {
     if (p.kernel != W4A16_KERNEL_PREFILL || p.k_split <= 1) return 0;
     return prefill_max_tiles(sh, p, max_blocks) * prefill_n_tiles(sh, p);
+}
+
+bool prefill_fused_supported(const GemmArgs& a13, const w4a16_plan& p13, const GemmArgs& a2, const w4a16_plan& p2) {
+    // tiles of 16-row route blocks, two n-blocks per wavefront, K whole, one tile height and one weight format
+    const int t13 = prefill_tile_rows(p13), t2 = prefill_tile_rows(p2);
+    return p13.kernel == W4A16_KERNEL_PREFILL && p2.kernel == W4A16_KERNEL_PREFILL && p13.block_m == 16 &&
+           p2.block_m == 16 && t13 == t2 && (t13 == 144 || t13 == 64) && p13.n_blocks == 2 && p2.n_blocks == 2 &&
+           p13.k_split == 1 && p2.k_split == 1 && a13.sh.fmt == a2.sh.fmt && prefill_supported(a13) &&
+           prefill_supported(a2);
+}
+
+hipError_t launch_gemm_prefill_fused(const GemmArgs& a13, const w4a16_plan& p13, const GemmArgs& a2,
+                                     const w4a16_plan& p2, unsigned* sync, hipStream_t s) {
+    if (a13.max_blocks == 0) return hipSuccess;
+    if (!prefill_fused_supported(a13, p13, a2, p2) || a13.out_mode != kOutAct || a2.out_mode != kOutF32 ||
+        sync == nullptr || a13.tiles == nullptr || a13.tile_count == nullptr || a13.tiles != a2.tiles ||
+        a13.max_blocks != a2.max_blocks)
+        return hipErrorInvalidValue;
+    const int mt = prefill_tile_rows(p13) / 16;
+    if (!a13.tiles_ready) {
+        if (a13.tile_scratch == nullptr) return hipErrorInvalidValue;
+        hipError_t err = launch_tile_map(a13.expert_ids, a13.ntp, p13.block_m, a13.max_blocks, mt, a13.tiles,
+                                         a13.tile_count, a13.tile_scratch, s);
+        if (err != hipSuccess) return err;
+    }
+    return mt == 9 ? launch_fused_t<9, 2, 1>(a13, a2, sync, s) : launch_fused_t<4, 2, 1>(a13, a2, sync, s);
 }
 
 hipError_t launch_gemm_prefill(const GemmArgs& a, const w4a16_plan& p, hipStream_t s) {

@@ -182,6 +182,11 @@ bool decode_fused_supported(const GemmArgs& a13, const w4a16_plan& p13, const Ge
 hipError_t launch_gemm_decode_fused(const GemmArgs& a13, const w4a16_plan& p13, const GemmArgs& a2,
                                     const w4a16_plan& p2, unsigned* sync, hipStream_t s);
 hipError_t launch_gemm_prefill(const GemmArgs& a, const w4a16_plan& p, hipStream_t s);
+// gate_up and down of a fused prefill step in one launch: down's workgroups of a tile wait until gate_up has stored
+// that tile's rows of h.  sync: 2 * max_blocks + 1 words, zero at rest (each launch leaves them zero).
+bool prefill_fused_supported(const GemmArgs& a13, const w4a16_plan& p13, const GemmArgs& a2, const w4a16_plan& p2);
+hipError_t launch_gemm_prefill_fused(const GemmArgs& a13, const w4a16_plan& p13, const GemmArgs& a2,
+                                     const w4a16_plan& p2, unsigned* sync, hipStream_t s);
 bool prefill_supported(const GemmArgs& a);
 // Rows per prefill workgroup tile (plan.tile_m, else block_m); 16- and 32-row route blocks are gathered into
 // taller tiles through a tile list.

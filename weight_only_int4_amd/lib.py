@@ -305,6 +305,14 @@ def one_launch(plans):
     return q, p2
 
 
+def two_launches(plans):
+    """The fused call's (gate_up, down) plans with W4A16_PLAN_ONE_LAUNCH cleared on the gate_up plan."""
+    p13, p2 = plans
+    q = Plan.from_buffer_copy(p13)
+    q.flags &= ~PLAN_ONE_LAUNCH
+    return q, p2
+
+
 def gemm_workspace_bytes(plan: Plan, R: int, E: int, N: int) -> int:
     out = _SZ(0)
     _check(load().w4a16_gemm_workspace_bytes(ctypes.byref(plan), R, E, N, ctypes.byref(out)))
