@@ -491,6 +491,7 @@ def main():
                    "local_routes": Rv, "weight_bytes_per_step": int(weight_bytes_step),
                    "weight_rotation_copies": ncopies, "parallelism": "none (one GPU)"},
         "stages_us": {n: round(float(v), 2) for n, v in zip(stages, stage.mean(0))},
+        "one_launch": bool(p13.flags & L.PLAN_ONE_LAUNCH),  # then stages_us.gate_up_silu holds both GEMMs
         "gpu_us_per_step_events": round(gpu_step_us, 2),
         "roofline": ({"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                       "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,

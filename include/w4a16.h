@@ -417,8 +417,10 @@ int w4a16_fused_moe(const uint16_t* x, const int32_t* topk_ids, const float* top
  * between its stages: stage_events[0] before routing, [1] before gate_up
  * (with the activation), [2] before down, [3] before the combine and [4]
  * after it (NULL = no events, identical to w4a16_fused_moe).  When gate_up
- * routes its own rows the routing stage is empty.  For per-stage
- * timing of eager calls; nothing else differs. */
+ * routes its own rows the routing stage is empty; when gate_up and down run
+ * in one launch (W4A16_PLAN_ONE_LAUNCH) the gate_up stage holds both and
+ * the down stage is empty.  For per-stage timing of eager calls; nothing
+ * else differs. */
 int w4a16_fused_moe_profiled(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, int T, int k,
                              const w4a16_weights* w13, const w4a16_weights* w2, uint16_t* out, void* ws,
                              size_t ws_bytes, hipStream_t s, hipEvent_t* stage_events);
