@@ -35,17 +35,19 @@ def _layer(seed, T, E, k, H, I):
     return u16(x), i32(ids), f32(tw), w13, w2
 
 
-# (T, E, k, H, I): a prefill step (tile list), then smaller decode steps, one of whose plans split K
+# (T, E, k, H, I): a prefill step (tile list; the planner runs its two GEMMs in one launch), then smaller decode
+# steps, one of whose plans split K
 CALLS = [(600, 8, 2, 512, 256), (64, 32, 4, 512, 256), (2, 48, 8, 512, 2048), (1, 8, 2, 256, 128)]
 
 
 def test_noalloc_equals_workspace_call_on_consecutive_calls():
-    plans_seen = set()
+    plans_seen, one_launch = set(), False
     for n, (T, E, k, H, I) in enumerate(CALLS):
         print("noalloc call %d: T=%d E=%d k=%d H=%d I=%d" % (n, T, E, k, H, I), flush=True)
         x, ids, tw, w13, w2 = _layer(500 + n, T, E, k, H, I)
         p13, p2 = w4.fused_moe_plans(T, k, w13, w2)
         plans_seen.add((p13.kernel, p13.k_split > 1 or p2.k_split > 1))
+        one_launch |= p13.kernel == w4.KERNEL_PREFILL and bool(p13.flags & L.PLAN_ONE_LAUNCH)
         assert w4.fused_moe_workspace_bytes(T, k, w13, w2) <= L.NOALLOC_SCRATCH_BYTES
         ref = bits(w4.fused_moe(x, ids, tw, w13, w2))
         out = torch.full((T, H), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
@@ -59,6 +61,7 @@ def test_noalloc_equals_workspace_call_on_consecutive_calls():
         assert np.array_equal(bits(out), ref), "call %d repeated differs" % n
     # the sequence covered a prefill plan and a decode plan that splits K
     assert (w4.KERNEL_PREFILL, False) in plans_seen and (w4.KERNEL_DECODE, True) in plans_seen
+    assert one_launch, "no prefill step ran gate_up and down in one launch"
 
 
 def test_noalloc_refuses_a_step_beyond_the_scratch():
