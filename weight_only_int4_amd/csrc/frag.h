@@ -157,7 +157,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
     return __builtin_bit_cast(uint16_t, b);
 }
 
-// silu(g) * u in binary32 from unrounded gate and up accumulators.
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+// silu(g) * u in binary32 from unrounded gate and up accumulators, with the hardware's exponential and reciprocal
+// (a few binary32 ulps, far below the BF16 rounding of h that follows; the full-precision expf and division cost
+// about 25 VALU instructions per output, which the epilogue of a VALU-bound GEMM pays for)
+__device__ __forceinline__ float silu_mul(float g, float u) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u; }
 
 }  // namespace w4a16
