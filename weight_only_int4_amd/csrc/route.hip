@@ -9,7 +9,8 @@
 // Order inside an expert is ascending route index: each chunk of 1024 routes
 // is ranked by (earlier chunks) + (earlier wavefronts of this chunk) + (lower
 // lanes of this wavefront with the same expert).  The last term comes from a
-// lane-match mask built from one ballot per bit of the expert id.
+// per-expert lane mask that the wavefront's lanes build in LDS with one atomic
+// OR each (wave_rank).
 #include <climits>
 
 #include "w4a16_internal.h"
@@ -23,6 +24,22 @@ constexpr int kSmallThreads = 512;  // workgroup of the routing of few routes an
 constexpr int kRegChunks = 4;       // chunks of routes the one-workgroup routing keeps in registers
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Rank of this lane's route among the lanes of its wavefront routed to the same expert e, in lane order.  mrow is
+// the wavefront's row of per-expert lane masks in LDS, zero at rest: every valid lane sets its bit in mrow[e] with
+// one atomic OR, reads the mask back (a wavefront's LDS operations complete in issue order, so the read sees every
+// lane's OR) and counts the set bits below its own.  The lowest lane of each expert (the leader, rank 0) then
+// replaces the mask by the number of lanes routed to e, which the caller reads as that wavefront's count and resets
+// to zero once every wavefront of the workgroup has read it.
+__device__ __forceinline__ int wave_rank(uint64_t* mrow, int e, bool valid, int lane, bool* leader) {
+    if (valid) __hip_atomic_fetch_or(&mrow[e], 1ull << lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const uint64_t m = valid ? __hip_atomic_load(&mrow[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) : 0ull;
+    const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int rank = __popcll(m & lower);
+    *leader = valid && rank == 0;
+    if (*leader) __hip_atomic_store(&mrow[e], (uint64_t)__popcll(m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return rank;
+}
 
 // Exclusive scan of one int per thread across the workgroup; returns the
 // thread's exclusive prefix and writes the total to *total (all threads).
@@ -73,7 +90,8 @@ __device__ void emit_tiles(const TileOut& to, int L, int b0e, int* wave_tot) {
     if (threadIdx.x == 0) *to.count = total;
 }
 
-// Shared memory layout (ints): cnt[E] | pad_off[E+1] | base[E] | wave_cnt[(NT / 64)][E] | wave_tot[(NT / 64)+1]
+// Shared memory layout: wave_cnt[(NT / 64)][E] (64-bit lane masks, then counts) | ints cnt[E] | pad_off[E+1] |
+// base[E] | wave_tot[(NT / 64)+1]
 template <int NT>
 __global__ __launch_bounds__(NT) void route_prep_kernel(const int32_t* __restrict__ ids, int R, int E, int BM,
                                                               int max_padded, int max_blocks,
@@ -82,16 +100,16 @@ __global__ __launch_bounds__(NT) void route_prep_kernel(const int32_t* __restric
                                                               int32_t* __restrict__ ntp_out,
                                                               int32_t* __restrict__ offsets_out,
                                                               int32_t* __restrict__ counts_out, TileOut to) {
-    extern __shared__ int smem[];
-    int* cnt = smem;
+    extern __shared__ uint64_t smem64[];
+    uint64_t* wave_cnt = smem64;
+    int* cnt = reinterpret_cast<int*>(wave_cnt + (NT / 64) * E);
     int* pad_off = cnt + E;
     int* base = pad_off + E + 1;
-    int* wave_cnt = base + E;
-    int* wave_tot = wave_cnt + (NT / 64) * E;
+    int* wave_tot = base + E;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
     for (int e = tid; e < E; e += NT) cnt[e] = 0;
-    for (int x = tid; x < (NT / 64) * E; x += NT) wave_cnt[x] = 0;
+    for (int x = tid; x < (NT / 64) * E; x += NT) wave_cnt[x] = 0ull;
     __syncthreads();
     // the ids of the first kRegChunks chunks are loaded together and stay in registers for the scatter below, so
     // neither pass waits on a load per chunk (later chunks, past kRegChunks * NT routes, are read again)
@@ -142,34 +160,25 @@ __global__ __launch_bounds__(NT) void route_prep_kernel(const int32_t* __restric
         }
         expert_ids[b] = owner;
     }
-    int nbits = 1;
-    while ((1 << nbits) < E) ++nbits;
     __syncthreads();  // sentinel stores complete before any scatter store
 
     // one chunk of NT routes, ranked in route order: earlier chunks (base), earlier wavefronts (wave_cnt), lower
-    // lanes with the same expert (a lane-match mask from one ballot per bit of the expert id)
+    // lanes with the same expert (wave_rank)
     auto scatter_chunk = [&](int chunk, int e) {
         const int i = chunk + tid;
         const bool valid = e >= 0 && e < E;
-        uint64_t match = __ballot(valid);
-        for (int bit = 0; bit < nbits; ++bit) {
-            const uint64_t ones = __ballot(valid && ((e >> bit) & 1));
-            match &= ((e >> bit) & 1) ? ones : ~ones;
-        }
-        const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-        const int rank_w = __popcll(match & lower);
-        const bool leader = valid && rank_w == 0;
-        if (leader) wave_cnt[wave * E + e] = __popcll(match);
+        bool leader;
+        const int rank_w = wave_rank(wave_cnt + (size_t)wave * E, e, valid, lane, &leader);
         __syncthreads();
         if (valid) {
             int prior = base[e];
-            for (int w = 0; w < wave; ++w) prior += wave_cnt[w * E + e];
+            for (int w = 0; w < wave; ++w) prior += (int)wave_cnt[w * E + e];
             sorted_ids[prior + rank_w] = i;
         }
         __syncthreads();
         if (leader) {
-            atomicAdd(&base[e], wave_cnt[wave * E + e]);
-            wave_cnt[wave * E + e] = 0;
+            atomicAdd(&base[e], (int)wave_cnt[wave * E + e]);
+            wave_cnt[wave * E + e] = 0ull;
         }
         __syncthreads();
     };
@@ -273,13 +282,13 @@ __global__ __launch_bounds__(kThreads) void route_scan_kernel(int R, int E, int 
     }
 }
 
-// Shared memory (ints): base[E] | wave_cnt[kWaves][E]
+// Shared memory: wave_cnt[kWaves][E] (64-bit lane masks, then counts) | ints base[E]
 __global__ __launch_bounds__(kThreads) void route_scatter_kernel(const int32_t* __restrict__ ids, int R, int E,
                                                                  const int32_t* __restrict__ chunk_base,
                                                                  int32_t* __restrict__ sorted_ids) {
-    extern __shared__ int smem[];
-    int* base = smem;
-    int* wave_cnt = base + E;
+    extern __shared__ uint64_t smem64[];
+    uint64_t* wave_cnt = smem64;
+    int* base = reinterpret_cast<int*>(wave_cnt + kWaves * E);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = blockIdx.x;
     const int end = min(R, (c + 1) * kChunk);
     // the chunk's ids, loaded together up front
@@ -291,9 +300,7 @@ __global__ __launch_bounds__(kThreads) void route_scatter_kernel(const int32_t* 
         e_reg[u] = i < end ? ids[i] : -1;
     }
     for (int e = tid; e < E; e += kThreads) base[e] = chunk_base[(size_t)c * E + e];
-    for (int x = tid; x < kWaves * E; x += kThreads) wave_cnt[x] = 0;
-    int nbits = 1;
-    while ((1 << nbits) < E) ++nbits;
+    for (int x = tid; x < kWaves * E; x += kThreads) wave_cnt[x] = 0ull;
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < kSubs; ++u) {
@@ -302,25 +309,18 @@ __global__ __launch_bounds__(kThreads) void route_scatter_kernel(const int32_t* 
         const int i = sub + tid;
         const int e = e_reg[u];
         const bool valid = e >= 0 && e < E;
-        uint64_t match = __ballot(valid);
-        for (int bit = 0; bit < nbits; ++bit) {
-            const uint64_t ones = __ballot(valid && ((e >> bit) & 1));
-            match &= ((e >> bit) & 1) ? ones : ~ones;
-        }
-        const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-        const int rank_w = __popcll(match & lower);
-        const bool leader = valid && rank_w == 0;
-        if (leader) wave_cnt[wave * E + e] = __popcll(match);
+        bool leader;
+        const int rank_w = wave_rank(wave_cnt + (size_t)wave * E, e, valid, lane, &leader);
         __syncthreads();
         if (valid) {
             int prior = base[e];
-            for (int w = 0; w < wave; ++w) prior += wave_cnt[w * E + e];
+            for (int w = 0; w < wave; ++w) prior += (int)wave_cnt[w * E + e];
             sorted_ids[prior + rank_w] = i;
         }
         __syncthreads();
         if (leader) {
-            atomicAdd(&base[e], wave_cnt[wave * E + e]);
-            wave_cnt[wave * E + e] = 0;
+            atomicAdd(&base[e], (int)wave_cnt[wave * E + e]);
+            wave_cnt[wave * E + e] = 0ull;
         }
         __syncthreads();
     }
@@ -533,12 +533,12 @@ hipError_t launch_route_prep(const int32_t* topk_ids, int R, int E, int block_m,
         // few routes and experts (decode steps): half the workgroup, half the barrier cost and LDS to clear;
         // thread e still owns expert e (measured: 0.5-0.7 us less at up to 512 routes, slower beyond)
         constexpr int NT = kSmallThreads, NW = NT / 64;
-        const size_t shmem = sizeof(int) * ((size_t)E + (E + 1) + E + (size_t)NW * E + (NW + 1));
+        const size_t shmem = sizeof(uint64_t) * (size_t)NW * E + sizeof(int) * ((size_t)E + (E + 1) + E + (NW + 1));
         hipLaunchKernelGGL(route_prep_kernel<NT>, dim3(1), dim3(NT), shmem, s, topk_ids, R, E, block_m,
                            max_padded, max_blocks, sorted_ids, expert_ids, ntp, offsets, counts, to);
         return hipGetLastError();
     }
-    const size_t shmem = sizeof(int) * ((size_t)E + (E + 1) + E + (size_t)kWaves * E + (kWaves + 1));
+    const size_t shmem = sizeof(uint64_t) * (size_t)kWaves * E + sizeof(int) * ((size_t)E + (E + 1) + E + (kWaves + 1));
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(route_prep_kernel<kThreads>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (shmem > 65536 && attr != hipSuccess) return attr;
@@ -568,7 +568,7 @@ hipError_t launch_route_prep_scratch(const int32_t* topk_ids, int R, int E, int 
                        counts, to);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const size_t scatter_lds = sizeof(int) * ((size_t)E + (size_t)kWaves * E);
+    const size_t scatter_lds = sizeof(uint64_t) * (size_t)kWaves * E + sizeof(int) * (size_t)E;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(route_scatter_kernel),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (scatter_lds > 65536 && attr != hipSuccess) return attr;
