@@ -852,8 +852,8 @@ def test_fused_moe_one_launch(orc, shape, plans, fmt):
     """W4A16_PLAN_ONE_LAUNCH: gate_up and down of a decode step in one launch, down's workgroups of a route block
     waiting for that block's rows of h; of a prefill step of tiled 16-row blocks, down's workgroups of a tile
     waiting for that tile's rows of h.  Bit for bit the two-launch call with the same plans, every graph replay
-    too (the wait counters reset themselves); past 4096 routes of a decode plan, and on plain prefill blocks, the
-    flag is ignored."""
+    too; the wait counters are zero again after every call and no bounded wait gave up; past 4096 routes of a
+    decode plan, and on plain prefill blocks, the flag is ignored."""
     T, E, k, H, I = shape
     _say("one launch %s %s" % (shape, fmt))
     rng = np.random.default_rng(T * 17 + E)
@@ -899,6 +899,13 @@ def test_fused_moe_one_launch(orc, shape, plans, fmt):
         w4.fused_moe(xd, idsd, twd, w13, w2, out=out, ws=ws, plans=one)  # eager work between replays
         torch.cuda.synchronize()
         assert np.array_equal(bits(out), ref)
+    # where the step ran as one launch, the workspace starts with the wait words (ready and done per route block or
+    # tile, then the count of bounded waits that gave up): zero again after every call, and no wait gave up
+    if (one[0].kernel == w4.lib.KERNEL_DECODE and T * k <= 4096) or (
+            one[0].kernel == w4.lib.KERNEL_PREFILL and one[0].block_m == 16):
+        _, maxB = w4.lib.route_bounds(T, k, E, one[0].block_m)
+        sync = ws[: 4 * (2 * maxB + 1)].view(torch.int32).cpu().numpy()
+        assert not sync.any(), "wait words not reset: %d nonzero, timeouts %d" % (int((sync != 0).sum()), int(sync[-1]))
     _, _, y_ref = orc.fused_moe(x, ids, tw, c13, s13, c2, s2, fmt=fmt)
     worst, plain = check_fused(got, orc.last_out_acc, y_ref, tw, ids, E, label="one launch")
     _say("  fused worst %.2e of S_t (%.2e of max|out|)" % (worst, plain))
