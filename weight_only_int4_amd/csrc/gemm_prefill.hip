@@ -401,11 +401,51 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, uint8_t* sl
         return;
     }
 
-    // ---- epilogue: lane holds rows 4c + r of each 16-row tile, column j of each n-block
+    // ---- epilogue: lane holds rows 4c + r of each 16-row tile, column j of each n-block.  The activation output
+    // goes through LDS when the staged tile fits one ring slot and rows are whole 16-byte chunks: each wavefront
+    // writes its h values to the staged tile, then the workgroup stores whole rows with 16-byte stores (8 lanes
+    // cover a row's 128 bytes), not 2-byte stores four rows at a time.
+    constexpr int OC = kWaves * 16 * (NBW / 2);  // activation columns of the tile
+    constexpr int RS = OC * 2 + 16;              // bytes of a staged row (padded against bank conflicts)
+    constexpr bool kStageFits = OM == kOutAct && 16 * MTA * RS <= 16 * MT * KT * 2;
+    bool staged = false;
+    if constexpr (kStageFits) {
+        const int NO = sh.N / 2;
+        staged = (NO & 7) == 0 && (reinterpret_cast<uintptr_t>(p.out) & 15) == 0;
+        if (staged) {
+            uint8_t* stg = slot0;
+            __syncthreads();  // every wavefront has finished reading the ring
+#pragma unroll
+            for (int mt = 0; mt < MTA; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int q = 0; q < NBW / 2; ++q)
+                        *reinterpret_cast<uint16_t*>(stg + (mt * 16 + 4 * c + r) * RS + ((w * (NBW / 2) + q) * 16 + j) * 2) =
+                            f32_to_bf16_bits(silu_mul(acc[mt][q][r], acc[mt][q + NBW / 2][r]));
+            __syncthreads();
+            constexpr int CPR = OC / 8;  // 16-byte chunks per row
+            // gate_up role: h is read by down workgroups of the same launch, so it is stored device-coherently
+            // (the fused launch only runs where h is below 2 GiB, so buffer offsets reach every row)
+            const __amdgpu_buffer_rsrc_t hres = buffer_resource(p.out, (uint32_t)p.R * (uint32_t)NO * 2u);
+            for (int idx = threadIdx.x; idx < BM * CPR; idx += kThreads) {
+                const int row = idx / CPR, ch = idx % CPR;
+                const int sid = ssid[row], n = nt * OC + ch * 8;
+                if (sid < 0 || n >= NO) continue;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * RS + ch * 16);
+                if constexpr (ROLE == kRoleGateUp)
+                    __builtin_amdgcn_raw_buffer_store_b128(v, hres, (int)(((uint32_t)sid * (uint32_t)NO + (uint32_t)n) * 2u), 0,
+                                                          kBufferDeviceCoherent);
+                else
+                    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.out) + (size_t)sid * NO + n) = v;
+            }
+        }
+    }
 #pragma unroll
     for (int mt = 0; mt < MTA; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
+            if (staged) break;
             const int sid = ssid[mt * 16 + 4 * c + r];
             if (sid < 0) continue;
             if (OM == kOutAct) {
