@@ -441,6 +441,48 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, uint8_t* sl
             }
         }
     }
+    // The binary32 output goes through the ring slots too, GP row groups of 16 rows per pass, alternating slots
+    // (a pass writes one slot while nothing reads it: every thread finished the previous pass on that slot before
+    // it reached the last barrier).  Staged chunks of odd quads of rows are XOR-swizzled by 64 bytes, so the four
+    // rows a wavefront writes per instruction fall on two halves of the banks, not one.
+    constexpr int COLS = kWaves * NBW * 16;   // binary32 columns of the tile
+    constexpr int RB = COLS * 4;              // bytes of a staged binary32 row
+    constexpr int GP = (16 * MT * KT * 2) / (16 * RB);
+    if constexpr (OM == kOutF32 && GP >= 1 && NBW == 2) {
+        staged = (sh.N & 3) == 0 && (reinterpret_cast<uintptr_t>(p.out) & 15) == 0;
+        if (staged) {
+            constexpr int NPASS = (MTA + GP - 1) / GP;
+            constexpr int CPR = RB / 16;  // 16-byte chunks per row
+            __syncthreads();  // every wavefront has finished reading the ring
+#pragma unroll
+            for (int pass = 0; pass < NPASS; ++pass) {
+                uint8_t* stg = (pass & 1) ? slot1 : slot0;
+#pragma unroll
+                for (int gi = 0; gi < GP; ++gi) {
+                    const int mt = pass * GP + gi;
+                    if (mt < MTA) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+#pragma unroll
+                            for (int q = 0; q < NBW; ++q) {
+                                const int row = gi * 16 + 4 * c + r, byte = ((w * NBW + q) * 16 + j) * 4;
+                                const int pch = (byte >> 4) ^ (((row >> 2) & 1) << 2);
+                                *reinterpret_cast<float*>(stg + row * RB + pch * 16 + (byte & 15)) = acc[mt][q][r];
+                            }
+                    }
+                }
+                __syncthreads();
+                const int rows = (MTA - pass * GP < GP ? MTA - pass * GP : GP) * 16;
+                for (int idx = threadIdx.x; idx < rows * CPR; idx += kThreads) {
+                    const int row = idx / CPR, ch = idx % CPR;
+                    const int sid = ssid[pass * GP * 16 + row], n = nt * COLS + ch * 4;
+                    if (sid < 0 || n >= sh.N) continue;
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * RB + ((ch ^ (((row >> 2) & 1) << 2)) * 16));
+                    *reinterpret_cast<u32x4*>(static_cast<float*>(p.out) + (size_t)sid * sh.N + n) = v;
+                }
+            }
+        }
+    }
 #pragma unroll
     for (int mt = 0; mt < MTA; ++mt)
 #pragma unroll
