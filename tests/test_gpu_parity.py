@@ -872,7 +872,7 @@ def test_fused_moe_one_launch(orc, shape, plans, fmt):
     if plans is None:
         dflt = w4.fused_moe_plans(T, k, w13, w2)
         # the planner turns one launch on for prefill steps of tiled 16-row blocks whose down GEMM reads h again
-        # below 0.85 GB (every shape here), never for decode steps
+        # below 2 GB (every shape here), never for decode steps
         small = all(q.kernel == w4.lib.KERNEL_PREFILL and q.tile_m in (64, 144) and q.block_m == 16 and
                     q.n_blocks == 2 and q.k_split == 1 for q in dflt)
         assert dflt[0].flags == (w4.lib.PLAN_ONE_LAUNCH if small else 0), dflt

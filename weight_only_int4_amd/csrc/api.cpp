@@ -987,21 +987,20 @@ int w4a16_fused_moe_plans_hint(int T, int k, const w4a16_weights* w13, const w4a
     rc = validate_plan(&p2, what);
     if (rc) return rc;
     // Prefill steps of tiled 16-row blocks run gate_up and down in one launch when the volume of h that down's column
-    // tiles read, n_tiles(down) x R x I x 2 bytes, is below 0.85 GB: an empirical threshold.  Measured, fused step in
-    // one launch against two: Qwen3-30B-A3B-shaped steps of 256 .. 4096 tokens 1.2 .. 6% faster (0.1 .. 0.8 GB),
-    // DeepSeek-V3-shaped steps of 512 and 1024 tokens the same (0.9, 1.9 GB), of 2048 and 4096 tokens 1.4% and
-    // 1.7% slower (3.8, 7.5 GB), the Kimi-K2 prefill share of 8192 tokens 1.7% slower (R counts every route; about
-    // an eighth are local).  The one launch fills the tail of gate_up's last round with down's first workgroups and
-    // saves a launch gap, but every gate_up workgroup waits for its stores of h before it counts its tile ready; a
-    // step of many gate_up rounds pays that wait more often than it gains at the one tail (reading h through the L2
-    // instead of device-coherently measured the same).  W4A16_ONE_LAUNCH=0 or 1 forces the choice where the plans
-    // allow it.
+    // tiles read, n_tiles(down) x R x I x 2 bytes, is below 2 GB: an empirical threshold.  Measured, fused step in one
+    // launch against two: Qwen3-30B-A3B-shaped steps of 256 .. 4096 tokens 1.2 .. 6% faster (0.1 .. 0.8 GB), of 8192
+    // tokens the same (1.6 GB); DeepSeek-V3-shaped steps of 512 and 1024 tokens 0.4% and 0.5% faster (0.9, 1.9 GB),
+    // of 2048 and 4096 tokens 0.8% and 0.9% slower (3.8, 7.5 GB); the Kimi-K2 prefill share of 8192 tokens 0.7%
+    // slower (R counts every route; about an eighth are local).  The one launch fills the tail of gate_up's last
+    // round with down's first workgroups and saves a launch gap, but every gate_up workgroup stores its rows of h
+    // device-coherently and waits for them before it counts its tile ready; a step of many gate_up rounds pays that
+    // more often than it gains at the one tail.  W4A16_ONE_LAUNCH=0 or 1 forces the choice where the plans allow it.
     if (p13.kernel == W4A16_KERNEL_PREFILL) {
         GemmArgs g13{nullptr, k, nullptr, w13->shape, nullptr, nullptr, T * k, 0, nullptr, kOutAct};
         GemmArgs g2{nullptr, 1, nullptr, w2->shape, nullptr, nullptr, T * k, 0, nullptr, kOutF32};
         const double reread = (double)prefill_n_tiles(w2->shape, p2) * T * k * I * 2.0;
         const char* force = getenv("W4A16_ONE_LAUNCH");
-        const bool want = force && *force ? atoi(force) != 0 : reread < 0.85e9;
+        const bool want = force && *force ? atoi(force) != 0 : reread < 2.0e9;
         if (want && prefill_fused_supported(g13, p13, g2, p2)) p13.flags |= W4A16_PLAN_ONE_LAUNCH;
     }
     *gate_up = p13;
