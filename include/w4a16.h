@@ -84,16 +84,20 @@ typedef struct w4a16_plan {
     int32_t reserved[1];   /* must be zero */
 } w4a16_plan;
 
-/* Plan flag, read on the gate_up plan of w4a16_fused_moe_planned: run a decode
+/* Plan flag, read on the gate_up plan of w4a16_fused_moe_planned: run the
  * step's gate_up and down GEMMs in one launch, down's workgroups of a route
- * block starting once gate_up has stored that block's rows of h (humans& page,
- * "Blackwell hides the conversion work").  Applies when both plans are decode
- * plans of 16-row blocks on the register-streaming kernel, the step has at
- * most 4096 routes and both weight sets share a format; otherwise ignored.
- * Outputs are bit-identical either way.  The planner never sets it: on the
- * Qwen3-, Kimi-K2- and DeepSeek-V3-shaped decode steps the two launches were
- * faster (one kernel's register budget for both GEMMs, and no tail of gate_up
- * for down to fill). */
+ * block (decode) or tile (prefill) starting once gate_up has stored those rows
+ * of h (humans& page, "Blackwell hides the conversion work").  Applies to
+ * decode plans of 16-row blocks on the register-streaming kernel with at most
+ * 4096 routes, and to prefill plans of 16-row blocks in tiles of 64 or 144
+ * rows with two n-blocks per wavefront and K whole, both weight sets of one
+ * format; otherwise ignored.  Outputs are bit-identical either way.  The
+ * fused planner (w4a16_fused_moe_plans*) sets it on prefill plans whose down
+ * GEMM reads less than 2 GB of h (n_tiles(down) x T*k x I x 2 bytes), where
+ * one launch measured faster; W4A16_ONE_LAUNCH=0 or 1 (read once) forces the
+ * choice.  It never sets it on decode plans: two launches were faster on the
+ * Qwen3-, Kimi-K2- and DeepSeek-V3-shaped decode steps (one kernel's register
+ * budget for both GEMMs, and no tail of gate_up for down to fill). */
 #define W4A16_PLAN_ONE_LAUNCH 1
 
 /* Host handle describing one packed weight set (E experts of N x K). */
@@ -405,7 +409,8 @@ int w4a16_fused_moe_workspace_bytes(int T, int k, const w4a16_weights* w13, cons
                                     size_t* bytes);
 
 /* The two plans w4a16_fused_moe uses (they share block_m, hence one set of
- * routing tensors; the gate_up plan has n_blocks >= 2). */
+ * routing tensors; the gate_up plan has n_blocks >= 2, and carries
+ * W4A16_PLAN_ONE_LAUNCH where the planner runs the two GEMMs in one launch). */
 int w4a16_fused_moe_plans(int T, int k, const w4a16_weights* w13, const w4a16_weights* w2, w4a16_plan* gate_up,
                           w4a16_plan* down);
 

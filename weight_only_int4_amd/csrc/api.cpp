@@ -76,6 +76,7 @@ int env_int(const char* name, int dflt) {
 struct Overrides {
     int force_kernel = 0;  // 0 auto, else W4A16_KERNEL_*
     int block_m = 0, n_blocks = 0, waves = 0, k_split = 0, tile_m = -1;
+    int one_launch = -1;  // -1 the planner's rule, 0 or 1 forced (fused prefill steps)
 };
 
 const Overrides& overrides() {
@@ -90,6 +91,7 @@ const Overrides& overrides() {
         r.waves = env_int("W4A16_WAVES", 0);
         r.k_split = env_int("W4A16_K_SPLIT", 0);
         r.tile_m = env_int("W4A16_TILE_M", -1);
+        r.one_launch = env_int("W4A16_ONE_LAUNCH", -1);
         return r;
     }();
     return o;
@@ -999,8 +1001,8 @@ int w4a16_fused_moe_plans_hint(int T, int k, const w4a16_weights* w13, const w4a
         GemmArgs g13{nullptr, k, nullptr, w13->shape, nullptr, nullptr, T * k, 0, nullptr, kOutAct};
         GemmArgs g2{nullptr, 1, nullptr, w2->shape, nullptr, nullptr, T * k, 0, nullptr, kOutF32};
         const double reread = (double)prefill_n_tiles(w2->shape, p2) * T * k * I * 2.0;
-        const char* force = getenv("W4A16_ONE_LAUNCH");
-        const bool want = force && *force ? atoi(force) != 0 : reread < 2.0e9;
+        const int force = overrides().one_launch;
+        const bool want = force >= 0 ? force != 0 : reread < 2.0e9;
         if (want && prefill_fused_supported(g13, p13, g2, p2)) p13.flags |= W4A16_PLAN_ONE_LAUNCH;
     }
     *gate_up = p13;
