@@ -339,6 +339,53 @@ def test_gemm_prefill_split_k(orc, plan_args):
         assert np.array_equal(bits(out), first), "replay %d differs" % rep
 
 
+@pytest.mark.parametrize("plan_args", [("prefill", 16, 2, 4, 1, 64), ("prefill", 16, 2, 4, 1, 144), ("prefill", 64, 2, 4, 1),
+                                       ("prefill", 32, 2, 4, 1, 128)], ids=PLAN_ID)
+@pytest.mark.parametrize("N", [96, 40, 42])
+def test_prefill_epilogue_store_paths(orc, plan_args, N):
+    """The prefill epilogue stores binary32 and SiLU*mul outputs through an LDS-staged tile with 16-byte stores
+    when rows are whole 16-byte chunks and the output is 16-byte aligned, and lane by lane otherwise.  N = 42
+    (rows of 168 bytes) and outputs that start 4 or 2 bytes into their buffer take the lane path.  Both paths
+    give the same bits, within the GEMM bar of the oracle, and leave the rows of non-local routes untouched."""
+    _say("prefill epilogue paths N=%d %s" % (N, plan_args))
+    rng = np.random.default_rng(4100 + N)
+    T, E, k, K = 150, 5, 2, 288
+    x = synth.activations(rng, T, K)
+    codes, scales = synth.codes(rng, E, N, K), synth.scales(rng, E, N, K)
+    ids = synth.uniform_topk(rng, T, E, k)
+    ids[3, 0] = -1
+    ids[90, 1] = E + 2
+    w = _pack(codes, scales)
+    plan = w4.make_plan(*plan_args)
+    route = w4.route_prep(i32(ids), E, plan.block_m)
+    acc, _ = orc.grouped_gemm(x, k, codes, scales, ids, acc64=True)
+    flat = ids.reshape(-1)
+    valid = (flat >= 0) & (flat < E)
+    R = T * k
+    aligned = torch.full((R, N), float("nan"), dtype=torch.float32, device="cuda")
+    buf = torch.full((R * N + 4,), float("nan"), dtype=torch.float32, device="cuda")
+    shifted = buf[1:1 + R * N].view(R, N)  # starts 4 bytes into its buffer
+    assert shifted.data_ptr() % 16 == 4
+    xd = u16(x)
+    w4.grouped_gemm(xd, k, w, route, plan, out=aligned, out_f32=True)
+    w4.grouped_gemm(xd, k, w, route, plan, out=shifted, out_f32=True)
+    a, b = aligned.cpu().numpy(), shifted.cpu().numpy()
+    assert np.array_equal(a[valid].view(np.uint32), b[valid].view(np.uint32)), "staged and lane stores differ"
+    assert np.all(np.isnan(a[~valid])) and np.all(np.isnan(b[~valid])), "a row of a non-local route was written"
+    assert np.all(np.isnan(buf[:1].cpu().numpy())) and np.all(np.isnan(buf[1 + R * N:].cpu().numpy()))
+    check_gemm_f32(a.astype(np.float64), acc, flat, E, "epilogue f32 N=%d" % N)
+    if N % 32 == 0:  # the SiLU*mul epilogue pairs 16-column gate and up blocks
+        h_al = poison_bf16(R, N // 2)
+        hbuf = torch.full((R * (N // 2) + 8,), -1, dtype=torch.int16, device="cuda")
+        h_sh = hbuf[1:1 + R * (N // 2)].view(R, N // 2).view(torch.bfloat16)  # 2 bytes into its buffer
+        w4.grouped_gemm_silu(xd, k, w, route, plan, out=h_al)
+        w4.grouped_gemm_silu(xd, k, w, route, plan, out=h_sh)
+        ha, hb = bits(h_al), bits(h_sh)
+        assert np.array_equal(ha, hb), "staged and lane SiLU*mul stores differ"
+        assert np.all(hbuf[:1].cpu().numpy() == -1) and np.all(hbuf[1 + R * (N // 2):].cpu().numpy() == -1)
+        check_act(ha, acc, ids, E, label="epilogue silu N=%d" % N)
+
+
 @pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
 @pytest.mark.parametrize("plan_args", [("decode", 16, 4, 4, 1), ("decode", 16, 2, 4, 3), ("prefill", 64, 2, 4, 1),
                                        ("prefill", 32, 2, 4, 1, 128), ("prefill", 32, 4, 4, 2, 64),
