@@ -343,10 +343,11 @@ def test_gemm_prefill_split_k(orc, plan_args):
                                        ("prefill", 32, 2, 4, 1, 128)], ids=PLAN_ID)
 @pytest.mark.parametrize("N", [96, 40, 42])
 def test_prefill_epilogue_store_paths(orc, plan_args, N):
-    """The prefill epilogue stores binary32 and SiLU*mul outputs through an LDS-staged tile with 16-byte stores
-    when rows are whole 16-byte chunks and the output is 16-byte aligned, and lane by lane otherwise.  N = 42
-    (rows of 168 bytes) and outputs that start 4 or 2 bytes into their buffer take the lane path.  Both paths
-    give the same bits, within the GEMM bar of the oracle, and leave the rows of non-local routes untouched."""
+    """The prefill epilogue stores binary32, BF16 and SiLU*mul outputs through an LDS-staged tile with 16-byte
+    stores when rows are whole 16-byte chunks and the output is 16-byte aligned, and lane by lane otherwise.
+    N = 42 (rows of 168 or 84 bytes) and outputs that start 4 or 2 bytes into their buffer take the lane path.
+    Both paths give the same bits, within the GEMM bar of the oracle, and leave the rows of non-local routes
+    and the memory around the output untouched."""
     _say("prefill epilogue paths N=%d %s" % (N, plan_args))
     rng = np.random.default_rng(4100 + N)
     T, E, k, K = 150, 5, 2, 288
@@ -374,6 +375,16 @@ def test_prefill_epilogue_store_paths(orc, plan_args, N):
     assert np.all(np.isnan(a[~valid])) and np.all(np.isnan(b[~valid])), "a row of a non-local route was written"
     assert np.all(np.isnan(buf[:1].cpu().numpy())) and np.all(np.isnan(buf[1 + R * N:].cpu().numpy()))
     check_gemm_f32(a.astype(np.float64), acc, flat, E, "epilogue f32 N=%d" % N)
+    # BF16 output: staged where rows are whole 16-byte chunks (N % 8 == 0) and the output is 16-byte aligned
+    o_al = poison_bf16(R, N)
+    obuf = torch.full((R * N + 8,), -1, dtype=torch.int16, device="cuda")
+    o_sh = obuf[1:1 + R * N].view(R, N).view(torch.bfloat16)  # 2 bytes into its buffer
+    w4.grouped_gemm(xd, k, w, route, plan, out=o_al)
+    w4.grouped_gemm(xd, k, w, route, plan, out=o_sh)
+    oa, ob = bits(o_al), bits(o_sh)
+    assert np.array_equal(oa, ob), "staged and lane BF16 stores differ"
+    assert np.all(obuf[:1].cpu().numpy() == -1) and np.all(obuf[1 + R * N:].cpu().numpy() == -1)
+    check_gemm(oa, acc, ids, E, label="epilogue bf16 N=%d" % N)
     if N % 32 == 0:  # the SiLU*mul epilogue pairs 16-column gate and up blocks
         h_al = poison_bf16(R, N // 2)
         hbuf = torch.full((R * (N // 2) + 8,), -1, dtype=torch.int16, device="cuda")

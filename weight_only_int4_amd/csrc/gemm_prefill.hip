@@ -483,6 +483,38 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, uint8_t* sl
             }
         }
     }
+    // The BF16 output likewise, in one pass for tiles of up to 144 rows (256-byte rows with two n-blocks per
+    // wavefront); the four row quads of an instruction are XOR-swizzled by 32 bytes each, which spreads them over
+    // all the banks.
+    constexpr int RB2 = COLS * 2;  // bytes of a staged BF16 row
+    constexpr int GP2 = (16 * MT * KT * 2) / (16 * RB2);
+    if constexpr (OM == kOutBf16 && GP2 >= MTA && NBW == 2) {
+        staged = (sh.N & 7) == 0 && (reinterpret_cast<uintptr_t>(p.out) & 15) == 0;
+        if (staged) {
+            constexpr int CPR = RB2 / 16;  // 16-byte chunks per row
+            uint8_t* stg = slot0;
+            __syncthreads();  // every wavefront has finished reading the ring
+#pragma unroll
+            for (int mt = 0; mt < MTA; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int q = 0; q < NBW; ++q) {
+                        const int row = mt * 16 + 4 * c + r, byte = ((w * NBW + q) * 16 + j) * 2;
+                        const int pch = (byte >> 4) ^ (((row >> 2) & 3) << 1);
+                        *reinterpret_cast<uint16_t*>(stg + row * RB2 + pch * 16 + (byte & 15)) =
+                            f32_to_bf16_bits(acc[mt][q][r]);
+                    }
+            __syncthreads();
+            for (int idx = threadIdx.x; idx < BM * CPR; idx += kThreads) {
+                const int row = idx / CPR, ch = idx % CPR;
+                const int sid = ssid[row], n = nt * COLS + ch * 8;
+                if (sid < 0 || n >= sh.N) continue;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * RB2 + ((ch ^ (((row >> 2) & 3) << 1)) * 16));
+                *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.out) + (size_t)sid * sh.N + n) = v;
+            }
+        }
+    }
 #pragma unroll
     for (int mt = 0; mt < MTA; ++mt)
 #pragma unroll
