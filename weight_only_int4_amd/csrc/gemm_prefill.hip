@@ -406,7 +406,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, uint8_t* sl
     // writes its h values to the staged tile, then the workgroup stores whole rows with 16-byte stores (8 lanes
     // cover a row's 128 bytes), not 2-byte stores four rows at a time.
     constexpr int OC = kWaves * 16 * (NBW / 2);  // activation columns of the tile
-    constexpr int RS = OC * 2 + 16;              // bytes of a staged row (padded against bank conflicts)
+    constexpr int RS = OC * 2;                   // bytes of a staged row
     constexpr bool kStageFits = OM == kOutAct && 16 * MTA * RS <= 16 * MT * KT * 2;
     bool staged = false;
     if constexpr (kStageFits) {
@@ -421,8 +421,13 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, uint8_t* sl
                 for (int r = 0; r < 4; ++r)
 #pragma unroll
                     for (int q = 0; q < NBW / 2; ++q)
-                        *reinterpret_cast<uint16_t*>(stg + (mt * 16 + 4 * c + r) * RS + ((w * (NBW / 2) + q) * 16 + j) * 2) =
+                    {
+                        // the four row quads of an instruction XOR-swizzled by 32 bytes each: all banks, no conflict
+                        const int row = mt * 16 + 4 * c + r, byte = ((w * (NBW / 2) + q) * 16 + j) * 2;
+                        const int pch = (byte >> 4) ^ (((row >> 2) & 3) << 1);
+                        *reinterpret_cast<uint16_t*>(stg + row * RS + pch * 16 + (byte & 15)) =
                             f32_to_bf16_bits(silu_mul(acc[mt][q][r], acc[mt][q + NBW / 2][r]));
+                    }
             __syncthreads();
             constexpr int CPR = OC / 8;  // 16-byte chunks per row
             // gate_up role: h is read by down workgroups of the same launch, so it is stored device-coherently
@@ -432,7 +437,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, uint8_t* sl
                 const int row = idx / CPR, ch = idx % CPR;
                 const int sid = ssid[row], n = nt * OC + ch * 8;
                 if (sid < 0 || n >= NO) continue;
-                const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * RS + ch * 16);
+                const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * RS + ((ch ^ (((row >> 2) & 3) << 1)) * 16));
                 if constexpr (ROLE == kRoleGateUp)
                     __builtin_amdgcn_raw_buffer_store_b128(v, hres, (int)(((uint32_t)sid * (uint32_t)NO + (uint32_t)n) * 2u), 0,
                                                           kBufferDeviceCoherent);
