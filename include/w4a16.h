@@ -387,11 +387,21 @@ int w4a16_silu_mul_f32(const float* gu, int rows, int I, uint16_t* h, hipStream_
 int w4a16_moe_combine(const float* y, const float* topk_w, const int32_t* topk_ids, int T, int k, int E,
                       int H, uint16_t* out, hipStream_t s);
 
+/* w4a16_moe_combine over y in BF16 (y device BF16 bits [T*k, H], 4-byte
+ * aligned): each y value is widened exactly to binary32, then summed as
+ * above.  The fused step's y is BF16 (the survey's reading of the rounding of
+ * intermediates: the GPU path may round the down projection's output to BF16,
+ * an error of at most 2^-9 relative, while the oracle keeps it binary32). */
+int w4a16_moe_combine_bf16(const uint16_t* y, const float* topk_w, const int32_t* topk_ids, int T, int k, int E,
+                           int H, uint16_t* out, hipStream_t s);
+
 /* Fused expert MLP: route_prep -> gate_up GEMM with SiLU*mul -> down GEMM ->
  * weighted top-k combine.  Its output is exactly that of the sequence
  * w4a16_route_prep, w4a16_grouped_gemm_silu (a_row_div = k),
- * w4a16_grouped_gemm_f32 (down, a_row_div = 1), w4a16_moe_combine, with the
- * plans of w4a16_fused_moe_plans and the buffers carved from ws.  A decode
+ * w4a16_grouped_gemm (down, a_row_div = 1, BF16 y), w4a16_moe_combine_bf16,
+ * with the plans of w4a16_fused_moe_plans and the buffers carved from ws.
+ * y is BF16: half the bytes of binary32 for down to write and the combine to
+ * read, for one more rounding per route (at most 2^-9 of that route's value).  A decode
  * step (decode plans of 16-row blocks, at most 4096 routes) routes its rows
  * inside the gate_up kernel instead of a separate launch: the same routing
  * tensors and outputs, one launch fewer.
@@ -470,8 +480,8 @@ int w4a16_fused_moe_planned(const uint16_t* x, const int32_t* topk_ids, const fl
  *   x, topk_ids, topk_w, T, k, w13, w2, out: as in w4a16_fused_moe.
  * A call whose workspace (w4a16_fused_moe_workspace_bytes) exceeds the
  * scratch fails with WORKSPACE_TOO_SMALL before anything is launched; that
- * covers decode steps up to about R*(4H + 2I) bytes of intermediates, e.g.
- * 256 tokens of the Kimi-K2 one-GPU share or 512 of a Qwen3-30B-A3B layer.
+ * covers steps up to about R*(2H + 2I) bytes of intermediates, e.g.
+ * 512 tokens of the Kimi-K2 one-GPU share or 2048 of a Qwen3-30B-A3B layer.
  * Every call on one GPU shares that GPU's scratch and leaves its contents
  * behind; the split-K counters are cleared on the stream before use.  Calls
  * that overlap on one GPU (other streams, other threads) race.

@@ -111,12 +111,12 @@ def check_act(got_bits: np.ndarray, gu_ref: np.ndarray, topk_flat: np.ndarray, E
 # over the token's valid routes j (y_j: the oracle's binary32 down-projection row of route t*k + j).  S_t is the
 # scale the token's weighted sum is built from: the combine adds the routes' errors with weights tw, so
 # normalising by max|out_t| instead would make the bar depend on how far the k weighted rows cancel.  Derived
-# from the GEMM bar (5e-3 of an output's scale, BF16 output rounding included): y_j carries the down GEMM's own
-# error plus the gate_up error passed on through h (silu*mul has slope of about 1, the down GEMM is linear), at
-# most 5e-3 each; y stays binary32 and the single BF16 rounding of the output (at most 2^-9 |out_t| <= 2^-9 S_t)
-# stands in for the GEMM's.  Measured worst cases: 5.5e-3 of S_t (300 tokens, top-2, H 256, I 128: short sums),
-# 2.5e-3 at the DeepSeek-V3 layer of 4096 tokens.
-FUSED_TOL = 1e-2
+# from the GEMM bar (5e-3 of an output's scale, BF16 output rounding included): the GPU's y_j is the down GEMM's
+# BF16 output, so it carries that GEMM's own error with its rounding (at most 5e-3) plus the gate_up error passed
+# on through h (silu*mul has slope of about 1, the down GEMM is linear; at most 5e-3), and the single BF16
+# rounding of the output adds at most 2^-9 |out_t| <= 2^-9 S_t.  The oracle keeps y binary32 (the survey's
+# reading of intermediates lets the GPU path round it).
+FUSED_TOL = 1e-2 + 2.0 ** -9
 
 
 def check_fused(got_bits: np.ndarray, out_acc: np.ndarray, y: np.ndarray, tw: np.ndarray, ids: np.ndarray, E: int,

@@ -759,18 +759,32 @@ def orc_bf16_to_f64(b):
     return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
+@pytest.mark.parametrize("ydt", ["f32", "bf16", "bf16-shifted"])
 @pytest.mark.parametrize("T,k,H,E", [(21, 4, 128, 6), (5, 8, 7168, 9), (7, 10, 2056, 12), (9, 3, 130, 4),
                                      (70000, 2, 16, 5)],
                          ids=lambda v: str(v))
-def test_moe_combine(orc, T, k, H, E):
+def test_moe_combine(orc, T, k, H, E, ydt):
     # eight columns per lane when H % 8 == 0 (with a partial last column group, and more routes than one unrolled
-    # pass), two per lane otherwise; past 65535 tokens the tokens go in grid.x
+    # pass), two per lane otherwise; past 65535 tokens the tokens go in grid.x.  y binary32 or BF16 (the fused
+    # step's); "bf16-shifted" starts y 4 bytes past a 16-byte boundary, which takes the two-column kernel.
     rng = np.random.default_rng(8 + H)
     y = rng.standard_normal((T * k, H)).astype(np.float32)
     tw = rng.uniform(0, 1, (T, k)).astype(np.float32)
     ids = rng.integers(-2, E + 2, (T, k)).astype(np.int32)
     ids[3, :] = -1
-    got = bits(w4.moe_combine(f32(y), f32(tw), i32(ids), E))
+    if ydt == "f32":
+        got = bits(w4.moe_combine(f32(y), f32(tw), i32(ids), E))
+    else:
+        yb = torch.from_numpy(y).to(torch.bfloat16)
+        y = yb.float().numpy()  # the BF16 values the kernel reads, exactly
+        if ydt == "bf16-shifted":
+            buf = torch.empty(T * k * H + 8, dtype=torch.bfloat16, device="cuda")
+            yd = buf[2:2 + T * k * H].view(T * k, H)
+            assert yd.data_ptr() % 16 == 4
+            yd.copy_(yb.cuda())
+        else:
+            yd = yb.cuda()
+        got = bits(w4.moe_combine(yd, f32(tw), i32(ids), E))
     ref = orc.combine(y.astype(np.float64), tw, ids, E)
     g, r = orc_bf16_to_f64(got), orc_bf16_to_f64(ref)
     assert np.all(got[3] == 0)
@@ -878,7 +892,7 @@ def test_fused_moe_equals_sequence(orc, shape, plans):
     route = w4.route_prep(i32(ids), E, p13.block_m)
     h = poison_bf16(T * k, I)
     w4.grouped_gemm_silu(u16(x), k, w13, route, p13, out=h)
-    y = w4.grouped_gemm(h, 1, w2, route, p2, out_f32=True)
+    y = w4.grouped_gemm(h, 1, w2, route, p2)  # the fused step's y is BF16
     seq = bits(w4.moe_combine(y, f32(tw), i32(ids), E))
     got = bits(out)
     assert np.all(got[0] == 0)
@@ -1101,7 +1115,7 @@ def test_fused_moe_random_shapes(orc, seed, fmt):
     route = w4.route_prep(i32(ids), E, p13.block_m)
     h = poison_bf16(T * k, I)
     w4.grouped_gemm_silu(u16(x), k, w13, route, p13, out=h)
-    y = w4.grouped_gemm(h, 1, w2, route, p2, out_f32=True)
+    y = w4.grouped_gemm(h, 1, w2, route, p2)  # the fused step's y is BF16
     seq = bits(w4.moe_combine(y, f32(tw), i32(ids), E))
     assert np.array_equal(got, seq), "fused differs from the sequence in %d values" % int((got != seq).sum())
     _, _, y_ref = orc.fused_moe(x, ids, tw, c13, s13, c2, s2, fmt=fmt)

@@ -65,7 +65,7 @@ def test_noalloc_equals_workspace_call_on_consecutive_calls():
 
 
 def test_noalloc_refuses_a_step_beyond_the_scratch():
-    T, E, k, H, I = 2048, 16, 8, 2048, 256  # y alone is T*k*H*4 = 128 MiB
+    T, E, k, H, I = 4096, 16, 8, 2048, 256  # y (BF16) alone is T*k*H*2 = 128 MiB
     x, ids, tw, w13, w2 = _layer(7, T, E, k, H, I)
     assert w4.fused_moe_workspace_bytes(T, k, w13, w2) > L.NOALLOC_SCRATCH_BYTES
     out = torch.full((T, H), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)

@@ -296,7 +296,7 @@ FusedLayout fused_layout(int T, int k, int E, int H, int I, int BM, size_t split
     f.off_offsets = o; o = align_up(o + sizeof(int32_t) * (size_t)(E + 1), 256);
     f.off_counts = o; o = align_up(o + sizeof(int32_t) * (size_t)E, 256);
     f.off_h = o;      o = align_up(o + sizeof(uint16_t) * R * I, 256);
-    f.off_y = o;      o = align_up(o + sizeof(float) * R * H, 256);
+    f.off_y = o;      o = align_up(o + sizeof(uint16_t) * R * H, 256);  // y in BF16
     f.total = o;
     return f;
 }
@@ -853,6 +853,18 @@ int w4a16_moe_combine(const float* y, const float* topk_w, const int32_t* topk_i
     return check_launch(launch_combine(y, topk_w, topk_ids, T, k, E, H, out, s), "w4a16_moe_combine");
 }
 
+int w4a16_moe_combine_bf16(const uint16_t* y, const float* topk_w, const int32_t* topk_ids, int T, int k, int E, int H,
+                           uint16_t* out, hipStream_t s) {
+    if (T < 0 || k < 1 || E < 1 || H < 2 || H % 2)
+        return fail(W4A16_INVALID_ARG, "w4a16_moe_combine_bf16: T=%d k=%d E=%d H=%d (H must be even)", T, k, E, H);
+    if (T == 0) return ok();
+    if (!y || !topk_w || !topk_ids || !out)
+        return fail(W4A16_INVALID_ARG, "w4a16_moe_combine_bf16: NULL pointer argument");
+    if (((uintptr_t)y & 3u) || ((uintptr_t)out & 3u))
+        return fail(W4A16_INVALID_ARG, "w4a16_moe_combine_bf16: misaligned buffer");
+    return check_launch(launch_combine_bf16(y, topk_w, topk_ids, T, k, E, H, out, s), "w4a16_moe_combine_bf16");
+}
+
 // A decode step of 16-row blocks on the register-streaming kernel with at most kSelfRouteMaxRoutes routes routes its
 // rows inside the gate_up kernel (every gate_up workgroup reads all the ids into LDS, so larger steps keep the
 // routing launch).  With W4A16_PLAN_ONE_LAUNCH on the gate_up plan such a step also runs down in the same launch (down's
@@ -882,7 +894,7 @@ static FusedPlan fused_full_layout(int T, int k, const w4a16_weights* w13, const
     route_bounds(T, k, E, p13.block_m, &maxP, &maxB);
     const GemmWs a = gemm_ws(w13->shape, p13, maxB), b = gemm_ws(w2->shape, p2, maxB);
     GemmArgs g13{nullptr, k, nullptr, w13->shape, nullptr, nullptr, R, maxB, nullptr, kOutAct};
-    GemmArgs g2{nullptr, 1, nullptr, w2->shape, nullptr, nullptr, R, maxB, nullptr, kOutF32};
+    GemmArgs g2{nullptr, 1, nullptr, w2->shape, nullptr, nullptr, R, maxB, nullptr, kOutBf16};
     FusedPlan fp;
     fp.one_launch = (p13.flags & W4A16_PLAN_ONE_LAUNCH) &&
                     ((fused_self_route(R, E, g13, p13) && decode_fused_supported(g13, p13, g2, p2)) ||
@@ -999,7 +1011,7 @@ int w4a16_fused_moe_plans_hint(int T, int k, const w4a16_weights* w13, const w4a
     // more often than it gains at the one tail.  W4A16_ONE_LAUNCH=0 or 1 forces the choice where the plans allow it.
     if (p13.kernel == W4A16_KERNEL_PREFILL) {
         GemmArgs g13{nullptr, k, nullptr, w13->shape, nullptr, nullptr, T * k, 0, nullptr, kOutAct};
-        GemmArgs g2{nullptr, 1, nullptr, w2->shape, nullptr, nullptr, T * k, 0, nullptr, kOutF32};
+        GemmArgs g2{nullptr, 1, nullptr, w2->shape, nullptr, nullptr, T * k, 0, nullptr, kOutBf16};
         const double reread = (double)prefill_n_tiles(w2->shape, p2) * T * k * I * 2.0;
         const int force = overrides().one_launch;
         const bool want = force >= 0 ? force != 0 : reread < 2.0e9;
@@ -1050,11 +1062,11 @@ int w4a16_fused_moe_planned(const uint16_t* x, const int32_t* topk_ids, const fl
     int32_t* offsets = reinterpret_cast<int32_t*>(base + f.off_offsets);
     int32_t* counts = reinterpret_cast<int32_t*>(base + f.off_counts);
     uint16_t* h = reinterpret_cast<uint16_t*>(base + f.off_h);
-    float* y = reinterpret_cast<float*>(base + f.off_y);
+    uint16_t* y = reinterpret_cast<uint16_t*>(base + f.off_y);
     const int R = T * k;
     GemmArgs g13{x, k, w13->packed, w13->shape, sorted_ids, expert_ids, R, f.maxB, h, kOutAct};
     g13.ntp = ntp;
-    GemmArgs g2{h, 1, w2->packed, w2->shape, sorted_ids, expert_ids, R, f.maxB, y, kOutF32};
+    GemmArgs g2{h, 1, w2->packed, w2->shape, sorted_ids, expert_ids, R, f.maxB, y, kOutBf16};
     g2.ntp = ntp;
     rc = check_prefill_shape(what, g13, p13);
     if (!rc) rc = check_prefill_shape(what, g2, p2);
@@ -1125,7 +1137,7 @@ int w4a16_fused_moe_planned(const uint16_t* x, const int32_t* topk_ids, const fl
         if (rc) return rc;
     }
     W4A16_STAGE(3);
-    rc = check_launch(launch_combine(y, topk_w, topk_ids, T, k, E, H, out, s), "w4a16_fused_moe (combine)");
+    rc = check_launch(launch_combine_bf16(y, topk_w, topk_ids, T, k, E, H, out, s), "w4a16_fused_moe (combine)");
     if (rc) return rc;
     W4A16_STAGE(4);
 #undef W4A16_STAGE

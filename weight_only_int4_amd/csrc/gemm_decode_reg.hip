@@ -403,7 +403,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void gemm_decode_reg_kernel(Deco
                                                      blockIdx.z, ssid, &s_last, sr_lds, FusedSync{});
 }
 
-// gate_up (SiLU*mul into h) and down (binary32 y) of one decode step in one launch; both route their rows in-kernel.
+// gate_up (SiLU*mul into h) and down (BF16 y) of one decode step in one launch; both route their rows in-kernel.
 // Workgroups [0, ng) are gate_up's (pos_gu positions per K slice), the rest down's.
 template <int NBW1, int NBW2, int D, int FMT>
 __global__ __launch_bounds__(kDecodeThreads, 1) void gemm_decode_fused_kernel(DecodeParams gu, DecodeParams dn,
@@ -418,7 +418,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void gemm_decode_fused_kernel(De
         decode_reg_body<NBW1, D, kOutAct, FMT, true, kRoleGateUp>(gu, x % pos_gu, nt_gu, ks_gu, x / pos_gu, ssid, &s_last,
                                                                   sr_lds, fs);
     else
-        decode_reg_body<NBW2, D, kOutF32, FMT, true, kRoleDown>(dn, (x - ng) % pos_dn, nt_dn, ks_dn, (x - ng) / pos_dn,
+        decode_reg_body<NBW2, D, kOutBf16, FMT, true, kRoleDown>(dn, (x - ng) % pos_dn, nt_dn, ks_dn, (x - ng) / pos_dn,
                                                                 ssid, &s_last, sr_lds, fs);
 }
 
@@ -529,7 +529,7 @@ hipError_t launch_gemm_decode_fused(const GemmArgs& a13, const w4a16_plan& p13, 
                                     const w4a16_plan& p2, unsigned* sync, hipStream_t s) {
     if (a13.max_blocks == 0) return hipSuccess;
     if (!decode_fused_supported(a13, p13, a2, p2) || a13.self_route_ids == nullptr || a2.self_route_ids == nullptr ||
-        a13.out_mode != kOutAct || a2.out_mode != kOutF32 || sync == nullptr || a13.R > kSelfRouteMaxRoutes ||
+        a13.out_mode != kOutAct || a2.out_mode != kOutBf16 || sync == nullptr || a13.R > kSelfRouteMaxRoutes ||
         a2.R > kSelfRouteMaxRoutes || a13.sh.E > W4A16_MAX_EXPERTS)
         return hipErrorInvalidValue;
     if ((p13.k_split > 1 && (a13.partials == nullptr || a13.counters == nullptr)) ||

@@ -629,7 +629,7 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<MT, NBW>())) void
     prefill_body<MT, NBW, OM, RB16, FMT, kRolePlain>(p, (int)blockIdx.x, slot0, slot1, ssid, &s_last, nullptr);
 }
 
-// gate_up (SiLU*mul into h) and down (binary32 y) of a fused step in one launch: workgroups [0, ng) are gate_up's,
+// gate_up (SiLU*mul into h) and down (BF16 y) of a fused step in one launch: workgroups [0, ng) are gate_up's,
 // the rest down's.  Every gate_up workgroup of an XCD is dispatched before that XCD's first down workgroup and
 // waits on nothing, so a down workgroup's wait for its tile always ends.  ng is a multiple of 8, so the XCD of a
 // workgroup is the XCD its role's position maps to.
@@ -645,7 +645,7 @@ __global__ __launch_bounds__(kThreads, (prefill_waves_per_simd<MT, NBW>())) void
     __shared__ int s_last;
     const int id = (int)blockIdx.x;
     if (id < ng) prefill_body<MT, NBW, kOutAct, RB16, FMT, kRoleGateUp>(gu, id, slot0, slot1, ssid, &s_last, &fs);
-    else prefill_body<MT, NBW, kOutF32, RB16, FMT, kRoleDown>(dn, id - ng, slot0, slot1, ssid, &s_last, &fs);
+    else prefill_body<MT, NBW, kOutBf16, RB16, FMT, kRoleDown>(dn, id - ng, slot0, slot1, ssid, &s_last, &fs);
 }
 
 template <int MT, int NBW, int OM, int RB16>
@@ -781,7 +781,7 @@ bool prefill_fused_supported(const GemmArgs& a13, const w4a16_plan& p13, const G
 hipError_t launch_gemm_prefill_fused(const GemmArgs& a13, const w4a16_plan& p13, const GemmArgs& a2,
                                      const w4a16_plan& p2, unsigned* sync, hipStream_t s) {
     if (a13.max_blocks == 0) return hipSuccess;
-    if (!prefill_fused_supported(a13, p13, a2, p2) || a13.out_mode != kOutAct || a2.out_mode != kOutF32 ||
+    if (!prefill_fused_supported(a13, p13, a2, p2) || a13.out_mode != kOutAct || a2.out_mode != kOutBf16 ||
         sync == nullptr || a13.tiles == nullptr || a13.tile_count == nullptr || a13.tiles != a2.tiles ||
         a13.max_blocks != a2.max_blocks)
         return hipErrorInvalidValue;

@@ -41,8 +41,51 @@ __global__ __launch_bounds__(256) void silu_mul_f32_kernel(const float* __restri
     *reinterpret_cast<uint32_t*>(h + (size_t)r * I + c) = packed;
 }
 
+// Loads of y rows: binary32 (the unfused down projection's output) or BF16 bits (the fused step's y).
+__device__ __forceinline__ void load_y2(const float* p, float* v) {
+    const float2 t = *reinterpret_cast<const float2*>(p);
+    v[0] = t.x;
+    v[1] = t.y;
+}
+__device__ __forceinline__ void load_y2(const uint16_t* p, float* v) {
+    const uint32_t t = *reinterpret_cast<const uint32_t*>(p);
+    v[0] = bf16_to_f32(t & 0xFFFFu);
+    v[1] = bf16_to_f32(t >> 16);
+}
+
+// Eight consecutive values of a y row, fetched into registers (issue) and widened to binary32 (unpack), so that
+// the loads of several routes can be in flight before the first is used.
+template <typename Y>
+struct Y8;
+template <>
+struct Y8<float> {
+    float4 a, b;
+    __device__ __forceinline__ void issue(const float* p) {
+        a = reinterpret_cast<const float4*>(p)[0];
+        b = reinterpret_cast<const float4*>(p)[1];
+    }
+    __device__ __forceinline__ void unpack(float* v) const {
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+};
+template <>
+struct Y8<uint16_t> {
+    uint4 a;
+    __device__ __forceinline__ void issue(const uint16_t* p) { a = *reinterpret_cast<const uint4*>(p); }
+    __device__ __forceinline__ void unpack(float* v) const {
+        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+            v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+        }
+    }
+};
+
 // out[t,n] = bf16(sum_{valid j ascending} tw[t,j] * y[t*k+j, n]); two columns per thread.
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const float* __restrict__ tw,
+template <typename Y>
+__global__ __launch_bounds__(256) void combine_kernel(const Y* __restrict__ y, const float* __restrict__ tw,
                                                       const int32_t* __restrict__ ids, int T, int k, int E, int H,
                                                       uint16_t* __restrict__ out) {
     const int pairs = H >> 1;
@@ -54,24 +97,25 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         const int e = ids[(size_t)t * k + jj];
         if (e < 0 || e >= E) continue;
         const float wt = tw[(size_t)t * k + jj];
-        const float2 v = *reinterpret_cast<const float2*>(y + ((size_t)t * k + jj) * H + n);
-        a0 = __builtin_fmaf(wt, v.x, a0);  // one rounding per route, as in every combine of this library
-        a1 = __builtin_fmaf(wt, v.y, a1);
+        float v[2];
+        load_y2(y + ((size_t)t * k + jj) * H + n, v);
+        a0 = __builtin_fmaf(wt, v[0], a0);  // one rounding per route, as in every combine of this library
+        a1 = __builtin_fmaf(wt, v[1], a1);
     }
     const uint32_t packed = (uint32_t)f32_to_bf16_bits(a0) | ((uint32_t)f32_to_bf16_bits(a1) << 16);
     *reinterpret_cast<uint32_t*>(out + (size_t)t * H + n) = packed;
 }
 
 // The same sum, eight columns per lane: one workgroup per (token, 2048 columns).  The token's ids and weights
-// are uniform across the workgroup; the y rows of up to eight routes are in flight together (two 16-byte loads
-// per route and lane) before any is accumulated, in route order as above.  Needs H % 8 == 0.
+// are uniform across the workgroup; the y rows of up to eight routes are in flight together (one or two 16-byte
+// loads per route and lane) before any is accumulated, in route order as above.  Needs H % 8 == 0.
 constexpr int kCombineCols = 8;
 constexpr int kCombineUnroll = 8;
 
 // COLS_FAST: the column group is grid.x, so the workgroups of one token run next to each other and read its
 // rows of y together (grid.y then holds the tokens, at most 65535)
-template <bool COLS_FAST>
-__global__ __launch_bounds__(256) void combine8_kernel(const float* __restrict__ y, const float* __restrict__ tw,
+template <typename Y, bool COLS_FAST>
+__global__ __launch_bounds__(256) void combine8_kernel(const Y* __restrict__ y, const float* __restrict__ tw,
                                                        const int32_t* __restrict__ ids, int T, int k, int E, int H,
                                                        uint16_t* __restrict__ out) {
     const int t = COLS_FAST ? blockIdx.y : blockIdx.x;
@@ -83,7 +127,7 @@ __global__ __launch_bounds__(256) void combine8_kernel(const float* __restrict__
 #pragma unroll
     for (int c = 0; c < kCombineCols; ++c) acc[c] = 0.f;
     for (int j0 = 0; j0 < k; j0 += kCombineUnroll) {
-        float4 v[kCombineUnroll][2];
+        Y8<Y> v[kCombineUnroll];
         float wt[kCombineUnroll];
         bool ok[kCombineUnroll];
 #pragma unroll
@@ -92,17 +136,13 @@ __global__ __launch_bounds__(256) void combine8_kernel(const float* __restrict__
             const int e = j < k ? tid[j] : -1;
             ok[u] = e >= 0 && e < E;
             wt[u] = ok[u] ? tww[j] : 0.f;
-            if (ok[u]) {
-                const float4* row = reinterpret_cast<const float4*>(y + ((size_t)t * k + j) * H + n);
-                v[u][0] = row[0];
-                v[u][1] = row[1];
-            }
+            if (ok[u]) v[u].issue(y + ((size_t)t * k + j) * H + n);
         }
 #pragma unroll
         for (int u = 0; u < kCombineUnroll; ++u) {
             if (!ok[u]) continue;
-            const float vv[kCombineCols] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w,
-                                            v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
+            float vv[kCombineCols];
+            v[u].unpack(vv);
 #pragma unroll
             for (int c = 0; c < kCombineCols; ++c) acc[c] = __builtin_fmaf(wt[u], vv[c], acc[c]);
         }
@@ -143,23 +183,34 @@ hipError_t launch_silu_mul_f32(const float* gu, int rows, int I, uint16_t* h, hi
     return hipGetLastError();
 }
 
-hipError_t launch_combine(const float* y, const float* tw, const int32_t* ids, int T, int k, int E, int H,
-                          uint16_t* out, hipStream_t s) {
+template <typename Y>
+hipError_t launch_combine_t(const Y* y, const float* tw, const int32_t* ids, int T, int k, int E, int H,
+                            uint16_t* out, hipStream_t s) {
     const long work = (long)T * (H / 2);
     if (work == 0) return hipSuccess;
     if (H % kCombineCols == 0 && ((uintptr_t)y & 15u) == 0 && ((uintptr_t)out & 15u) == 0) {
         const unsigned col_groups = (unsigned)((H / kCombineCols + 255) / 256);
         if (T <= 65535)
-            hipLaunchKernelGGL(combine8_kernel<true>, dim3(col_groups, (unsigned)T), dim3(256), 0, s, y, tw, ids, T, k,
-                               E, H, out);
+            hipLaunchKernelGGL((combine8_kernel<Y, true>), dim3(col_groups, (unsigned)T), dim3(256), 0, s, y, tw, ids,
+                               T, k, E, H, out);
         else
-            hipLaunchKernelGGL(combine8_kernel<false>, dim3((unsigned)T, col_groups), dim3(256), 0, s, y, tw, ids, T, k,
-                               E, H, out);
+            hipLaunchKernelGGL((combine8_kernel<Y, false>), dim3((unsigned)T, col_groups), dim3(256), 0, s, y, tw, ids,
+                               T, k, E, H, out);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, y, tw, ids, T, k, E, H,
-                       out);
+    hipLaunchKernelGGL((combine_kernel<Y>), dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, y, tw, ids, T, k, E,
+                       H, out);
     return hipGetLastError();
+}
+
+hipError_t launch_combine(const float* y, const float* tw, const int32_t* ids, int T, int k, int E, int H,
+                          uint16_t* out, hipStream_t s) {
+    return launch_combine_t(y, tw, ids, T, k, E, H, out, s);
+}
+
+hipError_t launch_combine_bf16(const uint16_t* y, const float* tw, const int32_t* ids, int T, int k, int E, int H,
+                               uint16_t* out, hipStream_t s) {
+    return launch_combine_t(y, tw, ids, T, k, E, H, out, s);
 }
 
 }  // namespace w4a16

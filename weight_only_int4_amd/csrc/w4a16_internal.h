@@ -174,7 +174,7 @@ size_t decode_counters(const Shape& sh, const w4a16_plan& p, int max_blocks);
 hipError_t launch_gemm_decode(const GemmArgs& a, const w4a16_plan& p, hipStream_t s);
 bool decode_reg_supported(const GemmArgs& a, const w4a16_plan& p);
 hipError_t launch_gemm_decode_reg(const GemmArgs& a, const w4a16_plan& p, hipStream_t s);
-// The decode step's gate_up (SiLU*mul into h) and down (binary32 y) in one launch, both on the register-streaming
+// The decode step's gate_up (SiLU*mul into h) and down (BF16 y) in one launch, both on the register-streaming
 // kernel with in-kernel routing (self_route_ids set in both), down's workgroups of a route block starting once
 // gate_up's column tiles of that block have stored h.  sync: 2 * max_blocks + 1 words, zero at rest; each
 // GEMM's split-K area its own.
@@ -201,5 +201,7 @@ hipError_t launch_silu_mul_f32(const float* gu, int rows, int I, uint16_t* h, hi
 hipError_t launch_zero_words(uint32_t* p, size_t n, hipStream_t s);
 hipError_t launch_combine(const float* y, const float* tw, const int32_t* ids, int T, int k, int E, int H,
                           uint16_t* out, hipStream_t s);
+hipError_t launch_combine_bf16(const uint16_t* y, const float* tw, const int32_t* ids, int T, int k, int E, int H,
+                               uint16_t* out, hipStream_t s);
 
 }  // namespace w4a16

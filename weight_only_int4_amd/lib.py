@@ -79,6 +79,7 @@ _SIGS = {
     "w4a16_grouped_gemm_offsets": (_I, [_P, _P, _I, _P, ctypes.POINTER(Plan), _P, _P, _SZ, _P]),
     "w4a16_silu_mul": (_I, [_P, _I, _I, _P, _P]),
     "w4a16_moe_combine": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P]),
+    "w4a16_moe_combine_bf16": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "w4a16_fused_moe_workspace_bytes": (_I, [_I, _I, _P, _P, ctypes.POINTER(_SZ)]),
     "w4a16_fused_moe": (_I, [_P, _P, _P, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "w4a16_fused_moe_profiled": (_I, [_P, _P, _P, _I, _I, _P, _P, _P, _P, _SZ, _P, _P]),
@@ -436,11 +437,13 @@ def silu_mul(gu: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> 
 
 def moe_combine(y: torch.Tensor, topk_w: torch.Tensor, topk_ids: torch.Tensor, E: int,
                 out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Weighted top-k combine of y [T*k, H], binary32 or BF16 (the BF16 entry point for the latter)."""
     T, k = topk_ids.shape
     H = y.shape[1]
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
-    _check(load().w4a16_moe_combine(_ptr(y), _ptr(topk_w), _ptr(topk_ids), T, k, E, H, _ptr(out), _stream(stream)))
+    fn = load().w4a16_moe_combine_bf16 if y.dtype in (torch.bfloat16, torch.int16) else load().w4a16_moe_combine
+    _check(fn(_ptr(y), _ptr(topk_w), _ptr(topk_ids), T, k, E, H, _ptr(out), _stream(stream)))
     return out
 
 
