@@ -389,9 +389,9 @@ int w4a16_moe_combine(const float* y, const float* topk_w, const int32_t* topk_i
 
 /* w4a16_moe_combine over y in BF16 (y device BF16 bits [T*k, H], 4-byte
  * aligned): each y value is widened exactly to binary32, then summed as
- * above.  The fused step's y is BF16 (the survey's reading of the rounding of
- * intermediates: the GPU path may round the down projection's output to BF16,
- * an error of at most 2^-9 relative, while the oracle keeps it binary32). */
+ * above.  The fused step's y is BF16: rounding the down projection's output
+ * costs at most 2^-9 of each value and halves the bytes that down writes and
+ * this combine reads. */
 int w4a16_moe_combine_bf16(const uint16_t* y, const float* topk_w, const int32_t* topk_ids, int T, int k, int E,
                            int H, uint16_t* out, hipStream_t s);
 

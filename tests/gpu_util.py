@@ -114,8 +114,7 @@ def check_act(got_bits: np.ndarray, gu_ref: np.ndarray, topk_flat: np.ndarray, E
 # from the GEMM bar (5e-3 of an output's scale, BF16 output rounding included): the GPU's y_j is the down GEMM's
 # BF16 output, so it carries that GEMM's own error with its rounding (at most 5e-3) plus the gate_up error passed
 # on through h (silu*mul has slope of about 1, the down GEMM is linear; at most 5e-3), and the single BF16
-# rounding of the output adds at most 2^-9 |out_t| <= 2^-9 S_t.  The oracle keeps y binary32 (the survey's
-# reading of intermediates lets the GPU path round it).
+# rounding of the output adds at most 2^-9 |out_t| <= 2^-9 S_t.  The oracle keeps y binary32.
 FUSED_TOL = 1e-2 + 2.0 ** -9
 
 
