@@ -489,6 +489,27 @@ def test_gemm_prefill_tile_list(orc, plan_args):
     assert np.array_equal(gi, ref_bits), "tile list, integer regime over several column tiles: must be bit-exact"
 
 
+def test_gemm_prefill_tile_list_many_blocks(orc):
+    # more than 8192 route blocks of 16 rows (about 150 000 routed rows over 1000 experts): the tile list is built by
+    # the kernel that keeps its runs in scratch memory, past the register form's reach; integer regime, bit-exact
+    _say("gemm prefill tile list, many blocks")
+    rng = np.random.default_rng(4343)
+    E, N, K = 1000, 32, 64
+    counts = rng.integers(0, 300, E)
+    counts[rng.integers(0, E, 40)] = 0                         # some empty experts
+    ids = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(counts)])
+    ids = ids[rng.permutation(ids.size)].reshape(-1, 1)
+    plan = w4.make_plan("prefill", 16, 2, 4, 1, 144)
+    max_p, max_b = w4.route_bounds(ids.shape[0], 1, E, 16)
+    assert max_b > 8192, max_b
+    xi = synth.to_bf16_bits(rng.integers(-2, 3, size=(ids.shape[0], K)).astype(np.float32))
+    ci = synth.codes(rng, E, N, K)
+    si = np.full((E, N, K // 32), 0x3D80, np.uint16)  # 2^-4
+    gi = _run_gemm(synth.GemmCase("tile list many", xi, 1, ci, si, ids), plan)
+    _, ref_bits = orc.grouped_gemm(xi, 1, ci, si, ids)
+    assert np.array_equal(gi, ref_bits), "tile list beyond 8192 blocks, integer regime: must be bit-exact"
+
+
 # ------------------------------------------------------------------ offsets form
 
 @pytest.mark.parametrize("plan_args", [("decode", 16, 4, 4, 1), ("decode", 16, 2, 4, 2), ("prefill", 64, 4, 4, 1),

@@ -6,11 +6,15 @@
 // one workgroup with no host readback, so the routed count never leaves the
 // device (Chord page, "vLLM integration").
 //
-// Order inside an expert is ascending route index: each chunk of 1024 routes
-// is ranked by (earlier chunks) + (earlier wavefronts of this chunk) + (lower
-// lanes of this wavefront with the same expert).  The last term comes from a
+// Order inside an expert is ascending route index.  The routes are cut into
+// super-chunks of kRegChunks * (workgroup size) routes, and each wavefront
+// takes a contiguous run of kRegChunks * 64 routes of a super-chunk, 64 at a
+// time.  A route's rank is (earlier super-chunks) + (earlier wavefronts of
+// its super-chunk) + (the wavefront's earlier routes of that expert) + (lower
+// lanes of the same 64 with the same expert).  The last term comes from a
 // per-expert lane mask that the wavefront's lanes build in LDS with one atomic
-// OR each (wave_rank).
+// OR each; the third from a per-wavefront running count, so the wavefronts
+// rank their runs without a barrier between the groups of 64.
 #include <climits>
 
 #include "w4a16_internal.h"
@@ -25,20 +29,80 @@ constexpr int kRegChunks = 4;       // chunks of routes the one-workgroup routin
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-// Rank of this lane's route among the lanes of its wavefront routed to the same expert e, in lane order.  mrow is
-// the wavefront's row of per-expert lane masks in LDS, zero at rest: every valid lane sets its bit in mrow[e] with
-// one atomic OR, reads the mask back (a wavefront's LDS operations complete in issue order, so the read sees every
-// lane's OR) and counts the set bits below its own.  The lowest lane of each expert (the leader, rank 0) then
-// replaces the mask by the number of lanes routed to e, which the caller reads as that wavefront's count and resets
-// to zero once every wavefront of the workgroup has read it.
-__device__ __forceinline__ int wave_rank(uint64_t* mrow, int e, bool valid, int lane, bool* leader) {
-    if (valid) __hip_atomic_fetch_or(&mrow[e], 1ull << lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    const uint64_t m = valid ? __hip_atomic_load(&mrow[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) : 0ull;
+// Scatter of one super-chunk of routes into sorted_ids.  Lane `lane` of wavefront `wave` holds in e_reg[u] the
+// expert of route first + (wave * kRegChunks + u) * 64 + lane (-1 when past the routes or when the caller has no
+// route there).  base[e] is the slot of expert e's next route and is advanced by the super-chunk's routes of e.
+// mrow: per wavefront and expert a 64-bit word, run: per wavefront and expert a byte, both zero at rest and left
+// zero.  Every thread of the workgroup calls this (it has barriers).
+//
+// Ranking inside a wavefront, for the u-th group of 64: every valid lane sets its bit in mrow[wave][e] with one
+// atomic OR and reads the mask back (a wavefront's LDS operations complete in issue order, so the read sees every
+// lane's OR); its rank among the wavefront's routes of e so far is run[wave][e] (the earlier groups) plus the set
+// bits below its own.  The lowest lane of each expert (rank 0 within the group) then adds the group's count to
+// run (at most 64 per group, so it holds at most 192 before the last group) and clears the mask, or in the last
+// group leaves the group's count in the mask.  The wavefront's count of e is then run + mask.
+template <int NT>
+__device__ void scatter_super_chunk(const int (&e_reg)[kRegChunks], int first, int E, uint64_t* mrow, uint8_t* run,
+                                   int* base, int32_t* __restrict__ sorted_ids) {
+    constexpr int NW = NT / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint64_t* mw = mrow + (size_t)wave * E;
+    uint8_t* rw = run + (size_t)wave * E;
     const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int rank = __popcll(m & lower);
-    *leader = valid && rank == 0;
-    if (*leader) __hip_atomic_store(&mrow[e], (uint64_t)__popcll(m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    return rank;
+    int rank[kRegChunks];
+#pragma unroll
+    for (int u = 0; u < kRegChunks; ++u) {
+        const int e = e_reg[u];
+        const bool valid = e >= 0 && e < E;
+        if (valid) __hip_atomic_fetch_or(&mw[e], 1ull << lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const uint64_t m = valid ? __hip_atomic_load(&mw[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) : 0ull;
+        const int prev = valid ? (int)rw[e] : 0;
+        const int r = __popcll(m & lower);
+        rank[u] = prev + r;
+        if (valid && r == 0) {
+            if (u + 1 < kRegChunks) {
+                rw[e] = (uint8_t)(prev + __popcll(m));
+                __hip_atomic_store(&mw[e], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            } else {
+                __hip_atomic_store(&mw[e], (uint64_t)__popcll(m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+        }
+    }
+    __syncthreads();
+    // per expert: the first slot of each wavefront's routes of e (earlier wavefronts first), kept in the mask word
+    for (int e = tid; e < E; e += NT) {
+        int slot = base[e];
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const int c = (int)run[(size_t)w * E + e] + (int)mrow[(size_t)w * E + e];
+            mrow[(size_t)w * E + e] = (uint64_t)slot;
+            run[(size_t)w * E + e] = 0;
+            slot += c;
+        }
+        base[e] = slot;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kRegChunks; ++u) {
+        const int e = e_reg[u];
+        if (e >= 0 && e < E) sorted_ids[(int)mw[e] + rank[u]] = first + (wave * kRegChunks + u) * 64 + lane;
+    }
+    __syncthreads();
+    for (int x = tid; x < NW * E; x += NT) mrow[x] = 0ull;
+    __syncthreads();
+}
+
+// Experts of one super-chunk in the layout scatter_super_chunk takes: lane `lane` of wavefront `wave` loads route
+// first + (wave * kRegChunks + u) * 64 + lane, for routes below `end` (64 consecutive ids per load).
+template <int NT>
+__device__ __forceinline__ void load_super_chunk(const int32_t* __restrict__ ids, int first, int end,
+                                                 int (&e_reg)[kRegChunks]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int u = 0; u < kRegChunks; ++u) {
+        const int i = first + (wave * kRegChunks + u) * 64 + lane;
+        e_reg[u] = i < end ? ids[i] : -1;
+    }
 }
 
 // Exclusive scan of one int per thread across the workgroup; returns the
@@ -55,14 +119,17 @@ __device__ int block_exclusive_scan(int v, int* wave_tot, int* total) {
     }
     if (lane == 63) wave_tot[wave] = incl;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        int run = 0;
-        for (int w = 0; w < kW; ++w) {
-            const int t = wave_tot[w];
-            wave_tot[w] = run;
-            run += t;
+    if (wave == 0) {
+        // the wavefront totals, scanned across the lanes of the first wavefront (no serial chain of LDS accesses)
+        const int t = lane < kW ? wave_tot[lane] : 0;
+        int run = t;
+#pragma unroll
+        for (int off = 1; off < kW; off <<= 1) {
+            const int o = __shfl_up(run, off, 64);
+            if (lane >= off) run += o;
         }
-        wave_tot[kW] = run;
+        if (lane < kW) wave_tot[lane] = run - t;
+        if (lane == kW - 1) wave_tot[kW] = run;
     }
     __syncthreads();
     const int excl = wave_tot[wave] + incl - v;
@@ -91,7 +158,7 @@ __device__ void emit_tiles(const TileOut& to, int L, int b0e, int* wave_tot) {
 }
 
 // Shared memory layout: wave_cnt[(NT / 64)][E] (64-bit lane masks, then counts) | ints cnt[E] | pad_off[E+1] |
-// base[E] | wave_tot[(NT / 64)+1]
+// base[E] | wave_tot[(NT / 64)+1] | bytes run[(NT / 64)][E]
 template <int NT>
 __global__ __launch_bounds__(NT) void route_prep_kernel(const int32_t* __restrict__ ids, int R, int E, int BM,
                                                               int max_padded, int max_blocks,
@@ -106,20 +173,24 @@ __global__ __launch_bounds__(NT) void route_prep_kernel(const int32_t* __restric
     int* pad_off = cnt + E;
     int* base = pad_off + E + 1;
     int* wave_tot = base + E;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint8_t* run = reinterpret_cast<uint8_t*>(wave_tot + (NT / 64) + 1);
+    const int tid = threadIdx.x;
 
     for (int e = tid; e < E; e += NT) cnt[e] = 0;
-    for (int x = tid; x < (NT / 64) * E; x += NT) wave_cnt[x] = 0ull;
+    for (int x = tid; x < (NT / 64) * E; x += NT) {
+        wave_cnt[x] = 0ull;
+        run[x] = 0;
+    }
     __syncthreads();
-    // the ids of the first kRegChunks chunks are loaded together and stay in registers for the scatter below, so
-    // neither pass waits on a load per chunk (later chunks, past kRegChunks * NT routes, are read again)
+    // the ids of the first super-chunk are loaded together and stay in registers for the scatter below, so neither
+    // pass waits on a load per group (later super-chunks, past kRegChunks * NT routes, are read again)
+    constexpr int kSuper = kRegChunks * NT;
     int e_reg[kRegChunks];
-#pragma unroll
-    for (int ci = 0; ci < kRegChunks; ++ci) e_reg[ci] = ci * NT + tid < R ? ids[ci * NT + tid] : -1;
+    load_super_chunk<NT>(ids, 0, R, e_reg);
 #pragma unroll
     for (int ci = 0; ci < kRegChunks; ++ci)
         if (e_reg[ci] >= 0 && e_reg[ci] < E) atomicAdd(&cnt[e_reg[ci]], 1);
-    for (int i = tid + kRegChunks * NT; i < R; i += NT) {
+    for (int i = tid + kSuper; i < R; i += NT) {
         const int e = ids[i];
         if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
     }
@@ -145,8 +216,11 @@ __global__ __launch_bounds__(NT) void route_prep_kernel(const int32_t* __restric
     if (to.tiles) emit_tiles<NT>(to, padded / BM, off_p / BM, wave_tot);
     __syncthreads();
 
-    // every slot starts as the sentinel; the scatter below overwrites valid ones
-    for (int p = tid; p < max_padded; p += NT) sorted_ids[p] = R;
+    // the sentinel in every slot the scatter below leaves alone: each expert's padding [off_p + c, off_p + padded)
+    // and everything from tot_p on (the scatter writes exactly the slots [off_p, off_p + c) of each expert)
+    if (tid < E)
+        for (int p = off_p + c; p < off_p + padded; ++p) sorted_ids[p] = R;
+    for (int p = tot_p + tid; p < max_padded; p += NT) sorted_ids[p] = R;
     for (int b = tid; b < max_blocks; b += NT) {
         const int p = b * BM;
         int owner = -1;
@@ -160,42 +234,23 @@ __global__ __launch_bounds__(NT) void route_prep_kernel(const int32_t* __restric
         }
         expert_ids[b] = owner;
     }
-    __syncthreads();  // sentinel stores complete before any scatter store
 
-    // one chunk of NT routes, ranked in route order: earlier chunks (base), earlier wavefronts (wave_cnt), lower
-    // lanes with the same expert (wave_rank)
-    auto scatter_chunk = [&](int chunk, int e) {
-        const int i = chunk + tid;
-        const bool valid = e >= 0 && e < E;
-        bool leader;
-        const int rank_w = wave_rank(wave_cnt + (size_t)wave * E, e, valid, lane, &leader);
-        __syncthreads();
-        if (valid) {
-            int prior = base[e];
-            for (int w = 0; w < wave; ++w) prior += (int)wave_cnt[w * E + e];
-            sorted_ids[prior + rank_w] = i;
-        }
-        __syncthreads();
-        if (leader) {
-            atomicAdd(&base[e], (int)wave_cnt[wave * E + e]);
-            wave_cnt[wave * E + e] = 0ull;
-        }
-        __syncthreads();
-    };
-#pragma unroll
-    for (int ci = 0; ci < kRegChunks; ++ci)
-        if (ci * NT < R) scatter_chunk(ci * NT, e_reg[ci]);  // uniform
-    for (int chunk = kRegChunks * NT; chunk < R; chunk += NT)
-        scatter_chunk(chunk, chunk + tid < R ? ids[chunk + tid] : -1);
+    // super-chunks in route order, each ranked from base (the routes of earlier super-chunks)
+    scatter_super_chunk<NT>(e_reg, 0, E, wave_cnt, run, base, sorted_ids);
+    for (int first = kSuper; first < R; first += kSuper) {  // uniform
+        load_super_chunk<NT>(ids, first, R, e_reg);
+        scatter_super_chunk<NT>(e_reg, first, E, wave_cnt, run, base, sorted_ids);
+    }
 }
 
 // ---- the same routing tensors from several workgroups, for many routes (needs scratch)
 //
-// Routes are cut into chunks of kChunk.  (1) Each chunk's workgroup counts its routes per expert.  (2) One
-// workgroup turns the counts into per-expert totals, offsets and padded offsets (as above), and each chunk's
-// first slot per expert: the expert's padded offset plus the routes of that expert in earlier chunks; it also
-// writes the sentinels and expert_ids.  (3) Each chunk's workgroup scatters its routes from those bases with the
-// same in-chunk ranking as above, so the order inside an expert is again ascending route index.
+// Routes are cut into chunks of kChunk (one super-chunk).  (1) Each chunk's workgroup counts its routes per
+// expert.  (2) One workgroup turns the counts into per-expert totals, offsets and padded offsets (as above), and
+// each chunk's first slot per expert: the expert's padded offset plus the routes of that expert in earlier
+// chunks; it also writes the sentinels of the padding slots and expert_ids.  (3) Each chunk's workgroup scatters
+// its routes from those bases with the same ranking as above, so the order inside an expert is again ascending
+// route index.
 constexpr int kChunk = 4 * kThreads;
 constexpr int kScanRegChunks = 16;  // chunk counts per expert the scan holds in registers (65536 routes)
 
@@ -266,7 +321,10 @@ __global__ __launch_bounds__(kThreads) void route_scan_kernel(int R, int E, int 
     }
     if (to.tiles) emit_tiles<kThreads>(to, padded / BM, off_p / BM, wave_tot);
     __syncthreads();
-    for (int p = tid; p < max_padded; p += kThreads) sorted_ids[p] = R;
+    // the sentinel in the slots the scatter kernel leaves alone (as in route_prep_kernel)
+    if (tid < E)
+        for (int p = off_p + c; p < off_p + padded; ++p) sorted_ids[p] = R;
+    for (int p = tot_p + tid; p < max_padded; p += kThreads) sorted_ids[p] = R;
     for (int b = tid; b < max_blocks; b += kThreads) {
         const int p = b * BM;
         int owner = -1;
@@ -282,48 +340,27 @@ __global__ __launch_bounds__(kThreads) void route_scan_kernel(int R, int E, int 
     }
 }
 
-// Shared memory: wave_cnt[kWaves][E] (64-bit lane masks, then counts) | ints base[E]
+// Shared memory: wave_cnt[kWaves][E] (64-bit lane masks, then first slots) | ints base[E] | bytes run[kWaves][E]
 __global__ __launch_bounds__(kThreads) void route_scatter_kernel(const int32_t* __restrict__ ids, int R, int E,
                                                                  const int32_t* __restrict__ chunk_base,
                                                                  int32_t* __restrict__ sorted_ids) {
+    static_assert(kChunk == kRegChunks * kThreads, "a chunk is one super-chunk");
     extern __shared__ uint64_t smem64[];
     uint64_t* wave_cnt = smem64;
     int* base = reinterpret_cast<int*>(wave_cnt + kWaves * E);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = blockIdx.x;
+    uint8_t* run = reinterpret_cast<uint8_t*>(base + E);
+    const int tid = threadIdx.x, c = blockIdx.x;
     const int end = min(R, (c + 1) * kChunk);
     // the chunk's ids, loaded together up front
-    constexpr int kSubs = kChunk / kThreads;
-    int e_reg[kSubs];
-#pragma unroll
-    for (int u = 0; u < kSubs; ++u) {
-        const int i = c * kChunk + u * kThreads + tid;
-        e_reg[u] = i < end ? ids[i] : -1;
-    }
+    int e_reg[kRegChunks];
+    load_super_chunk<kThreads>(ids, c * kChunk, end, e_reg);
     for (int e = tid; e < E; e += kThreads) base[e] = chunk_base[(size_t)c * E + e];
-    for (int x = tid; x < kWaves * E; x += kThreads) wave_cnt[x] = 0ull;
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < kSubs; ++u) {
-        const int sub = c * kChunk + u * kThreads;
-        if (sub >= end) break;  // uniform
-        const int i = sub + tid;
-        const int e = e_reg[u];
-        const bool valid = e >= 0 && e < E;
-        bool leader;
-        const int rank_w = wave_rank(wave_cnt + (size_t)wave * E, e, valid, lane, &leader);
-        __syncthreads();
-        if (valid) {
-            int prior = base[e];
-            for (int w = 0; w < wave; ++w) prior += (int)wave_cnt[w * E + e];
-            sorted_ids[prior + rank_w] = i;
-        }
-        __syncthreads();
-        if (leader) {
-            atomicAdd(&base[e], (int)wave_cnt[wave * E + e]);
-            wave_cnt[wave * E + e] = 0ull;
-        }
-        __syncthreads();
+    for (int x = tid; x < kWaves * E; x += kThreads) {
+        wave_cnt[x] = 0ull;
+        run[x] = 0;
     }
+    __syncthreads();
+    scatter_super_chunk<kThreads>(e_reg, c * kChunk, E, wave_cnt, run, base, sorted_ids);
 }
 
 // Inclusive max-scan of one int per thread across the workgroup.
@@ -337,13 +374,17 @@ __device__ int block_inclusive_max(int v, int* wave_tot) {
     }
     if (lane == 63) wave_tot[wave] = incl;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        int run = INT_MIN;
-        for (int w = 0; w < kWaves; ++w) {
-            const int t = wave_tot[w];
-            wave_tot[w] = run;
-            run = t > run ? t : run;
+    if (wave == 0) {
+        // exclusive max over the earlier wavefronts' totals, across the lanes of the first wavefront
+        const int t = lane < kWaves ? wave_tot[lane] : INT_MIN;
+        int run = t;
+#pragma unroll
+        for (int off = 1; off < kWaves; off <<= 1) {
+            const int o = __shfl_up(run, off, 64);
+            if (lane >= off && o > run) run = o;
         }
+        const int prev = __shfl_up(run, 1, 64);
+        if (lane < kWaves) wave_tot[lane] = lane == 0 ? INT_MIN : prev;
     }
     __syncthreads();
     const int r = wave_tot[wave] > incl ? wave_tot[wave] : incl;
@@ -362,16 +403,85 @@ __device__ int block_suffix_min(int v, int* wave_tot) {
     }
     if (lane == 0) wave_tot[wave] = incl;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        int run = INT_MAX;
-        for (int w = kWaves - 1; w >= 0; --w) {
-            const int t = wave_tot[w];
-            wave_tot[w] = run;
-            run = t < run ? t : run;
+    if (wave == 0) {
+        // exclusive min over the later wavefronts' totals, across the lanes of the first wavefront
+        const int t = lane < kWaves ? wave_tot[lane] : INT_MAX;
+        int run = t;
+#pragma unroll
+        for (int off = 1; off < kWaves; off <<= 1) {
+            const int o = __shfl_down(run, off, 64);
+            if (lane + off < kWaves && o < run) run = o;
         }
+        const int next = __shfl_down(run, 1, 64);
+        if (lane < kWaves) wave_tot[lane] = lane == kWaves - 1 ? INT_MAX : next;
     }
     __syncthreads();
     const int r = wave_tot[wave] < incl ? wave_tot[wave] : incl;
+    __syncthreads();
+    return r;
+}
+
+// Exclusive max-scan of one int per thread across a workgroup of NT threads (INT_MIN for thread 0).
+template <int NT>
+__device__ int block_exclusive_max(int v, int* wave_tot) {
+    constexpr int kW = NT / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off, 64);
+        if (lane >= off && o > incl) incl = o;
+    }
+    int excl = __shfl_up(incl, 1, 64);
+    if (lane == 0) excl = INT_MIN;
+    if (lane == 63) wave_tot[wave] = incl;
+    __syncthreads();
+    if (wave == 0) {
+        const int t = lane < kW ? wave_tot[lane] : INT_MIN;
+        int run = t;
+#pragma unroll
+        for (int off = 1; off < kW; off <<= 1) {
+            const int o = __shfl_up(run, off, 64);
+            if (lane >= off && o > run) run = o;
+        }
+        const int prev = __shfl_up(run, 1, 64);
+        if (lane < kW) wave_tot[lane] = lane == 0 ? INT_MIN : prev;
+    }
+    __syncthreads();
+    const int r = wave_tot[wave] > excl ? wave_tot[wave] : excl;
+    __syncthreads();
+    return r;
+}
+
+// Exclusive min-scan from the right of one int per thread across a workgroup of NT threads (INT_MAX for the last
+// thread).
+template <int NT>
+__device__ int block_exclusive_suffix_min(int v, int* wave_tot) {
+    constexpr int kW = NT / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_down(incl, off, 64);
+        if (lane + off < 64 && o < incl) incl = o;
+    }
+    int excl = __shfl_down(incl, 1, 64);
+    if (lane == 63) excl = INT_MAX;
+    if (lane == 0) wave_tot[wave] = incl;
+    __syncthreads();
+    if (wave == 0) {
+        const int t = lane < kW ? wave_tot[lane] : INT_MAX;
+        int run = t;
+#pragma unroll
+        for (int off = 1; off < kW; off <<= 1) {
+            const int o = __shfl_down(run, off, 64);
+            if (lane + off < kW && o < run) run = o;
+        }
+        const int next = __shfl_down(run, 1, 64);
+        if (lane < kW) wave_tot[lane] = lane == kW - 1 ? INT_MAX : next;
+    }
+    __syncthreads();
+    const int r = wave_tot[wave] < excl ? wave_tot[wave] : excl;
     __syncthreads();
     return r;
 }
@@ -459,6 +569,81 @@ __global__ __launch_bounds__(kThreads) void tile_map_kernel(const int32_t* __res
     if (tid == 0) *count = carry[1];
 }
 
+// The same tile list for up to NT * CH route blocks with the blocks in registers: thread t owns blocks
+// t*CH .. t*CH + CH - 1, so run starts, run ends and tile positions each take one workgroup scan of a per-thread
+// value (the thread's own blocks are scanned in registers), and nothing goes through scratch memory.  The expert
+// ids are loaded up to max_blocks, together with num_tokens_padded rather than behind it.
+template <int NT, int CH>
+__global__ __launch_bounds__(NT) void tile_map_reg_kernel(const int32_t* __restrict__ expert_ids,
+                                                          const int32_t* __restrict__ ntp, int BM, int max_blocks,
+                                                          int group, int32_t* __restrict__ tiles,
+                                                          int32_t* __restrict__ count) {
+    __shared__ int wave_tot[NT / 64 + 1];
+    const int tid = threadIdx.x, b0 = tid * CH;
+    // e[j + 1]: expert of block b0 + j, with the neighbours e[0] and e[CH + 1]; INT_MIN outside [0, nvalid)
+    int e[CH + 2];
+#pragma unroll
+    for (int j = 0; j < CH + 2; ++j) {
+        const int b = b0 + j - 1;
+        e[j] = (b >= 0 && b < max_blocks) ? expert_ids[b] : INT_MIN;
+    }
+    int nvalid = ntp ? *ntp / BM : max_blocks;
+    if (nvalid > max_blocks) nvalid = max_blocks;
+#pragma unroll
+    for (int j = 0; j < CH + 2; ++j)
+        if (b0 + j - 1 >= nvalid) e[j] = INT_MIN;
+    // run starts: the last start at or before each block
+    int first[CH];
+    int m = -1;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+        const int b = b0 + j;
+        if (b < nvalid && e[j] != e[j + 1]) m = b;
+        first[j] = m;
+    }
+    const int carry_first = block_exclusive_max<NT>(m, wave_tot);
+    // run ends: the first end at or after each block
+    int last[CH];
+    int mn = INT_MAX;
+#pragma unroll
+    for (int j = CH - 1; j >= 0; --j) {
+        const int b = b0 + j;
+        if (b < nvalid && e[j + 2] != e[j + 1]) mn = b;
+        last[j] = mn;
+    }
+    const int carry_last = block_exclusive_suffix_min<NT>(mn, wave_tot);
+    // tile anchors in block order
+    int nanchor = 0;
+    int tsize[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+        const int b = b0 + j;
+        tsize[j] = 0;
+        if (b < nvalid && e[j + 1] >= 0) {
+            const int r0 = first[j] > carry_first ? first[j] : carry_first;
+            const int r1 = last[j] < carry_last ? last[j] : carry_last;
+            const int L = r1 - r0 + 1, pos = b - r0;
+            const int nt = (L + group - 1) / group, base = L / nt, rem = L % nt;
+            const int big = rem * (base + 1);  // blocks in the first rem tiles, of base + 1 blocks each
+            const bool anchor = pos < big ? pos % (base + 1) == 0 : (pos - big) % base == 0;
+            if (anchor) {
+                tsize[j] = pos < big ? base + 1 : base;
+                ++nanchor;
+            }
+        }
+    }
+    int total;
+    int at = block_exclusive_scan<NT>(nanchor, wave_tot, &total);
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+        if (tsize[j] > 0) {
+            tiles[2 * at] = b0 + j;
+            tiles[2 * at + 1] = tsize[j];
+            ++at;
+        }
+    if (tid == 0) *count = total;
+}
+
 // Row ranges -> indexed form: rows [start(e), start(e) + count(e)) of expert e become slots of e's padded
 // segment; the sentinel is rows_max.  Offsets form: start(e) = off[e], count(e) = off[e+1] - off[e].  Masked
 // form (off == NULL): start(e) = e * max_m, count(e) = masked_m[e] clamped to [0, max_m].
@@ -533,12 +718,14 @@ hipError_t launch_route_prep(const int32_t* topk_ids, int R, int E, int block_m,
         // few routes and experts (decode steps): half the workgroup, half the barrier cost and LDS to clear;
         // thread e still owns expert e (measured: 0.5-0.7 us less at up to 512 routes, slower beyond)
         constexpr int NT = kSmallThreads, NW = NT / 64;
-        const size_t shmem = sizeof(uint64_t) * (size_t)NW * E + sizeof(int) * ((size_t)E + (E + 1) + E + (NW + 1));
+        const size_t shmem = sizeof(uint64_t) * (size_t)NW * E + sizeof(int) * ((size_t)E + (E + 1) + E + (NW + 1)) +
+                             (size_t)NW * E;
         hipLaunchKernelGGL(route_prep_kernel<NT>, dim3(1), dim3(NT), shmem, s, topk_ids, R, E, block_m,
                            max_padded, max_blocks, sorted_ids, expert_ids, ntp, offsets, counts, to);
         return hipGetLastError();
     }
-    const size_t shmem = sizeof(uint64_t) * (size_t)kWaves * E + sizeof(int) * ((size_t)E + (E + 1) + E + (kWaves + 1));
+    const size_t shmem = sizeof(uint64_t) * (size_t)kWaves * E + sizeof(int) * ((size_t)E + (E + 1) + E + (kWaves + 1)) +
+                         (size_t)kWaves * E;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(route_prep_kernel<kThreads>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (shmem > 65536 && attr != hipSuccess) return attr;
@@ -568,7 +755,7 @@ hipError_t launch_route_prep_scratch(const int32_t* topk_ids, int R, int E, int 
                        counts, to);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const size_t scatter_lds = sizeof(uint64_t) * (size_t)kWaves * E + sizeof(int) * (size_t)E;
+    const size_t scatter_lds = sizeof(uint64_t) * (size_t)kWaves * E + sizeof(int) * (size_t)E + (size_t)kWaves * E;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(route_scatter_kernel),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (scatter_lds > 65536 && attr != hipSuccess) return attr;
@@ -597,6 +784,19 @@ hipError_t launch_masked_to_route(const int32_t* masked_m, int E, int max_m, int
 
 hipError_t launch_tile_map(const int32_t* expert_ids, const int32_t* ntp, int block_m, int max_blocks, int group,
                            int32_t* tiles, int32_t* count, int32_t* scratch, hipStream_t s) {
+    // the register form, 8 route blocks per thread: 256 threads up to 2048 blocks (four wavefronts keep the scans'
+    // barriers cheap), 1024 threads up to 8192 (measured: 32 blocks per thread on 256 threads took twice as long,
+    // its loads strided 128 bytes apart across the lanes)
+    if (max_blocks <= 256 * 8) {
+        hipLaunchKernelGGL((tile_map_reg_kernel<256, 8>), dim3(1), dim3(256), 0, s, expert_ids, ntp, block_m,
+                           max_blocks, group, tiles, count);
+        return hipGetLastError();
+    }
+    if (max_blocks <= kThreads * 8) {
+        hipLaunchKernelGGL((tile_map_reg_kernel<kThreads, 8>), dim3(1), dim3(kThreads), 0, s, expert_ids, ntp,
+                           block_m, max_blocks, group, tiles, count);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(kThreads), 0, s, expert_ids, ntp, block_m, max_blocks, group,
                        tiles, count, scratch);
     return hipGetLastError();
