@@ -812,6 +812,25 @@ def test_moe_combine(orc, T, k, H, E, ydt):
     assert np.all(np.abs(g - r) <= np.abs(r) * 2.0 ** -7 + 1e-6)
 
 
+def test_moe_combine_rejects_bad_arguments():
+    # host-side checks of both combine entry points, before any launch: an odd H, and y off its element alignment
+    # (binary32 y on 8 bytes, BF16 y on 4)
+    T, k, H, E = 4, 2, 64, 3
+    tw = torch.ones((T, k), dtype=torch.float32, device="cuda")
+    ids = torch.zeros((T, k), dtype=torch.int32, device="cuda")
+    out = torch.full((T, H), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    for dt, shift in ((torch.float32, 1), (torch.bfloat16, 1)):
+        buf = torch.zeros(T * k * H + 8, dtype=dt, device="cuda")
+        with pytest.raises(w4.W4A16Error, match="misaligned") as ei:
+            w4.moe_combine(buf[shift:shift + T * k * H].view(T * k, H), tw, ids, E, out=out)
+        assert ei.value.code == -1
+        with pytest.raises(w4.W4A16Error, match="H must be even") as ei:
+            w4.moe_combine(buf[:T * k * (H - 1)].view(T * k, H - 1), tw, ids, E)
+        assert ei.value.code == -1
+    torch.cuda.synchronize()
+    assert np.all(bits(out) == 0xFFFF), "a refused call must write nothing"
+
+
 @pytest.mark.parametrize("shape", [(16, 8, 2, 256, 128), (64, 16, 4, 512, 256), (300, 8, 2, 256, 128),
                                    (3, 4, 2, 128, 64), (2100, 16, 4, 128, 64)],
                          ids=lambda s: "T%d-E%d-k%d-H%d-I%d" % s)
