@@ -1005,7 +1005,8 @@ int w4a16_fused_moe_plans_hint(int T, int k, const w4a16_weights* w13, const w4a
     // launch against two: Qwen3-30B-A3B-shaped steps of 256 .. 4096 tokens 1.2 .. 6% faster (0.1 .. 0.8 GB), of 8192
     // tokens the same (1.6 GB); DeepSeek-V3-shaped steps of 512 and 1024 tokens 0.4% and 0.5% faster (0.9, 1.9 GB),
     // of 2048 and 4096 tokens 0.8% and 0.9% slower (3.8, 7.5 GB); the Kimi-K2 prefill share of 8192 tokens 0.7%
-    // slower (R counts every route; about an eighth are local).  The one launch fills the tail of gate_up's last
+    // slower (R counts every route; about an eighth are local); with y in BF16, DeepSeek-V3-shaped 4096 tokens 1.0%
+    // slower and the Kimi-K2 share the same.  The one launch fills the tail of gate_up's last
     // round with down's first workgroups and saves a launch gap, but every gate_up workgroup stores its rows of h
     // device-coherently and waits for them before it counts its tile ready; a step of many gate_up rounds pays that
     // more often than it gains at the one tail.  W4A16_ONE_LAUNCH=0 or 1 forces the choice where the plans allow it.
