@@ -714,9 +714,10 @@ __global__ __launch_bounds__(kThreads) void offsets_to_route_kernel(const int32_
 hipError_t launch_route_prep(const int32_t* topk_ids, int R, int E, int block_m, int max_padded, int max_blocks,
                              int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntp, int32_t* offsets,
                              int32_t* counts, hipStream_t s, TileOut to) {
-    if (E <= kSmallThreads && R <= kSmallThreads) {
-        // few routes and experts (decode steps): half the workgroup, half the barrier cost and LDS to clear;
-        // thread e still owns expert e (measured: 0.5-0.7 us less at up to 512 routes, slower beyond)
+    if (E <= kSmallThreads && R <= kRegChunks * kSmallThreads) {
+        // few routes and experts: half the workgroup, half the barrier cost and LDS to clear, all routes in one
+        // super-chunk; thread e still owns expert e (measured with 128 and 48 experts: 2048 routes 5.3 us against
+        // 5.9, 4096 routes 8.2 against 7.3 on 1024 threads)
         constexpr int NT = kSmallThreads, NW = NT / 64;
         const size_t shmem = sizeof(uint64_t) * (size_t)NW * E + sizeof(int) * ((size_t)E + (E + 1) + E + (NW + 1)) +
                              (size_t)NW * E;
