@@ -2,9 +2,10 @@
 //
 // Produces the indexed routing tensors (Chord page, "Two kernel families" and
 // Figure 3: activations stay unpadded, padding lives in the index tensors as
-// sentinels) and per-expert offsets (nf4 page, "Usage").  Everything runs in
-// one workgroup with no host readback, so the routed count never leaves the
-// device (Chord page, "vLLM integration").
+// sentinels) and per-expert offsets (nf4 page, "Usage").  Up to 8192 routes
+// everything runs in one workgroup, beyond that in three launches; there is
+// no host readback, so the routed count never leaves the device (Chord page,
+// "vLLM integration").
 //
 // Order inside an expert is ascending route index.  The routes are cut into
 // super-chunks of kRegChunks * (workgroup size) routes, and each wavefront
@@ -25,7 +26,7 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kSmallThreads = 512;  // workgroup of the routing of few routes and experts
-constexpr int kRegChunks = 4;       // chunks of routes the one-workgroup routing keeps in registers
+constexpr int kRegChunks = 4;       // routes per lane held in registers: a super-chunk is kRegChunks x workgroup
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
