@@ -111,10 +111,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const Y* __restrict__ y, c
 // loads per route and lane) before any is accumulated, in route order as above.  Needs H % 8 == 0.
 constexpr int kCombineCols = 8;
 constexpr int kCombineUnroll = 8;
+constexpr size_t kCombineSpecBytes = (size_t)4 << 20;  // y up to this size is loaded before the ids arrive
 
 // COLS_FAST: the column group is grid.x, so the workgroups of one token run next to each other and read its
-// rows of y together (grid.y then holds the tokens, at most 65535)
-template <typename Y, bool COLS_FAST>
+// rows of y together (grid.y then holds the tokens, at most 65535).  SPEC: the y rows of all k routes are
+// loaded before the ids say which are valid (row t*k + j exists for every j), so the loads do not wait for the
+// ids; invalid rows are loaded but not added.  For small y only: a step whose routes are mostly non-local would
+// read many rows it does not need.
+template <typename Y, bool COLS_FAST, bool SPEC>
 __global__ __launch_bounds__(256) void combine8_kernel(const Y* __restrict__ y, const float* __restrict__ tw,
                                                        const int32_t* __restrict__ ids, int T, int k, int E, int H,
                                                        uint16_t* __restrict__ out) {
@@ -133,10 +137,11 @@ __global__ __launch_bounds__(256) void combine8_kernel(const Y* __restrict__ y, 
 #pragma unroll
         for (int u = 0; u < kCombineUnroll; ++u) {
             const int j = j0 + u;
+            if (SPEC && j < k) v[u].issue(y + ((size_t)t * k + j) * H + n);
             const int e = j < k ? tid[j] : -1;
             ok[u] = e >= 0 && e < E;
             wt[u] = ok[u] ? tww[j] : 0.f;
-            if (ok[u]) v[u].issue(y + ((size_t)t * k + j) * H + n);
+            if (!SPEC && ok[u]) v[u].issue(y + ((size_t)t * k + j) * H + n);
         }
 #pragma unroll
         for (int u = 0; u < kCombineUnroll; ++u) {
@@ -190,12 +195,15 @@ hipError_t launch_combine_t(const Y* y, const float* tw, const int32_t* ids, int
     if (work == 0) return hipSuccess;
     if (H % kCombineCols == 0 && ((uintptr_t)y & 15u) == 0 && ((uintptr_t)out & 15u) == 0) {
         const unsigned col_groups = (unsigned)((H / kCombineCols + 255) / 256);
-        if (T <= 65535)
-            hipLaunchKernelGGL((combine8_kernel<Y, true>), dim3(col_groups, (unsigned)T), dim3(256), 0, s, y, tw, ids,
-                               T, k, E, H, out);
+        if (T <= 65535 && (size_t)T * k * H * sizeof(Y) <= kCombineSpecBytes)
+            hipLaunchKernelGGL((combine8_kernel<Y, true, true>), dim3(col_groups, (unsigned)T), dim3(256), 0, s, y, tw,
+                               ids, T, k, E, H, out);
+        else if (T <= 65535)
+            hipLaunchKernelGGL((combine8_kernel<Y, true, false>), dim3(col_groups, (unsigned)T), dim3(256), 0, s, y,
+                               tw, ids, T, k, E, H, out);
         else
-            hipLaunchKernelGGL((combine8_kernel<Y, false>), dim3((unsigned)T, col_groups), dim3(256), 0, s, y, tw, ids,
-                               T, k, E, H, out);
+            hipLaunchKernelGGL((combine8_kernel<Y, false, false>), dim3((unsigned)T, col_groups), dim3(256), 0, s, y,
+                               tw, ids, T, k, E, H, out);
         return hipGetLastError();
     }
     hipLaunchKernelGGL((combine_kernel<Y>), dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, y, tw, ids, T, k, E,
