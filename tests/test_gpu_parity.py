@@ -1127,7 +1127,10 @@ def _random_fused_case(seed):
     return rng, T, E, k, H, I, ids, plans
 
 
-@pytest.mark.parametrize("seed,fmt", [(s, "int4") for s in range(24)] + [(s, "mxfp4") for s in range(24, 32)])
+# seeds 165, 240 and 344: the largest errors of a 300-seed sweep of this generator (1.07e-2 to 1.13e-2 of S_t,
+# short down sums on plain 64-row prefill plans), kept as the cases nearest the bar
+@pytest.mark.parametrize("seed,fmt", [(s, "int4") for s in list(range(24)) + [165, 240, 344]] +
+                         [(s, "mxfp4") for s in range(24, 32)])
 def test_fused_moe_random_shapes(orc, seed, fmt):
     """Seeded random shapes, routings and plans through the fused call, against the oracle (R18's bar) and, bit
     for bit, against the routed sequence with the same plans; the last seeds with MXFP4 weights."""
