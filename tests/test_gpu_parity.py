@@ -782,12 +782,13 @@ def orc_bf16_to_f64(b):
 
 @pytest.mark.parametrize("ydt", ["f32", "bf16", "bf16-shifted"])
 @pytest.mark.parametrize("T,k,H,E", [(21, 4, 128, 6), (5, 8, 7168, 9), (7, 10, 2056, 12), (9, 3, 130, 4),
-                                     (70000, 2, 16, 5)],
+                                     (70000, 2, 16, 5), (600, 8, 1024, 20)],
                          ids=lambda v: str(v))
 def test_moe_combine(orc, T, k, H, E, ydt):
     # eight columns per lane when H % 8 == 0 (with a partial last column group, and more routes than one unrolled
-    # pass), two per lane otherwise; past 65535 tokens the tokens go in grid.x.  y binary32 or BF16 (the fused
-    # step's); "bf16-shifted" starts y 4 bytes past a 16-byte boundary, which takes the two-column kernel.
+    # pass), two per lane otherwise; past 65535 tokens the tokens go in grid.x; y of at most 4 MB is loaded before
+    # the ids (the last shape's y is larger).  y binary32 or BF16 (the fused step's); "bf16-shifted" starts y 4
+    # bytes past a 16-byte boundary, which takes the two-column kernel.
     rng = np.random.default_rng(8 + H)
     y = rng.standard_normal((T * k, H)).astype(np.float32)
     tw = rng.uniform(0, 1, (T, k)).astype(np.float32)
