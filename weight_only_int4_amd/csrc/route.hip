@@ -30,27 +30,15 @@ constexpr int kRegChunks = 4;       // routes per lane held in registers: a supe
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-// Scatter of one super-chunk of routes into sorted_ids.  Lane `lane` of wavefront `wave` holds in e_reg[u] the
-// expert of route first + (wave * kRegChunks + u) * 64 + lane (-1 when past the routes or when the caller has no
-// route there).  base[e] is the slot of expert e's next route and is advanced by the super-chunk's routes of e.
-// mrow: per wavefront and expert a 64-bit word, run: per wavefront and expert a byte, both zero at rest and left
-// zero.  Every thread of the workgroup calls this (it has barriers).
-//
-// Ranking inside a wavefront, for the u-th group of 64: every valid lane sets its bit in mrow[wave][e] with one
-// atomic OR and reads the mask back (a wavefront's LDS operations complete in issue order, so the read sees every
-// lane's OR); its rank among the wavefront's routes of e so far is run[wave][e] (the earlier groups) plus the set
-// bits below its own.  The lowest lane of each expert (rank 0 within the group) then adds the group's count to
-// run (at most 64 per group, so it holds at most 192 before the last group) and clears the mask, or in the last
-// group leaves the group's count in the mask.  The wavefront's count of e is then run + mask.
-template <int NT>
-__device__ void scatter_super_chunk(const int (&e_reg)[kRegChunks], int first, int E, uint64_t* mrow, uint8_t* run,
-                                   int* base, int32_t* __restrict__ sorted_ids) {
-    constexpr int NW = NT / 64;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// The ranking pass of scatter_super_chunk, wavefront by wavefront with no barrier: rank[u] is the rank of the
+// lane's u-th route among its wavefront's routes of the same expert, and afterwards the wavefront's count of e
+// is run[wave][e] + mrow[wave][e].
+__device__ __forceinline__ void rank_super_chunk(const int (&e_reg)[kRegChunks], int E, uint64_t* mrow, uint8_t* run,
+                                                 int (&rank)[kRegChunks]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     uint64_t* mw = mrow + (size_t)wave * E;
     uint8_t* rw = run + (size_t)wave * E;
     const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    int rank[kRegChunks];
 #pragma unroll
     for (int u = 0; u < kRegChunks; ++u) {
         const int e = e_reg[u];
@@ -69,6 +57,28 @@ __device__ void scatter_super_chunk(const int (&e_reg)[kRegChunks], int first, i
             }
         }
     }
+}
+
+// Scatter of one super-chunk of routes into sorted_ids.  Lane `lane` of wavefront `wave` holds in e_reg[u] the
+// expert of route first + (wave * kRegChunks + u) * 64 + lane (-1 when past the routes or when the caller has no
+// route there).  base[e] is the slot of expert e's next route and is advanced by the super-chunk's routes of e.
+// mrow: per wavefront and expert a 64-bit word, run: per wavefront and expert a byte, both zero at rest and left
+// zero.  Every thread of the workgroup calls this (it has barriers).
+//
+// Ranking inside a wavefront, for the u-th group of 64: every valid lane sets its bit in mrow[wave][e] with one
+// atomic OR and reads the mask back (a wavefront's LDS operations complete in issue order, so the read sees every
+// lane's OR); its rank among the wavefront's routes of e so far is run[wave][e] (the earlier groups) plus the set
+// bits below its own.  The lowest lane of each expert (rank 0 within the group) then adds the group's count to
+// run (at most 64 per group, so it holds at most 192 before the last group) and clears the mask, or in the last
+// group leaves the group's count in the mask.  The wavefront's count of e is then run + mask.
+template <int NT>
+__device__ void scatter_super_chunk(const int (&e_reg)[kRegChunks], int first, int E, uint64_t* mrow, uint8_t* run,
+                                   int* base, int32_t* __restrict__ sorted_ids) {
+    constexpr int NW = NT / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint64_t* mw = mrow + (size_t)wave * E;
+    int rank[kRegChunks];
+    rank_super_chunk(e_reg, E, mrow, run, rank);
     __syncthreads();
     // per expert: the first slot of each wavefront's routes of e (earlier wavefronts first), kept in the mask word
     for (int e = tid; e < E; e += NT) {
@@ -186,23 +196,62 @@ __global__ __launch_bounds__(NT) void route_prep_kernel(const int32_t* __restric
     // the ids of the first super-chunk are loaded together and stay in registers for the scatter below, so neither
     // pass waits on a load per group (later super-chunks, past kRegChunks * NT routes, are read again)
     constexpr int kSuper = kRegChunks * NT;
+    constexpr int NW = NT / 64;
     int e_reg[kRegChunks];
     load_super_chunk<NT>(ids, 0, R, e_reg);
+    // One super-chunk (uniform): the ranking pass runs first and its per-wavefront counts give the totals, so
+    // there is no separate counting pass; thread e keeps its expert's wavefront counts in wc.  Otherwise the
+    // routes are counted with LDS atomics and every super-chunk is scattered after the scans.
+    const bool one = R <= kSuper;
+    int rank[kRegChunks];
+    int wc[NW];
+    int c = 0;
+    if (one) {
+        rank_super_chunk(e_reg, E, wave_cnt, run, rank);
+        __syncthreads();
+        if (tid < E) {
 #pragma unroll
-    for (int ci = 0; ci < kRegChunks; ++ci)
-        if (e_reg[ci] >= 0 && e_reg[ci] < E) atomicAdd(&cnt[e_reg[ci]], 1);
-    for (int i = tid + kSuper; i < R; i += NT) {
-        const int e = ids[i];
-        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+            for (int w = 0; w < NW; ++w) {
+                wc[w] = (int)run[(size_t)w * E + tid] + (int)wave_cnt[(size_t)w * E + tid];
+                c += wc[w];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int ci = 0; ci < kRegChunks; ++ci)
+            if (e_reg[ci] >= 0 && e_reg[ci] < E) atomicAdd(&cnt[e_reg[ci]], 1);
+        for (int i = tid + kSuper; i < R; i += NT) {
+            const int e = ids[i];
+            if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+        }
+        __syncthreads();
+        c = tid < E ? cnt[tid] : 0;
     }
-    __syncthreads();
 
-    // scans of counts (unpadded offsets) and padded sizes, E <= NT
-    const int c = tid < E ? cnt[tid] : 0;
+    // scans of counts (unpadded offsets) and padded sizes, E <= NT; one scan of both packed into 16-bit halves
+    // when every partial sum stays below 2^15 (uniform; no sum then reaches the sign bit)
     const int padded = tid < E ? ceil_div(c, BM) * BM : 0;
-    int tot_c, tot_p;
-    const int off_c = block_exclusive_scan<NT>(c, wave_tot, &tot_c);
-    const int off_p = block_exclusive_scan<NT>(padded, wave_tot, &tot_p);
+    int tot_c, tot_p, off_c, off_p;
+    if (R + E * (BM - 1) < 32768) {
+        int tot;
+        const int off = block_exclusive_scan<NT>((padded << 16) | c, wave_tot, &tot);
+        off_c = off & 0xFFFF;
+        off_p = off >> 16;
+        tot_c = tot & 0xFFFF;
+        tot_p = tot >> 16;
+    } else {
+        off_c = block_exclusive_scan<NT>(c, wave_tot, &tot_c);
+        off_p = block_exclusive_scan<NT>(padded, wave_tot, &tot_p);
+    }
+    if (one && tid < E) {
+        // the first slot of each wavefront's routes of this expert, in the mask word (read by the stores below)
+        int slot = off_p;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            wave_cnt[(size_t)w * E + tid] = (uint64_t)slot;
+            slot += wc[w];
+        }
+    }
     if (tid < E) {
         counts_out[tid] = c;
         offsets_out[tid] = off_c;
@@ -236,6 +285,17 @@ __global__ __launch_bounds__(NT) void route_prep_kernel(const int32_t* __restric
         expert_ids[b] = owner;
     }
 
+    if (one) {
+        // the slots were written before the barrier that follows the tile list
+        const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+        for (int u = 0; u < kRegChunks; ++u) {
+            const int e = e_reg[u];
+            if (e >= 0 && e < E)
+                sorted_ids[(int)wave_cnt[(size_t)wave * E + e] + rank[u]] = (wave * kRegChunks + u) * 64 + lane;
+        }
+        return;
+    }
     // super-chunks in route order, each ranked from base (the routes of earlier super-chunks)
     scatter_super_chunk<NT>(e_reg, 0, E, wave_cnt, run, base, sorted_ids);
     for (int first = kSuper; first < R; first += kSuper) {  // uniform
