@@ -57,24 +57,29 @@ __device__ __forceinline__ void load_y2(const uint16_t* p, float* v) {
 // the loads of several routes can be in flight before the first is used.
 template <typename Y>
 struct Y8;
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 template <>
 struct Y8<float> {
-    float4 a, b;
+    f32x4_t a, b;
+    // y is read once: non-temporal loads keep it from displacing other lines in the caches
     __device__ __forceinline__ void issue(const float* p) {
-        a = reinterpret_cast<const float4*>(p)[0];
-        b = reinterpret_cast<const float4*>(p)[1];
+        a = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+        b = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p) + 1);
     }
     __device__ __forceinline__ void unpack(float* v) const {
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+        v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
     }
 };
 template <>
 struct Y8<uint16_t> {
-    uint4 a;
-    __device__ __forceinline__ void issue(const uint16_t* p) { a = *reinterpret_cast<const uint4*>(p); }
+    u32x4 a;
+    // y is read once: non-temporal loads keep it from displacing other lines in the caches
+    __device__ __forceinline__ void issue(const uint16_t* p) {
+        a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    }
     __device__ __forceinline__ void unpack(float* v) const {
-        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+        const uint32_t w[4] = {a[0], a[1], a[2], a[3]};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
